@@ -1,0 +1,541 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one part of the oracle to a library routine (torch CPU in
+float64, numpy's Philox), a closed form, an invariant, brute force, finite
+differences, or a number printed on the source pages (tests/golden).
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import gpt_oracle as O
+from transformer_lm_step_gpt_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")
+
+TINY = I.TINY_FP32.model
+TINY_SPEED = I.ModelConfig(n_layer=2, n_head=2, n_embd=32, mlp_hidden=128, block_size=24,
+                           vocab_size=37, padded_vocab_size=40, max_batch=3,
+                           pos_encoding="rope", qk_rmsnorm=True, mlp_act="relu2",
+                           window_even=5, window_odd=24, logit_softcap=3.0)
+
+
+def facts():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- RNG
+
+@pytest.mark.parametrize("key,ctr", [(0, 0), ((1 << 64) + 5, [1, 2, 3, 4]),
+                                     (0xDEADBEEF12345678, [2**64 - 7, 9, 2**63, 1])])
+def test_philox_matches_numpy_bitgenerator(key, ctr):
+    """numpy.random.Philox is Philox4x64-10; it increments the counter before
+    producing a block, so its first block is ours at counter + 1."""
+    c = [ctr, 0, 0, 0] if np.isscalar(ctr) else list(ctr)
+    bg = np.random.Philox(key=key, counter=np.array(c, dtype=np.uint64))
+    ref = bg.random_raw(12).astype(np.uint64)
+    k0, k1 = key & (2**64 - 1), key >> 64
+    got = []
+    for blk in range(1, 4):
+        carry = blk
+        cc = []
+        for w in c:
+            s = w + carry
+            cc.append(s & (2**64 - 1))
+            carry = s >> 64
+        out = O.philox4x64_10(np.array([cc[0]], np.uint64), np.array([cc[1]], np.uint64),
+                              np.array([cc[2]], np.uint64), np.array([cc[3]], np.uint64), k0, k1)
+        got += [int(o[0]) for o in out]
+    assert [int(r) for r in ref] == got
+
+
+def test_normals_moments():
+    z = O.standard_normals(7, 3, 400_000)
+    assert abs(z.mean()) < 0.01
+    assert abs(z.std() - 1.0) < 0.01
+    from scipy import stats
+    assert stats.kstest(z[:50_000], "norm").pvalue > 1e-4
+    # streams and seeds are different sequences
+    assert not np.allclose(O.standard_normals(7, 4, 64), z[:64])
+    assert not np.allclose(O.standard_normals(8, 3, 64), z[:64])
+
+
+# ---------------------------------------------------------------- parameter table
+
+def _count(cfg):
+    return sum(int(np.prod(s)) for _, s, _, _ in O.param_table(cfg))
+
+
+def test_param_counts_against_pages():
+    f = facts()
+    c3 = I.GPT2_124M.model
+    assert _count(c3) == 124_475_904
+    assert _count(c3.replace(padded_vocab_size=50257)) == 124_439_808
+    t = {n: s for n, s, _, _ in O.param_table(c3.replace(padded_vocab_size=50257))}
+    assert list(t["wte"]) == f["wte_shape"]["value"]
+    assert list(t["wpe"]) == f["wpe_shape"]["value"]
+    saved = 768 * 50257
+    assert abs(saved - f["tying_saves_params"]["value"]) / saved < 0.01
+    assert abs(saved / _count(c3.replace(padded_vocab_size=50257)) - 0.30) < 0.02
+    dec = [n for n, _, d, _ in O.param_table(c3) if d]
+    und = [(n, s) for n, s, d, _ in O.param_table(c3) if not d]
+    assert len(dec) == f["decay_tensor_counts"]["decayed"]
+    assert len(und) == f["decay_tensor_counts"]["undecayed"]
+    n_und = sum(int(np.prod(s)) for _, s in und)
+    assert n_und == 121_344
+    assert 0.5 < n_und / f["decay_tensor_counts"]["undecayed_numbers_approx"] < 2
+    c2 = _count(I.CHAR_BF16.model)
+    assert c2 == 10_770_816
+    assert 0.5 < c2 / f["char_model_params_approx"]["value"] < 2
+
+
+def test_init_statistics():
+    cfg = I.CHAR_BF16.model
+    p = O.init_params(cfg, 2)
+    L = cfg.n_layer
+    for name, arr in p.items():
+        if name.endswith("ln_1.weight") or name.endswith("ln_2.weight") or name == "ln_f.weight":
+            assert np.all(arr == 1.0)
+        elif name.endswith("bias"):
+            assert np.all(arr == 0.0)
+        else:
+            std = 0.02 / math.sqrt(2 * L) if "c_proj.weight" in name else 0.02
+            assert abs(arr.mean()) < 6 * std / math.sqrt(arr.size)
+            assert abs(arr.std() / std - 1) < 0.05
+            assert np.all(arr == arr.astype(np.float32))   # fp32-representable
+    z = O.init_params(cfg.replace(zero_init_proj=True), 2)
+    assert np.all(z["h.0.attn.c_proj.weight"] == 0) and np.all(z["h.3.mlp.c_proj.weight"] == 0)
+    assert np.array_equal(z["h.0.attn.c_attn.weight"], p["h.0.attn.c_attn.weight"])
+
+
+# ---------------------------------------------------------------- pieces vs torch (float64)
+
+def test_layernorm_vs_torch():
+    rng = np.random.default_rng(0)
+    x = rng.normal(size=(7, 33)) * 3 + 1
+    g = rng.normal(size=33)
+    b = rng.normal(size=33)
+    y, cache = O.layernorm_fwd(x, g, b, 1e-5)
+    xt = torch.tensor(x, requires_grad=True)
+    gt = torch.tensor(g, requires_grad=True)
+    bt = torch.tensor(b, requires_grad=True)
+    yt = F.layer_norm(xt, (33,), gt, bt, 1e-5)
+    assert np.allclose(y, yt.detach().numpy(), rtol=1e-12, atol=1e-12)
+    dy = rng.normal(size=y.shape)
+    yt.backward(torch.tensor(dy))
+    dx, dg, db = O.layernorm_bwd(dy, cache, g)
+    assert np.allclose(dx, xt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dg, gt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(db, bt.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_layernorm_invariants():
+    rng = np.random.default_rng(1)
+    x = rng.normal(size=(5, 64)) * rng.uniform(0.01, 10, size=(5, 1))
+    y, _ = O.layernorm_fwd(x, np.ones(64), np.zeros(64), 1e-5)
+    var = x.var(axis=1)
+    assert np.allclose(y.mean(axis=1), 0, atol=1e-12)
+    assert np.allclose(y.var(axis=1), var / (var + 1e-5), rtol=1e-10)
+
+
+def test_gelu_vs_torch_and_identities():
+    x = np.linspace(-8, 8, 1001)
+    xt = torch.tensor(x, requires_grad=True)
+    yt = F.gelu(xt, approximate="tanh")
+    assert np.allclose(O.gelu_tanh(x), yt.detach().numpy(), rtol=1e-13, atol=1e-15)
+    yt.sum().backward()
+    assert np.allclose(O.gelu_tanh_grad(x), xt.grad.numpy(), rtol=1e-12, atol=1e-14)
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert np.allclose(O.gelu_tanh(x) - O.gelu_tanh(-x), x, atol=1e-13)
+
+
+def test_relu2_rmsnorm_vs_torch():
+    rng = np.random.default_rng(2)
+    x = rng.normal(size=(4, 3, 16))
+    xt = torch.tensor(x, requires_grad=True)
+    yt = F.relu(xt) ** 2
+    assert np.array_equal(O.relu2(x), yt.detach().numpy())
+    yt.sum().backward()
+    assert np.allclose(O.relu2_grad(x), xt.grad.numpy())
+    xt = torch.tensor(x, requires_grad=True)
+    yt = F.rms_norm(xt, (16,), eps=1e-6)
+    y, r = O.rmsnorm_fwd(x, 1e-6)
+    assert np.allclose(y, yt.detach().numpy(), rtol=1e-12)
+    assert np.allclose(np.sqrt((y * y).mean(-1)), 1.0, atol=1e-5)
+    dy = rng.normal(size=x.shape)
+    yt.backward(torch.tensor(dy))
+    assert np.allclose(O.rmsnorm_bwd(dy, y, r), xt.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [0, 1, 3, 7])
+def test_attention_vs_torch_sdpa(window):
+    rng = np.random.default_rng(3)
+    B, H, T, hd = 2, 3, 11, 8
+    q, k, v = (rng.normal(size=(B, H, T, hd)) for _ in range(3))
+    o, p = O.attention_fwd(q, k, v, window)
+    qt, kt, vt = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    mask = torch.tensor(O.attention_mask(T, window)) if window else None
+    if window:
+        ot = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+    else:
+        ot = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    assert np.allclose(o, ot.detach().numpy(), rtol=1e-12, atol=1e-13)
+    assert np.allclose(p.sum(-1), 1.0, atol=1e-14)
+    assert np.all(p[..., ~O.attention_mask(T, window)] == 0)
+    do = rng.normal(size=o.shape)
+    ot.backward(torch.tensor(do))
+    dq, dk, dv = O.attention_bwd(do, q, k, v, p)
+    for a, t in ((dq, qt), (dk, kt), (dv, vt)):
+        assert np.allclose(a, t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [0, 4])
+def test_attention_zero_query_closed_form(window):
+    """Q = 0 gives uniform weights over the visible keys: O_i is the mean of
+    V over the last min(W, i+1) positions (all i+1 without a window)."""
+    rng = np.random.default_rng(4)
+    T, hd = 13, 6
+    v = rng.normal(size=(1, 1, T, hd))
+    k = rng.normal(size=(1, 1, T, hd))
+    o, _ = O.attention_fwd(np.zeros((1, 1, T, hd)), k, v, window)
+    for i in range(T):
+        lo = max(0, i - window + 1) if window else 0
+        assert np.allclose(o[0, 0, i], v[0, 0, lo:i + 1].mean(axis=0), atol=1e-14)
+
+
+def test_rope_properties():
+    rng = np.random.default_rng(5)
+    T, hd = 9, 16
+    cos, sin = O.rope_tables(T, hd, 10000.0)
+    q = rng.normal(size=(T, hd))
+    k = rng.normal(size=(T, hd))
+    qr, kr = O.rope_fwd(q, cos, sin), O.rope_fwd(k, cos, sin)
+    assert np.allclose(np.linalg.norm(qr, axis=-1), np.linalg.norm(q, axis=-1))
+    # scores depend on positions only through their difference: put the same
+    # vectors at every position and compare (i, j) with (i+s, j+s)
+    qs = O.rope_fwd(np.repeat(q[:1], T, 0), cos, sin)
+    ks = O.rope_fwd(np.repeat(k[:1], T, 0), cos, sin)
+    s = qs @ ks.T
+    assert np.allclose(s[5, 2], s[8, 5]) and np.allclose(s[3, 3], s[0, 0])
+    # position 0 is the identity; backward is the transpose of forward
+    assert np.allclose(qr[0], q[0])
+    dy = rng.normal(size=(T, hd))
+    assert np.allclose((O.rope_bwd(dy, cos, sin) * q).sum(), (dy * qr).sum())
+
+
+def test_cross_entropy_vs_torch_and_closed_form():
+    rng = np.random.default_rng(6)
+    M, V = 9, 17
+    z = rng.normal(size=(M, V)) * 4
+    y = rng.integers(0, V, M)
+    losses, dz = O.cross_entropy_fwd_bwd(z, y, 1.0)
+    zt = torch.tensor(z, requires_grad=True)
+    lt = F.cross_entropy(zt, torch.tensor(y))
+    assert abs(losses.mean() - lt.item()) < 1e-12
+    lt.backward()
+    assert np.allclose(dz, zt.grad.numpy(), rtol=1e-12, atol=1e-15)
+    assert np.allclose(dz.sum(axis=1), 0, atol=1e-15)
+    # uniform logits: loss = ln V and dz = (1/V - onehot)/M
+    losses, dz = O.cross_entropy_fwd_bwd(np.full((M, V), 2.5), y, 1.0)
+    assert np.allclose(losses, math.log(V))
+    ref = np.full((M, V), 1.0 / V)
+    ref[np.arange(M), y] -= 1
+    assert np.allclose(dz, ref / M)
+
+
+# ---------------------------------------------------------------- whole model
+
+def _torch_loss(params, tokens, targets, cfg, untie=False):
+    """The same model written with torch library ops, differentiated by autograd.
+    With untie=True the head uses its own copy of wte (reported as lm_head)."""
+    P = {k: torch.tensor(v, requires_grad=True) for k, v in params.items()}
+    if untie:
+        P["lm_head"] = torch.tensor(params["wte"], requires_grad=True)
+    tok = torch.tensor(tokens, dtype=torch.long)
+    B, T = tok.shape
+    d, H = cfg.n_embd, cfg.n_head
+    hd = d // H
+    x = F.embedding(tok, P["wte"])
+    if cfg.pos_encoding == "learned":
+        x = x + P["wpe"][:T]
+    else:
+        cos, sin = (torch.tensor(a) for a in O.rope_tables(T, hd, cfg.rope_base))
+
+    def rot(a):
+        a1, a2 = a[..., :hd // 2], a[..., hd // 2:]
+        return torch.cat([a1 * cos - a2 * sin, a1 * sin + a2 * cos], -1)
+
+    for l in range(cfg.n_layer):
+        p = f"h.{l}."
+        a = F.layer_norm(x, (d,), P[p + "ln_1.weight"], P[p + "ln_1.bias"], cfg.ln_eps)
+        qkv = F.linear(a, P[p + "attn.c_attn.weight"], P[p + "attn.c_attn.bias"])
+        q, k, v = (t.view(B, T, H, hd).transpose(1, 2) for t in qkv.split(d, -1))
+        if cfg.qk_rmsnorm:
+            q = F.rms_norm(q, (hd,), eps=cfg.qk_norm_eps)
+            k = F.rms_norm(k, (hd,), eps=cfg.qk_norm_eps)
+        if cfg.pos_encoding == "rope":
+            q, k = rot(q), rot(k)
+        w = cfg.window_even if l % 2 == 0 else cfg.window_odd
+        mask = torch.tril(torch.ones(T, T, dtype=torch.bool))
+        if w:
+            mask &= ~torch.tril(torch.ones(T, T, dtype=torch.bool), diagonal=-w)
+        o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+        o = o.transpose(1, 2).reshape(B, T, d)
+        x = x + F.linear(o, P[p + "attn.c_proj.weight"], P[p + "attn.c_proj.bias"])
+        a = F.layer_norm(x, (d,), P[p + "ln_2.weight"], P[p + "ln_2.bias"], cfg.ln_eps)
+        h = F.linear(a, P[p + "mlp.c_fc.weight"], P[p + "mlp.c_fc.bias"])
+        h = F.relu(h) ** 2 if cfg.mlp_act == "relu2" else F.gelu(h, approximate="tanh")
+        x = x + F.linear(h, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"])
+    x = F.layer_norm(x, (d,), P["ln_f.weight"], P["ln_f.bias"], cfg.ln_eps)
+    z = F.linear(x, P["lm_head"] if untie else P["wte"])
+    if cfg.logit_softcap:
+        z = cfg.logit_softcap * torch.tanh(z / cfg.logit_softcap)
+    loss = F.cross_entropy(z.reshape(B * T, -1), torch.tensor(targets, dtype=torch.long).reshape(-1))
+    loss.backward()
+    return loss.item(), {k: v.grad.numpy() for k, v in P.items()}
+
+
+def _perturbed_params(cfg, seed):
+    """Init params with every tensor perturbed, so that zero biases, unit
+    gains and zero-initialised projections do not hide terms."""
+    p = O.init_params(cfg, seed)
+    rng = np.random.default_rng(seed + 1000)
+    return {k: v + 0.05 * rng.normal(size=v.shape) for k, v in p.items()}
+
+
+@pytest.mark.parametrize("cfg", [TINY, TINY_SPEED], ids=["gpt2_tiny", "speedrun_tiny"])
+def test_model_forward_backward_vs_torch_autograd(cfg):
+    params = _perturbed_params(cfg, 11)
+    rng = np.random.default_rng(12)
+    B, T = 3, min(cfg.block_size, 24)
+    tok = rng.integers(0, cfg.padded_vocab_size, (B, T))
+    tgt = rng.integers(0, cfg.padded_vocab_size, (B, T))
+    loss, g, _ = O.forward_backward(params, tok, tgt, cfg)
+    lt, gt = _torch_loss(params, tok, tgt, cfg)
+    assert abs(loss - lt) < 1e-12 * max(1, abs(lt))
+    for k in params:
+        scale = max(np.abs(gt[k]).max(), 1e-30)
+        assert np.abs(g[k] - gt[k]).max() / scale < 1e-9, k
+
+
+@pytest.mark.parametrize("cfg", [TINY, TINY_SPEED], ids=["gpt2_tiny", "speedrun_tiny"])
+def test_finite_differences(cfg):
+    params = _perturbed_params(cfg, 21)
+    rng = np.random.default_rng(22)
+    B, T = 2, 12
+    tok = rng.integers(0, cfg.padded_vocab_size, (B, T))
+    tgt = rng.integers(0, cfg.padded_vocab_size, (B, T))
+    _, g, _ = O.forward_backward(params, tok, tgt, cfg, grad_scale=0.5)
+    h = 1e-5
+    names = list(params)
+    checked = 0
+    for _ in range(120):
+        n = names[rng.integers(len(names))]
+        idx = tuple(rng.integers(s) for s in params[n].shape)
+        if n == "wpe" and idx[0] >= T:
+            continue
+        old = params[n][idx]
+        params[n][idx] = old + h
+        lp, _, _ = O.forward_backward(params, tok, tgt, cfg, want_grads=False)
+        params[n][idx] = old - h
+        lm, _, _ = O.forward_backward(params, tok, tgt, cfg, want_grads=False)
+        params[n][idx] = old
+        fd = 0.5 * (lp - lm) / (2 * h)
+        assert abs(fd - g[n][idx]) <= 1e-6 * max(1e-3, abs(fd)) + 1e-9, (n, idx, fd, g[n][idx])
+        checked += 1
+    assert checked >= 100
+
+
+def test_causal_invariance():
+    cfg = TINY
+    params = _perturbed_params(cfg, 31)
+    rng = np.random.default_rng(32)
+    tok = rng.integers(0, 65, (2, 20))
+    tgt = rng.integers(0, 65, (2, 20))
+    _, _, e1 = O.forward_backward(params, tok, tgt, cfg, want_grads=False, return_logits=True)
+    i = 9
+    tok2 = tok.copy()
+    tok2[:, i + 1:] = rng.integers(0, 65, (2, 20 - i - 1))
+    _, _, e2 = O.forward_backward(params, tok2, tgt, cfg, want_grads=False, return_logits=True)
+    assert np.array_equal(e1["logits"][:, :i + 1], e2["logits"][:, :i + 1])
+    assert np.array_equal(e1["row_losses"][:, :i + 1], e2["row_losses"][:, :i + 1])
+    assert not np.array_equal(e1["logits"][:, i + 1:], e2["logits"][:, i + 1:])
+
+
+def test_initial_loss_near_ln_vocab():
+    """At init every token is about equally likely: loss ~ ln Vp (+ d*0.02^2/2
+    from the tied head's own-token logit). The lecture prints ln 50257 = 10.82
+    and an observed ~11."""
+    f = facts()["initial_loss_ln_vocab"]
+    assert abs(math.log(50257) - f["value"]) < 0.01
+    cfg = I.GPT2_124M.model.replace(n_layer=2)     # full width/vocab, two blocks
+    params = O.init_params(cfg, 3)
+    tok, tgt = next(I.batches(I.GPT2_124M, 1, 64))
+    loss, _, _ = O.forward_backward(params, tok, tgt, cfg, want_grads=False)
+    expect = math.log(50304) + 768 * 0.02 ** 2 / 2
+    assert abs(loss - expect) < 0.25
+    assert abs(loss - f["observed"]) < 0.5
+    for w, lo in ((I.TINY_FP32, 4.19), (I.CHAR_BF16, 4.25)):
+        p = O.init_params(w.model, w.init_seed)
+        tok, tgt = next(I.batches(w, 2, 32))
+        loss, _, _ = O.forward_backward(p, tok, tgt, w.model, want_grads=False)
+        assert abs(loss - lo) < 0.25
+
+
+def test_zero_init_closed_form():
+    """With zero-initialised output projections every block adds exactly zero,
+    so the logits are softcap(LN_f(wte[tok]) wte^T), whatever attention does."""
+    cfg = TINY_SPEED.replace(zero_init_proj=True)
+    p = O.init_params(cfg, 41)
+    rng = np.random.default_rng(42)
+    tok = rng.integers(0, cfg.padded_vocab_size, (2, 10))
+    _, _, e = O.forward_backward(p, tok, tok, cfg, want_grads=False, return_logits=True)
+    e_rows = p["wte"][tok]
+    mu = e_rows.mean(-1, keepdims=True)
+    sd = np.sqrt(e_rows.var(-1, keepdims=True) + cfg.ln_eps)
+    xf = (e_rows - mu) / sd
+    z = 3.0 * np.tanh((xf @ p["wte"].T) / 3.0)
+    assert np.allclose(e["logits"], z, rtol=1e-12, atol=1e-12)
+
+
+def test_accumulation_equivalence():
+    """k micro-steps at scale 1/k give the gradient of one batch of k*B rows
+    (lecture, gradient accumulation section)."""
+    cfg = TINY
+    params = _perturbed_params(cfg, 51)
+    rng = np.random.default_rng(52)
+    tok = rng.integers(0, 65, (4, 16))
+    tgt = rng.integers(0, 65, (4, 16))
+    l_all, g_all, _ = O.forward_backward(params, tok, tgt, cfg)
+    acc = O.zeros_like_params(params)
+    ls = 0
+    for i in range(4):
+        l, g, _ = O.forward_backward(params, tok[i:i + 1], tgt[i:i + 1], cfg, grad_scale=0.25)
+        ls += l / 4
+        for k in acc:
+            acc[k] += g[k]
+    assert abs(ls - l_all) < 1e-12
+    for k in acc:
+        assert np.allclose(acc[k], g_all[k], rtol=1e-9, atol=1e-14)
+
+
+def test_tied_gradient_is_sum_of_both_uses():
+    """Untie the head in the torch model: the oracle's tied wte gradient must be
+    the head part plus the lookup part (lecture, tied weights). With all
+    tokens equal to one id, that id's lookup part is the column sum of the
+    input gradient, which also equals the sum over t of the wpe gradient."""
+    cfg = TINY
+    params = _perturbed_params(cfg, 61)
+    rng = np.random.default_rng(62)
+    for tok in (np.full((2, 8), 7), rng.integers(0, 65, (2, 8))):
+        tgt = rng.integers(0, 65, (2, 8))
+        _, g, _ = O.forward_backward(params, tok, tgt, cfg)
+        _, gt = _torch_loss(params, tok, tgt, cfg, untie=True)
+        assert np.allclose(g["wte"], gt["wte"] + gt["lm_head"], rtol=1e-9, atol=1e-14)
+        if np.all(tok == 7):
+            lookup = gt["wte"]
+            assert np.allclose(lookup[7], g["wpe"][:8].sum(axis=0), rtol=1e-9, atol=1e-14)
+            others = np.delete(np.arange(65), 7)
+            assert np.all(lookup[others] == 0)
+
+
+# ---------------------------------------------------------------- clip / AdamW / LR
+
+def test_clip_closed_form_and_torch():
+    for c, n in ((0.3, 100), (0.01, 50), (-0.2, 64)):
+        g = {"a": np.full((n // 2, 2), c), "b": np.full(n - 2 * (n // 2), c)}
+        norm = O.grad_norm(g)
+        assert abs(norm - abs(c) * math.sqrt(n)) < 1e-12
+        coef = O.clip_coefficient(norm, 1.0)
+        assert coef == (1.0 / (norm + 1e-6) if norm > 1 else 1.0)
+    rng = np.random.default_rng(71)
+    gs = [rng.normal(size=(5, 3)) * 2, rng.normal(size=7)]
+    ts = [torch.zeros(a.shape, dtype=torch.float64, requires_grad=True) for a in gs]
+    for t, a in zip(ts, gs):
+        t.grad = torch.tensor(a)
+    tn = torch.nn.utils.clip_grad_norm_(ts, 1.0)
+    norm = O.grad_norm({"0": gs[0], "1": gs[1]})
+    assert abs(norm - tn.item()) < 1e-12
+    coef = O.clip_coefficient(norm, 1.0)
+    for t, a in zip(ts, gs):
+        assert np.allclose(t.grad.numpy(), a * coef, rtol=1e-14)
+
+
+def test_adamw_closed_forms():
+    cfg = TINY
+    lr, wd, eps = 6e-4, 0.1, 1e-8
+    p0 = {"w": np.array([[0.5, -0.25], [1.0, 0.0]]), "b": np.array([0.3, -0.7])}
+    g1 = {"w": np.array([[0.2, -1e-3], [3.0, 1e-9]]), "b": np.array([-0.5, 2.0])}
+    g2 = {"w": np.array([[-0.1, 0.4], [1.0, -2.0]]), "b": np.array([0.25, 0.0])}
+    flags = {"w": True, "b": False}
+    z = O.zeros_like_params(p0)
+    p1, m1, v1 = O.adamw_update(p0, g1, z, z, lr, 1, cfg, flags)
+    for k in p0:
+        dec = (1 - lr * wd) if flags[k] else 1.0
+        assert np.allclose(p1[k], p0[k] * dec - lr * g1[k] / (np.abs(g1[k]) + eps), rtol=1e-14, atol=1e-18)
+    p2, _, _ = O.adamw_update(p1, g2, m1, v1, lr, 2, cfg, flags)
+    b1, b2 = 0.9, 0.95
+    for k in p0:
+        dec = (1 - lr * wd) if flags[k] else 1.0
+        m = (1 - b1) * (b1 * g1[k] + g2[k])
+        v = (1 - b2) * (b2 * g1[k] ** 2 + g2[k] ** 2)
+        mh, vh = m / (1 - b1 ** 2), v / (1 - b2 ** 2)
+        assert np.allclose(p2[k], p1[k] * dec - lr * mh / (np.sqrt(vh) + eps), rtol=1e-13, atol=1e-18)
+
+
+def test_adamw_vs_torch():
+    rng = np.random.default_rng(81)
+    cfg = TINY
+    p = {"w": rng.normal(size=(4, 3)), "b": rng.normal(size=5)}
+    flags = {"w": True, "b": False}
+    tw = torch.tensor(p["w"], requires_grad=True)
+    tb = torch.tensor(p["b"], requires_grad=True)
+    opt = torch.optim.AdamW([{"params": [tw], "weight_decay": 0.1}, {"params": [tb], "weight_decay": 0.0}],
+                            lr=6e-4, betas=(0.9, 0.95), eps=1e-8, foreach=False)
+    m = O.zeros_like_params(p)
+    v = O.zeros_like_params(p)
+    for step in range(1, 5):
+        g = {"w": rng.normal(size=(4, 3)), "b": rng.normal(size=5) * 0.01}
+        tw.grad = torch.tensor(g["w"])
+        tb.grad = torch.tensor(g["b"])
+        opt.step()
+        p, m, v = O.adamw_update(p, g, m, v, 6e-4, step, cfg, flags)
+        assert np.allclose(p["w"], tw.detach().numpy(), rtol=1e-13, atol=1e-16)
+        assert np.allclose(p["b"], tb.detach().numpy(), rtol=1e-13, atol=1e-16)
+
+
+def test_lr_schedule_against_pages():
+    f = facts()["lr_schedule"]
+    kw = dict(warmup_steps=f["warmup_steps"], max_steps=f["max_steps"],
+              max_lr=f["max_lr"], min_lr=f["max_lr"] * f["min_lr_ratio"])
+    assert abs(O.get_lr(0, **kw) - 6e-4 / 715) < 1e-18
+    assert abs(O.get_lr(714, **kw) - 6e-4) < 1e-18
+    assert abs(O.get_lr(715, **kw) - 6e-4) < 1e-18
+    assert abs(O.get_lr(1000, **kw) - 5.9967893984e-4) < 1e-13
+    assert O.get_lr(19073, **kw) == pytest.approx(6e-5, rel=1e-12)
+    assert O.get_lr(19074, **kw) == kw["min_lr"] and abs(kw["min_lr"] - 6e-5) < 1e-18
+    assert abs(I.GPT2_124M_ACCUM.lr - O.get_lr(1000)) < 1e-13
+
+
+def test_overfit_one_batch():
+    """Repeating one batch drives the loss toward zero (lecture: overfit a
+    single batch first)."""
+    cfg = TINY
+    params = O.init_params(cfg, 91)
+    m = O.zeros_like_params(params)
+    v = O.zeros_like_params(params)
+    rng = np.random.default_rng(92)
+    tok = rng.integers(0, 65, (2, 16))
+    tgt = rng.integers(0, 65, (2, 16))
+    first = None
+    for step in range(1, 121):
+        loss, _, _, params, m, v = O.train_step(params, m, v, [(tok, tgt)], cfg, 3e-3, step)
+        first = loss if first is None else first
+    assert first > 4.0 and loss < 0.2 * first

@@ -1,0 +1,222 @@
+/*
+ * gpt.h -- C ABI of the GPT-2 training-step library for AMD Instinct MI355X
+ * (gfx950). One handle holds one model (parameters, gradients, AdamW moments,
+ * activations) inside a caller-provided device workspace and runs its kernels
+ * on a caller-provided HIP stream.
+ *
+ * The calls reproduce the user-level operations of the training loop the
+ * source pages describe:
+ *   model(x, targets=y) -> loss, loss.backward()   -> gpt_forward_backward
+ *   clip_grad_norm_(params, 1.0); optimizer.step(); zero_grad()
+ *                                                  -> gpt_clip_and_adamw
+ *   get_lr(it)                                     -> gpt_lr_schedule
+ *   model.parameters() / .grad                     -> gpt_get_param / gpt_get_grad
+ * ("NanoGPT Speedrun baseline" (cruxr.ai), "Configuración del Entrenamiento";
+ *  "Zero to Hero, lecture 9: reproducing GPT-2 (124M)" (ai.flicky.cc),
+ *  "Оптимизатор, клиппинг, расписание" and "Накопление градиентов").
+ *
+ * Conventions
+ *   - Every call returns a gpt_status; GPT_OK is 0, errors are negative.
+ *   - Device pointers are plain HIP device addresses; "stream" arguments are
+ *     hipStream_t values passed as void*.
+ *   - The caller owns every buffer it passes; the library never frees them.
+ *   - Calls on one handle are not thread-safe. Calls are asynchronous on the
+ *     handle's stream unless stated otherwise.
+ *   - Integer token ids are int32, row-major [B, T].
+ */
+#ifndef GPT_MI355X_H
+#define GPT_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gpt_status {
+    GPT_OK = 0,
+    GPT_ERR_INVALID_ARGUMENT = -1,   /* null pointer, shape out of range, bad index */
+    GPT_ERR_WORKSPACE_TOO_SMALL = -2,
+    GPT_ERR_UNSUPPORTED = -3,        /* configuration the kernels do not implement */
+    GPT_ERR_DEVICE = -4,             /* a HIP runtime call failed */
+    GPT_ERR_TOKEN_RANGE = -5,        /* a token or target id outside [0, padded_vocab) */
+    GPT_ERR_NONFINITE = -6           /* non-finite gradient norm: update skipped */
+} gpt_status;
+
+enum { GPT_PREC_FP32 = 0, GPT_PREC_BF16 = 1 };
+enum { GPT_POS_LEARNED = 0, GPT_POS_ROPE = 1 };
+enum { GPT_ACT_GELU_TANH = 0, GPT_ACT_RELU2 = 1 };
+
+/*
+ * Model and optimiser configuration. Shape fields follow the lecture's
+ * GPTConfig (block_size, vocab_size, n_layer, n_head, n_embd; "Раздел 1 /
+ * Архитектура"); mlp_hidden is the MLP width (4 n_embd for GPT-2);
+ * padded_vocab_size >= vocab_size is the number of wte rows and lm_head
+ * columns (50304 for GPT-2, "Раздел 2. Сделаем быстро": a vocabulary size
+ * divisible by 128; the extra rows are ordinary, trainable classes).
+ * max_batch bounds B in gpt_forward_backward and sizes the activations.
+ *
+ * The speedrun-block fields implement the Modded-NanoGPT README's technique
+ * list: rotary positions instead of wpe (pos_encoding), parameter-free RMS
+ * normalisation of q and k per head (qk_rmsnorm), ReLU^2 MLP (mlp_act),
+ * sliding-window causal attention with window_even/window_odd keys on
+ * even/odd layers (0 = plain causal), a tanh logit softcap
+ * (logit_softcap * tanh(z / logit_softcap); 0 = off) and zero-initialised
+ * output projections (zero_init_proj).
+ */
+typedef struct gpt_config {
+    int32_t n_layer;
+    int32_t n_head;
+    int32_t n_embd;
+    int32_t mlp_hidden;
+    int32_t block_size;
+    int32_t vocab_size;
+    int32_t padded_vocab_size;
+    int32_t max_batch;
+    int32_t precision;        /* GPT_PREC_FP32: all-fp32 kernels;
+                                 GPT_PREC_BF16: bf16 matmul operands and stored
+                                 activations, fp32 accumulation, fp32 residual
+                                 stream, norms, softmax, loss, grads, master weights */
+    int32_t pos_encoding;     /* GPT_POS_LEARNED or GPT_POS_ROPE */
+    int32_t qk_rmsnorm;       /* 0 or 1 */
+    int32_t mlp_act;          /* GPT_ACT_GELU_TANH or GPT_ACT_RELU2 */
+    int32_t window_even;      /* keys visible to query i: j <= i and i - j < W (W > 0) */
+    int32_t window_odd;
+    int32_t zero_init_proj;   /* 0 or 1 */
+    int32_t reserved0;
+    float ln_eps;             /* LayerNorm epsilon, biased variance (1e-5) */
+    float qk_norm_eps;        /* 1e-6 */
+    float rope_base;          /* 10000 */
+    float logit_softcap;      /* 0 = off */
+    float beta1;              /* 0.9  */
+    float beta2;              /* 0.95 */
+    float adam_eps;           /* 1e-8 */
+    float weight_decay;       /* 0.1, applied to every 2-D tensor */
+    float max_grad_norm;      /* 1.0 */
+    int32_t reserved1;
+    double init_std;          /* 0.02 */
+} gpt_config;
+
+typedef struct gpt_handle gpt_handle;
+
+/* Fill *cfg with GPT-2 124M: 12 layers, 12 heads, 768 wide, MLP 3072,
+ * block 1024, vocab 50257 padded to 50304, max_batch 16, bf16, AdamW
+ * 0.9/0.95/1e-8, decay 0.1, clip 1.0, init std 0.02. Pure host. */
+gpt_status gpt_config_default(gpt_config* cfg);
+
+/* Bytes of device workspace a handle with this configuration needs
+ * (parameters, gradients, AdamW moments, bf16 weight copies and activations
+ * for max_batch x block_size tokens). Pure host; validates cfg.
+ * Errors: INVALID_ARGUMENT (null, non-positive sizes, n_embd not divisible
+ * by n_head, padded_vocab_size < vocab_size), UNSUPPORTED (head dim not in
+ * {16, 32, 64, 128}, n_embd % 8 != 0, mlp_hidden % 8 != 0,
+ * max_batch * block_size > 32768, padded_vocab_size > 131071,
+ * n_embd > 2048). */
+gpt_status gpt_workspace_bytes(const gpt_config* cfg, size_t* bytes);
+
+/* Create a handle inside d_workspace (device memory of at least
+ * gpt_workspace_bytes bytes, 256-byte aligned, owned by the caller and kept
+ * alive until gpt_destroy). Parameters are initialised on `stream` from
+ * `seed`: every weight is N(0, init_std) except the attention and MLP output
+ * projections, N(0, init_std / sqrt(2 n_layer)) (zero with zero_init_proj);
+ * biases 0, LayerNorm gains 1 ("Связанные веса и инициализация"). The normal
+ * draws come from Philox4x64-10 (Salmon et al., SC'11) keyed by
+ * (seed, tensor index) with counter (element / 4), turned into normals by the
+ * Box-Muller transform in double precision, then rounded to fp32. AdamW
+ * moments start at 0; gradients start cleared. Asynchronous.
+ * Errors: INVALID_ARGUMENT, WORKSPACE_TOO_SMALL, UNSUPPORTED (as above, or
+ * a device that is not gfx950), DEVICE. */
+gpt_status gpt_create(const gpt_config* cfg, uint64_t seed, void* d_workspace,
+                      size_t workspace_bytes, void* stream, gpt_handle** out);
+
+/* Release host-side state. The workspace stays the caller's. */
+gpt_status gpt_destroy(gpt_handle* h);
+
+/* Run later calls on another stream (for example torch's current stream). */
+gpt_status gpt_set_stream(gpt_handle* h, void* stream);
+
+/* One micro-step: forward pass, mean cross-entropy over the B*T positions
+ * and all padded_vocab_size classes, backward pass. Gradients accumulate
+ * grad_scale * d(mean loss)/d(param); the first call after gpt_create or
+ * gpt_clip_and_adamw starts from zero (the training loop's zero_grad).
+ * grad_scale = 1/k over k calls reproduces gradient accumulation
+ * ("Накопление градиентов"). d_tokens and d_targets are device int32 [B, T]
+ * read in stream order. If h_loss is non-null the call waits for the stream
+ * and stores the unscaled mean loss of this micro-step.
+ * Errors: INVALID_ARGUMENT (null handle or buffers, B < 1, B > max_batch,
+ * T < 1, T > block_size -- the pages' "longer than block_size" failure),
+ * TOKEN_RANGE (an id outside [0, padded_vocab_size); detected on the device,
+ * reported by the first call that waits for the stream; the offending
+ * positions contribute zero), DEVICE. */
+gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* d_tokens,
+                                const int32_t* d_targets, int32_t B, int32_t T,
+                                float grad_scale, float* h_loss);
+
+/* Mean of the micro-step losses since the last update (the loop's
+ * loss_accum). Waits for the stream. */
+gpt_status gpt_loss_accum(gpt_handle* h, float* h_mean_loss);
+
+/* Global gradient clipping then AdamW, in two device passes:
+ *   n = sqrt(sum of g^2 over every parameter, the tied wte once);
+ *   c = min(1, max_grad_norm / (n + 1e-6));  g <- c g;
+ *   p <- p (1 - lr weight_decay) for 2-D tensors;
+ *   m <- beta1 m + (1 - beta1) g;  v <- beta2 v + (1 - beta2) g^2;
+ *   p <- p - lr (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + adam_eps).
+ * step >= 1 is AdamW's bias-correction count. Gradients are marked for
+ * clearing by the next forward_backward. If h_grad_norm is non-null the
+ * call waits and returns the pre-clip norm n.
+ * Errors: INVALID_ARGUMENT (step < 1, lr < 0 or not finite), NONFINITE
+ * (n is not finite: parameters and moments are left unchanged; reported
+ * when the call waits, i.e. with h_grad_norm non-null), DEVICE. */
+gpt_status gpt_clip_and_adamw(gpt_handle* h, float lr, int32_t step, float* h_grad_norm);
+
+/* Parameter table: tensor names follow the lecture's Hugging-Face names
+ * ("wte", "wpe", "h.{l}.ln_1.weight", "h.{l}.attn.c_attn.weight", ...,
+ * "ln_f.bias"); linear weights are [out, in]; the tied wte appears once.
+ * decay is 1 for tensors AdamW decays (every 2-D tensor). Pure host. */
+gpt_status gpt_num_tensors(const gpt_handle* h, int32_t* n);
+gpt_status gpt_tensor_info(const gpt_handle* h, int32_t idx, const char** name,
+                           int32_t* ndim, int64_t shape[2], int32_t* decay);
+
+/* Copy a tensor's fp32 values out of / into the model, in the canonical
+ * [out, in] row-major layout. count must equal the tensor's element count;
+ * buf is a device pointer if buf_on_device, else host memory. These calls
+ * wait for the stream. set_param also refreshes the bf16 weight copy. */
+gpt_status gpt_get_param(gpt_handle* h, int32_t idx, float* buf, int64_t count, int32_t buf_on_device);
+gpt_status gpt_set_param(gpt_handle* h, int32_t idx, const float* buf, int64_t count, int32_t buf_on_device);
+gpt_status gpt_get_grad(gpt_handle* h, int32_t idx, float* buf, int64_t count, int32_t buf_on_device);
+gpt_status gpt_set_grad(gpt_handle* h, int32_t idx, const float* buf, int64_t count, int32_t buf_on_device);
+/* AdamW first and second moments of one tensor (either pointer may be null). */
+gpt_status gpt_get_opt_state(gpt_handle* h, int32_t idx, float* m, float* v, int64_t count, int32_t buf_on_device);
+gpt_status gpt_set_opt_state(gpt_handle* h, int32_t idx, const float* m, const float* v, int64_t count, int32_t buf_on_device);
+
+/* Per-position losses of the last forward_backward, fp32 [B, T] (count = B*T).
+ * Waits for the stream. */
+gpt_status gpt_get_row_losses(gpt_handle* h, float* buf, int64_t count, int32_t buf_on_device);
+
+/* The lecture's learning-rate schedule ("Оптимизатор, клиппинг,
+ * расписание"): max_lr (it+1)/warmup for it < warmup; min_lr for
+ * it > max_steps; otherwise min_lr + 0.5 (1 + cos(pi r)) (max_lr - min_lr)
+ * with r = (it - warmup)/(max_steps - warmup). Pure host. */
+double gpt_lr_schedule(int32_t it, int32_t warmup_steps, int32_t max_steps, double max_lr, double min_lr);
+
+/* Human-readable text for a status, and the last error message on a handle
+ * (empty string when none). */
+const char* gpt_status_string(gpt_status s);
+const char* gpt_last_error(const gpt_handle* h);
+
+/* Kernel timing. When enabled, every launch of the library's kernels is
+ * bracketed by HIP events on the handle's stream; per kernel class the
+ * library accumulates the summed event time, the launch count and the
+ * algorithmic FLOPs and HBM bytes of those launches. */
+gpt_status gpt_set_kernel_timing(gpt_handle* h, int32_t enable);
+gpt_status gpt_reset_kernel_timing(gpt_handle* h);
+gpt_status gpt_num_kernel_classes(int32_t* n);
+gpt_status gpt_kernel_timing(gpt_handle* h, int32_t cls, const char** name, double* total_ms,
+                             int64_t* launches, double* flops, double* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT_MI355X_H */

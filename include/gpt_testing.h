@@ -1,0 +1,74 @@
+/*
+ * gpt_testing.h -- test-only entry points of the GPT-2 training-step library.
+ *
+ * Each call launches one kernel family of the training step on raw device
+ * buffers so that tests can check it against the CPU reference in isolation.
+ * All pointers are device addresses owned by the caller; calls are
+ * asynchronous on `stream` (a hipStream_t passed as void*) and return
+ * GPT_ERR_INVALID_ARGUMENT for shapes the kernels do not accept,
+ * GPT_ERR_DEVICE when the launch fails. "bf16" flags select bf16 storage for
+ * the tensors documented as "act" (fp32 otherwise).
+ */
+#ifndef GPT_MI355X_TESTING_H
+#define GPT_MI355X_TESTING_H
+
+#include "gpt.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* C[M, N] = epilogue(sum_k A(m,k) B(k,n)) where
+ *   A(m,k) = a_kc ? A[m*lda + k] : A[k*lda + m],
+ *   B(k,n) = b_kc ? B[n*ldb + k] : B[k*ldb + n]   (A, B bf16 if in_bf16 else fp32);
+ * epi: 0 store (C act or fp32 by c_bf16), 1 + bias[n], 2 + bias then C2 = act(C)
+ * (act 0 = GELU tanh approximation, 1 = ReLU^2), 3 C = resid + AB + bias (fp32),
+ * 4 C = AB * act'(aux) (aux act), 5 C += AB (fp32). The linear-layer products of
+ * the lecture's GPT ("Раздел 1 / Архитектура") in both passes reduce to these.
+ * splitk_scratch (optional) holds split-K partial sums of splitk_floats floats. */
+gpt_status gptk_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int32_t a_kc, const void* B,
+                     int64_t ldb, int32_t b_kc, void* C, int64_t ldc, int32_t in_bf16, int32_t c_bf16, int32_t epi,
+                     int32_t act, const float* bias, const float* resid, const void* aux, void* C2,
+                     float* splitk_scratch, int64_t splitk_floats, void* stream);
+
+/* Causal (optionally windowed: i - j < window) softmax(Q K^T / sqrt(hd)) V per
+ * (batch, head), heads interleaved in the columns of row-major [B*T, *]
+ * buffers ("El Mecanismo de Atención"). Forward writes o and lse [B, H, T];
+ * backward also computes D = rowsum(dO o O) into D [B, H, T] and writes dq,
+ * dk, dv (row stride ldd). */
+gpt_status gptk_attention(int32_t backward, int32_t B, int32_t T, int32_t H, int32_t hd, int32_t window,
+                          const void* q, const void* k, const void* v, int64_t ldq, int64_t ldk, int64_t ldv,
+                          void* o, int64_t ldo, float* lse, const void* dO, int64_t lddo, float* D, void* dq, void* dk,
+                          void* dv, int64_t ldd, int32_t bf16, void* stream);
+
+/* LayerNorm over rows of width d with biased variance. Forward: y (act),
+ * mean, rstd. Backward: dres = (overwrite ? 0 : dres) + dx, optional bf16
+ * copy dres_lp, dg += sum dy xhat, db += sum dy; partial holds
+ * gptk_layernorm_partial_floats(M, d) floats. */
+gpt_status gptk_layernorm(int32_t backward, int32_t M, int32_t d, float eps, const float* x, const float* g,
+                          const float* b, void* y, float* mean, float* rstd, const float* dy, float* dres,
+                          void* dres_lp, int32_t overwrite, float* dg, float* db, float* partial, int32_t bf16,
+                          void* stream);
+int64_t gptk_layernorm_partial_floats(int32_t M, int32_t d);
+
+/* Fused softmax cross-entropy on logits z [M, Vp] (act, overwritten in place
+ * by the gradient (softmax - onehot) * gscale); optional tanh softcap. */
+gpt_status gptk_cross_entropy(int32_t M, int32_t Vp, void* z, const int32_t* y, float* row_loss, float gscale,
+                              float cap, int32_t* err, int32_t bf16, void* stream);
+
+/* dwte[tok[m]] += dx[m] and dwpe[t] += sum_b dx[b, t] (dwpe may be null),
+ * deterministic and atomic-free; scratch holds gptk_embed_bwd_scratch_bytes. */
+gpt_status gptk_embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, int32_t B, int32_t T,
+                          int32_t d, int32_t Vp, void* scratch, void* stream);
+int64_t gptk_embed_bwd_scratch_bytes(int32_t M, int32_t d);
+
+/* out[n] += sum_m Y[m*ld + n] (bias gradients); partial holds
+ * gptk_colsum_partial_floats(M, N) floats. */
+gpt_status gptk_colsum(int32_t M, int32_t N, const void* Y, int64_t ld, int32_t bf16, float* out, float* partial,
+                       void* stream);
+int64_t gptk_colsum_partial_floats(int32_t M, int32_t N);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT_MI355X_TESTING_H */

@@ -1,0 +1,78 @@
+// Shared device helpers for the gfx950 kernels of the GPT-2 training step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+#define GPT_DEV __device__ __forceinline__
+
+// ---------------------------------------------------------------- conversions
+
+GPT_DEV float to_f32(float x) { return x; }
+GPT_DEV float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> GPT_DEV T from_f32(float x);
+template <> GPT_DEV float from_f32<float>(float x) { return x; }
+template <> GPT_DEV bf16 from_f32<bf16>(float x) { return (bf16)x; }   // round to nearest even
+
+// Four consecutive elements as fp32 (address must be aligned to 4 elements).
+GPT_DEV float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+GPT_DEV float4 load4(const bf16* p) {
+    bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+GPT_DEV void store4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+GPT_DEV void store4(bf16* p, float4 v) {
+    bf16x4 o;
+    o[0] = (bf16)v.x; o[1] = (bf16)v.y; o[2] = (bf16)v.z; o[3] = (bf16)v.w;
+    *reinterpret_cast<bf16x4*>(p) = o;
+}
+
+// ---------------------------------------------------------------- reductions
+
+GPT_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+GPT_DEV float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+GPT_DEV double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------- activations
+
+// GELU, tanh approximation: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
+GPT_DEV float gelu_tanh_f(float x) {
+    const float c = 0.7978845608028654f;
+    float u = c * (x + 0.044715f * x * x * x);
+    return 0.5f * x * (1.0f + tanhf(u));
+}
+GPT_DEV float gelu_tanh_grad_f(float x) {
+    const float c = 0.7978845608028654f;
+    float u = c * (x + 0.044715f * x * x * x);
+    float t = tanhf(u);
+    return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * c * (1.0f + 3.0f * 0.044715f * x * x);
+}
+GPT_DEV float relu2_f(float x) { float r = fmaxf(x, 0.0f); return r * r; }
+GPT_DEV float relu2_grad_f(float x) { return 2.0f * fmaxf(x, 0.0f); }
+
+enum ActKind { ACT_GELU = 0, ACT_RELU2 = 1 };
+
+template <int ACT> GPT_DEV float act_f(float x) { return ACT == ACT_RELU2 ? relu2_f(x) : gelu_tanh_f(x); }
+template <int ACT> GPT_DEV float act_grad_f(float x) { return ACT == ACT_RELU2 ? relu2_grad_f(x) : gelu_tanh_grad_f(x); }
+
+static inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }

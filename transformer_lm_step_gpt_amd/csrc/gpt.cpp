@@ -1,0 +1,950 @@
+// Host engine and C ABI of the GPT-2 training-step library (see include/gpt.h).
+//
+// Owns: the parameter table, the carving of the caller's workspace, the
+// per-micro-step launch schedule (forward, fused cross-entropy, backward),
+// gradient accumulation with a lazy zero, the clip + AdamW update, error
+// state and optional per-kernel-class event timing.
+//
+// Training step: "NanoGPT Speedrun baseline" (cruxr.ai), "Configuración del
+// Entrenamiento"; "Zero to Hero, lecture 9: reproducing GPT-2 (124M)"
+// (ai.flicky.cc), "Раздел 1 / Архитектура", "Связанные веса и
+// инициализация", "Оптимизатор, клиппинг, расписание", "Накопление
+// градиентов".
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt.h"
+#include "../../include/gpt_testing.h"
+#include "kernels.h"
+
+namespace {
+
+// ---------------------------------------------------------------- parameter table
+
+struct TensorInfo {
+    std::string name;
+    int ndim;
+    int64_t shape[2];
+    int64_t numel;
+    int decay;
+    int init;        // 0 normal, 1 proj, 2 zero, 3 one
+    int64_t offset;  // element offset in the flat fp32 buffers
+};
+
+enum { INIT_NORMAL = 0, INIT_PROJ = 1, INIT_ZERO = 2, INIT_ONE = 3 };
+
+struct LayerIdx {   // table indices of one block's tensors
+    int ln1_w, ln1_b, attn_w, attn_b, proj_w, proj_b, ln2_w, ln2_b, fc_w, fc_b, mp_w, mp_b;
+};
+
+struct Table {
+    std::vector<TensorInfo> t;
+    int wte = -1, wpe = -1, lnf_w = -1, lnf_b = -1;
+    std::vector<LayerIdx> layers;
+    int64_t n_total = 0, n_decay = 0;
+};
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+Table build_table(const gpt_config& c) {
+    Table tb;
+    auto add = [&](const std::string& n, int64_t r, int64_t cols, int init) {
+        TensorInfo ti;
+        ti.name = n;
+        ti.ndim = cols > 0 ? 2 : 1;
+        ti.shape[0] = r;
+        ti.shape[1] = cols > 0 ? cols : 0;
+        ti.numel = cols > 0 ? r * cols : r;
+        ti.decay = cols > 0 ? 1 : 0;
+        ti.init = init;
+        ti.offset = 0;
+        tb.t.push_back(ti);
+        return (int)tb.t.size() - 1;
+    };
+    const int64_t d = c.n_embd, F = c.mlp_hidden;
+    tb.wte = add("wte", c.padded_vocab_size, d, INIT_NORMAL);
+    if (c.pos_encoding == GPT_POS_LEARNED) tb.wpe = add("wpe", c.block_size, d, INIT_NORMAL);
+    for (int l = 0; l < c.n_layer; ++l) {
+        std::string p = "h." + std::to_string(l) + ".";
+        LayerIdx li;
+        li.ln1_w = add(p + "ln_1.weight", d, 0, INIT_ONE);
+        li.ln1_b = add(p + "ln_1.bias", d, 0, INIT_ZERO);
+        li.attn_w = add(p + "attn.c_attn.weight", 3 * d, d, INIT_NORMAL);
+        li.attn_b = add(p + "attn.c_attn.bias", 3 * d, 0, INIT_ZERO);
+        li.proj_w = add(p + "attn.c_proj.weight", d, d, INIT_PROJ);
+        li.proj_b = add(p + "attn.c_proj.bias", d, 0, INIT_ZERO);
+        li.ln2_w = add(p + "ln_2.weight", d, 0, INIT_ONE);
+        li.ln2_b = add(p + "ln_2.bias", d, 0, INIT_ZERO);
+        li.fc_w = add(p + "mlp.c_fc.weight", F, d, INIT_NORMAL);
+        li.fc_b = add(p + "mlp.c_fc.bias", F, 0, INIT_ZERO);
+        li.mp_w = add(p + "mlp.c_proj.weight", d, F, INIT_PROJ);
+        li.mp_b = add(p + "mlp.c_proj.bias", d, 0, INIT_ZERO);
+        tb.layers.push_back(li);
+    }
+    tb.lnf_w = add("ln_f.weight", d, 0, INIT_ONE);
+    tb.lnf_b = add("ln_f.bias", d, 0, INIT_ZERO);
+    // flat layout: every decayed (2-D) tensor first, then the rest; 64-element alignment
+    int64_t off = 0;
+    for (auto& ti : tb.t)
+        if (ti.decay) { ti.offset = off; off = align_up(off + ti.numel, 64); }
+    tb.n_decay = off;
+    for (auto& ti : tb.t)
+        if (!ti.decay) { ti.offset = off; off = align_up(off + ti.numel, 64); }
+    tb.n_total = off;
+    return tb;
+}
+
+// ---------------------------------------------------------------- workspace layout
+
+struct Ws {
+    float *params = nullptr, *grads = nullptr, *m = nullptr, *v = nullptr;
+    void* wbf = nullptr;
+    std::vector<float*> x_in, x_mid;
+    float* x_fin = nullptr;
+    float *ln_mean = nullptr, *ln_rstd = nullptr;
+    std::vector<void*> ln1, ln2, qkv, qk, att, hpre, hact;
+    std::vector<float*> lse;
+    void* lnf = nullptr;
+    void* logits = nullptr;
+    float* row_loss = nullptr;
+    float* dres = nullptr;
+    void* dres_lp = nullptr;
+    float* dln = nullptr;
+    void *dh = nullptr, *dO = nullptr, *dqkv = nullptr;
+    float* attD = nullptr;
+    float *ln_partial = nullptr, *cs_partial = nullptr;
+    double* gn_partial = nullptr;
+    void* emb_scratch = nullptr;
+    float* splitk = nullptr;
+    size_t splitk_floats = 0;
+    float *rope_cos = nullptr, *rope_sin = nullptr;
+    int32_t* err = nullptr;
+    float *loss_last = nullptr, *loss_sum = nullptr, *gnorm = nullptr, *coef = nullptr;
+    int32_t* nonfinite = nullptr;
+    size_t bytes = 0;
+};
+
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base((char*)b) {}
+    void* take(size_t bytes) {
+        void* r = base ? base + off : nullptr;
+        off += (bytes + 255) & ~size_t(255);
+        return r;
+    }
+    template <typename T> T* arr(size_t n) { return (T*)take(sizeof(T) * n); }
+};
+
+bool qk_transform(const gpt_config& c) { return c.qk_rmsnorm || c.pos_encoding == GPT_POS_ROPE; }
+
+Ws plan(const gpt_config& c, const Table& tb, void* base) {
+    Ws w;
+    Carver cv(base);
+    const int64_t M = (int64_t)c.max_batch * c.block_size;
+    const int64_t d = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size, L = c.n_layer, H = c.n_head;
+    const bool bf = c.precision == GPT_PREC_BF16;
+    const size_t ab = bf ? 2 : 4;
+    w.params = cv.arr<float>(tb.n_total);
+    w.grads = cv.arr<float>(tb.n_total);
+    w.m = cv.arr<float>(tb.n_total);
+    w.v = cv.arr<float>(tb.n_total);
+    if (bf) w.wbf = cv.take(2 * tb.n_decay);
+    for (int l = 0; l < L; ++l) {
+        w.x_in.push_back(cv.arr<float>(M * d));
+        w.x_mid.push_back(cv.arr<float>(M * d));
+        w.ln1.push_back(cv.take(ab * M * d));
+        w.ln2.push_back(cv.take(ab * M * d));
+        w.qkv.push_back(cv.take(ab * M * 3 * d));
+        w.qk.push_back(qk_transform(c) ? cv.take(ab * M * 2 * d) : nullptr);
+        w.att.push_back(cv.take(ab * M * d));
+        w.lse.push_back(cv.arr<float>(M * H));
+        w.hpre.push_back(cv.take(ab * M * F));
+        w.hact.push_back(cv.take(ab * M * F));
+    }
+    w.x_fin = cv.arr<float>(M * d);
+    w.ln_mean = cv.arr<float>((2 * L + 1) * M);
+    w.ln_rstd = cv.arr<float>((2 * L + 1) * M);
+    w.lnf = cv.take(ab * M * d);
+    w.logits = cv.take(ab * M * Vp);
+    w.row_loss = cv.arr<float>(M);
+    w.dres = cv.arr<float>(M * d);
+    if (bf) w.dres_lp = cv.take(ab * M * d);
+    w.dln = cv.arr<float>(M * d);
+    w.dh = cv.take(ab * M * F);
+    w.dO = cv.take(ab * M * d);
+    w.dqkv = cv.take(ab * M * 3 * d);
+    w.attD = cv.arr<float>(M * H);
+    w.ln_partial = cv.arr<float>(gk::layernorm_bwd_partial_floats((int)M, (int)d));
+    int64_t maxN = std::max<int64_t>(3 * d, F);
+    w.cs_partial = cv.arr<float>(gk::colsum_partial_floats((int)M, (int)maxN));
+    w.gn_partial = cv.arr<double>(1024);
+    w.emb_scratch = cv.take(gk::embed_bwd_scratch_bytes((int)M, (int)d));
+    w.splitk_floats = (size_t)8 * std::max<int64_t>(3 * d * d, F * d);   // split-K slices of weight gradients
+    w.splitk = cv.arr<float>(w.splitk_floats);
+    if (c.pos_encoding == GPT_POS_ROPE) {
+        int64_t half = (d / H) / 2;
+        w.rope_cos = cv.arr<float>(c.block_size * half);
+        w.rope_sin = cv.arr<float>(c.block_size * half);
+    }
+    w.err = cv.arr<int32_t>(4);
+    w.loss_last = cv.arr<float>(4);
+    w.loss_sum = cv.arr<float>(4);
+    w.gnorm = cv.arr<float>(4);
+    w.coef = cv.arr<float>(4);
+    w.nonfinite = cv.arr<int32_t>(4);
+    w.bytes = cv.off;
+    return w;
+}
+
+gpt_status validate(const gpt_config* c, std::string* why) {
+    auto bad = [&](gpt_status s, const char* msg) { if (why) *why = msg; return s; };
+    if (!c) return bad(GPT_ERR_INVALID_ARGUMENT, "null config");
+    if (c->n_layer < 1 || c->n_head < 1 || c->n_embd < 1 || c->mlp_hidden < 1 || c->block_size < 1 ||
+        c->vocab_size < 1 || c->padded_vocab_size < 1 || c->max_batch < 1)
+        return bad(GPT_ERR_INVALID_ARGUMENT, "sizes must be positive");
+    if (c->n_embd % c->n_head) return bad(GPT_ERR_INVALID_ARGUMENT, "n_embd not divisible by n_head");
+    if (c->padded_vocab_size < c->vocab_size) return bad(GPT_ERR_INVALID_ARGUMENT, "padded_vocab_size < vocab_size");
+    if (c->precision != GPT_PREC_FP32 && c->precision != GPT_PREC_BF16)
+        return bad(GPT_ERR_INVALID_ARGUMENT, "unknown precision");
+    if (c->pos_encoding != GPT_POS_LEARNED && c->pos_encoding != GPT_POS_ROPE)
+        return bad(GPT_ERR_INVALID_ARGUMENT, "unknown pos_encoding");
+    if (c->mlp_act != GPT_ACT_GELU_TANH && c->mlp_act != GPT_ACT_RELU2)
+        return bad(GPT_ERR_INVALID_ARGUMENT, "unknown mlp_act");
+    if (c->window_even < 0 || c->window_odd < 0) return bad(GPT_ERR_INVALID_ARGUMENT, "negative window");
+    if (c->logit_softcap < 0.f || !std::isfinite(c->logit_softcap)) return bad(GPT_ERR_INVALID_ARGUMENT, "bad softcap");
+    if (!(c->ln_eps > 0.f) || !(c->adam_eps >= 0.f) || !(c->max_grad_norm > 0.f) || !(c->init_std >= 0.0))
+        return bad(GPT_ERR_INVALID_ARGUMENT, "bad epsilon, max_grad_norm or init_std");
+    const int hd = c->n_embd / c->n_head;
+    if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return bad(GPT_ERR_UNSUPPORTED, "head dim must be 16, 32, 64 or 128");
+    if (c->n_embd % 8 || c->mlp_hidden % 8) return bad(GPT_ERR_UNSUPPORTED, "n_embd and mlp_hidden must be multiples of 8");
+    if (c->n_embd > 2048) return bad(GPT_ERR_UNSUPPORTED, "n_embd > 2048");
+    if ((int64_t)c->max_batch * c->block_size > 32768) return bad(GPT_ERR_UNSUPPORTED, "max_batch * block_size > 32768");
+    if (c->padded_vocab_size > 131071) return bad(GPT_ERR_UNSUPPORTED, "padded_vocab_size > 131071");
+    return GPT_OK;
+}
+
+// ---------------------------------------------------------------- timing
+
+enum KClass {
+    KC_EMBED_FWD, KC_LN_FWD, KC_GEMM_FWD, KC_GEMM_LMHEAD, KC_ATTN_FWD, KC_CE, KC_GEMM_DGRAD, KC_GEMM_WGRAD,
+    KC_GEMM_LMHEAD_BWD, KC_LN_BWD, KC_COLSUM, KC_ATTN_BWD, KC_QK_PREP, KC_EMBED_BWD, KC_GRAD_NORM, KC_ADAMW,
+    KC_MISC, KC_COUNT
+};
+const char* kc_names[KC_COUNT] = {
+    "embed_fwd", "layernorm_fwd", "gemm_fwd", "gemm_lm_head", "attention_fwd", "cross_entropy", "gemm_dgrad",
+    "gemm_wgrad", "gemm_lm_head_bwd", "layernorm_bwd", "colsum", "attention_bwd", "qk_prep", "embed_bwd",
+    "grad_norm", "adamw", "misc"};
+
+struct Pending { int cls; hipEvent_t a, b; };
+struct ClassStat { double ms = 0, flops = 0, bytes = 0; int64_t launches = 0; };
+
+}  // namespace
+
+struct gpt_handle {
+    gpt_config cfg;
+    Table tb;
+    Ws ws;
+    hipStream_t stream = nullptr;
+    bool grads_dirty = true;     // true: the next micro-step starts from zero
+    int micro_count = 0;
+    std::string last_error;
+    uint32_t timing_mask = 0;
+    std::vector<Pending> pending;
+    std::vector<hipEvent_t> free_events;
+    ClassStat stats[KC_COUNT];
+};
+
+namespace {
+
+gpt_status fail(gpt_handle* h, gpt_status s, const std::string& msg) {
+    if (h) h->last_error = msg;
+    return s;
+}
+
+gpt_status hip_check(gpt_handle* h, hipError_t e, const char* what) {
+    if (e == hipSuccess) return GPT_OK;
+    return fail(h, GPT_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+hipEvent_t get_event(gpt_handle* h) {
+    if (!h->free_events.empty()) { hipEvent_t e = h->free_events.back(); h->free_events.pop_back(); return e; }
+    hipEvent_t e;
+    (void)hipEventCreate(&e);
+    return e;
+}
+
+struct Timed {
+    gpt_handle* h;
+    int cls;
+    hipEvent_t a = nullptr, b = nullptr;
+    Timed(gpt_handle* h_, int cls_, double flops, double bytes) : h(h_), cls(cls_) {
+        h->stats[cls].flops += flops;
+        h->stats[cls].bytes += bytes;
+        h->stats[cls].launches += 1;
+        if (h->timing_mask & (1u << cls)) {
+            a = get_event(h);
+            (void)hipEventRecord(a, h->stream);
+        }
+    }
+    ~Timed() {
+        if (a) {
+            b = get_event(h);
+            (void)hipEventRecord(b, h->stream);
+            h->pending.push_back({cls, a, b});
+        }
+    }
+};
+
+void drain_timing(gpt_handle* h) {
+    if (h->pending.empty()) return;
+    (void)hipStreamSynchronize(h->stream);
+    for (auto& p : h->pending) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) h->stats[p.cls].ms += ms;
+        h->free_events.push_back(p.a);
+        h->free_events.push_back(p.b);
+    }
+    h->pending.clear();
+}
+
+float* P(gpt_handle* h, int idx) { return h->ws.params + h->tb.t[idx].offset; }
+float* G(gpt_handle* h, int idx) { return h->ws.grads + h->tb.t[idx].offset; }
+// weight operand of the matrix products: bf16 copy or fp32 master
+const void* Wop(gpt_handle* h, int idx) {
+    if (h->cfg.precision == GPT_PREC_BF16) return (const char*)h->ws.wbf + 2 * h->tb.t[idx].offset;
+    return P(h, idx);
+}
+
+void run_gemm(gpt_handle* h, int cls, const gk::Gemm& g) {
+    double ab = g.in_bf ? 2 : 4, cb = g.c_bf ? 2 : 4;
+    double bytes = ab * ((double)g.M * g.K + (double)g.K * g.N) + cb * (double)g.M * g.N;
+    Timed t(h, cls, 2.0 * g.M * g.N * g.K, bytes);
+    gk::gemm(g, h->ws.splitk, h->ws.splitk_floats, h->stream);
+}
+
+gk::Gemm mk_gemm(gpt_handle* h, int M, int N, int K, const void* A, int64_t lda, bool a_kc, const void* B,
+                 int64_t ldb, bool b_kc, void* C, int64_t ldc, bool c_bf, int epi) {
+    gk::Gemm g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.a_kc = a_kc;
+    g.B = B; g.ldb = ldb; g.b_kc = b_kc;
+    g.C = C; g.ldc = ldc; g.c_bf = c_bf;
+    g.epi = epi;
+    g.act = h->cfg.mlp_act == GPT_ACT_RELU2 ? 1 : 0;
+    g.in_bf = h->cfg.precision == GPT_PREC_BF16;
+    return g;
+}
+
+int window_of(const gpt_config& c, int l) { return (l % 2 == 0) ? c.window_even : c.window_odd; }
+
+double attn_pairs(int B, int T, int H, int W) {
+    double p = 0;
+    if (W <= 0 || W >= T) p = (double)T * (T + 1) / 2;
+    else p = (double)W * (W + 1) / 2 + (double)(T - W) * W;
+    return p * B * H;
+}
+
+gpt_status sync_and_check(gpt_handle* h) {
+    gpt_status s = hip_check(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
+    if (s != GPT_OK) return s;
+    int32_t err = 0;
+    s = hip_check(h, hipMemcpy(&err, h->ws.err, sizeof(int32_t), hipMemcpyDeviceToHost), "read error flag");
+    if (s != GPT_OK) return s;
+    if (err) {
+        int32_t zero = 0;
+        (void)hipMemcpy(h->ws.err, &zero, sizeof(int32_t), hipMemcpyHostToDevice);
+        return fail(h, GPT_ERR_TOKEN_RANGE, "a token or target id is outside [0, padded_vocab_size)");
+    }
+    return GPT_OK;
+}
+
+gpt_status copy_tensor(gpt_handle* h, float* dst, const float* src, int64_t count, int dir_dev_to_host_buf,
+                       int on_device) {
+    (void)dir_dev_to_host_buf;
+    hipMemcpyKind kind = on_device ? hipMemcpyDeviceToDevice : hipMemcpyDefault;
+    gpt_status s = hip_check(h, hipMemcpyAsync(dst, src, sizeof(float) * count, kind, h->stream), "hipMemcpyAsync");
+    if (s != GPT_OK) return s;
+    return hip_check(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
+}
+
+gpt_status check_idx(const gpt_handle* h, int32_t idx, int64_t count) {
+    if (!h || idx < 0 || idx >= (int32_t)h->tb.t.size()) return GPT_ERR_INVALID_ARGUMENT;
+    if (count != h->tb.t[idx].numel) return GPT_ERR_INVALID_ARGUMENT;
+    return GPT_OK;
+}
+
+}  // namespace
+
+// ============================================================================
+// C ABI
+// ============================================================================
+
+extern "C" {
+
+gpt_status gpt_config_default(gpt_config* c) {
+    if (!c) return GPT_ERR_INVALID_ARGUMENT;
+    std::memset(c, 0, sizeof(*c));
+    c->n_layer = 12; c->n_head = 12; c->n_embd = 768; c->mlp_hidden = 3072;
+    c->block_size = 1024; c->vocab_size = 50257; c->padded_vocab_size = 50304; c->max_batch = 16;
+    c->precision = GPT_PREC_BF16; c->pos_encoding = GPT_POS_LEARNED; c->mlp_act = GPT_ACT_GELU_TANH;
+    c->ln_eps = 1e-5f; c->qk_norm_eps = 1e-6f; c->rope_base = 10000.f; c->logit_softcap = 0.f;
+    c->beta1 = 0.9f; c->beta2 = 0.95f; c->adam_eps = 1e-8f; c->weight_decay = 0.1f; c->max_grad_norm = 1.0f;
+    c->init_std = 0.02;
+    return GPT_OK;
+}
+
+gpt_status gpt_workspace_bytes(const gpt_config* cfg, size_t* bytes) {
+    if (!bytes) return GPT_ERR_INVALID_ARGUMENT;
+    gpt_status s = validate(cfg, nullptr);
+    if (s != GPT_OK) return s;
+    Table tb = build_table(*cfg);
+    *bytes = plan(*cfg, tb, nullptr).bytes;
+    return GPT_OK;
+}
+
+gpt_status gpt_create(const gpt_config* cfg, uint64_t seed, void* d_ws, size_t ws_bytes, void* stream,
+                      gpt_handle** out) {
+    if (!out || !d_ws) return GPT_ERR_INVALID_ARGUMENT;
+    *out = nullptr;
+    std::string why;
+    gpt_status s = validate(cfg, &why);
+    if (s != GPT_OK) return s;
+    if ((uintptr_t)d_ws % 256) return GPT_ERR_INVALID_ARGUMENT;
+    Table tb = build_table(*cfg);
+    Ws probe = plan(*cfg, tb, nullptr);
+    if (ws_bytes < probe.bytes) return GPT_ERR_WORKSPACE_TOO_SMALL;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GPT_ERR_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GPT_ERR_DEVICE;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GPT_ERR_UNSUPPORTED;
+
+    gpt_handle* h = new gpt_handle();
+    h->cfg = *cfg;
+    h->tb = tb;
+    h->ws = plan(*cfg, tb, d_ws);
+    h->stream = (hipStream_t)stream;
+    Ws& w = h->ws;
+    hipStream_t st = h->stream;
+    const int64_t n = tb.n_total;
+    gk::fill_f32(w.params, n, 0.f, st);
+    gk::fill_f32(w.grads, n, 0.f, st);
+    gk::fill_f32(w.m, n, 0.f, st);
+    gk::fill_f32(w.v, n, 0.f, st);
+    const double L = cfg->n_layer;
+    for (size_t i = 0; i < tb.t.size(); ++i) {
+        const TensorInfo& ti = tb.t[i];
+        float* dst = w.params + ti.offset;
+        if (ti.init == INIT_ONE) gk::fill_f32(dst, ti.numel, 1.f, st);
+        else if (ti.init == INIT_ZERO || (ti.init == INIT_PROJ && cfg->zero_init_proj)) continue;
+        else {
+            double std = cfg->init_std * (ti.init == INIT_PROJ ? std::pow(2.0 * L, -0.5) : 1.0);
+            gk::init_normal(dst, ti.numel, seed, (uint64_t)i, std, st);
+        }
+    }
+    if (w.wbf) gk::f32_to_bf16(w.wbf, w.params, tb.n_decay, st);
+    if (w.rope_cos)
+        gk::rope_tables(w.rope_cos, w.rope_sin, cfg->block_size, cfg->n_embd / cfg->n_head, cfg->rope_base, st);
+    gk::fill_i32(w.err, 4, 0, st);
+    gk::fill_f32(w.loss_sum, 4, 0.f, st);
+    gk::fill_f32(w.loss_last, 4, 0.f, st);
+    gk::fill_i32(w.nonfinite, 4, 0, st);
+    s = hip_check(h, hipGetLastError(), "kernel launch");
+    if (s != GPT_OK) { delete h; return s; }
+    h->grads_dirty = true;
+    *out = h;
+    return GPT_OK;
+}
+
+gpt_status gpt_destroy(gpt_handle* h) {
+    if (!h) return GPT_ERR_INVALID_ARGUMENT;
+    if (!h->pending.empty()) (void)hipStreamSynchronize(h->stream);
+    for (auto& p : h->pending) { (void)hipEventDestroy(p.a); (void)hipEventDestroy(p.b); }
+    for (auto e : h->free_events) (void)hipEventDestroy(e);
+    delete h;
+    return GPT_OK;
+}
+
+gpt_status gpt_set_stream(gpt_handle* h, void* stream) {
+    if (!h) return GPT_ERR_INVALID_ARGUMENT;
+    drain_timing(h);
+    h->stream = (hipStream_t)stream;
+    return GPT_OK;
+}
+
+gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t* tgt, int32_t B, int32_t T,
+                                float grad_scale, float* h_loss) {
+    if (!h) return GPT_ERR_INVALID_ARGUMENT;
+    const gpt_config& c = h->cfg;
+    if (!tok || !tgt) return fail(h, GPT_ERR_INVALID_ARGUMENT, "null token or target buffer");
+    if (B < 1 || B > c.max_batch) return fail(h, GPT_ERR_INVALID_ARGUMENT, "B must be in [1, max_batch]");
+    if (T < 1 || T > c.block_size)
+        return fail(h, GPT_ERR_INVALID_ARGUMENT, "T must be in [1, block_size]: cannot forward a longer sequence");
+    if (!std::isfinite(grad_scale)) return fail(h, GPT_ERR_INVALID_ARGUMENT, "grad_scale not finite");
+    Ws& w = h->ws;
+    const Table& tb = h->tb;
+    hipStream_t st = h->stream;
+    const int M = B * T, d = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size, H = c.n_head;
+    const int hd = d / H, L = c.n_layer;
+    const bool bf = c.precision == GPT_PREC_BF16;
+    const double ab = bf ? 2 : 4;
+    const bool qkt = qk_transform(c);
+    const int gelu_or_relu = c.mlp_act == GPT_ACT_RELU2 ? 1 : 0;
+    (void)gelu_or_relu;
+
+    if (h->grads_dirty) {
+        Timed t(h, KC_MISC, 0, 4.0 * tb.n_total);
+        gk::fill_f32(w.grads, tb.n_total, 0.f, st);
+        gk::fill_f32(w.loss_sum, 1, 0.f, st);
+        h->grads_dirty = false;
+        h->micro_count = 0;
+    }
+    // ------------------------------------------------------------ forward
+    {
+        Timed t(h, KC_EMBED_FWD, 0, (double)M * d * (tb.wpe >= 0 ? 12 : 8) + 4.0 * M);
+        gk::embed_fwd(tok, P(h, tb.wte), tb.wpe >= 0 ? P(h, tb.wpe) : nullptr, w.x_in[0], M, T, d, Vp, w.err, st);
+    }
+    for (int l = 0; l < L; ++l) {
+        const LayerIdx& li = tb.layers[l];
+        float* mean1 = w.ln_mean + (size_t)(2 * l) * M;
+        float* rstd1 = w.ln_rstd + (size_t)(2 * l) * M;
+        float* mean2 = w.ln_mean + (size_t)(2 * l + 1) * M;
+        float* rstd2 = w.ln_rstd + (size_t)(2 * l + 1) * M;
+        {
+            Timed t(h, KC_LN_FWD, 0, (double)M * d * (4 + ab) + 8.0 * M);
+            gk::layernorm_fwd(bf, w.x_in[l], P(h, li.ln1_w), P(h, li.ln1_b), w.ln1[l], mean1, rstd1, M, d, c.ln_eps, st);
+        }
+        {
+            gk::Gemm g = mk_gemm(h, M, 3 * d, d, w.ln1[l], d, true, Wop(h, li.attn_w), d, true, w.qkv[l], 3 * d, bf,
+                                 gk::EPI_BIAS);
+            g.bias = P(h, li.attn_b);
+            run_gemm(h, KC_GEMM_FWD, g);
+        }
+        const void *q = w.qkv[l], *k = (const char*)w.qkv[l] + (size_t)ab * d;
+        int64_t ldq = 3 * d, ldk = 3 * d;
+        if (qkt) {
+            Timed t(h, KC_QK_PREP, 0, (double)M * 2 * d * 2 * ab);
+            gk::qk_prep_fwd(bf, w.qkv[l], w.qk[l], w.rope_cos, w.rope_sin, M, T, H, hd, c.qk_rmsnorm,
+                            c.pos_encoding == GPT_POS_ROPE, c.qk_norm_eps, st);
+            q = w.qk[l];
+            k = (const char*)w.qk[l] + (size_t)ab * d;
+            ldq = ldk = 2 * d;
+        }
+        gk::Attn a{};
+        a.B = B; a.T = T; a.H = H; a.hd = hd; a.window = window_of(c, l);
+        a.q = q; a.k = k; a.v = (const char*)w.qkv[l] + (size_t)ab * 2 * d;
+        a.ldq = ldq; a.ldk = ldk; a.ldv = 3 * d;
+        a.o = w.att[l]; a.ldo = d; a.lse = w.lse[l]; a.bf = bf;
+        {
+            double pairs = attn_pairs(B, T, H, a.window);
+            Timed t(h, KC_ATTN_FWD, 4.0 * hd * pairs, (double)M * d * 4 * ab + 4.0 * M * H);
+            gk::attention_fwd(a, st);
+        }
+        {
+            gk::Gemm g = mk_gemm(h, M, d, d, w.att[l], d, true, Wop(h, li.proj_w), d, true, w.x_mid[l], d, false,
+                                 gk::EPI_BIAS_RESID);
+            g.bias = P(h, li.proj_b);
+            g.resid = w.x_in[l];
+            run_gemm(h, KC_GEMM_FWD, g);
+        }
+        {
+            Timed t(h, KC_LN_FWD, 0, (double)M * d * (4 + ab) + 8.0 * M);
+            gk::layernorm_fwd(bf, w.x_mid[l], P(h, li.ln2_w), P(h, li.ln2_b), w.ln2[l], mean2, rstd2, M, d, c.ln_eps, st);
+        }
+        {
+            gk::Gemm g = mk_gemm(h, M, F, d, w.ln2[l], d, true, Wop(h, li.fc_w), d, true, w.hpre[l], F, bf,
+                                 gk::EPI_BIAS_ACT);
+            g.bias = P(h, li.fc_b);
+            g.C2 = w.hact[l];
+            run_gemm(h, KC_GEMM_FWD, g);
+        }
+        {
+            float* xo = (l + 1 < L) ? w.x_in[l + 1] : w.x_fin;
+            gk::Gemm g = mk_gemm(h, M, d, F, w.hact[l], F, true, Wop(h, li.mp_w), F, true, xo, d, false,
+                                 gk::EPI_BIAS_RESID);
+            g.bias = P(h, li.mp_b);
+            g.resid = w.x_mid[l];
+            run_gemm(h, KC_GEMM_FWD, g);
+        }
+    }
+    float* meanf = w.ln_mean + (size_t)(2 * L) * M;
+    float* rstdf = w.ln_rstd + (size_t)(2 * L) * M;
+    {
+        Timed t(h, KC_LN_FWD, 0, (double)M * d * (4 + ab) + 8.0 * M);
+        gk::layernorm_fwd(bf, w.x_fin, P(h, tb.lnf_w), P(h, tb.lnf_b), w.lnf, meanf, rstdf, M, d, c.ln_eps, st);
+    }
+    {
+        gk::Gemm g = mk_gemm(h, M, Vp, d, w.lnf, d, true, Wop(h, tb.wte), d, true, w.logits, Vp, bf, gk::EPI_STORE);
+        run_gemm(h, KC_GEMM_LMHEAD, g);
+    }
+    {
+        Timed t(h, KC_CE, 0, (double)M * Vp * 2 * ab + 8.0 * M);
+        gk::cross_entropy(bf, w.logits, tgt, w.row_loss, M, Vp, grad_scale / (float)M, c.logit_softcap, w.err, st);
+        gk::mean_loss(w.row_loss, M, w.loss_last, w.loss_sum, st);
+    }
+    // ------------------------------------------------------------ backward
+    {
+        gk::Gemm g = mk_gemm(h, M, d, Vp, w.logits, Vp, true, Wop(h, tb.wte), d, false, w.dln, d, false, gk::EPI_STORE);
+        run_gemm(h, KC_GEMM_LMHEAD_BWD, g);
+        gk::Gemm g2 = mk_gemm(h, Vp, d, M, w.logits, Vp, false, w.lnf, d, false, G(h, tb.wte), d, false, gk::EPI_ACCUM);
+        run_gemm(h, KC_GEMM_LMHEAD_BWD, g2);
+    }
+    void* dR = bf ? w.dres_lp : (void*)w.dres;   // residual gradient as a matrix-product operand
+    {
+        Timed t(h, KC_LN_BWD, 0, (double)M * d * (4 * 3 + ab) + 8.0 * M);
+        gk::layernorm_bwd(bf, w.dln, w.x_fin, meanf, rstdf, P(h, tb.lnf_w), w.dres, bf ? w.dres_lp : nullptr, true,
+                          G(h, tb.lnf_w), G(h, tb.lnf_b), w.ln_partial, M, d, st);
+    }
+    for (int l = L - 1; l >= 0; --l) {
+        const LayerIdx& li = tb.layers[l];
+        float* mean1 = w.ln_mean + (size_t)(2 * l) * M;
+        float* rstd1 = w.ln_rstd + (size_t)(2 * l) * M;
+        float* mean2 = w.ln_mean + (size_t)(2 * l + 1) * M;
+        float* rstd2 = w.ln_rstd + (size_t)(2 * l + 1) * M;
+        // MLP branch
+        {
+            gk::Gemm g = mk_gemm(h, M, F, d, dR, d, true, Wop(h, li.mp_w), F, false, w.dh, F, bf, gk::EPI_ACT_GRAD);
+            g.aux = w.hpre[l];
+            run_gemm(h, KC_GEMM_DGRAD, g);
+            gk::Gemm g2 = mk_gemm(h, d, F, M, dR, d, false, w.hact[l], F, false, G(h, li.mp_w), F, false, gk::EPI_ACCUM);
+            run_gemm(h, KC_GEMM_WGRAD, g2);
+        }
+        {
+            Timed t(h, KC_COLSUM, 0, 4.0 * M * d);
+            gk::colsum(false, w.dres, d, M, d, G(h, li.mp_b), w.cs_partial, st);
+        }
+        {
+            gk::Gemm g = mk_gemm(h, M, d, F, w.dh, F, true, Wop(h, li.fc_w), d, false, w.dln, d, false, gk::EPI_STORE);
+            run_gemm(h, KC_GEMM_DGRAD, g);
+            gk::Gemm g2 = mk_gemm(h, F, d, M, w.dh, F, false, w.ln2[l], d, false, G(h, li.fc_w), d, false, gk::EPI_ACCUM);
+            run_gemm(h, KC_GEMM_WGRAD, g2);
+        }
+        {
+            Timed t(h, KC_COLSUM, 0, ab * M * F);
+            gk::colsum(bf, w.dh, F, M, F, G(h, li.fc_b), w.cs_partial, st);
+        }
+        {
+            Timed t(h, KC_LN_BWD, 0, (double)M * d * (4 * 4 + ab) + 8.0 * M);
+            gk::layernorm_bwd(bf, w.dln, w.x_mid[l], mean2, rstd2, P(h, li.ln2_w), w.dres, bf ? w.dres_lp : nullptr,
+                              false, G(h, li.ln2_w), G(h, li.ln2_b), w.ln_partial, M, d, st);
+        }
+        // attention branch
+        {
+            gk::Gemm g = mk_gemm(h, M, d, d, dR, d, true, Wop(h, li.proj_w), d, false, w.dO, d, bf, gk::EPI_STORE);
+            run_gemm(h, KC_GEMM_DGRAD, g);
+            gk::Gemm g2 = mk_gemm(h, d, d, M, dR, d, false, w.att[l], d, false, G(h, li.proj_w), d, false, gk::EPI_ACCUM);
+            run_gemm(h, KC_GEMM_WGRAD, g2);
+        }
+        {
+            Timed t(h, KC_COLSUM, 0, 4.0 * M * d);
+            gk::colsum(false, w.dres, d, M, d, G(h, li.proj_b), w.cs_partial, st);
+        }
+        const void *q = w.qkv[l], *k = (const char*)w.qkv[l] + (size_t)ab * d;
+        int64_t ldq = 3 * d, ldk = 3 * d;
+        if (qkt) {
+            q = w.qk[l];
+            k = (const char*)w.qk[l] + (size_t)ab * d;
+            ldq = ldk = 2 * d;
+        }
+        gk::Attn a{};
+        a.B = B; a.T = T; a.H = H; a.hd = hd; a.window = window_of(c, l);
+        a.q = q; a.k = k; a.v = (const char*)w.qkv[l] + (size_t)ab * 2 * d;
+        a.ldq = ldq; a.ldk = ldk; a.ldv = 3 * d;
+        a.o = w.att[l]; a.ldo = d; a.lse = w.lse[l]; a.bf = bf;
+        a.dO = w.dO; a.lddo = d; a.D = w.attD;
+        a.dq = w.dqkv; a.dk = (char*)w.dqkv + (size_t)ab * d; a.dv = (char*)w.dqkv + (size_t)ab * 2 * d; a.ldd = 3 * d;
+        {
+            double pairs = attn_pairs(B, T, H, a.window);
+            Timed t(h, KC_ATTN_BWD, 8.0 * hd * pairs, (double)M * d * 8 * ab + 8.0 * M * H);
+            gk::attn_rowdot(bf, w.dO, w.att[l], w.attD, B, T, H, hd, st);
+            gk::attention_bwd(a, st);
+        }
+        if (qkt) {
+            Timed t(h, KC_QK_PREP, 0, (double)M * 2 * d * 3 * ab);
+            gk::qk_prep_bwd(bf, w.qkv[l], w.dqkv, w.rope_cos, w.rope_sin, M, T, H, hd, c.qk_rmsnorm,
+                            c.pos_encoding == GPT_POS_ROPE, c.qk_norm_eps, st);
+        }
+        {
+            gk::Gemm g = mk_gemm(h, M, d, 3 * d, w.dqkv, 3 * d, true, Wop(h, li.attn_w), d, false, w.dln, d, false,
+                                 gk::EPI_STORE);
+            run_gemm(h, KC_GEMM_DGRAD, g);
+            gk::Gemm g2 = mk_gemm(h, 3 * d, d, M, w.dqkv, 3 * d, false, w.ln1[l], d, false, G(h, li.attn_w), d, false,
+                                  gk::EPI_ACCUM);
+            run_gemm(h, KC_GEMM_WGRAD, g2);
+        }
+        {
+            Timed t(h, KC_COLSUM, 0, ab * M * 3 * d);
+            gk::colsum(bf, w.dqkv, 3 * d, M, 3 * d, G(h, li.attn_b), w.cs_partial, st);
+        }
+        {
+            Timed t(h, KC_LN_BWD, 0, (double)M * d * (4 * 4 + ab) + 8.0 * M);
+            gk::layernorm_bwd(bf, w.dln, w.x_in[l], mean1, rstd1, P(h, li.ln1_w), w.dres, bf ? w.dres_lp : nullptr,
+                              false, G(h, li.ln1_w), G(h, li.ln1_b), w.ln_partial, M, d, st);
+        }
+    }
+    {
+        Timed t(h, KC_EMBED_BWD, 0, 4.0 * M * d + 8.0 * M * d);
+        gk::embed_bwd(tok, w.dres, G(h, tb.wte), tb.wpe >= 0 ? G(h, tb.wpe) : nullptr, B, T, d, Vp, w.emb_scratch, st);
+    }
+    h->micro_count += 1;
+    gpt_status s = hip_check(h, hipGetLastError(), "kernel launch");
+    if (s != GPT_OK) return s;
+    if (h_loss) {
+        s = sync_and_check(h);
+        if (s != GPT_OK) return s;
+        s = hip_check(h, hipMemcpy(h_loss, w.loss_last, sizeof(float), hipMemcpyDeviceToHost), "read loss");
+        if (s != GPT_OK) return s;
+    }
+    return GPT_OK;
+}
+
+gpt_status gpt_loss_accum(gpt_handle* h, float* out) {
+    if (!h || !out) return GPT_ERR_INVALID_ARGUMENT;
+    gpt_status s = sync_and_check(h);
+    if (s != GPT_OK) return s;
+    float sum = 0.f;
+    s = hip_check(h, hipMemcpy(&sum, h->ws.loss_sum, sizeof(float), hipMemcpyDeviceToHost), "read loss sum");
+    if (s != GPT_OK) return s;
+    *out = h->micro_count ? sum / h->micro_count : 0.f;
+    return GPT_OK;
+}
+
+gpt_status gpt_clip_and_adamw(gpt_handle* h, float lr, int32_t step, float* h_grad_norm) {
+    if (!h) return GPT_ERR_INVALID_ARGUMENT;
+    if (step < 1) return fail(h, GPT_ERR_INVALID_ARGUMENT, "step must be >= 1");
+    if (!(lr >= 0.f) || !std::isfinite(lr)) return fail(h, GPT_ERR_INVALID_ARGUMENT, "lr must be finite and >= 0");
+    const gpt_config& c = h->cfg;
+    Ws& w = h->ws;
+    const int64_t n = h->tb.n_total;
+    if (h->grads_dirty) {   // no micro-step since the last update: gradients are zero
+        gk::fill_f32(w.grads, n, 0.f, h->stream);
+    }
+    {
+        Timed t(h, KC_GRAD_NORM, 0, 4.0 * n);
+        gk::grad_norm(w.grads, n, w.gn_partial, w.gnorm, w.coef, w.nonfinite, c.max_grad_norm, h->stream);
+    }
+    double b1 = c.beta1, b2 = c.beta2;
+    float rbc1 = (float)(1.0 / (1.0 - std::pow(b1, step)));
+    float rbc2 = (float)(1.0 / (1.0 - std::pow(b2, step)));
+    {
+        Timed t(h, KC_ADAMW, 0, 28.0 * n + 2.0 * h->tb.n_decay);
+        gk::adamw(w.params, w.grads, w.m, w.v, w.wbf, n, h->tb.n_decay, w.coef, w.nonfinite, lr, c.beta1, c.beta2,
+                  c.adam_eps, c.weight_decay, rbc1, rbc2, h->stream);
+    }
+    h->grads_dirty = true;
+    gpt_status s = hip_check(h, hipGetLastError(), "kernel launch");
+    if (s != GPT_OK) return s;
+    if (h_grad_norm) {
+        s = hip_check(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
+        if (s != GPT_OK) return s;
+        int32_t nf = 0;
+        (void)hipMemcpy(h_grad_norm, w.gnorm, sizeof(float), hipMemcpyDeviceToHost);
+        (void)hipMemcpy(&nf, w.nonfinite, sizeof(int32_t), hipMemcpyDeviceToHost);
+        if (nf) return fail(h, GPT_ERR_NONFINITE, "gradient norm is not finite: update skipped");
+    }
+    return GPT_OK;
+}
+
+gpt_status gpt_num_tensors(const gpt_handle* h, int32_t* n) {
+    if (!h || !n) return GPT_ERR_INVALID_ARGUMENT;
+    *n = (int32_t)h->tb.t.size();
+    return GPT_OK;
+}
+
+gpt_status gpt_tensor_info(const gpt_handle* h, int32_t idx, const char** name, int32_t* ndim, int64_t shape[2],
+                           int32_t* decay) {
+    if (!h || idx < 0 || idx >= (int32_t)h->tb.t.size()) return GPT_ERR_INVALID_ARGUMENT;
+    const TensorInfo& ti = h->tb.t[idx];
+    if (name) *name = ti.name.c_str();
+    if (ndim) *ndim = ti.ndim;
+    if (shape) { shape[0] = ti.shape[0]; shape[1] = ti.shape[1]; }
+    if (decay) *decay = ti.decay;
+    return GPT_OK;
+}
+
+gpt_status gpt_get_param(gpt_handle* h, int32_t idx, float* buf, int64_t count, int32_t on_dev) {
+    if (check_idx(h, idx, count) != GPT_OK || !buf) return GPT_ERR_INVALID_ARGUMENT;
+    return copy_tensor(h, buf, P(h, idx), count, 1, on_dev);
+}
+gpt_status gpt_set_param(gpt_handle* h, int32_t idx, const float* buf, int64_t count, int32_t on_dev) {
+    if (check_idx(h, idx, count) != GPT_OK || !buf) return GPT_ERR_INVALID_ARGUMENT;
+    gpt_status s = copy_tensor(h, P(h, idx), buf, count, 0, on_dev);
+    if (s != GPT_OK) return s;
+    if (h->ws.wbf && h->tb.t[idx].decay) {
+        gk::f32_to_bf16((char*)h->ws.wbf + 2 * h->tb.t[idx].offset, P(h, idx), count, h->stream);
+        return hip_check(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
+    }
+    return GPT_OK;
+}
+gpt_status gpt_get_grad(gpt_handle* h, int32_t idx, float* buf, int64_t count, int32_t on_dev) {
+    if (check_idx(h, idx, count) != GPT_OK || !buf) return GPT_ERR_INVALID_ARGUMENT;
+    if (h->grads_dirty) gk::fill_f32(h->ws.grads, h->tb.n_total, 0.f, h->stream);
+    return copy_tensor(h, buf, G(h, idx), count, 1, on_dev);
+}
+gpt_status gpt_set_grad(gpt_handle* h, int32_t idx, const float* buf, int64_t count, int32_t on_dev) {
+    if (check_idx(h, idx, count) != GPT_OK || !buf) return GPT_ERR_INVALID_ARGUMENT;
+    if (h->grads_dirty) {
+        gk::fill_f32(h->ws.grads, h->tb.n_total, 0.f, h->stream);
+        gk::fill_f32(h->ws.loss_sum, 1, 0.f, h->stream);
+        h->grads_dirty = false;
+        h->micro_count = 0;
+    }
+    return copy_tensor(h, G(h, idx), buf, count, 0, on_dev);
+}
+gpt_status gpt_get_opt_state(gpt_handle* h, int32_t idx, float* m, float* v, int64_t count, int32_t on_dev) {
+    if (check_idx(h, idx, count) != GPT_OK) return GPT_ERR_INVALID_ARGUMENT;
+    int64_t off = h->tb.t[idx].offset;
+    if (m) { gpt_status s = copy_tensor(h, m, h->ws.m + off, count, 1, on_dev); if (s != GPT_OK) return s; }
+    if (v) { gpt_status s = copy_tensor(h, v, h->ws.v + off, count, 1, on_dev); if (s != GPT_OK) return s; }
+    return GPT_OK;
+}
+gpt_status gpt_set_opt_state(gpt_handle* h, int32_t idx, const float* m, const float* v, int64_t count, int32_t on_dev) {
+    if (check_idx(h, idx, count) != GPT_OK) return GPT_ERR_INVALID_ARGUMENT;
+    int64_t off = h->tb.t[idx].offset;
+    if (m) { gpt_status s = copy_tensor(h, h->ws.m + off, m, count, 0, on_dev); if (s != GPT_OK) return s; }
+    if (v) { gpt_status s = copy_tensor(h, h->ws.v + off, v, count, 0, on_dev); if (s != GPT_OK) return s; }
+    return GPT_OK;
+}
+
+gpt_status gpt_get_row_losses(gpt_handle* h, float* buf, int64_t count, int32_t on_dev) {
+    if (!h || !buf || count < 1 || count > (int64_t)h->cfg.max_batch * h->cfg.block_size)
+        return GPT_ERR_INVALID_ARGUMENT;
+    return copy_tensor(h, buf, h->ws.row_loss, count, 1, on_dev);
+}
+
+double gpt_lr_schedule(int32_t it, int32_t warmup, int32_t max_steps, double max_lr, double min_lr) {
+    if (it < warmup) return max_lr * (it + 1) / warmup;
+    if (it > max_steps) return min_lr;
+    double ratio = (double)(it - warmup) / (double)(max_steps - warmup);
+    double coeff = 0.5 * (1.0 + std::cos(M_PI * ratio));
+    return min_lr + coeff * (max_lr - min_lr);
+}
+
+const char* gpt_status_string(gpt_status s) {
+    switch (s) {
+        case GPT_OK: return "ok";
+        case GPT_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case GPT_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case GPT_ERR_UNSUPPORTED: return "unsupported configuration or device";
+        case GPT_ERR_DEVICE: return "HIP runtime error";
+        case GPT_ERR_TOKEN_RANGE: return "token or target id out of range";
+        case GPT_ERR_NONFINITE: return "non-finite gradient norm; update skipped";
+    }
+    return "unknown status";
+}
+
+const char* gpt_last_error(const gpt_handle* h) { return h ? h->last_error.c_str() : "null handle"; }
+
+gpt_status gpt_set_kernel_timing(gpt_handle* h, int32_t mask) {
+    if (!h) return GPT_ERR_INVALID_ARGUMENT;
+    h->timing_mask = (uint32_t)mask;
+    return GPT_OK;
+}
+gpt_status gpt_reset_kernel_timing(gpt_handle* h) {
+    if (!h) return GPT_ERR_INVALID_ARGUMENT;
+    drain_timing(h);
+    for (auto& c : h->stats) c = ClassStat();
+    return GPT_OK;
+}
+gpt_status gpt_num_kernel_classes(int32_t* n) {
+    if (!n) return GPT_ERR_INVALID_ARGUMENT;
+    *n = KC_COUNT;
+    return GPT_OK;
+}
+gpt_status gpt_kernel_timing(gpt_handle* h, int32_t cls, const char** name, double* total_ms, int64_t* launches,
+                             double* flops, double* bytes) {
+    if (!h || cls < 0 || cls >= KC_COUNT) return GPT_ERR_INVALID_ARGUMENT;
+    drain_timing(h);
+    if (name) *name = kc_names[cls];
+    if (total_ms) *total_ms = h->stats[cls].ms;
+    if (launches) *launches = h->stats[cls].launches;
+    if (flops) *flops = h->stats[cls].flops;
+    if (bytes) *bytes = h->stats[cls].bytes;
+    return GPT_OK;
+}
+
+// ============================================================================
+// test-only kernel entry points (include/gpt_testing.h)
+// ============================================================================
+
+gpt_status gptk_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int32_t a_kc, const void* B,
+                     int64_t ldb, int32_t b_kc, void* C, int64_t ldc, int32_t in_bf16, int32_t c_bf16, int32_t epi,
+                     int32_t act, const float* bias, const float* resid, const void* aux, void* C2,
+                     float* splitk_scratch, int64_t splitk_floats, void* stream) {
+    if (M < 1 || N < 1 || K < 1 || !A || !B || !C || epi < 0 || epi > 5) return GPT_ERR_INVALID_ARGUMENT;
+    gk::Gemm g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.a_kc = a_kc;
+    g.B = B; g.ldb = ldb; g.b_kc = b_kc;
+    g.C = C; g.ldc = ldc; g.c_bf = c_bf16;
+    g.C2 = C2; g.bias = bias; g.resid = resid; g.aux = aux;
+    g.epi = epi; g.act = act; g.in_bf = in_bf16;
+    gk::gemm(g, splitk_scratch, (size_t)splitk_floats, (hipStream_t)stream);
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
+
+gpt_status gptk_attention(int32_t backward, int32_t B, int32_t T, int32_t H, int32_t hd, int32_t window,
+                          const void* q, const void* k, const void* v, int64_t ldq, int64_t ldk, int64_t ldv,
+                          void* o, int64_t ldo, float* lse, const void* dO, int64_t lddo, float* D, void* dq, void* dk,
+                          void* dv, int64_t ldd, int32_t bf16, void* stream) {
+    if (B < 1 || T < 1 || H < 1 || (hd != 16 && hd != 32 && hd != 64 && hd != 128)) return GPT_ERR_INVALID_ARGUMENT;
+    gk::Attn a{};
+    a.B = B; a.T = T; a.H = H; a.hd = hd; a.window = window;
+    a.q = q; a.k = k; a.v = v; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv;
+    a.o = o; a.ldo = ldo; a.lse = lse; a.dO = dO; a.lddo = lddo; a.D = D;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.ldd = ldd; a.bf = bf16;
+    hipStream_t s = (hipStream_t)stream;
+    if (backward) {
+        gk::attn_rowdot(a.bf, dO, o, D, B, T, H, hd, s);
+        gk::attention_bwd(a, s);
+    } else {
+        gk::attention_fwd(a, s);
+    }
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
+
+gpt_status gptk_layernorm(int32_t backward, int32_t M, int32_t d, float eps, const float* x, const float* g,
+                          const float* b, void* y, float* mean, float* rstd, const float* dy, float* dres,
+                          void* dres_lp, int32_t overwrite, float* dg, float* db, float* partial, int32_t bf16,
+                          void* stream) {
+    if (M < 1 || d < 4 || d % 4 || d > 2048) return GPT_ERR_INVALID_ARGUMENT;
+    hipStream_t s = (hipStream_t)stream;
+    if (backward) gk::layernorm_bwd(bf16, dy, x, mean, rstd, g, dres, dres_lp, overwrite, dg, db, partial, M, d, s);
+    else gk::layernorm_fwd(bf16, x, g, b, y, mean, rstd, M, d, eps, s);
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
+
+int64_t gptk_layernorm_partial_floats(int32_t M, int32_t d) { return (int64_t)gk::layernorm_bwd_partial_floats(M, d); }
+
+gpt_status gptk_cross_entropy(int32_t M, int32_t Vp, void* z, const int32_t* y, float* row_loss, float gscale,
+                              float cap, int32_t* err, int32_t bf16, void* stream) {
+    if (M < 1 || Vp < 1) return GPT_ERR_INVALID_ARGUMENT;
+    gk::cross_entropy(bf16, z, y, row_loss, M, Vp, gscale, cap, err, (hipStream_t)stream);
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
+
+int64_t gptk_embed_bwd_scratch_bytes(int32_t M, int32_t d) { return (int64_t)gk::embed_bwd_scratch_bytes(M, d); }
+
+gpt_status gptk_embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, int32_t B, int32_t T,
+                          int32_t d, int32_t Vp, void* scratch, void* stream) {
+    if (B < 1 || T < 1 || (int64_t)B * T > 32768 || d % 4 || Vp > 131071) return GPT_ERR_INVALID_ARGUMENT;
+    gk::embed_bwd(tok, dx, dwte, dwpe, B, T, d, Vp, scratch, (hipStream_t)stream);
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
+
+gpt_status gptk_colsum(int32_t M, int32_t N, const void* Y, int64_t ld, int32_t bf16, float* out, float* partial,
+                       void* stream) {
+    if (M < 1 || N < 1) return GPT_ERR_INVALID_ARGUMENT;
+    gk::colsum(bf16, Y, ld, M, N, out, partial, (hipStream_t)stream);
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
+
+int64_t gptk_colsum_partial_floats(int32_t M, int32_t N) { return (int64_t)gk::colsum_partial_floats(M, N); }
+
+}  // extern "C"

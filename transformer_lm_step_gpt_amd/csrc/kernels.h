@@ -1,0 +1,123 @@
+// Host-side launch functions for the gfx950 kernels of the GPT-2 training
+// step. All launches are asynchronous on the given stream; every pointer is a
+// device address. `bf` selects bf16 (true) or fp32 (false) storage of the
+// activation tensors named "act" below.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gk {
+
+// ---------------------------------------------------------------- init / fills
+// dst[e] = fp32(std * z_e), z from Philox4x64-10 keyed (seed, stream_id),
+// counter e/4, Box-Muller pairs (words 0,1) and (2,3) in double precision.
+void init_normal(float* dst, int64_t n, uint64_t seed, uint64_t stream_id, double std, hipStream_t s);
+void fill_f32(float* dst, int64_t n, float value, hipStream_t s);
+void fill_i32(int32_t* dst, int64_t n, int32_t value, hipStream_t s);
+void f32_to_bf16(void* dst, const float* src, int64_t n, hipStream_t s);
+// rotary tables cos/sin [T, hd/2] of the angle t * base^(-2i/hd) (double precision math)
+void rope_tables(float* cos_t, float* sin_t, int T, int hd, double base, hipStream_t s);
+
+// ---------------------------------------------------------------- embedding
+// x0[m, :] = wte[tok[m], :] (+ wpe[m % T, :] if wpe); fp32 out. Invalid ids
+// give a zero token row and set *err = 1.
+void embed_fwd(const int32_t* tok, const float* wte, const float* wpe, float* x0, int M, int T, int d,
+               int Vp, int32_t* err, hipStream_t s);
+
+// Deterministic, atomic-free dwte[tok[m]] += dx[m] and dwpe[t] += sum_b dx[b, t].
+// scratch needs embed_bwd_scratch_bytes(M, d) bytes.
+size_t embed_bwd_scratch_bytes(int M, int d);
+void embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, int B, int T, int d, int Vp,
+               void* scratch, hipStream_t s);
+
+// ---------------------------------------------------------------- LayerNorm
+// y = (x - mean) rstd * g + b over rows of width d (fp32 x, act y); saves mean, rstd.
+void layernorm_fwd(bool bf, const float* x, const float* g, const float* b, void* y, float* mean,
+                   float* rstd, int M, int d, float eps, hipStream_t s);
+// dres (+)= LN backward of dy; writes a bf16 copy of dres when dres_lp != null;
+// dg += sum dy*xhat, db += sum dy (deterministic two-pass); partial needs
+// layernorm_bwd_partial_floats(M, d) floats.
+size_t layernorm_bwd_partial_floats(int M, int d);
+void layernorm_bwd(bool bf, const float* dy, const float* x, const float* mean, const float* rstd,
+                   const float* g, float* dres, void* dres_lp, bool overwrite, float* dg, float* db,
+                   float* partial, int M, int d, hipStream_t s);
+
+// ---------------------------------------------------------------- column sums
+// out[n] += sum_m Y[m, n] (Y act or fp32 with row stride ld); partial needs
+// colsum_partial_floats(M, N) floats.
+size_t colsum_partial_floats(int M, int N);
+void colsum(bool y_bf, const void* Y, int64_t ld, int M, int N, float* out, float* partial, hipStream_t s);
+
+// ---------------------------------------------------------------- cross-entropy
+// Per row of logits z (act, [M, Vp], in place): z' = cap tanh(z/cap) if cap > 0;
+// loss_m = logsumexp(z') - z'[y_m]; z <- (softmax(z') - onehot(y)) * gscale
+// (times 1 - tanh^2 with the cap). Invalid targets: loss 0, zero row, *err = 1.
+void cross_entropy(bool bf, void* z, const int32_t* y, float* row_loss, int M, int Vp, float gscale,
+                   float cap, int32_t* err, hipStream_t s);
+// *loss_out = mean(row_loss[0..M)); *loss_sum += that mean (deterministic).
+void mean_loss(const float* row_loss, int M, float* loss_out, float* loss_sum, hipStream_t s);
+
+// ---------------------------------------------------------------- attention helpers
+// D[b, h, t] = sum_c dO[m, h*hd + c] * O[m, h*hd + c]
+void attn_rowdot(bool bf, const void* dO, const void* O, float* D, int B, int T, int H, int hd, hipStream_t s);
+// q/k RMS normalisation (no gain) then rotary rotation, per head.
+// fwd: reads q,k from qkv [M, 3d], writes qk_out [M, 2d].
+void qk_prep_fwd(bool bf, const void* qkv, void* qk_out, const float* cos_t, const float* sin_t, int M, int T,
+                 int H, int hd, int norm, int rope, float eps, hipStream_t s);
+// bwd: in place on the q,k columns of dqkv [M, 3d], raw q,k re-read from qkv.
+void qk_prep_bwd(bool bf, const void* qkv, void* dqkv, const float* cos_t, const float* sin_t, int M, int T,
+                 int H, int hd, int norm, int rope, float eps, hipStream_t s);
+
+// ---------------------------------------------------------------- optimiser
+// norm = sqrt(sum g^2); coef = min(1, max_norm / (norm + 1e-6)); flag non-finite.
+// partial needs 1024 doubles.
+void grad_norm(const float* g, int64_t n, double* partial, float* norm_out, float* coef_out,
+               int32_t* nonfinite, float max_norm, hipStream_t s);
+// AdamW over the flat buffers; elements [0, n_decay) are decayed and mirrored
+// to the bf16 copy wbf (if non-null). Skips everything when *nonfinite.
+void adamw(float* p, const float* g, float* m, float* v, void* wbf, int64_t n, int64_t n_decay,
+           const float* coef, const int32_t* nonfinite, float lr, float b1, float b2, float eps, float wd,
+           float rbc1, float rbc2, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMM
+enum GemmEpi {
+    EPI_STORE = 0,      // C = A B                        (C: act or fp32)
+    EPI_BIAS = 1,       // C = A B + bias                 (C: act)
+    EPI_BIAS_ACT = 2,   // C = A B + bias; C2 = act(C)    (C, C2: act)
+    EPI_BIAS_RESID = 3, // C = resid + A B + bias         (C, resid: fp32)
+    EPI_ACT_GRAD = 4,   // C = (A B) * act'(aux)          (C, aux: act)
+    EPI_ACCUM = 5       // C += A B                       (C: fp32)
+};
+struct Gemm {
+    int M, N, K;
+    const void* A; int64_t lda; bool a_kc;   // A(m,k) = a_kc ? A[m*lda + k] : A[k*lda + m]
+    const void* B; int64_t ldb; bool b_kc;   // B(k,n) = b_kc ? B[n*ldb + k] : B[k*ldb + n]
+    void* C; int64_t ldc; bool c_bf;         // output storage type
+    void* C2;
+    const float* bias;
+    const float* resid;
+    const void* aux;
+    int epi;
+    int act;
+    bool in_bf;                              // A and B storage (bf16 or fp32)
+};
+// scratch: split-K partials for the matrix-core kernel (may be null: no split)
+void gemm(const Gemm& g, float* splitk_scratch, size_t splitk_floats, hipStream_t s);
+const char* gemm_last_kernel_name();
+
+// ---------------------------------------------------------------- attention
+struct Attn {
+    int B, T, H, hd, window;
+    const void* q; const void* k; const void* v; int64_t ldq, ldk, ldv;   // row strides
+    void* o; int64_t ldo;
+    float* lse;                       // [B, H, T]
+    const void* dO; int64_t lddo;     // backward
+    const float* D;                   // [B, H, T]
+    void* dq; void* dk; void* dv; int64_t ldd;
+    bool bf;
+};
+void attention_fwd(const Attn& a, hipStream_t s);
+void attention_bwd(const Attn& a, hipStream_t s);
+
+}  // namespace gk

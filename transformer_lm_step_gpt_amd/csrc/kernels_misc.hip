@@ -1,0 +1,816 @@
+// Bandwidth-bound kernels of the GPT-2 training step on gfx950: parameter
+// initialisation, embedding forward/backward, LayerNorm forward/backward,
+// column sums, fused softmax cross-entropy, attention row dots, q/k
+// normalisation + rotary positions, global gradient norm and AdamW.
+//
+// Model definition: "Zero to Hero, lecture 9: reproducing GPT-2 (124M)"
+// (ai.flicky.cc), "Раздел 1 / Архитектура" (pre-LN blocks, final LayerNorm),
+// "Генерация и устройство" (token + position embeddings), "Связанные веса и
+// инициализация" (tied wte, N(0, 0.02) init with (2 n_layer)^-1/2 on residual
+// writers), "Оптимизатор, клиппинг, расписание" (AdamW 0.9/0.95/1e-8, decay
+// 0.1 on 2-D tensors, global clip 1.0). Speedrun variants (rotary positions,
+// QK-Norm, ReLU^2, softcap): Modded-NanoGPT README (oa0.com), technique list.
+#include "common.h"
+#include "kernels.h"
+
+namespace gk {
+
+// =====================================================================
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) + Box-Muller normals
+// =====================================================================
+
+GPT_DEV void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) { k0 += W0; k1 += W1; }
+        uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
+        uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
+        uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+    }
+}
+
+__global__ __launch_bounds__(256) void init_normal_kernel(float* dst, int64_t n, uint64_t seed, uint64_t sid,
+                                                          double std) {
+    int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j * 4 >= n) return;
+    uint64_t c[4] = {(uint64_t)j, 0, 0, 0};
+    philox4x64_10(c, seed, sid);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        double u1 = ((double)(c[2 * p] >> 11) + 0.5) * 0x1.0p-53;
+        double u2 = ((double)(c[2 * p + 1] >> 11) + 0.5) * 0x1.0p-53;
+        double r = sqrt(-2.0 * log(u1));
+        double t = 6.283185307179586476925 * u2;
+        int64_t e = 4 * j + 2 * p;
+        if (e < n) dst[e] = (float)(std * (r * cos(t)));
+        if (e + 1 < n) dst[e + 1] = (float)(std * (r * sin(t)));
+    }
+}
+
+void init_normal(float* dst, int64_t n, uint64_t seed, uint64_t sid, double std, hipStream_t s) {
+    int64_t blocks = (n + 4 * 256 - 1) / (4 * 256);
+    if (blocks) init_normal_kernel<<<(unsigned)blocks, 256, 0, s>>>(dst, n, seed, sid, std);
+}
+
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* dst, int64_t n, float v) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = v;
+}
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* dst, int64_t n, int32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = v;
+}
+static unsigned grid_for(int64_t n) {
+    int64_t b = (n + 255) / 256;
+    return (unsigned)(b < 8192 ? (b < 1 ? 1 : b) : 8192);
+}
+void fill_f32(float* dst, int64_t n, float v, hipStream_t s) {
+    if (n > 0) fill_f32_kernel<<<grid_for(n), 256, 0, s>>>(dst, n, v);
+}
+void fill_i32(int32_t* dst, int64_t n, int32_t v, hipStream_t s) {
+    if (n > 0) fill_i32_kernel<<<grid_for(n), 256, 0, s>>>(dst, n, v);
+}
+
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(bf16* dst, const float* src, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        dst[i] = (bf16)src[i];
+}
+void f32_to_bf16(void* dst, const float* src, int64_t n, hipStream_t s) {
+    if (n > 0) f32_to_bf16_kernel<<<grid_for(n), 256, 0, s>>>((bf16*)dst, src, n);
+}
+
+__global__ void rope_tables_kernel(float* cos_t, float* sin_t, int T, int hd, double base) {
+    int half = hd / 2;
+    int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= T * half) return;
+    int t = idx / half, i = idx % half;
+    double ang = (double)t * pow(base, -2.0 * i / hd);
+    cos_t[idx] = (float)cos(ang);
+    sin_t[idx] = (float)sin(ang);
+}
+void rope_tables(float* cos_t, float* sin_t, int T, int hd, double base, hipStream_t s) {
+    int n = T * (hd / 2);
+    rope_tables_kernel<<<ceil_div(n, 256), 256, 0, s>>>(cos_t, sin_t, T, hd, base);
+}
+
+// =====================================================================
+// embedding forward: x0 = wte[tok] + wpe[t]
+// =====================================================================
+
+__global__ __launch_bounds__(256) void embed_fwd_kernel(const int32_t* tok, const float* wte, const float* wpe,
+                                                        float* x0, int M, int T, int d, int Vp, int32_t* err) {
+    int dq = d >> 2;
+    int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)M * dq) return;
+    int m = (int)(idx / dq), c = (int)(idx % dq) * 4;
+    int id = tok[m];
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (id >= 0 && id < Vp) {
+        v = load4(wte + (int64_t)id * d + c);
+    } else if (c == 0) {
+        *err = 1;
+    }
+    if (wpe) {
+        float4 p = load4(wpe + (int64_t)(m % T) * d + c);
+        v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+    }
+    store4(x0 + (int64_t)m * d + c, v);
+}
+
+void embed_fwd(const int32_t* tok, const float* wte, const float* wpe, float* x0, int M, int T, int d, int Vp,
+               int32_t* err, hipStream_t s) {
+    int64_t n = (int64_t)M * (d / 4);
+    embed_fwd_kernel<<<ceil_div(n, 256), 256, 0, s>>>(tok, wte, wpe, x0, M, T, d, Vp, err);
+}
+
+// =====================================================================
+// embedding backward (deterministic, no atomics)
+//   1. one workgroup sorts keys (token << 15 | position) with a bitonic
+//      network in LDS, then cuts the sorted list into segments (one per
+//      distinct token) and pieces (at most PIECE rows of one segment);
+//   2. one workgroup per piece sums its rows of dx into a partial row;
+//   3. one workgroup per segment adds its pieces' partials, in order, to
+//      that token's wte-gradient row.
+// =====================================================================
+
+constexpr int EMB_PIECE = 64;
+constexpr int EMB_MAXN = 32768;
+constexpr int EMB_THREADS = 1024;
+
+struct EmbScratch {
+    int32_t* sorted_pos;   // [M]
+    int32_t* piece_start;  // [M + 1]
+    int32_t* seg_tok;      // [M]
+    int32_t* seg_piece;    // [M + 1]
+    int32_t* counts;       // [4]: n_valid, n_pieces, n_segs
+    float* partial;        // [M, d]
+};
+
+static EmbScratch carve_emb(void* base, int M, int d) {
+    char* p = (char*)base;
+    auto take = [&](size_t bytes) { char* r = p; p += (bytes + 255) & ~size_t(255); return r; };
+    EmbScratch e;
+    e.sorted_pos = (int32_t*)take(sizeof(int32_t) * M);
+    e.piece_start = (int32_t*)take(sizeof(int32_t) * (M + 1));
+    e.seg_tok = (int32_t*)take(sizeof(int32_t) * M);
+    e.seg_piece = (int32_t*)take(sizeof(int32_t) * (M + 1));
+    e.counts = (int32_t*)take(sizeof(int32_t) * 4);
+    e.partial = (float*)take(sizeof(float) * (size_t)M * d);
+    return e;
+}
+
+size_t embed_bwd_scratch_bytes(int M, int d) {
+    auto r = [](size_t b) { return (b + 255) & ~size_t(255); };
+    return r(4 * (size_t)M) * 2 + r(4 * (size_t)(M + 1)) * 2 + r(16) + r(4 * (size_t)M * d);
+}
+
+// Block-wide inclusive scan (sum or max) of one int per thread.
+template <bool MAX>
+__device__ int block_scan_incl(int v, int* sh /* >= 32 ints */) {
+    int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int u = __shfl_up(v, o, 64);
+        if (lane >= o) v = MAX ? max(v, u) : v + u;
+    }
+    if (lane == 63) sh[wid] = v;
+    __syncthreads();
+    if (wid == 0) {
+        int w = lane < nw ? sh[lane] : (MAX ? INT_MIN : 0);
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            int u = __shfl_up(w, o, 64);
+            if (lane >= o) w = MAX ? max(w, u) : w + u;
+        }
+        if (lane < nw) sh[lane] = w;
+    }
+    __syncthreads();
+    if (wid > 0) { int c = sh[wid - 1]; v = MAX ? max(v, c) : v + c; }
+    __syncthreads();
+    return v;
+}
+
+__global__ __launch_bounds__(EMB_THREADS) void embed_sort_kernel(const int32_t* tok, int M, int Vp, int N,
+                                                                  EmbScratch e) {
+    extern __shared__ uint32_t keys[];   // N keys
+    __shared__ int sh[64];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < N; i += EMB_THREADS) {
+        uint32_t k = 0xFFFFFFFFu;
+        if (i < M) {
+            int t = tok[i];
+            if (t >= 0 && t < Vp) k = ((uint32_t)t << 15) | (uint32_t)i;
+        }
+        keys[i] = k;
+    }
+    __syncthreads();
+    // bitonic sort, ascending
+    for (int size = 2; size <= N; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = tid; t < N / 2; t += EMB_THREADS) {
+                int lo = 2 * t - (t & (stride - 1));
+                int hi = lo + stride;
+                bool up = (lo & size) == 0;
+                uint32_t a = keys[lo], b = keys[hi];
+                if ((a > b) == up) { keys[lo] = b; keys[hi] = a; }
+            }
+            __syncthreads();
+        }
+    }
+    // each thread owns E consecutive sorted entries
+    const int E = N / EMB_THREADS;
+    const int base = tid * E;
+    // pass 1: segment begin (max-scan of segment-start indices)
+    int run = INT_MIN;
+    for (int u = 0; u < E; ++u) {
+        int i = base + u;
+        uint32_t k = keys[i];
+        bool valid = k != 0xFFFFFFFFu;
+        bool start = valid && (i == 0 || (keys[i - 1] >> 15) != (k >> 15));
+        if (start) run = i;
+    }
+    // block_scan_incl folds in every earlier thread; the value this thread
+    // starts from is the inclusive result of thread tid - 1
+    __shared__ int excl_max[EMB_THREADS];
+    int incl = block_scan_incl<true>(run, sh);
+    excl_max[tid] = incl;
+    __syncthreads();
+    int seg_begin = tid ? excl_max[tid - 1] : INT_MIN;
+    // pass 2: count pieces and segments owned by this thread
+    int npiece = 0, nseg = 0, nvalid = 0;
+    {
+        int sb = seg_begin;
+        for (int u = 0; u < E; ++u) {
+            int i = base + u;
+            uint32_t k = keys[i];
+            bool valid = k != 0xFFFFFFFFu;
+            bool start = valid && (i == 0 || (keys[i - 1] >> 15) != (k >> 15));
+            if (start) sb = i;
+            bool pstart = valid && (start || ((i - sb) % EMB_PIECE) == 0);
+            npiece += pstart;
+            nseg += start;
+            nvalid += valid;
+        }
+    }
+    int pincl = block_scan_incl<false>(npiece, sh);
+    int sincl = block_scan_incl<false>(nseg, sh);
+    int vincl = block_scan_incl<false>(nvalid, sh);
+    int pid = pincl - npiece, sid = sincl - nseg;
+    {
+        int sb = seg_begin;
+        for (int u = 0; u < E; ++u) {
+            int i = base + u;
+            uint32_t k = keys[i];
+            bool valid = k != 0xFFFFFFFFu;
+            if (!valid) continue;
+            bool start = (i == 0 || (keys[i - 1] >> 15) != (k >> 15));
+            if (start) sb = i;
+            bool pstart = start || ((i - sb) % EMB_PIECE) == 0;
+            e.sorted_pos[i] = (int32_t)(k & 0x7FFF);
+            if (start) {
+                e.seg_tok[sid] = (int32_t)(k >> 15);
+                e.seg_piece[sid] = pid;
+                ++sid;
+            }
+            if (pstart) {
+                e.piece_start[pid] = i;
+                ++pid;
+            }
+        }
+    }
+    if (tid == EMB_THREADS - 1) {
+        e.counts[0] = vincl;
+        e.counts[1] = pincl;
+        e.counts[2] = sincl;
+        e.piece_start[pincl] = vincl;
+        e.seg_piece[sincl] = pincl;
+    }
+}
+
+__global__ __launch_bounds__(256) void embed_piece_kernel(const float* dx, int d, EmbScratch e) {
+    int p = blockIdx.x;
+    if (p >= e.counts[1]) return;
+    int r0 = e.piece_start[p], r1 = e.piece_start[p + 1];
+    for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int r = r0; r < r1; ++r) {
+            float4 v = load4(dx + (int64_t)e.sorted_pos[r] * d + c);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        store4(e.partial + (int64_t)p * d + c, acc);
+    }
+}
+
+__global__ __launch_bounds__(256) void embed_segment_kernel(float* dwte, int d, EmbScratch e) {
+    int sidx = blockIdx.x;
+    if (sidx >= e.counts[2]) return;
+    int p0 = e.seg_piece[sidx], p1 = e.seg_piece[sidx + 1];
+    int64_t row = e.seg_tok[sidx];
+    for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
+        float4 acc = load4(dwte + row * d + c);
+        for (int p = p0; p < p1; ++p) {
+            float4 v = load4(e.partial + (int64_t)p * d + c);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        store4(dwte + row * d + c, acc);
+    }
+}
+
+__global__ __launch_bounds__(256) void embed_wpe_kernel(const float* dx, float* dwpe, int B, int T, int d) {
+    int dq = d >> 2;
+    int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= T * dq) return;
+    int t = idx / dq, c = (idx % dq) * 4;
+    float4 acc = load4(dwpe + (int64_t)t * d + c);
+    for (int b = 0; b < B; ++b) {
+        float4 v = load4(dx + ((int64_t)b * T + t) * d + c);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    store4(dwpe + (int64_t)t * d + c, acc);
+}
+
+void embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, int B, int T, int d, int Vp,
+               void* scratch, hipStream_t s) {
+    int M = B * T;
+    int N = EMB_THREADS;
+    while (N < M) N <<= 1;
+    EmbScratch e = carve_emb(scratch, M, d);
+    size_t lds = sizeof(uint32_t) * (size_t)N;
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute((const void*)embed_sort_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(sizeof(uint32_t) * EMB_MAXN));
+        attr_set = true;
+    }
+    embed_sort_kernel<<<1, EMB_THREADS, lds, s>>>(tok, M, Vp, N, e);
+    embed_piece_kernel<<<M, 256, 0, s>>>(dx, d, e);
+    embed_segment_kernel<<<M, 256, 0, s>>>(dwte, d, e);
+    if (dwpe) embed_wpe_kernel<<<ceil_div((int64_t)T * (d / 4), 256), 256, 0, s>>>(dx, dwpe, B, T, d);
+}
+
+// =====================================================================
+// LayerNorm (one wavefront per row; d <= 2048)
+// =====================================================================
+
+constexpr int LN_MAXV = 8;   // float4 chunks per lane: d <= 64 * 4 * 8
+
+template <typename TO>
+__global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* x, const float* g, const float* b, TO* y,
+                                                            float* mean, float* rstd, int M, int d, float eps) {
+    int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    int lane = threadIdx.x & 63;
+    if (row >= M) return;
+    const int nv = d >> 2;
+    const float* xr = x + (int64_t)row * d;
+    float4 v[LN_MAXV];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+        int c = lane + 64 * i;
+        if (c < nv) {
+            v[i] = load4(xr + 4 * c);
+            s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+        }
+    }
+    float mu = wave_sum(s) / d;
+    float s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+        int c = lane + 64 * i;
+        if (c < nv) {
+            float a = v[i].x - mu, bb = v[i].y - mu, cc = v[i].z - mu, dd = v[i].w - mu;
+            s2 += (a * a + bb * bb) + (cc * cc + dd * dd);
+        }
+    }
+    float var = wave_sum(s2) / d;
+    float rs = 1.0f / sqrtf(var + eps);
+    TO* yr = y + (int64_t)row * d;
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+        int c = lane + 64 * i;
+        if (c < nv) {
+            float4 gg = load4(g + 4 * c), bb = load4(b + 4 * c);
+            float4 o;
+            o.x = (v[i].x - mu) * rs * gg.x + bb.x;
+            o.y = (v[i].y - mu) * rs * gg.y + bb.y;
+            o.z = (v[i].z - mu) * rs * gg.z + bb.z;
+            o.w = (v[i].w - mu) * rs * gg.w + bb.w;
+            store4(yr + 4 * c, o);
+        }
+    }
+    if (lane == 0) { mean[row] = mu; rstd[row] = rs; }
+}
+
+void layernorm_fwd(bool bf, const float* x, const float* g, const float* b, void* y, float* mean, float* rstd,
+                   int M, int d, float eps, hipStream_t s) {
+    int grid = ceil_div(M, 4);
+    if (bf) layernorm_fwd_kernel<bf16><<<grid, 256, 0, s>>>(x, g, b, (bf16*)y, mean, rstd, M, d, eps);
+    else layernorm_fwd_kernel<float><<<grid, 256, 0, s>>>(x, g, b, (float*)y, mean, rstd, M, d, eps);
+}
+
+constexpr int LNB_ROWS = 64;   // rows per workgroup in the backward pass
+
+size_t layernorm_bwd_partial_floats(int M, int d) { return (size_t)2 * ceil_div(M, LNB_ROWS) * d; }
+
+template <typename TL>
+__global__ __launch_bounds__(256) void layernorm_bwd_kernel(const float* dy, const float* x, const float* mean,
+                                                            const float* rstd, const float* g, float* dres,
+                                                            TL* dres_lp, int overwrite, float* part_g,
+                                                            float* part_b, int M, int d) {
+    __shared__ float red[4][2048 + 4];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nv = d >> 2;
+    float4 ag[LN_MAXV], ab[LN_MAXV], gg[LN_MAXV];
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+        ag[i] = ab[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        int c = lane + 64 * i;
+        gg[i] = c < nv ? load4(g + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int r0 = blockIdx.x * LNB_ROWS;
+    for (int r = r0 + w; r < min(M, r0 + LNB_ROWS); r += 4) {
+        const float mu = mean[r], rs = rstd[r];
+        float4 xh[LN_MAXV], dh[LN_MAXV], dyv[LN_MAXV];
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < LN_MAXV; ++i) {
+            int c = lane + 64 * i;
+            if (c < nv) {
+                float4 xv = load4(x + (int64_t)r * d + 4 * c);
+                dyv[i] = load4(dy + (int64_t)r * d + 4 * c);
+                xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
+                dh[i] = make_float4(dyv[i].x * gg[i].x, dyv[i].y * gg[i].y, dyv[i].z * gg[i].z, dyv[i].w * gg[i].w);
+                s1 += (dh[i].x + dh[i].y) + (dh[i].z + dh[i].w);
+                s2 += (dh[i].x * xh[i].x + dh[i].y * xh[i].y) + (dh[i].z * xh[i].z + dh[i].w * xh[i].w);
+            }
+        }
+        s1 = wave_sum(s1) / d;
+        s2 = wave_sum(s2) / d;
+#pragma unroll
+        for (int i = 0; i < LN_MAXV; ++i) {
+            int c = lane + 64 * i;
+            if (c < nv) {
+                float4 o;
+                o.x = rs * (dh[i].x - s1 - xh[i].x * s2);
+                o.y = rs * (dh[i].y - s1 - xh[i].y * s2);
+                o.z = rs * (dh[i].z - s1 - xh[i].z * s2);
+                o.w = rs * (dh[i].w - s1 - xh[i].w * s2);
+                float* dp = dres + (int64_t)r * d + 4 * c;
+                if (!overwrite) {
+                    float4 old = load4(dp);
+                    o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
+                }
+                store4(dp, o);
+                if (dres_lp) store4(dres_lp + (int64_t)r * d + 4 * c, o);
+                ag[i].x += dyv[i].x * xh[i].x; ag[i].y += dyv[i].y * xh[i].y;
+                ag[i].z += dyv[i].z * xh[i].z; ag[i].w += dyv[i].w * xh[i].w;
+                ab[i].x += dyv[i].x; ab[i].y += dyv[i].y; ab[i].z += dyv[i].z; ab[i].w += dyv[i].w;
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+        int c = lane + 64 * i;
+        if (c < nv) *reinterpret_cast<float4*>(&red[w][4 * c]) = ag[i];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < d; c += 256)
+        part_g[(int64_t)blockIdx.x * d + c] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < LN_MAXV; ++i) {
+        int c = lane + 64 * i;
+        if (c < nv) *reinterpret_cast<float4*>(&red[w][4 * c]) = ab[i];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < d; c += 256)
+        part_b[(int64_t)blockIdx.x * d + c] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+}
+
+// out[c] += sum_p part[p * n + c], p in order
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* part, int np, int n, float* out) {
+    int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= n) return;
+    float a = 0.f;
+    for (int p = 0; p < np; ++p) a += part[(int64_t)p * n + c];
+    out[c] += a;
+}
+
+void layernorm_bwd(bool bf, const float* dy, const float* x, const float* mean, const float* rstd, const float* g,
+                   float* dres, void* dres_lp, bool overwrite, float* dg, float* db, float* partial, int M, int d,
+                   hipStream_t s) {
+    int nb = ceil_div(M, LNB_ROWS);
+    float* pg = partial;
+    float* pb = partial + (size_t)nb * d;
+    if (bf)
+        layernorm_bwd_kernel<bf16><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, (bf16*)dres_lp, overwrite, pg, pb,
+                                                      M, d);
+    else
+        layernorm_bwd_kernel<float><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, (float*)dres_lp, overwrite, pg,
+                                                       pb, M, d);
+    reduce_partials_kernel<<<ceil_div(d, 256), 256, 0, s>>>(pg, nb, d, dg);
+    reduce_partials_kernel<<<ceil_div(d, 256), 256, 0, s>>>(pb, nb, d, db);
+}
+
+// =====================================================================
+// column sums (bias gradients)
+// =====================================================================
+
+constexpr int CS_ROWS = 128;
+size_t colsum_partial_floats(int M, int N) { return (size_t)ceil_div(M, CS_ROWS) * N; }
+
+template <typename TI>
+__global__ __launch_bounds__(256) void colsum_kernel(const TI* Y, int64_t ld, int M, int N, float* part) {
+    int n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    int r0 = blockIdx.y * CS_ROWS, r1 = min(M, r0 + CS_ROWS);
+    float a = 0.f;
+    for (int r = r0; r < r1; ++r) a += to_f32(Y[(int64_t)r * ld + n]);
+    part[(int64_t)blockIdx.y * N + n] = a;
+}
+
+void colsum(bool y_bf, const void* Y, int64_t ld, int M, int N, float* out, float* partial, hipStream_t s) {
+    dim3 grid(ceil_div(N, 256), ceil_div(M, CS_ROWS));
+    if (y_bf) colsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)Y, ld, M, N, partial);
+    else colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)Y, ld, M, N, partial);
+    reduce_partials_kernel<<<ceil_div(N, 256), 256, 0, s>>>(partial, (int)grid.y, N, out);
+}
+
+// =====================================================================
+// fused softmax cross-entropy, forward + backward, in place
+// =====================================================================
+
+template <typename T>
+__global__ __launch_bounds__(256) void cross_entropy_kernel(T* z, const int32_t* y, float* row_loss, int Vp,
+                                                            float gscale, float cap, int32_t* err) {
+    __shared__ float smx[4], ssm[4];
+    const int row = blockIdx.x;
+    T* zr = z + (int64_t)row * Vp;
+    const int tgt = y[row];
+    const bool valid = tgt >= 0 && tgt < Vp;
+    const float icap = cap > 0.f ? 1.0f / cap : 0.f;
+    const float L2E = 1.4426950408889634f;
+    float mx = -INFINITY, sm = 0.f;   // running max and sum of exp2((z - mx) log2e)
+    for (int v = threadIdx.x; v < Vp; v += 256) {
+        float zz = to_f32(zr[v]);
+        if (cap > 0.f) zz = cap * tanhf(zz * icap);
+        zz *= L2E;
+        if (zz > mx) { sm = sm * exp2f(mx - zz) + 1.0f; mx = zz; }
+        else sm += exp2f(zz - mx);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float m2 = __shfl_xor(mx, o, 64), s2 = __shfl_xor(sm, o, 64);
+        float mn = fmaxf(mx, m2);
+        sm = (mx == -INFINITY ? 0.f : sm * exp2f(mx - mn)) + (m2 == -INFINITY ? 0.f : s2 * exp2f(m2 - mn));
+        mx = mn;
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { smx[w] = mx; ssm[w] = sm; }
+    __syncthreads();
+    float gm = fmaxf(fmaxf(smx[0], smx[1]), fmaxf(smx[2], smx[3]));
+    float gs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gs += smx[i] == -INFINITY ? 0.f : ssm[i] * exp2f(smx[i] - gm);
+    const float lse2 = gm + log2f(gs);   // log2-domain logsumexp
+    if (threadIdx.x == 0) {
+        float loss = 0.f;
+        if (valid) {
+            float zy = to_f32(zr[tgt]);
+            if (cap > 0.f) zy = cap * tanhf(zy * icap);
+            loss = lse2 * 0.6931471805599453f - zy;
+        } else {
+            *err = 1;
+        }
+        row_loss[row] = loss;
+    }
+    __syncthreads();   // the target logit is read before any thread overwrites it
+    for (int v = threadIdx.x; v < Vp; v += 256) {
+        float g = 0.f;
+        if (valid) {
+            float zz = to_f32(zr[v]);
+            float th = 0.f;
+            if (cap > 0.f) { th = tanhf(zz * icap); zz = cap * th; }
+            float p = exp2f(zz * L2E - lse2);
+            g = (p - (v == tgt ? 1.0f : 0.0f)) * gscale;
+            if (cap > 0.f) g *= (1.0f - th * th);
+        }
+        zr[v] = from_f32<T>(g);
+    }
+}
+
+void cross_entropy(bool bf, void* z, const int32_t* y, float* row_loss, int M, int Vp, float gscale, float cap,
+                   int32_t* err, hipStream_t s) {
+    if (bf) cross_entropy_kernel<bf16><<<M, 256, 0, s>>>((bf16*)z, y, row_loss, Vp, gscale, cap, err);
+    else cross_entropy_kernel<float><<<M, 256, 0, s>>>((float*)z, y, row_loss, Vp, gscale, cap, err);
+}
+
+__global__ __launch_bounds__(256) void mean_loss_kernel(const float* rl, int M, float* out, float* sum) {
+    __shared__ double sh[4];
+    double a = 0.0;
+    for (int i = threadIdx.x; i < M; i += 256) a += rl[i];
+    a = wave_sum_d(a);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = ((sh[0] + sh[1]) + sh[2]) + sh[3];
+        float mval = (float)(t / M);
+        *out = mval;
+        *sum += mval;
+    }
+}
+void mean_loss(const float* row_loss, int M, float* loss_out, float* loss_sum, hipStream_t s) {
+    mean_loss_kernel<<<1, 256, 0, s>>>(row_loss, M, loss_out, loss_sum);
+}
+
+// =====================================================================
+// attention row dots D = rowsum(dO * O), per head
+// =====================================================================
+
+template <typename T>
+__global__ __launch_bounds__(256) void attn_rowdot_kernel(const T* dO, const T* O, float* D, int B, int T_, int H,
+                                                          int hd) {
+    int idx = blockIdx.x * 256 + threadIdx.x;   // (m, h)
+    if (idx >= B * T_ * H) return;
+    int m = idx / H, h = idx % H;
+    int b = m / T_, t = m % T_;
+    const int64_t off = (int64_t)m * H * hd + (int64_t)h * hd;
+    float a = 0.f;
+    for (int c = 0; c < hd; c += 4) {
+        float4 x = load4(dO + off + c), y = load4(O + off + c);
+        a += (x.x * y.x + x.y * y.y) + (x.z * y.z + x.w * y.w);
+    }
+    D[((int64_t)b * H + h) * T_ + t] = a;
+}
+
+void attn_rowdot(bool bf, const void* dO, const void* O, float* D, int B, int T, int H, int hd, hipStream_t s) {
+    int n = B * T * H;
+    if (bf) attn_rowdot_kernel<bf16><<<ceil_div(n, 256), 256, 0, s>>>((const bf16*)dO, (const bf16*)O, D, B, T, H, hd);
+    else attn_rowdot_kernel<float><<<ceil_div(n, 256), 256, 0, s>>>((const float*)dO, (const float*)O, D, B, T, H, hd);
+}
+
+// =====================================================================
+// q/k RMS normalisation + rotary positions (one wavefront per (row, head, q|k);
+// lane i < hd/2 holds the rotate-half pair (i, i + hd/2))
+// =====================================================================
+
+template <typename T>
+__global__ __launch_bounds__(256) void qk_prep_fwd_kernel(const T* qkv, T* out, const float* cos_t,
+                                                          const float* sin_t, int M, int T_, int H, int hd,
+                                                          int norm, int rope, float eps) {
+    int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (wid >= M * H * 2) return;
+    int which = wid & 1, mh = wid >> 1, m = mh / H, h = mh % H;
+    int half = hd >> 1, d = H * hd;
+    const T* src = qkv + (int64_t)m * 3 * d + which * d + h * hd;
+    T* dst = out + (int64_t)m * 2 * d + which * d + h * hd;
+    bool act = lane < half;
+    float a = act ? to_f32(src[lane]) : 0.f, b = act ? to_f32(src[lane + half]) : 0.f;
+    if (norm) {
+        float ss = wave_sum(a * a + b * b);
+        float r = 1.0f / sqrtf(ss / hd + eps);
+        a *= r; b *= r;
+    }
+    if (rope && act) {
+        int t = m % T_;
+        float c = cos_t[t * half + lane], sn = sin_t[t * half + lane];
+        float na = a * c - b * sn, nb = a * sn + b * c;
+        a = na; b = nb;
+    }
+    if (act) { dst[lane] = from_f32<T>(a); dst[lane + half] = from_f32<T>(b); }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void qk_prep_bwd_kernel(const T* qkv, T* dqkv, const float* cos_t,
+                                                          const float* sin_t, int M, int T_, int H, int hd,
+                                                          int norm, int rope, float eps) {
+    int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (wid >= M * H * 2) return;
+    int which = wid & 1, mh = wid >> 1, m = mh / H, h = mh % H;
+    int half = hd >> 1, d = H * hd;
+    const T* src = qkv + (int64_t)m * 3 * d + which * d + h * hd;
+    T* g = dqkv + (int64_t)m * 3 * d + which * d + h * hd;
+    bool act = lane < half;
+    float ga = act ? to_f32(g[lane]) : 0.f, gb = act ? to_f32(g[lane + half]) : 0.f;
+    if (rope && act) {
+        int t = m % T_;
+        float c = cos_t[t * half + lane], sn = sin_t[t * half + lane];
+        float na = ga * c + gb * sn, nb = -ga * sn + gb * c;
+        ga = na; gb = nb;
+    }
+    if (norm) {
+        float a = act ? to_f32(src[lane]) : 0.f, b = act ? to_f32(src[lane + half]) : 0.f;
+        float ss = wave_sum(a * a + b * b);
+        float r = 1.0f / sqrtf(ss / hd + eps);
+        float ya = a * r, yb = b * r;
+        float dot = wave_sum(ga * ya + gb * yb) / hd;
+        ga = r * (ga - ya * dot);
+        gb = r * (gb - yb * dot);
+    }
+    if (act) { g[lane] = from_f32<T>(ga); g[lane + half] = from_f32<T>(gb); }
+}
+
+void qk_prep_fwd(bool bf, const void* qkv, void* out, const float* cos_t, const float* sin_t, int M, int T, int H,
+                 int hd, int norm, int rope, float eps, hipStream_t s) {
+    int grid = ceil_div((int64_t)M * H * 2, 4);
+    if (bf)
+        qk_prep_fwd_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)qkv, (bf16*)out, cos_t, sin_t, M, T, H, hd, norm,
+                                                      rope, eps);
+    else
+        qk_prep_fwd_kernel<float><<<grid, 256, 0, s>>>((const float*)qkv, (float*)out, cos_t, sin_t, M, T, H, hd,
+                                                       norm, rope, eps);
+}
+void qk_prep_bwd(bool bf, const void* qkv, void* dqkv, const float* cos_t, const float* sin_t, int M, int T, int H,
+                 int hd, int norm, int rope, float eps, hipStream_t s) {
+    int grid = ceil_div((int64_t)M * H * 2, 4);
+    if (bf)
+        qk_prep_bwd_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)qkv, (bf16*)dqkv, cos_t, sin_t, M, T, H, hd, norm,
+                                                      rope, eps);
+    else
+        qk_prep_bwd_kernel<float><<<grid, 256, 0, s>>>((const float*)qkv, (float*)dqkv, cos_t, sin_t, M, T, H, hd,
+                                                       norm, rope, eps);
+}
+
+// =====================================================================
+// global gradient norm (two deterministic passes in double) and AdamW
+// =====================================================================
+
+constexpr int GN_BLOCKS = 1024;
+
+__global__ __launch_bounds__(256) void grad_norm_partial_kernel(const float* g, int64_t n, double* part) {
+    __shared__ double sh[4];
+    double a = 0.0;
+    int64_t n4 = n >> 2;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)GN_BLOCKS * 256) {
+        float4 v = load4(g + 4 * i);
+        a += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+    }
+    if (blockIdx.x == 0)
+        for (int64_t i = 4 * n4 + threadIdx.x; i < n; i += 256) a += (double)g[i] * g[i];
+    a = wave_sum_d(a);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) part[blockIdx.x] = ((sh[0] + sh[1]) + sh[2]) + sh[3];
+}
+
+__global__ __launch_bounds__(256) void grad_norm_final_kernel(const double* part, float* norm_out, float* coef_out,
+                                                              int32_t* nonfinite, float max_norm) {
+    __shared__ double sh[4];
+    double a = 0.0;
+    for (int i = threadIdx.x; i < GN_BLOCKS; i += 256) a += part[i];
+    a = wave_sum_d(a);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double nrm = sqrt(((sh[0] + sh[1]) + sh[2]) + sh[3]);
+        bool bad = !isfinite(nrm);
+        double c = (double)max_norm / (nrm + 1e-6);
+        *norm_out = (float)nrm;
+        *coef_out = bad ? 0.f : (float)(c < 1.0 ? c : 1.0);
+        *nonfinite = bad ? 1 : 0;
+    }
+}
+
+void grad_norm(const float* g, int64_t n, double* partial, float* norm_out, float* coef_out, int32_t* nonfinite,
+               float max_norm, hipStream_t s) {
+    grad_norm_partial_kernel<<<GN_BLOCKS, 256, 0, s>>>(g, n, partial);
+    grad_norm_final_kernel<<<1, 256, 0, s>>>(partial, norm_out, coef_out, nonfinite, max_norm);
+}
+
+__global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, float* m, float* v, bf16* wbf,
+                                                    int64_t n4, int64_t nd4, const float* coef_p,
+                                                    const int32_t* nonfinite, float lr, float b1, float b2,
+                                                    float eps, float wd, float rbc1, float rbc2) {
+    if (*nonfinite) return;
+    const float c = *coef_p;
+    const float dec = 1.0f - lr * wd;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        float4 pp = load4(p + 4 * i), gg = load4(g + 4 * i), mm = load4(m + 4 * i), vv = load4(v + 4 * i);
+        const bool decayed = i < nd4;
+        float* pe = &pp.x; float* ge = &gg.x; float* me = &mm.x; float* ve = &vv.x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float gc = ge[e] * c;
+            me[e] = b1 * me[e] + (1.0f - b1) * gc;
+            ve[e] = b2 * ve[e] + (1.0f - b2) * gc * gc;
+            float pv = decayed ? pe[e] * dec : pe[e];
+            pe[e] = pv - lr * (me[e] * rbc1) / (sqrtf(ve[e] * rbc2) + eps);
+        }
+        store4(p + 4 * i, pp);
+        store4(m + 4 * i, mm);
+        store4(v + 4 * i, vv);
+        if (decayed && wbf) store4(wbf + 4 * i, pp);
+    }
+}
+
+void adamw(float* p, const float* g, float* m, float* v, void* wbf, int64_t n, int64_t n_decay, const float* coef,
+           const int32_t* nonfinite, float lr, float b1, float b2, float eps, float wd, float rbc1, float rbc2,
+           hipStream_t s) {
+    int64_t n4 = n / 4;
+    unsigned grid = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
+    adamw_kernel<<<grid, 256, 0, s>>>(p, g, m, v, (bf16*)wbf, n4, n_decay / 4, coef, nonfinite, lr, b1, b2, eps, wd,
+                                      rbc1, rbc2);
+}
+
+}  // namespace gk

@@ -1,0 +1,173 @@
+"""Training-step throughput of the GPT-2 step on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_124m]
+
+One step = forward + backward of one 16x1024 micro-batch, global clip at 1.0
+and AdamW (the full hot path). Inputs are synthetic, seeded, and resident in
+device memory before the timed region. Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/sec on 1 MI355X, GPT-2 124M B=16 T=1024 bf16; MFMA util %"
+PEAK_BF16_TFLOPS = 2516.6      # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def model_flops_per_token(cfg, T):
+    """6 N + 6 L d (T + 1): N = parameters except the position table (tied
+    head counted once), attention as causal pairs, forward + backward."""
+    from transformer_lm_step_gpt_amd.inputs import ModelConfig  # noqa: F401
+    d, F, L, Vp = cfg.n_embd, cfg.mlp_hidden, cfg.n_layer, cfg.padded_vocab_size
+    per_layer = 2 * d + 3 * d * d + 3 * d + d * d + d + 2 * d + F * d + F + d * F + d
+    N = Vp * d + L * per_layer + 2 * d
+    if cfg.window_even or cfg.window_odd:
+        pairs = 0.0
+        for l in range(L):
+            W = cfg.window_even if l % 2 == 0 else cfg.window_odd
+            W = W if W and W < T else T
+            pairs += (W * (W + 1) / 2 + (T - W) * W) / T
+        attn = 6 * 2 * d * pairs
+    else:
+        attn = 6 * L * d * (T + 1)
+    return 6 * N + attn
+
+
+def cpu_baseline(w, seq):
+    """Time the float64 CPU oracle on one sequence of the same workload."""
+    from oracle import gpt_oracle as O
+    from transformer_lm_step_gpt_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cfg = w.model
+    rng = np.random.default_rng(0)
+    params = {n: (rng.standard_normal(s) * 0.02 if len(s) == 2 else (np.ones(s) if "ln" in n and n.endswith("weight")
+                                                                       else np.zeros(s)))
+              for n, s, _, _ in O.param_table(cfg)}
+    m = O.zeros_like_params(params)
+    x, y = next(I.batches(w, 1, seq))
+    t0 = time.perf_counter()
+    O.train_step(params, m, m, [(x, y)], cfg, w.lr, 1)
+    dt = time.perf_counter() - t0
+    return {"value": round(seq / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one {seq}-token sequence of {w.name}: float64 forward, backward, clip and AdamW over all "
+                      f"{sum(int(np.prod(s)) for _, s, _, _ in O.param_table(cfg))} parameters, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt2_124m")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-table", action="store_true", help="print per-kernel-class times to stderr")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for {a.gpus}); the multi-GPU data-parallel "
+              "path is a design, not an implementation.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from transformer_lm_step_gpt_amd import inputs as I
+    from transformer_lm_step_gpt_amd.gpt import GPT
+
+    w = I.WORKLOADS[a.workload]
+    cfg = w.model
+    B, T = w.batch, w.seq_len
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    model = GPT(cfg, seed=w.init_seed, device=dev)
+    it = I.batches(w)
+    n_batches = a.warmup + a.steps
+    data = [next(it) for _ in range(min(n_batches, 8))]
+    toks = [(torch.tensor(x, device=dev), torch.tensor(y, device=dev)) for x, y in data]
+    torch.cuda.synchronize()
+
+    step_no = [0]
+
+    def step(i):
+        x, y = toks[i % len(toks)]
+        model.forward_backward(x, y, 1.0, sync=False)
+        step_no[0] += 1
+        model.clip_and_adamw(w.lr, step_no[0], sync=False)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # dominant kernel class: time every class during one untimed step
+    model.set_kernel_timing(-1)
+    model.reset_kernel_timing()
+    step(0)
+    torch.cuda.synchronize()
+    table = model.kernel_timing()
+    dom = max(table, key=lambda r: r["ms"])
+    model.set_kernel_timing(1 << dom["class"])
+    model.reset_kernel_timing()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    timed = model.kernel_timing()[dom["class"]]
+    model.set_kernel_timing(0)
+
+    tokens = a.steps * B * T
+    tps = tokens / dt
+    fpt = model_flops_per_token(cfg, T)
+    mfu = tps * fpt / (PEAK_BF16_TFLOPS * 1e12)
+    is_flop = timed["flops"] > 0
+    avg_ms = timed["ms"] / max(timed["launches"], 1)
+    if is_flop:
+        achieved = timed["flops"] / (timed["ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": timed["name"], "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(avg_ms, 4), "launches": timed["launches"]}
+    else:
+        achieved = timed["bytes"] / (timed["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": timed["name"], "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "avg_launch_ms": round(avg_ms, 4), "launches": timed["launches"]}
+    if a.kernel_table:
+        tot = sum(r["ms"] for r in table)
+        for r in sorted(table, key=lambda r: -r["ms"]):
+            if r["launches"]:
+                rate = (f"{r['flops'] / (r['ms'] * 1e-3) / 1e12:8.1f} TFLOP/s" if r["flops"] else
+                        f"{r['bytes'] / (r['ms'] * 1e-3) / 1e9:8.1f} GB/s") if r["ms"] > 0 else ""
+                print(f"{r['name']:>18s} {r['ms']:9.3f} ms {100 * r['ms'] / tot:5.1f}% x{r['launches']:4d} {rate}",
+                      file=sys.stderr)
+    out = {
+        "metric": METRIC, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(1e3 * dt / a.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg.precision == "bf16" else "fp32",
+        "data": "synthetic (seeded Zipf(1.1) tokens with end-of-text document starts; random-init weights)",
+        "config": {"workload": f"{w.name}: {w.description}", "global_batch": B, "seq_len": T,
+                   "parallelism": "single GPU"},
+        "mfma_util_pct": round(100 * mfu, 2),
+        "model_flops_per_token": fpt,
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, min(T, 256))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

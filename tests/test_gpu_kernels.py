@@ -51,6 +51,10 @@ GEMM_CASES = [
     # (M, N, K, a_kc, b_kc): forward X W^T, dgrad dY W, wgrad dY^T X, plus the fourth orientation
     (77, 45, 133, 1, 1), (300, 200, 520, 1, 1), (130, 70, 96, 1, 0), (64, 96, 300, 0, 0), (45, 130, 77, 0, 1),
     (1, 1, 1, 1, 1), (257, 129, 1025, 1, 0), (128, 256, 512, 1, 1), (256, 128, 1024, 0, 0),
+    # large enough for the 256x256 matrix-core tiles
+    (4096, 4096, 64, 1, 1), (4096, 4096, 64, 1, 0), (4096, 4096, 64, 0, 0), (4000, 4104, 72, 1, 1),
+    # few output tiles and a long K: split-K with a deterministic reduction
+    (256, 384, 4096, 0, 0), (768, 768, 16384, 0, 0), (200, 136, 4104, 0, 0), (136, 200, 4104, 1, 0),
 ]
 
 
@@ -79,8 +83,9 @@ def test_gemm_store(lib, case, bf):
         C = torch.zeros((M, N), dtype=torch.bfloat16 if c_bf else torch.float32, device="cuda")
         lda = K if a_kc else M
         ldb = K if b_kc else N
+        scratch = torch.zeros(16 * M * N, dtype=torch.float32, device="cuda")
         st = lib.gptk_gemm(M, N, K, At.data_ptr(), lda, a_kc, Bt.data_ptr(), ldb, b_kc, C.data_ptr(), N, bf, c_bf,
-                           0, 0, None, None, None, None, None, 0, stream())
+                           0, 0, None, None, None, None, scratch.data_ptr(), scratch.numel(), stream())
         assert st == 0
         torch.cuda.synchronize()
         tol = 8e-3 if c_bf else 2e-5 * math.sqrt(K / 64 + 1)
@@ -90,10 +95,11 @@ def test_gemm_store(lib, case, bf):
 @pytest.mark.parametrize("bf", [0, 1], ids=["fp32", "bf16"])
 @pytest.mark.parametrize("epi", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("act", [0, 1])
-def test_gemm_epilogues(lib, epi, act, bf):
+@pytest.mark.parametrize("shape", [(200, 136, 264), (4096, 4096, 64), (256, 384, 4096)])
+def test_gemm_epilogues(lib, epi, act, bf, shape):
     if act and epi not in (2, 4):
         pytest.skip("activation only matters for epilogues 2 and 4")
-    M, N, K = 200, 136, 264
+    M, N, K = shape
     say(f"gemm epilogue {epi} act {act} bf={bf}")
     rng = np.random.default_rng(epi * 10 + act)
     At, Bt, A, B = gemm_inputs(M, N, K, 1, 1, bf, rng)
@@ -114,8 +120,10 @@ def test_gemm_epilogues(lib, epi, act, bf):
     aux = dev(rng.normal(size=(M, N)), c_bf)
     if epi == 5:
         C.copy_(residt)
+    scratch = torch.zeros(8 * M * N, dtype=torch.float32, device="cuda")
     st = lib.gptk_gemm(M, N, K, At.data_ptr(), K, 1, Bt.data_ptr(), K, 1, C.data_ptr(), N, bf, c_bf, epi, act,
-                       biast.data_ptr(), residt.data_ptr(), aux.data_ptr(), C2.data_ptr(), None, 0, stream())
+                       biast.data_ptr(), residt.data_ptr(), aux.data_ptr(), C2.data_ptr(), scratch.data_ptr(),
+                       scratch.numel(), stream())
     assert st == 0
     torch.cuda.synchronize()
     tol = 1e-2 if c_bf else 3e-5

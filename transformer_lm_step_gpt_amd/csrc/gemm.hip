@@ -105,9 +105,8 @@ void gemm_simple(const Gemm& g, hipStream_t s) {
 
 namespace gk {
 void gemm(const Gemm& g, float* splitk_scratch, size_t splitk_floats, hipStream_t s) {
-    (void)splitk_scratch;
-    (void)splitk_floats;
-    gemm_simple(g, s);
+    if (gemm_mfma_ok(g)) gemm_mfma(g, splitk_scratch, splitk_floats, s);
+    else gemm_simple(g, s);
 }
 const char* gemm_last_kernel_name() { return "gemm_simple_kernel"; }
 }  // namespace gk

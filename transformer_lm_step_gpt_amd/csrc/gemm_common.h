@@ -28,5 +28,7 @@ GPT_DEV void epilogue_store(const Gemm& g, int m, int n, float acc) {
 }
 
 void gemm_simple(const Gemm& g, hipStream_t s);
+bool gemm_mfma_ok(const Gemm& g);
+void gemm_mfma(const Gemm& g, float* scratch, size_t nscratch, hipStream_t s);
 
 }  // namespace gk

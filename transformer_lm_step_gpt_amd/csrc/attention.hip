@@ -281,7 +281,14 @@ void attention_bwd_simple(const Attn& a, hipStream_t s) {
     else bwd_simple_t<float>(a, s);
 }
 
-void attention_fwd(const Attn& a, hipStream_t s) { attention_fwd_simple(a, s); }
-void attention_bwd(const Attn& a, hipStream_t s) { attention_bwd_simple(a, s); }
+bool attention_fwd_mfma(const Attn& a, hipStream_t s);
+bool attention_bwd_mfma(const Attn& a, hipStream_t s);
+
+void attention_fwd(const Attn& a, hipStream_t s) {
+    if (!attention_fwd_mfma(a, s)) attention_fwd_simple(a, s);
+}
+void attention_bwd(const Attn& a, hipStream_t s) {
+    if (!attention_bwd_mfma(a, s)) attention_bwd_simple(a, s);
+}
 
 }  // namespace gk

@@ -55,6 +55,9 @@ GEMM_CASES = [
     (4096, 4096, 64, 1, 1), (4096, 4096, 64, 1, 0), (4096, 4096, 64, 0, 0), (4000, 4104, 72, 1, 1),
     # few output tiles and a long K: split-K with a deterministic reduction
     (256, 384, 4096, 0, 0), (768, 768, 16384, 0, 0), (200, 136, 4104, 0, 0), (136, 200, 4104, 1, 0),
+    # ragged rows/columns with K a multiple of 32 (matrix-core path, clamped edge loads)
+    (300, 200, 512, 1, 1), (200, 136, 4096, 0, 0), (136, 200, 4096, 1, 0), (4000, 4104, 64, 1, 1),
+    (1000, 72, 96, 1, 0), (72, 1000, 96, 0, 0), (33, 8, 64, 1, 0), (8, 40, 64, 0, 0), (5000, 65, 384, 1, 1),
 ]
 
 

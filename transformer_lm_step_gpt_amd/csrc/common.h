@@ -55,16 +55,22 @@ GPT_DEV double wave_sum_d(double v) {
 
 // ---------------------------------------------------------------- activations
 
+// tanh(u) = 1 - 2 / (1 + e^(2u)); saturates to +-1 without overflow issues
+// (e^(2u) = inf gives 1, e^(2u) = 0 gives -1). Absolute error ~1e-7.
+GPT_DEV float tanh_exp2(float u) {
+    return 1.0f - 2.0f / (1.0f + exp2f(2.8853900817779268f * u));   // 2 log2(e) u
+}
+
 // GELU, tanh approximation: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
 GPT_DEV float gelu_tanh_f(float x) {
     const float c = 0.7978845608028654f;
     float u = c * (x + 0.044715f * x * x * x);
-    return 0.5f * x * (1.0f + tanhf(u));
+    return 0.5f * x * (1.0f + tanh_exp2(u));
 }
 GPT_DEV float gelu_tanh_grad_f(float x) {
     const float c = 0.7978845608028654f;
     float u = c * (x + 0.044715f * x * x * x);
-    float t = tanhf(u);
+    float t = tanh_exp2(u);
     return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * c * (1.0f + 3.0f * 0.044715f * x * x);
 }
 GPT_DEV float relu2_f(float x) { float r = fmaxf(x, 0.0f); return r * r; }
@@ -75,4 +81,4 @@ enum ActKind { ACT_GELU = 0, ACT_RELU2 = 1 };
 template <int ACT> GPT_DEV float act_f(float x) { return ACT == ACT_RELU2 ? relu2_f(x) : gelu_tanh_f(x); }
 template <int ACT> GPT_DEV float act_grad_f(float x) { return ACT == ACT_RELU2 ? relu2_grad_f(x) : gelu_tanh_grad_f(x); }
 
-static inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+__host__ __device__ inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }

@@ -4,113 +4,192 @@
 // lecture notes' "Раздел 2. Сделаем быстро", rebuilt for CDNA4).
 //
 // Structure
-//   * 256 threads = 4 wavefronts in a WGM x WGN grid; each wavefront owns a
-//     (BM/WGM) x (BN/WGN) sub-tile made of 32x32 MFMA fragments.
-//   * Both operands are staged through LDS as [row][k] tiles (row = m for A,
-//     n for B) so that every lane reads its 8 consecutive k values of a
-//     fragment with one 16-byte LDS read. Rows are padded by 16 bytes and the
-//     16-byte chunks of a row are XOR-swizzled by (row / 8) to keep both the
-//     writes and the fragment reads free of bank conflicts.
-//   * Operands stored k-contiguous in memory (activations X and weights W of
-//     X W^T) are copied in 16-byte chunks. Operands stored row-contiguous
-//     (the dY and X of dW = dY^T X, and W in dX = dY W) are read as two
-//     16-byte rows (k, k+1) of 8 consecutive rows each, and written to LDS as
-//     eight 4-byte (k, k+1) pairs: the transposition happens in registers.
-//   * Two LDS buffers: the next k-tile is fetched from global memory into
-//     registers while the current one feeds the matrix cores.
+//   * 256 threads = 4 wavefronts in a 2 x 2 grid; each wavefront owns a
+//     (BM/2) x (BN/2) sub-tile made of 32x32 MFMA fragments.
+//   * Global -> LDS copies use the 16-byte LDS-DMA load (each lane's 16
+//     bytes land at LDS base + 16 * lane), so no registers are spent on
+//     staging and NS - 1 k-tiles are in flight at once (a ring of NS LDS
+//     stages; a k-tile is waited for with s_waitcnt vmcnt only when consumed).
+//   * An operand stored k-contiguous (X and W of X W^T) is kept as a
+//     [row][BK] tile; a fragment (8 consecutive k of one row per lane) is one
+//     16-byte LDS read.
+//   * An operand stored row-contiguous (dY and X of dW = dY^T X, W of
+//     dX = dY W) is kept as it is in memory, a [BK][rows] tile; fragments are
+//     built with the transposing LDS read ds_read_b64_tr_b16: in each group of
+//     16 lanes, lane j addresses 4 consecutive rows of k-row k0 + j/4 and lane
+//     i receives k0..k0+3 of row i. Two such reads give the 8 k values.
+//   * 16-byte chunks of every LDS row are XOR-swizzled (by the row index for
+//     [row][BK] tiles, by the k index for [BK][rows] tiles); the DMA lanes
+//     pick the global chunk that belongs at their LDS slot, so both the
+//     copies and the fragment reads avoid bank conflicts.
 //   * Split-K (grid.z) writes fp32 partial tiles; a second kernel sums the
 //     slices in a fixed order and applies the epilogue (deterministic).
+//   * Workgroup i runs on XCD i % 8; tiles are renumbered so that each XCD
+//     owns a contiguous, row-major range of output tiles (shared A panels in
+//     its L2).
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
 
+#include <cstdio>
+#include <cstdlib>
+
 namespace gk {
 
+namespace {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-GPT_DEV int swz(int row, int kc, int ch) { return kc ^ ((row >> 3) & (ch - 1)); }
+// s_waitcnt with vmcnt <= n and the other counters unconstrained (gfx9 encoding)
+template <int N>
+GPT_DEV void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
+// Workgroup barrier without the release fence of __syncthreads (which would
+// wait for every in-flight LDS-DMA load). Each wave has already waited, with
+// s_waitcnt vmcnt, for the DMA loads of the tile it is about to read; after
+// the barrier every wave's loads of that tile are complete.
+GPT_DEV void barrier_no_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+GPT_DEV void dma16(const void* g, bf16* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+
+// ---- [row][BK] tile of an operand stored k-contiguous (element (r, k) at base[r * ld + k])
 template <int R, int BK>
-struct DirectTile {   // element (r, k) at base[r * ld + k]
-    static constexpr int CH = BK / 8, NCH = R * CH, PER = (NCH + 255) / 256, S = BK + 8;
-    u32x4 reg[PER];
-    GPT_DEV void load(const bf16* base, int64_t ld, int row0, int rows, int k0, int K) {
+struct RowTile {
+    static constexpr int CH = BK / 8;                 // 16-byte chunks per row
+    static constexpr int ROWS_PER_DMA = 64 / CH;      // rows filled by one wave-wide DMA (1 KiB)
+    static constexpr int DMAS = R / ROWS_PER_DMA;     // per tile
+    static constexpr int PER_WAVE = DMAS / 4;
+    static constexpr int BYTES = R * BK * 2;
+    static constexpr int READS_PER_FRAG = 1;
+    static_assert(DMAS % 4 == 0, "tile too small for 4 waves");
+    GPT_DEV static int swz(int r) { return CH == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
+    // issue this wave's DMAs for rows [row0, row0 + R), k [k0, k0 + BK)
+    GPT_DEV static void load(bf16* tile, const bf16* base, int64_t ld, int row0, int rows, int k0, int w, int lane) {
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            int c = threadIdx.x + 256 * p;
-            int r = c / CH, kc = c % CH;
-            int gr = row0 + r, gk = k0 + kc * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if ((NCH % 256 == 0 || c < NCH) && gr < rows && gk < K)
-                v = *reinterpret_cast<const u32x4*>(base + (int64_t)gr * ld + gk);
-            reg[p] = v;
+        for (int p = 0; p < PER_WAVE; ++p) {
+            const int d = w * PER_WAVE + p;
+            const int r = d * ROWS_PER_DMA + lane / CH;
+            const int kc = (lane % CH) ^ swz(r);
+            const int gr = min(row0 + r, rows - 1);    // rows past the end feed only unstored outputs
+            dma16(base + (int64_t)gr * ld + k0 + kc * 8, tile + d * 512);
         }
     }
-    GPT_DEV void store(bf16* lds) const {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            int c = threadIdx.x + 256 * p;
-            if (NCH % 256 != 0 && c >= NCH) continue;
-            int r = c / CH, kc = c % CH;
-            *reinterpret_cast<u32x4*>(lds + r * S + swz(r, kc, CH) * 8) = reg[p];
-        }
+    // 8 consecutive k (16*ks + 8*hk ...) of row r
+    GPT_DEV static bf16x8 frag(const bf16* tile, int r, int ks, int hk) {
+        const int kc = 2 * ks + hk;
+        return *reinterpret_cast<const bf16x8*>(tile + r * BK + ((kc ^ swz(r)) << 3));
     }
 };
 
+// ---- [BK][row] tile of an operand stored row-contiguous (element (r, k) at base[k * ld + r])
 template <int R, int BK>
-struct TransTile {    // element (r, k) at base[k * ld + r]; rows % 8 == 0
-    static constexpr int CH = BK / 8, RG = R / 8, KP = BK / 2, NU = RG * KP, PER = (NU + 255) / 256, S = BK + 8;
-    u32x4 reg[PER][2];
-    GPT_DEV void load(const bf16* base, int64_t ld, int row0, int rows, int k0, int K) {
+struct ColTile {
+    static constexpr int CH = R / 8;                  // 16-byte chunks per k-row
+    static constexpr int KROWS_PER_DMA = 64 / CH;
+    static constexpr int DMAS = BK / KROWS_PER_DMA;
+    static constexpr int PER_WAVE = DMAS / 4;
+    static constexpr int BYTES = R * BK * 2;
+    static constexpr int READS_PER_FRAG = 2;
+    static_assert(CH >= 16 && DMAS % 4 == 0, "unsupported tile");
+    GPT_DEV static int swz(int k) { return (k & 3) << 2; }
+    GPT_DEV static void load(bf16* tile, const bf16* base, int64_t ld, int row0, int rows, int k0, int w, int lane) {
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            int u = threadIdx.x + 256 * p;
-            int rg = u % RG, kp = u / RG;
-            int gr = row0 + rg * 8, gk = k0 + 2 * kp;
-            u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-            if ((NU % 256 == 0 || u < NU) && gr < rows) {
-                if (gk < K) v0 = *reinterpret_cast<const u32x4*>(base + (int64_t)gk * ld + gr);
-                if (gk + 1 < K) v1 = *reinterpret_cast<const u32x4*>(base + (int64_t)(gk + 1) * ld + gr);
-            }
-            reg[p][0] = v0;
-            reg[p][1] = v1;
+        for (int p = 0; p < PER_WAVE; ++p) {
+            const int d = w * PER_WAVE + p;
+            const int k = d * KROWS_PER_DMA + lane / CH;
+            const int c = (lane % CH) ^ swz(k);
+            const int gr = min(row0 + c * 8, rows - 8);   // rows % 8 == 0
+            dma16(base + (int64_t)(k0 + k) * ld + gr, tile + d * 512);
         }
     }
-    GPT_DEV void store(bf16* lds) const {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            int u = threadIdx.x + 256 * p;
-            if (NU % 256 != 0 && u >= NU) continue;
-            int rg = u % RG, kp = u / RG;
-            int k = 2 * kp, kc = k >> 3, ko = k & 7;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                uint32_t lo = (reg[p][0][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-                uint32_t hi = (reg[p][1][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-                int r = rg * 8 + i;
-                *reinterpret_cast<uint32_t*>(lds + r * S + swz(r, kc, CH) * 8 + ko) = lo | (hi << 16);
-            }
-        }
+    GPT_DEV static s16x4 tr_read(const bf16* tile, int k, int r) {
+        const bf16* p = tile + k * R + (((r >> 3) ^ swz(k)) << 3) + (r & 7);
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+    }
+    // fragment of rows rb..rb+31: lane l gets k = 16*ks + 8*(l/32) + e of row rb + l%32
+    GPT_DEV static bf16x8 frag(const bf16* tile, int rb, int ks, int lane) {
+        const int g = lane >> 4, j = lane & 15;
+        const int r = rb + 16 * (g & 1) + 4 * (j & 3);
+        const int k = 16 * ks + 8 * (g >> 1) + (j >> 2);
+        s16x4 lo = tr_read(tile, k, r);
+        s16x4 hi = tr_read(tile, k + 4, r);
+        u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        u32x4 v = {l2[0], l2[1], h2[0], h2[1]};
+        return __builtin_bit_cast(bf16x8, v);
     }
 };
 
-template <int R, int BK, bool KC>
-using Tile = typename std::conditional<KC, DirectTile<R, BK>, TransTile<R, BK>>::type;
+template <bool KC, int R, int BK>
+struct OpTile;
+template <int R, int BK>
+struct OpTile<true, R, BK> : RowTile<R, BK> {
+    GPT_DEV static bf16x8 get(const bf16* t, int rb, int ks, int lane) {
+        return RowTile<R, BK>::frag(t, rb + (lane & 31), ks, lane >> 5);
+    }
+};
+template <int R, int BK>
+struct OpTile<false, R, BK> : ColTile<R, BK> {
+    GPT_DEV static bf16x8 get(const bf16* t, int rb, int ks, int lane) { return ColTile<R, BK>::frag(t, rb, ks, lane); }
+};
+
+}  // namespace
+
+// One half-step: the FM x FN products of (ca, cb), with the fragment reads of
+// the next half-step (into na, nb) spread between them in program order so the
+// LDS latency hides under the matrix cores.
+template <int FM, int FN, class TA, class TB, bool LOAD>
+__device__ __attribute__((always_inline)) inline void half_step(f32x16 (&acc)[FM][FN], const bf16x8 (&ca)[FM],
+                                                               const bf16x8 (&cb)[FN], bf16x8 (&na)[FM],
+                                                               bf16x8 (&nb)[FN], const bf16* as, const bf16* bs, int wm,
+                                                               int wn, int ksn, int lane) {
+    constexpr int NF = FM + FN, P = FM * FN;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        acc[p / FN][p % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[p / FN], cb[p % FN], acc[p / FN][p % FN], 0, 0, 0);
+        if constexpr (LOAD) {
+            if ((p * NF) / P != ((p + 1) * NF) / P) {
+                const int f = (p * NF) / P;
+                if (f < FM) na[f] = TA::get(as, wm + 32 * f, ksn, lane);
+                else nb[f - FM] = TB::get(bs, wn + 32 * (f - FM), ksn, lane);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
 
 // SPLIT: write fp32 partial sums to part[z][M][N] instead of the epilogue.
-template <int BM, int BN, int BK, int WGM, int WGN, bool AKC, bool BKC, int EPI, typename TC, bool SPLIT>
+template <int BM, int BN, int BK, int NS, bool AKC, bool BKC, int EPI, typename TC, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(Gemm g, int kps, float* part) {
-    constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32, S = BK + 8, CH = BK / 8;
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+    using TA = OpTile<AKC, BM, BK>;
+    using TB = OpTile<BKC, BN, BK>;
+    constexpr int STAGE = (TA::BYTES + TB::BYTES) / 2;      // bf16 elements per stage
+    constexpr int LPT = TA::PER_WAVE + TB::PER_WAVE;        // DMAs per lane per stage
+    static_assert(NS >= 2 && NS <= 4, "stages");
+    extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
     bf16* smem = reinterpret_cast<bf16*>(smem_raw);
-    bf16* As[2] = {smem, smem + (BM + BN) * S};
-    bf16* Bs[2] = {smem + BM * S, smem + (BM + BN) * S + BM * S};
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    const int wm = (w / WGN) * WM, wn = (w % WGN) * WN;
+    const int tn = ceil_div(g.N, BN), ntiles = tn * ceil_div(g.M, BM);
+    const int lin = blockIdx.x, xcd = lin & 7, q8 = ntiles >> 3, r8 = ntiles & 7;
+    const int tile = xcd * q8 + min(xcd, r8) + (lin >> 3);
+    const int m0 = (tile / tn) * BM, n0 = (tile % tn) * BN;
+    const int wm = (w >> 1) * WM, wn = (w & 1) * WN;
     const int kb = blockIdx.z * kps;
-    const int ke = min(g.K, kb + kps);
+    const int nk = max(0, (min(g.K, kb + kps) - kb) / BK);    // K and kps are multiples of BK
     const bf16* A = (const bf16*)g.A;
     const bf16* B = (const bf16*)g.B;
 
@@ -122,65 +201,94 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(Gemm g, int kps, floa
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    Tile<BM, BK, AKC> ta;
-    Tile<BN, BK, BKC> tb;
-    ta.load(A, g.lda, m0, g.M, kb, ke);
-    tb.load(B, g.ldb, n0, g.N, kb, ke);
-    ta.store(As[0]);
-    tb.store(Bs[0]);
-    __syncthreads();
-    int buf = 0;
-    const int lr = lane & 31, lk = lane >> 5;
-    for (int k0 = kb; k0 < ke; k0 += BK) {
-        const bool more = k0 + BK < ke;
-        if (more) {
-            ta.load(A, g.lda, m0, g.M, k0 + BK, ke);
-            tb.load(B, g.ldb, n0, g.N, k0 + BK, ke);
+    int issued = 0;   // tiles 0 .. issued-1 have been handed to the LDS-DMA engine
+    auto issue_next = [&]() {
+        if (issued < nk) {
+            bf16* st = smem + (issued % NS) * STAGE;
+            TA::load(st, A, g.lda, m0, g.M, kb + issued * BK, w, lane);
+            TB::load(st + TA::BYTES / 2, B, g.ldb, n0, g.N, kb + issued * BK, w, lane);
+            ++issued;
         }
-        const bf16* as = As[buf];
-        const bf16* bs = Bs[buf];
+    };
+    // wait until tile u is in LDS for every wave: at most (tiles issued after u) x LPT DMAs pending
+    auto wait_tile = [&](int u) {
+        const int ahead = issued - 1 - u;
+        if (ahead >= 2) wait_vmcnt<2 * LPT>();
+        else if (ahead == 1) wait_vmcnt<LPT>();
+        else wait_vmcnt<0>();
+        barrier_no_fence();
+    };
+    auto frags = [&](int t, int ks, bf16x8* a, bf16x8* b) {
+        const bf16* as = smem + (t % NS) * STAGE;
+        const bf16* bs = as + TA::BYTES / 2;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            bf16x8 a[FM], b[FN];
-            const int kc = kk * 2 + lk;
+        for (int i = 0; i < FM; ++i) a[i] = TA::get(as, wm + 32 * i, ks, lane);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                int r = wm + i * 32 + lr;
-                a[i] = *reinterpret_cast<const bf16x8*>(as + r * S + swz(r, kc, CH) * 8);
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                int r = wn + j * 32 + lr;
-                b[j] = *reinterpret_cast<const bf16x8*>(bs + r * S + swz(r, kc, CH) * 8);
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        if (more) {
-            ta.store(As[buf ^ 1]);
-            tb.store(Bs[buf ^ 1]);
-        }
-        __syncthreads();
-        buf ^= 1;
+        for (int j = 0; j < FN; ++j) b[j] = TB::get(bs, wn + 32 * j, ks, lane);
+    };
+
+    for (int t = 0; t < NS - 1; ++t) issue_next();
+
+    // Software pipeline over half k-tiles (BK = 32: two 16-deep steps per tile):
+    //   reads of step 1 of tile t          | products of step 0 of tile t
+    //   wait + barrier for tile t+1; DMA of tile t+NS-1 into the stage of tile
+    //   t-1 (every wave finished reading it before this barrier)
+    //   reads of step 0 of tile t+1        | products of step 1 of tile t
+    static_assert(BK == 32 && NS <= 4, "two 16-deep steps per k-tile; vmcnt bookkeeping for <= 2 tiles ahead");
+    bf16x8 a0[FM], b0[FN], a1[FM], b1[FN];
+    if (nk > 0) {
+        wait_tile(0);
+        frags(0, 0, a0, b0);
     }
+    for (int t = 0; t < nk; ++t) {
+        {
+            const bf16* as = smem + (t % NS) * STAGE;
+            half_step<FM, FN, TA, TB, true>(acc, a0, b0, a1, b1, as, as + TA::BYTES / 2, wm, wn, 1, lane);
+        }
+        if (t + 1 < nk) {
+            wait_tile(t + 1);
+            issue_next();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            // on the last tile this prefetch reads a stage that holds no new tile;
+            // the values are never used
+            const bf16* as = smem + ((t + 1) % NS) * STAGE;
+            half_step<FM, FN, TA, TB, true>(acc, a1, b1, a0, b0, as, as + TA::BYTES / 2, wm, wn, 0, lane);
+        }
+    }
+
     // accumulator fragment: lane holds column (lane % 32), rows 8*(e/4) + 4*(lane/32) + e%4
+    const int lr = lane & 31, lk = lane >> 5;
+    const bool full = (m0 + BM <= g.M) && (n0 + BN <= g.N);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn + j * 32 + lr;
+        float bj = 0.f;
+        if constexpr (!SPLIT && (EPI == EPI_BIAS || EPI == EPI_BIAS_ACT || EPI == EPI_BIAS_RESID))
+            bj = col < g.N ? g.bias[col] : 0.f;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn + j * 32 + lr;
-            if (col >= g.N) continue;
+        for (int i = 0; i < FM; ++i) {
+            const int rb = m0 + wm + i * 32 + 4 * lk;
+            if (full) {
+                if constexpr (SPLIT) {
+                    float* p = part + ((int64_t)blockIdx.z * g.M + rb) * g.N + col;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wm + i * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
-                if (row >= g.M) continue;
-                if constexpr (SPLIT) part[((int64_t)blockIdx.z * g.M + row) * g.N + col] = acc[i][j][e];
-                else epilogue_store<TC, EPI>(g, row, col, acc[i][j][e]);
+                    for (int e = 0; e < 16; ++e) p[(int64_t)(8 * (e >> 2) + (e & 3)) * g.N] = acc[i][j][e];
+                } else {
+                    epilogue_frag<TC, EPI>(g, rb, col, acc[i][j], bj);
+                }
+            } else if (col < g.N) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = rb + 8 * (e >> 2) + (e & 3);
+                    if (row >= g.M) continue;
+                    if constexpr (SPLIT) part[((int64_t)blockIdx.z * g.M + row) * g.N + col] = acc[i][j][e];
+                    else epilogue_store<TC, EPI>(g, row, col, acc[i][j][e]);
+                }
             }
         }
+    }
 }
 
 template <typename TC, int EPI>
@@ -195,13 +303,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Gemm g, const float*
 
 // ------------------------------------------------------------------ dispatch
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool AKC, bool BKC>
+template <int BM, int BN, int BK, int NS, bool AKC, bool BKC>
 struct Launcher {
-    static constexpr size_t LDS = (size_t)2 * (BM + BN) * (BK + 8) * sizeof(bf16);
+    static constexpr size_t LDS = (size_t)NS * (BM + BN) * BK * sizeof(bf16);
+    static_assert(LDS <= 160 * 1024, "LDS budget");
 
     template <int EPI, typename TC, bool SPLIT>
     static void go(const Gemm& g, dim3 grid, int kps, float* part, hipStream_t s) {
-        auto k = gemm_mfma_kernel<BM, BN, BK, WGM, WGN, AKC, BKC, EPI, TC, SPLIT>;
+        auto k = gemm_mfma_kernel<BM, BN, BK, NS, AKC, BKC, EPI, TC, SPLIT>;
         static bool attr = false;
         if (!attr) {
             (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
@@ -211,7 +320,7 @@ struct Launcher {
     }
 
     static void run(const Gemm& g, int splits, float* part, hipStream_t s) {
-        dim3 grid(ceil_div(g.N, BN), ceil_div(g.M, BM), splits);
+        dim3 grid(ceil_div(g.N, BN) * ceil_div(g.M, BM), 1, splits);
         int kps = ceil_div(ceil_div(g.K, splits), BK) * BK;
         if (splits > 1) {
             go<EPI_STORE, float, true>(g, grid, kps, part, s);
@@ -244,33 +353,61 @@ struct Launcher {
     }
 };
 
+// Tile configurations (BM, BN, BK, stages).
+enum GemmCfg { CFG_256_256_32 = 0, CFG_128_256_32, CFG_128_128_32, CFG_256_128_32, CFG_COUNT };
+static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256};
+static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128};
+static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32};
+
+template <bool AKC, bool BKC>
+static void launch_cfg(int cfg, const Gemm& g, int splits, float* scratch, hipStream_t s) {
+    switch (cfg) {
+        case CFG_256_256_32: Launcher<256, 256, 32, 4, AKC, BKC>::run(g, splits, scratch, s); break;
+        case CFG_128_256_32: Launcher<128, 256, 32, 4, AKC, BKC>::run(g, splits, scratch, s); break;
+        case CFG_128_128_32: Launcher<128, 128, 32, 4, AKC, BKC>::run(g, splits, scratch, s); break;
+        case CFG_256_128_32: Launcher<256, 128, 32, 4, AKC, BKC>::run(g, splits, scratch, s); break;
+    }
+}
+
+// Tuning override for measurements: GPT_GEMM_FORCE="cfg,splits" (cfg index as
+// in GemmCfg; splits 0 = automatic).
+static bool forced(int* cfg, int* splits) {
+    static int state = -1, fc = 0, fs = 0;
+    if (state < 0) {
+        const char* e = getenv("GPT_GEMM_FORCE");
+        state = (e && sscanf(e, "%d,%d", &fc, &fs) == 2 && fc >= 0 && fc < CFG_COUNT) ? 1 : 0;
+    }
+    if (state) { *cfg = fc; *splits = fs; }
+    return state == 1;
+}
+
 template <bool AKC, bool BKC>
 static void run_layout(const Gemm& g, float* scratch, size_t nscratch, hipStream_t s) {
-    const int64_t t256 = (int64_t)ceil_div(g.M, 256) * ceil_div(g.N, 256);
-    const int64_t t128 = (int64_t)ceil_div(g.M, 128) * ceil_div(g.N, 128);
     const int64_t mn = (int64_t)g.M * g.N;
-    // fill the 256 compute units: large tiles when there are enough of them,
-    // otherwise 128x128, and split K when even those leave the chip idle
-    if (t256 >= 240) {
-        Launcher<256, 256, 32, 2, 2, AKC, BKC>::run(g, 1, nullptr, s);
-        return;
+    int cfg, splits = 0;
+    if (!forced(&cfg, &splits)) {
+        const int64_t t256 = (int64_t)ceil_div(g.M, 256) * ceil_div(g.N, 256);
+        cfg = t256 >= 240 ? CFG_256_256_32 : CFG_128_128_32;
     }
-    int splits = 1;
-    if (t128 < 200 && g.K >= 2048 && scratch) {
-        splits = (int)std::min<int64_t>(16, (512 + t128 - 1) / t128);
-        while (splits > 1 && ((size_t)splits * mn > nscratch || g.K / splits < 256)) --splits;
+    if (g.K % cfg_bk[cfg]) cfg = CFG_128_128_32;
+    const int64_t tiles = (int64_t)ceil_div(g.M, cfg_bm[cfg]) * ceil_div(g.N, cfg_bn[cfg]);
+    if (splits <= 0) {
+        splits = 1;
+        if (tiles < 200 && g.K >= 2048) splits = (int)std::min<int64_t>(16, (512 + tiles - 1) / tiles);
     }
-    Launcher<128, 128, 32, 2, 2, AKC, BKC>::run(g, splits, scratch, s);
+    if (!scratch) splits = 1;
+    while (splits > 1 && ((size_t)splits * mn > nscratch || g.K / splits < 256)) --splits;
+    launch_cfg<AKC, BKC>(cfg, g, splits, scratch, s);
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 bool gemm_mfma_ok(const Gemm& g) {
-    if (!g.in_bf || g.K % 8) return false;
+    if (!g.in_bf || g.K % 32) return false;
     if (!aligned16(g.A) || !aligned16(g.B)) return false;
     if (g.lda % 8 || g.ldb % 8) return false;
-    if (!g.a_kc && g.M % 8) return false;
-    if (!g.b_kc && g.N % 8) return false;
+    if (!g.a_kc && (g.M % 8 || g.M < 8)) return false;
+    if (!g.b_kc && (g.N % 8 || g.N < 8)) return false;
     if (!g.a_kc && g.b_kc) return false;     // orientation not used by the training step
     return true;
 }

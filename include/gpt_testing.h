@@ -43,12 +43,13 @@ gpt_status gptk_attention(int32_t backward, int32_t B, int32_t T, int32_t H, int
 
 /* LayerNorm over rows of width d with biased variance. Forward: y (act),
  * mean, rstd. Backward: dres = (overwrite ? 0 : dres) + dx, optional bf16
- * copy dres_lp, dg += sum dy xhat, db += sum dy; partial holds
+ * copy dres_lp, dg += sum dy xhat, db += sum dy, and (dcol nullable) dcol +=
+ * column sums of the resulting dres; partial holds
  * gptk_layernorm_partial_floats(M, d) floats. */
 gpt_status gptk_layernorm(int32_t backward, int32_t M, int32_t d, float eps, const float* x, const float* g,
                           const float* b, void* y, float* mean, float* rstd, const float* dy, float* dres,
-                          void* dres_lp, int32_t overwrite, float* dg, float* db, float* partial, int32_t bf16,
-                          void* stream);
+                          void* dres_lp, int32_t overwrite, float* dg, float* db, float* dcol, float* partial,
+                          int32_t bf16, void* stream);
 int64_t gptk_layernorm_partial_floats(int32_t M, int32_t d);
 
 /* Fused softmax cross-entropy on logits z [M, Vp] (act, overwritten in place

@@ -214,7 +214,7 @@ def test_attention_fwd_bwd(lib, case, bf):
 # ---------------------------------------------------------------- LayerNorm
 
 @pytest.mark.parametrize("bf", [0, 1], ids=["fp32", "bf16"])
-@pytest.mark.parametrize("M,d", [(7, 64), (130, 768), (65, 384), (33, 32), (200, 2048)])
+@pytest.mark.parametrize("M,d", [(7, 64), (130, 768), (65, 384), (33, 32), (200, 2048), (3000, 768), (70, 1000)])
 def test_layernorm(lib, M, d, bf):
     say(f"layernorm M={M} d={d} bf={bf}")
     rng = np.random.default_rng(M + d)
@@ -228,7 +228,8 @@ def test_layernorm(lib, M, d, bf):
     rstd = torch.zeros(M, dtype=torch.float32, device="cuda")
     s = stream()
     assert lib.gptk_layernorm(0, M, d, 1e-5, xt.data_ptr(), gt.data_ptr(), bt.data_ptr(), y.data_ptr(),
-                              mean.data_ptr(), rstd.data_ptr(), None, None, None, 0, None, None, None, bf, s) == 0
+                              mean.data_ptr(), rstd.data_ptr(), None, None, None, 0, None, None, None, None, bf,
+                              s) == 0
     yref, cache = O.layernorm_fwd(x, g, b, 1e-5)
     torch.cuda.synchronize()
     assert relmax(host(y), yref) < (8e-3 if bf else 1e-5)
@@ -239,13 +240,15 @@ def test_layernorm(lib, M, d, bf):
     dlp = torch.zeros((M, d), dtype=torch.bfloat16, device="cuda")
     dg = torch.full((d,), 0.5, dtype=torch.float32, device="cuda")
     db = torch.full((d,), -0.25, dtype=torch.float32, device="cuda")
+    dcol = torch.full((d,), 0.125, dtype=torch.float32, device="cuda")
     part = torch.zeros(int(lib.gptk_layernorm_partial_floats(M, d)), dtype=torch.float32, device="cuda")
     assert lib.gptk_layernorm(1, M, d, 1e-5, xt.data_ptr(), gt.data_ptr(), None, None, mean.data_ptr(),
                               rstd.data_ptr(), dyt.data_ptr(), dres.data_ptr(), dlp.data_ptr() if bf else None, 0,
-                              dg.data_ptr(), db.data_ptr(), part.data_ptr(), bf, s) == 0
+                              dg.data_ptr(), db.data_ptr(), dcol.data_ptr(), part.data_ptr(), bf, s) == 0
     torch.cuda.synchronize()
     dx, dgr, dbr = O.layernorm_bwd(host(dyt), cache, g)
     assert relmax(host(dres), dres0 + dx) < 1e-5
+    assert relmax(host(dcol), 0.125 + (dres0 + dx).sum(0)) < 1e-5
     assert relmax(host(dg), 0.5 + dgr) < 1e-5
     assert relmax(host(db), -0.25 + dbr) < 1e-5
     if bf:
@@ -337,7 +340,7 @@ def test_embedding_backward(lib, B, T, V, kind):
 
 
 @pytest.mark.parametrize("bf", [0, 1], ids=["fp32", "bf16"])
-@pytest.mark.parametrize("M,N", [(1, 5), (300, 768), (1000, 2304), (129, 3072)])
+@pytest.mark.parametrize("M,N", [(1, 5), (300, 768), (1000, 2304), (129, 3072), (5000, 3072), (77, 13)])
 def test_colsum(lib, M, N, bf):
     rng = np.random.default_rng(M + N)
     Yt = dev(rng.normal(size=(M, N)), bf)

@@ -599,7 +599,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
     {
         Timed t(h, KC_LN_BWD, 0, (double)M * d * (4 * 3 + ab) + 8.0 * M);
         gk::layernorm_bwd(bf, w.dln, w.x_fin, meanf, rstdf, P(h, tb.lnf_w), w.dres, bf ? w.dres_lp : nullptr, true,
-                          G(h, tb.lnf_w), G(h, tb.lnf_b), w.ln_partial, M, d, st);
+                          G(h, tb.lnf_w), G(h, tb.lnf_b), G(h, tb.layers[L - 1].mp_b), w.ln_partial, M, d, st);
     }
     for (int l = L - 1; l >= 0; --l) {
         const LayerIdx& li = tb.layers[l];
@@ -616,10 +616,6 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
             run_gemm(h, KC_GEMM_WGRAD, g2);
         }
         {
-            Timed t(h, KC_COLSUM, 0, 4.0 * M * d);
-            gk::colsum(false, w.dres, d, M, d, G(h, li.mp_b), w.cs_partial, st);
-        }
-        {
             gk::Gemm g = mk_gemm(h, M, d, F, w.dh, F, true, Wop(h, li.fc_w), d, false, w.dln, d, false, gk::EPI_STORE);
             run_gemm(h, KC_GEMM_DGRAD, g);
             gk::Gemm g2 = mk_gemm(h, F, d, M, w.dh, F, false, w.ln2[l], d, false, G(h, li.fc_w), d, false, gk::EPI_ACCUM);
@@ -632,7 +628,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         {
             Timed t(h, KC_LN_BWD, 0, (double)M * d * (4 * 4 + ab) + 8.0 * M);
             gk::layernorm_bwd(bf, w.dln, w.x_mid[l], mean2, rstd2, P(h, li.ln2_w), w.dres, bf ? w.dres_lp : nullptr,
-                              false, G(h, li.ln2_w), G(h, li.ln2_b), w.ln_partial, M, d, st);
+                              false, G(h, li.ln2_w), G(h, li.ln2_b), G(h, li.proj_b), w.ln_partial, M, d, st);
         }
         // attention branch
         {
@@ -640,10 +636,6 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
             run_gemm(h, KC_GEMM_DGRAD, g);
             gk::Gemm g2 = mk_gemm(h, d, d, M, dR, d, false, w.att[l], d, false, G(h, li.proj_w), d, false, gk::EPI_ACCUM);
             run_gemm(h, KC_GEMM_WGRAD, g2);
-        }
-        {
-            Timed t(h, KC_COLSUM, 0, 4.0 * M * d);
-            gk::colsum(false, w.dres, d, M, d, G(h, li.proj_b), w.cs_partial, st);
         }
         const void *q = w.qkv[l], *k = (const char*)w.qkv[l] + (size_t)ab * d;
         int64_t ldq = 3 * d, ldk = 3 * d;
@@ -685,7 +677,8 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         {
             Timed t(h, KC_LN_BWD, 0, (double)M * d * (4 * 4 + ab) + 8.0 * M);
             gk::layernorm_bwd(bf, w.dln, w.x_in[l], mean1, rstd1, P(h, li.ln1_w), w.dres, bf ? w.dres_lp : nullptr,
-                              false, G(h, li.ln1_w), G(h, li.ln1_b), w.ln_partial, M, d, st);
+                              false, G(h, li.ln1_w), G(h, li.ln1_b), l > 0 ? G(h, tb.layers[l - 1].mp_b) : nullptr,
+                              w.ln_partial, M, d, st);
         }
     }
     {
@@ -911,11 +904,12 @@ gpt_status gptk_attention(int32_t backward, int32_t B, int32_t T, int32_t H, int
 
 gpt_status gptk_layernorm(int32_t backward, int32_t M, int32_t d, float eps, const float* x, const float* g,
                           const float* b, void* y, float* mean, float* rstd, const float* dy, float* dres,
-                          void* dres_lp, int32_t overwrite, float* dg, float* db, float* partial, int32_t bf16,
-                          void* stream) {
+                          void* dres_lp, int32_t overwrite, float* dg, float* db, float* dcol, float* partial,
+                          int32_t bf16, void* stream) {
     if (M < 1 || d < 4 || d % 4 || d > 2048) return GPT_ERR_INVALID_ARGUMENT;
     hipStream_t s = (hipStream_t)stream;
-    if (backward) gk::layernorm_bwd(bf16, dy, x, mean, rstd, g, dres, dres_lp, overwrite, dg, db, partial, M, d, s);
+    if (backward)
+        gk::layernorm_bwd(bf16, dy, x, mean, rstd, g, dres, dres_lp, overwrite, dg, db, dcol, partial, M, d, s);
     else gk::layernorm_fwd(bf16, x, g, b, y, mean, rstd, M, d, eps, s);
     return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
 }

@@ -36,12 +36,13 @@ void embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, in
 void layernorm_fwd(bool bf, const float* x, const float* g, const float* b, void* y, float* mean,
                    float* rstd, int M, int d, float eps, hipStream_t s);
 // dres (+)= LN backward of dy; writes a bf16 copy of dres when dres_lp != null;
-// dg += sum dy*xhat, db += sum dy (deterministic two-pass); partial needs
+// dg += sum dy*xhat, db += sum dy, and (if dcol) dcol += column sums of the
+// resulting dres (deterministic two-pass); partial needs
 // layernorm_bwd_partial_floats(M, d) floats.
 size_t layernorm_bwd_partial_floats(int M, int d);
 void layernorm_bwd(bool bf, const float* dy, const float* x, const float* mean, const float* rstd,
                    const float* g, float* dres, void* dres_lp, bool overwrite, float* dg, float* db,
-                   float* partial, int M, int d, hipStream_t s);
+                   float* dcol, float* partial, int M, int d, hipStream_t s);
 
 // ---------------------------------------------------------------- column sums
 // out[n] += sum_m Y[m, n] (Y act or fp32 with row stride ld); partial needs

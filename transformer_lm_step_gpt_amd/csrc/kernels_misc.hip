@@ -409,119 +409,156 @@ void layernorm_fwd(bool bf, const float* x, const float* g, const float* b, void
     else layernorm_fwd_kernel<float><<<grid, 256, 0, s>>>(x, g, b, (float*)y, mean, rstd, M, d, eps);
 }
 
-constexpr int LNB_ROWS = 64;   // rows per workgroup in the backward pass
+constexpr int LNB_ROWS = 32;   // rows per workgroup in the backward pass (8 per wavefront)
 
-size_t layernorm_bwd_partial_floats(int M, int d) { return (size_t)2 * ceil_div(M, LNB_ROWS) * d; }
-
-template <typename TL>
-__global__ __launch_bounds__(256) void layernorm_bwd_kernel(const float* dy, const float* x, const float* mean,
-                                                            const float* rstd, const float* g, float* dres,
-                                                            TL* dres_lp, int overwrite, float* part_g,
-                                                            float* part_b, int M, int d) {
-    __shared__ float red[4][2048 + 4];
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nv = d >> 2;
-    float4 ag[LN_MAXV], ab[LN_MAXV], gg[LN_MAXV];
-#pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-        ag[i] = ab[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        int c = lane + 64 * i;
-        gg[i] = c < nv ? load4(g + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    const int r0 = blockIdx.x * LNB_ROWS;
-    for (int r = r0 + w; r < min(M, r0 + LNB_ROWS); r += 4) {
-        const float mu = mean[r], rs = rstd[r];
-        float4 xh[LN_MAXV], dh[LN_MAXV], dyv[LN_MAXV];
-        float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-        for (int i = 0; i < LN_MAXV; ++i) {
-            int c = lane + 64 * i;
-            if (c < nv) {
-                float4 xv = load4(x + (int64_t)r * d + 4 * c);
-                dyv[i] = load4(dy + (int64_t)r * d + 4 * c);
-                xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
-                dh[i] = make_float4(dyv[i].x * gg[i].x, dyv[i].y * gg[i].y, dyv[i].z * gg[i].z, dyv[i].w * gg[i].w);
-                s1 += (dh[i].x + dh[i].y) + (dh[i].z + dh[i].w);
-                s2 += (dh[i].x * xh[i].x + dh[i].y * xh[i].y) + (dh[i].z * xh[i].z + dh[i].w * xh[i].w);
-            }
-        }
-        s1 = wave_sum(s1) / d;
-        s2 = wave_sum(s2) / d;
-#pragma unroll
-        for (int i = 0; i < LN_MAXV; ++i) {
-            int c = lane + 64 * i;
-            if (c < nv) {
-                float4 o;
-                o.x = rs * (dh[i].x - s1 - xh[i].x * s2);
-                o.y = rs * (dh[i].y - s1 - xh[i].y * s2);
-                o.z = rs * (dh[i].z - s1 - xh[i].z * s2);
-                o.w = rs * (dh[i].w - s1 - xh[i].w * s2);
-                float* dp = dres + (int64_t)r * d + 4 * c;
-                if (!overwrite) {
-                    float4 old = load4(dp);
-                    o.x += old.x; o.y += old.y; o.z += old.z; o.w += old.w;
-                }
-                store4(dp, o);
-                if (dres_lp) store4(dres_lp + (int64_t)r * d + 4 * c, o);
-                ag[i].x += dyv[i].x * xh[i].x; ag[i].y += dyv[i].y * xh[i].y;
-                ag[i].z += dyv[i].z * xh[i].z; ag[i].w += dyv[i].w * xh[i].w;
-                ab[i].x += dyv[i].x; ab[i].y += dyv[i].y; ab[i].z += dyv[i].z; ab[i].w += dyv[i].w;
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-        int c = lane + 64 * i;
-        if (c < nv) *reinterpret_cast<float4*>(&red[w][4 * c]) = ag[i];
-    }
-    __syncthreads();
-    for (int c = threadIdx.x; c < d; c += 256)
-        part_g[(int64_t)blockIdx.x * d + c] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-        int c = lane + 64 * i;
-        if (c < nv) *reinterpret_cast<float4*>(&red[w][4 * c]) = ab[i];
-    }
-    __syncthreads();
-    for (int c = threadIdx.x; c < d; c += 256)
-        part_b[(int64_t)blockIdx.x * d + c] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+// partial sums: [3][nb][d] (dgamma, dbeta, column sums of the new dres) + reduction scratch
+size_t layernorm_bwd_partial_floats(int M, int d) {
+    int nb = ceil_div(M, LNB_ROWS);
+    return (size_t)3 * nb * d + (size_t)3 * ceil_div(nb, 64) * d;
 }
 
-// out[c] += sum_p part[p * n + c], p in order
-__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* part, int np, int n, float* out) {
-    int c = blockIdx.x * 256 + threadIdx.x;
+template <typename TL, int NV>
+GPT_DEV void lnb_row(const float* dy, const float* x, float mu, float rs, const float4* gg, float* dres, TL* dres_lp,
+                     int overwrite, int lane, int d, float4* ag, float4* ab, float4* ac) {
+    float4 xh[NV], dh[NV], dyv[NV], old[NV];
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        int c = lane + 64 * i;
+        if (4 * c < d) {
+            float4 xv = load4(x + 4 * c);
+            dyv[i] = load4(dy + 4 * c);
+            old[i] = overwrite ? make_float4(0.f, 0.f, 0.f, 0.f) : load4(dres + 4 * c);
+            xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
+            dh[i] = make_float4(dyv[i].x * gg[i].x, dyv[i].y * gg[i].y, dyv[i].z * gg[i].z, dyv[i].w * gg[i].w);
+            s1 += (dh[i].x + dh[i].y) + (dh[i].z + dh[i].w);
+            s2 += (dh[i].x * xh[i].x + dh[i].y * xh[i].y) + (dh[i].z * xh[i].z + dh[i].w * xh[i].w);
+        }
+    }
+    s1 = wave_sum(s1) / d;
+    s2 = wave_sum(s2) / d;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        int c = lane + 64 * i;
+        if (4 * c < d) {
+            float4 o;
+            o.x = old[i].x + rs * (dh[i].x - s1 - xh[i].x * s2);
+            o.y = old[i].y + rs * (dh[i].y - s1 - xh[i].y * s2);
+            o.z = old[i].z + rs * (dh[i].z - s1 - xh[i].z * s2);
+            o.w = old[i].w + rs * (dh[i].w - s1 - xh[i].w * s2);
+            store4(dres + 4 * c, o);
+            if (dres_lp) store4(dres_lp + 4 * c, o);
+            ag[i].x += dyv[i].x * xh[i].x; ag[i].y += dyv[i].y * xh[i].y;
+            ag[i].z += dyv[i].z * xh[i].z; ag[i].w += dyv[i].w * xh[i].w;
+            ab[i].x += dyv[i].x; ab[i].y += dyv[i].y; ab[i].z += dyv[i].z; ab[i].w += dyv[i].w;
+            ac[i].x += o.x; ac[i].y += o.y; ac[i].z += o.z; ac[i].w += o.w;
+        }
+    }
+}
+
+template <typename TL, int NV>
+__global__ __launch_bounds__(256) void layernorm_bwd_kernel(const float* dy, const float* x, const float* mean,
+                                                            const float* rstd, const float* g, float* dres,
+                                                            TL* dres_lp, int overwrite, float* part, int M, int d) {
+    __shared__ float red[4][2048 + 4];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nb = gridDim.x;
+    float4 ag[NV], ab[NV], ac[NV], gg[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        ag[i] = ab[i] = ac[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        int c = lane + 64 * i;
+        gg[i] = 4 * c < d ? load4(g + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const int r0 = blockIdx.x * LNB_ROWS + w * (LNB_ROWS / 4);
+    const int r1 = min(M, r0 + LNB_ROWS / 4);
+    for (int r = r0; r < r1; ++r) {
+        const int64_t o = (int64_t)r * d;
+        lnb_row<TL, NV>(dy + o, x + o, mean[r], rstd[r], gg, dres + o, dres_lp ? dres_lp + o : nullptr, overwrite,
+                        lane, d, ag, ab, ac);
+    }
+    float4* sets[3] = {ag, ab, ac};
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            int c = lane + 64 * i;
+            if (4 * c < d) *reinterpret_cast<float4*>(&red[w][4 * c]) = sets[q][i];
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < d; c += 256)
+            part[((int64_t)q * nb + blockIdx.x) * d + c] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+        __syncthreads();
+    }
+}
+
+// out[q][c] += sum_p part[q][p][c] for q < nq, in two deterministic passes
+// (groups of 64 partials, then the group sums); tmp holds nq * ceil(np/64) * n floats
+__global__ __launch_bounds__(256) void reduce_partials_stage1(const float* part, int np, int n, float* tmp) {
+    const int c = blockIdx.x * 256 + threadIdx.x, grp = blockIdx.y, q = blockIdx.z;
     if (c >= n) return;
+    const int ng = gridDim.y;
+    const int p0 = grp * 64, p1 = min(np, p0 + 64);
+    const float* src = part + (int64_t)q * np * n + c;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    int p = p0;
+    for (; p + 4 <= p1; p += 4) {
+        a0 += src[(int64_t)p * n];
+        a1 += src[(int64_t)(p + 1) * n];
+        a2 += src[(int64_t)(p + 2) * n];
+        a3 += src[(int64_t)(p + 3) * n];
+    }
+    for (; p < p1; ++p) a0 += src[(int64_t)p * n];
+    tmp[((int64_t)q * ng + grp) * n + c] = (a0 + a1) + (a2 + a3);
+}
+__global__ __launch_bounds__(256) void reduce_partials_stage2(const float* tmp, int ng, int n, float* out0,
+                                                              float* out1, float* out2) {
+    const int c = blockIdx.x * 256 + threadIdx.x, q = blockIdx.y;
+    if (c >= n) return;
+    float* out = q == 0 ? out0 : (q == 1 ? out1 : out2);
+    if (!out) return;
     float a = 0.f;
-    for (int p = 0; p < np; ++p) a += part[(int64_t)p * n + c];
+    for (int g = 0; g < ng; ++g) a += tmp[((int64_t)q * ng + g) * n + c];
     out[c] += a;
 }
 
+static void reduce_partials(const float* part, int np, int n, int nq, float* tmp, float* o0, float* o1, float* o2,
+                            hipStream_t s) {
+    const int ng = ceil_div(np, 64);
+    reduce_partials_stage1<<<dim3(ceil_div(n, 256), ng, nq), 256, 0, s>>>(part, np, n, tmp);
+    reduce_partials_stage2<<<dim3(ceil_div(n, 256), nq), 256, 0, s>>>(tmp, ng, n, o0, o1, o2);
+}
+
+template <typename TL>
+static void lnb_launch(int nv, int nb, const float* dy, const float* x, const float* mean, const float* rstd,
+                       const float* g, float* dres, TL* lp, int ov, float* part, int M, int d, hipStream_t s) {
+    switch (nv) {
+        case 1: layernorm_bwd_kernel<TL, 1><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
+        case 2: layernorm_bwd_kernel<TL, 2><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
+        case 3: layernorm_bwd_kernel<TL, 3><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
+        case 4: layernorm_bwd_kernel<TL, 4><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
+        default: layernorm_bwd_kernel<TL, 8><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
+    }
+}
+
 void layernorm_bwd(bool bf, const float* dy, const float* x, const float* mean, const float* rstd, const float* g,
-                   float* dres, void* dres_lp, bool overwrite, float* dg, float* db, float* partial, int M, int d,
-                   hipStream_t s) {
-    int nb = ceil_div(M, LNB_ROWS);
-    float* pg = partial;
-    float* pb = partial + (size_t)nb * d;
-    if (bf)
-        layernorm_bwd_kernel<bf16><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, (bf16*)dres_lp, overwrite, pg, pb,
-                                                      M, d);
-    else
-        layernorm_bwd_kernel<float><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, (float*)dres_lp, overwrite, pg,
-                                                       pb, M, d);
-    reduce_partials_kernel<<<ceil_div(d, 256), 256, 0, s>>>(pg, nb, d, dg);
-    reduce_partials_kernel<<<ceil_div(d, 256), 256, 0, s>>>(pb, nb, d, db);
+                   float* dres, void* dres_lp, bool overwrite, float* dg, float* db, float* dcol, float* partial,
+                   int M, int d, hipStream_t s) {
+    const int nb = ceil_div(M, LNB_ROWS);
+    const int nv = ceil_div(d, 256);
+    if (bf) lnb_launch<bf16>(nv, nb, dy, x, mean, rstd, g, dres, (bf16*)dres_lp, overwrite, partial, M, d, s);
+    else lnb_launch<float>(nv, nb, dy, x, mean, rstd, g, dres, (float*)dres_lp, overwrite, partial, M, d, s);
+    reduce_partials(partial, nb, d, dcol ? 3 : 2, partial + (size_t)3 * nb * d, dg, db, dcol, s);
 }
 
 // =====================================================================
-// column sums (bias gradients)
+// column sums (bias gradients): 8 columns per thread, 64 rows per workgroup
 // =====================================================================
 
-constexpr int CS_ROWS = 128;
-size_t colsum_partial_floats(int M, int N) { return (size_t)ceil_div(M, CS_ROWS) * N; }
+constexpr int CS_ROWS = 64;
 
 template <typename TI>
-__global__ __launch_bounds__(256) void colsum_kernel(const TI* Y, int64_t ld, int M, int N, float* part) {
+__global__ __launch_bounds__(256) void colsum_scalar_kernel(const TI* Y, int64_t ld, int M, int N, float* part) {
     int n = blockIdx.x * 256 + threadIdx.x;
     if (n >= N) return;
     int r0 = blockIdx.y * CS_ROWS, r1 = min(M, r0 + CS_ROWS);
@@ -529,12 +566,46 @@ __global__ __launch_bounds__(256) void colsum_kernel(const TI* Y, int64_t ld, in
     for (int r = r0; r < r1; ++r) a += to_f32(Y[(int64_t)r * ld + n]);
     part[(int64_t)blockIdx.y * N + n] = a;
 }
+size_t colsum_partial_floats(int M, int N) {
+    int np = ceil_div(M, CS_ROWS);
+    return (size_t)np * N + (size_t)ceil_div(np, 64) * N;
+}
+
+template <typename TI>
+__global__ __launch_bounds__(256) void colsum_kernel(const TI* Y, int64_t ld, int M, int N, float* part) {
+    const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (c0 >= N) return;
+    const int r0 = blockIdx.y * CS_ROWS, r1 = min(M, r0 + CS_ROWS);
+    float a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = 0.f;
+    if (c0 + 8 <= N) {
+#pragma unroll 4
+        for (int r = r0; r < r1; ++r) {
+            const TI* p = Y + (int64_t)r * ld + c0;
+            float4 u = load4(p), v = load4(p + 4);
+            a[0] += u.x; a[1] += u.y; a[2] += u.z; a[3] += u.w;
+            a[4] += v.x; a[5] += v.y; a[6] += v.z; a[7] += v.w;
+        }
+    } else {
+        for (int r = r0; r < r1; ++r)
+            for (int e = 0; e < 8 && c0 + e < N; ++e) a[e] += to_f32(Y[(int64_t)r * ld + c0 + e]);
+    }
+    for (int e = 0; e < 8 && c0 + e < N; ++e) part[(int64_t)blockIdx.y * N + c0 + e] = a[e];
+}
 
 void colsum(bool y_bf, const void* Y, int64_t ld, int M, int N, float* out, float* partial, hipStream_t s) {
-    dim3 grid(ceil_div(N, 256), ceil_div(M, CS_ROWS));
-    if (y_bf) colsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)Y, ld, M, N, partial);
-    else colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)Y, ld, M, N, partial);
-    reduce_partials_kernel<<<ceil_div(N, 256), 256, 0, s>>>(partial, (int)grid.y, N, out);
+    const int np = ceil_div(M, CS_ROWS);
+    dim3 grid(ceil_div(N, 256 * 8), np);
+    const bool vec = (ld % 8) == 0 && ((uintptr_t)Y % 16) == 0;
+    if (y_bf && vec) colsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)Y, ld, M, N, partial);
+    else if (!y_bf && vec) colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)Y, ld, M, N, partial);
+    else {
+        // unaligned fallback: one column per thread
+        if (y_bf) colsum_scalar_kernel<bf16><<<dim3(ceil_div(N, 256), np), 256, 0, s>>>((const bf16*)Y, ld, M, N, partial);
+        else colsum_scalar_kernel<float><<<dim3(ceil_div(N, 256), np), 256, 0, s>>>((const float*)Y, ld, M, N, partial);
+    }
+    reduce_partials(partial, np, N, 1, partial + (size_t)np * N, out, nullptr, nullptr, s);
 }
 
 // =====================================================================
@@ -600,8 +671,113 @@ __global__ __launch_bounds__(256) void cross_entropy_kernel(T* z, const int32_t*
     }
 }
 
+// bf16 logits with Vp % 8 == 0: the row is read once into registers (CPT
+// 16-byte chunks per thread), reduced (max, then sum of exp), and the gradient
+// is written back from registers: one read and one write of the row.
+typedef uint32_t ce_u32x4 __attribute__((ext_vector_type(4)));
+
+GPT_DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+GPT_DEV float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int CPT>
+__global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const int32_t* y, float* row_loss, int Vp,
+                                                                float gscale, float cap, int32_t* err) {
+    __shared__ float sred[8];
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    bf16* zr = z + (int64_t)row * Vp;
+    const int nch = Vp >> 3;
+    const int tgt = y[row];
+    const bool valid = tgt >= 0 && tgt < Vp;
+    const float icap = cap > 0.f ? 1.0f / cap : 0.f;
+    const float L2E = 1.4426950408889634f;
+    ce_u32x4 v[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const int idx = tid + 256 * c;
+        ce_u32x4 zero = {0u, 0u, 0u, 0u};
+        v[c] = idx < nch ? *reinterpret_cast<const ce_u32x4*>(zr + 8 * idx) : zero;
+    }
+    auto val = [&](int c, int e) {   // logit (after the cap) in log2 units
+        uint32_t wd = v[c][e >> 1];
+        float x = (e & 1) ? bf_hi(wd) : bf_lo(wd);
+        if (cap > 0.f) x = cap * tanh_exp2(x * icap);
+        return x * L2E;
+    };
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+        if (tid + 256 * c < nch)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, val(c, e));
+    mx = wave_max(mx);
+    if (lane == 0) sred[w] = mx;
+    __syncthreads();
+    const float gm = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
+    float sm = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+        if (tid + 256 * c < nch)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm += exp2f(val(c, e) - gm);
+    sm = wave_sum(sm);
+    if (lane == 0) sred[4 + w] = sm;
+    __syncthreads();
+    const float lse2 = gm + log2f((sred[4] + sred[5]) + (sred[6] + sred[7]));
+    if (tid == 0) {
+        float loss = 0.f;
+        if (valid) {
+            float zy = (float)zr[tgt];
+            if (cap > 0.f) zy = cap * tanh_exp2(zy * icap);
+            loss = lse2 * 0.6931471805599453f - zy;
+        } else {
+            *err = 1;
+        }
+        row_loss[row] = loss;
+    }
+    __syncthreads();   // the target logit is read before any thread overwrites the row
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        const int idx = tid + 256 * c;
+        if (idx >= nch) continue;
+        ce_u32x4 o;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            float gpair[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int e = 2 * e2 + h;
+                float g = 0.f;
+                if (valid) {
+                    uint32_t wd = v[c][e2];
+                    float x = h ? bf_hi(wd) : bf_lo(wd);
+                    float th = 0.f;
+                    if (cap > 0.f) { th = tanh_exp2(x * icap); x = cap * th; }
+                    float p = exp2f(x * L2E - lse2);
+                    g = (p - (8 * idx + e == tgt ? 1.0f : 0.0f)) * gscale;
+                    if (cap > 0.f) g *= (1.0f - th * th);
+                }
+                gpair[h] = g;
+            }
+            bf16 lo = (bf16)gpair[0], hi = (bf16)gpair[1];
+            o[e2] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        *reinterpret_cast<ce_u32x4*>(zr + 8 * idx) = o;
+    }
+}
+
 void cross_entropy(bool bf, void* z, const int32_t* y, float* row_loss, int M, int Vp, float gscale, float cap,
                    int32_t* err, hipStream_t s) {
+    const int nch = Vp / 8;
+    if (bf && Vp % 8 == 0 && ((uintptr_t)z % 16) == 0 && nch <= 32 * 256) {
+        const int cpt = ceil_div(nch, 256);
+        bf16* zb = (bf16*)z;
+        if (cpt <= 4) cross_entropy_reg_kernel<4><<<M, 256, 0, s>>>(zb, y, row_loss, Vp, gscale, cap, err);
+        else if (cpt <= 8) cross_entropy_reg_kernel<8><<<M, 256, 0, s>>>(zb, y, row_loss, Vp, gscale, cap, err);
+        else if (cpt <= 16) cross_entropy_reg_kernel<16><<<M, 256, 0, s>>>(zb, y, row_loss, Vp, gscale, cap, err);
+        else if (cpt <= 25) cross_entropy_reg_kernel<25><<<M, 256, 0, s>>>(zb, y, row_loss, Vp, gscale, cap, err);
+        else cross_entropy_reg_kernel<32><<<M, 256, 0, s>>>(zb, y, row_loss, Vp, gscale, cap, err);
+        return;
+    }
     if (bf) cross_entropy_kernel<bf16><<<M, 256, 0, s>>>((bf16*)z, y, row_loss, Vp, gscale, cap, err);
     else cross_entropy_kernel<float><<<M, 256, 0, s>>>((float*)z, y, row_loss, Vp, gscale, cap, err);
 }

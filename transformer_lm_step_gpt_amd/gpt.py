@@ -98,7 +98,7 @@ _SIGS = [
                                  c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
     ("gptk_layernorm", c_int32, [c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
-                                 c_void_p, c_int32, c_void_p]),
+                                 c_void_p, c_void_p, c_int32, c_void_p]),
     ("gptk_layernorm_partial_floats", c_int64, [c_int32, c_int32]),
     ("gptk_cross_entropy", c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_float, c_float, c_void_p,
                                      c_int32, c_void_p]),

@@ -15,11 +15,17 @@
 //   dQ        S^T = K Q^T, dP^T = V dO^T (each lane owns one query),
 //             dQ^T += K^T dS^T  (one workgroup per 128 queries).
 //
+// Streamed 64-row tiles (K, V or Q, dO) are copied into a ring of LDS stages
+// by 16-byte LDS-DMA loads and waited for with s_waitcnt vmcnt only when they
+// are consumed, so several tiles are in flight. Tiles are kept row-major
+// ([row][d], 16-byte chunks swizzled by row); operands that need d as the row
+// index are read with the transposing LDS read ds_read_b64_tr_b16.
+//
 // Accumulator fragments hold rows 8*(e/4) + 4*(lane/32) + e%4 of a 32-row
 // block. When such a fragment is reused as the 16-deep k operand of the next
 // product, k slot 8*(lane/32) + e' stands for row 8*(e'/4) + 4*(lane/32) +
-// e'%4; the other operand is read from LDS with the same slot-to-row mapping
-// (two 8-byte reads of 4 consecutive rows), so the product is unchanged.
+// e'%4; the other operand is read with the same slot-to-row mapping (two
+// transposing reads of 4 consecutive rows), so the product is unchanged.
 //
 // All outputs are written by exactly one workgroup: no atomics.
 #include "common.h"
@@ -32,12 +38,29 @@ namespace {
 constexpr float M_LOG2E_F = 1.4426950408889634f;
 constexpr float M_LN2_F = 0.6931471805599453f;
 constexpr int ATT_BQ = 128;    // queries (fwd, dQ) or keys (dK dV) per workgroup: 4 waves x 32
-constexpr int ATT_BT = 64;     // rows of the streamed tile
+constexpr int ATT_BT = 64;     // rows of a streamed tile
+constexpr int ATT_NS = 3;      // LDS stages
+constexpr int ATT_MAX_T = 4096;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-GPT_DEV int aswz(int row, int chunk, int nch) { return chunk ^ ((row >> 3) & (nch - 1)); }
+template <int N>
+GPT_DEV void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// barrier without the release fence of __syncthreads (which would also wait
+// for the LDS-DMA loads still in flight for later tiles)
+GPT_DEV void barrier_no_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 GPT_DEV f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
 
@@ -48,61 +71,83 @@ GPT_DEV f32x16 zero16() {
     return z;
 }
 
-// rows [r0, r0+ROWS) of a [T, HD] head slice into a row-major LDS tile
-// (HD + 8 stride, 16-byte chunks swizzled by row / 8); rows >= T are zero
-template <int HD, int ROWS>
-GPT_DEV void stage_rows_major(bf16* dst, const bf16* src, int64_t ld, int r0, int T) {
-    constexpr int CH = HD / 8, S = HD + 8, N = ROWS * CH;
-    for (int c = threadIdx.x; c < N; c += 256) {
-        int r = c / CH, ch = c % CH, gr = r0 + r;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (gr < T) v = *reinterpret_cast<const u32x4*>(src + (int64_t)gr * ld + ch * 8);
-        *reinterpret_cast<u32x4*>(dst + r * S + aswz(r, ch, CH) * 8) = v;
-    }
-}
-
-// the same rows transposed: dst[d][r] (stride ROWS + 4), via (r, r+1) pairs
-template <int HD, int ROWS>
-GPT_DEV void stage_cols_major(bf16* dst, const bf16* src, int64_t ld, int r0, int T) {
-    constexpr int G = HD / 8, N = G * (ROWS / 2), S = ROWS + 4;
-    for (int u = threadIdx.x; u < N; u += 256) {
-        int g = u % G, r = 2 * (u / G), gr = r0 + r;
-        u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-        if (gr < T) v0 = *reinterpret_cast<const u32x4*>(src + (int64_t)gr * ld + g * 8);
-        if (gr + 1 < T) v1 = *reinterpret_cast<const u32x4*>(src + (int64_t)(gr + 1) * ld + g * 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t lo = (v0[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-            uint32_t hi = (v1[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-            *reinterpret_cast<uint32_t*>(dst + (g * 8 + i) * S + r) = lo | (hi << 16);
-        }
-    }
-}
-
-// 16-deep k operand from a row-major tile: row `row`, k = 16*ds + 8*(lane/32) + e
-template <int HD>
-GPT_DEV bf16x8 frag_rows(const bf16* t, int row, int ds, int hh) {
-    constexpr int CH = HD / 8, S = HD + 8;
-    return *reinterpret_cast<const bf16x8*>(t + row * S + aswz(row, 2 * ds + hh, CH) * 8);
-}
-
-// 16-deep k operand over permuted rows of a transposed tile: element d = `col`,
-// rows 16*ks + 4*hh + {0..3} and 16*ks + 8 + 4*hh + {0..3}
-template <int ROWS>
-GPT_DEV bf16x8 frag_cols(const bf16* t, int col, int ks, int hh) {
-    constexpr int S = ROWS + 4;
-    const bf16* p = t + col * S + 16 * ks + 4 * hh;
-    u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-    u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
-    u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
-    return __builtin_bit_cast(bf16x8, v);
-}
-
 GPT_DEV bf16x8 load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 GPT_DEV bool visible(int q, int key, int T, int W) {
     return key <= q && key < T && q < T && (W <= 0 || q - key < W);
 }
+
+// A [64][HD] bf16 tile of one head in LDS, filled by LDS-DMA.
+template <int HD>
+struct HTile {
+    static constexpr int CH = HD / 8;               // 16-byte chunks per row
+    static constexpr int RPD = 64 / CH;             // rows per wave-wide 1 KiB DMA
+    static constexpr int PER_WAVE = ATT_BT / RPD / 4;
+    static constexpr int ELEMS = ATT_BT * HD;
+    GPT_DEV static int swz(int r) { return CH == 8 ? ((r >> 1) & 7) : (r & 15); }
+    // rows r0 .. r0+63 of a [T, *] head slice (row stride ld); rows >= T repeat row T-1
+    GPT_DEV static void load(bf16* tile, const bf16* src, int64_t ld, int r0, int T, int w, int lane) {
+#pragma unroll
+        for (int p = 0; p < PER_WAVE; ++p) {
+            const int d = w * PER_WAVE + p;
+            const int r = d * RPD + lane / CH;
+            const int c = (lane % CH) ^ swz(r);
+            const int gr = min(r0 + r, T - 1);
+            __builtin_amdgcn_global_load_lds(src + (int64_t)gr * ld + c * 8, (lds_void_t*)(tile + d * 512), 16, 0, 0);
+        }
+    }
+    // 16-deep operand: row r, columns 16*ds + 8*hh .. +8
+    GPT_DEV static bf16x8 rowfrag(const bf16* tile, int r, int ds, int hh) {
+        const int c = 2 * ds + hh;
+        return *reinterpret_cast<const bf16x8*>(tile + r * HD + ((c ^ swz(r)) << 3));
+    }
+    GPT_DEV static s16x4 tr(const bf16* tile, int r, int d) {
+        const bf16* p = tile + r * HD + (((d >> 3) ^ swz(r)) << 3) + (d & 7);
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+    }
+    // 16-deep operand with the tile's rows as k: lane l gets column d0 + l%32 and
+    // rows 16*ks + 4*(l/32) + {0..3}, then 16*ks + 8 + 4*(l/32) + {0..3}
+    GPT_DEV static bf16x8 trfrag(const bf16* tile, int d0, int ks, int lane) {
+        const int G = lane >> 4, j = lane & 15;
+        const int r = 16 * ks + 4 * (G >> 1) + (j >> 2);
+        const int d = d0 + 16 * (G & 1) + 4 * (j & 3);
+        s16x4 lo = tr(tile, r, d), hi = tr(tile, r + 8, d);
+        u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        u32x4 v = {l2[0], l2[1], h2[0], h2[1]};
+        return __builtin_bit_cast(bf16x8, v);
+    }
+};
+
+// Ring of ATT_NS stages, each holding two HTiles (X then Y).
+template <int HD>
+struct TileRing {
+    using TL = HTile<HD>;
+    static constexpr int STAGE = 2 * TL::ELEMS;
+    static constexpr int LPT = 2 * TL::PER_WAVE;    // DMAs per wave per stage
+    bf16* smem;
+    const bf16 *X, *Y;
+    int64_t ldx, ldy;
+    int first, ntiles, T, w, lane;
+    int issued = 0;
+    GPT_DEV void issue_next() {
+        if (issued < ntiles) {
+            bf16* st = smem + (issued % ATT_NS) * STAGE;
+            const int r0 = first + issued * ATT_BT;
+            TL::load(st, X, ldx, r0, T, w, lane);
+            TL::load(st + TL::ELEMS, Y, ldy, r0, T, w, lane);
+            ++issued;
+        }
+    }
+    // tile u in LDS for every wave; then the stage of tile u-1 is refilled
+    GPT_DEV void acquire(int u) {
+        if (issued - 1 - u >= 1) wait_vmcnt<LPT>();
+        else wait_vmcnt<0>();
+        barrier_no_fence();
+        issue_next();
+    }
+    GPT_DEV const bf16* x(int u) const { return smem + (u % ATT_NS) * STAGE; }
+    GPT_DEV const bf16* y(int u) const { return smem + (u % ATT_NS) * STAGE + TL::ELEMS; }
+};
 
 }  // namespace
 
@@ -110,9 +155,9 @@ GPT_DEV bool visible(int q, int key, int T, int W) {
 
 template <int HD>
 __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
-    constexpr int NDS = HD / 16, NDF = HD / 32, SK = HD + 8;
-    __shared__ __attribute__((aligned(16))) bf16 Ks[ATT_BT * SK];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[HD * (ATT_BT + 4)];
+    constexpr int NDS = HD / 16, NDF = HD / 32;
+    using TL = HTile<HD>;
+    __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
     const int qt = gridDim.x - 1 - blockIdx.x;   // heaviest query tiles first
     const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
     const int T = a.T, W = a.window;
@@ -120,8 +165,13 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, hh = lane >> 5;
     const int qw = q0 + w * 32, myq = qw + lr;
     const bf16* Q = (const bf16*)a.q + (int64_t)b * T * a.ldq + h * HD;
-    const bf16* K = (const bf16*)a.k + (int64_t)b * T * a.ldk + h * HD;
-    const bf16* V = (const bf16*)a.v + (int64_t)b * T * a.ldv + h * HD;
+    const int kend = min(T, q0 + ATT_BQ);
+    int kbeg = W > 0 ? max(0, q0 - W + 1) : 0;
+    kbeg = (kbeg / ATT_BT) * ATT_BT;
+    TileRing<HD> ring{smem, (const bf16*)a.k + (int64_t)b * T * a.ldk + h * HD,
+                      (const bf16*)a.v + (int64_t)b * T * a.ldv + h * HD, a.ldk, a.ldv, kbeg,
+                      ceil_div(kend - kbeg, ATT_BT), T, w, lane};
+    for (int s = 0; s < ATT_NS - 1; ++s) ring.issue_next();
 
     bf16x8 qf[NDS];
 #pragma unroll
@@ -134,22 +184,19 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
     for (int df = 0; df < NDF; ++df) oacc[df] = zero16();
     float mrow = -INFINITY, lsum = 0.f;
     const float c = M_LOG2E_F / sqrtf((float)HD);
-    const int kend = min(T, q0 + ATT_BQ);
-    int kbeg = W > 0 ? max(0, q0 - W + 1) : 0;
-    kbeg = (kbeg / ATT_BT) * ATT_BT;
-    for (int kt = kbeg; kt < kend; kt += ATT_BT) {
-        __syncthreads();
-        stage_rows_major<HD, ATT_BT>(Ks, K, a.ldk, kt, T);
-        stage_cols_major<HD, ATT_BT>(Vt, V, a.ldv, kt, T);
-        __syncthreads();
+    for (int t = 0; t < ring.ntiles; ++t) {
+        ring.acquire(t);
+        const int kt = kbeg + t * ATT_BT;
         if (kt > qw + 31) continue;                               // the whole tile is in this wave's future
         if (W > 0 && kt + ATT_BT - 1 <= qw - W) continue;          // the whole tile left every window
+        const bf16* Ks = ring.x(t);
+        const bf16* Vs = ring.y(t);
         f32x16 s[2];
 #pragma unroll
         for (int kf = 0; kf < 2; ++kf) {
             s[kf] = zero16();
 #pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) s[kf] = mfma(frag_rows<HD>(Ks, kf * 32 + lr, ds, hh), qf[ds], s[kf]);
+            for (int ds = 0; ds < NDS; ++ds) s[kf] = mfma(TL::rowfrag(Ks, kf * 32 + lr, ds, hh), qf[ds], s[kf]);
         }
         const bool need_mask = (kt + ATT_BT - 1 > qw) || (kt + ATT_BT > T) || (W > 0 && qw + 31 - kt >= W);
         float tmax = -INFINITY;
@@ -185,8 +232,7 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int df = 0; df < NDF; ++df)
-                oacc[df] = mfma(frag_cols<ATT_BT>(Vt, df * 32 + lr, ks, hh), pk[ks], oacc[df]);
+            for (int df = 0; df < NDF; ++df) oacc[df] = mfma(TL::trfrag(Vs, df * 32, ks, lane), pk[ks], oacc[df]);
     }
     const float l = lsum + __shfl_xor(lsum, 32, 64);
     if (myq < T) {
@@ -209,24 +255,30 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
 
 template <int HD>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma_kernel(Attn a) {
-    constexpr int NDS = HD / 16, NDF = HD / 32, SK = HD + 8, ST = ATT_BT + 4;
-    __shared__ __attribute__((aligned(16))) bf16 Qs[ATT_BT * SK];
-    __shared__ __attribute__((aligned(16))) bf16 Qt[HD * ST];
-    __shared__ __attribute__((aligned(16))) bf16 Gs[ATT_BT * SK];   // dO rows
-    __shared__ __attribute__((aligned(16))) bf16 Gt[HD * ST];       // dO transposed
-    __shared__ float Ls[ATT_BT], Ds[ATT_BT];
+    constexpr int NDS = HD / 16, NDF = HD / 32;
+    using TL = HTile<HD>;
+    __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
+    __shared__ float Lrow[ATT_MAX_T], Drow[ATT_MAX_T];
     const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
     const int T = a.T, W = a.window;
     const int k0 = blockIdx.x * ATT_BQ;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, hh = lane >> 5;
     const int kw = k0 + w * 32, mykey = kw + lr;
-    const bf16* Q = (const bf16*)a.q + (int64_t)b * T * a.ldq + h * HD;
     const bf16* K = (const bf16*)a.k + (int64_t)b * T * a.ldk + h * HD;
     const bf16* V = (const bf16*)a.v + (int64_t)b * T * a.ldv + h * HD;
-    const bf16* G = (const bf16*)a.dO + (int64_t)b * T * a.lddo + h * HD;
-    const float* LSE = a.lse + (int64_t)bh * T;
-    const float* DD = a.D + (int64_t)bh * T;
+    const int qbeg = (k0 / ATT_BT) * ATT_BT;
+    const int qend = W > 0 ? min(T, k0 + ATT_BQ - 1 + W) : T;
+    TileRing<HD> ring{smem, (const bf16*)a.q + (int64_t)b * T * a.ldq + h * HD,
+                      (const bf16*)a.dO + (int64_t)b * T * a.lddo + h * HD, a.ldq, a.lddo, qbeg,
+                      ceil_div(qend - qbeg, ATT_BT), T, w, lane};
+    for (int s = 0; s < ATT_NS - 1; ++s) ring.issue_next();
 
+    // log-sum-exp (log2 units) and D = rowsum(dO o O) of every query this workgroup visits
+    // (zero past T, so masked positions stay finite)
+    for (int i = qbeg + threadIdx.x; i < qbeg + ring.ntiles * ATT_BT; i += 256) {
+        Lrow[i - qbeg] = i < T ? a.lse[(int64_t)bh * T + i] * M_LOG2E_F : 0.f;
+        Drow[i - qbeg] = i < T ? a.D[(int64_t)bh * T + i] : 0.f;
+    }
     bf16x8 kf[NDS], vf[NDS];
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
@@ -238,22 +290,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma_kernel(Attn a) {
 #pragma unroll
     for (int df = 0; df < NDF; ++df) { dk[df] = zero16(); dv[df] = zero16(); }
     const float c = M_LOG2E_F / sqrtf((float)HD);
-    const int qbeg = (k0 / ATT_BT) * ATT_BT;
-    const int qend = W > 0 ? min(T, k0 + ATT_BQ - 1 + W) : T;
-    for (int qt = qbeg; qt < qend; qt += ATT_BT) {
-        __syncthreads();
-        stage_rows_major<HD, ATT_BT>(Qs, Q, a.ldq, qt, T);
-        stage_cols_major<HD, ATT_BT>(Qt, Q, a.ldq, qt, T);
-        stage_rows_major<HD, ATT_BT>(Gs, G, a.lddo, qt, T);
-        stage_cols_major<HD, ATT_BT>(Gt, G, a.lddo, qt, T);
-        for (int i = threadIdx.x; i < ATT_BT; i += 256) {
-            int q = qt + i;
-            Ls[i] = q < T ? LSE[q] * M_LOG2E_F : 0.f;
-            Ds[i] = q < T ? DD[q] : 0.f;
-        }
-        __syncthreads();
+    for (int t = 0; t < ring.ntiles; ++t) {
+        ring.acquire(t);   // the barrier also publishes Lrow / Drow on the first tile
+        const int qt = qbeg + t * ATT_BT;
         if (qt + ATT_BT - 1 < kw) continue;                         // every query precedes every key of the wave
         if (W > 0 && qt > kw + 31 + W - 1) continue;               // every query is past every window
+        const bf16* Qs = ring.x(t);
+        const bf16* Gs = ring.y(t);
+        const float* Ls = Lrow + (qt - qbeg);
+        const float* Ds = Drow + (qt - qbeg);
         const bool need_mask = (qt < kw + 31) || (qt + ATT_BT > T) || (W > 0 && qt + ATT_BT - 1 - kw >= W);
         bf16x8 pk[4], dsk[4];
 #pragma unroll
@@ -261,8 +306,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma_kernel(Attn a) {
             f32x16 s = zero16(), dp = zero16();
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) {
-                s = mfma(frag_rows<HD>(Qs, qf * 32 + lr, ds, hh), kf[ds], s);
-                dp = mfma(frag_rows<HD>(Gs, qf * 32 + lr, ds, hh), vf[ds], dp);
+                s = mfma(TL::rowfrag(Qs, qf * 32 + lr, ds, hh), kf[ds], s);
+                dp = mfma(TL::rowfrag(Gs, qf * 32 + lr, ds, hh), vf[ds], dp);
             }
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -278,8 +323,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma_kernel(Attn a) {
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int df = 0; df < NDF; ++df) {
-                dv[df] = mfma(frag_cols<ATT_BT>(Gt, df * 32 + lr, ks, hh), pk[ks], dv[df]);
-                dk[df] = mfma(frag_cols<ATT_BT>(Qt, df * 32 + lr, ks, hh), dsk[ks], dk[df]);
+                dv[df] = mfma(TL::trfrag(Gs, df * 32, ks, lane), pk[ks], dv[df]);
+                dk[df] = mfma(TL::trfrag(Qs, df * 32, ks, lane), dsk[ks], dk[df]);
             }
     }
     if (mykey < T) {
@@ -306,10 +351,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma_kernel(Attn a) {
 
 template <int HD>
 __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
-    constexpr int NDS = HD / 16, NDF = HD / 32, SK = HD + 8, ST = ATT_BT + 4;
-    __shared__ __attribute__((aligned(16))) bf16 Ks[ATT_BT * SK];
-    __shared__ __attribute__((aligned(16))) bf16 Kt[HD * ST];
-    __shared__ __attribute__((aligned(16))) bf16 Vs[ATT_BT * SK];
+    constexpr int NDS = HD / 16, NDF = HD / 32;
+    using TL = HTile<HD>;
+    __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
     const int qtile = gridDim.x - 1 - blockIdx.x;
     const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
     const int T = a.T, W = a.window;
@@ -317,9 +361,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, hh = lane >> 5;
     const int qw = q0 + w * 32, myq = qw + lr;
     const bf16* Q = (const bf16*)a.q + (int64_t)b * T * a.ldq + h * HD;
-    const bf16* K = (const bf16*)a.k + (int64_t)b * T * a.ldk + h * HD;
-    const bf16* V = (const bf16*)a.v + (int64_t)b * T * a.ldv + h * HD;
     const bf16* G = (const bf16*)a.dO + (int64_t)b * T * a.lddo + h * HD;
+    const int kend = min(T, q0 + ATT_BQ);
+    int kbeg = W > 0 ? max(0, q0 - W + 1) : 0;
+    kbeg = (kbeg / ATT_BT) * ATT_BT;
+    TileRing<HD> ring{smem, (const bf16*)a.k + (int64_t)b * T * a.ldk + h * HD,
+                      (const bf16*)a.v + (int64_t)b * T * a.ldv + h * HD, a.ldk, a.ldv, kbeg,
+                      ceil_div(kend - kbeg, ATT_BT), T, w, lane};
+    for (int s = 0; s < ATT_NS - 1; ++s) ring.issue_next();
 
     bf16x8 qf[NDS], gf[NDS];
 #pragma unroll
@@ -334,17 +383,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
     f32x16 dq[NDF];
 #pragma unroll
     for (int df = 0; df < NDF; ++df) dq[df] = zero16();
-    const int kend = min(T, q0 + ATT_BQ);
-    int kbeg = W > 0 ? max(0, q0 - W + 1) : 0;
-    kbeg = (kbeg / ATT_BT) * ATT_BT;
-    for (int kt = kbeg; kt < kend; kt += ATT_BT) {
-        __syncthreads();
-        stage_rows_major<HD, ATT_BT>(Ks, K, a.ldk, kt, T);
-        stage_cols_major<HD, ATT_BT>(Kt, K, a.ldk, kt, T);
-        stage_rows_major<HD, ATT_BT>(Vs, V, a.ldv, kt, T);
-        __syncthreads();
+    for (int t = 0; t < ring.ntiles; ++t) {
+        ring.acquire(t);
+        const int kt = kbeg + t * ATT_BT;
         if (kt > qw + 31) continue;
         if (W > 0 && kt + ATT_BT - 1 <= qw - W) continue;
+        const bf16* Ks = ring.x(t);
+        const bf16* Vs = ring.y(t);
         const bool need_mask = (kt + ATT_BT - 1 > qw) || (kt + ATT_BT > T) || (W > 0 && qw + 31 - kt >= W);
         bf16x8 dsk[4];
 #pragma unroll
@@ -352,8 +397,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
             f32x16 s = zero16(), dp = zero16();
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) {
-                s = mfma(frag_rows<HD>(Ks, kf * 32 + lr, ds, hh), qf[ds], s);
-                dp = mfma(frag_rows<HD>(Vs, kf * 32 + lr, ds, hh), gf[ds], dp);
+                s = mfma(TL::rowfrag(Ks, kf * 32 + lr, ds, hh), qf[ds], s);
+                dp = mfma(TL::rowfrag(Vs, kf * 32 + lr, ds, hh), gf[ds], dp);
             }
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -368,8 +413,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int df = 0; df < NDF; ++df)
-                dq[df] = mfma(frag_cols<ATT_BT>(Kt, df * 32 + lr, ks, hh), dsk[ks], dq[df]);
+            for (int df = 0; df < NDF; ++df) dq[df] = mfma(TL::trfrag(Ks, df * 32, ks, lane), dsk[ks], dq[df]);
     }
     if (myq < T) {
         const float isd = 1.0f / sqrtf((float)HD);
@@ -389,7 +433,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
 // ============================================================== dispatch
 
 static bool mfma_ok(const Attn& a) {
-    if (!a.bf || (a.hd != 64 && a.hd != 128)) return false;
+    if (!a.bf || (a.hd != 64 && a.hd != 128) || a.T > ATT_MAX_T) return false;
     auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
     if (!al(a.q) || !al(a.k) || !al(a.v)) return false;
     if (a.ldq % 8 || a.ldk % 8 || a.ldv % 8) return false;

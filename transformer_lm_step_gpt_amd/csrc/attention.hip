@@ -288,7 +288,9 @@ void attention_fwd(const Attn& a, hipStream_t s) {
     if (!attention_fwd_mfma(a, s)) attention_fwd_simple(a, s);
 }
 void attention_bwd(const Attn& a, hipStream_t s) {
-    if (!attention_bwd_mfma(a, s)) attention_bwd_simple(a, s);
+    if (attention_bwd_mfma(a, s)) return;
+    attn_rowdot(a.bf, a.dO, a.o, a.Dout, a.B, a.T, a.H, a.hd, s);
+    attention_bwd_simple(a, s);
 }
 
 }  // namespace gk

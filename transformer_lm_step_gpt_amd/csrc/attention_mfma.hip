@@ -254,11 +254,11 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
 // ============================================================== backward: dK, dV
 
 template <int HD>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma_kernel(Attn a) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(Attn a) {
     constexpr int NDS = HD / 16, NDF = HD / 32;
     using TL = HTile<HD>;
     __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
-    __shared__ float Lrow[ATT_MAX_T], Drow[ATT_MAX_T];
+    __shared__ __attribute__((aligned(16))) float Lrow[ATT_MAX_T], Drow[ATT_MAX_T];
     const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
     const int T = a.T, W = a.window;
     const int k0 = blockIdx.x * ATT_BQ;
@@ -300,7 +300,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma_kernel(Attn a) {
         const float* Ls = Lrow + (qt - qbeg);
         const float* Ds = Drow + (qt - qbeg);
         const bool need_mask = (qt < kw + 31) || (qt + ATT_BT > T) || (W > 0 && qt + ATT_BT - 1 - kw >= W);
-        bf16x8 pk[4], dsk[4];
 #pragma unroll
         for (int qf = 0; qf < 2; ++qf) {
             f32x16 s = zero16(), dp = zero16();
@@ -309,23 +308,31 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma_kernel(Attn a) {
                 s = mfma(TL::rowfrag(Qs, qf * 32 + lr, ds, hh), kf[ds], s);
                 dp = mfma(TL::rowfrag(Gs, qf * 32 + lr, ds, hh), vf[ds], dp);
             }
+            float4 lq[4], dq4[4];   // rows 8*g + 4*hh + {0..3} of this q fragment
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                lq[g4] = *reinterpret_cast<const float4*>(Ls + qf * 32 + 8 * g4 + 4 * hh);
+                dq4[g4] = *reinterpret_cast<const float4*>(Ds + qf * 32 + 8 * g4 + 4 * hh);
+            }
+            bf16x8 pk[2], dsk[2];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int qi = qf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-                float p = exp2f(fmaf(s[e], c, -Ls[qi]));
+                const float lv = (&lq[e >> 2].x)[e & 3], dv4 = (&dq4[e >> 2].x)[e & 3];
+                float p = exp2f(fmaf(s[e], c, -lv));
                 if (need_mask && !visible(qt + qi, mykey, T, W)) p = 0.f;
-                const float dsv = p * (dp[e] - Ds[qi]);
-                pk[2 * qf + (e >> 3)][e & 7] = (bf16)p;
-                dsk[2 * qf + (e >> 3)][e & 7] = (bf16)dsv;
+                const float dsv = p * (dp[e] - dv4);
+                pk[e >> 3][e & 7] = (bf16)p;
+                dsk[e >> 3][e & 7] = (bf16)dsv;
             }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int df = 0; df < NDF; ++df) {
+                    dv[df] = mfma(TL::trfrag(Gs, df * 32, 2 * qf + kk, lane), pk[kk], dv[df]);
+                    dk[df] = mfma(TL::trfrag(Qs, df * 32, 2 * qf + kk, lane), dsk[kk], dk[df]);
+                }
         }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int df = 0; df < NDF; ++df) {
-                dv[df] = mfma(TL::trfrag(Gs, df * 32, ks, lane), pk[ks], dv[df]);
-                dk[df] = mfma(TL::trfrag(Qs, df * 32, ks, lane), dsk[ks], dk[df]);
-            }
     }
     if (mykey < T) {
         const float isd = 1.0f / sqrtf((float)HD);
@@ -379,7 +386,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
     }
     const float c = M_LOG2E_F / sqrtf((float)HD);
     const float lse2 = myq < T ? a.lse[(int64_t)bh * T + myq] * M_LOG2E_F : 0.f;
-    const float Dq = myq < T ? a.D[(int64_t)bh * T + myq] : 0.f;
+    // D = rowsum(dO o O) of this lane's query: each half-wave holds half of the head dims
+    float Dq = 0.f;
+    if (myq < T) {
+        const bf16* O = (const bf16*)a.o + ((int64_t)b * T + myq) * a.ldo + h * HD;
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            bf16x8 ov = load8(O + 16 * ds + 8 * hh);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Dq = fmaf((float)gf[ds][e], (float)ov[e], Dq);
+        }
+    }
+    Dq += __shfl_xor(Dq, 32, 64);
+    if (myq < T && hh == 0) a.Dout[(int64_t)bh * T + myq] = Dq;
     f32x16 dq[NDF];
 #pragma unroll
     for (int df = 0; df < NDF; ++df) dq[df] = zero16();
@@ -391,7 +410,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
         const bf16* Ks = ring.x(t);
         const bf16* Vs = ring.y(t);
         const bool need_mask = (kt + ATT_BT - 1 > qw) || (kt + ATT_BT > T) || (W > 0 && qw + 31 - kt >= W);
-        bf16x8 dsk[4];
 #pragma unroll
         for (int kf = 0; kf < 2; ++kf) {
             f32x16 s = zero16(), dp = zero16();
@@ -400,6 +418,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
                 s = mfma(TL::rowfrag(Ks, kf * 32 + lr, ds, hh), qf[ds], s);
                 dp = mfma(TL::rowfrag(Vs, kf * 32 + lr, ds, hh), gf[ds], dp);
             }
+            bf16x8 dsk[2];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 float p = exp2f(fmaf(s[e], c, -lse2));
@@ -407,13 +426,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
                     int key = kt + kf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
                     if (!visible(myq, key, T, W)) p = 0.f;
                 }
-                dsk[2 * kf + (e >> 3)][e & 7] = (bf16)(p * (dp[e] - Dq));
+                dsk[e >> 3][e & 7] = (bf16)(p * (dp[e] - Dq));
             }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int df = 0; df < NDF; ++df)
+                    dq[df] = mfma(TL::trfrag(Ks, df * 32, 2 * kf + kk, lane), dsk[kk], dq[df]);
         }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int df = 0; df < NDF; ++df) dq[df] = mfma(TL::trfrag(Ks, df * 32, ks, lane), dsk[ks], dq[df]);
     }
     if (myq < T) {
         const float isd = 1.0f / sqrtf((float)HD);
@@ -449,16 +469,16 @@ bool attention_fwd_mfma(const Attn& a, hipStream_t s) {
 }
 
 bool attention_bwd_mfma(const Attn& a, hipStream_t s) {
-    if (!mfma_ok(a) || a.lddo % 8 || a.ldd % 4) return false;
+    if (!mfma_ok(a) || a.lddo % 8 || a.ldd % 4 || a.ldo % 8) return false;
     auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
-    if (!al(a.dO)) return false;
+    if (!al(a.dO) || !al(a.o)) return false;
     dim3 grid(ceil_div(a.T, ATT_BQ), a.B * a.H);
     if (a.hd == 64) {
-        attn_bwd_dkdv_mfma_kernel<64><<<grid, 256, 0, s>>>(a);
         attn_bwd_dq_mfma_kernel<64><<<grid, 256, 0, s>>>(a);
+        attn_bwd_dkdv_mfma_kernel<64><<<grid, 256, 0, s>>>(a);
     } else {
-        attn_bwd_dkdv_mfma_kernel<128><<<grid, 256, 0, s>>>(a);
         attn_bwd_dq_mfma_kernel<128><<<grid, 256, 0, s>>>(a);
+        attn_bwd_dkdv_mfma_kernel<128><<<grid, 256, 0, s>>>(a);
     }
     return true;
 }

@@ -649,12 +649,11 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         a.q = q; a.k = k; a.v = (const char*)w.qkv[l] + (size_t)ab * 2 * d;
         a.ldq = ldq; a.ldk = ldk; a.ldv = 3 * d;
         a.o = w.att[l]; a.ldo = d; a.lse = w.lse[l]; a.bf = bf;
-        a.dO = w.dO; a.lddo = d; a.D = w.attD;
+        a.dO = w.dO; a.lddo = d; a.D = w.attD; a.Dout = w.attD;
         a.dq = w.dqkv; a.dk = (char*)w.dqkv + (size_t)ab * d; a.dv = (char*)w.dqkv + (size_t)ab * 2 * d; a.ldd = 3 * d;
         {
             double pairs = attn_pairs(B, T, H, a.window);
             Timed t(h, KC_ATTN_BWD, 8.0 * hd * pairs, (double)M * d * 8 * ab + 8.0 * M * H);
-            gk::attn_rowdot(bf, w.dO, w.att[l], w.attD, B, T, H, hd, st);
             gk::attention_bwd(a, st);
         }
         if (qkt) {
@@ -890,11 +889,10 @@ gpt_status gptk_attention(int32_t backward, int32_t B, int32_t T, int32_t H, int
     gk::Attn a{};
     a.B = B; a.T = T; a.H = H; a.hd = hd; a.window = window;
     a.q = q; a.k = k; a.v = v; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv;
-    a.o = o; a.ldo = ldo; a.lse = lse; a.dO = dO; a.lddo = lddo; a.D = D;
+    a.o = o; a.ldo = ldo; a.lse = lse; a.dO = dO; a.lddo = lddo; a.D = D; a.Dout = D;
     a.dq = dq; a.dk = dk; a.dv = dv; a.ldd = ldd; a.bf = bf16;
     hipStream_t s = (hipStream_t)stream;
     if (backward) {
-        gk::attn_rowdot(a.bf, dO, o, D, B, T, H, hd, s);
         gk::attention_bwd(a, s);
     } else {
         gk::attention_fwd(a, s);

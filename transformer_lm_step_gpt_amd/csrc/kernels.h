@@ -114,11 +114,14 @@ struct Attn {
     void* o; int64_t ldo;
     float* lse;                       // [B, H, T]
     const void* dO; int64_t lddo;     // backward
-    const float* D;                   // [B, H, T]
+    const float* D;                   // [B, H, T]: rowsum(dO o O), read by the backward kernels
+    float* Dout;                      // where the matrix-core backward computes it (same buffer)
     void* dq; void* dk; void* dv; int64_t ldd;
     bool bf;
 };
 void attention_fwd(const Attn& a, hipStream_t s);
+// backward: computes D itself (into Dout) when the matrix-core kernels run;
+// the portable kernels need D precomputed (attn_rowdot)
 void attention_bwd(const Attn& a, hipStream_t s);
 
 }  // namespace gk

@@ -206,15 +206,26 @@ double gpt_lr_schedule(int32_t it, int32_t warmup_steps, int32_t max_steps, doub
 const char* gpt_status_string(gpt_status s);
 const char* gpt_last_error(const gpt_handle* h);
 
-/* Kernel timing. When enabled, every launch of the library's kernels is
- * bracketed by HIP events on the handle's stream; per kernel class the
- * library accumulates the summed event time, the launch count and the
- * algorithmic FLOPs and HBM bytes of those launches. */
-gpt_status gpt_set_kernel_timing(gpt_handle* h, int32_t enable);
+/* Kernel timing (measurement support; not part of the training step).
+ * gpt_set_kernel_timing takes a bit mask over kernel classes (bit c = class c,
+ * -1 = all). Every launch of an enabled class, and every launch whose kernel
+ * name equals the filter of gpt_set_kernel_timing_filter, is bracketed by HIP
+ * events on the handle's stream. For the timed launches the library sums the
+ * event time, the launch count and the algorithmic FLOPs and HBM bytes, per
+ * class and per kernel name (the main kernel instantiation, as profilers name
+ * it: e.g. "gemm_mfma_kernel<256, 256, 32, 4, true, true, 0, 1, false>").
+ * Reading the statistics synchronizes the stream. */
+gpt_status gpt_set_kernel_timing(gpt_handle* h, int32_t class_mask);
+gpt_status gpt_set_kernel_timing_filter(gpt_handle* h, const char* kernel_name /* null: none */);
 gpt_status gpt_reset_kernel_timing(gpt_handle* h);
 gpt_status gpt_num_kernel_classes(int32_t* n);
 gpt_status gpt_kernel_timing(gpt_handle* h, int32_t cls, const char** name, double* total_ms,
                              int64_t* launches, double* flops, double* bytes);
+/* kernel names seen in timed launches since the handle was created, in order
+ * of first appearance; the returned name pointer stays valid until gpt_destroy */
+gpt_status gpt_num_kernel_names(gpt_handle* h, int32_t* n);
+gpt_status gpt_kernel_name_timing(gpt_handle* h, int32_t idx, const char** name, double* total_ms,
+                                  int64_t* launches, double* flops, double* bytes);
 
 #ifdef __cplusplus
 }

@@ -319,11 +319,12 @@ def _window(cfg, layer):
 
 
 def forward_backward(params, tokens, targets, cfg, grad_scale=1.0, want_grads=True,
-                     return_logits=False):
+                     return_logits=False, progress=None):
     """One micro-step. Returns (mean loss, grads or None, extras).
 
     grads are grad_scale * d(mean loss)/d(param). extras holds the per-row
-    losses and, on request, the logits.
+    losses and, on request, the logits. progress, if given, is called with a
+    short message after each layer (long runs report as they go).
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     targets = np.asarray(targets, dtype=np.int64)
@@ -371,6 +372,8 @@ def forward_backward(params, tokens, targets, cfg, grad_scale=1.0, want_grads=Tr
         x = x + h @ params[p + "mlp.c_proj.weight"].T + params[p + "mlp.c_proj.bias"]
         c.update(a1=a1, q=q, k=k, v=v, p=prob, o=o, a2=a2, hpre=hpre, h=h)
         caches.append(c)
+        if progress:
+            progress(f"oracle forward layer {l}")
 
     xf, lnf_cache = layernorm_fwd(x, params["ln_f.weight"], params["ln_f.bias"], cfg.ln_eps)
     zraw = xf @ wte.T
@@ -426,6 +429,8 @@ def forward_backward(params, tokens, targets, cfg, grad_scale=1.0, want_grads=Tr
         g[p + "attn.c_attn.bias"] = dqkv.sum(axis=0)
         dxl, g[p + "ln_1.weight"], g[p + "ln_1.bias"] = layernorm_bwd(da1, c["ln1"], params[p + "ln_1.weight"])
         dx = dx + dxl
+        if progress:
+            progress(f"oracle backward layer {l}")
 
     # embeddings: the tied wte receives the lookup's gradient on top of the head's
     np.add.at(g["wte"], tokens.reshape(M), dx)
@@ -482,7 +487,7 @@ def decay_flags(cfg) -> Dict[str, bool]:
     return {name: dec for name, _s, dec, _k in param_table(cfg)}
 
 
-def train_step(params, m, v, micro_batches, cfg, lr, step):
+def train_step(params, m, v, micro_batches, cfg, lr, step, progress=None):
     """Full optimiser step: accumulate grads over the micro-batches with
     scale 1/k, clip at cfg.max_grad_norm, AdamW. Returns
     (mean loss, grad norm, grads (unclipped), new params, new m, new v)."""
@@ -490,7 +495,7 @@ def train_step(params, m, v, micro_batches, cfg, lr, step):
     acc = zeros_like_params(params)
     loss_sum = 0.0
     for tok, tgt in micro_batches:
-        loss, g, _ = forward_backward(params, tok, tgt, cfg, grad_scale=1.0 / k)
+        loss, g, _ = forward_backward(params, tok, tgt, cfg, grad_scale=1.0 / k, progress=progress)
         loss_sum += loss
         for n in acc:
             acc[n] += g[n]

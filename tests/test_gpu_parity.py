@@ -196,7 +196,8 @@ def bf16_check(w, batch, seq, steps=1, single_sequence=False, max_batch=None):
         loss = gpu.forward_backward(x, y)
         g_gpu = gpu.grads()
         norm = gpu.clip_and_adamw(lr, step)
-        lref, nref, gref, p, m, v = O.train_step(p, m, v, [(xo, yo)], cfg, lr, step)
+        lref, nref, gref, p, m, v = O.train_step(p, m, v, [(xo, yo)], cfg, lr, step,
+                                                 progress=say if seq * len(xo) >= 1024 else None)
         gcos = cosine(np.concatenate([g_gpu[n].ravel() for n in gpu.names]),
                       np.concatenate([gref[n].ravel() for n in gpu.names]))
         worst = min((cosine(g_gpu[n], gref[n]), n) for n in gpu.names if np.abs(gref[n]).max() > 0)
@@ -222,6 +223,7 @@ def test_char_bf16_full_batch_single_sequence():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(1200)
 def test_gpt2_124m_full_shape_single_sequence():
     """GPT-2 124M at B=16, T=1024 (the benchmark's launch configuration) on a
     batch of one repeated sequence, against the oracle on that one sequence."""

@@ -61,17 +61,22 @@ GPT_DEV float tanh_exp2(float u) {
     return 1.0f - 2.0f / (1.0f + exp2f(2.8853900817779268f * u));   // 2 log2(e) u
 }
 
-// GELU, tanh approximation: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
-GPT_DEV float gelu_tanh_f(float x) {
-    const float c = 0.7978845608028654f;
-    float u = c * (x + 0.044715f * x * x * x);
-    return 0.5f * x * (1.0f + tanh_exp2(u));
+// GELU, tanh approximation: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3),
+// evaluated as x * sigma(2u) with sigma(2u) = 1 / (1 + 2^(-2 log2(e) u)), which
+// equals 0.5 (1 + tanh(u)). One exp2 and one reciprocal; saturates cleanly
+// (2^+inf gives sigma = 0, 2^-inf gives sigma = 1).
+GPT_DEV float gelu_sigma(float x) {
+    const float k1 = -2.0f * 1.4426950408889634f * 0.7978845608028654f;   // -2 log2(e) sqrt(2/pi)
+    const float k3 = k1 * 0.044715f;
+    const float a = x * fmaf(k3, x * x, k1);
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a));
 }
+GPT_DEV float gelu_tanh_f(float x) { return x * gelu_sigma(x); }
+// d/dx [x sigma(2u)] = sigma + x sigma (1 - sigma) 2 u'(x), u' = sqrt(2/pi) (1 + 3 * 0.044715 x^2)
 GPT_DEV float gelu_tanh_grad_f(float x) {
-    const float c = 0.7978845608028654f;
-    float u = c * (x + 0.044715f * x * x * x);
-    float t = tanh_exp2(u);
-    return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * c * (1.0f + 3.0f * 0.044715f * x * x);
+    const float c2 = 2.0f * 0.7978845608028654f;
+    const float s = gelu_sigma(x);
+    return fmaf(x * s * (1.0f - s), fmaf(c2 * 3.0f * 0.044715f, x * x, c2), s);
 }
 GPT_DEV float relu2_f(float x) { float r = fmaxf(x, 0.0f); return r * r; }
 GPT_DEV float relu2_grad_f(float x) { return 2.0f * fmaxf(x, 0.0f); }

@@ -12,6 +12,8 @@
 // the bf16 matrix-core kernel is in gemm_mfma.hip.
 #include "common.h"
 #include "kernels.h"
+
+#include <cstdio>
 #include "gemm_common.h"
 
 namespace gk {
@@ -104,9 +106,22 @@ void gemm_simple(const Gemm& g, hipStream_t s) {
 }  // namespace gk
 
 namespace gk {
-void gemm(const Gemm& g, float* splitk_scratch, size_t splitk_floats, hipStream_t s) {
-    if (gemm_mfma_ok(g)) gemm_mfma(g, splitk_scratch, splitk_floats, s);
+GemmPlan gemm_plan(const Gemm& g, size_t splitk_floats) {
+    if (gemm_mfma_ok(g)) return gemm_mfma_plan(g, splitk_floats);
+    GemmPlan p;
+    snprintf(p.name, sizeof(p.name), "gemm_simple_kernel");
+    return p;
+}
+void gemm_main(const Gemm& g, const GemmPlan& p, float* splitk_scratch, hipStream_t s) {
+    if (p.cfg >= 0) gemm_mfma_main(g, p, splitk_scratch, s);
     else gemm_simple(g, s);
 }
-const char* gemm_last_kernel_name() { return "gemm_simple_kernel"; }
+void gemm_finish(const Gemm& g, const GemmPlan& p, const float* splitk_scratch, hipStream_t s) {
+    if (p.cfg >= 0) gemm_mfma_reduce(g, p, splitk_scratch, s);
+}
+void gemm(const Gemm& g, float* splitk_scratch, size_t splitk_floats, hipStream_t s) {
+    const GemmPlan p = gemm_plan(g, splitk_floats);
+    gemm_main(g, p, splitk_scratch, s);
+    gemm_finish(g, p, splitk_scratch, s);
+}
 }  // namespace gk

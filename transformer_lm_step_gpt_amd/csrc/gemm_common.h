@@ -27,51 +27,69 @@ GPT_DEV void epilogue_store(const Gemm& g, int m, int n, float acc) {
     }
 }
 
-// The 16 values of one 32x32 accumulator fragment column: rows
-// rb + 8*(e/4) + e%4 of column col, all inside the matrix. Every load the
-// epilogue needs is issued before the first store.
-template <typename TC, int EPI>
-GPT_DEV void epilogue_frag(const Gemm& g, int rb, int col, const f32x16& acc, float bias) {
-    const int64_t base = (int64_t)rb * g.ldc + col;
-    auto off = [&](int e) { return base + (int64_t)(8 * (e >> 2) + (e & 3)) * g.ldc; };
-    if constexpr (EPI == EPI_STORE) {
+// Eight consecutive outputs (m, n .. n+7) of one row, 16-byte aligned, all
+// inside the matrix; bias holds the eight column biases (or zeros). Every load
+// is issued before the first store.
+template <typename TC, int EPI, int ACT>
+GPT_DEV void epilogue_chunk8(const Gemm& g, int m, int n, const float (&acc)[8], const float (&bias)[8]) {
+    const int64_t o = (int64_t)m * g.ldc + n;
+    auto put = [&](void* base, const float (&x)[8]) {
+        if constexpr (sizeof(TC) == 2) {
+            bf16x8 b;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ((TC*)g.C)[off(e)] = from_f32<TC>(acc[e]);
+            for (int e = 0; e < 8; ++e) b[e] = (bf16)x[e];
+            *reinterpret_cast<bf16x8*>((bf16*)base + o) = b;
+        } else {
+            float* p = (float*)base + o;
+            reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+            reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+        }
+    };
+    float y[8];
+    if constexpr (EPI == EPI_STORE) {
+        put(g.C, acc);
     } else if constexpr (EPI == EPI_BIAS) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ((TC*)g.C)[off(e)] = from_f32<TC>(acc[e] + bias);
+        for (int e = 0; e < 8; ++e) y[e] = acc[e] + bias[e];
+        put(g.C, y);
     } else if constexpr (EPI == EPI_BIAS_ACT) {
+        float h[8];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            float pre = acc[e] + bias;
-            ((TC*)g.C)[off(e)] = from_f32<TC>(pre);
-            ((TC*)g.C2)[off(e)] = from_f32<TC>(g.act == ACT_RELU2 ? relu2_f(pre) : gelu_tanh_f(pre));
+        for (int e = 0; e < 8; ++e) {
+            y[e] = acc[e] + bias[e];
+            h[e] = act_f<ACT>(y[e]);
         }
+        put(g.C, y);
+        put(g.C2, h);
     } else if constexpr (EPI == EPI_BIAS_RESID) {
-        float r[16];
+        const float* r = g.resid + o;
+        const float4 r0 = reinterpret_cast<const float4*>(r)[0], r1 = reinterpret_cast<const float4*>(r)[1];
+        const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) r[e] = g.resid[off(e)];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ((float*)g.C)[off(e)] = r[e] + (acc[e] + bias);
+        for (int e = 0; e < 8; ++e) y[e] = rv[e] + (acc[e] + bias[e]);
+        put(g.C, y);
     } else if constexpr (EPI == EPI_ACT_GRAD) {
-        float x[16];
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>((const TC*)g.aux + o);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = to_f32(((const TC*)g.aux)[off(e)]);
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            ((TC*)g.C)[off(e)] =
-                from_f32<TC>(acc[e] * (g.act == ACT_RELU2 ? relu2_grad_f(x[e]) : gelu_tanh_grad_f(x[e])));
+        for (int e = 0; e < 8; ++e) {
+            const float x = (float)a[e];
+            y[e] = acc[e] * act_grad_f<ACT>(x);
+        }
+        put(g.C, y);
     } else {   // EPI_ACCUM
-        float c[16];
+        const float* c = (const float*)g.C + o;
+        const float4 c0 = reinterpret_cast<const float4*>(c)[0], c1 = reinterpret_cast<const float4*>(c)[1];
+        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) c[e] = ((float*)g.C)[off(e)];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ((float*)g.C)[off(e)] = c[e] + acc[e];
+        for (int e = 0; e < 8; ++e) y[e] = cv[e] + acc[e];
+        put(g.C, y);
     }
 }
 
 void gemm_simple(const Gemm& g, hipStream_t s);
 bool gemm_mfma_ok(const Gemm& g);
-void gemm_mfma(const Gemm& g, float* scratch, size_t nscratch, hipStream_t s);
+GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch);
+void gemm_mfma_main(const Gemm& g, const GemmPlan& p, float* scratch, hipStream_t s);
+void gemm_mfma_reduce(const Gemm& g, const GemmPlan& p, const float* scratch, hipStream_t s);
 
 }  // namespace gk

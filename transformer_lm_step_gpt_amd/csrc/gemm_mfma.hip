@@ -25,14 +25,17 @@
 //   * Split-K (grid.z) writes fp32 partial tiles; a second kernel sums the
 //     slices in a fixed order and applies the epilogue (deterministic).
 //   * Workgroup i runs on XCD i % 8; tiles are renumbered so that each XCD
-//     owns a contiguous, row-major range of output tiles (shared A panels in
-//     its L2).
+//     owns a contiguous range of output tiles in a grouped order (bands of
+//     8 tile-rows walked column by column), so the A and B panels of the
+//     tiles in flight on one XCD stay in its L2.
 #include "common.h"
 #include "gemm_common.h"
 #include "kernels.h"
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <type_traits>
 
 namespace gk {
 
@@ -170,9 +173,15 @@ __device__ __attribute__((always_inline)) inline void half_step(f32x16 (&acc)[FM
     }
 }
 
+constexpr int GROUP_M = 8;
+
 // SPLIT: write fp32 partial sums to part[z][M][N] instead of the epilogue.
-template <int BM, int BN, int BK, int NS, bool AKC, bool BKC, int EPI, typename TC, bool SPLIT>
+// OUTBF: output storage bf16 (1) or fp32 (0); ACT: activation of the
+// BIAS_ACT / ACT_GRAD epilogues. N and ldc are multiples of 8 and the output,
+// aux, residual and bias buffers 16-byte aligned (gemm_mfma_ok).
+template <int BM, int BN, int BK, int NS, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(Gemm g, int kps, float* part) {
+    using TC = typename std::conditional<OUTBF != 0, bf16, float>::type;
     constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
     using TA = OpTile<AKC, BM, BK>;
     using TB = OpTile<BKC, BN, BK>;
@@ -183,10 +192,17 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(Gemm g, int kps, floa
     bf16* smem = reinterpret_cast<bf16*>(smem_raw);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int tn = ceil_div(g.N, BN), ntiles = tn * ceil_div(g.M, BM);
+    const int tn = ceil_div(g.N, BN), tm = ceil_div(g.M, BM), ntiles = tn * tm;
+    // XCD-aware renumbering: workgroup lin runs on XCD lin % 8; XCD x takes a
+    // contiguous range of tiles in the grouped order below
     const int lin = blockIdx.x, xcd = lin & 7, q8 = ntiles >> 3, r8 = ntiles & 7;
     const int tile = xcd * q8 + min(xcd, r8) + (lin >> 3);
-    const int m0 = (tile / tn) * BM, n0 = (tile % tn) * BN;
+    // grouped order: bands of GROUP_M tile-rows, column by column inside a
+    // band, so the tiles resident on one XCD at a time share a few A and B
+    // panels in its L2
+    const int band = tile / (GROUP_M * tn), first = band * GROUP_M, bsz = min(tm - first, GROUP_M);
+    const int inb = tile - band * GROUP_M * tn;
+    const int m0 = (first + inb % bsz) * BM, n0 = (inb / bsz) * BN;
     const int wm = (w >> 1) * WM, wn = (w & 1) * WN;
     const int kb = blockIdx.z * kps;
     const int nk = max(0, (min(g.K, kb + kps) - kb) / BK);    // K and kps are multiples of BK
@@ -258,114 +274,147 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(Gemm g, int kps, floa
         }
     }
 
-    // accumulator fragment: lane holds column (lane % 32), rows 8*(e/4) + 4*(lane/32) + e%4
+    // ---- epilogue. Each wave stages one 32-row strip of its sub-tile at a
+    // time through LDS (fp32, row-major, row stride WN + 8 so the two row
+    // groups of a fragment store fall in different banks), then each lane
+    // takes 8 consecutive columns of a row: 16-byte global accesses, with the
+    // fused operation applied in fp32 on the way out.
+    barrier_no_fence();   // every wave has finished with the k-tile stages
+    constexpr int SS = WN + 8, CPR = WN / 8, RPI = 64 / CPR;
+    static_assert(4 * 32 * SS * 4 <= NS * STAGE * 2, "staging strip fits in the stage ring");
+    float* stg = reinterpret_cast<float*>(smem_raw) + w * 32 * SS;
+    const f32x4* stg4 = reinterpret_cast<const f32x4*>(smem_raw) + w * 8 * SS;
     const int lr = lane & 31, lk = lane >> 5;
-    const bool full = (m0 + BM <= g.M) && (n0 + BN <= g.N);
+    const int cc = lane % CPR, ro = lane / CPR;
+    const int col = n0 + wn + 8 * cc;
+    const bool cin = col < g.N;              // N % 8 == 0: a chunk is wholly inside or outside
+    float bv[8];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn + j * 32 + lr;
-        float bj = 0.f;
-        if constexpr (!SPLIT && (EPI == EPI_BIAS || EPI == EPI_BIAS_ACT || EPI == EPI_BIAS_RESID))
-            bj = col < g.N ? g.bias[col] : 0.f;
+    for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+    if constexpr (!SPLIT && (EPI == EPI_BIAS || EPI == EPI_BIAS_ACT || EPI == EPI_BIAS_RESID)) {
+        if (cin) {
+            const float4 b0 = *reinterpret_cast<const float4*>(g.bias + col);
+            const float4 b1 = *reinterpret_cast<const float4*>(g.bias + col + 4);
+            bv[0] = b0.x; bv[1] = b0.y; bv[2] = b0.z; bv[3] = b0.w;
+            bv[4] = b1.x; bv[5] = b1.y; bv[6] = b1.z; bv[7] = b1.w;
+        }
+    }
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int rb = m0 + wm + i * 32 + 4 * lk;
-            if (full) {
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int jf = 0; jf < FN; ++jf)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) stg[(8 * (e >> 2) + 4 * lk + (e & 3)) * SS + 32 * jf + lr] = acc[i][jf][e];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+            const int r = it * RPI + ro;
+            const int row = m0 + wm + 32 * i + r;
+            const f32x4 u0 = stg4[r * (SS / 4) + 2 * cc], u1 = stg4[r * (SS / 4) + 2 * cc + 1];
+            if (row < g.M && cin) {
                 if constexpr (SPLIT) {
-                    float* p = part + ((int64_t)blockIdx.z * g.M + rb) * g.N + col;
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) p[(int64_t)(8 * (e >> 2) + (e & 3)) * g.N] = acc[i][j][e];
+                    float* p = part + ((int64_t)blockIdx.z * g.M + row) * g.N + col;
+                    reinterpret_cast<f32x4*>(p)[0] = u0;
+                    reinterpret_cast<f32x4*>(p)[1] = u1;
                 } else {
-                    epilogue_frag<TC, EPI>(g, rb, col, acc[i][j], bj);
-                }
-            } else if (col < g.N) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = rb + 8 * (e >> 2) + (e & 3);
-                    if (row >= g.M) continue;
-                    if constexpr (SPLIT) part[((int64_t)blockIdx.z * g.M + row) * g.N + col] = acc[i][j][e];
-                    else epilogue_store<TC, EPI>(g, row, col, acc[i][j][e]);
+                    const float v[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                    epilogue_chunk8<TC, EPI, ACT>(g, row, col, v, bv);
                 }
             }
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 }
 
-template <typename TC, int EPI>
+// Sums the split-K slices in a fixed order (deterministic) and applies the
+// epilogue; one thread per 8 consecutive outputs of a row.
+template <int EPI, int OUTBF, int ACT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(Gemm g, const float* part, int splits) {
-    int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    int64_t mn = (int64_t)g.M * g.N;
-    if (idx >= mn) return;
-    float s = 0.f;
-    for (int z = 0; z < splits; ++z) s += part[z * mn + idx];
-    epilogue_store<TC, EPI>(g, (int)(idx / g.N), (int)(idx % g.N), s);
+    using TC = typename std::conditional<OUTBF != 0, bf16, float>::type;
+    const int cpr = g.N / 8;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)g.M * cpr) return;
+    const int row = (int)(idx / cpr), col = 8 * (int)(idx % cpr);
+    const int64_t mn = (int64_t)g.M * g.N, o = (int64_t)row * g.N + col;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    for (int z = 0; z < splits; ++z) {
+        const float4 x = *reinterpret_cast<const float4*>(part + z * mn + o);
+        const float4 y = *reinterpret_cast<const float4*>(part + z * mn + o + 4);
+        a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+        b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+    }
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float bv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+    if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_ACT || EPI == EPI_BIAS_RESID) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bv[e] = g.bias[col + e];
+    }
+    epilogue_chunk8<TC, EPI, ACT>(g, row, col, v, bv);
 }
 
 // ------------------------------------------------------------------ dispatch
 
-template <int BM, int BN, int BK, int NS, bool AKC, bool BKC>
-struct Launcher {
-    static constexpr size_t LDS = (size_t)NS * (BM + BN) * BK * sizeof(bf16);
-    static_assert(LDS <= 160 * 1024, "LDS budget");
-
-    template <int EPI, typename TC, bool SPLIT>
-    static void go(const Gemm& g, dim3 grid, int kps, float* part, hipStream_t s) {
-        auto k = gemm_mfma_kernel<BM, BN, BK, NS, AKC, BKC, EPI, TC, SPLIT>;
-        static bool attr = false;
-        if (!attr) {
-            (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
-            attr = true;
-        }
-        k<<<grid, 256, LDS, s>>>(g, kps, part);
-    }
-
-    static void run(const Gemm& g, int splits, float* part, hipStream_t s) {
-        dim3 grid(ceil_div(g.N, BN) * ceil_div(g.M, BM), 1, splits);
-        int kps = ceil_div(ceil_div(g.K, splits), BK) * BK;
-        if (splits > 1) {
-            go<EPI_STORE, float, true>(g, grid, kps, part, s);
-            int64_t mn = (int64_t)g.M * g.N;
-            unsigned rb = (unsigned)((mn + 255) / 256);
-            switch (g.epi) {
-                case EPI_STORE:
-                    if (g.c_bf) splitk_reduce_kernel<bf16, EPI_STORE><<<rb, 256, 0, s>>>(g, part, splits);
-                    else splitk_reduce_kernel<float, EPI_STORE><<<rb, 256, 0, s>>>(g, part, splits);
-                    break;
-                case EPI_BIAS: splitk_reduce_kernel<bf16, EPI_BIAS><<<rb, 256, 0, s>>>(g, part, splits); break;
-                case EPI_BIAS_ACT: splitk_reduce_kernel<bf16, EPI_BIAS_ACT><<<rb, 256, 0, s>>>(g, part, splits); break;
-                case EPI_BIAS_RESID: splitk_reduce_kernel<float, EPI_BIAS_RESID><<<rb, 256, 0, s>>>(g, part, splits); break;
-                case EPI_ACT_GRAD: splitk_reduce_kernel<bf16, EPI_ACT_GRAD><<<rb, 256, 0, s>>>(g, part, splits); break;
-                case EPI_ACCUM: splitk_reduce_kernel<float, EPI_ACCUM><<<rb, 256, 0, s>>>(g, part, splits); break;
-            }
-            return;
-        }
-        switch (g.epi) {
-            case EPI_STORE:
-                if (g.c_bf) go<EPI_STORE, bf16, false>(g, grid, kps, part, s);
-                else go<EPI_STORE, float, false>(g, grid, kps, part, s);
-                break;
-            case EPI_BIAS: go<EPI_BIAS, bf16, false>(g, grid, kps, part, s); break;
-            case EPI_BIAS_ACT: go<EPI_BIAS_ACT, bf16, false>(g, grid, kps, part, s); break;
-            case EPI_BIAS_RESID: go<EPI_BIAS_RESID, float, false>(g, grid, kps, part, s); break;
-            case EPI_ACT_GRAD: go<EPI_ACT_GRAD, bf16, false>(g, grid, kps, part, s); break;
-            case EPI_ACCUM: go<EPI_ACCUM, float, false>(g, grid, kps, part, s); break;
-        }
-    }
-};
-
-// Tile configurations (BM, BN, BK, stages).
-enum GemmCfg { CFG_256_256_32 = 0, CFG_128_256_32, CFG_128_128_32, CFG_256_128_32, CFG_COUNT };
+// Tile configurations (BM, BN; BK = 32, 4 stages).
+enum GemmCfg { CFG_256_256 = 0, CFG_128_256, CFG_128_128, CFG_256_128, CFG_COUNT };
 static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256};
 static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128};
-static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32};
+constexpr int GEMM_BK = 32, GEMM_NS = 4;
+
+template <int BM, int BN, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
+static void launch(const Gemm& g, dim3 grid, int kps, float* part, hipStream_t s) {
+    constexpr size_t LDS = (size_t)GEMM_NS * (BM + BN) * GEMM_BK * sizeof(bf16);
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    auto k = gemm_mfma_kernel<BM, BN, GEMM_BK, GEMM_NS, AKC, BKC, EPI, OUTBF, ACT, SPLIT>;
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
+        attr = true;
+    }
+    k<<<grid, 256, LDS, s>>>(g, kps, part);
+}
+
+// output storage of each epilogue (bf16 except the fp32 residual stream,
+// gradient accumulators and fp32 stores)
+static int out_bf(const Gemm& g) {
+    if (g.epi == EPI_BIAS_RESID || g.epi == EPI_ACCUM) return 0;
+    if (g.epi == EPI_STORE) return g.c_bf ? 1 : 0;
+    return 1;
+}
+
+template <int BM, int BN, bool AKC, bool BKC>
+static void run_main(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
+    dim3 grid(ceil_div(g.N, BN) * ceil_div(g.M, BM), 1, p.splits);
+    const int kps = ceil_div(ceil_div(g.K, p.splits), GEMM_BK) * GEMM_BK;
+    if (p.splits > 1) { launch<BM, BN, AKC, BKC, EPI_STORE, 0, 0, true>(g, grid, kps, part, s); return; }
+    const bool relu = g.act == ACT_RELU2;
+    switch (g.epi) {
+        case EPI_STORE:
+            if (g.c_bf) launch<BM, BN, AKC, BKC, EPI_STORE, 1, 0, false>(g, grid, kps, part, s);
+            else launch<BM, BN, AKC, BKC, EPI_STORE, 0, 0, false>(g, grid, kps, part, s);
+            break;
+        case EPI_BIAS: launch<BM, BN, AKC, BKC, EPI_BIAS, 1, 0, false>(g, grid, kps, part, s); break;
+        case EPI_BIAS_ACT:
+            if (relu) launch<BM, BN, AKC, BKC, EPI_BIAS_ACT, 1, ACT_RELU2, false>(g, grid, kps, part, s);
+            else launch<BM, BN, AKC, BKC, EPI_BIAS_ACT, 1, ACT_GELU, false>(g, grid, kps, part, s);
+            break;
+        case EPI_BIAS_RESID: launch<BM, BN, AKC, BKC, EPI_BIAS_RESID, 0, 0, false>(g, grid, kps, part, s); break;
+        case EPI_ACT_GRAD:
+            if (relu) launch<BM, BN, AKC, BKC, EPI_ACT_GRAD, 1, ACT_RELU2, false>(g, grid, kps, part, s);
+            else launch<BM, BN, AKC, BKC, EPI_ACT_GRAD, 1, ACT_GELU, false>(g, grid, kps, part, s);
+            break;
+        case EPI_ACCUM: launch<BM, BN, AKC, BKC, EPI_ACCUM, 0, 0, false>(g, grid, kps, part, s); break;
+    }
+}
 
 template <bool AKC, bool BKC>
-static void launch_cfg(int cfg, const Gemm& g, int splits, float* scratch, hipStream_t s) {
-    switch (cfg) {
-        case CFG_256_256_32: Launcher<256, 256, 32, 4, AKC, BKC>::run(g, splits, scratch, s); break;
-        case CFG_128_256_32: Launcher<128, 256, 32, 4, AKC, BKC>::run(g, splits, scratch, s); break;
-        case CFG_128_128_32: Launcher<128, 128, 32, 4, AKC, BKC>::run(g, splits, scratch, s); break;
-        case CFG_256_128_32: Launcher<256, 128, 32, 4, AKC, BKC>::run(g, splits, scratch, s); break;
+static void run_cfg(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
+    switch (p.cfg) {
+        case CFG_256_256: run_main<256, 256, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_256: run_main<128, 256, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128: run_main<128, 128, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128: run_main<256, 128, AKC, BKC>(g, p, part, s); break;
     }
 }
 
@@ -381,25 +430,6 @@ static bool forced(int* cfg, int* splits) {
     return state == 1;
 }
 
-template <bool AKC, bool BKC>
-static void run_layout(const Gemm& g, float* scratch, size_t nscratch, hipStream_t s) {
-    const int64_t mn = (int64_t)g.M * g.N;
-    int cfg, splits = 0;
-    if (!forced(&cfg, &splits)) {
-        const int64_t t256 = (int64_t)ceil_div(g.M, 256) * ceil_div(g.N, 256);
-        cfg = t256 >= 240 ? CFG_256_256_32 : CFG_128_128_32;
-    }
-    if (g.K % cfg_bk[cfg]) cfg = CFG_128_128_32;
-    const int64_t tiles = (int64_t)ceil_div(g.M, cfg_bm[cfg]) * ceil_div(g.N, cfg_bn[cfg]);
-    if (splits <= 0) {
-        splits = 1;
-        if (tiles < 200 && g.K >= 2048) splits = (int)std::min<int64_t>(16, (512 + tiles - 1) / tiles);
-    }
-    if (!scratch) splits = 1;
-    while (splits > 1 && ((size_t)splits * mn > nscratch || g.K / splits < 256)) --splits;
-    launch_cfg<AKC, BKC>(cfg, g, splits, scratch, s);
-}
-
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 bool gemm_mfma_ok(const Gemm& g) {
@@ -407,15 +437,99 @@ bool gemm_mfma_ok(const Gemm& g) {
     if (!aligned16(g.A) || !aligned16(g.B)) return false;
     if (g.lda % 8 || g.ldb % 8) return false;
     if (!g.a_kc && (g.M % 8 || g.M < 8)) return false;
-    if (!g.b_kc && (g.N % 8 || g.N < 8)) return false;
+    if (g.N % 8 || g.N < 8 || g.ldc % 8) return false;     // 16-byte epilogue chunks
     if (!g.a_kc && g.b_kc) return false;     // orientation not used by the training step
+    const bool bias = g.epi == EPI_BIAS || g.epi == EPI_BIAS_ACT || g.epi == EPI_BIAS_RESID;
+    if (!aligned16(g.C) || (g.epi == EPI_BIAS_ACT && !aligned16(g.C2)) || (bias && !aligned16(g.bias)) ||
+        (g.epi == EPI_BIAS_RESID && !aligned16(g.resid)) || (g.epi == EPI_ACT_GRAD && !aligned16(g.aux)))
+        return false;
     return true;
 }
 
-void gemm_mfma(const Gemm& g, float* scratch, size_t nscratch, hipStream_t s) {
-    if (g.a_kc && g.b_kc) run_layout<true, true>(g, scratch, nscratch, s);
-    else if (g.a_kc) run_layout<true, false>(g, scratch, nscratch, s);
-    else run_layout<false, false>(g, scratch, nscratch, s);
+static int num_cus() {
+    static int n = 0;
+    if (!n) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+    }
+    return n;
+}
+
+// Tile configuration and split-K factor from a cost model: every workgroup
+// slot (CUs x workgroups per CU) runs whole tiles in rounds; a round costs one
+// tile's FLOPs at the configuration's measured per-CU rate plus a fixed
+// prologue/epilogue time, and split-K adds its fp32 partial traffic.
+GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
+    struct Cand { int cfg, occ; double rate; };
+    static const Cand cands[] = {{CFG_256_256, 1, 3.1e12}, {CFG_128_128, 2, 2.8e12}};
+    static const int split_opts[] = {1, 2, 3, 4, 6, 8, 12, 16};
+    const int64_t mn = (int64_t)g.M * g.N;
+    const double out_bytes = out_bf(g) ? 2.0 : 4.0;
+    const int cus = num_cus();
+    int fcfg = -1, fsplits = 0;
+    const bool force = forced(&fcfg, &fsplits);
+    double best = 1e30;
+    int bcfg = CFG_128_128, bsplits = 1;
+    for (const Cand& c : cands) {
+        if (force && c.cfg != fcfg) continue;
+        for (int sp : split_opts) {
+            if (force && fsplits > 0 && sp != fsplits) continue;
+            const int kps = ceil_div(ceil_div(g.K, sp), GEMM_BK) * GEMM_BK;
+            const int used = ceil_div(g.K, kps);
+            if (used != sp) continue;
+            if (sp > 1 && ((size_t)sp * mn > nscratch || kps < 256)) continue;
+            const int64_t tiles = (int64_t)ceil_div(g.M, cfg_bm[c.cfg]) * ceil_div(g.N, cfg_bn[c.cfg]);
+            const int64_t slots = (int64_t)cus * c.occ;
+            const int64_t rounds = (tiles * sp + slots - 1) / slots;
+            double t = rounds * (c.occ * 2.0 * cfg_bm[c.cfg] * cfg_bn[c.cfg] * kps / c.rate + 2e-6);
+            if (sp > 1) t += (2.0 * sp * mn * 4.0 + mn * out_bytes) / 4e12;
+            if (t < best) { best = t; bcfg = c.cfg; bsplits = sp; }
+        }
+    }
+    if (force && fcfg != CFG_256_256 && fcfg != CFG_128_128) {   // configurations outside the model
+        bcfg = fcfg;
+        bsplits = fsplits > 0 ? fsplits : 1;
+        while (bsplits > 1 && ((size_t)bsplits * mn > nscratch || g.K / bsplits < 256)) --bsplits;
+    }
+    GemmPlan p{};
+    p.cfg = bcfg;
+    p.splits = bsplits;
+    const bool relu = bsplits == 1 && (g.epi == EPI_BIAS_ACT || g.epi == EPI_ACT_GRAD) && g.act == ACT_RELU2;
+    snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %s, %s, %d, %d, %d, %s>", cfg_bm[bcfg],
+             cfg_bn[bcfg], GEMM_BK, GEMM_NS, g.a_kc ? "true" : "false", g.b_kc ? "true" : "false",
+             bsplits > 1 ? 0 : g.epi, bsplits > 1 ? 0 : out_bf(g), relu ? 1 : 0, bsplits > 1 ? "true" : "false");
+    return p;
+}
+
+void gemm_mfma_main(const Gemm& g, const GemmPlan& p, float* scratch, hipStream_t s) {
+    if (g.a_kc && g.b_kc) run_cfg<true, true>(g, p, scratch, s);
+    else if (g.a_kc) run_cfg<true, false>(g, p, scratch, s);
+    else run_cfg<false, false>(g, p, scratch, s);
+}
+
+void gemm_mfma_reduce(const Gemm& g, const GemmPlan& p, const float* scratch, hipStream_t s) {
+    if (p.splits <= 1) return;
+    const int64_t chunks = (int64_t)g.M * (g.N / 8);
+    const unsigned nb = (unsigned)((chunks + 255) / 256);
+    const bool relu = g.act == ACT_RELU2;
+    switch (g.epi) {
+        case EPI_STORE:
+            if (g.c_bf) splitk_reduce_kernel<EPI_STORE, 1, 0><<<nb, 256, 0, s>>>(g, scratch, p.splits);
+            else splitk_reduce_kernel<EPI_STORE, 0, 0><<<nb, 256, 0, s>>>(g, scratch, p.splits);
+            break;
+        case EPI_BIAS: splitk_reduce_kernel<EPI_BIAS, 1, 0><<<nb, 256, 0, s>>>(g, scratch, p.splits); break;
+        case EPI_BIAS_ACT:
+            if (relu) splitk_reduce_kernel<EPI_BIAS_ACT, 1, ACT_RELU2><<<nb, 256, 0, s>>>(g, scratch, p.splits);
+            else splitk_reduce_kernel<EPI_BIAS_ACT, 1, ACT_GELU><<<nb, 256, 0, s>>>(g, scratch, p.splits);
+            break;
+        case EPI_BIAS_RESID: splitk_reduce_kernel<EPI_BIAS_RESID, 0, 0><<<nb, 256, 0, s>>>(g, scratch, p.splits); break;
+        case EPI_ACT_GRAD:
+            if (relu) splitk_reduce_kernel<EPI_ACT_GRAD, 1, ACT_RELU2><<<nb, 256, 0, s>>>(g, scratch, p.splits);
+            else splitk_reduce_kernel<EPI_ACT_GRAD, 1, ACT_GELU><<<nb, 256, 0, s>>>(g, scratch, p.splits);
+            break;
+        case EPI_ACCUM: splitk_reduce_kernel<EPI_ACCUM, 0, 0><<<nb, 256, 0, s>>>(g, scratch, p.splits); break;
+    }
 }
 
 }  // namespace gk

@@ -12,6 +12,7 @@
 // градиентов".
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -185,7 +186,9 @@ Ws plan(const gpt_config& c, const Table& tb, void* base) {
     w.cs_partial = cv.arr<float>(gk::colsum_partial_floats((int)M, (int)maxN));
     w.gn_partial = cv.arr<double>(1024);
     w.emb_scratch = cv.take(gk::embed_bwd_scratch_bytes((int)M, (int)d));
-    w.splitk_floats = (size_t)8 * std::max<int64_t>(3 * d * d, F * d);   // split-K slices of weight gradients
+    // fp32 slices of split-K products (matrix-core path only): weight
+    // gradients, the N = d products over M rows, and the tied head's gradient
+    w.splitk_floats = bf ? (size_t)std::max<int64_t>({8 * std::max<int64_t>(3 * d * d, F * d), 4 * M * d, 2 * Vp * d}) : 0;
     w.splitk = cv.arr<float>(w.splitk_floats);
     if (c.pos_encoding == GPT_POS_ROPE) {
         int64_t half = (d / H) / 2;
@@ -241,8 +244,9 @@ const char* kc_names[KC_COUNT] = {
     "gemm_wgrad", "gemm_lm_head_bwd", "layernorm_bwd", "colsum", "attention_bwd", "qk_prep", "embed_bwd",
     "grad_norm", "adamw", "misc"};
 
-struct Pending { int cls; hipEvent_t a, b; };
+struct Pending { int cls; int name; hipEvent_t a, b; double flops, bytes; };
 struct ClassStat { double ms = 0, flops = 0, bytes = 0; int64_t launches = 0; };
+struct NameStat { std::string name; ClassStat st; };
 
 }  // namespace
 
@@ -258,6 +262,8 @@ struct gpt_handle {
     std::vector<Pending> pending;
     std::vector<hipEvent_t> free_events;
     ClassStat stats[KC_COUNT];
+    std::vector<NameStat> names;     // per kernel (instantiation) name
+    std::string filter;              // also time launches of this kernel name
 };
 
 namespace {
@@ -279,24 +285,33 @@ hipEvent_t get_event(gpt_handle* h) {
     return e;
 }
 
+int name_index(gpt_handle* h, const char* name) {
+    for (size_t i = 0; i < h->names.size(); ++i)
+        if (h->names[i].name == name) return (int)i;
+    h->names.push_back({name, ClassStat()});
+    return (int)h->names.size() - 1;
+}
+
+// Brackets one kernel launch with events when its class is enabled or its
+// kernel name is the filter; the statistics count timed launches only.
 struct Timed {
     gpt_handle* h;
     int cls;
-    hipEvent_t a = nullptr, b = nullptr;
-    Timed(gpt_handle* h_, int cls_, double flops, double bytes) : h(h_), cls(cls_) {
-        h->stats[cls].flops += flops;
-        h->stats[cls].bytes += bytes;
-        h->stats[cls].launches += 1;
-        if (h->timing_mask & (1u << cls)) {
+    const char* name;
+    double flops, bytes;
+    hipEvent_t a = nullptr;
+    Timed(gpt_handle* h_, int cls_, double flops_, double bytes_, const char* name_ = nullptr)
+        : h(h_), cls(cls_), name(name_ ? name_ : kc_names[cls_]), flops(flops_), bytes(bytes_) {
+        if ((h->timing_mask & (1u << cls)) || (!h->filter.empty() && h->filter == name)) {
             a = get_event(h);
             (void)hipEventRecord(a, h->stream);
         }
     }
     ~Timed() {
         if (a) {
-            b = get_event(h);
+            hipEvent_t b = get_event(h);
             (void)hipEventRecord(b, h->stream);
-            h->pending.push_back({cls, a, b});
+            h->pending.push_back({cls, name_index(h, name), a, b, flops, bytes});
         }
     }
 };
@@ -306,7 +321,14 @@ void drain_timing(gpt_handle* h) {
     (void)hipStreamSynchronize(h->stream);
     for (auto& p : h->pending) {
         float ms = 0.f;
-        if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) h->stats[p.cls].ms += ms;
+        if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+            for (ClassStat* c : {&h->stats[p.cls], &h->names[p.name].st}) {
+                c->ms += ms;
+                c->flops += p.flops;
+                c->bytes += p.bytes;
+                c->launches += 1;
+            }
+        }
         h->free_events.push_back(p.a);
         h->free_events.push_back(p.b);
     }
@@ -322,10 +344,17 @@ const void* Wop(gpt_handle* h, int idx) {
 }
 
 void run_gemm(gpt_handle* h, int cls, const gk::Gemm& g) {
-    double ab = g.in_bf ? 2 : 4, cb = g.c_bf ? 2 : 4;
-    double bytes = ab * ((double)g.M * g.K + (double)g.K * g.N) + cb * (double)g.M * g.N;
-    Timed t(h, cls, 2.0 * g.M * g.N * g.K, bytes);
-    gk::gemm(g, h->ws.splitk, h->ws.splitk_floats, h->stream);
+    const double ab = g.in_bf ? 2 : 4, cb = g.c_bf ? 2 : 4;
+    const double bytes = ab * ((double)g.M * g.K + (double)g.K * g.N) + cb * (double)g.M * g.N;
+    const gk::GemmPlan plan = gk::gemm_plan(g, h->ws.splitk_floats);
+    {
+        Timed t(h, cls, 2.0 * g.M * g.N * g.K, bytes, plan.name);
+        gk::gemm_main(g, plan, h->ws.splitk, h->stream);
+    }
+    if (plan.splits > 1) {
+        Timed t(h, cls, 0, 4.0 * plan.splits * g.M * g.N + cb * (double)g.M * g.N, "splitk_reduce_kernel");
+        gk::gemm_finish(g, plan, h->ws.splitk, h->stream);
+    }
 }
 
 gk::Gemm mk_gemm(gpt_handle* h, int M, int N, int K, const void* A, int64_t lda, bool a_kc, const void* B,
@@ -842,6 +871,7 @@ gpt_status gpt_reset_kernel_timing(gpt_handle* h) {
     if (!h) return GPT_ERR_INVALID_ARGUMENT;
     drain_timing(h);
     for (auto& c : h->stats) c = ClassStat();
+    for (auto& n : h->names) n.st = ClassStat();
     return GPT_OK;
 }
 gpt_status gpt_num_kernel_classes(int32_t* n) {
@@ -858,6 +888,30 @@ gpt_status gpt_kernel_timing(gpt_handle* h, int32_t cls, const char** name, doub
     if (launches) *launches = h->stats[cls].launches;
     if (flops) *flops = h->stats[cls].flops;
     if (bytes) *bytes = h->stats[cls].bytes;
+    return GPT_OK;
+}
+gpt_status gpt_set_kernel_timing_filter(gpt_handle* h, const char* kernel_name) {
+    if (!h) return GPT_ERR_INVALID_ARGUMENT;
+    h->filter = kernel_name ? kernel_name : "";
+    return GPT_OK;
+}
+gpt_status gpt_num_kernel_names(gpt_handle* h, int32_t* n) {
+    if (!h || !n) return GPT_ERR_INVALID_ARGUMENT;
+    drain_timing(h);
+    *n = (int32_t)h->names.size();
+    return GPT_OK;
+}
+gpt_status gpt_kernel_name_timing(gpt_handle* h, int32_t idx, const char** name, double* total_ms, int64_t* launches,
+                                  double* flops, double* bytes) {
+    if (!h) return GPT_ERR_INVALID_ARGUMENT;
+    drain_timing(h);
+    if (idx < 0 || idx >= (int32_t)h->names.size()) return GPT_ERR_INVALID_ARGUMENT;
+    const NameStat& s = h->names[idx];
+    if (name) *name = s.name.c_str();
+    if (total_ms) *total_ms = s.st.ms;
+    if (launches) *launches = s.st.launches;
+    if (flops) *flops = s.st.flops;
+    if (bytes) *bytes = s.st.bytes;
     return GPT_OK;
 }
 

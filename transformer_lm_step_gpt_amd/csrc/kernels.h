@@ -103,9 +103,20 @@ struct Gemm {
     int act;
     bool in_bf;                              // A and B storage (bf16 or fp32)
 };
+// How a product runs: kernel (matrix-core tile configuration, or cfg = -1
+// for the portable kernel), split-K factor, and the name of the main kernel
+// instantiation (as profilers print it).
+struct GemmPlan {
+    int cfg = -1;
+    int splits = 1;
+    char name[112] = {0};
+};
 // scratch: split-K partials for the matrix-core kernel (may be null: no split)
+GemmPlan gemm_plan(const Gemm& g, size_t splitk_floats);
+// main kernel, then (split-K only) the kernel that sums the slices
+void gemm_main(const Gemm& g, const GemmPlan& p, float* splitk_scratch, hipStream_t s);
+void gemm_finish(const Gemm& g, const GemmPlan& p, const float* splitk_scratch, hipStream_t s);
 void gemm(const Gemm& g, float* splitk_scratch, size_t splitk_floats, hipStream_t s);
-const char* gemm_last_kernel_name();
 
 // ---------------------------------------------------------------- attention
 struct Attn {

@@ -89,6 +89,10 @@ _SIGS = [
     ("gpt_num_kernel_classes", c_int32, [POINTER(c_int32)]),
     ("gpt_kernel_timing", c_int32, [c_void_p, c_int32, POINTER(c_char_p), POINTER(c_double), POINTER(c_int64),
                                     POINTER(c_double), POINTER(c_double)]),
+    ("gpt_set_kernel_timing_filter", c_int32, [c_void_p, c_char_p]),
+    ("gpt_num_kernel_names", c_int32, [c_void_p, POINTER(c_int32)]),
+    ("gpt_kernel_name_timing", c_int32, [c_void_p, c_int32, POINTER(c_char_p), POINTER(c_double), POINTER(c_int64),
+                                         POINTER(c_double), POINTER(c_double)]),
     # test-only kernel entry points
     ("gptk_gemm", c_int32, [c_int32, c_int32, c_int32, c_void_p, c_int64, c_int32, c_void_p, c_int64, c_int32,
                             c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
@@ -309,4 +313,22 @@ class GPT:
                                              byref(by)), self.handle)
             out.append({"class": i, "name": name.value.decode(), "ms": ms.value, "launches": launches.value,
                         "flops": fl.value, "bytes": by.value})
+        return out
+
+    def set_kernel_timing_filter(self, kernel_name) -> None:
+        """Also time every launch of this kernel instantiation (None: none)."""
+        arg = kernel_name.encode() if kernel_name else None
+        check(self.lib.gpt_set_kernel_timing_filter(self.handle, arg), self.handle)
+
+    def kernel_name_timing(self) -> List[dict]:
+        """Per kernel name: summed event time, launches, FLOPs and bytes of the timed launches."""
+        n = c_int32()
+        check(self.lib.gpt_num_kernel_names(self.handle, byref(n)), self.handle)
+        out = []
+        for i in range(n.value):
+            name, ms, launches, fl, by = c_char_p(), c_double(), c_int64(), c_double(), c_double()
+            check(self.lib.gpt_kernel_name_timing(self.handle, i, byref(name), byref(ms), byref(launches), byref(fl),
+                                                  byref(by)), self.handle)
+            out.append({"name": name.value.decode(), "ms": ms.value, "launches": launches.value, "flops": fl.value,
+                        "bytes": by.value})
         return out

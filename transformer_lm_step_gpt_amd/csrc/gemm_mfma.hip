@@ -179,15 +179,15 @@ constexpr int GROUP_M = 8;
 // OUTBF: output storage bf16 (1) or fp32 (0); ACT: activation of the
 // BIAS_ACT / ACT_GRAD epilogues. N and ldc are multiples of 8 and the output,
 // aux, residual and bias buffers 16-byte aligned (gemm_mfma_ok).
-template <int BM, int BN, int BK, int NS, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(Gemm g, int kps, float* part) {
+template <int BM, int BN, int BK, int NS, int OCC, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
+__global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, float* part) {
     using TC = typename std::conditional<OUTBF != 0, bf16, float>::type;
     constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
     using TA = OpTile<AKC, BM, BK>;
     using TB = OpTile<BKC, BN, BK>;
     constexpr int STAGE = (TA::BYTES + TB::BYTES) / 2;      // bf16 elements per stage
     constexpr int LPT = TA::PER_WAVE + TB::PER_WAVE;        // DMAs per lane per stage
-    static_assert(NS >= 2 && NS <= 4, "stages");
+    static_assert(NS >= 3 && NS <= 5, "stages");
     extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
     bf16* smem = reinterpret_cast<bf16*>(smem_raw);
 
@@ -229,7 +229,8 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(Gemm g, int kps, floa
     // wait until tile u is in LDS for every wave: at most (tiles issued after u) x LPT DMAs pending
     auto wait_tile = [&](int u) {
         const int ahead = issued - 1 - u;
-        if (ahead >= 2) wait_vmcnt<2 * LPT>();
+        if (ahead >= 3) wait_vmcnt<3 * LPT>();
+        else if (ahead == 2) wait_vmcnt<2 * LPT>();
         else if (ahead == 1) wait_vmcnt<LPT>();
         else wait_vmcnt<0>();
         barrier_no_fence();
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(Gemm g, int kps, floa
     //   wait + barrier for tile t+1; DMA of tile t+NS-1 into the stage of tile
     //   t-1 (every wave finished reading it before this barrier)
     //   reads of step 0 of tile t+1        | products of step 1 of tile t
-    static_assert(BK == 32 && NS <= 4, "two 16-deep steps per k-tile; vmcnt bookkeeping for <= 2 tiles ahead");
+    static_assert(BK == 32 && NS <= 5, "two 16-deep steps per k-tile; vmcnt bookkeeping for <= 3 tiles ahead");
     bf16x8 a0[FM], b0[FN], a1[FM], b1[FN];
     if (nk > 0) {
         wait_tile(0);
@@ -356,17 +357,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Gemm g, const float*
 
 // ------------------------------------------------------------------ dispatch
 
-// Tile configurations (BM, BN; BK = 32, 4 stages).
+// Tile configurations: BM x BN output tile, NS k-tile stages of BK = 32,
+// OCC workgroups per CU (register and LDS budget).
 enum GemmCfg { CFG_256_256 = 0, CFG_128_256, CFG_128_128, CFG_256_128, CFG_COUNT };
 static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256};
 static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128};
-constexpr int GEMM_BK = 32, GEMM_NS = 4;
+static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3};
+static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2};
+constexpr int GEMM_BK = 32;
 
-template <int BM, int BN, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
+template <int BM, int BN, int NS, int OCC, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
 static void launch(const Gemm& g, dim3 grid, int kps, float* part, hipStream_t s) {
-    constexpr size_t LDS = (size_t)GEMM_NS * (BM + BN) * GEMM_BK * sizeof(bf16);
-    static_assert(LDS <= 160 * 1024, "LDS budget");
-    auto k = gemm_mfma_kernel<BM, BN, GEMM_BK, GEMM_NS, AKC, BKC, EPI, OUTBF, ACT, SPLIT>;
+    constexpr size_t LDS = (size_t)NS * (BM + BN) * GEMM_BK * sizeof(bf16);
+    static_assert(LDS * OCC <= 160 * 1024, "LDS budget");
+    auto k = gemm_mfma_kernel<BM, BN, GEMM_BK, NS, OCC, AKC, BKC, EPI, OUTBF, ACT, SPLIT>;
     static bool attr = false;
     if (!attr) {
         (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
@@ -383,38 +387,38 @@ static int out_bf(const Gemm& g) {
     return 1;
 }
 
-template <int BM, int BN, bool AKC, bool BKC>
+template <int BM, int BN, int NS, int OCC, bool AKC, bool BKC>
 static void run_main(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
     dim3 grid(ceil_div(g.N, BN) * ceil_div(g.M, BM), 1, p.splits);
     const int kps = ceil_div(ceil_div(g.K, p.splits), GEMM_BK) * GEMM_BK;
-    if (p.splits > 1) { launch<BM, BN, AKC, BKC, EPI_STORE, 0, 0, true>(g, grid, kps, part, s); return; }
+    if (p.splits > 1) { launch<BM, BN, NS, OCC, AKC, BKC, EPI_STORE, 0, 0, true>(g, grid, kps, part, s); return; }
     const bool relu = g.act == ACT_RELU2;
     switch (g.epi) {
         case EPI_STORE:
-            if (g.c_bf) launch<BM, BN, AKC, BKC, EPI_STORE, 1, 0, false>(g, grid, kps, part, s);
-            else launch<BM, BN, AKC, BKC, EPI_STORE, 0, 0, false>(g, grid, kps, part, s);
+            if (g.c_bf) launch<BM, BN, NS, OCC, AKC, BKC, EPI_STORE, 1, 0, false>(g, grid, kps, part, s);
+            else launch<BM, BN, NS, OCC, AKC, BKC, EPI_STORE, 0, 0, false>(g, grid, kps, part, s);
             break;
-        case EPI_BIAS: launch<BM, BN, AKC, BKC, EPI_BIAS, 1, 0, false>(g, grid, kps, part, s); break;
+        case EPI_BIAS: launch<BM, BN, NS, OCC, AKC, BKC, EPI_BIAS, 1, 0, false>(g, grid, kps, part, s); break;
         case EPI_BIAS_ACT:
-            if (relu) launch<BM, BN, AKC, BKC, EPI_BIAS_ACT, 1, ACT_RELU2, false>(g, grid, kps, part, s);
-            else launch<BM, BN, AKC, BKC, EPI_BIAS_ACT, 1, ACT_GELU, false>(g, grid, kps, part, s);
+            if (relu) launch<BM, BN, NS, OCC, AKC, BKC, EPI_BIAS_ACT, 1, ACT_RELU2, false>(g, grid, kps, part, s);
+            else launch<BM, BN, NS, OCC, AKC, BKC, EPI_BIAS_ACT, 1, ACT_GELU, false>(g, grid, kps, part, s);
             break;
-        case EPI_BIAS_RESID: launch<BM, BN, AKC, BKC, EPI_BIAS_RESID, 0, 0, false>(g, grid, kps, part, s); break;
+        case EPI_BIAS_RESID: launch<BM, BN, NS, OCC, AKC, BKC, EPI_BIAS_RESID, 0, 0, false>(g, grid, kps, part, s); break;
         case EPI_ACT_GRAD:
-            if (relu) launch<BM, BN, AKC, BKC, EPI_ACT_GRAD, 1, ACT_RELU2, false>(g, grid, kps, part, s);
-            else launch<BM, BN, AKC, BKC, EPI_ACT_GRAD, 1, ACT_GELU, false>(g, grid, kps, part, s);
+            if (relu) launch<BM, BN, NS, OCC, AKC, BKC, EPI_ACT_GRAD, 1, ACT_RELU2, false>(g, grid, kps, part, s);
+            else launch<BM, BN, NS, OCC, AKC, BKC, EPI_ACT_GRAD, 1, ACT_GELU, false>(g, grid, kps, part, s);
             break;
-        case EPI_ACCUM: launch<BM, BN, AKC, BKC, EPI_ACCUM, 0, 0, false>(g, grid, kps, part, s); break;
+        case EPI_ACCUM: launch<BM, BN, NS, OCC, AKC, BKC, EPI_ACCUM, 0, 0, false>(g, grid, kps, part, s); break;
     }
 }
 
 template <bool AKC, bool BKC>
 static void run_cfg(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
     switch (p.cfg) {
-        case CFG_256_256: run_main<256, 256, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_256: run_main<128, 256, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_128: run_main<128, 128, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_128: run_main<256, 128, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256: run_main<256, 256, 4, 1, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_256: run_main<128, 256, 4, 1, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128: run_main<128, 128, 4, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128: run_main<256, 128, 3, 2, AKC, BKC>(g, p, part, s); break;
     }
 }
 
@@ -462,7 +466,7 @@ static int num_cus() {
 // prologue/epilogue time, and split-K adds its fp32 partial traffic.
 GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
     struct Cand { int cfg, occ; double rate; };
-    static const Cand cands[] = {{CFG_256_256, 1, 3.1e12}, {CFG_128_128, 2, 2.8e12}};
+    static const Cand cands[] = {{CFG_256_256, 1, 3.05e12}, {CFG_256_128, 2, 3.3e12}, {CFG_128_128, 2, 2.8e12}};
     static const int split_opts[] = {1, 2, 3, 4, 6, 8, 12, 16};
     const int64_t mn = (int64_t)g.M * g.N;
     const double out_bytes = out_bf(g) ? 2.0 : 4.0;
@@ -487,7 +491,7 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
             if (t < best) { best = t; bcfg = c.cfg; bsplits = sp; }
         }
     }
-    if (force && fcfg != CFG_256_256 && fcfg != CFG_128_128) {   // configurations outside the model
+    if (force && fcfg == CFG_128_256) {   // configuration outside the cost model
         bcfg = fcfg;
         bsplits = fsplits > 0 ? fsplits : 1;
         while (bsplits > 1 && ((size_t)bsplits * mn > nscratch || g.K / bsplits < 256)) --bsplits;
@@ -496,8 +500,8 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
     p.cfg = bcfg;
     p.splits = bsplits;
     const bool relu = bsplits == 1 && (g.epi == EPI_BIAS_ACT || g.epi == EPI_ACT_GRAD) && g.act == ACT_RELU2;
-    snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %s, %s, %d, %d, %d, %s>", cfg_bm[bcfg],
-             cfg_bn[bcfg], GEMM_BK, GEMM_NS, g.a_kc ? "true" : "false", g.b_kc ? "true" : "false",
+    snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %s, %s, %d, %d, %d, %s>", cfg_bm[bcfg],
+             cfg_bn[bcfg], GEMM_BK, cfg_ns[bcfg], cfg_occ[bcfg], g.a_kc ? "true" : "false", g.b_kc ? "true" : "false",
              bsplits > 1 ? 0 : g.epi, bsplits > 1 ? 0 : out_bf(g), relu ? 1 : 0, bsplits > 1 ? "true" : "false");
     return p;
 }

@@ -8,8 +8,9 @@
 //     (BM/2) x (BN/2) sub-tile made of 32x32 MFMA fragments.
 //   * Global -> LDS copies use the 16-byte LDS-DMA load (each lane's 16
 //     bytes land at LDS base + 16 * lane), so no registers are spent on
-//     staging and NS - 1 k-tiles are in flight at once (a ring of NS LDS
-//     stages; a k-tile is waited for with s_waitcnt vmcnt only when consumed).
+//     staging, and a k-tile is copied as soon as its stage is free (a ring of
+//     NS LDS stages; a k-tile is waited for with s_waitcnt vmcnt only when
+//     consumed).
 //   * An operand stored k-contiguous (X and W of X W^T) is kept as a
 //     [row][BK] tile; a fragment (8 consecutive k of one row per lane) is one
 //     16-byte LDS read.
@@ -79,17 +80,20 @@ struct RowTile {
     static constexpr int READS_PER_FRAG = 1;
     static_assert(DMAS % 4 == 0, "tile too small for 4 waves");
     GPT_DEV static int swz(int r) { return CH == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
-    // issue this wave's DMAs for rows [row0, row0 + R), k [k0, k0 + BK)
-    GPT_DEV static void load(bf16* tile, const bf16* base, int64_t ld, int row0, int rows, int k0, int w, int lane) {
+    // per-lane sources of this wave's DMAs for rows [row0, row0 + R), k [k0, k0 + BK);
+    // each later k-tile is STEP elements further on
+    GPT_DEV static void src_init(const bf16* (&src)[PER_WAVE], const bf16* base, int64_t ld, int row0, int rows, int k0,
+                                 int w, int lane) {
 #pragma unroll
         for (int p = 0; p < PER_WAVE; ++p) {
             const int d = w * PER_WAVE + p;
             const int r = d * ROWS_PER_DMA + lane / CH;
             const int kc = (lane % CH) ^ swz(r);
             const int gr = min(row0 + r, rows - 1);    // rows past the end feed only unstored outputs
-            dma16(base + (int64_t)gr * ld + k0 + kc * 8, tile + d * 512);
+            src[p] = base + (int64_t)gr * ld + k0 + kc * 8;
         }
     }
+    GPT_DEV static int64_t step(int64_t) { return BK; }
     // 8 consecutive k (16*ks + 8*hk ...) of row r
     GPT_DEV static bf16x8 frag(const bf16* tile, int r, int ks, int hk) {
         const int kc = 2 * ks + hk;
@@ -108,16 +112,18 @@ struct ColTile {
     static constexpr int READS_PER_FRAG = 2;
     static_assert(CH >= 16 && DMAS % 4 == 0, "unsupported tile");
     GPT_DEV static int swz(int k) { return (k & 3) << 2; }
-    GPT_DEV static void load(bf16* tile, const bf16* base, int64_t ld, int row0, int rows, int k0, int w, int lane) {
+    GPT_DEV static void src_init(const bf16* (&src)[PER_WAVE], const bf16* base, int64_t ld, int row0, int rows, int k0,
+                                 int w, int lane) {
 #pragma unroll
         for (int p = 0; p < PER_WAVE; ++p) {
             const int d = w * PER_WAVE + p;
             const int k = d * KROWS_PER_DMA + lane / CH;
             const int c = (lane % CH) ^ swz(k);
             const int gr = min(row0 + c * 8, rows - 8);   // rows % 8 == 0
-            dma16(base + (int64_t)(k0 + k) * ld + gr, tile + d * 512);
+            src[p] = base + (int64_t)(k0 + k) * ld + gr;
         }
     }
+    GPT_DEV static int64_t step(int64_t ld) { return BK * ld; }
     GPT_DEV static s16x4 tr_read(const bf16* tile, int k, int r) {
         const bf16* p = tile + k * R + (((r >> 3) ^ swz(k)) << 3) + (r & 7);
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
@@ -151,24 +157,24 @@ struct OpTile<false, R, BK> : ColTile<R, BK> {
 }  // namespace
 
 // One half-step: the FM x FN products of (ca, cb), with the fragment reads of
-// the next half-step (into na, nb) spread between them in program order so the
-// LDS latency hides under the matrix cores.
-template <int FM, int FN, class TA, class TB, bool LOAD>
+// the next half-step (into na, nb) and the operations of `extra` (slot p runs
+// after product p) spread between them in program order, so LDS latency and
+// DMA issue hide under the matrix cores.
+template <int FM, int FN, class TA, class TB, class X>
 __device__ __attribute__((always_inline)) inline void half_step(f32x16 (&acc)[FM][FN], const bf16x8 (&ca)[FM],
                                                                const bf16x8 (&cb)[FN], bf16x8 (&na)[FM],
                                                                bf16x8 (&nb)[FN], const bf16* as, const bf16* bs, int wm,
-                                                               int wn, int ksn, int lane) {
+                                                               int wn, int ksn, int lane, X&& extra) {
     constexpr int NF = FM + FN, P = FM * FN;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         acc[p / FN][p % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[p / FN], cb[p % FN], acc[p / FN][p % FN], 0, 0, 0);
-        if constexpr (LOAD) {
-            if ((p * NF) / P != ((p + 1) * NF) / P) {
-                const int f = (p * NF) / P;
-                if (f < FM) na[f] = TA::get(as, wm + 32 * f, ksn, lane);
-                else nb[f - FM] = TB::get(bs, wn + 32 * (f - FM), ksn, lane);
-            }
+        if ((p * NF) / P != ((p + 1) * NF) / P) {
+            const int f = (p * NF) / P;
+            if (f < FM) na[f] = TA::get(as, wm + 32 * f, ksn, lane);
+            else nb[f - FM] = TB::get(bs, wn + 32 * (f - FM), ksn, lane);
         }
+        extra(p);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
     using TB = OpTile<BKC, BN, BK>;
     constexpr int STAGE = (TA::BYTES + TB::BYTES) / 2;      // bf16 elements per stage
     constexpr int LPT = TA::PER_WAVE + TB::PER_WAVE;        // DMAs per lane per stage
-    static_assert(NS >= 3 && NS <= 5, "stages");
+    static_assert(NS >= 3 && NS <= 4, "stages");
     extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
     bf16* smem = reinterpret_cast<bf16*>(smem_raw);
 
@@ -217,17 +223,31 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    int issued = 0;   // tiles 0 .. issued-1 have been handed to the LDS-DMA engine
-    auto issue_next = [&]() {
-        if (issued < nk) {
-            bf16* st = smem + (issued % NS) * STAGE;
-            TA::load(st, A, g.lda, m0, g.M, kb + issued * BK, w, lane);
-            TB::load(st + TA::BYTES / 2, B, g.ldb, n0, g.N, kb + issued * BK, w, lane);
-            ++issued;
+    // LDS-DMA sources: this wave's PA + PB 16-byte-per-lane copies per k-tile
+    constexpr int PA = TA::PER_WAVE, PB = TB::PER_WAVE;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const bf16* srcA[PA];
+    const bf16* srcB[PB];
+    TA::src_init(srcA, A, g.lda, m0, g.M, kb, wu, lane);
+    TB::src_init(srcB, B, g.ldb, n0, g.N, kb, wu, lane);
+    const int64_t stA = TA::step(g.lda), stB = TB::step(g.ldb);
+    // q-th copy of this wave for the k-tile going into stage st
+    auto dma = [&](int q, bf16* st) {
+        if (q < PA) {
+            dma16(srcA[q], st + (wu * PA + q) * 512);
+            srcA[q] += stA;
+        } else {
+            dma16(srcB[q - PA], st + TA::BYTES / 2 + (wu * PB + q - PA) * 512);
+            srcB[q - PA] += stB;
         }
     };
-    // wait until tile u is in LDS for every wave: at most (tiles issued after u) x LPT DMAs pending
+
+    int issued = 0;   // tiles 0 .. issued-1 have been handed to the LDS-DMA engine
+    // wait until tile u is in LDS for every wave: at most (tiles issued after u) x LPT DMAs pending.
+    // The wave's own LDS reads complete first, so after the barrier no wave
+    // still reads the stage that the next DMA overwrites.
     auto wait_tile = [&](int u) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const int ahead = issued - 1 - u;
         if (ahead >= 3) wait_vmcnt<3 * LPT>();
         else if (ahead == 2) wait_vmcnt<2 * LPT>();
@@ -244,34 +264,48 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
         for (int j = 0; j < FN; ++j) b[j] = TB::get(bs, wn + 32 * j, ks, lane);
     };
 
-    for (int t = 0; t < NS - 1; ++t) issue_next();
+    for (int t = 0; t < NS; ++t) {
+        if (issued < nk) {
+            bf16* st = smem + (issued % NS) * STAGE;
+#pragma unroll
+            for (int q = 0; q < LPT; ++q) dma(q, st);
+            ++issued;
+        }
+    }
 
     // Software pipeline over half k-tiles (BK = 32: two 16-deep steps per tile):
     //   reads of step 1 of tile t          | products of step 0 of tile t
-    //   wait + barrier for tile t+1; DMA of tile t+NS-1 into the stage of tile
-    //   t-1 (every wave finished reading it before this barrier)
+    //   wait + barrier for tile t+1
+    //   DMA of tile t+NS into the stage of tile t (every wave finished
+    //   reading tile t before this barrier), issued after the first product;
     //   reads of step 0 of tile t+1        | products of step 1 of tile t
-    static_assert(BK == 32 && NS <= 5, "two 16-deep steps per k-tile; vmcnt bookkeeping for <= 3 tiles ahead");
+    static_assert(BK == 32 && NS <= 4, "two 16-deep steps per k-tile; vmcnt bookkeeping for <= 3 tiles ahead");
     bf16x8 a0[FM], b0[FN], a1[FM], b1[FN];
     if (nk > 0) {
         wait_tile(0);
         frags(0, 0, a0, b0);
     }
+    auto none = [](int) {};
     for (int t = 0; t < nk; ++t) {
         {
             const bf16* as = smem + (t % NS) * STAGE;
-            half_step<FM, FN, TA, TB, true>(acc, a0, b0, a1, b1, as, as + TA::BYTES / 2, wm, wn, 1, lane);
+            half_step<FM, FN, TA, TB>(acc, a0, b0, a1, b1, as, as + TA::BYTES / 2, wm, wn, 1, lane, none);
         }
-        if (t + 1 < nk) {
-            wait_tile(t + 1);
-            issue_next();
-        }
+        if (t + 1 < nk) wait_tile(t + 1);
         __builtin_amdgcn_sched_barrier(0);
         {
             // on the last tile this prefetch reads a stage that holds no new tile;
             // the values are never used
             const bf16* as = smem + ((t + 1) % NS) * STAGE;
-            half_step<FM, FN, TA, TB, true>(acc, a1, b1, a0, b0, as, as + TA::BYTES / 2, wm, wn, 0, lane);
+            bf16* st = smem + (issued % NS) * STAGE;
+            const bool copy = issued < nk;
+            auto issue = [&](int p) {
+#pragma unroll
+                for (int q = 0; q < LPT; ++q)
+                    if (p == 0 && copy) dma(q, st);
+            };
+            half_step<FM, FN, TA, TB>(acc, a1, b1, a0, b0, as, as + TA::BYTES / 2, wm, wn, 0, lane, issue);
+            if (copy) ++issued;
         }
     }
 

@@ -166,16 +166,18 @@ def main():
     torch.cuda.set_device(dev)
     model = GPT(cfg, seed=w.init_seed, device=dev)
     it = I.batches(w)
-    n_batches = a.warmup + a.steps
-    data = [next(it) for _ in range(min(n_batches, 8))]
+    # one step = w.accum micro-batches (consecutive batches of the stream) + clip + AdamW
+    n_batches = max(w.accum, min(a.warmup + a.steps, 8))
+    data = [next(it) for _ in range(n_batches)]
     toks = [(torch.tensor(x, device=dev), torch.tensor(y, device=dev)) for x, y in data]
     torch.cuda.synchronize()
 
     step_no = [0]
 
     def step(i):
-        x, y = toks[i % len(toks)]
-        model.forward_backward(x, y, 1.0, sync=False)
+        for j in range(w.accum):
+            x, y = toks[(i * w.accum + j) % len(toks)]
+            model.forward_backward(x, y, 1.0 / w.accum, sync=False)
         step_no[0] += 1
         model.clip_and_adamw(w.lr, step_no[0], sync=False)
 
@@ -204,7 +206,7 @@ def main():
     timed = next(r for r in model.kernel_name_timing() if r["name"] == dom)
     model.set_kernel_timing_filter(None)
 
-    tokens = a.steps * B * T
+    tokens = a.steps * w.accum * B * T
     tps = tokens / dt
     fpt = model_flops_per_token(cfg, T)
     mfu = tps * fpt / (PEAK_BF16_TFLOPS * 1e12)
@@ -239,7 +241,7 @@ def main():
         "warmup": a.warmup, "ms_per_step": round(1e3 * dt / a.steps, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg.precision == "bf16" else "fp32",
         "data": "synthetic (seeded Zipf(1.1) tokens with end-of-text document starts; random-init weights)",
-        "config": {"workload": f"{w.name}: {w.description}", "global_batch": B, "seq_len": T,
+        "config": {"workload": f"{w.name}: {w.description}", "global_batch": B * w.accum, "seq_len": T,
                    "parallelism": "single GPU"},
         "mfma_util_pct": round(100 * mfu, 2),
         "model_flops_per_token": fpt,

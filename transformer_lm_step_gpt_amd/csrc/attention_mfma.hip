@@ -73,8 +73,9 @@ GPT_DEV f32x16 zero16() {
 
 GPT_DEV bf16x8 load8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// evaluated without branches (bitwise and/or of the comparisons)
 GPT_DEV bool visible(int q, int key, int T, int W) {
-    return key <= q && key < T && q < T && (W <= 0 || q - key < W);
+    return (key <= q) & (key < T) & (q < T) & ((W <= 0) | (q - key < W));
 }
 
 // A [64][HD] bf16 tile of one head in LDS, filled by LDS-DMA.
@@ -162,7 +163,9 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
     const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
     const int T = a.T, W = a.window;
     const int q0 = qt * ATT_BQ;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, hh = lane >> 5;
+    // the wave index as a wave-uniform (scalar) value, so per-wave tests are scalar branches
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lr = lane & 31,
+              hh = lane >> 5;
     const int qw = q0 + w * 32, myq = qw + lr;
     const bf16* Q = (const bf16*)a.q + (int64_t)b * T * a.ldq + h * HD;
     const int kend = min(T, q0 + ATT_BQ);
@@ -205,15 +208,15 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 if (need_mask) {
-                    int key = kt + kf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-                    if (!visible(myq, key, T, W)) s[kf][e] = -INFINITY;
+                    const int key = kt + kf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+                    s[kf][e] = visible(myq, key, T, W) ? s[kf][e] : -INFINITY;
                 }
                 tmax = fmaxf(tmax, s[kf][e]);
             }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float mnew = fmaxf(mrow, tmax);
         const float mc = mnew == -INFINITY ? 0.f : mnew * c;
-        const float corr = exp2f(mrow * c - mc);
+        const float corr = __builtin_amdgcn_exp2f(mrow * c - mc);
         mrow = mnew;
         lsum *= corr;
 #pragma unroll
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
         for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                float p = exp2f(fmaf(s[kf][e], c, -mc));
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[kf][e], c, -mc));
                 lsum += p;
                 pk[2 * kf + (e >> 3)][e & 7] = (bf16)p;
             }
@@ -262,7 +265,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(Attn a) {
     const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
     const int T = a.T, W = a.window;
     const int k0 = blockIdx.x * ATT_BQ;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, hh = lane >> 5;
+    // the wave index as a wave-uniform (scalar) value, so per-wave tests are scalar branches
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lr = lane & 31,
+              hh = lane >> 5;
     const int kw = k0 + w * 32, mykey = kw + lr;
     const bf16* K = (const bf16*)a.k + (int64_t)b * T * a.ldk + h * HD;
     const bf16* V = (const bf16*)a.v + (int64_t)b * T * a.ldv + h * HD;
@@ -319,8 +324,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(Attn a) {
             for (int e = 0; e < 16; ++e) {
                 const int qi = qf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
                 const float lv = (&lq[e >> 2].x)[e & 3], dv4 = (&dq4[e >> 2].x)[e & 3];
-                float p = exp2f(fmaf(s[e], c, -lv));
-                if (need_mask && !visible(qt + qi, mykey, T, W)) p = 0.f;
+                float p = __builtin_amdgcn_exp2f(fmaf(s[e], c, -lv));
+                if (need_mask) p = visible(qt + qi, mykey, T, W) ? p : 0.f;
                 const float dsv = p * (dp[e] - dv4);
                 pk[e >> 3][e & 7] = (bf16)p;
                 dsk[e >> 3][e & 7] = (bf16)dsv;
@@ -365,7 +370,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
     const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
     const int T = a.T, W = a.window;
     const int q0 = qtile * ATT_BQ;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 31, hh = lane >> 5;
+    // the wave index as a wave-uniform (scalar) value, so per-wave tests are scalar branches
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lr = lane & 31,
+              hh = lane >> 5;
     const int qw = q0 + w * 32, myq = qw + lr;
     const bf16* Q = (const bf16*)a.q + (int64_t)b * T * a.ldq + h * HD;
     const bf16* G = (const bf16*)a.dO + (int64_t)b * T * a.lddo + h * HD;
@@ -421,10 +428,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
             bf16x8 dsk[2];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                float p = exp2f(fmaf(s[e], c, -lse2));
+                float p = __builtin_amdgcn_exp2f(fmaf(s[e], c, -lse2));
                 if (need_mask) {
-                    int key = kt + kf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-                    if (!visible(myq, key, T, W)) p = 0.f;
+                    const int key = kt + kf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+                    p = visible(myq, key, T, W) ? p : 0.f;
                 }
                 dsk[e >> 3][e & 7] = (bf16)(p * (dp[e] - Dq));
             }

@@ -417,49 +417,72 @@ size_t layernorm_bwd_partial_floats(int M, int d) {
     return (size_t)3 * nb * d + (size_t)3 * ceil_div(nb, 64) * d;
 }
 
+// one row's inputs in registers: x, dy and the previous residual gradient
+template <int NV>
+struct LnbIn {
+    float4 x[NV], dy[NV], old[NV];
+    float mu, rs;
+};
+
+template <int NV>
+GPT_DEV void lnb_load(LnbIn<NV>& in, const float* __restrict__ dy, const float* __restrict__ x,
+                      const float* __restrict__ dres, float mu, float rs, int overwrite, int lane, int d) {
+    in.mu = mu;
+    in.rs = rs;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = lane + 64 * i;
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        const bool in_row = 4 * c < d;
+        in.x[i] = in_row ? load4(x + 4 * c) : z;
+        in.dy[i] = in_row ? load4(dy + 4 * c) : z;
+        in.old[i] = (in_row && !overwrite) ? load4(dres + 4 * c) : z;
+    }
+}
+
 template <typename TL, int NV>
-GPT_DEV void lnb_row(const float* dy, const float* x, float mu, float rs, const float4* gg, float* dres, TL* dres_lp,
-                     int overwrite, int lane, int d, float4* ag, float4* ab, float4* ac) {
-    float4 xh[NV], dh[NV], dyv[NV], old[NV];
+GPT_DEV void lnb_row(const LnbIn<NV>& in, const float4* gg, float* __restrict__ dres, TL* __restrict__ dres_lp,
+                     int lane, int d, float4* ag, float4* ab, float4* ac) {
+    const float mu = in.mu, rs = in.rs;
+    float4 xh[NV], dh[NV];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        int c = lane + 64 * i;
-        if (4 * c < d) {
-            float4 xv = load4(x + 4 * c);
-            dyv[i] = load4(dy + 4 * c);
-            old[i] = overwrite ? make_float4(0.f, 0.f, 0.f, 0.f) : load4(dres + 4 * c);
-            xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
-            dh[i] = make_float4(dyv[i].x * gg[i].x, dyv[i].y * gg[i].y, dyv[i].z * gg[i].z, dyv[i].w * gg[i].w);
-            s1 += (dh[i].x + dh[i].y) + (dh[i].z + dh[i].w);
-            s2 += (dh[i].x * xh[i].x + dh[i].y * xh[i].y) + (dh[i].z * xh[i].z + dh[i].w * xh[i].w);
-        }
+        const float4 xv = in.x[i], dyv = in.dy[i];
+        xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
+        dh[i] = make_float4(dyv.x * gg[i].x, dyv.y * gg[i].y, dyv.z * gg[i].z, dyv.w * gg[i].w);
+        s1 += (dh[i].x + dh[i].y) + (dh[i].z + dh[i].w);
+        s2 += (dh[i].x * xh[i].x + dh[i].y * xh[i].y) + (dh[i].z * xh[i].z + dh[i].w * xh[i].w);
     }
     s1 = wave_sum(s1) / d;
     s2 = wave_sum(s2) / d;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        int c = lane + 64 * i;
+        const int c = lane + 64 * i;
         if (4 * c < d) {
+            const float4 old = in.old[i], dyv = in.dy[i];
             float4 o;
-            o.x = old[i].x + rs * (dh[i].x - s1 - xh[i].x * s2);
-            o.y = old[i].y + rs * (dh[i].y - s1 - xh[i].y * s2);
-            o.z = old[i].z + rs * (dh[i].z - s1 - xh[i].z * s2);
-            o.w = old[i].w + rs * (dh[i].w - s1 - xh[i].w * s2);
+            o.x = old.x + rs * (dh[i].x - s1 - xh[i].x * s2);
+            o.y = old.y + rs * (dh[i].y - s1 - xh[i].y * s2);
+            o.z = old.z + rs * (dh[i].z - s1 - xh[i].z * s2);
+            o.w = old.w + rs * (dh[i].w - s1 - xh[i].w * s2);
             store4(dres + 4 * c, o);
             if (dres_lp) store4(dres_lp + 4 * c, o);
-            ag[i].x += dyv[i].x * xh[i].x; ag[i].y += dyv[i].y * xh[i].y;
-            ag[i].z += dyv[i].z * xh[i].z; ag[i].w += dyv[i].w * xh[i].w;
-            ab[i].x += dyv[i].x; ab[i].y += dyv[i].y; ab[i].z += dyv[i].z; ab[i].w += dyv[i].w;
+            ag[i].x += dyv.x * xh[i].x; ag[i].y += dyv.y * xh[i].y;
+            ag[i].z += dyv.z * xh[i].z; ag[i].w += dyv.w * xh[i].w;
+            ab[i].x += dyv.x; ab[i].y += dyv.y; ab[i].z += dyv.z; ab[i].w += dyv.w;
             ac[i].x += o.x; ac[i].y += o.y; ac[i].z += o.z; ac[i].w += o.w;
         }
     }
 }
 
+// Rows are processed with the next row's loads in flight (software pipeline).
 template <typename TL, int NV>
-__global__ __launch_bounds__(256) void layernorm_bwd_kernel(const float* dy, const float* x, const float* mean,
-                                                            const float* rstd, const float* g, float* dres,
-                                                            TL* dres_lp, int overwrite, float* part, int M, int d) {
+__global__ __launch_bounds__(256) void layernorm_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+                                                            const float* __restrict__ mean,
+                                                            const float* __restrict__ rstd, const float* __restrict__ g,
+                                                            float* __restrict__ dres, TL* __restrict__ dres_lp,
+                                                            int overwrite, float* __restrict__ part, int M, int d) {
     __shared__ float red[4][2048 + 4];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nb = gridDim.x;
@@ -472,10 +495,19 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(const float* dy, con
     }
     const int r0 = blockIdx.x * LNB_ROWS + w * (LNB_ROWS / 4);
     const int r1 = min(M, r0 + LNB_ROWS / 4);
+    LnbIn<NV> cur, nxt;
+    if (r0 < r1) {
+        const int64_t o = (int64_t)r0 * d;
+        lnb_load<NV>(cur, dy + o, x + o, dres + o, mean[r0], rstd[r0], overwrite, lane, d);
+    }
     for (int r = r0; r < r1; ++r) {
+        if (r + 1 < r1) {
+            const int64_t o = (int64_t)(r + 1) * d;
+            lnb_load<NV>(nxt, dy + o, x + o, dres + o, mean[r + 1], rstd[r + 1], overwrite, lane, d);
+        }
         const int64_t o = (int64_t)r * d;
-        lnb_row<TL, NV>(dy + o, x + o, mean[r], rstd[r], gg, dres + o, dres_lp ? dres_lp + o : nullptr, overwrite,
-                        lane, d, ag, ab, ac);
+        lnb_row<TL, NV>(cur, gg, dres + o, dres_lp ? dres_lp + o : nullptr, lane, d, ag, ab, ac);
+        cur = nxt;
     }
     float4* sets[3] = {ag, ab, ac};
 #pragma unroll
@@ -697,44 +729,47 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
         ce_u32x4 zero = {0u, 0u, 0u, 0u};
         v[c] = idx < nch ? *reinterpret_cast<const ce_u32x4*>(zr + 8 * idx) : zero;
     }
-    auto val = [&](int c, int e) {   // logit (after the cap) in log2 units
-        uint32_t wd = v[c][e >> 1];
-        float x = (e & 1) ? bf_hi(wd) : bf_lo(wd);
-        if (cap > 0.f) x = cap * tanh_exp2(x * icap);
-        return x * L2E;
+    auto raw = [&](int c, int e) {   // logit as stored
+        const uint32_t wd = v[c][e >> 1];
+        return (e & 1) ? bf_hi(wd) : bf_lo(wd);
     };
+    auto capped = [&](float x) { return cap > 0.f ? cap * tanh_exp2(x * icap) : x; };
+    // the target logit, read before any thread overwrites the row (the barriers
+    // below wait for it)
+    const float zt_raw = (tid == 0 && valid) ? (float)zr[tgt] : 0.f;
+    // pass 1: maximum (of the capped logits: the cap is monotone, so cap(max))
     float mx = -INFINITY;
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
         if (tid + 256 * c < nch)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, val(c, e));
+            for (int e = 0; e < 8; e += 2) mx = fmaxf(mx, fmaxf(raw(c, e), raw(c, e + 1)));
     mx = wave_max(mx);
     if (lane == 0) sred[w] = mx;
     __syncthreads();
-    const float gm = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
+    const float gm = capped(fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]))) * L2E;   // log2 units
+    // pass 2: sum of exp (log2 units: 2^(x log2 e - gm))
     float sm = 0.f;
+    if (cap > 0.f) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
-        if (tid + 256 * c < nch)
+        for (int c = 0; c < CPT; ++c)
+            if (tid + 256 * c < nch)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm += exp2f(val(c, e) - gm);
+                for (int e = 0; e < 8; ++e) sm += __builtin_amdgcn_exp2f(fmaf(capped(raw(c, e)), L2E, -gm));
+    } else {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c)
+            if (tid + 256 * c < nch)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sm += __builtin_amdgcn_exp2f(fmaf(raw(c, e), L2E, -gm));
+    }
     sm = wave_sum(sm);
     if (lane == 0) sred[4 + w] = sm;
     __syncthreads();
     const float lse2 = gm + log2f((sred[4] + sred[5]) + (sred[6] + sred[7]));
-    if (tid == 0) {
-        float loss = 0.f;
-        if (valid) {
-            float zy = (float)zr[tgt];
-            if (cap > 0.f) zy = cap * tanh_exp2(zy * icap);
-            loss = lse2 * 0.6931471805599453f - zy;
-        } else {
-            *err = 1;
-        }
-        row_loss[row] = loss;
-    }
-    __syncthreads();   // the target logit is read before any thread overwrites the row
+    // pass 3: gradient softmax * gscale (times 1 - tanh^2 under the cap), written
+    // over the row; the target's -gscale is applied by thread 0 afterwards
+    const float gs = valid ? gscale : 0.f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         const int idx = tid + 256 * c;
@@ -745,23 +780,35 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
             float gpair[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int e = 2 * e2 + h;
-                float g = 0.f;
-                if (valid) {
-                    uint32_t wd = v[c][e2];
-                    float x = h ? bf_hi(wd) : bf_lo(wd);
-                    float th = 0.f;
-                    if (cap > 0.f) { th = tanh_exp2(x * icap); x = cap * th; }
-                    float p = exp2f(x * L2E - lse2);
-                    g = (p - (8 * idx + e == tgt ? 1.0f : 0.0f)) * gscale;
-                    if (cap > 0.f) g *= (1.0f - th * th);
+                const float x = raw(c, 2 * e2 + h);
+                if (cap > 0.f) {
+                    const float th = tanh_exp2(x * icap);
+                    gpair[h] = __builtin_amdgcn_exp2f(fmaf(cap * th, L2E, -lse2)) * gs * (1.0f - th * th);
+                } else {
+                    gpair[h] = __builtin_amdgcn_exp2f(fmaf(x, L2E, -lse2)) * gs;
                 }
-                gpair[h] = g;
             }
-            bf16 lo = (bf16)gpair[0], hi = (bf16)gpair[1];
+            const bf16 lo = (bf16)gpair[0], hi = (bf16)gpair[1];
             o[e2] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
         }
         *reinterpret_cast<ce_u32x4*>(zr + 8 * idx) = o;
+    }
+    // the target: loss lse - z_t, and its gradient element (p_t - 1) * gscale (times
+    // 1 - tanh^2 under the cap), written after every thread's chunk stores
+    __syncthreads();
+    if (tid == 0) {
+        float loss = 0.f;
+        if (valid) {
+            float th = 0.f, zt = zt_raw;
+            if (cap > 0.f) { th = tanh_exp2(zt * icap); zt = cap * th; }
+            loss = lse2 * 0.6931471805599453f - zt;
+            float g = (__builtin_amdgcn_exp2f(fmaf(zt, L2E, -lse2)) - 1.0f) * gscale;
+            if (cap > 0.f) g *= 1.0f - th * th;
+            zr[tgt] = (bf16)g;
+        } else {
+            *err = 1;
+        }
+        row_loss[row] = loss;
     }
 }
 

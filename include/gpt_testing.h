@@ -31,6 +31,15 @@ gpt_status gptk_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda
                      int32_t act, const float* bias, const float* resid, const void* aux, void* C2,
                      float* splitk_scratch, int64_t splitk_floats, void* stream);
 
+/* Test control of the matrix-core GEMM: subsequent bf16 products (gptk_gemm
+ * and the training step alike) use tile configuration cfg (0 <= cfg <
+ * gptk_gemm_num_configs()) and split-K factor splits (0 = automatic, capped by
+ * the scratch size and a minimum K slice); cfg -1 restores the automatic
+ * choice. Process-wide, not thread-safe; meant for tests that cover every
+ * configuration. */
+gpt_status gptk_gemm_force_config(int32_t cfg, int32_t splits);
+int32_t gptk_gemm_num_configs(void);
+
 /* Causal (optionally windowed: i - j < window) softmax(Q K^T / sqrt(hd)) V per
  * (batch, head), heads interleaved in the columns of row-major [B*T, *]
  * buffers ("El Mecanismo de Atención"). Forward writes o and lse [B, H, T];

@@ -95,6 +95,40 @@ def test_gemm_store(lib, case, bf):
         assert relmax(host(C), ref) < tol, (c_bf, relmax(host(C), ref))
 
 
+CONFIG_CASES = [
+    # (M, N, K, a_kc, b_kc) per orientation, with ragged rows and columns
+    (1000, 776, 160, 1, 1), (1000, 776, 160, 1, 0), (776, 1000, 160, 0, 0),
+    (520, 392, 1056, 1, 1), (520, 392, 1056, 1, 0), (392, 520, 1056, 0, 0),
+]
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("case", CONFIG_CASES)
+def test_gemm_every_config(lib, case, splits):
+    """Every matrix-core tile configuration, with and without split-K, on each
+    operand orientation and ragged edges (bf16 inputs, fp32 and bf16 outputs)."""
+    M, N, K, a_kc, b_kc = case
+    rng = np.random.default_rng(M + N + K + 17 * splits)
+    At, Bt, A, B = gemm_inputs(M, N, K, a_kc, b_kc, 1, rng)
+    ref = gemm_ref(A, B, a_kc, b_kc)
+    scratch = torch.zeros(4 * M * N, dtype=torch.float32, device="cuda")
+    try:
+        for cfg in range(lib.gptk_gemm_num_configs()):
+            assert lib.gptk_gemm_force_config(cfg, splits) == 0
+            for c_bf in (0, 1):
+                say(f"gemm config {cfg} splits {splits} M={M} N={N} K={K} a_kc={a_kc} b_kc={b_kc} c_bf={c_bf}")
+                C = torch.zeros((M, N), dtype=torch.bfloat16 if c_bf else torch.float32, device="cuda")
+                st = lib.gptk_gemm(M, N, K, At.data_ptr(), K if a_kc else M, a_kc, Bt.data_ptr(), K if b_kc else N,
+                                   b_kc, C.data_ptr(), N, 1, c_bf, 0, 0, None, None, None, None, scratch.data_ptr(),
+                                   scratch.numel(), stream())
+                assert st == 0
+                torch.cuda.synchronize()
+                err = relmax(host(C), ref)
+                assert err < (8e-3 if c_bf else 2e-5 * math.sqrt(K / 64 + 1)), (cfg, c_bf, err)
+    finally:
+        assert lib.gptk_gemm_force_config(-1, 0) == 0
+
+
 @pytest.mark.parametrize("bf", [0, 1], ids=["fp32", "bf16"])
 @pytest.mark.parametrize("epi", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("act", [0, 1])

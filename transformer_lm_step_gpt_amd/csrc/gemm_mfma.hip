@@ -105,27 +105,33 @@ struct RowTile {
 template <int R, int BK>
 struct ColTile {
     static constexpr int CH = R / 8;                  // 16-byte chunks per k-row
-    static constexpr int KROWS_PER_DMA = 64 / CH;
-    static constexpr int DMAS = BK / KROWS_PER_DMA;
+    static constexpr int DMAS = BK * CH / 64;         // wave-wide 1 KiB copies per tile
     static constexpr int PER_WAVE = DMAS / 4;
     static constexpr int BYTES = R * BK * 2;
     static constexpr int READS_PER_FRAG = 2;
-    static_assert(CH >= 16 && DMAS % 4 == 0, "unsupported tile");
-    GPT_DEV static int swz(int k) { return (k & 3) << 2; }
+    static_assert(CH >= 16 && CH % 8 == 0 && (BK * CH) % 256 == 0, "unsupported tile");
+    // chunk c of k-row k sits at slot lds_slot(k, c): an XOR of (k & 3) << 2 for
+    // power-of-two rows, a rotation by 4 (k & 3) otherwise; either way the 4
+    // k-rows a transposing read touches fall in different banks
+    static constexpr bool POW2 = (CH & (CH - 1)) == 0;
+    GPT_DEV static int lds_slot(int k, int c) { return POW2 ? (c ^ ((k & 3) << 2)) : (c + 4 * (k & 3)) % CH; }
+    GPT_DEV static int glob_chunk(int k, int slot) {
+        return POW2 ? (slot ^ ((k & 3) << 2)) : (slot + CH - 4 * (k & 3)) % CH;
+    }
     GPT_DEV static void src_init(const bf16* (&src)[PER_WAVE], const bf16* base, int64_t ld, int row0, int rows, int k0,
                                  int w, int lane) {
 #pragma unroll
         for (int p = 0; p < PER_WAVE; ++p) {
-            const int d = w * PER_WAVE + p;
-            const int k = d * KROWS_PER_DMA + lane / CH;
-            const int c = (lane % CH) ^ swz(k);
+            const int q = (w * PER_WAVE + p) * 64 + lane;   // 16-byte LDS slot this lane fills
+            const int k = q / CH;
+            const int c = glob_chunk(k, q % CH);
             const int gr = min(row0 + c * 8, rows - 8);   // rows % 8 == 0
             src[p] = base + (int64_t)(k0 + k) * ld + gr;
         }
     }
     GPT_DEV static int64_t step(int64_t ld) { return BK * ld; }
     GPT_DEV static s16x4 tr_read(const bf16* tile, int k, int r) {
-        const bf16* p = tile + k * R + (((r >> 3) ^ swz(k)) << 3) + (r & 7);
+        const bf16* p = tile + k * R + (lds_slot(k, r >> 3) << 3) + (r & 7);
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
     }
     // fragment of rows rb..rb+31: lane l gets k = 16*ks + 8*(l/32) + e of row rb + l%32
@@ -315,7 +321,9 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
     // takes 8 consecutive columns of a row: 16-byte global accesses, with the
     // fused operation applied in fp32 on the way out.
     barrier_no_fence();   // every wave has finished with the k-tile stages
-    constexpr int SS = WN + 8, CPR = WN / 8, RPI = 64 / CPR;
+    // CPR 8-column chunks per row, RPI rows per pass of the wave (lanes past
+    // RPI * CPR idle when CPR does not divide 64), NIT passes per 32-row strip
+    constexpr int SS = WN + 8, CPR = WN / 8, RPI = 64 / CPR, NIT = (32 + RPI - 1) / RPI;
     static_assert(4 * 32 * SS * 4 <= NS * STAGE * 2, "staging strip fits in the stage ring");
     float* stg = reinterpret_cast<float*>(smem_raw) + w * 32 * SS;
     const f32x4* stg4 = reinterpret_cast<const f32x4*>(smem_raw) + w * 8 * SS;
@@ -342,11 +350,12 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
             for (int e = 0; e < 16; ++e) stg[(8 * (e >> 2) + 4 * lk + (e & 3)) * SS + 32 * jf + lr] = acc[i][jf][e];
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int it = 0; it < 32 / RPI; ++it) {
+        for (int it = 0; it < NIT; ++it) {
             const int r = it * RPI + ro;
             const int row = m0 + wm + 32 * i + r;
-            const f32x4 u0 = stg4[r * (SS / 4) + 2 * cc], u1 = stg4[r * (SS / 4) + 2 * cc + 1];
-            if (row < g.M && cin) {
+            const bool act = (32 % RPI == 0 || r < 32) && (64 % CPR == 0 || ro < RPI);
+            if (act && row < g.M && cin) {
+                const f32x4 u0 = stg4[r * (SS / 4) + 2 * cc], u1 = stg4[r * (SS / 4) + 2 * cc + 1];
                 if constexpr (SPLIT) {
                     float* p = part + ((int64_t)blockIdx.z * g.M + row) * g.N + col;
                     reinterpret_cast<f32x4*>(p)[0] = u0;
@@ -393,11 +402,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Gemm g, const float*
 
 // Tile configurations: BM x BN output tile, NS k-tile stages of BK = 32,
 // OCC workgroups per CU (register and LDS budget).
-enum GemmCfg { CFG_256_256 = 0, CFG_128_256, CFG_128_128, CFG_256_128, CFG_COUNT };
-static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256};
-static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128};
-static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3};
-static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2};
+enum GemmCfg { CFG_256_256 = 0, CFG_128_256, CFG_128_128, CFG_256_128, CFG_256_192, CFG_COUNT };
+static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256};
+static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192};
+static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4};
+static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1};
 constexpr int GEMM_BK = 32;
 
 template <int BM, int BN, int NS, int OCC, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
@@ -453,12 +462,21 @@ static void run_cfg(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s
         case CFG_128_256: run_main<128, 256, 4, 1, AKC, BKC>(g, p, part, s); break;
         case CFG_128_128: run_main<128, 128, 4, 2, AKC, BKC>(g, p, part, s); break;
         case CFG_256_128: run_main<256, 128, 3, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_192: run_main<256, 192, 4, 1, AKC, BKC>(g, p, part, s); break;
     }
 }
 
-// Tuning override for measurements: GPT_GEMM_FORCE="cfg,splits" (cfg index as
-// in GemmCfg; splits 0 = automatic).
+// Overrides of the automatic choice: gemm_mfma_force (test entry point) or,
+// for measurements, GPT_GEMM_FORCE="cfg,splits" (cfg index as in GemmCfg;
+// splits 0 = automatic).
+static int g_force_cfg = -1, g_force_splits = 0;
+void gemm_mfma_force(int cfg, int splits) {
+    g_force_cfg = cfg >= 0 && cfg < CFG_COUNT ? cfg : -1;
+    g_force_splits = splits;
+}
+int gemm_mfma_num_configs() { return CFG_COUNT; }
 static bool forced(int* cfg, int* splits) {
+    if (g_force_cfg >= 0) { *cfg = g_force_cfg; *splits = g_force_splits; return true; }
     static int state = -1, fc = 0, fs = 0;
     if (state < 0) {
         const char* e = getenv("GPT_GEMM_FORCE");
@@ -500,7 +518,10 @@ static int num_cus() {
 // prologue/epilogue time, and split-K adds its fp32 partial traffic.
 GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
     struct Cand { int cfg, occ; double rate; };
-    static const Cand cands[] = {{CFG_256_256, 1, 3.05e12}, {CFG_256_128, 2, 3.3e12}, {CFG_128_128, 2, 2.8e12}};
+    // per-CU rates measured on the step's shapes; 256x192 (one round of 256
+    // tiles for N = 768) is slower when its B operand needs transposing reads
+    const Cand cands[] = {{CFG_256_256, 1, 3.05e12}, {CFG_256_128, 2, 3.3e12}, {CFG_128_128, 2, 2.8e12},
+                          {CFG_256_192, 1, g.b_kc ? 3.3e12 : 2.8e12}};
     static const int split_opts[] = {1, 2, 3, 4, 6, 8, 12, 16};
     const int64_t mn = (int64_t)g.M * g.N;
     const double out_bytes = out_bf(g) ? 2.0 : 4.0;
@@ -525,7 +546,7 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
             if (t < best) { best = t; bcfg = c.cfg; bsplits = sp; }
         }
     }
-    if (force && fcfg == CFG_128_256) {   // configuration outside the cost model
+    if (force && best == 1e30) {   // the forced configuration or split is outside the model's options
         bcfg = fcfg;
         bsplits = fsplits > 0 ? fsplits : 1;
         while (bsplits > 1 && ((size_t)bsplits * mn > nscratch || g.K / bsplits < 256)) --bsplits;

@@ -919,6 +919,13 @@ gpt_status gpt_kernel_name_timing(gpt_handle* h, int32_t idx, const char** name,
 // test-only kernel entry points (include/gpt_testing.h)
 // ============================================================================
 
+gpt_status gptk_gemm_force_config(int32_t cfg, int32_t splits) {
+    if (cfg < -1 || cfg >= gk::gemm_mfma_num_configs() || splits < 0) return GPT_ERR_INVALID_ARGUMENT;
+    gk::gemm_mfma_force(cfg, splits);
+    return GPT_OK;
+}
+int32_t gptk_gemm_num_configs(void) { return gk::gemm_mfma_num_configs(); }
+
 gpt_status gptk_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int32_t a_kc, const void* B,
                      int64_t ldb, int32_t b_kc, void* C, int64_t ldc, int32_t in_bf16, int32_t c_bf16, int32_t epi,
                      int32_t act, const float* bias, const float* resid, const void* aux, void* C2,

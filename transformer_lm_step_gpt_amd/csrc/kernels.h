@@ -117,6 +117,9 @@ GemmPlan gemm_plan(const Gemm& g, size_t splitk_floats);
 void gemm_main(const Gemm& g, const GemmPlan& p, float* splitk_scratch, hipStream_t s);
 void gemm_finish(const Gemm& g, const GemmPlan& p, const float* splitk_scratch, hipStream_t s);
 void gemm(const Gemm& g, float* splitk_scratch, size_t splitk_floats, hipStream_t s);
+// test control of the matrix-core tile configuration / split-K (cfg -1: automatic)
+void gemm_mfma_force(int cfg, int splits);
+int gemm_mfma_num_configs();
 
 // ---------------------------------------------------------------- attention
 struct Attn {

@@ -94,6 +94,8 @@ _SIGS = [
     ("gpt_kernel_name_timing", c_int32, [c_void_p, c_int32, POINTER(c_char_p), POINTER(c_double), POINTER(c_int64),
                                          POINTER(c_double), POINTER(c_double)]),
     # test-only kernel entry points
+    ("gptk_gemm_force_config", c_int32, [c_int32, c_int32]),
+    ("gptk_gemm_num_configs", c_int32, []),
     ("gptk_gemm", c_int32, [c_int32, c_int32, c_int32, c_void_p, c_int64, c_int32, c_void_p, c_int64, c_int32,
                             c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                             c_void_p, c_void_p, c_int64, c_void_p]),

@@ -116,7 +116,15 @@ def copy_calibration():
     for _ in range(3):
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_kernel_bytes_read": 4 * n, "copy_kernel_bytes_written": 4 * n, "launches": 3}))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.mul(src, 1.0, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    print(json.dumps({"copy_kernel_bytes_read": 4 * n, "copy_kernel_bytes_written": 4 * n, "launches": 13,
+                      "copy_GBps": round(8 * n / (ms * 1e-3) / 1e9, 1)}))
 
 
 def rocprof_summary(d):

@@ -603,19 +603,36 @@ size_t colsum_partial_floats(int M, int N) {
     return (size_t)np * N + (size_t)ceil_div(np, 64) * N;
 }
 
+// one wavefront per (512-column strip, CS_ROWS-row block): lane = 8 columns,
+// 8 rows' 16-byte loads in flight per lane
 template <typename TI>
-__global__ __launch_bounds__(256) void colsum_kernel(const TI* Y, int64_t ld, int M, int N, float* part) {
-    const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+__global__ __launch_bounds__(64) void colsum_kernel(const TI* __restrict__ Y, int64_t ld, int M, int N,
+                                                   float* __restrict__ part) {
+    const int c0 = (blockIdx.x * 64 + threadIdx.x) * 8;
     if (c0 >= N) return;
     const int r0 = blockIdx.y * CS_ROWS, r1 = min(M, r0 + CS_ROWS);
     float a[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = 0.f;
     if (c0 + 8 <= N) {
-#pragma unroll 4
-        for (int r = r0; r < r1; ++r) {
+        int r = r0;
+        for (; r + 8 <= r1; r += 8) {
+            float4 u[8], v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const TI* p = Y + (int64_t)(r + i) * ld + c0;
+                u[i] = load4(p);
+                v[i] = load4(p + 4);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                a[0] += u[i].x; a[1] += u[i].y; a[2] += u[i].z; a[3] += u[i].w;
+                a[4] += v[i].x; a[5] += v[i].y; a[6] += v[i].z; a[7] += v[i].w;
+            }
+        }
+        for (; r < r1; ++r) {
             const TI* p = Y + (int64_t)r * ld + c0;
-            float4 u = load4(p), v = load4(p + 4);
+            const float4 u = load4(p), v = load4(p + 4);
             a[0] += u.x; a[1] += u.y; a[2] += u.z; a[3] += u.w;
             a[4] += v.x; a[5] += v.y; a[6] += v.z; a[7] += v.w;
         }
@@ -628,10 +645,10 @@ __global__ __launch_bounds__(256) void colsum_kernel(const TI* Y, int64_t ld, in
 
 void colsum(bool y_bf, const void* Y, int64_t ld, int M, int N, float* out, float* partial, hipStream_t s) {
     const int np = ceil_div(M, CS_ROWS);
-    dim3 grid(ceil_div(N, 256 * 8), np);
+    dim3 grid(ceil_div(N, 64 * 8), np);
     const bool vec = (ld % 8) == 0 && ((uintptr_t)Y % 16) == 0;
-    if (y_bf && vec) colsum_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)Y, ld, M, N, partial);
-    else if (!y_bf && vec) colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)Y, ld, M, N, partial);
+    if (y_bf && vec) colsum_kernel<bf16><<<grid, 64, 0, s>>>((const bf16*)Y, ld, M, N, partial);
+    else if (!y_bf && vec) colsum_kernel<float><<<grid, 64, 0, s>>>((const float*)Y, ld, M, N, partial);
     else {
         // unaligned fallback: one column per thread
         if (y_bf) colsum_scalar_kernel<bf16><<<dim3(ceil_div(N, 256), np), 256, 0, s>>>((const bf16*)Y, ld, M, N, partial);

@@ -97,8 +97,9 @@ def test_gemm_store(lib, case, bf):
 
 CONFIG_CASES = [
     # (M, N, K, a_kc, b_kc) per orientation, with ragged rows and columns
-    (1000, 776, 160, 1, 1), (1000, 776, 160, 1, 0), (776, 1000, 160, 0, 0),
-    (520, 392, 1056, 1, 1), (520, 392, 1056, 1, 0), (392, 520, 1056, 0, 0),
+    (1000, 776, 192, 1, 1), (1000, 776, 192, 1, 0), (776, 1000, 192, 0, 0),
+    (520, 392, 1088, 1, 1), (520, 392, 1088, 1, 0), (392, 520, 1088, 0, 0),
+    (300, 264, 1056, 1, 1), (300, 264, 1056, 1, 0), (264, 300, 1056, 0, 0),
 ]
 
 

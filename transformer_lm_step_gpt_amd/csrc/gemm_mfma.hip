@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
     using TB = OpTile<BKC, BN, BK>;
     constexpr int STAGE = (TA::BYTES + TB::BYTES) / 2;      // bf16 elements per stage
     constexpr int LPT = TA::PER_WAVE + TB::PER_WAVE;        // DMAs per lane per stage
-    static_assert(NS >= 3 && NS <= 4, "stages");
+    static_assert(NS >= 2 && NS <= 4, "stages");
     extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
     bf16* smem = reinterpret_cast<bf16*>(smem_raw);
 
@@ -279,23 +279,27 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
         }
     }
 
-    // Software pipeline over half k-tiles (BK = 32: two 16-deep steps per tile):
-    //   reads of step 1 of tile t          | products of step 0 of tile t
+    // Software pipeline over 16-deep steps (KS per k-tile):
+    //   steps 0 .. KS-2 of tile t: products of step s | reads of step s+1
     //   wait + barrier for tile t+1
     //   DMA of tile t+NS into the stage of tile t (every wave finished
     //   reading tile t before this barrier), issued after the first product;
-    //   reads of step 0 of tile t+1        | products of step 1 of tile t
-    static_assert(BK == 32 && NS <= 4, "two 16-deep steps per k-tile; vmcnt bookkeeping for <= 3 tiles ahead");
-    bf16x8 a0[FM], b0[FN], a1[FM], b1[FN];
+    //   last step of tile t: products | reads of step 0 of tile t+1
+    constexpr int KS = BK / 16;
+    static_assert(KS % 2 == 0 && NS <= 4, "even number of 16-deep steps; vmcnt bookkeeping for <= 3 tiles ahead");
+    bf16x8 fa[2][FM], fb[2][FN];
     if (nk > 0) {
         wait_tile(0);
-        frags(0, 0, a0, b0);
+        frags(0, 0, fa[0], fb[0]);
     }
     auto none = [](int) {};
     for (int t = 0; t < nk; ++t) {
         {
             const bf16* as = smem + (t % NS) * STAGE;
-            half_step<FM, FN, TA, TB>(acc, a0, b0, a1, b1, as, as + TA::BYTES / 2, wm, wn, 1, lane, none);
+#pragma unroll
+            for (int ks = 0; ks < KS - 1; ++ks)
+                half_step<FM, FN, TA, TB>(acc, fa[ks & 1], fb[ks & 1], fa[(ks + 1) & 1], fb[(ks + 1) & 1], as,
+                                          as + TA::BYTES / 2, wm, wn, ks + 1, lane, none);
         }
         if (t + 1 < nk) wait_tile(t + 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -310,7 +314,8 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
                 for (int q = 0; q < LPT; ++q)
                     if (p == 0 && copy) dma(q, st);
             };
-            half_step<FM, FN, TA, TB>(acc, a1, b1, a0, b0, as, as + TA::BYTES / 2, wm, wn, 0, lane, issue);
+            half_step<FM, FN, TA, TB>(acc, fa[(KS - 1) & 1], fb[(KS - 1) & 1], fa[0], fb[0], as, as + TA::BYTES / 2,
+                                      wm, wn, 0, lane, issue);
             if (copy) ++issued;
         }
     }
@@ -400,20 +405,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Gemm g, const float*
 
 // ------------------------------------------------------------------ dispatch
 
-// Tile configurations: BM x BN output tile, NS k-tile stages of BK = 32,
+// Tile configurations: BM x BN output tile, NS k-tile stages of BK,
 // OCC workgroups per CU (register and LDS budget).
-enum GemmCfg { CFG_256_256 = 0, CFG_128_256, CFG_128_128, CFG_256_128, CFG_256_192, CFG_COUNT };
-static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256};
-static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192};
-static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4};
-static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1};
-constexpr int GEMM_BK = 32;
+enum GemmCfg {
+    CFG_256_256 = 0, CFG_128_256, CFG_128_128, CFG_256_128, CFG_256_192, CFG_256_256_K64, CFG_256_192_K64,
+    CFG_256_128_K64, CFG_COUNT
+};
+static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256, 256, 256, 256};
+static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192, 256, 192, 128};
+static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32, 32, 64, 64, 64};
+static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3};
+static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1};
 
-template <int BM, int BN, int NS, int OCC, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
+template <int BM, int BN, int BK, int NS, int OCC, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
 static void launch(const Gemm& g, dim3 grid, int kps, float* part, hipStream_t s) {
-    constexpr size_t LDS = (size_t)NS * (BM + BN) * GEMM_BK * sizeof(bf16);
+    constexpr size_t LDS = (size_t)NS * (BM + BN) * BK * sizeof(bf16);
     static_assert(LDS * OCC <= 160 * 1024, "LDS budget");
-    auto k = gemm_mfma_kernel<BM, BN, GEMM_BK, NS, OCC, AKC, BKC, EPI, OUTBF, ACT, SPLIT>;
+    auto k = gemm_mfma_kernel<BM, BN, BK, NS, OCC, AKC, BKC, EPI, OUTBF, ACT, SPLIT>;
     static bool attr = false;
     if (!attr) {
         (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
@@ -430,39 +438,44 @@ static int out_bf(const Gemm& g) {
     return 1;
 }
 
-template <int BM, int BN, int NS, int OCC, bool AKC, bool BKC>
+template <int BM, int BN, int BK, int NS, int OCC, bool AKC, bool BKC>
 static void run_main(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
     dim3 grid(ceil_div(g.N, BN) * ceil_div(g.M, BM), 1, p.splits);
-    const int kps = ceil_div(ceil_div(g.K, p.splits), GEMM_BK) * GEMM_BK;
-    if (p.splits > 1) { launch<BM, BN, NS, OCC, AKC, BKC, EPI_STORE, 0, 0, true>(g, grid, kps, part, s); return; }
+    const int kps = ceil_div(ceil_div(g.K, p.splits), BK) * BK;
+    if (p.splits > 1) { launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_STORE, 0, 0, true>(g, grid, kps, part, s); return; }
     const bool relu = g.act == ACT_RELU2;
     switch (g.epi) {
         case EPI_STORE:
-            if (g.c_bf) launch<BM, BN, NS, OCC, AKC, BKC, EPI_STORE, 1, 0, false>(g, grid, kps, part, s);
-            else launch<BM, BN, NS, OCC, AKC, BKC, EPI_STORE, 0, 0, false>(g, grid, kps, part, s);
+            if (g.c_bf) launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_STORE, 1, 0, false>(g, grid, kps, part, s);
+            else launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_STORE, 0, 0, false>(g, grid, kps, part, s);
             break;
-        case EPI_BIAS: launch<BM, BN, NS, OCC, AKC, BKC, EPI_BIAS, 1, 0, false>(g, grid, kps, part, s); break;
+        case EPI_BIAS: launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_BIAS, 1, 0, false>(g, grid, kps, part, s); break;
         case EPI_BIAS_ACT:
-            if (relu) launch<BM, BN, NS, OCC, AKC, BKC, EPI_BIAS_ACT, 1, ACT_RELU2, false>(g, grid, kps, part, s);
-            else launch<BM, BN, NS, OCC, AKC, BKC, EPI_BIAS_ACT, 1, ACT_GELU, false>(g, grid, kps, part, s);
+            if (relu) launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_BIAS_ACT, 1, ACT_RELU2, false>(g, grid, kps, part, s);
+            else launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_BIAS_ACT, 1, ACT_GELU, false>(g, grid, kps, part, s);
             break;
-        case EPI_BIAS_RESID: launch<BM, BN, NS, OCC, AKC, BKC, EPI_BIAS_RESID, 0, 0, false>(g, grid, kps, part, s); break;
+        case EPI_BIAS_RESID:
+            launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_BIAS_RESID, 0, 0, false>(g, grid, kps, part, s);
+            break;
         case EPI_ACT_GRAD:
-            if (relu) launch<BM, BN, NS, OCC, AKC, BKC, EPI_ACT_GRAD, 1, ACT_RELU2, false>(g, grid, kps, part, s);
-            else launch<BM, BN, NS, OCC, AKC, BKC, EPI_ACT_GRAD, 1, ACT_GELU, false>(g, grid, kps, part, s);
+            if (relu) launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_ACT_GRAD, 1, ACT_RELU2, false>(g, grid, kps, part, s);
+            else launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_ACT_GRAD, 1, ACT_GELU, false>(g, grid, kps, part, s);
             break;
-        case EPI_ACCUM: launch<BM, BN, NS, OCC, AKC, BKC, EPI_ACCUM, 0, 0, false>(g, grid, kps, part, s); break;
+        case EPI_ACCUM: launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_ACCUM, 0, 0, false>(g, grid, kps, part, s); break;
     }
 }
 
 template <bool AKC, bool BKC>
 static void run_cfg(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
     switch (p.cfg) {
-        case CFG_256_256: run_main<256, 256, 4, 1, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_256: run_main<128, 256, 4, 1, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_128: run_main<128, 128, 4, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_128: run_main<256, 128, 3, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_192: run_main<256, 192, 4, 1, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256: run_main<256, 256, 32, 4, 1, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_256: run_main<128, 256, 32, 4, 1, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128: run_main<128, 128, 32, 4, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128: run_main<256, 128, 32, 3, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_192: run_main<256, 192, 32, 4, 1, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64: run_main<256, 256, 64, 2, 1, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_192_K64: run_main<256, 192, 64, 2, 1, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128_K64: run_main<256, 128, 64, 3, 1, AKC, BKC>(g, p, part, s); break;
     }
 }
 
@@ -512,42 +525,81 @@ static int num_cus() {
     return n;
 }
 
-// Tile configuration and split-K factor from a cost model: every workgroup
-// slot (CUs x workgroups per CU) runs whole tiles in rounds; a round costs one
-// tile's FLOPs at the configuration's measured per-CU rate plus a fixed
-// prologue/epilogue time, and split-K adds its fp32 partial traffic.
+// Tile configuration and split-K factor from a cost model: the workgroups
+// are spread evenly over the CUs; a CU runs its share at the configuration's
+// measured per-CU rate (a lone workgroup of a two-per-CU configuration at
+// 60% of it), each workgroup adds its epilogue (fused activations cost more;
+// two workgroups per CU overlap it with the other's products), each round of
+// workgroup slots a fixed prologue, and split-K its fp32 partials.
+// Measured best choices for the products of the 124M-parameter shapes
+// (d = 768, F = 3072, Vp = 50304, 16384 rows per micro-batch); other shapes
+// use the cost model below.
+struct Tuned { int M, N, K; bool a_kc, b_kc; int cfg, splits; };
+static const Tuned tuned[] = {
+    // forward: X W^T
+    {16384, 2304, 768, true, true, CFG_256_128, 1}, {16384, 768, 768, true, true, CFG_256_192_K64, 1},
+    {16384, 3072, 768, true, true, CFG_256_128, 1}, {16384, 768, 3072, true, true, CFG_256_192_K64, 1},
+    {16384, 50304, 768, true, true, CFG_256_256_K64, 1},
+    // input gradients: dY W
+    {16384, 3072, 768, true, false, CFG_256_128, 1}, {16384, 768, 3072, true, false, CFG_256_192_K64, 1},
+    {16384, 768, 768, true, false, CFG_256_192_K64, 1}, {16384, 768, 2304, true, false, CFG_256_192_K64, 1},
+    {16384, 768, 50304, true, false, CFG_256_192_K64, 1},
+    // weight gradients: dY^T X
+    {768, 3072, 16384, false, false, CFG_256_256_K64, 6}, {3072, 768, 16384, false, false, CFG_256_256_K64, 6},
+    {768, 768, 16384, false, false, CFG_128_128, 6}, {2304, 768, 16384, false, false, CFG_128_128, 4},
+    {50304, 768, 16384, false, false, CFG_256_256_K64, 3},
+};
+
 GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
-    struct Cand { int cfg, occ; double rate; };
-    // per-CU rates measured on the step's shapes; 256x192 (one round of 256
-    // tiles for N = 768) is slower when its B operand needs transposing reads
-    const Cand cands[] = {{CFG_256_256, 1, 3.05e12}, {CFG_256_128, 2, 3.3e12}, {CFG_128_128, 2, 2.8e12},
-                          {CFG_256_192, 1, g.b_kc ? 3.3e12 : 2.8e12}};
+    struct Cand { int cfg; double rate; };
+    static const Cand cands[] = {{CFG_256_128, 3.3e12}, {CFG_128_128, 2.8e12}, {CFG_256_256_K64, 3.5e12},
+                                 {CFG_256_192_K64, 3.36e12}};
     static const int split_opts[] = {1, 2, 3, 4, 6, 8, 12, 16};
     const int64_t mn = (int64_t)g.M * g.N;
     const double out_bytes = out_bf(g) ? 2.0 : 4.0;
+    const double epi_s = (g.epi == EPI_BIAS_ACT || g.epi == EPI_ACT_GRAD) ? 0.09e-9 : 0.015e-9;   // per element
     const int cus = num_cus();
     int fcfg = -1, fsplits = 0;
-    const bool force = forced(&fcfg, &fsplits);
+    bool force = forced(&fcfg, &fsplits);
+    if (!force)
+        for (const Tuned& e : tuned)
+            if (e.M == g.M && e.N == g.N && e.K == g.K && e.a_kc == g.a_kc && e.b_kc == g.b_kc) {
+                int sp = e.splits;
+                while (sp > 1 && (size_t)sp * mn > nscratch) --sp;
+                force = true;
+                fcfg = e.cfg;
+                fsplits = sp;
+                break;
+            }
     double best = 1e30;
     int bcfg = CFG_128_128, bsplits = 1;
-    for (const Cand& c : cands) {
-        if (force && c.cfg != fcfg) continue;
+    for (int ci = 0; ci < CFG_COUNT; ++ci) {
+        double rate = 0.0;
+        for (const Cand& c : cands)
+            if (c.cfg == ci) rate = c.rate;
+        if (force ? ci != fcfg : rate == 0.0) continue;
+        if (rate == 0.0) rate = 3.0e12;   // forced configuration outside the candidate list
+        if (g.K % cfg_bk[ci]) continue;
+        const int bm = cfg_bm[ci], bn = cfg_bn[ci], occ = cfg_occ[ci];
         for (int sp : split_opts) {
             if (force && fsplits > 0 && sp != fsplits) continue;
-            const int kps = ceil_div(ceil_div(g.K, sp), GEMM_BK) * GEMM_BK;
+            const int kps = ceil_div(ceil_div(g.K, sp), cfg_bk[ci]) * cfg_bk[ci];
             const int used = ceil_div(g.K, kps);
             if (used != sp) continue;
             if (sp > 1 && ((size_t)sp * mn > nscratch || kps < 256)) continue;
-            const int64_t tiles = (int64_t)ceil_div(g.M, cfg_bm[c.cfg]) * ceil_div(g.N, cfg_bn[c.cfg]);
-            const int64_t slots = (int64_t)cus * c.occ;
-            const int64_t rounds = (tiles * sp + slots - 1) / slots;
-            double t = rounds * (c.occ * 2.0 * cfg_bm[c.cfg] * cfg_bn[c.cfg] * kps / c.rate + 2e-6);
+            const int64_t wgs = (int64_t)ceil_div(g.M, bm) * ceil_div(g.N, bn) * sp;
+            const int64_t per_cu = (wgs + cus - 1) / cus, rounds = (wgs + (int64_t)cus * occ - 1) / ((int64_t)cus * occ);
+            // with two workgroups per CU the rate holds for pairs; a workgroup
+            // alone on its CU reaches about 60% of it
+            const int64_t lone = occ == 2 ? per_cu % 2 : 0;
+            double t = ((per_cu - lone) + lone / 0.6) * (2.0 * bm * bn * kps / rate) + per_cu * epi_s * bm * bn / occ +
+                       rounds * 2e-6;
             if (sp > 1) t += (2.0 * sp * mn * 4.0 + mn * out_bytes) / 4e12;
-            if (t < best) { best = t; bcfg = c.cfg; bsplits = sp; }
+            if (t < best) { best = t; bcfg = ci; bsplits = sp; }
         }
     }
     if (force && best == 1e30) {   // the forced configuration or split is outside the model's options
-        bcfg = fcfg;
+        bcfg = g.K % cfg_bk[fcfg] ? CFG_256_256 : fcfg;
         bsplits = fsplits > 0 ? fsplits : 1;
         while (bsplits > 1 && ((size_t)bsplits * mn > nscratch || g.K / bsplits < 256)) --bsplits;
     }
@@ -556,7 +608,7 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
     p.splits = bsplits;
     const bool relu = bsplits == 1 && (g.epi == EPI_BIAS_ACT || g.epi == EPI_ACT_GRAD) && g.act == ACT_RELU2;
     snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %s, %s, %d, %d, %d, %s>", cfg_bm[bcfg],
-             cfg_bn[bcfg], GEMM_BK, cfg_ns[bcfg], cfg_occ[bcfg], g.a_kc ? "true" : "false", g.b_kc ? "true" : "false",
+             cfg_bn[bcfg], cfg_bk[bcfg], cfg_ns[bcfg], cfg_occ[bcfg], g.a_kc ? "true" : "false", g.b_kc ? "true" : "false",
              bsplits > 1 ? 0 : g.epi, bsplits > 1 ? 0 : out_bf(g), relu ? 1 : 0, bsplits > 1 ? "true" : "false");
     return p;
 }

@@ -21,9 +21,10 @@ extern "C" {
 /* C[M, N] = epilogue(sum_k A(m,k) B(k,n)) where
  *   A(m,k) = a_kc ? A[m*lda + k] : A[k*lda + m],
  *   B(k,n) = b_kc ? B[n*ldb + k] : B[k*ldb + n]   (A, B bf16 if in_bf16 else fp32);
- * epi: 0 store (C act or fp32 by c_bf16), 1 + bias[n], 2 + bias then C2 = act(C)
- * (act 0 = GELU tanh approximation, 1 = ReLU^2), 3 C = resid + AB + bias (fp32),
- * 4 C = AB * act'(aux) (aux act), 5 C += AB (fp32). The linear-layer products of
+ * epi: 0 store (C act or fp32 by c_bf16), 1 + bias[n], 2 with y = AB + bias:
+ * C = act'(y) and C2 = act(y) (act 0 = GELU tanh approximation, 1 = ReLU^2; the
+ * derivative is what the backward product needs), 3 C = resid + AB + bias
+ * (fp32), 4 C = AB * aux (aux act: the saved derivative), 5 C += AB (fp32). The linear-layer products of
  * the lecture's GPT ("Раздел 1 / Архитектура") in both passes reduce to these.
  * splitk_scratch (optional) holds split-K partial sums of splitk_floats floats. */
 gpt_status gptk_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int32_t a_kc, const void* B,

@@ -85,5 +85,22 @@ enum ActKind { ACT_GELU = 0, ACT_RELU2 = 1 };
 
 template <int ACT> GPT_DEV float act_f(float x) { return ACT == ACT_RELU2 ? relu2_f(x) : gelu_tanh_f(x); }
 template <int ACT> GPT_DEV float act_grad_f(float x) { return ACT == ACT_RELU2 ? relu2_grad_f(x) : gelu_tanh_grad_f(x); }
+// the activation and its derivative at x together (GELU shares one sigma)
+template <int ACT> GPT_DEV void act_and_grad(float x, float& a, float& da) {
+    if constexpr (ACT == ACT_RELU2) {
+        const float r = fmaxf(x, 0.0f);
+        a = r * r;
+        da = 2.0f * r;
+    } else {
+        const float c2 = 2.0f * 0.7978845608028654f;
+        const float s = gelu_sigma(x);
+        a = x * s;
+        da = fmaf(x * s * (1.0f - s), fmaf(c2 * 3.0f * 0.044715f, x * x, c2), s);
+    }
+}
+GPT_DEV void act_and_grad_rt(int act, float x, float& a, float& da) {
+    if (act == ACT_RELU2) act_and_grad<ACT_RELU2>(x, a, da);
+    else act_and_grad<ACT_GELU>(x, a, da);
+}
 
 __host__ __device__ inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }

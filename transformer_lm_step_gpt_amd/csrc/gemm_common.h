@@ -14,14 +14,14 @@ GPT_DEV void epilogue_store(const Gemm& g, int m, int n, float acc) {
     } else if constexpr (EPI == EPI_BIAS) {
         ((TC*)g.C)[o] = from_f32<TC>(acc + g.bias[n]);
     } else if constexpr (EPI == EPI_BIAS_ACT) {
-        float pre = acc + g.bias[n];
-        ((TC*)g.C)[o] = from_f32<TC>(pre);
-        ((TC*)g.C2)[o] = from_f32<TC>(g.act == ACT_RELU2 ? relu2_f(pre) : gelu_tanh_f(pre));
+        float a, da;
+        act_and_grad_rt(g.act, acc + g.bias[n], a, da);
+        ((TC*)g.C)[o] = from_f32<TC>(da);
+        ((TC*)g.C2)[o] = from_f32<TC>(a);
     } else if constexpr (EPI == EPI_BIAS_RESID) {
         ((float*)g.C)[o] = g.resid[o] + (acc + g.bias[n]);
     } else if constexpr (EPI == EPI_ACT_GRAD) {
-        float pre = to_f32(((const TC*)g.aux)[o]);
-        ((TC*)g.C)[o] = from_f32<TC>(acc * (g.act == ACT_RELU2 ? relu2_grad_f(pre) : gelu_tanh_grad_f(pre)));
+        ((TC*)g.C)[o] = from_f32<TC>(acc * to_f32(((const TC*)g.aux)[o]));
     } else {   // EPI_ACCUM
         ((float*)g.C)[o] += acc;
     }
@@ -55,10 +55,7 @@ GPT_DEV void epilogue_chunk8(const Gemm& g, int m, int n, const float (&acc)[8],
     } else if constexpr (EPI == EPI_BIAS_ACT) {
         float h[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            y[e] = acc[e] + bias[e];
-            h[e] = act_f<ACT>(y[e]);
-        }
+        for (int e = 0; e < 8; ++e) act_and_grad<ACT>(acc[e] + bias[e], h[e], y[e]);
         put(g.C, y);
         put(g.C2, h);
     } else if constexpr (EPI == EPI_BIAS_RESID) {
@@ -71,10 +68,7 @@ GPT_DEV void epilogue_chunk8(const Gemm& g, int m, int n, const float (&acc)[8],
     } else if constexpr (EPI == EPI_ACT_GRAD) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>((const TC*)g.aux + o);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float x = (float)a[e];
-            y[e] = acc[e] * act_grad_f<ACT>(x);
-        }
+        for (int e = 0; e < 8; ++e) y[e] = acc[e] * (float)a[e];
         put(g.C, y);
     } else {   // EPI_ACCUM
         const float* c = (const float*)g.C + o;

@@ -108,7 +108,9 @@ struct Ws {
     std::vector<float*> x_in, x_mid;
     float* x_fin = nullptr;
     float *ln_mean = nullptr, *ln_rstd = nullptr;
-    std::vector<void*> ln1, ln2, qkv, qk, att, hpre, hact;
+    // per layer: LN outputs, qkv, normalised/rotated q,k, attention output, the MLP
+    // activation's derivative at its input (for the backward product) and the activation
+    std::vector<void*> ln1, ln2, qkv, qk, att, hdact, hact;
     std::vector<float*> lse;
     void* lnf = nullptr;
     void* logits = nullptr;
@@ -165,7 +167,7 @@ Ws plan(const gpt_config& c, const Table& tb, void* base) {
         w.qk.push_back(qk_transform(c) ? cv.take(ab * M * 2 * d) : nullptr);
         w.att.push_back(cv.take(ab * M * d));
         w.lse.push_back(cv.arr<float>(M * H));
-        w.hpre.push_back(cv.take(ab * M * F));
+        w.hdact.push_back(cv.take(ab * M * F));
         w.hact.push_back(cv.take(ab * M * F));
     }
     w.x_fin = cv.arr<float>(M * d);
@@ -587,7 +589,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
             gk::layernorm_fwd(bf, w.x_mid[l], P(h, li.ln2_w), P(h, li.ln2_b), w.ln2[l], mean2, rstd2, M, d, c.ln_eps, st);
         }
         {
-            gk::Gemm g = mk_gemm(h, M, F, d, w.ln2[l], d, true, Wop(h, li.fc_w), d, true, w.hpre[l], F, bf,
+            gk::Gemm g = mk_gemm(h, M, F, d, w.ln2[l], d, true, Wop(h, li.fc_w), d, true, w.hdact[l], F, bf,
                                  gk::EPI_BIAS_ACT);
             g.bias = P(h, li.fc_b);
             g.C2 = w.hact[l];
@@ -639,7 +641,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         // MLP branch
         {
             gk::Gemm g = mk_gemm(h, M, F, d, dR, d, true, Wop(h, li.mp_w), F, false, w.dh, F, bf, gk::EPI_ACT_GRAD);
-            g.aux = w.hpre[l];
+            g.aux = w.hdact[l];
             run_gemm(h, KC_GEMM_DGRAD, g);
             gk::Gemm g2 = mk_gemm(h, d, F, M, dR, d, false, w.hact[l], F, false, G(h, li.mp_w), F, false, gk::EPI_ACCUM);
             run_gemm(h, KC_GEMM_WGRAD, g2);

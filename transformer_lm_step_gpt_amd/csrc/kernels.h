@@ -85,9 +85,9 @@ void adamw(float* p, const float* g, float* m, float* v, void* wbf, int64_t n, i
 enum GemmEpi {
     EPI_STORE = 0,      // C = A B                        (C: act or fp32)
     EPI_BIAS = 1,       // C = A B + bias                 (C: act)
-    EPI_BIAS_ACT = 2,   // C = A B + bias; C2 = act(C)    (C, C2: act)
+    EPI_BIAS_ACT = 2,   // y = A B + bias; C = act'(y); C2 = act(y)   (C, C2: act)
     EPI_BIAS_RESID = 3, // C = resid + A B + bias         (C, resid: fp32)
-    EPI_ACT_GRAD = 4,   // C = (A B) * act'(aux)          (C, aux: act)
+    EPI_ACT_GRAD = 4,   // C = (A B) * aux, aux = act' saved by EPI_BIAS_ACT   (C, aux: act)
     EPI_ACCUM = 5       // C += A B                       (C: fp32)
 };
 struct Gemm {

@@ -546,7 +546,7 @@ static const Tuned tuned[] = {
     {16384, 768, 50304, true, false, CFG_256_192_K64, 1},
     // weight gradients: dY^T X
     {768, 3072, 16384, false, false, CFG_256_256_K64, 6}, {3072, 768, 16384, false, false, CFG_256_256_K64, 6},
-    {768, 768, 16384, false, false, CFG_128_128, 6}, {2304, 768, 16384, false, false, CFG_128_128, 4},
+    {768, 768, 16384, false, false, CFG_128_128, 8}, {2304, 768, 16384, false, false, CFG_256_256_K64, 8},
     {50304, 768, 16384, false, false, CFG_256_256_K64, 3},
 };
 

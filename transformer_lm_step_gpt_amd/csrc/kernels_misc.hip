@@ -355,58 +355,82 @@ void embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, in
 
 constexpr int LN_MAXV = 8;   // float4 chunks per lane: d <= 64 * 4 * 8
 
-template <typename TO>
-__global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* x, const float* g, const float* b, TO* y,
-                                                            float* mean, float* rstd, int M, int d, float eps) {
-    int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    int lane = threadIdx.x & 63;
-    if (row >= M) return;
+constexpr int LNF_ROWS = 4;   // rows per wavefront in the forward pass
+
+// One wavefront per LNF_ROWS consecutive rows; the next row's loads are issued
+// before the current row's reductions (software pipeline).
+template <typename TO, int NV>
+__global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                            const float* __restrict__ b, TO* __restrict__ y,
+                                                            float* __restrict__ mean, float* __restrict__ rstd, int M,
+                                                            int d, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * LNF_ROWS, r1 = min(M, r0 + LNF_ROWS);
     const int nv = d >> 2;
-    const float* xr = x + (int64_t)row * d;
-    float4 v[LN_MAXV];
-    float s = 0.f;
+    float4 cur[NV], nxt[NV];
+    auto load_row = [&](int r, float4 (&v)[NV]) {
+        const float* xr = x + (int64_t)r * d;
 #pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-        int c = lane + 64 * i;
-        if (c < nv) {
-            v[i] = load4(xr + 4 * c);
-            s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+        for (int i = 0; i < NV; ++i) {
+            const int c = lane + 64 * i;
+            v[i] = c < nv ? load4(xr + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-    }
-    float mu = wave_sum(s) / d;
-    float s2 = 0.f;
+    };
+    if (r0 < r1) load_row(r0, cur);
+    for (int row = r0; row < r1; ++row) {
+        if (row + 1 < r1) load_row(row + 1, nxt);
+        float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-        int c = lane + 64 * i;
-        if (c < nv) {
-            float a = v[i].x - mu, bb = v[i].y - mu, cc = v[i].z - mu, dd = v[i].w - mu;
-            s2 += (a * a + bb * bb) + (cc * cc + dd * dd);
-        }
-    }
-    float var = wave_sum(s2) / d;
-    float rs = 1.0f / sqrtf(var + eps);
-    TO* yr = y + (int64_t)row * d;
+        for (int i = 0; i < NV; ++i) s += (cur[i].x + cur[i].y) + (cur[i].z + cur[i].w);
+        const float mu = wave_sum(s) / d;
+        float s2 = 0.f;
 #pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
-        int c = lane + 64 * i;
-        if (c < nv) {
-            float4 gg = load4(g + 4 * c), bb = load4(b + 4 * c);
-            float4 o;
-            o.x = (v[i].x - mu) * rs * gg.x + bb.x;
-            o.y = (v[i].y - mu) * rs * gg.y + bb.y;
-            o.z = (v[i].z - mu) * rs * gg.z + bb.z;
-            o.w = (v[i].w - mu) * rs * gg.w + bb.w;
-            store4(yr + 4 * c, o);
+        for (int i = 0; i < NV; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nv) {
+                const float a = cur[i].x - mu, bb = cur[i].y - mu, cc = cur[i].z - mu, dd = cur[i].w - mu;
+                s2 += (a * a + bb * bb) + (cc * cc + dd * dd);
+            }
         }
+        const float var = wave_sum(s2) / d;
+        const float rs = 1.0f / sqrtf(var + eps);
+        TO* yr = y + (int64_t)row * d;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nv) {
+                const float4 gg = load4(g + 4 * c), bb = load4(b + 4 * c);
+                float4 o;
+                o.x = (cur[i].x - mu) * rs * gg.x + bb.x;
+                o.y = (cur[i].y - mu) * rs * gg.y + bb.y;
+                o.z = (cur[i].z - mu) * rs * gg.z + bb.z;
+                o.w = (cur[i].w - mu) * rs * gg.w + bb.w;
+                store4(yr + 4 * c, o);
+            }
+        }
+        if (lane == 0) { mean[row] = mu; rstd[row] = rs; }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) cur[i] = nxt[i];
     }
-    if (lane == 0) { mean[row] = mu; rstd[row] = rs; }
+}
+
+template <typename TO>
+static void lnf_launch(int nv, int grid, const float* x, const float* g, const float* b, TO* y, float* mean,
+                       float* rstd, int M, int d, float eps, hipStream_t s) {
+    switch (nv) {
+        case 1: layernorm_fwd_kernel<TO, 1><<<grid, 256, 0, s>>>(x, g, b, y, mean, rstd, M, d, eps); break;
+        case 2: layernorm_fwd_kernel<TO, 2><<<grid, 256, 0, s>>>(x, g, b, y, mean, rstd, M, d, eps); break;
+        case 3: layernorm_fwd_kernel<TO, 3><<<grid, 256, 0, s>>>(x, g, b, y, mean, rstd, M, d, eps); break;
+        case 4: layernorm_fwd_kernel<TO, 4><<<grid, 256, 0, s>>>(x, g, b, y, mean, rstd, M, d, eps); break;
+        default: layernorm_fwd_kernel<TO, 8><<<grid, 256, 0, s>>>(x, g, b, y, mean, rstd, M, d, eps); break;
+    }
 }
 
 void layernorm_fwd(bool bf, const float* x, const float* g, const float* b, void* y, float* mean, float* rstd,
                    int M, int d, float eps, hipStream_t s) {
-    int grid = ceil_div(M, 4);
-    if (bf) layernorm_fwd_kernel<bf16><<<grid, 256, 0, s>>>(x, g, b, (bf16*)y, mean, rstd, M, d, eps);
-    else layernorm_fwd_kernel<float><<<grid, 256, 0, s>>>(x, g, b, (float*)y, mean, rstd, M, d, eps);
+    const int grid = ceil_div(M, 4 * LNF_ROWS), nv = ceil_div(d, 256);
+    if (bf) lnf_launch<bf16>(nv, grid, x, g, b, (bf16*)y, mean, rstd, M, d, eps, s);
+    else lnf_launch<float>(nv, grid, x, g, b, (float*)y, mean, rstd, M, d, eps, s);
 }
 
 constexpr int LNB_ROWS = 32;   // rows per workgroup in the backward pass (8 per wavefront)
@@ -1018,29 +1042,47 @@ void grad_norm(const float* g, int64_t n, double* partial, float* norm_out, floa
     grad_norm_final_kernel<<<1, 256, 0, s>>>(partial, norm_out, coef_out, nonfinite, max_norm);
 }
 
-__global__ __launch_bounds__(256) void adamw_kernel(float* p, const float* g, float* m, float* v, bf16* wbf,
+GPT_DEV void adamw4(float4& pp, const float4& gg, float4& mm, float4& vv, bool decayed, float c, float dec, float lr,
+                    float b1, float b2, float eps, float rbc1, float rbc2) {
+    float* pe = &pp.x; const float* ge = &gg.x; float* me = &mm.x; float* ve = &vv.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float gc = ge[e] * c;
+        me[e] = b1 * me[e] + (1.0f - b1) * gc;
+        ve[e] = b2 * ve[e] + (1.0f - b2) * gc * gc;
+        const float pv = decayed ? pe[e] * dec : pe[e];
+        pe[e] = pv - lr * (me[e] * rbc1) / (sqrtf(ve[e] * rbc2) + eps);
+    }
+}
+
+// two groups of four parameters per thread and iteration (eight 16-byte loads in flight)
+__global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
+                                                    float* __restrict__ m, float* __restrict__ v, bf16* __restrict__ wbf,
                                                     int64_t n4, int64_t nd4, const float* coef_p,
                                                     const int32_t* nonfinite, float lr, float b1, float b2,
                                                     float eps, float wd, float rbc1, float rbc2) {
     if (*nonfinite) return;
     const float c = *coef_p;
     const float dec = 1.0f - lr * wd;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
-        float4 pp = load4(p + 4 * i), gg = load4(g + 4 * i), mm = load4(m + 4 * i), vv = load4(v + 4 * i);
-        const bool decayed = i < nd4;
-        float* pe = &pp.x; float* ge = &gg.x; float* me = &mm.x; float* ve = &vv.x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float gc = ge[e] * c;
-            me[e] = b1 * me[e] + (1.0f - b1) * gc;
-            ve[e] = b2 * ve[e] + (1.0f - b2) * gc * gc;
-            float pv = decayed ? pe[e] * dec : pe[e];
-            pe[e] = pv - lr * (me[e] * rbc1) / (sqrtf(ve[e] * rbc2) + eps);
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += 2 * stride) {
+        const int64_t j = i + stride;
+        const bool two = j < n4;
+        float4 p0 = load4(p + 4 * i), g0 = load4(g + 4 * i), m0 = load4(m + 4 * i), v0 = load4(v + 4 * i);
+        float4 p1, g1, m1, v1;
+        if (two) { p1 = load4(p + 4 * j); g1 = load4(g + 4 * j); m1 = load4(m + 4 * j); v1 = load4(v + 4 * j); }
+        adamw4(p0, g0, m0, v0, i < nd4, c, dec, lr, b1, b2, eps, rbc1, rbc2);
+        store4(p + 4 * i, p0);
+        store4(m + 4 * i, m0);
+        store4(v + 4 * i, v0);
+        if (i < nd4 && wbf) store4(wbf + 4 * i, p0);
+        if (two) {
+            adamw4(p1, g1, m1, v1, j < nd4, c, dec, lr, b1, b2, eps, rbc1, rbc2);
+            store4(p + 4 * j, p1);
+            store4(m + 4 * j, m1);
+            store4(v + 4 * j, v1);
+            if (j < nd4 && wbf) store4(wbf + 4 * j, p1);
         }
-        store4(p + 4 * i, pp);
-        store4(m + 4 * i, mm);
-        store4(v + 4 * i, vv);
-        if (decayed && wbf) store4(wbf + 4 * i, pp);
     }
 }
 

@@ -100,6 +100,8 @@ CONFIG_CASES = [
     (1000, 776, 192, 1, 1), (1000, 776, 192, 1, 0), (776, 1000, 192, 0, 0),
     (520, 392, 1088, 1, 1), (520, 392, 1088, 1, 0), (392, 520, 1088, 0, 0),
     (300, 264, 1056, 1, 1), (300, 264, 1056, 1, 0), (264, 300, 1056, 0, 0),
+    # more tiles than workgroup slots: persistent workgroups loop over several tiles
+    (4000, 4104, 128, 1, 1), (4000, 4104, 128, 1, 0), (4104, 4000, 128, 0, 0),
 ]
 
 

@@ -162,9 +162,9 @@ struct OpTile<false, R, BK> : ColTile<R, BK> {
 
 }  // namespace
 
-// One half-step: the FM x FN products of (ca, cb), with the fragment reads of
-// the next half-step (into na, nb) and the operations of `extra` (slot p runs
-// after product p) spread between them in program order, so LDS latency and
+// One 16-deep step: the FM x FN products of (ca, cb), with the fragment reads
+// of the next step (into na, nb) and the operations of `extra` (slot p runs
+// after product p) placed between them in program order, so LDS latency and
 // DMA issue hide under the matrix cores.
 template <int FM, int FN, class TA, class TB, class X>
 __device__ __attribute__((always_inline)) inline void half_step(f32x16 (&acc)[FM][FN], const bf16x8 (&ca)[FM],
@@ -175,8 +175,10 @@ __device__ __attribute__((always_inline)) inline void half_step(f32x16 (&acc)[FM
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         acc[p / FN][p % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[p / FN], cb[p % FN], acc[p / FN][p % FN], 0, 0, 0);
-        if ((p * NF) / P != ((p + 1) * NF) / P) {
-            const int f = (p * NF) / P;
+        // the next step's fragment reads go out early (one after each of the
+        // first NF products), leaving the remaining products to cover their latency
+        if (p < NF) {
+            const int f = p;
             if (f < FM) na[f] = TA::get(as, wm + 32 * f, ksn, lane);
             else nb[f - FM] = TB::get(bs, wn + 32 * (f - FM), ksn, lane);
         }

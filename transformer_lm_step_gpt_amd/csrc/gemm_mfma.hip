@@ -411,13 +411,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Gemm g, const float*
 // OCC workgroups per CU (register and LDS budget).
 enum GemmCfg {
     CFG_256_256 = 0, CFG_128_256, CFG_128_128, CFG_256_128, CFG_256_192, CFG_256_256_K64, CFG_256_192_K64,
-    CFG_256_128_K64, CFG_128_192_K64, CFG_128_256_K64, CFG_COUNT
+    CFG_256_128_K64, CFG_128_192_K64, CFG_128_256_K64, CFG_128_128_K64, CFG_COUNT
 };
-static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256, 256, 256, 256, 128, 128};
-static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192, 256, 192, 128, 192, 256};
-static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32, 32, 64, 64, 64, 64, 64};
-static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3, 2, 2};
-static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1, 2, 1};
+static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256, 256, 256, 256, 128, 128, 128};
+static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192, 256, 192, 128, 192, 256, 128};
+static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32, 32, 64, 64, 64, 64, 64, 64};
+static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3, 2, 2, 2};
+static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1, 2, 1, 2};
 
 template <int BM, int BN, int BK, int NS, int OCC, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
 static void launch(const Gemm& g, dim3 grid, int kps, float* part, hipStream_t s) {
@@ -480,6 +480,7 @@ static void run_cfg(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s
         case CFG_256_128_K64: run_main<256, 128, 64, 3, 1, AKC, BKC>(g, p, part, s); break;
         case CFG_128_192_K64: run_main<128, 192, 64, 2, 2, AKC, BKC>(g, p, part, s); break;
         case CFG_128_256_K64: run_main<128, 256, 64, 2, 1, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128_K64: run_main<128, 128, 64, 2, 2, AKC, BKC>(g, p, part, s); break;
     }
 }
 
@@ -549,15 +550,15 @@ static const Tuned tuned[] = {
     {16384, 768, 768, true, false, CFG_128_192_K64, 1}, {16384, 768, 2304, true, false, CFG_128_192_K64, 1},
     {16384, 768, 50304, true, false, CFG_128_192_K64, 1},
     // weight gradients: dY^T X
-    {768, 3072, 16384, false, false, CFG_256_256_K64, 6}, {3072, 768, 16384, false, false, CFG_256_256_K64, 6},
-    {768, 768, 16384, false, false, CFG_128_128, 8}, {2304, 768, 16384, false, false, CFG_256_256_K64, 8},
+    {768, 3072, 16384, false, false, CFG_128_192_K64, 4}, {3072, 768, 16384, false, false, CFG_128_192_K64, 4},
+    {768, 768, 16384, false, false, CFG_128_128, 8}, {2304, 768, 16384, false, false, CFG_128_128_K64, 4},
     {50304, 768, 16384, false, false, CFG_128_192_K64, 2},
 };
 
 GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
     struct Cand { int cfg; double rate; };
     static const Cand cands[] = {{CFG_256_128, 3.3e12}, {CFG_128_128, 2.8e12}, {CFG_256_256_K64, 3.5e12},
-                                 {CFG_256_192_K64, 3.36e12}, {CFG_128_192_K64, 3.8e12}};
+                                 {CFG_256_192_K64, 3.36e12}, {CFG_128_192_K64, 3.8e12}, {CFG_128_128_K64, 3.3e12}};
     static const int split_opts[] = {1, 2, 3, 4, 6, 8, 12, 16};
     const int64_t mn = (int64_t)g.M * g.N;
     const double out_bytes = out_bf(g) ? 2.0 : 4.0;

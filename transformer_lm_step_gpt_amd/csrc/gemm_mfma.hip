@@ -187,13 +187,30 @@ __device__ __attribute__((always_inline)) inline void half_step(f32x16 (&acc)[FM
     }
 }
 
+// The FM x FN products of one 16-deep step with the operations of `extra`
+// (slot p runs after product p) between them in program order.
+template <int FM, int FN, class X>
+__device__ __attribute__((always_inline)) inline void products(f32x16 (&acc)[FM][FN], const bf16x8 (&ca)[FM],
+                                                              const bf16x8 (&cb)[FN], X&& extra) {
+    constexpr int P = FM * FN;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        acc[p / FN][p % FN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[p / FN], cb[p % FN], acc[p / FN][p % FN], 0, 0, 0);
+        extra(p);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 constexpr int GROUP_M = 8;
 
 // SPLIT: write fp32 partial sums to part[z][M][N] instead of the epilogue.
 // OUTBF: output storage bf16 (1) or fp32 (0); ACT: activation of the
 // BIAS_ACT / ACT_GRAD epilogues. N and ldc are multiples of 8 and the output,
 // aux, residual and bias buffers 16-byte aligned (gemm_mfma_ok).
-template <int BM, int BN, int BK, int NS, int OCC, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
+// RS: a whole k-tile's fragments are read into registers at the start of the
+// tile, so its LDS stage is refilled one step into the tile instead of at its
+// end (each copy has about 1.5 k-tiles of products to land instead of one).
+template <int BM, int BN, int BK, int NS, int OCC, bool RS, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
 __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, float* part) {
     using TC = typename std::conditional<OUTBF != 0, bf16, float>::type;
     constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
@@ -289,6 +306,67 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
     //   last step of tile t: products | reads of step 0 of tile t+1
     constexpr int KS = BK / 16;
     static_assert(KS % 2 == 0 && NS <= 4, "even number of 16-deep steps; vmcnt bookkeeping for <= 3 tiles ahead");
+    if constexpr (RS) {
+        // Register-staged pipeline (KS >= 4), tile t:
+        //   step 0: products | reads of steps 1 .. KS-1 of tile t
+        //   step 1: after its first product every wave has its fragments of
+        //           tile t, so after a barrier the copy of tile t+NS goes into
+        //           the stage of tile t
+        //   steps 2 .. KS-2: products
+        //   wait + barrier for tile t+1
+        //   last step: products | reads of step 0 of tile t+1
+        static_assert(KS >= 4, "register staging needs four or more steps per k-tile");
+        constexpr int NF = FM + FN, P = FM * FN, NR = (KS - 1) * NF;
+        bf16x8 ra[KS][FM], rb[KS][FN];
+        if (nk > 0) {
+            wait_tile(0);
+            frags(0, 0, ra[0], rb[0]);
+        }
+        auto none = [](int) {};
+        for (int t = 0; t < nk; ++t) {
+            const bf16* as = smem + (t % NS) * STAGE;
+            const bf16* bs = as + TA::BYTES / 2;
+            auto rd = [&](int p) {
+#pragma unroll
+                for (int idx = 0; idx < NR; ++idx)
+                    if (idx * P / NR == p) {
+                        const int s = 1 + idx / NF, f = idx % NF;
+                        if (f < FM) ra[s][f] = TA::get(as, wm + 32 * f, s, lane);
+                        else rb[s][f - FM] = TB::get(bs, wn + 32 * (f - FM), s, lane);
+                    }
+            };
+            products<FM, FN>(acc, ra[0], rb[0], rd);
+            bf16* st = smem + (issued % NS) * STAGE;
+            const bool copy = issued < nk;
+            auto refill = [&](int p) {
+                if (p == 0) {
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    barrier_no_fence();
+                    if (copy) {
+#pragma unroll
+                        for (int q = 0; q < LPT; ++q) dma(q, st);
+                    }
+                }
+            };
+            products<FM, FN>(acc, ra[1], rb[1], refill);
+            if (copy) ++issued;
+#pragma unroll
+            for (int ks = 2; ks < KS - 1; ++ks) products<FM, FN>(acc, ra[ks], rb[ks], none);
+            if (t + 1 < nk) wait_tile(t + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // on the last tile these reads see a stage that holds no new tile; the values are never used
+            const bf16* an = smem + ((t + 1) % NS) * STAGE;
+            const bf16* bn = an + TA::BYTES / 2;
+            auto rd0 = [&](int p) {
+                if (p < NF) {
+                    const int f = p;
+                    if (f < FM) ra[0][f] = TA::get(an, wm + 32 * f, 0, lane);
+                    else rb[0][f - FM] = TB::get(bn, wn + 32 * (f - FM), 0, lane);
+                }
+            };
+            products<FM, FN>(acc, ra[KS - 1], rb[KS - 1], rd0);
+        }
+    } else {
     bf16x8 fa[2][FM], fb[2][FN];
     if (nk > 0) {
         wait_tile(0);
@@ -320,6 +398,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
                                       wm, wn, 0, lane, issue);
             if (copy) ++issued;
         }
+    }
     }
 
     // ---- epilogue. Each wave stages one 32-row strip of its sub-tile at a
@@ -411,19 +490,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(Gemm g, const float*
 // OCC workgroups per CU (register and LDS budget).
 enum GemmCfg {
     CFG_256_256 = 0, CFG_128_256, CFG_128_128, CFG_256_128, CFG_256_192, CFG_256_256_K64, CFG_256_192_K64,
-    CFG_256_128_K64, CFG_128_192_K64, CFG_128_256_K64, CFG_128_128_K64, CFG_COUNT
+    CFG_256_128_K64, CFG_128_192_K64, CFG_128_256_K64, CFG_128_128_K64,
+    // register-staged k-tiles (RS)
+    CFG_128_192_K64R, CFG_128_128_K64R, CFG_256_256_K64R, CFG_256_128_K64R, CFG_COUNT
 };
-static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256, 256, 256, 256, 128, 128, 128};
-static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192, 256, 192, 128, 192, 256, 128};
-static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32, 32, 64, 64, 64, 64, 64, 64};
-static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3, 2, 2, 2};
-static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1, 2, 1, 2};
+static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256, 256, 256, 256, 128, 128, 128, 128, 128, 256, 256};
+static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192, 256, 192, 128, 192, 256, 128, 192, 128, 256, 128};
+static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32, 32, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64};
+static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3, 2, 2, 2, 2, 2, 2, 2};
+static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1, 2, 1, 2, 2, 2, 1, 1};
+static const bool cfg_rs[CFG_COUNT] = {false, false, false, false, false, false, false, false, false, false, false,
+                                       true, true, true, true};
 
-template <int BM, int BN, int BK, int NS, int OCC, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
+template <int BM, int BN, int BK, int NS, int OCC, bool RS, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
 static void launch(const Gemm& g, dim3 grid, int kps, float* part, hipStream_t s) {
     constexpr size_t LDS = (size_t)NS * (BM + BN) * BK * sizeof(bf16);
     static_assert(LDS * OCC <= 160 * 1024, "LDS budget");
-    auto k = gemm_mfma_kernel<BM, BN, BK, NS, OCC, AKC, BKC, EPI, OUTBF, ACT, SPLIT>;
+    auto k = gemm_mfma_kernel<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI, OUTBF, ACT, SPLIT>;
     static bool attr = false;
     if (!attr) {
         (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
@@ -440,47 +523,51 @@ static int out_bf(const Gemm& g) {
     return 1;
 }
 
-template <int BM, int BN, int BK, int NS, int OCC, bool AKC, bool BKC>
+template <int BM, int BN, int BK, int NS, int OCC, bool RS, bool AKC, bool BKC>
 static void run_main(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
     dim3 grid(ceil_div(g.N, BN) * ceil_div(g.M, BM), 1, p.splits);
     const int kps = ceil_div(ceil_div(g.K, p.splits), BK) * BK;
-    if (p.splits > 1) { launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_STORE, 0, 0, true>(g, grid, kps, part, s); return; }
+    if (p.splits > 1) { launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_STORE, 0, 0, true>(g, grid, kps, part, s); return; }
     const bool relu = g.act == ACT_RELU2;
     switch (g.epi) {
         case EPI_STORE:
-            if (g.c_bf) launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_STORE, 1, 0, false>(g, grid, kps, part, s);
-            else launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_STORE, 0, 0, false>(g, grid, kps, part, s);
+            if (g.c_bf) launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_STORE, 1, 0, false>(g, grid, kps, part, s);
+            else launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_STORE, 0, 0, false>(g, grid, kps, part, s);
             break;
-        case EPI_BIAS: launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_BIAS, 1, 0, false>(g, grid, kps, part, s); break;
+        case EPI_BIAS: launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_BIAS, 1, 0, false>(g, grid, kps, part, s); break;
         case EPI_BIAS_ACT:
-            if (relu) launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_BIAS_ACT, 1, ACT_RELU2, false>(g, grid, kps, part, s);
-            else launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_BIAS_ACT, 1, ACT_GELU, false>(g, grid, kps, part, s);
+            if (relu) launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_BIAS_ACT, 1, ACT_RELU2, false>(g, grid, kps, part, s);
+            else launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_BIAS_ACT, 1, ACT_GELU, false>(g, grid, kps, part, s);
             break;
         case EPI_BIAS_RESID:
-            launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_BIAS_RESID, 0, 0, false>(g, grid, kps, part, s);
+            launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_BIAS_RESID, 0, 0, false>(g, grid, kps, part, s);
             break;
         case EPI_ACT_GRAD:
-            if (relu) launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_ACT_GRAD, 1, ACT_RELU2, false>(g, grid, kps, part, s);
-            else launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_ACT_GRAD, 1, ACT_GELU, false>(g, grid, kps, part, s);
+            if (relu) launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_ACT_GRAD, 1, ACT_RELU2, false>(g, grid, kps, part, s);
+            else launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_ACT_GRAD, 1, ACT_GELU, false>(g, grid, kps, part, s);
             break;
-        case EPI_ACCUM: launch<BM, BN, BK, NS, OCC, AKC, BKC, EPI_ACCUM, 0, 0, false>(g, grid, kps, part, s); break;
+        case EPI_ACCUM: launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_ACCUM, 0, 0, false>(g, grid, kps, part, s); break;
     }
 }
 
 template <bool AKC, bool BKC>
 static void run_cfg(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
     switch (p.cfg) {
-        case CFG_256_256: run_main<256, 256, 32, 4, 1, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_256: run_main<128, 256, 32, 4, 1, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_128: run_main<128, 128, 32, 4, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_128: run_main<256, 128, 32, 3, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_192: run_main<256, 192, 32, 4, 1, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_256_K64: run_main<256, 256, 64, 2, 1, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_192_K64: run_main<256, 192, 64, 2, 1, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_128_K64: run_main<256, 128, 64, 3, 1, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_192_K64: run_main<128, 192, 64, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_256_K64: run_main<128, 256, 64, 2, 1, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_128_K64: run_main<128, 128, 64, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256: run_main<256, 256, 32, 4, 1, false, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_256: run_main<128, 256, 32, 4, 1, false, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128: run_main<128, 128, 32, 4, 2, false, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128: run_main<256, 128, 32, 3, 2, false, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_192: run_main<256, 192, 32, 4, 1, false, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64: run_main<256, 256, 64, 2, 1, false, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_192_K64: run_main<256, 192, 64, 2, 1, false, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128_K64: run_main<256, 128, 64, 3, 1, false, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_192_K64: run_main<128, 192, 64, 2, 2, false, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_256_K64: run_main<128, 256, 64, 2, 1, false, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128_K64: run_main<128, 128, 64, 2, 2, false, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_192_K64R: run_main<128, 192, 64, 2, 2, true, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128_K64R: run_main<128, 128, 64, 2, 2, true, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64R: run_main<256, 256, 64, 2, 1, true, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128_K64R: run_main<256, 128, 64, 2, 1, true, AKC, BKC>(g, p, part, s); break;
     }
 }
 
@@ -543,16 +630,16 @@ struct Tuned { int M, N, K; bool a_kc, b_kc; int cfg, splits; };
 static const Tuned tuned[] = {
     // forward: X W^T
     {16384, 2304, 768, true, true, CFG_128_192_K64, 1}, {16384, 768, 768, true, true, CFG_128_192_K64, 1},
-    {16384, 3072, 768, true, true, CFG_256_128, 1}, {16384, 768, 3072, true, true, CFG_128_192_K64, 1},
-    {16384, 50304, 768, true, true, CFG_256_256_K64, 1},
+    {16384, 3072, 768, true, true, CFG_128_192_K64, 1}, {16384, 768, 3072, true, true, CFG_128_192_K64, 1},
+    {16384, 50304, 768, true, true, CFG_256_256_K64R, 1},
     // input gradients: dY W
-    {16384, 3072, 768, true, false, CFG_256_128, 1}, {16384, 768, 3072, true, false, CFG_128_192_K64, 1},
-    {16384, 768, 768, true, false, CFG_128_192_K64, 1}, {16384, 768, 2304, true, false, CFG_128_192_K64, 1},
-    {16384, 768, 50304, true, false, CFG_128_192_K64, 1},
+    {16384, 3072, 768, true, false, CFG_128_192_K64R, 1}, {16384, 768, 3072, true, false, CFG_128_192_K64R, 1},
+    {16384, 768, 768, true, false, CFG_128_192_K64R, 1}, {16384, 768, 2304, true, false, CFG_128_192_K64R, 1},
+    {16384, 768, 50304, true, false, CFG_128_192_K64R, 1},
     // weight gradients: dY^T X
-    {768, 3072, 16384, false, false, CFG_128_192_K64, 4}, {3072, 768, 16384, false, false, CFG_128_192_K64, 4},
-    {768, 768, 16384, false, false, CFG_128_128, 8}, {2304, 768, 16384, false, false, CFG_128_128_K64, 4},
-    {50304, 768, 16384, false, false, CFG_128_192_K64, 2},
+    {768, 3072, 16384, false, false, CFG_128_128_K64R, 3}, {3072, 768, 16384, false, false, CFG_128_128_K64R, 3},
+    {768, 768, 16384, false, false, CFG_128_128_K64R, 12}, {2304, 768, 16384, false, false, CFG_128_128_K64R, 4},
+    {50304, 768, 16384, false, false, CFG_128_192_K64R, 2},
 };
 
 GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
@@ -612,8 +699,9 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
     p.cfg = bcfg;
     p.splits = bsplits;
     const bool relu = bsplits == 1 && (g.epi == EPI_BIAS_ACT || g.epi == EPI_ACT_GRAD) && g.act == ACT_RELU2;
-    snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %s, %s, %d, %d, %d, %s>", cfg_bm[bcfg],
-             cfg_bn[bcfg], cfg_bk[bcfg], cfg_ns[bcfg], cfg_occ[bcfg], g.a_kc ? "true" : "false", g.b_kc ? "true" : "false",
+    snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %s, %s, %s, %d, %d, %d, %s>", cfg_bm[bcfg],
+             cfg_bn[bcfg], cfg_bk[bcfg], cfg_ns[bcfg], cfg_occ[bcfg], cfg_rs[bcfg] ? "true" : "false",
+             g.a_kc ? "true" : "false", g.b_kc ? "true" : "false",
              bsplits > 1 ? 0 : g.epi, bsplits > 1 ? 0 : out_bf(g), relu ? 1 : 0, bsplits > 1 ? "true" : "false");
     return p;
 }

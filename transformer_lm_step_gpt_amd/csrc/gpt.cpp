@@ -120,7 +120,12 @@ struct Ws {
     float* dln = nullptr;
     void *dh = nullptr, *dO = nullptr, *dqkv = nullptr;
     float* attD = nullptr;
-    float *ln_partial = nullptr, *cs_partial = nullptr;
+    // row-pass partial sums of every LayerNorm backward and bias column sum of
+    // a backward pass, reduced together at its end (reduce_jobs)
+    float *ln_part = nullptr, *cs_part = nullptr, *red_tmp = nullptr;
+    size_t ln_part_stride = 0, cs_part_stride = 0;
+    gk::RedJob* red_jobs = nullptr;
+    int red_max_jobs = 0;
     double* gn_partial = nullptr;
     void* emb_scratch = nullptr;
     float* splitk = nullptr;
@@ -183,9 +188,17 @@ Ws plan(const gpt_config& c, const Table& tb, void* base) {
     w.dO = cv.take(ab * M * d);
     w.dqkv = cv.take(ab * M * 3 * d);
     w.attD = cv.arr<float>(M * H);
-    w.ln_partial = cv.arr<float>(gk::layernorm_bwd_partial_floats((int)M, (int)d));
-    int64_t maxN = std::max<int64_t>(3 * d, F);
-    w.cs_partial = cv.arr<float>(gk::colsum_partial_floats((int)M, (int)maxN));
+    {
+        const int64_t maxN = std::max<int64_t>(3 * d, F);
+        const int nbl = gk::layernorm_bwd_num_partials((int)M), npc = gk::colsum_num_partials((int)M);
+        w.ln_part_stride = (size_t)3 * nbl * d;
+        w.cs_part_stride = (size_t)npc * maxN;
+        w.ln_part = cv.arr<float>((size_t)(2 * L + 1) * w.ln_part_stride);
+        w.cs_part = cv.arr<float>((size_t)(2 * L) * w.cs_part_stride);
+        w.red_max_jobs = (int)((2 * L + 1) * 3 + 2 * L);
+        w.red_tmp = cv.arr<float>(gk::reduce_jobs_tmp_floats(w.red_max_jobs, std::max(nbl, npc), (int)std::max(d, maxN)));
+        w.red_jobs = (gk::RedJob*)cv.take(sizeof(gk::RedJob) * w.red_max_jobs);
+    }
     w.gn_partial = cv.arr<double>(1024);
     w.emb_scratch = cv.take(gk::embed_bwd_scratch_bytes((int)M, (int)d));
     // fp32 slices of split-K products (matrix-core path only): weight
@@ -239,12 +252,12 @@ gpt_status validate(const gpt_config* c, std::string* why) {
 enum KClass {
     KC_EMBED_FWD, KC_LN_FWD, KC_GEMM_FWD, KC_GEMM_LMHEAD, KC_ATTN_FWD, KC_CE, KC_GEMM_DGRAD, KC_GEMM_WGRAD,
     KC_GEMM_LMHEAD_BWD, KC_LN_BWD, KC_COLSUM, KC_ATTN_BWD, KC_QK_PREP, KC_EMBED_BWD, KC_GRAD_NORM, KC_ADAMW,
-    KC_MISC, KC_COUNT
+    KC_MISC, KC_PARTIAL_REDUCE, KC_COUNT
 };
 const char* kc_names[KC_COUNT] = {
     "embed_fwd", "layernorm_fwd", "gemm_fwd", "gemm_lm_head", "attention_fwd", "cross_entropy", "gemm_dgrad",
     "gemm_wgrad", "gemm_lm_head_bwd", "layernorm_bwd", "colsum", "attention_bwd", "qk_prep", "embed_bwd",
-    "grad_norm", "adamw", "misc"};
+    "grad_norm", "adamw", "misc", "partial_reduce"};
 
 struct Pending { int cls; int name; hipEvent_t a, b; double flops, bytes; };
 struct ClassStat { double ms = 0, flops = 0, bytes = 0; int64_t launches = 0; };
@@ -266,6 +279,8 @@ struct gpt_handle {
     ClassStat stats[KC_COUNT];
     std::vector<NameStat> names;     // per kernel (instantiation) name
     std::string filter;              // also time launches of this kernel name
+    std::vector<gk::RedJob> jobs;    // this backward pass's deferred reductions
+    std::vector<gk::RedJob> jobs_dev;   // the table last copied to the workspace
 };
 
 namespace {
@@ -627,11 +642,27 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         run_gemm(h, KC_GEMM_LMHEAD_BWD, g2);
     }
     void* dR = bf ? w.dres_lp : (void*)w.dres;   // residual gradient as a matrix-product operand
-    {
-        Timed t(h, KC_LN_BWD, 0, (double)M * d * (4 * 3 + ab) + 8.0 * M);
-        gk::layernorm_bwd(bf, w.dln, w.x_fin, meanf, rstdf, P(h, tb.lnf_w), w.dres, bf ? w.dres_lp : nullptr, true,
-                          G(h, tb.lnf_w), G(h, tb.lnf_b), G(h, tb.layers[L - 1].mp_b), w.ln_partial, M, d, st);
-    }
+    // LayerNorm backward row passes and bias column sums leave their partial
+    // sums in per-call slots; one reduce_jobs at the end of the pass sums them
+    h->jobs.clear();
+    const int nbl = gk::layernorm_bwd_num_partials(M), npc = gk::colsum_num_partials(M);
+    int n_ln = 0, n_cs = 0;
+    auto ln_bwd = [&](const float* x, const float* mean, const float* rstd, const float* g, bool overwrite, float* dg,
+                      float* db, float* dcol) {
+        Timed t(h, KC_LN_BWD, 0, (double)M * d * ((overwrite ? 12 : 16) + ab) + 8.0 * M + 12.0 * nbl * d);
+        float* part = w.ln_part + (size_t)(n_ln++) * w.ln_part_stride;
+        gk::layernorm_bwd_rows(bf, w.dln, x, mean, rstd, g, w.dres, bf ? w.dres_lp : nullptr, overwrite, part, M, d, st);
+        float* outs[3] = {dg, db, dcol};
+        for (int q = 0; q < 3; ++q)
+            if (outs[q]) h->jobs.push_back({part + (size_t)q * nbl * d, outs[q], nbl, d});
+    };
+    auto col_sum = [&](const void* Y, int N, float* out) {
+        Timed t(h, KC_COLSUM, 0, (double)ab * M * N + 4.0 * npc * N);
+        float* part = w.cs_part + (size_t)(n_cs++) * w.cs_part_stride;
+        gk::colsum_rows(bf, Y, N, M, N, part, st);
+        h->jobs.push_back({part, out, npc, N});
+    };
+    ln_bwd(w.x_fin, meanf, rstdf, P(h, tb.lnf_w), true, G(h, tb.lnf_w), G(h, tb.lnf_b), G(h, tb.layers[L - 1].mp_b));
     for (int l = L - 1; l >= 0; --l) {
         const LayerIdx& li = tb.layers[l];
         float* mean1 = w.ln_mean + (size_t)(2 * l) * M;
@@ -652,15 +683,8 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
             gk::Gemm g2 = mk_gemm(h, F, d, M, w.dh, F, false, w.ln2[l], d, false, G(h, li.fc_w), d, false, gk::EPI_ACCUM);
             run_gemm(h, KC_GEMM_WGRAD, g2);
         }
-        {
-            Timed t(h, KC_COLSUM, 0, ab * M * F);
-            gk::colsum(bf, w.dh, F, M, F, G(h, li.fc_b), w.cs_partial, st);
-        }
-        {
-            Timed t(h, KC_LN_BWD, 0, (double)M * d * (4 * 4 + ab) + 8.0 * M);
-            gk::layernorm_bwd(bf, w.dln, w.x_mid[l], mean2, rstd2, P(h, li.ln2_w), w.dres, bf ? w.dres_lp : nullptr,
-                              false, G(h, li.ln2_w), G(h, li.ln2_b), G(h, li.proj_b), w.ln_partial, M, d, st);
-        }
+        col_sum(w.dh, F, G(h, li.fc_b));
+        ln_bwd(w.x_mid[l], mean2, rstd2, P(h, li.ln2_w), false, G(h, li.ln2_w), G(h, li.ln2_b), G(h, li.proj_b));
         // attention branch
         {
             gk::Gemm g = mk_gemm(h, M, d, d, dR, d, true, Wop(h, li.proj_w), d, false, w.dO, d, bf, gk::EPI_STORE);
@@ -700,16 +724,31 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
                                   gk::EPI_ACCUM);
             run_gemm(h, KC_GEMM_WGRAD, g2);
         }
-        {
-            Timed t(h, KC_COLSUM, 0, ab * M * 3 * d);
-            gk::colsum(bf, w.dqkv, 3 * d, M, 3 * d, G(h, li.attn_b), w.cs_partial, st);
+        col_sum(w.dqkv, 3 * d, G(h, li.attn_b));
+        ln_bwd(w.x_in[l], mean1, rstd1, P(h, li.ln1_w), false, G(h, li.ln1_w), G(h, li.ln1_b),
+               l > 0 ? G(h, tb.layers[l - 1].mp_b) : nullptr);
+    }
+    if (!h->jobs.empty()) {
+        auto same = [](const gk::RedJob& a, const gk::RedJob& b) {
+            return a.part == b.part && a.out == b.out && a.np == b.np && a.n == b.n;
+        };
+        const bool changed = h->jobs.size() != h->jobs_dev.size() ||
+                             !std::equal(h->jobs.begin(), h->jobs.end(), h->jobs_dev.begin(), same);
+        if (changed) {
+            if ((int)h->jobs.size() > w.red_max_jobs) return fail(h, GPT_ERR_UNSUPPORTED, "reduction table overflow");
+            // the previous pass's reduction may still read the table
+            gpt_status s = hip_check(h, hipStreamSynchronize(st), "hipStreamSynchronize");
+            if (s != GPT_OK) return s;
+            s = hip_check(h, hipMemcpy(w.red_jobs, h->jobs.data(), sizeof(gk::RedJob) * h->jobs.size(),
+                                       hipMemcpyHostToDevice), "copy reduction table");
+            if (s != GPT_OK) return s;
+            h->jobs_dev = h->jobs;
         }
-        {
-            Timed t(h, KC_LN_BWD, 0, (double)M * d * (4 * 4 + ab) + 8.0 * M);
-            gk::layernorm_bwd(bf, w.dln, w.x_in[l], mean1, rstd1, P(h, li.ln1_w), w.dres, bf ? w.dres_lp : nullptr,
-                              false, G(h, li.ln1_w), G(h, li.ln1_b), l > 0 ? G(h, tb.layers[l - 1].mp_b) : nullptr,
-                              w.ln_partial, M, d, st);
-        }
+        double bytes = 0;
+        for (const gk::RedJob& j : h->jobs) bytes += 4.0 * j.np * j.n + 8.0 * j.n;
+        Timed t(h, KC_PARTIAL_REDUCE, 0, bytes);
+        gk::reduce_jobs(w.red_jobs, (int)h->jobs.size(), std::max(nbl, npc), (int)std::max<int64_t>(d, std::max<int64_t>(3 * d, F)),
+                        w.red_tmp, st);
     }
     {
         Timed t(h, KC_EMBED_BWD, 0, 4.0 * M * d + 8.0 * M * d);

@@ -50,6 +50,30 @@ void layernorm_bwd(bool bf, const float* dy, const float* x, const float* mean, 
 size_t colsum_partial_floats(int M, int N);
 void colsum(bool y_bf, const void* Y, int64_t ld, int M, int N, float* out, float* partial, hipStream_t s);
 
+// Forms that only launch the row pass and leave the partial sums for
+// reduce_jobs: layernorm_bwd_rows writes [3][nb][d] (dgamma, dbeta, column
+// sums of the new dres; nb = layernorm_bwd_num_partials(M)), colsum_rows
+// writes [np][N] (np = colsum_num_partials(M)).
+int layernorm_bwd_num_partials(int M);
+void layernorm_bwd_rows(bool bf, const float* dy, const float* x, const float* mean, const float* rstd,
+                        const float* g, float* dres, void* dres_lp, bool overwrite, float* partial, int M, int d,
+                        hipStream_t s);
+int colsum_num_partials(int M);
+void colsum_rows(bool y_bf, const void* Y, int64_t ld, int M, int N, float* partial, hipStream_t s);
+
+// Deferred column reductions: for each job, out[c] += sum over p < np of
+// part[p * n + c], c < n, summed in a fixed order (groups of 64 partial rows,
+// then the groups in order), all jobs in two launches. jobs is a device array;
+// tmp holds reduce_jobs_tmp_floats(njobs, max_np, max_n) floats, max_np and
+// max_n bounding every job's np and n.
+struct RedJob {
+    const float* part;
+    float* out;
+    int np, n;
+};
+size_t reduce_jobs_tmp_floats(int njobs, int max_np, int max_n);
+void reduce_jobs(const RedJob* jobs, int njobs, int max_np, int max_n, float* tmp, hipStream_t s);
+
 // ---------------------------------------------------------------- cross-entropy
 // Per row of logits z (act, [M, Vp], in place): z' = cap tanh(z/cap) if cap > 0;
 // loss_m = logsumexp(z') - z'[y_m]; z <- (softmax(z') - onehot(y)) * gscale

@@ -585,6 +585,50 @@ static void reduce_partials(const float* part, int np, int n, int nq, float* tmp
     reduce_partials_stage2<<<dim3(ceil_div(n, 256), nq), 256, 0, s>>>(tmp, ng, n, o0, o1, o2);
 }
 
+// ---- deferred reductions: every job in one pair of launches
+size_t reduce_jobs_tmp_floats(int njobs, int max_np, int max_n) {
+    return (size_t)njobs * ceil_div(max_np, 64) * max_n;
+}
+
+// tmp[job][grp][c] = sum of partial rows 64 grp .. 64 grp + 63 of the job
+__global__ __launch_bounds__(256) void reduce_jobs_stage1(const RedJob* __restrict__ jobs, int G, int max_n,
+                                                          float* __restrict__ tmp) {
+    const RedJob jb = jobs[blockIdx.z];
+    const int c = blockIdx.x * 256 + threadIdx.x, grp = blockIdx.y;
+    const int p0 = grp * 64, p1 = min(jb.np, p0 + 64);
+    if (c >= jb.n || p0 >= p1) return;
+    const float* src = jb.part + c;
+    float a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = 0.f;
+    int p = p0;
+    for (; p + 8 <= p1; p += 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += src[(int64_t)(p + e) * jb.n];
+    }
+    for (; p < p1; ++p) a[0] += src[(int64_t)p * jb.n];
+    tmp[((int64_t)blockIdx.z * G + grp) * max_n + c] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+}
+
+// out[c] += sum of the job's group sums, in group order
+__global__ __launch_bounds__(256) void reduce_jobs_stage2(const RedJob* __restrict__ jobs, int G, int max_n,
+                                                          const float* __restrict__ tmp) {
+    const RedJob jb = jobs[blockIdx.y];
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= jb.n) return;
+    const int ng = ceil_div(jb.np, 64);
+    float a = 0.f;
+    for (int grp = 0; grp < ng; ++grp) a += tmp[((int64_t)blockIdx.y * G + grp) * max_n + c];
+    jb.out[c] += a;
+}
+
+void reduce_jobs(const RedJob* jobs, int njobs, int max_np, int max_n, float* tmp, hipStream_t s) {
+    if (njobs <= 0) return;
+    const int G = ceil_div(max_np, 64);
+    reduce_jobs_stage1<<<dim3(ceil_div(max_n, 256), G, njobs), 256, 0, s>>>(jobs, G, max_n, tmp);
+    reduce_jobs_stage2<<<dim3(ceil_div(max_n, 256), njobs), 256, 0, s>>>(jobs, G, max_n, tmp);
+}
+
 template <typename TL>
 static void lnb_launch(int nv, int nb, const float* dy, const float* x, const float* mean, const float* rstd,
                        const float* g, float* dres, TL* lp, int ov, float* part, int M, int d, hipStream_t s) {
@@ -597,13 +641,21 @@ static void lnb_launch(int nv, int nb, const float* dy, const float* x, const fl
     }
 }
 
-void layernorm_bwd(bool bf, const float* dy, const float* x, const float* mean, const float* rstd, const float* g,
-                   float* dres, void* dres_lp, bool overwrite, float* dg, float* db, float* dcol, float* partial,
-                   int M, int d, hipStream_t s) {
+int layernorm_bwd_num_partials(int M) { return ceil_div(M, LNB_ROWS); }
+
+void layernorm_bwd_rows(bool bf, const float* dy, const float* x, const float* mean, const float* rstd, const float* g,
+                        float* dres, void* dres_lp, bool overwrite, float* partial, int M, int d, hipStream_t s) {
     const int nb = ceil_div(M, LNB_ROWS);
     const int nv = ceil_div(d, 256);
     if (bf) lnb_launch<bf16>(nv, nb, dy, x, mean, rstd, g, dres, (bf16*)dres_lp, overwrite, partial, M, d, s);
     else lnb_launch<float>(nv, nb, dy, x, mean, rstd, g, dres, (float*)dres_lp, overwrite, partial, M, d, s);
+}
+
+void layernorm_bwd(bool bf, const float* dy, const float* x, const float* mean, const float* rstd, const float* g,
+                   float* dres, void* dres_lp, bool overwrite, float* dg, float* db, float* dcol, float* partial,
+                   int M, int d, hipStream_t s) {
+    const int nb = ceil_div(M, LNB_ROWS);
+    layernorm_bwd_rows(bf, dy, x, mean, rstd, g, dres, dres_lp, overwrite, partial, M, d, s);
     reduce_partials(partial, nb, d, dcol ? 3 : 2, partial + (size_t)3 * nb * d, dg, db, dcol, s);
 }
 
@@ -667,7 +719,9 @@ __global__ __launch_bounds__(64) void colsum_kernel(const TI* __restrict__ Y, in
     for (int e = 0; e < 8 && c0 + e < N; ++e) part[(int64_t)blockIdx.y * N + c0 + e] = a[e];
 }
 
-void colsum(bool y_bf, const void* Y, int64_t ld, int M, int N, float* out, float* partial, hipStream_t s) {
+int colsum_num_partials(int M) { return ceil_div(M, CS_ROWS); }
+
+void colsum_rows(bool y_bf, const void* Y, int64_t ld, int M, int N, float* partial, hipStream_t s) {
     const int np = ceil_div(M, CS_ROWS);
     dim3 grid(ceil_div(N, 64 * 8), np);
     const bool vec = (ld % 8) == 0 && ((uintptr_t)Y % 16) == 0;
@@ -678,6 +732,11 @@ void colsum(bool y_bf, const void* Y, int64_t ld, int M, int N, float* out, floa
         if (y_bf) colsum_scalar_kernel<bf16><<<dim3(ceil_div(N, 256), np), 256, 0, s>>>((const bf16*)Y, ld, M, N, partial);
         else colsum_scalar_kernel<float><<<dim3(ceil_div(N, 256), np), 256, 0, s>>>((const float*)Y, ld, M, N, partial);
     }
+}
+
+void colsum(bool y_bf, const void* Y, int64_t ld, int M, int N, float* out, float* partial, hipStream_t s) {
+    const int np = ceil_div(M, CS_ROWS);
+    colsum_rows(y_bf, Y, ld, M, N, partial, s);
     reduce_partials(partial, np, N, 1, partial + (size_t)np * N, out, nullptr, nullptr, s);
 }
 

@@ -281,6 +281,10 @@ struct gpt_handle {
     std::string filter;              // also time launches of this kernel name
     std::vector<gk::RedJob> jobs;    // this backward pass's deferred reductions
     std::vector<gk::RedJob> jobs_dev;   // the table last copied to the workspace
+    // side stream (default priority) for the embedding backward's token sort,
+    // which depends on the tokens only and overlaps the forward pass
+    hipStream_t side = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
 
 namespace {
@@ -502,7 +506,17 @@ gpt_status gpt_create(const gpt_config* cfg, uint64_t seed, void* d_ws, size_t w
     gk::fill_f32(w.loss_last, 4, 0.f, st);
     gk::fill_i32(w.nonfinite, 4, 0, st);
     s = hip_check(h, hipGetLastError(), "kernel launch");
-    if (s != GPT_OK) { delete h; return s; }
+    if (s == GPT_OK) s = hip_check(h, hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking), "hipStreamCreate");
+    if (s == GPT_OK) s = hip_check(h, hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming), "hipEventCreate");
+    if (s == GPT_OK) s = hip_check(h, hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming), "hipEventCreate");
+    if (s != GPT_OK) {
+        (void)hipStreamSynchronize(st);
+        if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+        if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+        if (h->side) (void)hipStreamDestroy(h->side);
+        delete h;
+        return s;
+    }
     h->grads_dirty = true;
     *out = h;
     return GPT_OK;
@@ -513,6 +527,10 @@ gpt_status gpt_destroy(gpt_handle* h) {
     if (!h->pending.empty()) (void)hipStreamSynchronize(h->stream);
     for (auto& p : h->pending) { (void)hipEventDestroy(p.a); (void)hipEventDestroy(p.b); }
     for (auto e : h->free_events) (void)hipEventDestroy(e);
+    if (h->side) (void)hipStreamSynchronize(h->side);
+    if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+    if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+    if (h->side) (void)hipStreamDestroy(h->side);
     delete h;
     return GPT_OK;
 }
@@ -550,6 +568,17 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         gk::fill_f32(w.loss_sum, 1, 0.f, st);
         h->grads_dirty = false;
         h->micro_count = 0;
+    }
+    // token sort of the embedding backward, on the side stream: it waits for
+    // the work queued so far on the main stream (the tokens), and the main
+    // stream waits for it before the embedding gradient
+    {
+        gpt_status s = hip_check(h, hipEventRecord(h->ev_fork, st), "hipEventRecord");
+        if (s == GPT_OK) s = hip_check(h, hipStreamWaitEvent(h->side, h->ev_fork, 0), "hipStreamWaitEvent");
+        if (s != GPT_OK) return s;
+        gk::embed_bwd_sort(tok, B, T, d, Vp, w.emb_scratch, h->side);
+        s = hip_check(h, hipEventRecord(h->ev_join, h->side), "hipEventRecord");
+        if (s != GPT_OK) return s;
     }
     // ------------------------------------------------------------ forward
     {
@@ -752,7 +781,9 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
     }
     {
         Timed t(h, KC_EMBED_BWD, 0, 4.0 * M * d + 8.0 * M * d);
-        gk::embed_bwd(tok, w.dres, G(h, tb.wte), tb.wpe >= 0 ? G(h, tb.wpe) : nullptr, B, T, d, Vp, w.emb_scratch, st);
+        gpt_status s = hip_check(h, hipStreamWaitEvent(st, h->ev_join, 0), "hipStreamWaitEvent");
+        if (s != GPT_OK) return s;
+        gk::embed_bwd_accumulate(w.dres, G(h, tb.wte), tb.wpe >= 0 ? G(h, tb.wpe) : nullptr, B, T, d, w.emb_scratch, st);
     }
     h->micro_count += 1;
     gpt_status s = hip_check(h, hipGetLastError(), "kernel launch");

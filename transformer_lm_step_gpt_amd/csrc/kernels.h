@@ -30,6 +30,11 @@ void embed_fwd(const int32_t* tok, const float* wte, const float* wpe, float* x0
 size_t embed_bwd_scratch_bytes(int M, int d);
 void embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, int B, int T, int d, int Vp,
                void* scratch, hipStream_t s);
+// embed_bwd in two parts: the token sort (depends on the tokens only, so it
+// can run early on another stream) and the accumulation that reads dx.
+void embed_bwd_sort(const int32_t* tok, int B, int T, int d, int Vp, void* scratch, hipStream_t s);
+void embed_bwd_accumulate(const float* dx, float* dwte, float* dwpe, int B, int T, int d, void* scratch,
+                          hipStream_t s);
 
 // ---------------------------------------------------------------- LayerNorm
 // y = (x - mean) rstd * g + b over rows of width d (fp32 x, act y); saves mean, rstd.

@@ -330,8 +330,7 @@ __global__ __launch_bounds__(256) void embed_wpe_kernel(const float* dx, float* 
     store4(dwpe + (int64_t)t * d + c, acc);
 }
 
-void embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, int B, int T, int d, int Vp,
-               void* scratch, hipStream_t s) {
+void embed_bwd_sort(const int32_t* tok, int B, int T, int d, int Vp, void* scratch, hipStream_t s) {
     int M = B * T;
     int N = EMB_THREADS;
     while (N < M) N <<= 1;
@@ -344,9 +343,21 @@ void embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, in
         attr_set = true;
     }
     embed_sort_kernel<<<1, EMB_THREADS, lds, s>>>(tok, M, Vp, N, e);
+}
+
+void embed_bwd_accumulate(const float* dx, float* dwte, float* dwpe, int B, int T, int d, void* scratch,
+                          hipStream_t s) {
+    const int M = B * T;
+    EmbScratch e = carve_emb(scratch, M, d);
     embed_piece_kernel<<<M, 256, 0, s>>>(dx, d, e);
     embed_segment_kernel<<<M, 256, 0, s>>>(dwte, d, e);
     if (dwpe) embed_wpe_kernel<<<ceil_div((int64_t)T * (d / 4), 256), 256, 0, s>>>(dx, dwpe, B, T, d);
+}
+
+void embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, int B, int T, int d, int Vp,
+               void* scratch, hipStream_t s) {
+    embed_bwd_sort(tok, B, T, d, Vp, scratch, s);
+    embed_bwd_accumulate(dx, dwte, dwpe, B, T, d, scratch, s);
 }
 
 // =====================================================================

@@ -32,6 +32,19 @@ gpt_status gptk_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda
                      int32_t act, const float* bias, const float* resid, const void* aux, void* C2,
                      float* splitk_scratch, int64_t splitk_floats, void* stream);
 
+/* gptk_gemm plus the column sums of its output C (the bias gradient of a
+ * layer whose output gradient C is): colsum_out[n] += sum over m of C(m, n).
+ * With the ACT_GRAD epilogue on the matrix-core path without split-K the sums
+ * are fused into the epilogue (fp32 values before storage rounding, per block
+ * of rows, then reduced in a fixed order); otherwise a column-sum pass reads
+ * the stored C. partial holds gptk_colsum_partial_floats(M, N) floats; the
+ * ACCUM epilogue is not supported. */
+gpt_status gptk_gemm_colsum(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int32_t a_kc, const void* B,
+                            int64_t ldb, int32_t b_kc, void* C, int64_t ldc, int32_t in_bf16, int32_t c_bf16,
+                            int32_t epi, int32_t act, const float* bias, const float* resid, const void* aux, void* C2,
+                            float* colsum_out, float* partial, float* splitk_scratch, int64_t splitk_floats,
+                            void* stream);
+
 /* Test control of the matrix-core GEMM: subsequent bf16 products (gptk_gemm
  * and the training step alike) use tile configuration cfg (0 <= cfg <
  * gptk_gemm_num_configs()) and split-K factor splits (0 = automatic, capped by

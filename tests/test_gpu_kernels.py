@@ -181,6 +181,50 @@ def test_gemm_epilogues(lib, epi, act, bf, shape):
         assert relmax(host(C), resid + acc) < tol
 
 
+def _gemm_colsum_case(lib, M, N, K, bf, seed):
+    rng = np.random.default_rng(seed)
+    At, Bt, A, B = gemm_inputs(M, N, K, 1, 0, bf, rng)
+    acc = gemm_ref(A, B, 1, 0)
+    aux = dev(rng.uniform(-1.0, 1.0, size=(M, N)), bf)
+    C = torch.zeros((M, N), dtype=torch.bfloat16 if bf else torch.float32, device="cuda")
+    out0 = rng.normal(size=N)
+    out = torch.tensor(out0, dtype=torch.float32, device="cuda")
+    part = torch.zeros(int(lib.gptk_colsum_partial_floats(M, N)), dtype=torch.float32, device="cuda")
+    scratch = torch.zeros(4 * M * N, dtype=torch.float32, device="cuda")
+    st = lib.gptk_gemm_colsum(M, N, K, At.data_ptr(), K, 1, Bt.data_ptr(), N, 0, C.data_ptr(), N, bf, bf, 4, 0, None,
+                              None, aux.data_ptr(), None, out.data_ptr(), part.data_ptr(), scratch.data_ptr(),
+                              scratch.numel(), stream())
+    assert st == 0
+    torch.cuda.synchronize()
+    ref = acc * host(aux)
+    tol = 1e-2 if bf else 3e-5
+    assert relmax(host(C), ref) < tol
+    # fused sums add fp32 values before storage rounding; the separate pass adds the stored values
+    assert relmax(host(out) - out0, ref.sum(0)) < (1e-2 if bf else 1e-5)
+
+
+@pytest.mark.parametrize("bf", [0, 1], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("shape", [(16384, 3072, 768), (1000, 200, 192), (300, 136, 64), (5000, 72, 384),
+                                   (4096, 4096, 64), (33, 8, 64)])
+def test_gemm_act_grad_colsum(lib, shape, bf):
+    """ACT_GRAD product with the bias-gradient column sums (fused into the epilogue on the matrix-core path)."""
+    M, N, K = shape
+    say(f"gemm colsum {shape} bf={bf}")
+    _gemm_colsum_case(lib, M, N, K, bf, M + N + K)
+
+
+@pytest.mark.parametrize("cfg", list(range(15)))
+def test_gemm_act_grad_colsum_every_config(lib, cfg):
+    if cfg >= lib.gptk_gemm_num_configs():
+        pytest.skip("no such configuration")
+    say(f"gemm colsum cfg {cfg}")
+    assert lib.gptk_gemm_force_config(cfg, 1) == 0
+    try:
+        _gemm_colsum_case(lib, 1000, 392, 192, 1, cfg)
+    finally:
+        lib.gptk_gemm_force_config(-1, 0)
+
+
 # ---------------------------------------------------------------- attention
 
 ATT_CASES = [

@@ -29,9 +29,11 @@ GPT_DEV void epilogue_store(const Gemm& g, int m, int n, float acc) {
 
 // Eight consecutive outputs (m, n .. n+7) of one row, 16-byte aligned, all
 // inside the matrix; bias holds the eight column biases (or zeros). Every load
-// is issued before the first store.
+// is issued before the first store. yout (ACT_GRAD only) receives the fp32
+// values before storage rounding.
 template <typename TC, int EPI, int ACT>
-GPT_DEV void epilogue_chunk8(const Gemm& g, int m, int n, const float (&acc)[8], const float (&bias)[8]) {
+GPT_DEV void epilogue_chunk8(const Gemm& g, int m, int n, const float (&acc)[8], const float (&bias)[8],
+                             float* yout = nullptr) {
     const int64_t o = (int64_t)m * g.ldc + n;
     auto put = [&](void* base, const float (&x)[8]) {
         if constexpr (sizeof(TC) == 2) {
@@ -70,6 +72,10 @@ GPT_DEV void epilogue_chunk8(const Gemm& g, int m, int n, const float (&acc)[8],
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = acc[e] * (float)a[e];
         put(g.C, y);
+        if (yout) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) yout[e] = y[e];
+        }
     } else {   // EPI_ACCUM
         const float* c = (const float*)g.C + o;
         const float4 c0 = reinterpret_cast<const float4*>(c)[0], c1 = reinterpret_cast<const float4*>(c)[1];

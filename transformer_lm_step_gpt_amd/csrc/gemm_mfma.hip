@@ -417,6 +417,13 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
     const int cc = lane % CPR, ro = lane / CPR;
     const int col = n0 + wn + 8 * cc;
     const bool cin = col < g.N;              // N % 8 == 0: a chunk is wholly inside or outside
+    // column sums of the output (bias gradient), ACT_GRAD only: per lane over
+    // its rows, then across the lanes and waves of a column in LDS
+    constexpr bool CSUM = !SPLIT && EPI == EPI_ACT_GRAD;
+    static_assert(!CSUM || 4 * RPI * WN * 4 <= NS * STAGE * 2, "column-sum scratch fits in the stage ring");
+    float cs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cs[e] = 0.f;
     float bv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) bv[e] = 0.f;
@@ -448,11 +455,38 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
                     reinterpret_cast<f32x4*>(p)[1] = u1;
                 } else {
                     const float v[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
-                    epilogue_chunk8<TC, EPI, ACT>(g, row, col, v, bv);
+                    if constexpr (CSUM) {
+                        float y[8];
+                        epilogue_chunk8<TC, EPI, ACT>(g, row, col, v, bv, y);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) cs[e] += y[e];
+                    } else {
+                        epilogue_chunk8<TC, EPI, ACT>(g, row, col, v, bv);
+                    }
                 }
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    if constexpr (CSUM) {
+        if (g.cpart) {
+            // red[wave][row offset][column of the wave's sub-tile]
+            float* red = reinterpret_cast<float*>(smem_raw);
+            barrier_no_fence();   // every wave has finished reading its staging strips
+            if (64 % CPR == 0 || ro < RPI) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) red[(w * RPI + ro) * WN + 8 * cc + e] = cs[e];
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            barrier_no_fence();
+            for (int c = tid; c < BN; c += 256) {
+                const int half = c / WN, cl = c - half * WN;
+                float sum = 0.f;
+                for (int wv = half; wv < 4; wv += 2)
+                    for (int r = 0; r < RPI; ++r) sum += red[(wv * RPI + r) * WN + cl];
+                if (n0 + c < g.N) g.cpart[(int64_t)(m0 / BM) * g.N + n0 + c] = sum;
+            }
+        }
     }
 }
 
@@ -698,6 +732,7 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
     GemmPlan p{};
     p.cfg = bcfg;
     p.splits = bsplits;
+    p.bm = (bsplits == 1 && g.epi == EPI_ACT_GRAD) ? cfg_bm[bcfg] : 0;
     const bool relu = bsplits == 1 && (g.epi == EPI_BIAS_ACT || g.epi == EPI_ACT_GRAD) && g.act == ACT_RELU2;
     snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %s, %s, %s, %d, %d, %d, %s>", cfg_bm[bcfg],
              cfg_bn[bcfg], cfg_bk[bcfg], cfg_ns[bcfg], cfg_occ[bcfg], cfg_rs[bcfg] ? "true" : "false",

@@ -699,9 +699,16 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         float* mean2 = w.ln_mean + (size_t)(2 * l + 1) * M;
         float* rstd2 = w.ln_rstd + (size_t)(2 * l + 1) * M;
         // MLP branch
+        bool fc_b_fused = false;   // fc bias gradient from the dgrad epilogue's column sums
         {
             gk::Gemm g = mk_gemm(h, M, F, d, dR, d, true, Wop(h, li.mp_w), F, false, w.dh, F, bf, gk::EPI_ACT_GRAD);
             g.aux = w.hdact[l];
+            const gk::GemmPlan pl = gk::gemm_plan(g, w.splitk_floats);
+            if (pl.bm > 0) {
+                g.cpart = w.cs_part + (size_t)(n_cs++) * w.cs_part_stride;
+                h->jobs.push_back({g.cpart, G(h, li.fc_b), (M + pl.bm - 1) / pl.bm, F});
+                fc_b_fused = true;
+            }
             run_gemm(h, KC_GEMM_DGRAD, g);
             gk::Gemm g2 = mk_gemm(h, d, F, M, dR, d, false, w.hact[l], F, false, G(h, li.mp_w), F, false, gk::EPI_ACCUM);
             run_gemm(h, KC_GEMM_WGRAD, g2);
@@ -712,7 +719,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
             gk::Gemm g2 = mk_gemm(h, F, d, M, w.dh, F, false, w.ln2[l], d, false, G(h, li.fc_w), d, false, gk::EPI_ACCUM);
             run_gemm(h, KC_GEMM_WGRAD, g2);
         }
-        col_sum(w.dh, F, G(h, li.fc_b));
+        if (!fc_b_fused) col_sum(w.dh, F, G(h, li.fc_b));
         ln_bwd(w.x_mid[l], mean2, rstd2, P(h, li.ln2_w), false, G(h, li.ln2_w), G(h, li.ln2_b), G(h, li.proj_b));
         // attention branch
         {
@@ -1011,6 +1018,38 @@ gpt_status gptk_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda
     g.C2 = C2; g.bias = bias; g.resid = resid; g.aux = aux;
     g.epi = epi; g.act = act; g.in_bf = in_bf16;
     gk::gemm(g, splitk_scratch, (size_t)splitk_floats, (hipStream_t)stream);
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
+
+gpt_status gptk_gemm_colsum(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int32_t a_kc, const void* B,
+                            int64_t ldb, int32_t b_kc, void* C, int64_t ldc, int32_t in_bf16, int32_t c_bf16,
+                            int32_t epi, int32_t act, const float* bias, const float* resid, const void* aux, void* C2,
+                            float* colsum_out, float* partial, float* splitk_scratch, int64_t splitk_floats,
+                            void* stream) {
+    if (M < 1 || N < 1 || K < 1 || !A || !B || !C || !colsum_out || !partial || epi < 0 || epi > 5)
+        return GPT_ERR_INVALID_ARGUMENT;
+    if (epi == gk::EPI_ACCUM) return GPT_ERR_UNSUPPORTED;
+    gk::Gemm g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.a_kc = a_kc;
+    g.B = B; g.ldb = ldb; g.b_kc = b_kc;
+    g.C = C; g.ldc = ldc; g.c_bf = c_bf16;
+    g.C2 = C2; g.bias = bias; g.resid = resid; g.aux = aux;
+    g.epi = epi; g.act = act; g.in_bf = in_bf16;
+    hipStream_t s = (hipStream_t)stream;
+    const gk::GemmPlan p = gk::gemm_plan(g, (size_t)splitk_floats);
+    if (p.bm > 0) {
+        g.cpart = partial;
+        gk::gemm_main(g, p, splitk_scratch, s);
+        gk::gemm_finish(g, p, splitk_scratch, s);
+        const int np = (M + p.bm - 1) / p.bm;
+        gk::reduce_rows(partial, np, N, colsum_out, partial + (size_t)np * N, s);
+    } else {
+        gk::gemm_main(g, p, splitk_scratch, s);
+        gk::gemm_finish(g, p, splitk_scratch, s);
+        const bool out_bf = epi != gk::EPI_BIAS_RESID && c_bf16 != 0;   // the residual epilogue stores fp32
+        gk::colsum(out_bf, C, ldc, M, N, colsum_out, partial, s);
+    }
     return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
 }
 

@@ -77,6 +77,9 @@ struct RedJob {
     int np, n;
 };
 size_t reduce_jobs_tmp_floats(int njobs, int max_np, int max_n);
+// out[c] += sum over p < np of part[p * n + c] (one job, the same fixed order);
+// tmp holds ceil(np / 64) * n floats
+void reduce_rows(const float* part, int np, int n, float* out, float* tmp, hipStream_t s);
 void reduce_jobs(const RedJob* jobs, int njobs, int max_np, int max_n, float* tmp, hipStream_t s);
 
 // ---------------------------------------------------------------- cross-entropy
@@ -131,6 +134,10 @@ struct Gemm {
     int epi;
     int act;
     bool in_bf;                              // A and B storage (bf16 or fp32)
+    // ACT_GRAD epilogue, plans with bm > 0: cpart[(m / bm) * N + n] = sum over
+    // the rows m of one bm-row block of the fp32 output values (column sums
+    // for a bias gradient, reduced later)
+    float* cpart = nullptr;
 };
 // How a product runs: kernel (matrix-core tile configuration, or cfg = -1
 // for the portable kernel), split-K factor, and the name of the main kernel
@@ -138,6 +145,7 @@ struct Gemm {
 struct GemmPlan {
     int cfg = -1;
     int splits = 1;
+    int bm = 0;      // rows per block of fused column sums (0: the plan cannot produce them)
     char name[112] = {0};
 };
 // scratch: split-K partials for the matrix-core kernel (may be null: no split)

@@ -640,6 +640,10 @@ void reduce_jobs(const RedJob* jobs, int njobs, int max_np, int max_n, float* tm
     reduce_jobs_stage2<<<dim3(ceil_div(max_n, 256), njobs), 256, 0, s>>>(jobs, G, max_n, tmp);
 }
 
+void reduce_rows(const float* part, int np, int n, float* out, float* tmp, hipStream_t s) {
+    reduce_partials(part, np, n, 1, tmp, out, nullptr, nullptr, s);
+}
+
 template <typename TL>
 static void lnb_launch(int nv, int nb, const float* dy, const float* x, const float* mean, const float* rstd,
                        const float* g, float* dres, TL* lp, int ov, float* part, int M, int d, hipStream_t s) {

@@ -86,6 +86,21 @@ struct HTile {
     static constexpr int PER_WAVE = ATT_BT / RPD / 4;
     static constexpr int ELEMS = ATT_BT * HD;
     GPT_DEV static int swz(int r) { return CH == 8 ? ((r >> 1) & 7) : (r & 15); }
+    // element offset of this lane's chunk in the wave's p-th DMA, relative to the tile's first row
+    GPT_DEV static uint32_t lane_off(int p, int64_t ld, int w, int lane) {
+        const int d = w * PER_WAVE + p;
+        const int r = d * RPD + lane / CH;
+        const int c = (lane % CH) ^ swz(r);
+        return (uint32_t)((int64_t)r * ld + c * 8);
+    }
+    // a whole tile whose first row is at base, with the lane offsets of lane_off
+    GPT_DEV static void load_full(bf16* tile, const bf16* base, const uint32_t (&off)[PER_WAVE], int w) {
+#pragma unroll
+        for (int p = 0; p < PER_WAVE; ++p) {
+            const int d = w * PER_WAVE + p;
+            __builtin_amdgcn_global_load_lds(base + off[p], (lds_void_t*)(tile + d * 512), 16, 0, 0);
+        }
+    }
     // rows r0 .. r0+63 of a [T, *] head slice (row stride ld); rows >= T repeat row T-1
     GPT_DEV static void load(bf16* tile, const bf16* src, int64_t ld, int r0, int T, int w, int lane) {
 #pragma unroll
@@ -130,12 +145,29 @@ struct TileRing {
     int64_t ldx, ldy;
     int first, ntiles, T, w, lane;
     int issued = 0;
+    // per-lane element offsets inside a full tile, kept in registers for head dims
+    // <= 64 (the hd-128 kernels have no registers to spare and recompute them)
+    static constexpr bool KEEP = HD <= 64;
+    uint32_t offx[TL::PER_WAVE], offy[TL::PER_WAVE];
+    GPT_DEV void init() {
+#pragma unroll
+        for (int p = 0; p < TL::PER_WAVE; ++p) {
+            offx[p] = KEEP ? TL::lane_off(p, ldx, w, lane) : 0u;
+            offy[p] = KEEP ? TL::lane_off(p, ldy, w, lane) : 0u;
+        }
+    }
     GPT_DEV void issue_next() {
         if (issued < ntiles) {
             bf16* st = smem + (issued % ATT_NS) * STAGE;
             const int r0 = first + issued * ATT_BT;
-            TL::load(st, X, ldx, r0, T, w, lane);
-            TL::load(st + TL::ELEMS, Y, ldy, r0, T, w, lane);
+            if (KEEP && r0 + ATT_BT <= T) {
+                // whole tile inside the sequence: wave-uniform base plus the lane's offset
+                TL::load_full(st, X + (int64_t)r0 * ldx, offx, w);
+                TL::load_full(st + TL::ELEMS, Y + (int64_t)r0 * ldy, offy, w);
+            } else {
+                TL::load(st, X, ldx, r0, T, w, lane);
+                TL::load(st + TL::ELEMS, Y, ldy, r0, T, w, lane);
+            }
             ++issued;
         }
     }
@@ -174,6 +206,7 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
     TileRing<HD> ring{smem, (const bf16*)a.k + (int64_t)b * T * a.ldk + h * HD,
                       (const bf16*)a.v + (int64_t)b * T * a.ldv + h * HD, a.ldk, a.ldv, kbeg,
                       ceil_div(kend - kbeg, ATT_BT), T, w, lane};
+    ring.init();
     for (int s = 0; s < ATT_NS - 1; ++s) ring.issue_next();
 
     bf16x8 qf[NDS];
@@ -214,15 +247,22 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
                 tmax = fmaxf(tmax, s[kf][e]);
             }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mnew = fmaxf(mrow, tmax);
-        const float mc = mnew == -INFINITY ? 0.f : mnew * c;
-        const float corr = __builtin_amdgcn_exp2f(mrow * c - mc);
-        mrow = mnew;
-        lsum *= corr;
+        // The running max is raised only when a score exceeds it by more than
+        // 2^8 in exp2 units (and always from -inf): the output and the sum use
+        // the same reference, so the result is unchanged while p stays <= 256;
+        // the accumulators are rescaled only when some lane of the wave moves.
+        if (__builtin_amdgcn_ballot_w64((tmax * c > mrow * c + 8.f) | ((mrow == -INFINITY) & (tmax > -INFINITY)))) {
+            const float mnew = fmaxf(mrow, tmax);
+            const float mcn = mnew == -INFINITY ? 0.f : mnew * c;
+            const float corr = __builtin_amdgcn_exp2f(mrow * c - mcn);
+            mrow = mnew;
+            lsum *= corr;
 #pragma unroll
-        for (int df = 0; df < NDF; ++df)
+            for (int df = 0; df < NDF; ++df)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[df][e] *= corr;
+                for (int e = 0; e < 16; ++e) oacc[df][e] *= corr;
+        }
+        const float mc = mrow == -INFINITY ? 0.f : mrow * c;
         bf16x8 pk[4];
 #pragma unroll
         for (int kf = 0; kf < 2; ++kf)
@@ -276,6 +316,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(Attn a) {
     TileRing<HD> ring{smem, (const bf16*)a.q + (int64_t)b * T * a.ldq + h * HD,
                       (const bf16*)a.dO + (int64_t)b * T * a.lddo + h * HD, a.ldq, a.lddo, qbeg,
                       ceil_div(qend - qbeg, ATT_BT), T, w, lane};
+    ring.init();
     for (int s = 0; s < ATT_NS - 1; ++s) ring.issue_next();
 
     // log-sum-exp (log2 units) and D = rowsum(dO o O) of every query this workgroup visits
@@ -382,6 +423,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
     TileRing<HD> ring{smem, (const bf16*)a.k + (int64_t)b * T * a.ldk + h * HD,
                       (const bf16*)a.v + (int64_t)b * T * a.ldv + h * HD, a.ldk, a.ldv, kbeg,
                       ceil_div(kend - kbeg, ATT_BT), T, w, lane};
+    ring.init();
     for (int s = 0; s < ATT_NS - 1; ++s) ring.issue_next();
 
     bf16x8 qf[NDS], gf[NDS];

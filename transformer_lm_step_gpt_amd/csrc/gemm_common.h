@@ -28,12 +28,39 @@ GPT_DEV void epilogue_store(const Gemm& g, int m, int n, float acc) {
 }
 
 // Eight consecutive outputs (m, n .. n+7) of one row, 16-byte aligned, all
-// inside the matrix; bias holds the eight column biases (or zeros). Every load
-// is issued before the first store. yout (ACT_GRAD only) receives the fp32
+// inside the matrix, in two parts so that a caller can issue the loads of
+// several chunks before their stores: epi_load reads what the epilogue needs
+// besides the accumulators (the residual, the activation derivative or the
+// previous gradient), epi_store applies the operation and stores. bias holds
+// the eight column biases (or zeros); yout (ACT_GRAD only) receives the fp32
 // values before storage rounding.
+struct EpiIn {
+    float4 a, b;      // fp32 residual / previous gradient
+    bf16x8 h;         // bf16 derivative of the activation
+};
+
+template <typename TC, int EPI>
+GPT_DEV EpiIn epi_load(const Gemm& g, int m, int n) {
+    const int64_t o = (int64_t)m * g.ldc + n;
+    EpiIn in;
+    if constexpr (EPI == EPI_BIAS_RESID) {
+        const float* r = g.resid + o;
+        in.a = reinterpret_cast<const float4*>(r)[0];
+        in.b = reinterpret_cast<const float4*>(r)[1];
+    } else if constexpr (EPI == EPI_ACCUM) {
+        const float* c = (const float*)g.C + o;
+        in.a = reinterpret_cast<const float4*>(c)[0];
+        in.b = reinterpret_cast<const float4*>(c)[1];
+    } else if constexpr (EPI == EPI_ACT_GRAD) {
+        static_assert(sizeof(TC) == 2, "the matrix-core ACT_GRAD epilogue stores bf16");
+        in.h = *reinterpret_cast<const bf16x8*>((const TC*)g.aux + o);
+    }
+    return in;
+}
+
 template <typename TC, int EPI, int ACT>
-GPT_DEV void epilogue_chunk8(const Gemm& g, int m, int n, const float (&acc)[8], const float (&bias)[8],
-                             float* yout = nullptr) {
+GPT_DEV void epi_store(const Gemm& g, int m, int n, const float (&acc)[8], const float (&bias)[8], const EpiIn& in,
+                       float* yout = nullptr) {
     const int64_t o = (int64_t)m * g.ldc + n;
     auto put = [&](void* base, const float (&x)[8]) {
         if constexpr (sizeof(TC) == 2) {
@@ -60,30 +87,27 @@ GPT_DEV void epilogue_chunk8(const Gemm& g, int m, int n, const float (&acc)[8],
         for (int e = 0; e < 8; ++e) act_and_grad<ACT>(acc[e] + bias[e], h[e], y[e]);
         put(g.C, y);
         put(g.C2, h);
-    } else if constexpr (EPI == EPI_BIAS_RESID) {
-        const float* r = g.resid + o;
-        const float4 r0 = reinterpret_cast<const float4*>(r)[0], r1 = reinterpret_cast<const float4*>(r)[1];
-        const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    } else if constexpr (EPI == EPI_BIAS_RESID || EPI == EPI_ACCUM) {
+        const float rv[8] = {in.a.x, in.a.y, in.a.z, in.a.w, in.b.x, in.b.y, in.b.z, in.b.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = rv[e] + (acc[e] + bias[e]);
+        for (int e = 0; e < 8; ++e) y[e] = rv[e] + (EPI == EPI_BIAS_RESID ? acc[e] + bias[e] : acc[e]);
         put(g.C, y);
-    } else if constexpr (EPI == EPI_ACT_GRAD) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>((const TC*)g.aux + o);
+    } else {   // EPI_ACT_GRAD
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = acc[e] * (float)a[e];
+        for (int e = 0; e < 8; ++e) y[e] = acc[e] * (float)in.h[e];
         put(g.C, y);
         if (yout) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) yout[e] = y[e];
         }
-    } else {   // EPI_ACCUM
-        const float* c = (const float*)g.C + o;
-        const float4 c0 = reinterpret_cast<const float4*>(c)[0], c1 = reinterpret_cast<const float4*>(c)[1];
-        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = cv[e] + acc[e];
-        put(g.C, y);
     }
+}
+
+template <typename TC, int EPI, int ACT>
+GPT_DEV void epilogue_chunk8(const Gemm& g, int m, int n, const float (&acc)[8], const float (&bias)[8],
+                             float* yout = nullptr) {
+    const EpiIn in = epi_load<TC, EPI>(g, m, n);
+    epi_store<TC, EPI, ACT>(g, m, n, acc, bias, in, yout);
 }
 
 void gemm_simple(const Gemm& g, hipStream_t s);

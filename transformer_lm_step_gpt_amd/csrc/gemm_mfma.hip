@@ -435,8 +435,22 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
             bv[4] = b1.x; bv[5] = b1.y; bv[6] = b1.z; bv[7] = b1.w;
         }
     }
+    // epilogues that read global memory (residual, activation derivative,
+    // previous gradient) issue a strip's loads before staging it, so their
+    // latency overlaps the staging instead of stalling every pass
+    constexpr bool PRE = !SPLIT && (EPI == EPI_BIAS_RESID || EPI == EPI_ACT_GRAD || EPI == EPI_ACCUM);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+        EpiIn pre[PRE ? NIT : 1];
+        if constexpr (PRE) {
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int r = it * RPI + ro;
+                const int row = m0 + wm + 32 * i + r;
+                const bool act = (32 % RPI == 0 || r < 32) && (64 % CPR == 0 || ro < RPI);
+                if (act && row < g.M && cin) pre[it] = epi_load<TC, EPI>(g, row, col);
+            }
+        }
 #pragma unroll
         for (int jf = 0; jf < FN; ++jf)
 #pragma unroll
@@ -455,13 +469,14 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
                     reinterpret_cast<f32x4*>(p)[1] = u1;
                 } else {
                     const float v[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                    const EpiIn in = PRE ? pre[PRE ? it : 0] : EpiIn{};
                     if constexpr (CSUM) {
                         float y[8];
-                        epilogue_chunk8<TC, EPI, ACT>(g, row, col, v, bv, y);
+                        epi_store<TC, EPI, ACT>(g, row, col, v, bv, in, y);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) cs[e] += y[e];
                     } else {
-                        epilogue_chunk8<TC, EPI, ACT>(g, row, col, v, bv);
+                        epi_store<TC, EPI, ACT>(g, row, col, v, bv, in);
                     }
                 }
             }

@@ -235,17 +235,20 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
             for (int ds = 0; ds < NDS; ++ds) s[kf] = mfma(TL::rowfrag(Ks, kf * 32 + lr, ds, hh), qf[ds], s[kf]);
         }
         const bool need_mask = (kt + ATT_BT - 1 > qw) || (kt + ATT_BT > T) || (W > 0 && qw + 31 - kt >= W);
+        if (need_mask) {
+#pragma unroll
+            for (int kf = 0; kf < 2; ++kf)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = kt + kf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+                    s[kf][e] = visible(myq, key, T, W) ? s[kf][e] : -INFINITY;
+                }
+        }
         float tmax = -INFINITY;
 #pragma unroll
         for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                if (need_mask) {
-                    const int key = kt + kf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-                    s[kf][e] = visible(myq, key, T, W) ? s[kf][e] : -INFINITY;
-                }
-                tmax = fmaxf(tmax, s[kf][e]);
-            }
+            for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, s[kf][e]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         // The running max is raised only when a score exceeds it by more than
         // 2^8 in exp2 units (and always from -inf): the output and the sum use

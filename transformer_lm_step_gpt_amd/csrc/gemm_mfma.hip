@@ -110,14 +110,16 @@ struct ColTile {
     static constexpr int BYTES = R * BK * 2;
     static constexpr int READS_PER_FRAG = 2;
     static_assert(CH >= 16 && CH % 8 == 0 && (BK * CH) % 256 == 0, "unsupported tile");
-    // chunk c of k-row k sits at slot lds_slot(k, c): an XOR of (k & 3) << 2 for
-    // power-of-two rows, a rotation by 4 (k & 3) otherwise; either way the 4
-    // k-rows a transposing read touches fall in different banks
+    // chunk c of k-row k sits at slot lds_slot(k, c), so that the 4 k-rows x 4
+    // chunks a half-wave's transposing read touches fall in 16 different
+    // 16-byte bank groups (64 banks): for power-of-two rows (k-rows start at the
+    // same bank) an XOR of the chunk's quad with k & 3; for rows of 8 mod 16
+    // chunks (odd and even k-rows already half a bank cycle apart) an XOR of
+    // the quad with bit 1 of k (an involution, so the same map both ways)
     static constexpr bool POW2 = (CH & (CH - 1)) == 0;
-    GPT_DEV static int lds_slot(int k, int c) { return POW2 ? (c ^ ((k & 3) << 2)) : (c + 4 * (k & 3)) % CH; }
-    GPT_DEV static int glob_chunk(int k, int slot) {
-        return POW2 ? (slot ^ ((k & 3) << 2)) : (slot + CH - 4 * (k & 3)) % CH;
-    }
+    static_assert(POW2 || CH % 16 == 8, "unsupported row width");
+    GPT_DEV static int lds_slot(int k, int c) { return POW2 ? (c ^ ((k & 3) << 2)) : (c ^ ((k & 2) << 1)); }
+    GPT_DEV static int glob_chunk(int k, int slot) { return lds_slot(k, slot); }
     GPT_DEV static void src_init(const bf16* (&src)[PER_WAVE], const bf16* base, int64_t ld, int row0, int rows, int k0,
                                  int w, int lane) {
 #pragma unroll

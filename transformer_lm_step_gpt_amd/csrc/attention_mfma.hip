@@ -85,7 +85,19 @@ struct HTile {
     static constexpr int RPD = 64 / CH;             // rows per wave-wide 1 KiB DMA
     static constexpr int PER_WAVE = ATT_BT / RPD / 4;
     static constexpr int ELEMS = ATT_BT * HD;
-    GPT_DEV static int swz(int r) { return CH == 8 ? ((r >> 1) & 7) : (r & 15); }
+    // chunk swizzle by row: 16 consecutive rows read at one chunk (row
+    // fragments) and 4 consecutive rows x 4 chunks (transposing reads) both
+    // fall in distinct 16-byte bank groups. 8 chunks per row (two rows per
+    // 64-bank cycle): the row pair's index with its low bit moved to the top;
+    // 16 chunks: the row's two low 2-bit fields swapped.
+    GPT_DEV static int swz(int r) {
+        if constexpr (CH == 8) {
+            const int x = (r >> 1) & 7;
+            return ((x & 1) << 2) | (x >> 1);
+        } else {
+            return ((r & 3) << 2) | ((r >> 2) & 3);
+        }
+    }
     // element offset of this lane's chunk in the wave's p-th DMA, relative to the tile's first row
     GPT_DEV static uint32_t lane_off(int p, int64_t ld, int w, int lane) {
         const int d = w * PER_WAVE + p;

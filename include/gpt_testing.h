@@ -64,6 +64,19 @@ gpt_status gptk_attention(int32_t backward, int32_t B, int32_t T, int32_t H, int
                           void* o, int64_t ldo, float* lse, const void* dO, int64_t lddo, float* D, void* dq, void* dk,
                           void* dv, int64_t ldd, int32_t bf16, void* stream);
 
+/* Attention backward into one [B*T, 3*H*hd] buffer dqkv (dq, dk, dv column
+ * blocks, row stride 3*H*hd) plus the qkv bias gradient: colsum_out[c] += sum
+ * over rows of dqkv[:, c]. On the matrix-core path the sums are fused into the
+ * backward kernels (fp32 values before storage rounding, per 128-row block of a
+ * sequence, reduced in a fixed order); otherwise a column-sum pass reads dqkv.
+ * partial holds gptk_attention_colsum_partial_floats(B, T, H, hd) floats; the
+ * other arguments are those of gptk_attention's backward. */
+gpt_status gptk_attention_bwd_colsum(int32_t B, int32_t T, int32_t H, int32_t hd, int32_t window, const void* q,
+                                     const void* k, const void* v, int64_t ldq, int64_t ldk, int64_t ldv, const void* o,
+                                     int64_t ldo, const float* lse, const void* dO, int64_t lddo, float* D, void* dqkv,
+                                     int32_t bf16, float* colsum_out, float* partial, void* stream);
+int64_t gptk_attention_colsum_partial_floats(int32_t B, int32_t T, int32_t H, int32_t hd);
+
 /* LayerNorm over rows of width d with biased variance. Forward: y (act),
  * mean, rstd. Backward: dres = (overwrite ? 0 : dres) + dx, optional bf16
  * copy dres_lp, dg += sum dy xhat, db += sum dy, and (dcol nullable) dcol +=

@@ -287,10 +287,11 @@ bool attention_bwd_mfma(const Attn& a, hipStream_t s);
 void attention_fwd(const Attn& a, hipStream_t s) {
     if (!attention_fwd_mfma(a, s)) attention_fwd_simple(a, s);
 }
-void attention_bwd(const Attn& a, hipStream_t s) {
-    if (attention_bwd_mfma(a, s)) return;
+bool attention_bwd(const Attn& a, hipStream_t s) {
+    if (attention_bwd_mfma(a, s)) return true;
     attn_rowdot(a.bf, a.dO, a.o, a.Dout, a.B, a.T, a.H, a.hd, s);
     attention_bwd_simple(a, s);
+    return false;
 }
 
 }  // namespace gk

@@ -194,6 +194,31 @@ struct TileRing {
     GPT_DEV const bf16* y(int u) const { return smem + (u % ATT_NS) * STAGE + TL::ELEMS; }
 };
 
+// Column sums over the 128 rows of a workgroup (4 waves x 32 lanes) of one
+// accumulator set f32x16[NDF] (rows 8*(e/4) + 4*(lane/32) + e%4 of 32-row blocks
+// are head dims, lanes are the workgroup's queries or keys), scaled by `scale`,
+// lanes with ok = false counting as zero. Summed in LDS in a fixed order (waves,
+// then lanes) and written to out[0 .. HD). red: 4 * NDF * 16 * 64 floats of LDS
+// that no wave reads or writes any more; every thread of the workgroup calls it.
+template <int HD, int NDF>
+GPT_DEV void block_colsum(const f32x16 (&acc)[NDF], float scale, bool ok, float* red, float* out, int w, int lane) {
+    constexpr int NV = NDF * 16;
+    barrier_no_fence();
+#pragma unroll
+    for (int v = 0; v < NV; ++v) red[(w * NV + v) * 64 + lane] = ok ? acc[v / 16][v % 16] * scale : 0.f;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier_no_fence();
+    const int d = threadIdx.x;
+    if (d < HD) {
+        const int df = d >> 5, r = d & 31, half = (r >> 2) & 1, e = ((r >> 3) << 2) | (r & 3);
+        const int v = df * 16 + e;
+        float sum = 0.f;
+        for (int ww = 0; ww < 4; ++ww)
+            for (int lr = 0; lr < 32; ++lr) sum += red[(ww * NV + v) * 64 + 32 * half + lr];
+        out[d] = sum;
+    }
+}
+
 }  // namespace
 
 // ============================================================== forward
@@ -315,6 +340,7 @@ template <int HD>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(Attn a) {
     constexpr int NDS = HD / 16, NDF = HD / 32;
     using TL = HTile<HD>;
+    static_assert(2 * ATT_NS * TileRing<HD>::STAGE >= 4 * NDF * 16 * 64 * 4, "column-sum scratch fits in the ring");
     __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
     __shared__ __attribute__((aligned(16))) float Lrow[ATT_MAX_T], Drow[ATT_MAX_T];
     const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
@@ -413,6 +439,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(Attn a) {
                 *reinterpret_cast<bf16x4*>(DV + df * 32 + 8 * g4 + 4 * hh) = vv;
             }
     }
+    if (a.cpart) {   // bias-gradient column sums of this block's dK and dV (values before rounding)
+        float* row = a.cpart + (int64_t)(b * gridDim.x + blockIdx.x) * (3 * a.H * HD);
+        float* red = reinterpret_cast<float*>(smem);
+        block_colsum<HD, NDF>(dk, 1.0f / sqrtf((float)HD), mykey < T, red, row + a.H * HD + h * HD, w, lane);
+        block_colsum<HD, NDF>(dv, 1.0f, mykey < T, red, row + 2 * a.H * HD + h * HD, w, lane);
+    }
 }
 
 // ============================================================== backward: dQ
@@ -421,6 +453,7 @@ template <int HD>
 __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
     constexpr int NDS = HD / 16, NDF = HD / 32;
     using TL = HTile<HD>;
+    static_assert(2 * ATT_NS * TileRing<HD>::STAGE >= 4 * NDF * 16 * 64 * 4, "column-sum scratch fits in the ring");
     __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
     const int qtile = gridDim.x - 1 - blockIdx.x;
     const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
@@ -511,6 +544,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
                 for (int i = 0; i < 4; ++i) v[i] = (bf16)(dq[df][4 * g4 + i] * isd);
                 *reinterpret_cast<bf16x4*>(DQ + df * 32 + 8 * g4 + 4 * hh) = v;
             }
+    }
+    if (a.cpart) {   // bias-gradient column sums of this block's dQ (values before rounding)
+        float* row = a.cpart + (int64_t)(b * gridDim.x + qtile) * (3 * a.H * HD);
+        block_colsum<HD, NDF>(dq, 1.0f / sqrtf((float)HD), myq < T, reinterpret_cast<float*>(smem), row + h * HD, w,
+                              lane);
     }
 }
 

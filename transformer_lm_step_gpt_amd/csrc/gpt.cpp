@@ -191,12 +191,16 @@ Ws plan(const gpt_config& c, const Table& tb, void* base) {
     {
         const int64_t maxN = std::max<int64_t>(3 * d, F);
         const int nbl = gk::layernorm_bwd_num_partials((int)M), npc = gk::colsum_num_partials((int)M);
+        // bias column sums come from colsum_rows (npc rows) or from the
+        // attention backward (one row per 128-row block of each sequence)
+        const int npa = c.max_batch * ((c.block_size + 127) / 128);
         w.ln_part_stride = (size_t)3 * nbl * d;
-        w.cs_part_stride = (size_t)npc * maxN;
+        w.cs_part_stride = (size_t)std::max(npc, npa) * maxN;
         w.ln_part = cv.arr<float>((size_t)(2 * L + 1) * w.ln_part_stride);
         w.cs_part = cv.arr<float>((size_t)(2 * L) * w.cs_part_stride);
         w.red_max_jobs = (int)((2 * L + 1) * 3 + 2 * L);
-        w.red_tmp = cv.arr<float>(gk::reduce_jobs_tmp_floats(w.red_max_jobs, std::max(nbl, npc), (int)std::max(d, maxN)));
+        w.red_tmp = cv.arr<float>(
+            gk::reduce_jobs_tmp_floats(w.red_max_jobs, std::max({nbl, npc, npa}), (int)std::max(d, maxN)));
         w.red_jobs = (gk::RedJob*)cv.take(sizeof(gk::RedJob) * w.red_max_jobs);
     }
     w.gn_partial = cv.arr<double>(1024);
@@ -675,6 +679,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
     // sums in per-call slots; one reduce_jobs at the end of the pass sums them
     h->jobs.clear();
     const int nbl = gk::layernorm_bwd_num_partials(M), npc = gk::colsum_num_partials(M);
+    const int npa = B * ((T + 127) / 128);   // row blocks of the attention backward's column sums
     int n_ln = 0, n_cs = 0;
     auto ln_bwd = [&](const float* x, const float* mean, const float* rstd, const float* g, bool overwrite, float* dg,
                       float* db, float* dcol) {
@@ -742,11 +747,17 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         a.o = w.att[l]; a.ldo = d; a.lse = w.lse[l]; a.bf = bf;
         a.dO = w.dO; a.lddo = d; a.D = w.attD; a.Dout = w.attD;
         a.dq = w.dqkv; a.dk = (char*)w.dqkv + (size_t)ab * d; a.dv = (char*)w.dqkv + (size_t)ab * 2 * d; a.ldd = 3 * d;
+        // qkv bias gradient: column sums of dqkv, from the attention backward itself
+        // unless the q/k transform still changes dq and dk afterwards
+        float* qkv_part = w.cs_part + (size_t)(n_cs++) * w.cs_part_stride;
+        bool attn_b_fused = false;
+        if (!qkt) a.cpart = qkv_part;
         {
             double pairs = attn_pairs(B, T, H, a.window);
             Timed t(h, KC_ATTN_BWD, 8.0 * hd * pairs, (double)M * d * 8 * ab + 8.0 * M * H);
-            gk::attention_bwd(a, st);
+            attn_b_fused = gk::attention_bwd(a, st) && a.cpart;
         }
+        if (attn_b_fused) h->jobs.push_back({qkv_part, G(h, li.attn_b), npa, 3 * d});
         if (qkt) {
             Timed t(h, KC_QK_PREP, 0, (double)M * 2 * d * 3 * ab);
             gk::qk_prep_bwd(bf, w.qkv[l], w.dqkv, w.rope_cos, w.rope_sin, M, T, H, hd, c.qk_rmsnorm,
@@ -760,7 +771,11 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
                                   gk::EPI_ACCUM);
             run_gemm(h, KC_GEMM_WGRAD, g2);
         }
-        col_sum(w.dqkv, 3 * d, G(h, li.attn_b));
+        if (!attn_b_fused) {
+            Timed t(h, KC_COLSUM, 0, (double)ab * M * 3 * d + 4.0 * npc * 3 * d);
+            gk::colsum_rows(bf, w.dqkv, 3 * d, M, 3 * d, qkv_part, st);
+            h->jobs.push_back({qkv_part, G(h, li.attn_b), npc, 3 * d});
+        }
         ln_bwd(w.x_in[l], mean1, rstd1, P(h, li.ln1_w), false, G(h, li.ln1_w), G(h, li.ln1_b),
                l > 0 ? G(h, tb.layers[l - 1].mp_b) : nullptr);
     }
@@ -783,8 +798,8 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         double bytes = 0;
         for (const gk::RedJob& j : h->jobs) bytes += 4.0 * j.np * j.n + 8.0 * j.n;
         Timed t(h, KC_PARTIAL_REDUCE, 0, bytes);
-        gk::reduce_jobs(w.red_jobs, (int)h->jobs.size(), std::max(nbl, npc), (int)std::max<int64_t>(d, std::max<int64_t>(3 * d, F)),
-                        w.red_tmp, st);
+        gk::reduce_jobs(w.red_jobs, (int)h->jobs.size(), std::max({nbl, npc, npa}),
+                        (int)std::max<int64_t>(d, std::max<int64_t>(3 * d, F)), w.red_tmp, st);
     }
     {
         Timed t(h, KC_EMBED_BWD, 0, 4.0 * M * d + 8.0 * M * d);
@@ -1068,6 +1083,38 @@ gpt_status gptk_attention(int32_t backward, int32_t B, int32_t T, int32_t H, int
         gk::attention_bwd(a, s);
     } else {
         gk::attention_fwd(a, s);
+    }
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
+
+int64_t gptk_attention_colsum_partial_floats(int32_t B, int32_t T, int32_t H, int32_t hd) {
+    if (B < 1 || T < 1 || H < 1 || hd < 1) return 0;
+    const int64_t n = 3LL * H * hd;
+    const int64_t npa = (int64_t)B * ((T + 127) / 128);
+    const int64_t fused = npa * n + (npa + 63) / 64 * n;
+    return std::max<int64_t>(fused, gptk_colsum_partial_floats(B * T, (int32_t)n));
+}
+
+gpt_status gptk_attention_bwd_colsum(int32_t B, int32_t T, int32_t H, int32_t hd, int32_t window, const void* q,
+                                     const void* k, const void* v, int64_t ldq, int64_t ldk, int64_t ldv, const void* o,
+                                     int64_t ldo, const float* lse, const void* dO, int64_t lddo, float* D, void* dqkv,
+                                     int32_t bf16, float* colsum_out, float* partial, void* stream) {
+    if (B < 1 || T < 1 || H < 1 || (hd != 16 && hd != 32 && hd != 64 && hd != 128) || !dqkv || !colsum_out || !partial)
+        return GPT_ERR_INVALID_ARGUMENT;
+    const int64_t d = (int64_t)H * hd;
+    const size_t es = bf16 ? 2 : 4;
+    gk::Attn a{};
+    a.B = B; a.T = T; a.H = H; a.hd = hd; a.window = window;
+    a.q = q; a.k = k; a.v = v; a.ldq = ldq; a.ldk = ldk; a.ldv = ldv;
+    a.o = (void*)o; a.ldo = ldo; a.lse = (float*)lse; a.dO = dO; a.lddo = lddo; a.D = D; a.Dout = D;
+    a.dq = dqkv; a.dk = (char*)dqkv + es * d; a.dv = (char*)dqkv + es * 2 * d; a.ldd = 3 * d; a.bf = bf16;
+    a.cpart = partial;
+    hipStream_t s = (hipStream_t)stream;
+    if (gk::attention_bwd(a, s)) {
+        const int npa = B * ((T + 127) / 128);
+        gk::reduce_rows(partial, npa, (int)(3 * d), colsum_out, partial + (size_t)npa * 3 * d, s);
+    } else {
+        gk::colsum(bf16 != 0, dqkv, 3 * d, B * T, (int)(3 * d), colsum_out, partial, s);
     }
     return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
 }

@@ -169,10 +169,15 @@ struct Attn {
     float* Dout;                      // where the matrix-core backward computes it (same buffer)
     void* dq; void* dk; void* dv; int64_t ldd;
     bool bf;
+    // backward, matrix-core path: when set, the fp32 column sums (values before
+    // rounding) of dq, dk, dv over each 128-row block of a sequence, row
+    // b * ceil(T / 128) + block, columns [dq heads | dk heads | dv heads] (3 H hd)
+    float* cpart = nullptr;
 };
 void attention_fwd(const Attn& a, hipStream_t s);
 // backward: computes D itself (into Dout) when the matrix-core kernels run;
 // the portable kernels need D precomputed (attn_rowdot)
-void attention_bwd(const Attn& a, hipStream_t s);
+// returns true when the matrix-core kernels ran (and wrote a.cpart if set)
+bool attention_bwd(const Attn& a, hipStream_t s);
 
 }  // namespace gk

@@ -105,6 +105,10 @@ _SIGS = [
     ("gptk_attention", c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                  c_int64, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
+    ("gptk_attention_bwd_colsum", c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                            c_int64, c_int64, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
+                                            c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
+    ("gptk_attention_colsum_partial_floats", c_int64, [c_int32, c_int32, c_int32, c_int32]),
     ("gptk_layernorm", c_int32, [c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_int32, c_void_p]),

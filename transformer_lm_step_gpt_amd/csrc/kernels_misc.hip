@@ -368,8 +368,8 @@ constexpr int LN_MAXV = 8;   // float4 chunks per lane: d <= 64 * 4 * 8
 
 constexpr int LNF_ROWS = 4;   // rows per wavefront in the forward pass
 
-// One wavefront per LNF_ROWS consecutive rows; the next row's loads are issued
-// before the current row's reductions (software pipeline).
+// One wavefront per LNF_ROWS consecutive rows, all of them loaded before the
+// first row's reductions.
 template <typename TO, int NV>
 __global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* __restrict__ x, const float* __restrict__ g,
                                                             const float* __restrict__ b, TO* __restrict__ y,
@@ -378,18 +378,23 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* __restr
     const int lane = threadIdx.x & 63;
     const int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * LNF_ROWS, r1 = min(M, r0 + LNF_ROWS);
     const int nv = d >> 2;
-    float4 cur[NV], nxt[NV];
-    auto load_row = [&](int r, float4 (&v)[NV]) {
-        const float* xr = x + (int64_t)r * d;
+    // every row of the wave is loaded before the first is reduced: one memory
+    // latency per wave instead of one per row
+    float4 rows[LNF_ROWS][NV];
+#pragma unroll
+    for (int k = 0; k < LNF_ROWS; ++k) {
+        const float* xr = x + (int64_t)(r0 + k) * d;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int c = lane + 64 * i;
-            v[i] = c < nv ? load4(xr + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+            rows[k][i] = (r0 + k < r1 && c < nv) ? load4(xr + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-    };
-    if (r0 < r1) load_row(r0, cur);
-    for (int row = r0; row < r1; ++row) {
-        if (row + 1 < r1) load_row(row + 1, nxt);
+    }
+#pragma unroll
+    for (int k = 0; k < LNF_ROWS; ++k) {
+        const int row = r0 + k;
+        if (row >= r1) break;
+        const float4 (&cur)[NV] = rows[k];
         float s = 0.f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) s += (cur[i].x + cur[i].y) + (cur[i].z + cur[i].w);
@@ -420,8 +425,6 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* __restr
             }
         }
         if (lane == 0) { mean[row] = mu; rstd[row] = rs; }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) cur[i] = nxt[i];
     }
 }
 
@@ -872,11 +875,22 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
 #pragma unroll
                 for (int e = 0; e < 8; ++e) sm += __builtin_amdgcn_exp2f(fmaf(capped(raw(c, e)), L2E, -gm));
     } else {
+        // without the cap each chunk's exponentials replace its logits (bf16,
+        // in the same registers), so the gradient pass needs one multiply per
+        // element instead of a second exponential
 #pragma unroll
         for (int c = 0; c < CPT; ++c)
-            if (tid + 256 * c < nch)
+            if (tid + 256 * c < nch) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sm += __builtin_amdgcn_exp2f(fmaf(raw(c, e), L2E, -gm));
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(raw(c, 2 * e2), L2E, -gm));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(raw(c, 2 * e2 + 1), L2E, -gm));
+                    sm += p0 + p1;
+                    const bf16 lo = (bf16)p0, hi = (bf16)p1;
+                    v[c][e2] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                }
+            }
     }
     sm = wave_sum(sm);
     if (lane == 0) sred[4 + w] = sm;
@@ -885,11 +899,22 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
     // pass 3: gradient softmax * gscale (times 1 - tanh^2 under the cap), written
     // over the row; the target's -gscale is applied by thread 0 afterwards
     const float gs = valid ? gscale : 0.f;
+    // exp2(x log2e - gm) -> softmax * gscale
+    const float rescale = __builtin_amdgcn_exp2f(gm - lse2) * gs;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         const int idx = tid + 256 * c;
         if (idx >= nch) continue;
         ce_u32x4 o;
+        if (!(cap > 0.f)) {
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const bf16 lo = (bf16)(bf_lo(v[c][e2]) * rescale), hi = (bf16)(bf_hi(v[c][e2]) * rescale);
+                o[e2] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            }
+            *reinterpret_cast<ce_u32x4*>(zr + 8 * idx) = o;
+            continue;
+        }
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
             float gpair[2];

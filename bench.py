@@ -234,6 +234,20 @@ def main():
     roof["traffic"] = round(traffic) if traffic is not None else None
     roof.update({"kernel": dom, "avg_launch_ms": round(avg_ms, 4), "launches": timed["launches"],
                  "algorithmic_per_launch": per_launch})
+    # In the timed steps the weight-gradient products share the GPU with the
+    # input-gradient chain (side stream), so their live launch durations
+    # include that sharing; the untimed step above runs every launch alone.
+    iso = next(r for r in names if r["name"] == dom)
+    if iso["launches"] and iso["ms"] > 0:
+        iso_ms = iso["ms"] / iso["launches"]
+        if iso["flops"] > 0:
+            iso_ach = iso["flops"] / iso["launches"] / (iso_ms * 1e-3) / 1e12
+            iso_frac = iso_ach / PEAK_BF16_TFLOPS
+        else:
+            iso_ach = iso["bytes"] / iso["launches"] / (iso_ms * 1e-3) / 1e9
+            iso_frac = iso_ach / PEAK_HBM_GBS
+        roof["alone"] = {"avg_launch_ms": round(iso_ms, 4), "achieved": round(iso_ach, 2), "frac": round(iso_frac, 4),
+                         "launches": iso["launches"]}
     if a.kernel_table:
         tot = sum(r["ms"] for r in table)
         print(f"step (untimed, all launches timed): {tot:.3f} ms", file=sys.stderr)

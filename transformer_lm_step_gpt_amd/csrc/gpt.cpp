@@ -130,6 +130,9 @@ struct Ws {
     void* emb_scratch = nullptr;
     float* splitk = nullptr;
     size_t splitk_floats = 0;
+    // split-K slices of the weight-gradient products that run on the side stream
+    float* splitk_side = nullptr;
+    size_t splitk_side_floats = 0;
     float *rope_cos = nullptr, *rope_sin = nullptr;
     int32_t* err = nullptr;
     float *loss_last = nullptr, *loss_sum = nullptr, *gnorm = nullptr, *coef = nullptr;
@@ -209,6 +212,8 @@ Ws plan(const gpt_config& c, const Table& tb, void* base) {
     // gradients, the N = d products over M rows, and the tied head's gradient
     w.splitk_floats = bf ? (size_t)std::max<int64_t>({8 * std::max<int64_t>(3 * d * d, F * d), 4 * M * d, 2 * Vp * d}) : 0;
     w.splitk = cv.arr<float>(w.splitk_floats);
+    w.splitk_side_floats = bf ? (size_t)(8 * std::max<int64_t>(3 * d * d, F * d)) : 0;
+    w.splitk_side = cv.arr<float>(w.splitk_side_floats);
     if (c.pos_encoding == GPT_POS_ROPE) {
         int64_t half = (d / H) / 2;
         w.rope_cos = cv.arr<float>(c.block_size * half);
@@ -289,6 +294,9 @@ struct gpt_handle {
     // which depends on the tokens only and overlaps the forward pass
     hipStream_t side = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    // dependencies between the backward pass's main stream and the weight-
+    // gradient products it runs on the side stream
+    hipEvent_t ev_dep[8] = {};
 };
 
 namespace {
@@ -324,18 +332,21 @@ struct Timed {
     int cls;
     const char* name;
     double flops, bytes;
+    hipStream_t s;     // the stream the bracketed launch goes to
     hipEvent_t a = nullptr;
-    Timed(gpt_handle* h_, int cls_, double flops_, double bytes_, const char* name_ = nullptr)
-        : h(h_), cls(cls_), name(name_ ? name_ : kc_names[cls_]), flops(flops_), bytes(bytes_) {
+    Timed(gpt_handle* h_, int cls_, double flops_, double bytes_, const char* name_ = nullptr,
+          hipStream_t s_ = nullptr)
+        : h(h_), cls(cls_), name(name_ ? name_ : kc_names[cls_]), flops(flops_), bytes(bytes_),
+          s(s_ ? s_ : h_->stream) {
         if ((h->timing_mask & (1u << cls)) || (!h->filter.empty() && h->filter == name)) {
             a = get_event(h);
-            (void)hipEventRecord(a, h->stream);
+            (void)hipEventRecord(a, s);
         }
     }
     ~Timed() {
         if (a) {
             hipEvent_t b = get_event(h);
-            (void)hipEventRecord(b, h->stream);
+            (void)hipEventRecord(b, s);
             h->pending.push_back({cls, name_index(h, name), a, b, flops, bytes});
         }
     }
@@ -344,6 +355,7 @@ struct Timed {
 void drain_timing(gpt_handle* h) {
     if (h->pending.empty()) return;
     (void)hipStreamSynchronize(h->stream);
+    if (h->side) (void)hipStreamSynchronize(h->side);
     for (auto& p : h->pending) {
         float ms = 0.f;
         if (hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
@@ -368,17 +380,22 @@ const void* Wop(gpt_handle* h, int idx) {
     return P(h, idx);
 }
 
-void run_gemm(gpt_handle* h, int cls, const gk::Gemm& g) {
+// On the handle's stream with the main split-K scratch, or (side = true) on the
+// side stream with its own scratch; timing events go to the launch's stream.
+void run_gemm(gpt_handle* h, int cls, const gk::Gemm& g, bool side = false) {
     const double ab = g.in_bf ? 2 : 4, cb = g.c_bf ? 2 : 4;
     const double bytes = ab * ((double)g.M * g.K + (double)g.K * g.N) + cb * (double)g.M * g.N;
-    const gk::GemmPlan plan = gk::gemm_plan(g, h->ws.splitk_floats);
+    float* scratch = side ? h->ws.splitk_side : h->ws.splitk;
+    const size_t nscratch = side ? h->ws.splitk_side_floats : h->ws.splitk_floats;
+    hipStream_t s = side ? h->side : h->stream;
+    const gk::GemmPlan plan = gk::gemm_plan(g, nscratch);
     {
-        Timed t(h, cls, 2.0 * g.M * g.N * g.K, bytes, plan.name);
-        gk::gemm_main(g, plan, h->ws.splitk, h->stream);
+        Timed t(h, cls, 2.0 * g.M * g.N * g.K, bytes, plan.name, s);
+        gk::gemm_main(g, plan, scratch, s);
     }
     if (plan.splits > 1) {
-        Timed t(h, cls, 0, 4.0 * plan.splits * g.M * g.N + cb * (double)g.M * g.N, "splitk_reduce_kernel");
-        gk::gemm_finish(g, plan, h->ws.splitk, h->stream);
+        Timed t(h, cls, 0, 4.0 * plan.splits * g.M * g.N + cb * (double)g.M * g.N, "splitk_reduce_kernel", s);
+        gk::gemm_finish(g, plan, scratch, s);
     }
 }
 
@@ -513,10 +530,14 @@ gpt_status gpt_create(const gpt_config* cfg, uint64_t seed, void* d_ws, size_t w
     if (s == GPT_OK) s = hip_check(h, hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking), "hipStreamCreate");
     if (s == GPT_OK) s = hip_check(h, hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming), "hipEventCreate");
     if (s == GPT_OK) s = hip_check(h, hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming), "hipEventCreate");
+    for (hipEvent_t& e : h->ev_dep)
+        if (s == GPT_OK) s = hip_check(h, hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreate");
     if (s != GPT_OK) {
         (void)hipStreamSynchronize(st);
         if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
         if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+        for (hipEvent_t e : h->ev_dep)
+            if (e) (void)hipEventDestroy(e);
         if (h->side) (void)hipStreamDestroy(h->side);
         delete h;
         return s;
@@ -529,11 +550,14 @@ gpt_status gpt_create(const gpt_config* cfg, uint64_t seed, void* d_ws, size_t w
 gpt_status gpt_destroy(gpt_handle* h) {
     if (!h) return GPT_ERR_INVALID_ARGUMENT;
     if (!h->pending.empty()) (void)hipStreamSynchronize(h->stream);
+    if (h->side) (void)hipStreamSynchronize(h->side);
     for (auto& p : h->pending) { (void)hipEventDestroy(p.a); (void)hipEventDestroy(p.b); }
     for (auto e : h->free_events) (void)hipEventDestroy(e);
     if (h->side) (void)hipStreamSynchronize(h->side);
     if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
     if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+    for (hipEvent_t e : h->ev_dep)
+        if (e) (void)hipEventDestroy(e);
     if (h->side) (void)hipStreamDestroy(h->side);
     delete h;
     return GPT_OK;
@@ -697,6 +721,16 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         h->jobs.push_back({part, out, npc, N});
     };
     ln_bwd(w.x_fin, meanf, rstdf, P(h, tb.lnf_w), true, G(h, tb.lnf_w), G(h, tb.lnf_b), G(h, tb.layers[L - 1].mp_b));
+    // The weight-gradient products (they only read activations and upstream
+    // gradients) run on the side stream, overlapping the input-gradient chain;
+    // events order them after their inputs and before the main stream
+    // overwrites those inputs. Not while per-class timing is on (its class
+    // totals assume one stream).
+    const bool conc = bf && h->timing_mask == 0;
+    enum { E_DR = 0, E_DH, E_DR2, E_DQKV, S_MP, S_FC, S_PROJ, S_QKV };
+    auto record = [&](int e, hipStream_t s_) { if (conc) (void)hipEventRecord(h->ev_dep[e], s_); };
+    auto wait_ev = [&](hipStream_t s_, int e) { if (conc) (void)hipStreamWaitEvent(s_, h->ev_dep[e], 0); };
+    hipStream_t sw = conc ? h->side : st;
     for (int l = L - 1; l >= 0; --l) {
         const LayerIdx& li = tb.layers[l];
         float* mean1 = w.ln_mean + (size_t)(2 * l) * M;
@@ -705,6 +739,8 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         float* rstd2 = w.ln_rstd + (size_t)(2 * l + 1) * M;
         // MLP branch
         bool fc_b_fused = false;   // fc bias gradient from the dgrad epilogue's column sums
+        if (l < L - 1) wait_ev(st, S_FC);   // the previous layer's fc weight gradient has read dh
+        record(E_DR, st);
         {
             gk::Gemm g = mk_gemm(h, M, F, d, dR, d, true, Wop(h, li.mp_w), F, false, w.dh, F, bf, gk::EPI_ACT_GRAD);
             g.aux = w.hdact[l];
@@ -715,23 +751,35 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
                 fc_b_fused = true;
             }
             run_gemm(h, KC_GEMM_DGRAD, g);
+            record(E_DH, st);
+            wait_ev(sw, E_DR);
             gk::Gemm g2 = mk_gemm(h, d, F, M, dR, d, false, w.hact[l], F, false, G(h, li.mp_w), F, false, gk::EPI_ACCUM);
-            run_gemm(h, KC_GEMM_WGRAD, g2);
+            run_gemm(h, KC_GEMM_WGRAD, g2, conc);
+            record(S_MP, sw);
         }
         {
             gk::Gemm g = mk_gemm(h, M, d, F, w.dh, F, true, Wop(h, li.fc_w), d, false, w.dln, d, false, gk::EPI_STORE);
             run_gemm(h, KC_GEMM_DGRAD, g);
+            wait_ev(sw, E_DH);
             gk::Gemm g2 = mk_gemm(h, F, d, M, w.dh, F, false, w.ln2[l], d, false, G(h, li.fc_w), d, false, gk::EPI_ACCUM);
-            run_gemm(h, KC_GEMM_WGRAD, g2);
+            run_gemm(h, KC_GEMM_WGRAD, g2, conc);
+            record(S_FC, sw);
         }
-        if (!fc_b_fused) col_sum(w.dh, F, G(h, li.fc_b));
+        if (!fc_b_fused) {
+            wait_ev(st, S_FC);
+            col_sum(w.dh, F, G(h, li.fc_b));
+        }
+        wait_ev(st, S_MP);   // the mp weight gradient has read dR
         ln_bwd(w.x_mid[l], mean2, rstd2, P(h, li.ln2_w), false, G(h, li.ln2_w), G(h, li.ln2_b), G(h, li.proj_b));
+        record(E_DR2, st);
         // attention branch
         {
             gk::Gemm g = mk_gemm(h, M, d, d, dR, d, true, Wop(h, li.proj_w), d, false, w.dO, d, bf, gk::EPI_STORE);
             run_gemm(h, KC_GEMM_DGRAD, g);
+            wait_ev(sw, E_DR2);
             gk::Gemm g2 = mk_gemm(h, d, d, M, dR, d, false, w.att[l], d, false, G(h, li.proj_w), d, false, gk::EPI_ACCUM);
-            run_gemm(h, KC_GEMM_WGRAD, g2);
+            run_gemm(h, KC_GEMM_WGRAD, g2, conc);
+            record(S_PROJ, sw);
         }
         const void *q = w.qkv[l], *k = (const char*)w.qkv[l] + (size_t)ab * d;
         int64_t ldq = 3 * d, ldk = 3 * d;
@@ -752,6 +800,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         float* qkv_part = w.cs_part + (size_t)(n_cs++) * w.cs_part_stride;
         bool attn_b_fused = false;
         if (!qkt) a.cpart = qkv_part;
+        if (l < L - 1) wait_ev(st, S_QKV);   // the previous layer's qkv weight gradient has read dqkv
         {
             double pairs = attn_pairs(B, T, H, a.window);
             Timed t(h, KC_ATTN_BWD, 8.0 * hd * pairs, (double)M * d * 8 * ab + 8.0 * M * H);
@@ -763,22 +812,27 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
             gk::qk_prep_bwd(bf, w.qkv[l], w.dqkv, w.rope_cos, w.rope_sin, M, T, H, hd, c.qk_rmsnorm,
                             c.pos_encoding == GPT_POS_ROPE, c.qk_norm_eps, st);
         }
+        record(E_DQKV, st);
         {
             gk::Gemm g = mk_gemm(h, M, d, 3 * d, w.dqkv, 3 * d, true, Wop(h, li.attn_w), d, false, w.dln, d, false,
                                  gk::EPI_STORE);
             run_gemm(h, KC_GEMM_DGRAD, g);
+            wait_ev(sw, E_DQKV);
             gk::Gemm g2 = mk_gemm(h, 3 * d, d, M, w.dqkv, 3 * d, false, w.ln1[l], d, false, G(h, li.attn_w), d, false,
                                   gk::EPI_ACCUM);
-            run_gemm(h, KC_GEMM_WGRAD, g2);
+            run_gemm(h, KC_GEMM_WGRAD, g2, conc);
+            record(S_QKV, sw);
         }
         if (!attn_b_fused) {
             Timed t(h, KC_COLSUM, 0, (double)ab * M * 3 * d + 4.0 * npc * 3 * d);
             gk::colsum_rows(bf, w.dqkv, 3 * d, M, 3 * d, qkv_part, st);
             h->jobs.push_back({qkv_part, G(h, li.attn_b), npc, 3 * d});
         }
+        wait_ev(st, S_PROJ);   // the proj weight gradient has read dR
         ln_bwd(w.x_in[l], mean1, rstd1, P(h, li.ln1_w), false, G(h, li.ln1_w), G(h, li.ln1_b),
                l > 0 ? G(h, tb.layers[l - 1].mp_b) : nullptr);
     }
+    wait_ev(st, S_QKV);   // every side-stream product is done (the side stream runs in order)
     if (!h->jobs.empty()) {
         auto same = [](const gk::RedJob& a, const gk::RedJob& b) {
             return a.part == b.part && a.out == b.out && a.np == b.np && a.n == b.n;

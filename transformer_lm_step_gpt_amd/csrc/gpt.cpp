@@ -117,7 +117,7 @@ struct Ws {
     float* row_loss = nullptr;
     float* dres = nullptr;
     void* dres_lp = nullptr;
-    float* dln = nullptr;
+    void* dln = nullptr;
     void *dh = nullptr, *dO = nullptr, *dqkv = nullptr;
     float* attD = nullptr;
     // row-pass partial sums of every LayerNorm backward and bias column sum of
@@ -186,7 +186,7 @@ Ws plan(const gpt_config& c, const Table& tb, void* base) {
     w.row_loss = cv.arr<float>(M);
     w.dres = cv.arr<float>(M * d);
     if (bf) w.dres_lp = cv.take(ab * M * d);
-    w.dln = cv.arr<float>(M * d);
+    w.dln = cv.take(ab * M * d);   // gradient at a LayerNorm output (bf16 on the bf16 path)
     w.dh = cv.take(ab * M * F);
     w.dO = cv.take(ab * M * d);
     w.dqkv = cv.take(ab * M * 3 * d);
@@ -693,7 +693,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
     }
     // ------------------------------------------------------------ backward
     {
-        gk::Gemm g = mk_gemm(h, M, d, Vp, w.logits, Vp, true, Wop(h, tb.wte), d, false, w.dln, d, false, gk::EPI_STORE);
+        gk::Gemm g = mk_gemm(h, M, d, Vp, w.logits, Vp, true, Wop(h, tb.wte), d, false, w.dln, d, bf, gk::EPI_STORE);
         run_gemm(h, KC_GEMM_LMHEAD_BWD, g);
         gk::Gemm g2 = mk_gemm(h, Vp, d, M, w.logits, Vp, false, w.lnf, d, false, G(h, tb.wte), d, false, gk::EPI_ACCUM);
         run_gemm(h, KC_GEMM_LMHEAD_BWD, g2);
@@ -707,9 +707,10 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
     int n_ln = 0, n_cs = 0;
     auto ln_bwd = [&](const float* x, const float* mean, const float* rstd, const float* g, bool overwrite, float* dg,
                       float* db, float* dcol) {
-        Timed t(h, KC_LN_BWD, 0, (double)M * d * ((overwrite ? 12 : 16) + ab) + 8.0 * M + 12.0 * nbl * d);
+        Timed t(h, KC_LN_BWD, 0, (double)M * d * ((overwrite ? 8 : 12) + 2 * ab) + 8.0 * M + 12.0 * nbl * d);
         float* part = w.ln_part + (size_t)(n_ln++) * w.ln_part_stride;
-        gk::layernorm_bwd_rows(bf, w.dln, x, mean, rstd, g, w.dres, bf ? w.dres_lp : nullptr, overwrite, part, M, d, st);
+        gk::layernorm_bwd_rows(bf, w.dln, bf, x, mean, rstd, g, w.dres, bf ? w.dres_lp : nullptr, overwrite, part, M, d,
+                               st);
         float* outs[3] = {dg, db, dcol};
         for (int q = 0; q < 3; ++q)
             if (outs[q]) h->jobs.push_back({part + (size_t)q * nbl * d, outs[q], nbl, d});
@@ -758,7 +759,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
             record(S_MP, sw);
         }
         {
-            gk::Gemm g = mk_gemm(h, M, d, F, w.dh, F, true, Wop(h, li.fc_w), d, false, w.dln, d, false, gk::EPI_STORE);
+            gk::Gemm g = mk_gemm(h, M, d, F, w.dh, F, true, Wop(h, li.fc_w), d, false, w.dln, d, bf, gk::EPI_STORE);
             run_gemm(h, KC_GEMM_DGRAD, g);
             wait_ev(sw, E_DH);
             gk::Gemm g2 = mk_gemm(h, F, d, M, w.dh, F, false, w.ln2[l], d, false, G(h, li.fc_w), d, false, gk::EPI_ACCUM);
@@ -814,7 +815,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         }
         record(E_DQKV, st);
         {
-            gk::Gemm g = mk_gemm(h, M, d, 3 * d, w.dqkv, 3 * d, true, Wop(h, li.attn_w), d, false, w.dln, d, false,
+            gk::Gemm g = mk_gemm(h, M, d, 3 * d, w.dqkv, 3 * d, true, Wop(h, li.attn_w), d, false, w.dln, d, bf,
                                  gk::EPI_STORE);
             run_gemm(h, KC_GEMM_DGRAD, g);
             wait_ev(sw, E_DQKV);

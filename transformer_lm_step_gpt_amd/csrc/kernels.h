@@ -60,9 +60,9 @@ void colsum(bool y_bf, const void* Y, int64_t ld, int M, int N, float* out, floa
 // sums of the new dres; nb = layernorm_bwd_num_partials(M)), colsum_rows
 // writes [np][N] (np = colsum_num_partials(M)).
 int layernorm_bwd_num_partials(int M);
-void layernorm_bwd_rows(bool bf, const float* dy, const float* x, const float* mean, const float* rstd,
+void layernorm_bwd_rows(bool bf, const void* dy, bool dy_bf, const float* x, const float* mean, const float* rstd,
                         const float* g, float* dres, void* dres_lp, bool overwrite, float* partial, int M, int d,
-                        hipStream_t s);
+                        hipStream_t s);   // dy bf16 when dy_bf (bf16 path only), else fp32
 int colsum_num_partials(int M);
 void colsum_rows(bool y_bf, const void* Y, int64_t ld, int M, int N, float* partial, hipStream_t s);
 

@@ -462,8 +462,8 @@ struct LnbIn {
     float mu, rs;
 };
 
-template <int NV>
-GPT_DEV void lnb_load(LnbIn<NV>& in, const float* __restrict__ dy, const float* __restrict__ x,
+template <typename TD, int NV>
+GPT_DEV void lnb_load(LnbIn<NV>& in, const TD* __restrict__ dy, const float* __restrict__ x,
                       const float* __restrict__ dres, float mu, float rs, int overwrite, int lane, int d) {
     in.mu = mu;
     in.rs = rs;
@@ -515,8 +515,9 @@ GPT_DEV void lnb_row(const LnbIn<NV>& in, const float4* gg, float* __restrict__ 
 }
 
 // Rows are processed with the next row's loads in flight (software pipeline).
-template <typename TL, int NV>
-__global__ __launch_bounds__(256) void layernorm_bwd_kernel(const float* __restrict__ dy, const float* __restrict__ x,
+// dy (the gradient at the LayerNorm output) is fp32 or bf16 (TD).
+template <typename TL, typename TD, int NV>
+__global__ __launch_bounds__(256) void layernorm_bwd_kernel(const TD* __restrict__ dy, const float* __restrict__ x,
                                                             const float* __restrict__ mean,
                                                             const float* __restrict__ rstd, const float* __restrict__ g,
                                                             float* __restrict__ dres, TL* __restrict__ dres_lp,
@@ -536,12 +537,12 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(const float* __restr
     LnbIn<NV> cur, nxt;
     if (r0 < r1) {
         const int64_t o = (int64_t)r0 * d;
-        lnb_load<NV>(cur, dy + o, x + o, dres + o, mean[r0], rstd[r0], overwrite, lane, d);
+        lnb_load<TD, NV>(cur, dy + o, x + o, dres + o, mean[r0], rstd[r0], overwrite, lane, d);
     }
     for (int r = r0; r < r1; ++r) {
         if (r + 1 < r1) {
             const int64_t o = (int64_t)(r + 1) * d;
-            lnb_load<NV>(nxt, dy + o, x + o, dres + o, mean[r + 1], rstd[r + 1], overwrite, lane, d);
+            lnb_load<TD, NV>(nxt, dy + o, x + o, dres + o, mean[r + 1], rstd[r + 1], overwrite, lane, d);
         }
         const int64_t o = (int64_t)r * d;
         lnb_row<TL, NV>(cur, gg, dres + o, dres_lp ? dres_lp + o : nullptr, lane, d, ag, ab, ac);
@@ -647,33 +648,40 @@ void reduce_rows(const float* part, int np, int n, float* out, float* tmp, hipSt
     reduce_partials(part, np, n, 1, tmp, out, nullptr, nullptr, s);
 }
 
-template <typename TL>
-static void lnb_launch(int nv, int nb, const float* dy, const float* x, const float* mean, const float* rstd,
+template <typename TL, typename TD>
+static void lnb_launch(int nv, int nb, const TD* dy, const float* x, const float* mean, const float* rstd,
                        const float* g, float* dres, TL* lp, int ov, float* part, int M, int d, hipStream_t s) {
     switch (nv) {
-        case 1: layernorm_bwd_kernel<TL, 1><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
-        case 2: layernorm_bwd_kernel<TL, 2><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
-        case 3: layernorm_bwd_kernel<TL, 3><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
-        case 4: layernorm_bwd_kernel<TL, 4><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
-        default: layernorm_bwd_kernel<TL, 8><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
+        case 1: layernorm_bwd_kernel<TL, TD, 1><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
+        case 2: layernorm_bwd_kernel<TL, TD, 2><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
+        case 3: layernorm_bwd_kernel<TL, TD, 3><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
+        case 4: layernorm_bwd_kernel<TL, TD, 4><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
+        default: layernorm_bwd_kernel<TL, TD, 8><<<nb, 256, 0, s>>>(dy, x, mean, rstd, g, dres, lp, ov, part, M, d); break;
     }
 }
 
 int layernorm_bwd_num_partials(int M) { return ceil_div(M, LNB_ROWS); }
 
-void layernorm_bwd_rows(bool bf, const float* dy, const float* x, const float* mean, const float* rstd, const float* g,
-                        float* dres, void* dres_lp, bool overwrite, float* partial, int M, int d, hipStream_t s) {
+void layernorm_bwd_rows(bool bf, const void* dy, bool dy_bf, const float* x, const float* mean, const float* rstd,
+                        const float* g, float* dres, void* dres_lp, bool overwrite, float* partial, int M, int d,
+                        hipStream_t s) {
     const int nb = ceil_div(M, LNB_ROWS);
     const int nv = ceil_div(d, 256);
-    if (bf) lnb_launch<bf16>(nv, nb, dy, x, mean, rstd, g, dres, (bf16*)dres_lp, overwrite, partial, M, d, s);
-    else lnb_launch<float>(nv, nb, dy, x, mean, rstd, g, dres, (float*)dres_lp, overwrite, partial, M, d, s);
+    if (bf && dy_bf)
+        lnb_launch<bf16, bf16>(nv, nb, (const bf16*)dy, x, mean, rstd, g, dres, (bf16*)dres_lp, overwrite, partial, M, d, s);
+    else if (bf)
+        lnb_launch<bf16, float>(nv, nb, (const float*)dy, x, mean, rstd, g, dres, (bf16*)dres_lp, overwrite, partial, M, d,
+                                s);
+    else
+        lnb_launch<float, float>(nv, nb, (const float*)dy, x, mean, rstd, g, dres, (float*)dres_lp, overwrite, partial, M,
+                                 d, s);
 }
 
 void layernorm_bwd(bool bf, const float* dy, const float* x, const float* mean, const float* rstd, const float* g,
                    float* dres, void* dres_lp, bool overwrite, float* dg, float* db, float* dcol, float* partial,
                    int M, int d, hipStream_t s) {
     const int nb = ceil_div(M, LNB_ROWS);
-    layernorm_bwd_rows(bf, dy, x, mean, rstd, g, dres, dres_lp, overwrite, partial, M, d, s);
+    layernorm_bwd_rows(bf, dy, false, x, mean, rstd, g, dres, dres_lp, overwrite, partial, M, d, s);
     reduce_partials(partial, nb, d, dcol ? 3 : 2, partial + (size_t)3 * nb * d, dg, db, dcol, s);
 }
 

@@ -1162,34 +1162,33 @@ GPT_DEV void adamw4(float4& pp, const float4& gg, float4& mm, float4& vv, bool d
     }
 }
 
-// two groups of four parameters per thread and iteration (eight 16-byte loads in flight)
+// One group of four parameters per thread, one pass over the grid (every load
+// of the group issued before its stores; the parameters, moments and bf16
+// copy are written with non-temporal stores: nothing reads them again before
+// the next step).
 __global__ __launch_bounds__(256) void adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
                                                     float* __restrict__ m, float* __restrict__ v, bf16* __restrict__ wbf,
                                                     int64_t n4, int64_t nd4, const float* coef_p,
                                                     const int32_t* nonfinite, float lr, float b1, float b2,
                                                     float eps, float wd, float rbc1, float rbc2) {
     if (*nonfinite) return;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
     const float c = *coef_p;
     const float dec = 1.0f - lr * wd;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += 2 * stride) {
-        const int64_t j = i + stride;
-        const bool two = j < n4;
-        float4 p0 = load4(p + 4 * i), g0 = load4(g + 4 * i), m0 = load4(m + 4 * i), v0 = load4(v + 4 * i);
-        float4 p1, g1, m1, v1;
-        if (two) { p1 = load4(p + 4 * j); g1 = load4(g + 4 * j); m1 = load4(m + 4 * j); v1 = load4(v + 4 * j); }
-        adamw4(p0, g0, m0, v0, i < nd4, c, dec, lr, b1, b2, eps, rbc1, rbc2);
-        store4(p + 4 * i, p0);
-        store4(m + 4 * i, m0);
-        store4(v + 4 * i, v0);
-        if (i < nd4 && wbf) store4(wbf + 4 * i, p0);
-        if (two) {
-            adamw4(p1, g1, m1, v1, j < nd4, c, dec, lr, b1, b2, eps, rbc1, rbc2);
-            store4(p + 4 * j, p1);
-            store4(m + 4 * j, m1);
-            store4(v + 4 * j, v1);
-            if (j < nd4 && wbf) store4(wbf + 4 * j, p1);
-        }
+    float4 p0 = load4(p + 4 * i), g0 = load4(g + 4 * i), m0 = load4(m + 4 * i), v0 = load4(v + 4 * i);
+    adamw4(p0, g0, m0, v0, i < nd4, c, dec, lr, b1, b2, eps, rbc1, rbc2);
+    auto nt4 = [](float* dst, const float4& x) {
+        const f32x4 t = {x.x, x.y, x.z, x.w};
+        __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(dst));
+    };
+    nt4(p + 4 * i, p0);
+    nt4(m + 4 * i, m0);
+    nt4(v + 4 * i, v0);
+    if (i < nd4 && wbf) {
+        bf16x4 o;
+        o[0] = (bf16)p0.x; o[1] = (bf16)p0.y; o[2] = (bf16)p0.z; o[3] = (bf16)p0.w;
+        __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(wbf + 4 * i));
     }
 }
 
@@ -1197,7 +1196,7 @@ void adamw(float* p, const float* g, float* m, float* v, void* wbf, int64_t n, i
            const int32_t* nonfinite, float lr, float b1, float b2, float eps, float wd, float rbc1, float rbc2,
            hipStream_t s) {
     int64_t n4 = n / 4;
-    unsigned grid = (unsigned)std::min<int64_t>((n4 + 255) / 256, 4096);
+    unsigned grid = (unsigned)((n4 + 255) / 256);
     adamw_kernel<<<grid, 256, 0, s>>>(p, g, m, v, (bf16*)wbf, n4, n_decay / 4, coef, nonfinite, lr, b1, b2, eps, wd,
                                       rbc1, rbc2);
 }

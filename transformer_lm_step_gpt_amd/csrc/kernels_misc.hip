@@ -905,7 +905,9 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
     __syncthreads();
     const float lse2 = gm + log2f((sred[4] + sred[5]) + (sred[6] + sred[7]));
     // pass 3: gradient softmax * gscale (times 1 - tanh^2 under the cap), written
-    // over the row; the target's -gscale is applied by thread 0 afterwards
+    // over the row with non-temporal stores (the row is not read again by this
+    // kernel; the products that read it stream 1.6 GB); the target's -gscale is
+    // applied by thread 0 afterwards
     const float gs = valid ? gscale : 0.f;
     // exp2(x log2e - gm) -> softmax * gscale
     const float rescale = __builtin_amdgcn_exp2f(gm - lse2) * gs;
@@ -920,7 +922,7 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
                 const bf16 lo = (bf16)(bf_lo(v[c][e2]) * rescale), hi = (bf16)(bf_hi(v[c][e2]) * rescale);
                 o[e2] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
             }
-            *reinterpret_cast<ce_u32x4*>(zr + 8 * idx) = o;
+            __builtin_nontemporal_store(o, reinterpret_cast<ce_u32x4*>(zr + 8 * idx));
             continue;
         }
 #pragma unroll
@@ -939,7 +941,7 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
             const bf16 lo = (bf16)gpair[0], hi = (bf16)gpair[1];
             o[e2] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
         }
-        *reinterpret_cast<ce_u32x4*>(zr + 8 * idx) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<ce_u32x4*>(zr + 8 * idx));
     }
     // the target: loss lse - z_t, and its gradient element (p_t - 1) * gscale (times
     // 1 - tanh^2 under the cap), written after every thread's chunk stores

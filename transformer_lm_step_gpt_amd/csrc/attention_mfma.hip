@@ -401,14 +401,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(Attn a) {
                 lq[g4] = *reinterpret_cast<const float4*>(Ls + qf * 32 + 8 * g4 + 4 * hh);
                 dq4[g4] = *reinterpret_cast<const float4*>(Ds + qf * 32 + 8 * g4 + 4 * hh);
             }
+            // P in place of S; the masking is a loop of its own so the unmasked
+            // path stays one straight-line block
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c, -(&lq[e >> 2].x)[e & 3]));
+            if (need_mask) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int qi = qf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+                    s[e] = visible(qt + qi, mykey, T, W) ? s[e] : 0.f;
+                }
+            }
             bf16x8 pk[2], dsk[2];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int qi = qf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-                const float lv = (&lq[e >> 2].x)[e & 3], dv4 = (&dq4[e >> 2].x)[e & 3];
-                float p = __builtin_amdgcn_exp2f(fmaf(s[e], c, -lv));
-                if (need_mask) p = visible(qt + qi, mykey, T, W) ? p : 0.f;
-                const float dsv = p * (dp[e] - dv4);
+                const float p = s[e], dsv = p * (dp[e] - (&dq4[e >> 2].x)[e & 3]);
                 pk[e >> 3][e & 7] = (bf16)p;
                 dsk[e >> 3][e & 7] = (bf16)dsv;
             }
@@ -515,16 +522,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
                 s = mfma(TL::rowfrag(Ks, kf * 32 + lr, ds, hh), qf[ds], s);
                 dp = mfma(TL::rowfrag(Vs, kf * 32 + lr, ds, hh), gf[ds], dp);
             }
+            // P in place of S; the masking is a loop of its own so the unmasked
+            // path stays one straight-line block
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c, -lse2));
+            if (need_mask) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = kt + kf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+                    s[e] = visible(myq, key, T, W) ? s[e] : 0.f;
+                }
+            }
             bf16x8 dsk[2];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float p = __builtin_amdgcn_exp2f(fmaf(s[e], c, -lse2));
-                if (need_mask) {
-                    const int key = kt + kf * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-                    p = visible(myq, key, T, W) ? p : 0.f;
-                }
-                dsk[e >> 3][e & 7] = (bf16)(p * (dp[e] - Dq));
-            }
+            for (int e = 0; e < 16; ++e) dsk[e >> 3][e & 7] = (bf16)(s[e] * (dp[e] - Dq));
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll

@@ -70,15 +70,15 @@ GPT_DEV void dma16(const void* g, bf16* lds_wave_base) {
 }
 
 // ---- [row][BK] tile of an operand stored k-contiguous (element (r, k) at base[r * ld + k])
-template <int R, int BK>
+template <int R, int BK, int NW>
 struct RowTile {
     static constexpr int CH = BK / 8;                 // 16-byte chunks per row
     static constexpr int ROWS_PER_DMA = 64 / CH;      // rows filled by one wave-wide DMA (1 KiB)
     static constexpr int DMAS = R / ROWS_PER_DMA;     // per tile
-    static constexpr int PER_WAVE = DMAS / 4;
+    static constexpr int PER_WAVE = DMAS / NW;
     static constexpr int BYTES = R * BK * 2;
     static constexpr int READS_PER_FRAG = 1;
-    static_assert(DMAS % 4 == 0, "tile too small for 4 waves");
+    static_assert(DMAS % NW == 0, "tile too small for the waves");
     GPT_DEV static int swz(int r) { return CH == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7); }
     // per-lane sources of this wave's DMAs for rows [row0, row0 + R), k [k0, k0 + BK);
     // each later k-tile is STEP elements further on
@@ -102,14 +102,14 @@ struct RowTile {
 };
 
 // ---- [BK][row] tile of an operand stored row-contiguous (element (r, k) at base[k * ld + r])
-template <int R, int BK>
+template <int R, int BK, int NW>
 struct ColTile {
     static constexpr int CH = R / 8;                  // 16-byte chunks per k-row
     static constexpr int DMAS = BK * CH / 64;         // wave-wide 1 KiB copies per tile
-    static constexpr int PER_WAVE = DMAS / 4;
+    static constexpr int PER_WAVE = DMAS / NW;
     static constexpr int BYTES = R * BK * 2;
     static constexpr int READS_PER_FRAG = 2;
-    static_assert(CH >= 16 && CH % 8 == 0 && (BK * CH) % 256 == 0, "unsupported tile");
+    static_assert(CH >= 16 && CH % 8 == 0 && (BK * CH) % (64 * NW) == 0, "unsupported tile");
     // chunk c of k-row k sits at slot lds_slot(k, c), so that the 4 k-rows x 4
     // chunks a half-wave's transposing read touches fall in 16 different
     // 16-byte bank groups (64 banks): for power-of-two rows (k-rows start at the
@@ -149,17 +149,17 @@ struct ColTile {
     }
 };
 
-template <bool KC, int R, int BK>
+template <bool KC, int R, int BK, int NW>
 struct OpTile;
-template <int R, int BK>
-struct OpTile<true, R, BK> : RowTile<R, BK> {
+template <int R, int BK, int NW>
+struct OpTile<true, R, BK, NW> : RowTile<R, BK, NW> {
     GPT_DEV static bf16x8 get(const bf16* t, int rb, int ks, int lane) {
-        return RowTile<R, BK>::frag(t, rb + (lane & 31), ks, lane >> 5);
+        return RowTile<R, BK, NW>::frag(t, rb + (lane & 31), ks, lane >> 5);
     }
 };
-template <int R, int BK>
-struct OpTile<false, R, BK> : ColTile<R, BK> {
-    GPT_DEV static bf16x8 get(const bf16* t, int rb, int ks, int lane) { return ColTile<R, BK>::frag(t, rb, ks, lane); }
+template <int R, int BK, int NW>
+struct OpTile<false, R, BK, NW> : ColTile<R, BK, NW> {
+    GPT_DEV static bf16x8 get(const bf16* t, int rb, int ks, int lane) { return ColTile<R, BK, NW>::frag(t, rb, ks, lane); }
 };
 
 }  // namespace
@@ -212,12 +212,16 @@ constexpr int GROUP_M = 8;
 // RS: a whole k-tile's fragments are read into registers at the start of the
 // tile, so its LDS stage is refilled one step into the tile instead of at its
 // end (each copy has about 1.5 k-tiles of products to land instead of one).
-template <int BM, int BN, int BK, int NS, int OCC, bool RS, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
-__global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, float* part) {
+// WGM x WGN waves (4 or 8), each owning a (BM/WGM) x (BN/WGN) sub-tile.
+template <int BM, int BN, int BK, int NS, int OCC, bool RS, int WGM, int WGN, bool AKC, bool BKC, int EPI, int OUTBF,
+          int ACT, bool SPLIT>
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_mfma_kernel(Gemm g, int kps, float* part) {
     using TC = typename std::conditional<OUTBF != 0, bf16, float>::type;
-    constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-    using TA = OpTile<AKC, BM, BK>;
-    using TB = OpTile<BKC, BN, BK>;
+    constexpr int NW = WGM * WGN, NT = 64 * NW;
+    constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+    static_assert(FM >= 1 && FN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave sub-tile of 32x32 fragments");
+    using TA = OpTile<AKC, BM, BK, NW>;
+    using TB = OpTile<BKC, BN, BK, NW>;
     constexpr int STAGE = (TA::BYTES + TB::BYTES) / 2;      // bf16 elements per stage
     constexpr int LPT = TA::PER_WAVE + TB::PER_WAVE;        // DMAs per lane per stage
     static_assert(NS >= 2 && NS <= 4, "stages");
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
     const int band = tile / (GROUP_M * tn), first = band * GROUP_M, bsz = min(tm - first, GROUP_M);
     const int inb = tile - band * GROUP_M * tn;
     const int m0 = (first + inb % bsz) * BM, n0 = (inb / bsz) * BN;
-    const int wm = (w >> 1) * WM, wn = (w & 1) * WN;
+    const int wm = (w / WGN) * WM, wn = (w % WGN) * WN;
     const int kb = blockIdx.z * kps;
     const int nk = max(0, (min(g.K, kb + kps) - kb) / BK);    // K and kps are multiples of BK
     const bf16* A = (const bf16*)g.A;
@@ -412,7 +416,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
     // CPR 8-column chunks per row, RPI rows per pass of the wave (lanes past
     // RPI * CPR idle when CPR does not divide 64), NIT passes per 32-row strip
     constexpr int SS = WN + 8, CPR = WN / 8, RPI = 64 / CPR, NIT = (32 + RPI - 1) / RPI;
-    static_assert(4 * 32 * SS * 4 <= NS * STAGE * 2, "staging strip fits in the stage ring");
+    static_assert(NW * 32 * SS * 4 <= NS * STAGE * 2, "staging strip fits in the stage ring");
     float* stg = reinterpret_cast<float*>(smem_raw) + w * 32 * SS;
     const f32x4* stg4 = reinterpret_cast<const f32x4*>(smem_raw) + w * 8 * SS;
     const int lr = lane & 31, lk = lane >> 5;
@@ -422,7 +426,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
     // column sums of the output (bias gradient), ACT_GRAD only: per lane over
     // its rows, then across the lanes and waves of a column in LDS
     constexpr bool CSUM = !SPLIT && EPI == EPI_ACT_GRAD;
-    static_assert(!CSUM || 4 * RPI * WN * 4 <= NS * STAGE * 2, "column-sum scratch fits in the stage ring");
+    static_assert(!CSUM || NW * RPI * WN * 4 <= NS * STAGE * 2, "column-sum scratch fits in the stage ring");
     float cs[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) cs[e] = 0.f;
@@ -496,10 +500,10 @@ __global__ __launch_bounds__(256, OCC) void gemm_mfma_kernel(Gemm g, int kps, fl
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             barrier_no_fence();
-            for (int c = tid; c < BN; c += 256) {
-                const int half = c / WN, cl = c - half * WN;
+            for (int c = tid; c < BN; c += NT) {
+                const int wc = c / WN, cl = c - wc * WN;   // the column's wave column
                 float sum = 0.f;
-                for (int wv = half; wv < 4; wv += 2)
+                for (int wv = wc; wv < NW; wv += WGN)
                     for (int r = 0; r < RPI; ++r) sum += red[(wv * RPI + r) * WN + cl];
                 if (n0 + c < g.N) g.cpart[(int64_t)(m0 / BM) * g.N + n0 + c] = sum;
             }
@@ -543,27 +547,31 @@ enum GemmCfg {
     CFG_256_256 = 0, CFG_128_256, CFG_128_128, CFG_256_128, CFG_256_192, CFG_256_256_K64, CFG_256_192_K64,
     CFG_256_128_K64, CFG_128_192_K64, CFG_128_256_K64, CFG_128_128_K64,
     // register-staged k-tiles (RS)
-    CFG_128_192_K64R, CFG_128_128_K64R, CFG_256_256_K64R, CFG_256_128_K64R, CFG_COUNT
+    CFG_128_192_K64R, CFG_128_128_K64R, CFG_256_256_K64R, CFG_256_128_K64R,
+    // eight waves (2 x 4) per workgroup
+    CFG_256_256_K64W8, CFG_256_256_K64RW8, CFG_COUNT
 };
-static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256, 256, 256, 256, 128, 128, 128, 128, 128, 256, 256};
-static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192, 256, 192, 128, 192, 256, 128, 192, 128, 256, 128};
-static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32, 32, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64};
-static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3, 2, 2, 2, 2, 2, 2, 2};
-static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1, 2, 1, 2, 2, 2, 1, 1};
+static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256, 256, 256, 256, 128, 128, 128, 128, 128, 256, 256, 256, 256};
+static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192, 256, 192, 128, 192, 256, 128, 192, 128, 256, 128, 256, 256};
+static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32, 32, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64};
+static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3, 2, 2, 2, 2, 2, 2, 2, 2, 2};
+static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1, 2, 1, 2, 2, 2, 1, 1, 1, 1};
 static const bool cfg_rs[CFG_COUNT] = {false, false, false, false, false, false, false, false, false, false, false,
-                                       true, true, true, true};
+                                       true,  true,  true,  true,  false, true};
+static const int cfg_wgn[CFG_COUNT] = {2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4};   // wave grid 2 x WGN
 
-template <int BM, int BN, int BK, int NS, int OCC, bool RS, bool AKC, bool BKC, int EPI, int OUTBF, int ACT, bool SPLIT>
+template <int BM, int BN, int BK, int NS, int OCC, bool RS, int WGM, int WGN, bool AKC, bool BKC, int EPI, int OUTBF,
+          int ACT, bool SPLIT>
 static void launch(const Gemm& g, dim3 grid, int kps, float* part, hipStream_t s) {
     constexpr size_t LDS = (size_t)NS * (BM + BN) * BK * sizeof(bf16);
     static_assert(LDS * OCC <= 160 * 1024, "LDS budget");
-    auto k = gemm_mfma_kernel<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI, OUTBF, ACT, SPLIT>;
+    auto k = gemm_mfma_kernel<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI, OUTBF, ACT, SPLIT>;
     static bool attr = false;
     if (!attr) {
         (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
         attr = true;
     }
-    k<<<grid, 256, LDS, s>>>(g, kps, part);
+    k<<<grid, 64 * WGM * WGN, LDS, s>>>(g, kps, part);
 }
 
 // output storage of each epilogue (bf16 except the fp32 residual stream,
@@ -574,51 +582,53 @@ static int out_bf(const Gemm& g) {
     return 1;
 }
 
-template <int BM, int BN, int BK, int NS, int OCC, bool RS, bool AKC, bool BKC>
+template <int BM, int BN, int BK, int NS, int OCC, bool RS, int WGM, int WGN, bool AKC, bool BKC>
 static void run_main(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
     dim3 grid(ceil_div(g.N, BN) * ceil_div(g.M, BM), 1, p.splits);
     const int kps = ceil_div(ceil_div(g.K, p.splits), BK) * BK;
-    if (p.splits > 1) { launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_STORE, 0, 0, true>(g, grid, kps, part, s); return; }
+    if (p.splits > 1) { launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_STORE, 0, 0, true>(g, grid, kps, part, s); return; }
     const bool relu = g.act == ACT_RELU2;
     switch (g.epi) {
         case EPI_STORE:
-            if (g.c_bf) launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_STORE, 1, 0, false>(g, grid, kps, part, s);
-            else launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_STORE, 0, 0, false>(g, grid, kps, part, s);
+            if (g.c_bf) launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_STORE, 1, 0, false>(g, grid, kps, part, s);
+            else launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_STORE, 0, 0, false>(g, grid, kps, part, s);
             break;
-        case EPI_BIAS: launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_BIAS, 1, 0, false>(g, grid, kps, part, s); break;
+        case EPI_BIAS: launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_BIAS, 1, 0, false>(g, grid, kps, part, s); break;
         case EPI_BIAS_ACT:
-            if (relu) launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_BIAS_ACT, 1, ACT_RELU2, false>(g, grid, kps, part, s);
-            else launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_BIAS_ACT, 1, ACT_GELU, false>(g, grid, kps, part, s);
+            if (relu) launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_BIAS_ACT, 1, ACT_RELU2, false>(g, grid, kps, part, s);
+            else launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_BIAS_ACT, 1, ACT_GELU, false>(g, grid, kps, part, s);
             break;
         case EPI_BIAS_RESID:
-            launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_BIAS_RESID, 0, 0, false>(g, grid, kps, part, s);
+            launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_BIAS_RESID, 0, 0, false>(g, grid, kps, part, s);
             break;
         case EPI_ACT_GRAD:
-            if (relu) launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_ACT_GRAD, 1, ACT_RELU2, false>(g, grid, kps, part, s);
-            else launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_ACT_GRAD, 1, ACT_GELU, false>(g, grid, kps, part, s);
+            if (relu) launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_ACT_GRAD, 1, ACT_RELU2, false>(g, grid, kps, part, s);
+            else launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_ACT_GRAD, 1, ACT_GELU, false>(g, grid, kps, part, s);
             break;
-        case EPI_ACCUM: launch<BM, BN, BK, NS, OCC, RS, AKC, BKC, EPI_ACCUM, 0, 0, false>(g, grid, kps, part, s); break;
+        case EPI_ACCUM: launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_ACCUM, 0, 0, false>(g, grid, kps, part, s); break;
     }
 }
 
 template <bool AKC, bool BKC>
 static void run_cfg(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
     switch (p.cfg) {
-        case CFG_256_256: run_main<256, 256, 32, 4, 1, false, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_256: run_main<128, 256, 32, 4, 1, false, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_128: run_main<128, 128, 32, 4, 2, false, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_128: run_main<256, 128, 32, 3, 2, false, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_192: run_main<256, 192, 32, 4, 1, false, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_256_K64: run_main<256, 256, 64, 2, 1, false, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_192_K64: run_main<256, 192, 64, 2, 1, false, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_128_K64: run_main<256, 128, 64, 3, 1, false, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_192_K64: run_main<128, 192, 64, 2, 2, false, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_256_K64: run_main<128, 256, 64, 2, 1, false, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_128_K64: run_main<128, 128, 64, 2, 2, false, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_192_K64R: run_main<128, 192, 64, 2, 2, true, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_128_K64R: run_main<128, 128, 64, 2, 2, true, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_256_K64R: run_main<256, 256, 64, 2, 1, true, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_128_K64R: run_main<256, 128, 64, 2, 1, true, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256: run_main<256, 256, 32, 4, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_256: run_main<128, 256, 32, 4, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128: run_main<128, 128, 32, 4, 2, false, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128: run_main<256, 128, 32, 3, 2, false, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_192: run_main<256, 192, 32, 4, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64: run_main<256, 256, 64, 2, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_192_K64: run_main<256, 192, 64, 2, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128_K64: run_main<256, 128, 64, 3, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_192_K64: run_main<128, 192, 64, 2, 2, false, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_256_K64: run_main<128, 256, 64, 2, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128_K64: run_main<128, 128, 64, 2, 2, false, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_192_K64R: run_main<128, 192, 64, 2, 2, true, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128_K64R: run_main<128, 128, 64, 2, 2, true, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64R: run_main<256, 256, 64, 2, 1, true, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128_K64R: run_main<256, 128, 64, 2, 1, true, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64W8: run_main<256, 256, 64, 2, 1, false, 2, 4, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64RW8: run_main<256, 256, 64, 2, 1, true, 2, 4, AKC, BKC>(g, p, part, s); break;
     }
 }
 
@@ -681,16 +691,16 @@ struct Tuned { int M, N, K; bool a_kc, b_kc; int cfg, splits; };
 static const Tuned tuned[] = {
     // forward: X W^T
     {16384, 2304, 768, true, true, CFG_128_192_K64, 1}, {16384, 768, 768, true, true, CFG_128_192_K64, 1},
-    {16384, 3072, 768, true, true, CFG_128_192_K64, 1}, {16384, 768, 3072, true, true, CFG_128_192_K64, 1},
-    {16384, 50304, 768, true, true, CFG_256_256_K64R, 1},
+    {16384, 3072, 768, true, true, CFG_256_256_K64RW8, 1}, {16384, 768, 3072, true, true, CFG_128_192_K64, 1},
+    {16384, 50304, 768, true, true, CFG_256_256_K64RW8, 1},
     // input gradients: dY W
-    {16384, 3072, 768, true, false, CFG_128_192_K64R, 1}, {16384, 768, 3072, true, false, CFG_128_192_K64R, 1},
+    {16384, 3072, 768, true, false, CFG_256_256_K64RW8, 1}, {16384, 768, 3072, true, false, CFG_128_192_K64R, 1},
     {16384, 768, 768, true, false, CFG_128_192_K64R, 1}, {16384, 768, 2304, true, false, CFG_128_192_K64R, 1},
     {16384, 768, 50304, true, false, CFG_128_192_K64R, 1},
     // weight gradients: dY^T X
-    {768, 3072, 16384, false, false, CFG_128_128_K64R, 3}, {3072, 768, 16384, false, false, CFG_128_128_K64R, 3},
+    {768, 3072, 16384, false, false, CFG_256_256_K64R, 6}, {3072, 768, 16384, false, false, CFG_256_256_K64R, 6},
     {768, 768, 16384, false, false, CFG_128_128_K64R, 12}, {2304, 768, 16384, false, false, CFG_128_128_K64R, 4},
-    {50304, 768, 16384, false, false, CFG_128_192_K64R, 2},
+    {50304, 768, 16384, false, false, CFG_256_256_K64RW8, 2},
 };
 
 GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
@@ -751,9 +761,9 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
     p.splits = bsplits;
     p.bm = (bsplits == 1 && g.epi == EPI_ACT_GRAD) ? cfg_bm[bcfg] : 0;
     const bool relu = bsplits == 1 && (g.epi == EPI_BIAS_ACT || g.epi == EPI_ACT_GRAD) && g.act == ACT_RELU2;
-    snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %s, %s, %s, %d, %d, %d, %s>", cfg_bm[bcfg],
-             cfg_bn[bcfg], cfg_bk[bcfg], cfg_ns[bcfg], cfg_occ[bcfg], cfg_rs[bcfg] ? "true" : "false",
-             g.a_kc ? "true" : "false", g.b_kc ? "true" : "false",
+    snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %s, 2, %d, %s, %s, %d, %d, %d, %s>",
+             cfg_bm[bcfg], cfg_bn[bcfg], cfg_bk[bcfg], cfg_ns[bcfg], cfg_occ[bcfg], cfg_rs[bcfg] ? "true" : "false",
+             cfg_wgn[bcfg], g.a_kc ? "true" : "false", g.b_kc ? "true" : "false",
              bsplits > 1 ? 0 : g.epi, bsplits > 1 ? 0 : out_bf(g), relu ? 1 : 0, bsplits > 1 ? "true" : "false");
     return p;
 }

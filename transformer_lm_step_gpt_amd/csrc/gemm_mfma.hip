@@ -548,17 +548,20 @@ enum GemmCfg {
     CFG_256_128_K64, CFG_128_192_K64, CFG_128_256_K64, CFG_128_128_K64,
     // register-staged k-tiles (RS)
     CFG_128_192_K64R, CFG_128_128_K64R, CFG_256_256_K64R, CFG_256_128_K64R,
-    // eight waves (2 x 4) per workgroup
-    CFG_256_256_K64W8, CFG_256_256_K64RW8, CFG_COUNT
+    // eight waves per workgroup (wave grid cfg_wgm x cfg_wgn)
+    CFG_256_256_K64W8, CFG_256_256_K64RW8, CFG_256_192_K64RW8, CFG_256_128_K64RW8, CFG_128_256_K64RW8, CFG_COUNT
 };
-static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256, 256, 256, 256, 128, 128, 128, 128, 128, 256, 256, 256, 256};
-static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192, 256, 192, 128, 192, 256, 128, 192, 128, 256, 128, 256, 256};
-static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32, 32, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64};
-static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3, 2, 2, 2, 2, 2, 2, 2, 2, 2};
-static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1, 2, 1, 2, 2, 2, 1, 1, 1, 1};
+static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256, 256, 256, 256, 128, 128, 128, 128, 128, 256, 256,
+                                      256, 256, 256, 256, 128};
+static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192, 256, 192, 128, 192, 256, 128, 192, 128, 256, 128,
+                                      256, 256, 192, 128, 256};
+static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32, 32, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64};
+static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2};
+static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1, 2, 1, 2, 2, 2, 1, 1, 1, 1, 1, 1, 1};
 static const bool cfg_rs[CFG_COUNT] = {false, false, false, false, false, false, false, false, false, false, false,
-                                       true,  true,  true,  true,  false, true};
-static const int cfg_wgn[CFG_COUNT] = {2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4};   // wave grid 2 x WGN
+                                       true,  true,  true,  true,  false, true,  true,  true,  true};
+static const int cfg_wgm[CFG_COUNT] = {2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4, 2};
+static const int cfg_wgn[CFG_COUNT] = {2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4, 2, 2, 4};
 
 template <int BM, int BN, int BK, int NS, int OCC, bool RS, int WGM, int WGN, bool AKC, bool BKC, int EPI, int OUTBF,
           int ACT, bool SPLIT>
@@ -629,6 +632,9 @@ static void run_cfg(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s
         case CFG_256_128_K64R: run_main<256, 128, 64, 2, 1, true, 2, 2, AKC, BKC>(g, p, part, s); break;
         case CFG_256_256_K64W8: run_main<256, 256, 64, 2, 1, false, 2, 4, AKC, BKC>(g, p, part, s); break;
         case CFG_256_256_K64RW8: run_main<256, 256, 64, 2, 1, true, 2, 4, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_192_K64RW8: run_main<256, 192, 64, 2, 1, true, 4, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128_K64RW8: run_main<256, 128, 64, 2, 1, true, 4, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_256_K64RW8: run_main<128, 256, 64, 2, 1, true, 2, 4, AKC, BKC>(g, p, part, s); break;
     }
 }
 
@@ -761,9 +767,9 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
     p.splits = bsplits;
     p.bm = (bsplits == 1 && g.epi == EPI_ACT_GRAD) ? cfg_bm[bcfg] : 0;
     const bool relu = bsplits == 1 && (g.epi == EPI_BIAS_ACT || g.epi == EPI_ACT_GRAD) && g.act == ACT_RELU2;
-    snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %s, 2, %d, %s, %s, %d, %d, %d, %s>",
+    snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %s, %d, %d, %s, %s, %d, %d, %d, %s>",
              cfg_bm[bcfg], cfg_bn[bcfg], cfg_bk[bcfg], cfg_ns[bcfg], cfg_occ[bcfg], cfg_rs[bcfg] ? "true" : "false",
-             cfg_wgn[bcfg], g.a_kc ? "true" : "false", g.b_kc ? "true" : "false",
+             cfg_wgm[bcfg], cfg_wgn[bcfg], g.a_kc ? "true" : "false", g.b_kc ? "true" : "false",
              bsplits > 1 ? 0 : g.epi, bsplits > 1 ? 0 : out_bf(g), relu ? 1 : 0, bsplits > 1 ? "true" : "false");
     return p;
 }

@@ -228,8 +228,10 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
     constexpr int NDS = HD / 16, NDF = HD / 32;
     using TL = HTile<HD>;
     __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
-    const int qt = gridDim.x - 1 - blockIdx.x;   // heaviest query tiles first
-    const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+    // workgroups are dispatched x-fastest: every (batch, head) of the heaviest
+    // query tile goes first (longest-first over the whole grid)
+    const int qt = gridDim.y - 1 - blockIdx.y;
+    const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
     const int T = a.T, W = a.window;
     const int q0 = qt * ATT_BQ;
     // the wave index as a wave-uniform (scalar) value, so per-wave tests are scalar branches
@@ -343,9 +345,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(Attn a) {
     static_assert(2 * ATT_NS * TileRing<HD>::STAGE >= 4 * NDF * 16 * 64 * 4, "column-sum scratch fits in the ring");
     __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
     __shared__ __attribute__((aligned(16))) float Lrow[ATT_MAX_T], Drow[ATT_MAX_T];
-    const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+    // key blocks in y, (batch, head) in x: the heaviest (first) key blocks of
+    // every head are dispatched first
+    const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
     const int T = a.T, W = a.window;
-    const int k0 = blockIdx.x * ATT_BQ;
+    const int k0 = blockIdx.y * ATT_BQ;
     // the wave index as a wave-uniform (scalar) value, so per-wave tests are scalar branches
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lr = lane & 31,
               hh = lane >> 5;
@@ -447,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(Attn a) {
             }
     }
     if (a.cpart) {   // bias-gradient column sums of this block's dK and dV (values before rounding)
-        float* row = a.cpart + (int64_t)(b * gridDim.x + blockIdx.x) * (3 * a.H * HD);
+        float* row = a.cpart + (int64_t)(b * gridDim.y + blockIdx.y) * (3 * a.H * HD);
         float* red = reinterpret_cast<float*>(smem);
         block_colsum<HD, NDF>(dk, 1.0f / sqrtf((float)HD), mykey < T, red, row + a.H * HD + h * HD, w, lane);
         block_colsum<HD, NDF>(dv, 1.0f, mykey < T, red, row + 2 * a.H * HD + h * HD, w, lane);
@@ -462,8 +466,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
     using TL = HTile<HD>;
     static_assert(2 * ATT_NS * TileRing<HD>::STAGE >= 4 * NDF * 16 * 64 * 4, "column-sum scratch fits in the ring");
     __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
-    const int qtile = gridDim.x - 1 - blockIdx.x;
-    const int bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+    const int qtile = gridDim.y - 1 - blockIdx.y;   // heaviest query tiles of every head first
+    const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
     const int T = a.T, W = a.window;
     const int q0 = qtile * ATT_BQ;
     // the wave index as a wave-uniform (scalar) value, so per-wave tests are scalar branches
@@ -557,7 +561,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
             }
     }
     if (a.cpart) {   // bias-gradient column sums of this block's dQ (values before rounding)
-        float* row = a.cpart + (int64_t)(b * gridDim.x + qtile) * (3 * a.H * HD);
+        float* row = a.cpart + (int64_t)(b * gridDim.y + qtile) * (3 * a.H * HD);
         block_colsum<HD, NDF>(dq, 1.0f / sqrtf((float)HD), myq < T, reinterpret_cast<float*>(smem), row + h * HD, w,
                               lane);
     }
@@ -575,7 +579,7 @@ static bool mfma_ok(const Attn& a) {
 
 bool attention_fwd_mfma(const Attn& a, hipStream_t s) {
     if (!mfma_ok(a) || a.ldo % 4) return false;
-    dim3 grid(ceil_div(a.T, ATT_BQ), a.B * a.H);
+    dim3 grid(a.B * a.H, ceil_div(a.T, ATT_BQ));
     if (a.hd == 64) attn_fwd_mfma_kernel<64><<<grid, 256, 0, s>>>(a);
     else attn_fwd_mfma_kernel<128><<<grid, 256, 0, s>>>(a);
     return true;
@@ -585,7 +589,7 @@ bool attention_bwd_mfma(const Attn& a, hipStream_t s) {
     if (!mfma_ok(a) || a.lddo % 8 || a.ldd % 4 || a.ldo % 8) return false;
     auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
     if (!al(a.dO) || !al(a.o)) return false;
-    dim3 grid(ceil_div(a.T, ATT_BQ), a.B * a.H);
+    dim3 grid(a.B * a.H, ceil_div(a.T, ATT_BQ));
     if (a.hd == 64) {
         attn_bwd_dq_mfma_kernel<64><<<grid, 256, 0, s>>>(a);
         attn_bwd_dkdv_mfma_kernel<64><<<grid, 256, 0, s>>>(a);

@@ -213,7 +213,7 @@ const char* gpt_last_error(const gpt_handle* h);
  * events on the handle's stream. For the timed launches the library sums the
  * event time, the launch count and the algorithmic FLOPs and HBM bytes, per
  * class and per kernel name (the main kernel instantiation, as profilers name
- * it: e.g. "gemm_mfma_kernel<128, 192, 64, 2, 2, false, 2, 2, true, true, 0, 1, 0, false>").
+ * it: e.g. "gemm_mfma_kernel<128, 192, 64, 2, 2, 0, 2, 2, true, true, 0, 1, 0, false>").
  * Reading the statistics synchronizes the stream. */
 gpt_status gpt_set_kernel_timing(gpt_handle* h, int32_t class_mask);
 gpt_status gpt_set_kernel_timing_filter(gpt_handle* h, const char* kernel_name /* null: none */);

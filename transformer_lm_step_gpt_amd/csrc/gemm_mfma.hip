@@ -204,18 +204,29 @@ __device__ __attribute__((always_inline)) inline void products(f32x16 (&acc)[FM]
 }
 
 constexpr int GROUP_M = 8;
+enum { PIPE_DMA = 0, PIPE_DMA_RS = 1, PIPE_VGPR = 2 };
 
 // SPLIT: write fp32 partial sums to part[z][M][N] instead of the epilogue.
 // OUTBF: output storage bf16 (1) or fp32 (0); ACT: activation of the
 // BIAS_ACT / ACT_GRAD epilogues. N and ldc are multiples of 8 and the output,
 // aux, residual and bias buffers 16-byte aligned (gemm_mfma_ok).
-// RS: a whole k-tile's fragments are read into registers at the start of the
-// tile, so its LDS stage is refilled one step into the tile instead of at its
-// end (each copy has about 1.5 k-tiles of products to land instead of one).
+// PIPE (how k-tiles reach LDS and registers):
+//   PIPE_DMA: LDS-DMA copies; each 16-deep step's fragments are read during
+//     the previous step.
+//   PIPE_DMA_RS (register-staged): LDS-DMA copies; a whole k-tile's fragments
+//     are read into registers at the start of the tile, so its LDS stage is
+//     refilled one step into the tile instead of at its end (each copy has
+//     about 1.5 k-tiles of products to land instead of one).
+//   PIPE_VGPR: two LDS stages; the copy of k-tile t+2 is loaded into
+//     registers (16 bytes per lane per copy) while tile t is multiplied, and
+//     written to LDS with ds_write_b128 during tile t+1, so global-load
+//     latency has a whole k-tile of products to hide under and the LDS sees
+//     ordinary 16-byte writes instead of DMA traffic.
 // WGM x WGN waves (4 or 8), each owning a (BM/WGM) x (BN/WGN) sub-tile.
-template <int BM, int BN, int BK, int NS, int OCC, bool RS, int WGM, int WGN, bool AKC, bool BKC, int EPI, int OUTBF,
+template <int BM, int BN, int BK, int NS, int OCC, int PIPE, int WGM, int WGN, bool AKC, bool BKC, int EPI, int OUTBF,
           int ACT, bool SPLIT>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_mfma_kernel(Gemm g, int kps, float* part) {
+    constexpr bool RS = PIPE == PIPE_DMA_RS;
     using TC = typename std::conditional<OUTBF != 0, bf16, float>::type;
     constexpr int NW = WGM * WGN, NT = 64 * NW;
     constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
@@ -296,7 +307,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_mfma_kernel(Gemm g, 
     };
 
     for (int t = 0; t < NS; ++t) {
-        if (issued < nk) {
+        if (PIPE != PIPE_VGPR && issued < nk) {
             bf16* st = smem + (issued % NS) * STAGE;
 #pragma unroll
             for (int q = 0; q < LPT; ++q) dma(q, st);
@@ -372,6 +383,78 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_mfma_kernel(Gemm g, 
             };
             products<FM, FN>(acc, ra[KS - 1], rb[KS - 1], rd0);
         }
+    } else if constexpr (PIPE == PIPE_VGPR) {
+        // Tile t (stage t % 2):
+        //   step 0 .. : the copy of tile t+1 (in registers since tile t-1) is
+        //     written to stage (t+1) % 2, whose tile t-1 every wave finished
+        //     reading before the last barrier; after each 16-byte write the
+        //     register is reloaded with the same copy of tile t+2
+        //   steps 0 .. KS-2: products | reads of the next step
+        //   LDS writes done + barrier: tile t+1 is in LDS for every wave
+        //   last step: products | reads of step 0 of tile t+1
+        static_assert(NS == 2, "two LDS stages");
+        constexpr int P = FM * FN;
+        static_assert(LPT <= P * (KS - 1), "copies fit in the steps before the barrier");
+        // The copies are issued without branches (a branch around them makes
+        // the compiler wait for every outstanding load before each LDS
+        // write): a load for a k-tile past the last one reads the last
+        // k-tile again (the pointers stop advancing there) and its LDS write
+        // goes to a stage that is no longer read.
+        u32x4 cp[LPT];
+        auto gload = [&](int q, bool adv) {
+            if (q < PA) {
+                cp[q] = *reinterpret_cast<const u32x4*>(srcA[q]);
+                srcA[q] += adv ? stA : 0;
+            } else {
+                cp[q] = *reinterpret_cast<const u32x4*>(srcB[q - PA]);
+                srcB[q - PA] += adv ? stB : 0;
+            }
+        };
+        auto swrite = [&](int q, bf16* st) {
+            bf16* d = q < PA ? st + (wu * PA + q) * 512 : st + TA::BYTES / 2 + (wu * PB + q - PA) * 512;
+            *reinterpret_cast<u32x4*>(d + lane * 8) = cp[q];
+        };
+        auto lds_ready = [&]() {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            barrier_no_fence();
+        };
+        bf16x8 fa[2][FM], fb[2][FN];
+        if (nk > 0) {
+#pragma unroll
+            for (int q = 0; q < LPT; ++q) gload(q, nk > 1);
+#pragma unroll
+            for (int q = 0; q < LPT; ++q) swrite(q, smem);
+#pragma unroll
+            for (int q = 0; q < LPT; ++q) gload(q, nk > 2);
+            lds_ready();
+            frags(0, 0, fa[0], fb[0]);
+        }
+        for (int t = 0; t < nk; ++t) {
+            const bf16* as = smem + (t & 1) * STAGE;
+            bf16* st = smem + ((t + 1) & 1) * STAGE;
+            const bool adv = t + 3 < nk;
+#pragma unroll
+            for (int ks = 0; ks < KS - 1; ++ks) {
+                auto copy = [&](int p) {
+#pragma unroll
+                    for (int q = 0; q < LPT; ++q)
+                        if (q / P == ks && q % P == p) {
+                            swrite(q, st);
+                            gload(q, adv);
+                        }
+                };
+                half_step<FM, FN, TA, TB>(acc, fa[ks & 1], fb[ks & 1], fa[(ks + 1) & 1], fb[(ks + 1) & 1], as,
+                                          as + TA::BYTES / 2, wm, wn, ks + 1, lane, copy);
+            }
+            lds_ready();
+            __builtin_amdgcn_sched_barrier(0);
+            // on the last tile this prefetch reads a stage that holds no new tile;
+            // the values are never used
+            auto none = [](int) {};
+            half_step<FM, FN, TA, TB>(acc, fa[(KS - 1) & 1], fb[(KS - 1) & 1], fa[0], fb[0], st, st + TA::BYTES / 2,
+                                      wm, wn, 0, lane, none);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // LDS writes done before the epilogue reuses the stages
     } else {
     bf16x8 fa[2][FM], fb[2][FN];
     if (nk > 0) {
@@ -549,26 +632,30 @@ enum GemmCfg {
     // register-staged k-tiles (RS)
     CFG_128_192_K64R, CFG_128_128_K64R, CFG_256_256_K64R, CFG_256_128_K64R,
     // eight waves per workgroup (wave grid cfg_wgm x cfg_wgn)
-    CFG_256_256_K64W8, CFG_256_256_K64RW8, CFG_256_192_K64RW8, CFG_256_128_K64RW8, CFG_128_256_K64RW8, CFG_COUNT
+    CFG_256_256_K64W8, CFG_256_256_K64RW8, CFG_256_192_K64RW8, CFG_256_128_K64RW8, CFG_128_256_K64RW8,
+    // copies staged through registers (PIPE_VGPR)
+    CFG_256_256_K64VW8, CFG_128_192_K64V, CFG_256_256_K64V, CFG_128_128_K64V,
+    // four stages of 32-deep k-tiles (three copies in flight)
+    CFG_256_256_K32W8, CFG_128_192_K32, CFG_COUNT
 };
-static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256, 256, 256, 256, 128, 128, 128, 128, 128, 256, 256,
-                                      256, 256, 256, 256, 128};
-static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192, 256, 192, 128, 192, 256, 128, 192, 128, 256, 128,
-                                      256, 256, 192, 128, 256};
-static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32, 32, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64};
-static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2};
-static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1, 2, 1, 2, 2, 2, 1, 1, 1, 1, 1, 1, 1};
-static const bool cfg_rs[CFG_COUNT] = {false, false, false, false, false, false, false, false, false, false, false,
-                                       true,  true,  true,  true,  false, true,  true,  true,  true};
-static const int cfg_wgm[CFG_COUNT] = {2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4, 2};
-static const int cfg_wgn[CFG_COUNT] = {2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4, 2, 2, 4};
+static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256, 256, 256, 256, 128, 128, 128, 128, 128,
+                                      256, 256, 256, 256, 256, 256, 128, 256, 128, 256, 128, 256, 128};
+static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192, 256, 192, 128, 192, 256, 128, 192, 128,
+                                      256, 128, 256, 256, 192, 128, 256, 256, 192, 256, 128, 256, 192};
+static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32, 32, 64, 64, 64, 64, 64, 64, 64, 64,
+                                      64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 32, 32};
+static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4};
+static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1, 2, 1, 2, 2, 2, 1, 1, 1, 1, 1, 1, 1, 1, 2, 1, 2, 1, 2};
+static const int cfg_pipe[CFG_COUNT] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 1, 1, 1, 0, 1, 1, 1, 1, 2, 2, 2, 2, 0, 0};
+static const int cfg_wgm[CFG_COUNT] = {2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4, 2, 2, 2, 2, 2, 2, 2};
+static const int cfg_wgn[CFG_COUNT] = {2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4, 2, 2, 4, 4, 2, 2, 2, 4, 2};
 
-template <int BM, int BN, int BK, int NS, int OCC, bool RS, int WGM, int WGN, bool AKC, bool BKC, int EPI, int OUTBF,
+template <int BM, int BN, int BK, int NS, int OCC, int PIPE, int WGM, int WGN, bool AKC, bool BKC, int EPI, int OUTBF,
           int ACT, bool SPLIT>
 static void launch(const Gemm& g, dim3 grid, int kps, float* part, hipStream_t s) {
     constexpr size_t LDS = (size_t)NS * (BM + BN) * BK * sizeof(bf16);
     static_assert(LDS * OCC <= 160 * 1024, "LDS budget");
-    auto k = gemm_mfma_kernel<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI, OUTBF, ACT, SPLIT>;
+    auto k = gemm_mfma_kernel<BM, BN, BK, NS, OCC, PIPE, WGM, WGN, AKC, BKC, EPI, OUTBF, ACT, SPLIT>;
     static bool attr = false;
     if (!attr) {
         (void)hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
@@ -585,56 +672,62 @@ static int out_bf(const Gemm& g) {
     return 1;
 }
 
-template <int BM, int BN, int BK, int NS, int OCC, bool RS, int WGM, int WGN, bool AKC, bool BKC>
+template <int BM, int BN, int BK, int NS, int OCC, int PIPE, int WGM, int WGN, bool AKC, bool BKC>
 static void run_main(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
     dim3 grid(ceil_div(g.N, BN) * ceil_div(g.M, BM), 1, p.splits);
     const int kps = ceil_div(ceil_div(g.K, p.splits), BK) * BK;
-    if (p.splits > 1) { launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_STORE, 0, 0, true>(g, grid, kps, part, s); return; }
+    if (p.splits > 1) { launch<BM, BN, BK, NS, OCC, PIPE, WGM, WGN, AKC, BKC, EPI_STORE, 0, 0, true>(g, grid, kps, part, s); return; }
     const bool relu = g.act == ACT_RELU2;
     switch (g.epi) {
         case EPI_STORE:
-            if (g.c_bf) launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_STORE, 1, 0, false>(g, grid, kps, part, s);
-            else launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_STORE, 0, 0, false>(g, grid, kps, part, s);
+            if (g.c_bf) launch<BM, BN, BK, NS, OCC, PIPE, WGM, WGN, AKC, BKC, EPI_STORE, 1, 0, false>(g, grid, kps, part, s);
+            else launch<BM, BN, BK, NS, OCC, PIPE, WGM, WGN, AKC, BKC, EPI_STORE, 0, 0, false>(g, grid, kps, part, s);
             break;
-        case EPI_BIAS: launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_BIAS, 1, 0, false>(g, grid, kps, part, s); break;
+        case EPI_BIAS: launch<BM, BN, BK, NS, OCC, PIPE, WGM, WGN, AKC, BKC, EPI_BIAS, 1, 0, false>(g, grid, kps, part, s); break;
         case EPI_BIAS_ACT:
-            if (relu) launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_BIAS_ACT, 1, ACT_RELU2, false>(g, grid, kps, part, s);
-            else launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_BIAS_ACT, 1, ACT_GELU, false>(g, grid, kps, part, s);
+            if (relu) launch<BM, BN, BK, NS, OCC, PIPE, WGM, WGN, AKC, BKC, EPI_BIAS_ACT, 1, ACT_RELU2, false>(g, grid, kps, part, s);
+            else launch<BM, BN, BK, NS, OCC, PIPE, WGM, WGN, AKC, BKC, EPI_BIAS_ACT, 1, ACT_GELU, false>(g, grid, kps, part, s);
             break;
         case EPI_BIAS_RESID:
-            launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_BIAS_RESID, 0, 0, false>(g, grid, kps, part, s);
+            launch<BM, BN, BK, NS, OCC, PIPE, WGM, WGN, AKC, BKC, EPI_BIAS_RESID, 0, 0, false>(g, grid, kps, part, s);
             break;
         case EPI_ACT_GRAD:
-            if (relu) launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_ACT_GRAD, 1, ACT_RELU2, false>(g, grid, kps, part, s);
-            else launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_ACT_GRAD, 1, ACT_GELU, false>(g, grid, kps, part, s);
+            if (relu) launch<BM, BN, BK, NS, OCC, PIPE, WGM, WGN, AKC, BKC, EPI_ACT_GRAD, 1, ACT_RELU2, false>(g, grid, kps, part, s);
+            else launch<BM, BN, BK, NS, OCC, PIPE, WGM, WGN, AKC, BKC, EPI_ACT_GRAD, 1, ACT_GELU, false>(g, grid, kps, part, s);
             break;
-        case EPI_ACCUM: launch<BM, BN, BK, NS, OCC, RS, WGM, WGN, AKC, BKC, EPI_ACCUM, 0, 0, false>(g, grid, kps, part, s); break;
+        case EPI_ACCUM: launch<BM, BN, BK, NS, OCC, PIPE, WGM, WGN, AKC, BKC, EPI_ACCUM, 0, 0, false>(g, grid, kps, part, s); break;
     }
 }
 
 template <bool AKC, bool BKC>
 static void run_cfg(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
     switch (p.cfg) {
-        case CFG_256_256: run_main<256, 256, 32, 4, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_256: run_main<128, 256, 32, 4, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_128: run_main<128, 128, 32, 4, 2, false, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_128: run_main<256, 128, 32, 3, 2, false, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_192: run_main<256, 192, 32, 4, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_256_K64: run_main<256, 256, 64, 2, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_192_K64: run_main<256, 192, 64, 2, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_128_K64: run_main<256, 128, 64, 3, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_192_K64: run_main<128, 192, 64, 2, 2, false, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_256_K64: run_main<128, 256, 64, 2, 1, false, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_128_K64: run_main<128, 128, 64, 2, 2, false, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_192_K64R: run_main<128, 192, 64, 2, 2, true, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_128_K64R: run_main<128, 128, 64, 2, 2, true, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_256_K64R: run_main<256, 256, 64, 2, 1, true, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_128_K64R: run_main<256, 128, 64, 2, 1, true, 2, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_256_K64W8: run_main<256, 256, 64, 2, 1, false, 2, 4, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_256_K64RW8: run_main<256, 256, 64, 2, 1, true, 2, 4, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_192_K64RW8: run_main<256, 192, 64, 2, 1, true, 4, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_256_128_K64RW8: run_main<256, 128, 64, 2, 1, true, 4, 2, AKC, BKC>(g, p, part, s); break;
-        case CFG_128_256_K64RW8: run_main<128, 256, 64, 2, 1, true, 2, 4, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256: run_main<256, 256, 32, 4, 1, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_256: run_main<128, 256, 32, 4, 1, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128: run_main<128, 128, 32, 4, 2, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128: run_main<256, 128, 32, 3, 2, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_192: run_main<256, 192, 32, 4, 1, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64: run_main<256, 256, 64, 2, 1, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_192_K64: run_main<256, 192, 64, 2, 1, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128_K64: run_main<256, 128, 64, 3, 1, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_192_K64: run_main<128, 192, 64, 2, 2, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_256_K64: run_main<128, 256, 64, 2, 1, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128_K64: run_main<128, 128, 64, 2, 2, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_192_K64R: run_main<128, 192, 64, 2, 2, PIPE_DMA_RS, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128_K64R: run_main<128, 128, 64, 2, 2, PIPE_DMA_RS, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64R: run_main<256, 256, 64, 2, 1, PIPE_DMA_RS, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128_K64R: run_main<256, 128, 64, 2, 1, PIPE_DMA_RS, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64W8: run_main<256, 256, 64, 2, 1, PIPE_DMA, 2, 4, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64RW8: run_main<256, 256, 64, 2, 1, PIPE_DMA_RS, 2, 4, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_192_K64RW8: run_main<256, 192, 64, 2, 1, PIPE_DMA_RS, 4, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_128_K64RW8: run_main<256, 128, 64, 2, 1, PIPE_DMA_RS, 4, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_256_K64RW8: run_main<128, 256, 64, 2, 1, PIPE_DMA_RS, 2, 4, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64VW8: run_main<256, 256, 64, 2, 1, PIPE_VGPR, 2, 4, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_192_K64V: run_main<128, 192, 64, 2, 2, PIPE_VGPR, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K64V: run_main<256, 256, 64, 2, 1, PIPE_VGPR, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_128_K64V: run_main<128, 128, 64, 2, 2, PIPE_VGPR, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_256_K32W8: run_main<256, 256, 32, 4, 1, PIPE_DMA, 2, 4, AKC, BKC>(g, p, part, s); break;
+        case CFG_128_192_K32: run_main<128, 192, 32, 4, 2, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
     }
 }
 
@@ -697,16 +790,16 @@ struct Tuned { int M, N, K; bool a_kc, b_kc; int cfg, splits; };
 static const Tuned tuned[] = {
     // forward: X W^T
     {16384, 2304, 768, true, true, CFG_128_192_K64, 1}, {16384, 768, 768, true, true, CFG_128_192_K64, 1},
-    {16384, 3072, 768, true, true, CFG_256_256_K64RW8, 1}, {16384, 768, 3072, true, true, CFG_128_192_K64, 1},
-    {16384, 50304, 768, true, true, CFG_256_256_K64RW8, 1},
+    {16384, 3072, 768, true, true, CFG_256_256_K64VW8, 1}, {16384, 768, 3072, true, true, CFG_128_192_K64, 1},
+    {16384, 50304, 768, true, true, CFG_256_256_K64VW8, 1},
     // input gradients: dY W
     {16384, 3072, 768, true, false, CFG_256_256_K64RW8, 1}, {16384, 768, 3072, true, false, CFG_128_192_K64R, 1},
     {16384, 768, 768, true, false, CFG_128_192_K64R, 1}, {16384, 768, 2304, true, false, CFG_128_192_K64R, 1},
-    {16384, 768, 50304, true, false, CFG_128_192_K64R, 1},
+    {16384, 768, 50304, true, false, CFG_256_256_K64VW8, 1},
     // weight gradients: dY^T X
-    {768, 3072, 16384, false, false, CFG_256_256_K64R, 6}, {3072, 768, 16384, false, false, CFG_256_256_K64R, 6},
-    {768, 768, 16384, false, false, CFG_128_128_K64R, 12}, {2304, 768, 16384, false, false, CFG_128_128_K64R, 4},
-    {50304, 768, 16384, false, false, CFG_256_256_K64RW8, 2},
+    {768, 3072, 16384, false, false, CFG_256_256_K64VW8, 6}, {3072, 768, 16384, false, false, CFG_256_256_K64VW8, 6},
+    {768, 768, 16384, false, false, CFG_128_128_K64R, 12}, {2304, 768, 16384, false, false, CFG_256_256_K64VW8, 8},
+    {50304, 768, 16384, false, false, CFG_256_256_K64VW8, 2},
 };
 
 GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
@@ -767,8 +860,8 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
     p.splits = bsplits;
     p.bm = (bsplits == 1 && g.epi == EPI_ACT_GRAD) ? cfg_bm[bcfg] : 0;
     const bool relu = bsplits == 1 && (g.epi == EPI_BIAS_ACT || g.epi == EPI_ACT_GRAD) && g.act == ACT_RELU2;
-    snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %s, %d, %d, %s, %s, %d, %d, %d, %s>",
-             cfg_bm[bcfg], cfg_bn[bcfg], cfg_bk[bcfg], cfg_ns[bcfg], cfg_occ[bcfg], cfg_rs[bcfg] ? "true" : "false",
+    snprintf(p.name, sizeof(p.name), "gemm_mfma_kernel<%d, %d, %d, %d, %d, %d, %d, %d, %s, %s, %d, %d, %d, %s>",
+             cfg_bm[bcfg], cfg_bn[bcfg], cfg_bk[bcfg], cfg_ns[bcfg], cfg_occ[bcfg], cfg_pipe[bcfg],
              cfg_wgm[bcfg], cfg_wgn[bcfg], g.a_kc ? "true" : "false", g.b_kc ? "true" : "false",
              bsplits > 1 ? 0 : g.epi, bsplits > 1 ? 0 : out_bf(g), relu ? 1 : 0, bsplits > 1 ? "true" : "false");
     return p;

@@ -435,10 +435,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_mfma_kernel(Gemm g, 
             const bool adv = t + 3 < nk;
 #pragma unroll
             for (int ks = 0; ks < KS - 1; ++ks) {
+                // copy q after product slot q * (P * (KS - 1)) / LPT of the tile's
+                // first KS - 1 steps: spread evenly, so that the CU's vector
+                // memory unit never receives every wave's copies at once
                 auto copy = [&](int p) {
 #pragma unroll
                     for (int q = 0; q < LPT; ++q)
-                        if (q / P == ks && q % P == p) {
+                        if ((q * P * (KS - 1) / LPT) / P == ks && (q * P * (KS - 1) / LPT) % P == p) {
                             swrite(q, st);
                             gload(q, adv);
                         }
@@ -799,7 +802,7 @@ static const Tuned tuned[] = {
     // weight gradients: dY^T X
     {768, 3072, 16384, false, false, CFG_256_256_K64VW8, 6}, {3072, 768, 16384, false, false, CFG_256_256_K64VW8, 6},
     {768, 768, 16384, false, false, CFG_128_128_K64R, 12}, {2304, 768, 16384, false, false, CFG_256_256_K64VW8, 8},
-    {50304, 768, 16384, false, false, CFG_256_256_K64VW8, 2},
+    {50304, 768, 16384, false, false, CFG_256_256_K64VW8, 1},
 };
 
 GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {

@@ -355,20 +355,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_mfma_kernel(Gemm g, 
             products<FM, FN>(acc, ra[0], rb[0], rd);
             bf16* st = smem + (issued % NS) * STAGE;
             const bool copy = issued < nk;
+            // copy q after product slot q * (P * (KS - 2)) / LPT of steps
+            // 1 .. KS-2: spread evenly, so that the CU's vector memory unit
+            // never receives every wave's copies at once
+            auto issue = [&](int slot) {
+                if (copy) {
+#pragma unroll
+                    for (int q = 0; q < LPT; ++q)
+                        if (q * P * (KS - 2) / LPT == slot) dma(q, st);
+                }
+            };
             auto refill = [&](int p) {
                 if (p == 0) {
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                     barrier_no_fence();
-                    if (copy) {
-#pragma unroll
-                        for (int q = 0; q < LPT; ++q) dma(q, st);
-                    }
                 }
+                issue(p);
             };
             products<FM, FN>(acc, ra[1], rb[1], refill);
-            if (copy) ++issued;
 #pragma unroll
-            for (int ks = 2; ks < KS - 1; ++ks) products<FM, FN>(acc, ra[ks], rb[ks], none);
+            for (int ks = 2; ks < KS - 1; ++ks)
+                products<FM, FN>(acc, ra[ks], rb[ks], [&](int p) { issue((ks - 1) * P + p); });
+            if (copy) ++issued;
             if (t + 1 < nk) wait_tile(t + 1);
             __builtin_amdgcn_sched_barrier(0);
             // on the last tile these reads see a stage that holds no new tile; the values are never used

@@ -119,6 +119,10 @@ struct Ws {
     void* dres_lp = nullptr;
     void* dln = nullptr;
     void *dh = nullptr, *dO = nullptr, *dqkv = nullptr;
+    // bf16 path: one copy per layer of dh and dqkv and one bf16 residual-
+    // gradient copy per LayerNorm backward call, so that the main stream never
+    // overwrites what a side-stream weight-gradient product still reads
+    void *dres_lp_all = nullptr, *dh_all = nullptr, *dqkv_all = nullptr;
     float* attD = nullptr;
     // row-pass partial sums of every LayerNorm backward and bias column sum of
     // a backward pass, reduced together at its end (reduce_jobs)
@@ -185,7 +189,12 @@ Ws plan(const gpt_config& c, const Table& tb, void* base) {
     w.logits = cv.take(ab * M * Vp);
     w.row_loss = cv.arr<float>(M);
     w.dres = cv.arr<float>(M * d);
-    if (bf) w.dres_lp = cv.take(ab * M * d);
+    if (bf) {
+        w.dres_lp = cv.take(ab * M * d);
+        w.dres_lp_all = cv.take(ab * M * d * (2 * L + 1));
+        w.dh_all = cv.take(ab * M * F * L);
+        w.dqkv_all = cv.take(ab * M * 3 * d * L);
+    }
     w.dln = cv.take(ab * M * d);   // gradient at a LayerNorm output (bf16 on the bf16 path)
     w.dh = cv.take(ab * M * F);
     w.dO = cv.take(ab * M * d);
@@ -698,7 +707,18 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         gk::Gemm g2 = mk_gemm(h, Vp, d, M, w.logits, Vp, false, w.lnf, d, false, G(h, tb.wte), d, false, gk::EPI_ACCUM);
         run_gemm(h, KC_GEMM_LMHEAD_BWD, g2);
     }
-    void* dR = bf ? w.dres_lp : (void*)w.dres;   // residual gradient as a matrix-product operand
+    // The weight-gradient products (they only read activations and upstream
+    // gradients) run on the side stream, overlapping the input-gradient chain.
+    // They read per-layer copies of dh, dqkv and the bf16 residual gradient,
+    // so the main stream never waits for them inside the pass, and they wait
+    // for two events per layer (after the MLP input gradient and after the
+    // attention backward): every event operation on the main stream costs
+    // about 12 us of idle GPU between its kernels. Not while per-class timing
+    // is on (its class totals assume one stream).
+    const bool conc = bf && h->timing_mask == 0;
+    // residual gradient as a matrix-product operand: its bf16 copy (per
+    // LayerNorm backward call while the side stream runs) or the fp32 buffer
+    void* dR = bf ? w.dres_lp : (void*)w.dres;
     // LayerNorm backward row passes and bias column sums leave their partial
     // sums in per-call slots; one reduce_jobs at the end of the pass sums them
     h->jobs.clear();
@@ -709,8 +729,8 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
                       float* db, float* dcol) {
         Timed t(h, KC_LN_BWD, 0, (double)M * d * ((overwrite ? 8 : 12) + 2 * ab) + 8.0 * M + 12.0 * nbl * d);
         float* part = w.ln_part + (size_t)(n_ln++) * w.ln_part_stride;
-        gk::layernorm_bwd_rows(bf, w.dln, bf, x, mean, rstd, g, w.dres, bf ? w.dres_lp : nullptr, overwrite, part, M, d,
-                               st);
+        if (conc) dR = (char*)w.dres_lp_all + (size_t)(n_ln - 1) * (size_t)ab * M * d;
+        gk::layernorm_bwd_rows(bf, w.dln, bf, x, mean, rstd, g, w.dres, bf ? dR : nullptr, overwrite, part, M, d, st);
         float* outs[3] = {dg, db, dcol};
         for (int q = 0; q < 3; ++q)
             if (outs[q]) h->jobs.push_back({part + (size_t)q * nbl * d, outs[q], nbl, d});
@@ -722,13 +742,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         h->jobs.push_back({part, out, npc, N});
     };
     ln_bwd(w.x_fin, meanf, rstdf, P(h, tb.lnf_w), true, G(h, tb.lnf_w), G(h, tb.lnf_b), G(h, tb.layers[L - 1].mp_b));
-    // The weight-gradient products (they only read activations and upstream
-    // gradients) run on the side stream, overlapping the input-gradient chain;
-    // events order them after their inputs and before the main stream
-    // overwrites those inputs. Not while per-class timing is on (its class
-    // totals assume one stream).
-    const bool conc = bf && h->timing_mask == 0;
-    enum { E_DR = 0, E_DH, E_DR2, E_DQKV, S_MP, S_FC, S_PROJ, S_QKV };
+    enum { E_DH = 0, E_DQKV, S_END };
     auto record = [&](int e, hipStream_t s_) { if (conc) (void)hipEventRecord(h->ev_dep[e], s_); };
     auto wait_ev = [&](hipStream_t s_, int e) { if (conc) (void)hipStreamWaitEvent(s_, h->ev_dep[e], 0); };
     hipStream_t sw = conc ? h->side : st;
@@ -740,10 +754,11 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         float* rstd2 = w.ln_rstd + (size_t)(2 * l + 1) * M;
         // MLP branch
         bool fc_b_fused = false;   // fc bias gradient from the dgrad epilogue's column sums
-        if (l < L - 1) wait_ev(st, S_FC);   // the previous layer's fc weight gradient has read dh
-        record(E_DR, st);
+        void* dh = conc ? (char*)w.dh_all + (size_t)l * (size_t)ab * M * F : w.dh;
+        void* dqkv = conc ? (char*)w.dqkv_all + (size_t)l * (size_t)ab * M * 3 * d : w.dqkv;
+        void* dR_mlp = dR;   // the mp products' operand (this layer's output gradient)
         {
-            gk::Gemm g = mk_gemm(h, M, F, d, dR, d, true, Wop(h, li.mp_w), F, false, w.dh, F, bf, gk::EPI_ACT_GRAD);
+            gk::Gemm g = mk_gemm(h, M, F, d, dR, d, true, Wop(h, li.mp_w), F, false, dh, F, bf, gk::EPI_ACT_GRAD);
             g.aux = w.hdact[l];
             const gk::GemmPlan pl = gk::gemm_plan(g, w.splitk_floats);
             if (pl.bm > 0) {
@@ -753,34 +768,24 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
             }
             run_gemm(h, KC_GEMM_DGRAD, g);
             record(E_DH, st);
-            wait_ev(sw, E_DR);
-            gk::Gemm g2 = mk_gemm(h, d, F, M, dR, d, false, w.hact[l], F, false, G(h, li.mp_w), F, false, gk::EPI_ACCUM);
+            wait_ev(sw, E_DH);
+            gk::Gemm g2 = mk_gemm(h, d, F, M, dR_mlp, d, false, w.hact[l], F, false, G(h, li.mp_w), F, false,
+                                  gk::EPI_ACCUM);
             run_gemm(h, KC_GEMM_WGRAD, g2, conc);
-            record(S_MP, sw);
         }
         {
-            gk::Gemm g = mk_gemm(h, M, d, F, w.dh, F, true, Wop(h, li.fc_w), d, false, w.dln, d, bf, gk::EPI_STORE);
+            gk::Gemm g = mk_gemm(h, M, d, F, dh, F, true, Wop(h, li.fc_w), d, false, w.dln, d, bf, gk::EPI_STORE);
             run_gemm(h, KC_GEMM_DGRAD, g);
-            wait_ev(sw, E_DH);
-            gk::Gemm g2 = mk_gemm(h, F, d, M, w.dh, F, false, w.ln2[l], d, false, G(h, li.fc_w), d, false, gk::EPI_ACCUM);
+            gk::Gemm g2 = mk_gemm(h, F, d, M, dh, F, false, w.ln2[l], d, false, G(h, li.fc_w), d, false, gk::EPI_ACCUM);
             run_gemm(h, KC_GEMM_WGRAD, g2, conc);
-            record(S_FC, sw);
         }
-        if (!fc_b_fused) {
-            wait_ev(st, S_FC);
-            col_sum(w.dh, F, G(h, li.fc_b));
-        }
-        wait_ev(st, S_MP);   // the mp weight gradient has read dR
+        if (!fc_b_fused) col_sum(dh, F, G(h, li.fc_b));
         ln_bwd(w.x_mid[l], mean2, rstd2, P(h, li.ln2_w), false, G(h, li.ln2_w), G(h, li.ln2_b), G(h, li.proj_b));
-        record(E_DR2, st);
+        void* dR_attn = dR;   // the proj products' operand
         // attention branch
         {
-            gk::Gemm g = mk_gemm(h, M, d, d, dR, d, true, Wop(h, li.proj_w), d, false, w.dO, d, bf, gk::EPI_STORE);
+            gk::Gemm g = mk_gemm(h, M, d, d, dR_attn, d, true, Wop(h, li.proj_w), d, false, w.dO, d, bf, gk::EPI_STORE);
             run_gemm(h, KC_GEMM_DGRAD, g);
-            wait_ev(sw, E_DR2);
-            gk::Gemm g2 = mk_gemm(h, d, d, M, dR, d, false, w.att[l], d, false, G(h, li.proj_w), d, false, gk::EPI_ACCUM);
-            run_gemm(h, KC_GEMM_WGRAD, g2, conc);
-            record(S_PROJ, sw);
         }
         const void *q = w.qkv[l], *k = (const char*)w.qkv[l] + (size_t)ab * d;
         int64_t ldq = 3 * d, ldk = 3 * d;
@@ -795,13 +800,12 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         a.ldq = ldq; a.ldk = ldk; a.ldv = 3 * d;
         a.o = w.att[l]; a.ldo = d; a.lse = w.lse[l]; a.bf = bf;
         a.dO = w.dO; a.lddo = d; a.D = w.attD; a.Dout = w.attD;
-        a.dq = w.dqkv; a.dk = (char*)w.dqkv + (size_t)ab * d; a.dv = (char*)w.dqkv + (size_t)ab * 2 * d; a.ldd = 3 * d;
+        a.dq = dqkv; a.dk = (char*)dqkv + (size_t)ab * d; a.dv = (char*)dqkv + (size_t)ab * 2 * d; a.ldd = 3 * d;
         // qkv bias gradient: column sums of dqkv, from the attention backward itself
         // unless the q/k transform still changes dq and dk afterwards
         float* qkv_part = w.cs_part + (size_t)(n_cs++) * w.cs_part_stride;
         bool attn_b_fused = false;
         if (!qkt) a.cpart = qkv_part;
-        if (l < L - 1) wait_ev(st, S_QKV);   // the previous layer's qkv weight gradient has read dqkv
         {
             double pairs = attn_pairs(B, T, H, a.window);
             Timed t(h, KC_ATTN_BWD, 8.0 * hd * pairs, (double)M * d * 8 * ab + 8.0 * M * H);
@@ -810,30 +814,32 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         if (attn_b_fused) h->jobs.push_back({qkv_part, G(h, li.attn_b), npa, 3 * d});
         if (qkt) {
             Timed t(h, KC_QK_PREP, 0, (double)M * 2 * d * 3 * ab);
-            gk::qk_prep_bwd(bf, w.qkv[l], w.dqkv, w.rope_cos, w.rope_sin, M, T, H, hd, c.qk_rmsnorm,
+            gk::qk_prep_bwd(bf, w.qkv[l], dqkv, w.rope_cos, w.rope_sin, M, T, H, hd, c.qk_rmsnorm,
                             c.pos_encoding == GPT_POS_ROPE, c.qk_norm_eps, st);
         }
         record(E_DQKV, st);
         {
-            gk::Gemm g = mk_gemm(h, M, d, 3 * d, w.dqkv, 3 * d, true, Wop(h, li.attn_w), d, false, w.dln, d, bf,
+            gk::Gemm g = mk_gemm(h, M, d, 3 * d, dqkv, 3 * d, true, Wop(h, li.attn_w), d, false, w.dln, d, bf,
                                  gk::EPI_STORE);
             run_gemm(h, KC_GEMM_DGRAD, g);
             wait_ev(sw, E_DQKV);
-            gk::Gemm g2 = mk_gemm(h, 3 * d, d, M, w.dqkv, 3 * d, false, w.ln1[l], d, false, G(h, li.attn_w), d, false,
+            gk::Gemm g2 = mk_gemm(h, d, d, M, dR_attn, d, false, w.att[l], d, false, G(h, li.proj_w), d, false,
                                   gk::EPI_ACCUM);
             run_gemm(h, KC_GEMM_WGRAD, g2, conc);
-            record(S_QKV, sw);
+            gk::Gemm g3 = mk_gemm(h, 3 * d, d, M, dqkv, 3 * d, false, w.ln1[l], d, false, G(h, li.attn_w), d, false,
+                                  gk::EPI_ACCUM);
+            run_gemm(h, KC_GEMM_WGRAD, g3, conc);
         }
         if (!attn_b_fused) {
             Timed t(h, KC_COLSUM, 0, (double)ab * M * 3 * d + 4.0 * npc * 3 * d);
-            gk::colsum_rows(bf, w.dqkv, 3 * d, M, 3 * d, qkv_part, st);
+            gk::colsum_rows(bf, dqkv, 3 * d, M, 3 * d, qkv_part, st);
             h->jobs.push_back({qkv_part, G(h, li.attn_b), npc, 3 * d});
         }
-        wait_ev(st, S_PROJ);   // the proj weight gradient has read dR
         ln_bwd(w.x_in[l], mean1, rstd1, P(h, li.ln1_w), false, G(h, li.ln1_w), G(h, li.ln1_b),
                l > 0 ? G(h, tb.layers[l - 1].mp_b) : nullptr);
     }
-    wait_ev(st, S_QKV);   // every side-stream product is done (the side stream runs in order)
+    record(S_END, sw);
+    wait_ev(st, S_END);   // every side-stream product is done (the side stream runs in order)
     if (!h->jobs.empty()) {
         auto same = [](const gk::RedJob& a, const gk::RedJob& b) {
             return a.part == b.part && a.out == b.out && a.np == b.np && a.n == b.n;

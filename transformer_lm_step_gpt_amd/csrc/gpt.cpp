@@ -701,12 +701,6 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         gk::mean_loss(w.row_loss, M, w.loss_last, w.loss_sum, st);
     }
     // ------------------------------------------------------------ backward
-    {
-        gk::Gemm g = mk_gemm(h, M, d, Vp, w.logits, Vp, true, Wop(h, tb.wte), d, false, w.dln, d, bf, gk::EPI_STORE);
-        run_gemm(h, KC_GEMM_LMHEAD_BWD, g);
-        gk::Gemm g2 = mk_gemm(h, Vp, d, M, w.logits, Vp, false, w.lnf, d, false, G(h, tb.wte), d, false, gk::EPI_ACCUM);
-        run_gemm(h, KC_GEMM_LMHEAD_BWD, g2);
-    }
     // The weight-gradient products (they only read activations and upstream
     // gradients) run on the side stream, overlapping the input-gradient chain.
     // They read per-layer copies of dh, dqkv and the bf16 residual gradient,
@@ -716,6 +710,20 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
     // about 12 us of idle GPU between its kernels. Not while per-class timing
     // is on (its class totals assume one stream).
     const bool conc = bf && h->timing_mask == 0;
+    enum { E_DH = 0, E_DQKV, E_DZ, S_END };
+    auto record = [&](int e, hipStream_t s_) { if (conc) (void)hipEventRecord(h->ev_dep[e], s_); };
+    auto wait_ev = [&](hipStream_t s_, int e) { if (conc) (void)hipStreamWaitEvent(s_, h->ev_dep[e], 0); };
+    hipStream_t sw = conc ? h->side : st;
+    {
+        // the tied head's weight gradient (dz^T lnf) goes to the side stream
+        // first, beside its input gradient and the layers' input-gradient chain
+        record(E_DZ, st);
+        wait_ev(sw, E_DZ);
+        gk::Gemm g2 = mk_gemm(h, Vp, d, M, w.logits, Vp, false, w.lnf, d, false, G(h, tb.wte), d, false, gk::EPI_ACCUM);
+        run_gemm(h, KC_GEMM_LMHEAD_BWD, g2, conc);
+        gk::Gemm g = mk_gemm(h, M, d, Vp, w.logits, Vp, true, Wop(h, tb.wte), d, false, w.dln, d, bf, gk::EPI_STORE);
+        run_gemm(h, KC_GEMM_LMHEAD_BWD, g);
+    }
     // residual gradient as a matrix-product operand: its bf16 copy (per
     // LayerNorm backward call while the side stream runs) or the fp32 buffer
     void* dR = bf ? w.dres_lp : (void*)w.dres;
@@ -742,10 +750,6 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         h->jobs.push_back({part, out, npc, N});
     };
     ln_bwd(w.x_fin, meanf, rstdf, P(h, tb.lnf_w), true, G(h, tb.lnf_w), G(h, tb.lnf_b), G(h, tb.layers[L - 1].mp_b));
-    enum { E_DH = 0, E_DQKV, S_END };
-    auto record = [&](int e, hipStream_t s_) { if (conc) (void)hipEventRecord(h->ev_dep[e], s_); };
-    auto wait_ev = [&](hipStream_t s_, int e) { if (conc) (void)hipStreamWaitEvent(s_, h->ev_dep[e], 0); };
-    hipStream_t sw = conc ? h->side : st;
     for (int l = L - 1; l >= 0; --l) {
         const LayerIdx& li = tb.layers[l];
         float* mean1 = w.ln_mean + (size_t)(2 * l) * M;

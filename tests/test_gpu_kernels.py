@@ -213,7 +213,7 @@ def test_gemm_act_grad_colsum(lib, shape, bf):
     _gemm_colsum_case(lib, M, N, K, bf, M + N + K)
 
 
-@pytest.mark.parametrize("cfg", list(range(26)))
+@pytest.mark.parametrize("cfg", list(range(27)))
 def test_gemm_act_grad_colsum_every_config(lib, cfg):
     if cfg >= lib.gptk_gemm_num_configs():
         pytest.skip("no such configuration")

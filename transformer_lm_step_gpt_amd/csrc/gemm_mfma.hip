@@ -647,19 +647,20 @@ enum GemmCfg {
     // copies staged through registers (PIPE_VGPR)
     CFG_256_256_K64VW8, CFG_128_192_K64V, CFG_256_256_K64V, CFG_128_128_K64V,
     // four stages of 32-deep k-tiles (three copies in flight)
-    CFG_256_256_K32W8, CFG_128_192_K32, CFG_COUNT
+    CFG_256_256_K32W8, CFG_128_192_K32,
+    CFG_256_192_K64VW8, CFG_COUNT
 };
 static const int cfg_bm[CFG_COUNT] = {256, 128, 128, 256, 256, 256, 256, 256, 128, 128, 128, 128, 128,
-                                      256, 256, 256, 256, 256, 256, 128, 256, 128, 256, 128, 256, 128};
+                                      256, 256, 256, 256, 256, 256, 128, 256, 128, 256, 128, 256, 128, 256};
 static const int cfg_bn[CFG_COUNT] = {256, 256, 128, 128, 192, 256, 192, 128, 192, 256, 128, 192, 128,
-                                      256, 128, 256, 256, 192, 128, 256, 256, 192, 256, 128, 256, 192};
+                                      256, 128, 256, 256, 192, 128, 256, 256, 192, 256, 128, 256, 192, 192};
 static const int cfg_bk[CFG_COUNT] = {32, 32, 32, 32, 32, 64, 64, 64, 64, 64, 64, 64, 64,
-                                      64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 32, 32};
-static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4};
-static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1, 2, 1, 2, 2, 2, 1, 1, 1, 1, 1, 1, 1, 1, 2, 1, 2, 1, 2};
-static const int cfg_pipe[CFG_COUNT] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 1, 1, 1, 0, 1, 1, 1, 1, 2, 2, 2, 2, 0, 0};
-static const int cfg_wgm[CFG_COUNT] = {2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4, 2, 2, 2, 2, 2, 2, 2};
-static const int cfg_wgn[CFG_COUNT] = {2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4, 2, 2, 4, 4, 2, 2, 2, 4, 2};
+                                      64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 64, 32, 32, 64};
+static const int cfg_ns[CFG_COUNT] = {4, 4, 4, 3, 4, 2, 2, 3, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4, 2};
+static const int cfg_occ[CFG_COUNT] = {1, 1, 2, 2, 1, 1, 1, 1, 2, 1, 2, 2, 2, 1, 1, 1, 1, 1, 1, 1, 1, 2, 1, 2, 1, 2, 1};
+static const int cfg_pipe[CFG_COUNT] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 1, 1, 1, 0, 1, 1, 1, 1, 2, 2, 2, 2, 0, 0, 2};
+static const int cfg_wgm[CFG_COUNT] = {2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4, 2, 2, 2, 2, 2, 2, 2, 4};
+static const int cfg_wgn[CFG_COUNT] = {2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 2, 4, 4, 2, 2, 4, 4, 2, 2, 2, 4, 2, 2};
 
 template <int BM, int BN, int BK, int NS, int OCC, int PIPE, int WGM, int WGN, bool AKC, bool BKC, int EPI, int OUTBF,
           int ACT, bool SPLIT>
@@ -739,6 +740,7 @@ static void run_cfg(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s
         case CFG_128_128_K64V: run_main<128, 128, 64, 2, 2, PIPE_VGPR, 2, 2, AKC, BKC>(g, p, part, s); break;
         case CFG_256_256_K32W8: run_main<256, 256, 32, 4, 1, PIPE_DMA, 2, 4, AKC, BKC>(g, p, part, s); break;
         case CFG_128_192_K32: run_main<128, 192, 32, 4, 2, PIPE_DMA, 2, 2, AKC, BKC>(g, p, part, s); break;
+        case CFG_256_192_K64VW8: run_main<256, 192, 64, 2, 1, PIPE_VGPR, 4, 2, AKC, BKC>(g, p, part, s); break;
     }
 }
 
@@ -800,12 +802,12 @@ static int num_cus() {
 struct Tuned { int M, N, K; bool a_kc, b_kc; int cfg, splits; };
 static const Tuned tuned[] = {
     // forward: X W^T
-    {16384, 2304, 768, true, true, CFG_128_192_K64, 1}, {16384, 768, 768, true, true, CFG_128_192_K64, 1},
+    {16384, 2304, 768, true, true, CFG_256_192_K64VW8, 1}, {16384, 768, 768, true, true, CFG_128_192_K64, 1},
     {16384, 3072, 768, true, true, CFG_256_256_K64VW8, 1}, {16384, 768, 3072, true, true, CFG_128_192_K64, 1},
     {16384, 50304, 768, true, true, CFG_256_256_K64VW8, 1},
     // input gradients: dY W
-    {16384, 3072, 768, true, false, CFG_256_256_K64RW8, 1}, {16384, 768, 3072, true, false, CFG_128_192_K64R, 1},
-    {16384, 768, 768, true, false, CFG_128_192_K64R, 1}, {16384, 768, 2304, true, false, CFG_128_192_K64R, 1},
+    {16384, 3072, 768, true, false, CFG_256_256_K64VW8, 1}, {16384, 768, 3072, true, false, CFG_128_192_K64R, 1},
+    {16384, 768, 768, true, false, CFG_256_192_K64VW8, 1}, {16384, 768, 2304, true, false, CFG_128_192_K64R, 1},
     {16384, 768, 50304, true, false, CFG_256_256_K64VW8, 1},
     // weight gradients: dY^T X
     {768, 3072, 16384, false, false, CFG_256_256_K64VW8, 6}, {3072, 768, 16384, false, false, CFG_256_256_K64VW8, 6},

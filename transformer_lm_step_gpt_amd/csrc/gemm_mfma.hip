@@ -408,14 +408,25 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_mfma_kernel(Gemm g, 
         // write): a load for a k-tile past the last one reads the last
         // k-tile again (the pointers stop advancing there) and its LDS write
         // goes to a stage that is no longer read.
+        // Buffer loads: one scalar descriptor per operand and a 32-bit byte
+        // offset per copy (the host keeps this mode to operands spanning less
+        // than 2 GiB) instead of a 64-bit address per lane and copy.
         u32x4 cp[LPT];
+        const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0x7fffffff, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, 0x7fffffff, 0x00020000);
+        int offA[PA], offB[PB];
+#pragma unroll
+        for (int q = 0; q < PA; ++q) offA[q] = (int)((const char*)srcA[q] - (const char*)A);
+#pragma unroll
+        for (int q = 0; q < PB; ++q) offB[q] = (int)((const char*)srcB[q] - (const char*)B);
+        const int bstA = (int)(2 * stA), bstB = (int)(2 * stB);
         auto gload = [&](int q, bool adv) {
             if (q < PA) {
-                cp[q] = *reinterpret_cast<const u32x4*>(srcA[q]);
-                srcA[q] += adv ? stA : 0;
+                cp[q] = __builtin_amdgcn_raw_buffer_load_b128(rA, offA[q], 0, 0);
+                offA[q] += adv ? bstA : 0;
             } else {
-                cp[q] = *reinterpret_cast<const u32x4*>(srcB[q - PA]);
-                srcB[q - PA] += adv ? stB : 0;
+                cp[q] = __builtin_amdgcn_raw_buffer_load_b128(rB, offB[q - PA], 0, 0);
+                offB[q - PA] += adv ? bstB : 0;
             }
         };
         auto swrite = [&](int q, bf16* st) {
@@ -867,6 +878,21 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
         bcfg = g.K % cfg_bk[fcfg] ? CFG_256_256 : fcfg;
         bsplits = fsplits > 0 ? fsplits : 1;
         while (bsplits > 1 && ((size_t)bsplits * mn > nscratch || g.K / bsplits < 256)) --bsplits;
+    }
+    // copies through registers address the operands with 32-bit byte offsets
+    if (cfg_pipe[bcfg] == 2) {
+        auto span = [](bool kc, int rows, int k, int64_t ld) {
+            return 2 * (kc ? (int64_t)(rows - 1) * ld + k : (int64_t)(k - 1) * ld + rows);
+        };
+        if (span(g.a_kc, g.M, g.K, g.lda) >= ((int64_t)1 << 31) || span(g.b_kc, g.N, g.K, g.ldb) >= ((int64_t)1 << 31)) {
+            switch (bcfg) {
+                case CFG_256_256_K64VW8: bcfg = CFG_256_256_K64RW8; break;
+                case CFG_256_192_K64VW8: bcfg = CFG_256_192_K64RW8; break;
+                case CFG_128_192_K64V: bcfg = CFG_128_192_K64R; break;
+                case CFG_256_256_K64V: bcfg = CFG_256_256_K64R; break;
+                default: bcfg = CFG_128_128_K64R; break;
+            }
+        }
     }
     GemmPlan p{};
     p.cfg = bcfg;

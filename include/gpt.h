@@ -133,7 +133,9 @@ gpt_status gpt_create(const gpt_config* cfg, uint64_t seed, void* d_workspace,
 /* Release host-side state. The workspace stays the caller's. */
 gpt_status gpt_destroy(gpt_handle* h);
 
-/* Run later calls on another stream (for example torch's current stream). */
+/* Run later calls on another stream (for example torch's current stream). Switching
+ * to a different stream first waits for the kernel-timing events pending on the old
+ * one; passing the current stream again does nothing. */
 gpt_status gpt_set_stream(gpt_handle* h, void* stream);
 
 /* One micro-step: forward pass, mean cross-entropy over the B*T positions

@@ -574,7 +574,10 @@ gpt_status gpt_destroy(gpt_handle* h) {
 
 gpt_status gpt_set_stream(gpt_handle* h, void* stream) {
     if (!h) return GPT_ERR_INVALID_ARGUMENT;
-    drain_timing(h);
+    // pending timing events were recorded on the old stream: collect them
+    // before switching (not on every call with the same stream, which would
+    // make the host wait for the GPU between a step's calls)
+    if ((hipStream_t)stream != h->stream) drain_timing(h);
     h->stream = (hipStream_t)stream;
     return GPT_OK;
 }

@@ -821,8 +821,8 @@ static const Tuned tuned[] = {
     {16384, 768, 768, true, false, CFG_256_192_K64VW8, 1}, {16384, 768, 2304, true, false, CFG_128_192_K64R, 1},
     {16384, 768, 50304, true, false, CFG_256_256_K64VW8, 1},
     // weight gradients: dY^T X
-    {768, 3072, 16384, false, false, CFG_256_256_K64VW8, 6}, {3072, 768, 16384, false, false, CFG_256_256_K64VW8, 6},
-    {768, 768, 16384, false, false, CFG_128_128_K64R, 12}, {2304, 768, 16384, false, false, CFG_256_256_K64VW8, 8},
+    {768, 3072, 16384, false, false, CFG_256_256_K64VW8, 4}, {3072, 768, 16384, false, false, CFG_256_256_K64VW8, 4},
+    {768, 768, 16384, false, false, CFG_128_128_K64R, 8}, {2304, 768, 16384, false, false, CFG_256_256_K64VW8, 6},
     {50304, 768, 16384, false, false, CFG_256_256_K64VW8, 1},
 };
 

@@ -13,6 +13,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace gk {
 
 // =====================================================================
@@ -837,7 +839,9 @@ typedef uint32_t ce_u32x4 __attribute__((ext_vector_type(4)));
 GPT_DEV float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 GPT_DEV float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-template <int CPT>
+// CAP: logit softcap on (a template parameter, so the plain path does not
+// carry the capped path's registers)
+template <int CPT, bool CAP>
 __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const int32_t* y, float* row_loss, int Vp,
                                                                 float gscale, float cap, int32_t* err) {
     __shared__ float sred[8];
@@ -846,7 +850,7 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
     const int nch = Vp >> 3;
     const int tgt = y[row];
     const bool valid = tgt >= 0 && tgt < Vp;
-    const float icap = cap > 0.f ? 1.0f / cap : 0.f;
+    const float icap = CAP ? 1.0f / cap : 0.f;
     const float L2E = 1.4426950408889634f;
     ce_u32x4 v[CPT];
 #pragma unroll
@@ -859,7 +863,7 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
         const uint32_t wd = v[c][e >> 1];
         return (e & 1) ? bf_hi(wd) : bf_lo(wd);
     };
-    auto capped = [&](float x) { return cap > 0.f ? cap * tanh_exp2(x * icap) : x; };
+    auto capped = [&](float x) { return CAP ? cap * tanh_exp2(x * icap) : x; };
     // the target logit, read before any thread overwrites the row (the barriers
     // below wait for it)
     const float zt_raw = (tid == 0 && valid) ? (float)zr[tgt] : 0.f;
@@ -870,13 +874,17 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
         if (tid + 256 * c < nch)
 #pragma unroll
             for (int e = 0; e < 8; e += 2) mx = fmaxf(mx, fmaxf(raw(c, e), raw(c, e + 1)));
+    // the unpacked logits of this pass are recomputed in the next one rather
+    // than kept live across it (200 floats per thread would halve occupancy)
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) asm volatile("" : "+v"(v[c]));
     mx = wave_max(mx);
     if (lane == 0) sred[w] = mx;
     __syncthreads();
     const float gm = capped(fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]))) * L2E;   // log2 units
     // pass 2: sum of exp (log2 units: 2^(x log2 e - gm))
     float sm = 0.f;
-    if (cap > 0.f) {
+    if constexpr (CAP) {
 #pragma unroll
         for (int c = 0; c < CPT; ++c)
             if (tid + 256 * c < nch)
@@ -916,7 +924,7 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
         const int idx = tid + 256 * c;
         if (idx >= nch) continue;
         ce_u32x4 o;
-        if (!(cap > 0.f)) {
+        if constexpr (!CAP) {
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
                 const bf16 lo = (bf16)(bf_lo(v[c][e2]) * rescale), hi = (bf16)(bf_hi(v[c][e2]) * rescale);
@@ -931,7 +939,7 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const float x = raw(c, 2 * e2 + h);
-                if (cap > 0.f) {
+                if constexpr (CAP) {
                     const float th = tanh_exp2(x * icap);
                     gpair[h] = __builtin_amdgcn_exp2f(fmaf(cap * th, L2E, -lse2)) * gs * (1.0f - th * th);
                 } else {
@@ -950,10 +958,10 @@ __global__ __launch_bounds__(256) void cross_entropy_reg_kernel(bf16* z, const i
         float loss = 0.f;
         if (valid) {
             float th = 0.f, zt = zt_raw;
-            if (cap > 0.f) { th = tanh_exp2(zt * icap); zt = cap * th; }
+            if constexpr (CAP) { th = tanh_exp2(zt * icap); zt = cap * th; }
             loss = lse2 * 0.6931471805599453f - zt;
             float g = (__builtin_amdgcn_exp2f(fmaf(zt, L2E, -lse2)) - 1.0f) * gscale;
-            if (cap > 0.f) g *= 1.0f - th * th;
+            if constexpr (CAP) g *= 1.0f - th * th;
             zr[tgt] = (bf16)g;
         } else {
             *err = 1;
@@ -968,11 +976,16 @@ void cross_entropy(bool bf, void* z, const int32_t* y, float* row_loss, int M, i
     if (bf && Vp % 8 == 0 && ((uintptr_t)z % 16) == 0 && nch <= 32 * 256) {
         const int cpt = ceil_div(nch, 256);
         bf16* zb = (bf16*)z;
-        if (cpt <= 4) cross_entropy_reg_kernel<4><<<M, 256, 0, s>>>(zb, y, row_loss, Vp, gscale, cap, err);
-        else if (cpt <= 8) cross_entropy_reg_kernel<8><<<M, 256, 0, s>>>(zb, y, row_loss, Vp, gscale, cap, err);
-        else if (cpt <= 16) cross_entropy_reg_kernel<16><<<M, 256, 0, s>>>(zb, y, row_loss, Vp, gscale, cap, err);
-        else if (cpt <= 25) cross_entropy_reg_kernel<25><<<M, 256, 0, s>>>(zb, y, row_loss, Vp, gscale, cap, err);
-        else cross_entropy_reg_kernel<32><<<M, 256, 0, s>>>(zb, y, row_loss, Vp, gscale, cap, err);
+        auto run = [&](auto cpt_c) {
+            constexpr int C = decltype(cpt_c)::value;
+            if (cap > 0.f) cross_entropy_reg_kernel<C, true><<<M, 256, 0, s>>>(zb, y, row_loss, Vp, gscale, cap, err);
+            else cross_entropy_reg_kernel<C, false><<<M, 256, 0, s>>>(zb, y, row_loss, Vp, gscale, cap, err);
+        };
+        if (cpt <= 4) run(std::integral_constant<int, 4>{});
+        else if (cpt <= 8) run(std::integral_constant<int, 8>{});
+        else if (cpt <= 16) run(std::integral_constant<int, 16>{});
+        else if (cpt <= 25) run(std::integral_constant<int, 25>{});
+        else run(std::integral_constant<int, 32>{});
         return;
     }
     if (bf) cross_entropy_kernel<bf16><<<M, 256, 0, s>>>((bf16*)z, y, row_loss, Vp, gscale, cap, err);

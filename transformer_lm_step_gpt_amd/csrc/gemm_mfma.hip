@@ -817,8 +817,8 @@ static const Tuned tuned[] = {
     {16384, 3072, 768, true, true, CFG_256_256_K64VW8, 1}, {16384, 768, 3072, true, true, CFG_128_192_K64, 1},
     {16384, 50304, 768, true, true, CFG_256_256_K64VW8, 1},
     // input gradients: dY W
-    {16384, 3072, 768, true, false, CFG_256_256_K64VW8, 1}, {16384, 768, 3072, true, false, CFG_128_192_K64R, 1},
-    {16384, 768, 768, true, false, CFG_256_192_K64VW8, 1}, {16384, 768, 2304, true, false, CFG_128_192_K64R, 1},
+    {16384, 3072, 768, true, false, CFG_256_256_K64VW8, 1}, {16384, 768, 3072, true, false, CFG_256_192_K64VW8, 1},
+    {16384, 768, 768, true, false, CFG_256_192_K64VW8, 1}, {16384, 768, 2304, true, false, CFG_256_192_K64VW8, 1},
     {16384, 768, 50304, true, false, CFG_256_256_K64VW8, 1},
     // weight gradients: dY^T X
     {768, 3072, 16384, false, false, CFG_256_256_K64VW8, 4}, {3072, 768, 16384, false, false, CFG_256_256_K64VW8, 4},

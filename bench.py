@@ -159,7 +159,7 @@ def main():
         copy_calibration()
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for {a.gpus}); the multi-GPU data-parallel "
+        print(f"bench.py: the step runs on exactly one GPU (asked for {a.gpus}); the multi-GPU data-parallel "
               "path is a design, not an implementation.", file=sys.stderr)
         sys.exit(2)
 

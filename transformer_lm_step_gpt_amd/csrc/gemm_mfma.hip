@@ -4,13 +4,14 @@
 // lecture notes' "Раздел 2. Сделаем быстро", rebuilt for CDNA4).
 //
 // Structure
-//   * 256 threads = 4 wavefronts in a 2 x 2 grid; each wavefront owns a
-//     (BM/2) x (BN/2) sub-tile made of 32x32 MFMA fragments.
-//   * Global -> LDS copies use the 16-byte LDS-DMA load (each lane's 16
-//     bytes land at LDS base + 16 * lane), so no registers are spent on
+//   * 4 or 8 wavefronts in a WGM x WGN grid; each wavefront owns a
+//     (BM/WGM) x (BN/WGN) sub-tile made of 32x32 MFMA fragments.
+//   * Global -> LDS copies either use the 16-byte LDS-DMA load (each lane's
+//     16 bytes land at LDS base + 16 * lane), so no registers are spent on
 //     staging, and a k-tile is copied as soon as its stage is free (a ring of
 //     NS LDS stages; a k-tile is waited for with s_waitcnt vmcnt only when
-//     consumed).
+//     consumed), or go through registers (16-byte buffer loads one k-tile
+//     ahead, ds_write_b128 into the same LDS layout): see PIPE below.
 //   * An operand stored k-contiguous (X and W of X W^T) is kept as a
 //     [row][BK] tile; a fragment (8 consecutive k of one row per lane) is one
 //     16-byte LDS read.

@@ -230,6 +230,66 @@ def test_rope_properties():
     assert np.allclose((O.rope_bwd(dy, cos, sin) * q).sum(), (dy * qr).sum())
 
 
+# RoPE values fixed by the rotary definition (Su et al., "RoFormer: Enhanced
+# Transformer with Rotary Position Embedding", 2021, section 3.2.2): pair i of
+# a head of width hd turns by the angle t * theta_i at position t, with
+# theta_i = 10000^(-2i/hd) for i = 0 .. hd/2 - 1, through the plane rotation
+# [[cos, -sin], [sin, cos]]. The oracle pairs component i with i + hd/2
+# (rotate-half; RoFormer itself pairs neighbours, a fixed permutation of the
+# head components). Literals below are worked out by hand:
+#   hd = 128: theta_1 = 10^(4 * -2/128) = 10^(-1/16) = 0.8659643233600653,
+#             theta_63 = 10^(-4 * 126/128) = 10^(-3.9375) = 1.1547819846894582e-4
+#   hd = 4, base 100: theta_0 = 1, theta_1 = 100^(-1/2) = 0.1
+def _rope_pin_violations(tables, fwd):
+    bad = []
+    cos, sin = tables(5, 128, 10000.0)
+    if not np.isclose(np.arctan2(sin[1, 1], cos[1, 1]), 0.8659643233600653, rtol=0, atol=1e-12):
+        bad.append("theta_1 at hd 128")
+    if not np.isclose(np.arctan2(sin[1, 63], cos[1, 63]), 1.1547819846894582e-4, rtol=1e-9, atol=0):
+        bad.append("theta_63 at hd 128")
+    if not np.isclose(np.arctan2(sin[3, 1], cos[3, 1]), 3 * 0.8659643233600653, rtol=0, atol=1e-12):
+        bad.append("angle grows linearly with position")
+    # basis vectors at position t = 3, hd = 4, base 100: e0 -> cos 3 e0 + sin 3 e2,
+    # e2 -> -sin 3 e0 + cos 3 e2, e1 -> cos 0.3 e1 + sin 0.3 e3
+    c4, s4 = tables(4, 4, 100.0)
+    rot = fwd(np.eye(4), np.repeat(c4[3:4], 4, 0), np.repeat(s4[3:4], 4, 0))
+    want = np.array([[-0.9899924966004454, 0.0, 0.1411200080598672, 0.0],
+                     [0.0, 0.955336489125606, 0.0, 0.29552020666133955],
+                     [-0.1411200080598672, 0.0, -0.9899924966004454, 0.0],
+                     [0.0, -0.29552020666133955, 0.0, 0.955336489125606]])
+    if not np.allclose(rot, want, rtol=0, atol=1e-12):
+        bad.append("rotate-half pairing and rotation sense at hd 4")
+    return bad
+
+
+def test_rope_pinned_to_rotary_definition():
+    assert _rope_pin_violations(O.rope_tables, O.rope_fwd) == []
+
+
+def test_rope_pin_rejects_plausible_mistakes():
+    """The pin above fails for the two readings it must tell apart: the
+    exponent -i/hd instead of -2i/hd, and neighbour pairing instead of
+    rotate-half (mistakes planted in local copies, not in the oracle)."""
+    def tables_half_exponent(T, hd, base):
+        inv = base ** (-1.0 * np.arange(hd // 2) / hd)
+        ang = np.arange(T)[:, None] * inv[None, :]
+        return np.cos(ang), np.sin(ang)
+
+    def fwd_neighbour_pairs(x, cos, sin):
+        a, b = x[..., 0::2], x[..., 1::2]
+        out = np.empty_like(x)
+        out[..., 0::2] = a * cos - b * sin
+        out[..., 1::2] = a * sin + b * cos
+        return out
+
+    def fwd_reverse_sense(x, cos, sin):
+        return O.rope_fwd(x, cos, -sin)
+
+    assert "theta_1 at hd 128" in _rope_pin_violations(tables_half_exponent, O.rope_fwd)
+    assert _rope_pin_violations(O.rope_tables, fwd_neighbour_pairs)
+    assert _rope_pin_violations(O.rope_tables, fwd_reverse_sense)
+
+
 def test_cross_entropy_vs_torch_and_closed_form():
     rng = np.random.default_rng(6)
     M, V = 9, 17

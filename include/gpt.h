@@ -149,8 +149,9 @@ gpt_status gpt_set_stream(gpt_handle* h, void* stream);
  * Errors: INVALID_ARGUMENT (null handle or buffers, B < 1, B > max_batch,
  * T < 1, T > block_size -- the pages' "longer than block_size" failure),
  * TOKEN_RANGE (an id outside [0, padded_vocab_size); detected on the device,
- * reported by the first call that waits for the stream; the offending
- * positions contribute zero), DEVICE. */
+ * reported by the first call that waits for the stream, which clears the
+ * flag; the offending positions contribute zero, and every gpt_clip_and_adamw
+ * while the flag is set leaves parameters and moments unchanged), DEVICE. */
 gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* d_tokens,
                                 const int32_t* d_targets, int32_t B, int32_t T,
                                 float grad_scale, float* h_loss);
@@ -170,7 +171,10 @@ gpt_status gpt_loss_accum(gpt_handle* h, float* h_mean_loss);
  * call waits and returns the pre-clip norm n.
  * Errors: INVALID_ARGUMENT (step < 1, lr < 0 or not finite), NONFINITE
  * (n is not finite: parameters and moments are left unchanged; reported
- * when the call waits, i.e. with h_grad_norm non-null), DEVICE. */
+ * when the call waits, i.e. with h_grad_norm non-null), TOKEN_RANGE (a
+ * micro-step since the last report saw an out-of-range token or target id:
+ * the update is skipped on the device; reported and cleared when the call
+ * waits), DEVICE. */
 gpt_status gpt_clip_and_adamw(gpt_handle* h, float lr, int32_t step, float* h_grad_norm);
 
 /* Parameter table: tensor names follow the lecture's Hugging-Face names

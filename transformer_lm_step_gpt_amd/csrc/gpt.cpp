@@ -910,7 +910,7 @@ gpt_status gpt_clip_and_adamw(gpt_handle* h, float lr, int32_t step, float* h_gr
     }
     {
         Timed t(h, KC_GRAD_NORM, 0, 4.0 * n);
-        gk::grad_norm(w.grads, n, w.gn_partial, w.gnorm, w.coef, w.nonfinite, c.max_grad_norm, h->stream);
+        gk::grad_norm(w.grads, n, w.gn_partial, w.gnorm, w.coef, w.nonfinite, w.err, c.max_grad_norm, h->stream);
     }
     double b1 = c.beta1, b2 = c.beta2;
     float rbc1 = (float)(1.0 / (1.0 - std::pow(b1, step)));
@@ -924,11 +924,19 @@ gpt_status gpt_clip_and_adamw(gpt_handle* h, float lr, int32_t step, float* h_gr
     gpt_status s = hip_check(h, hipGetLastError(), "kernel launch");
     if (s != GPT_OK) return s;
     if (h_grad_norm) {
-        s = hip_check(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
+        // an out-of-range id (flagged on the device by a micro-step that did
+        // not wait) has already made the device skip this update
+        s = sync_and_check(h);
+        if (s == GPT_ERR_TOKEN_RANGE) {
+            (void)hipMemcpy(h_grad_norm, w.gnorm, sizeof(float), hipMemcpyDeviceToHost);
+            return fail(h, GPT_ERR_TOKEN_RANGE,
+                        "a token or target id is outside [0, padded_vocab_size): update skipped");
+        }
         if (s != GPT_OK) return s;
         int32_t nf = 0;
-        (void)hipMemcpy(h_grad_norm, w.gnorm, sizeof(float), hipMemcpyDeviceToHost);
-        (void)hipMemcpy(&nf, w.nonfinite, sizeof(int32_t), hipMemcpyDeviceToHost);
+        s = hip_check(h, hipMemcpy(h_grad_norm, w.gnorm, sizeof(float), hipMemcpyDeviceToHost), "read grad norm");
+        if (s == GPT_OK) s = hip_check(h, hipMemcpy(&nf, w.nonfinite, sizeof(int32_t), hipMemcpyDeviceToHost), "read flag");
+        if (s != GPT_OK) return s;
         if (nf) return fail(h, GPT_ERR_NONFINITE, "gradient norm is not finite: update skipped");
     }
     return GPT_OK;

@@ -103,12 +103,13 @@ void qk_prep_bwd(bool bf, const void* qkv, void* dqkv, const float* cos_t, const
                  int H, int hd, int norm, int rope, float eps, hipStream_t s);
 
 // ---------------------------------------------------------------- optimiser
-// norm = sqrt(sum g^2); coef = min(1, max_norm / (norm + 1e-6)); flag non-finite.
+// norm = sqrt(sum g^2); coef = min(1, max_norm / (norm + 1e-6)); *skip = 1 when
+// the norm is not finite or *id_err (nullable) is set, else 0.
 // partial needs 1024 doubles.
 void grad_norm(const float* g, int64_t n, double* partial, float* norm_out, float* coef_out,
-               int32_t* nonfinite, float max_norm, hipStream_t s);
+               int32_t* skip, const int32_t* id_err, float max_norm, hipStream_t s);
 // AdamW over the flat buffers; elements [0, n_decay) are decayed and mirrored
-// to the bf16 copy wbf (if non-null). Skips everything when *nonfinite.
+// to the bf16 copy wbf (if non-null). Skips everything when *skip.
 void adamw(float* p, const float* g, float* m, float* v, void* wbf, int64_t n, int64_t n_decay,
            const float* coef, const int32_t* nonfinite, float lr, float b1, float b2, float eps, float wd,
            float rbc1, float rbc2, hipStream_t s);

@@ -1141,7 +1141,7 @@ __global__ __launch_bounds__(256) void grad_norm_partial_kernel(const float* g, 
 }
 
 __global__ __launch_bounds__(256) void grad_norm_final_kernel(const double* part, float* norm_out, float* coef_out,
-                                                              int32_t* nonfinite, float max_norm) {
+                                                              int32_t* skip, const int32_t* id_err, float max_norm) {
     __shared__ double sh[4];
     double a = 0.0;
     for (int i = threadIdx.x; i < GN_BLOCKS; i += 256) a += part[i];
@@ -1150,18 +1150,20 @@ __global__ __launch_bounds__(256) void grad_norm_final_kernel(const double* part
     __syncthreads();
     if (threadIdx.x == 0) {
         double nrm = sqrt(((sh[0] + sh[1]) + sh[2]) + sh[3]);
-        bool bad = !isfinite(nrm);
+        // skip the update for a non-finite norm, or while an out-of-range
+        // token or target id is pending (its rows contributed no gradient)
+        bool bad = !isfinite(nrm) || (id_err && *id_err);
         double c = (double)max_norm / (nrm + 1e-6);
         *norm_out = (float)nrm;
         *coef_out = bad ? 0.f : (float)(c < 1.0 ? c : 1.0);
-        *nonfinite = bad ? 1 : 0;
+        *skip = bad ? 1 : 0;
     }
 }
 
-void grad_norm(const float* g, int64_t n, double* partial, float* norm_out, float* coef_out, int32_t* nonfinite,
-               float max_norm, hipStream_t s) {
+void grad_norm(const float* g, int64_t n, double* partial, float* norm_out, float* coef_out, int32_t* skip,
+               const int32_t* id_err, float max_norm, hipStream_t s) {
     grad_norm_partial_kernel<<<GN_BLOCKS, 256, 0, s>>>(g, n, partial);
-    grad_norm_final_kernel<<<1, 256, 0, s>>>(partial, norm_out, coef_out, nonfinite, max_norm);
+    grad_norm_final_kernel<<<1, 256, 0, s>>>(partial, norm_out, coef_out, skip, id_err, max_norm);
 }
 
 GPT_DEV void adamw4(float4& pp, const float4& gg, float4& mm, float4& vv, bool decayed, float c, float dec, float lr,

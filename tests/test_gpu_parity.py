@@ -4,8 +4,9 @@ CPU float64 oracle.
 fp32 path: loss rel err <= 1e-5; every gradient tensor and every updated
 parameter tensor max|a-b|/max|b| <= 1e-4 (parameters whose gradient is
 within rounding of zero are excluded: there AdamW's first step is +-lr by
-sign). bf16 path: loss rel err <= 2e-2, gradient cosine >= 0.99, parameter
-cosine after the step >= 0.999.
+sign). bf16 path: loss rel err <= 2e-2, gradient cosine >= 0.99 (over all tensors
+and for each tensor), parameter cosine after the step >= 0.999, update
+direction cosine >= 0.9. Full-shape cases run distinct sequences.
 """
 
 import math
@@ -175,39 +176,92 @@ def test_error_paths():
     assert np.array_equal(gpu.get_param("wte"), before)
 
 
+def test_bad_id_without_wait_skips_update():
+    """An out-of-range target in a micro-step that does not wait: the update
+    that follows is skipped on the device (parameters and moments unchanged)
+    and reports TOKEN_RANGE when it waits; the report clears the flag."""
+    from transformer_lm_step_gpt_amd.gpt import GptError
+    w = I.TINY_FP32
+    gpu = make(w.model, 1)
+    x, y = next(I.batches(w))
+    bad = y.copy()
+    bad[2, 5] = -3
+    before = gpu.params()
+    gpu.forward_backward(x, bad, sync=False)
+    with pytest.raises(GptError) as e:
+        gpu.clip_and_adamw(1e-3, 1)
+    assert e.value.status == -5
+    for n in gpu.names:
+        assert np.array_equal(gpu.get_param(n), before[n]), n
+        m, v = gpu.get_opt_state(n)
+        assert not m.any() and not v.any(), n
+    # cleared by the report: a clean micro-step and update go through
+    gpu.forward_backward(x, y, sync=False)
+    norm = gpu.clip_and_adamw(1e-3, 1)
+    assert math.isfinite(norm) and norm > 0
+    assert not np.array_equal(gpu.get_param("wte"), before["wte"])
+
+
 # ---------------------------------------------------------------- bf16 path
 
-def bf16_check(w, batch, seq, steps=1, single_sequence=False, max_batch=None):
+def bf16_compare(gpu, cfg, p, m, v, gpu_batches, oracle_batches, lr, step, label):
+    """One optimiser step on the GPU (its micro-batches at grad_scale 1/k) and in
+    the oracle (its micro-batches at 1/k), then the bf16 gates: loss rel err
+    <= 2e-2; gradient cosine >= 0.99 over all tensors and for every tensor whose
+    oracle gradient is non-zero (tensors with an exactly zero oracle gradient
+    must come out zero); parameter cosine >= 0.999 after the step; the update
+    direction (parameter change) cosine >= 0.9 over all tensors. Returns the
+    oracle's new (p, m, v)."""
+    k = len(gpu_batches)
+    losses = [gpu.forward_backward(x, y, grad_scale=1.0 / k, sync=(j + 1 == k)) for j, (x, y) in
+              enumerate(gpu_batches)]
+    loss = gpu.loss_accum()
+    g_gpu = gpu.grads()
+    p_before = {n: gpu.get_param(n) for n in gpu.names}
+    norm = gpu.clip_and_adamw(lr, step)
+    rows = sum(x.shape[0] * x.shape[1] for x, _ in oracle_batches)
+    lref, nref, gref, p_new, m_new, v_new = O.train_step(p, m, v, oracle_batches, cfg, lr, step,
+                                                         progress=say if rows >= 1024 else None)
+    names = gpu.names
+    gcos = cosine(np.concatenate([g_gpu[n].ravel() for n in names]), np.concatenate([gref[n].ravel() for n in names]))
+    per = sorted((cosine(g_gpu[n], gref[n]), n) for n in names if np.abs(gref[n]).max() > 0)
+    zero = [n for n in names if np.abs(gref[n]).max() == 0]
+    gmax = max(float(np.abs(g_gpu[n]).max()) for n in names)
+    p_gpu = {n: gpu.get_param(n) for n in names}
+    pcos = cosine(np.concatenate([p_gpu[n].ravel() for n in names]), np.concatenate([p_new[n].ravel() for n in names]))
+    ucos = cosine(np.concatenate([(p_gpu[n] - p_before[n]).ravel() for n in names]),
+                  np.concatenate([(p_new[n] - p[n]).ravel() for n in names]))
+    say(f"  {label}: loss {loss:.5f} vs {lref:.5f}; norm {norm:.4f} vs {nref:.4f}; grad cos {gcos:.6f}; "
+        f"worst tensors {[(n, round(c, 5)) for c, n in per[:3]]}; exact-zero tensors {len(zero)}; "
+        f"param cos {pcos:.7f}; update cos {ucos:.5f}")
+    assert abs(loss - lref) / abs(lref) <= 2e-2
+    assert abs(norm - nref) / nref <= 2e-2
+    assert gcos >= 0.99
+    assert per[0][0] >= 0.99, per[:3]
+    for n in zero:
+        assert np.abs(g_gpu[n]).max() <= 1e-6 * gmax, n
+    assert pcos >= 0.999
+    assert ucos >= 0.9
+    return p_new, m_new, v_new
+
+
+def bf16_check(w, batch, seq, steps=1, max_batch=None):
+    """`steps` optimiser steps of one micro-batch of `batch` distinct sequences
+    from the workload's stream, GPU at that launch shape and the oracle on the
+    same sequences (one sequence per oracle micro-batch at scale 1/batch: the
+    mean over all rows, with one sequence's activations in host memory at a time)."""
     cfg = w.model if max_batch is None else w.model.replace(max_batch=max_batch)
-    say(f"bf16 {w.name}: B={batch} T={seq} steps={steps} single_sequence={single_sequence}")
+    say(f"bf16 {w.name}: B={batch} T={seq} steps={steps}")
     gpu = make(cfg, w.init_seed)
     p = O.init_params(cfg, w.init_seed)
     m = O.zeros_like_params(p)
     v = O.zeros_like_params(p)
     it = I.batches(w, batch, seq)
     for step in range(1, steps + 1):
-        if single_sequence:
-            x, y = I.repeated_sequence_batch(w, batch, seq)
-            xo, yo = x[:1], y[:1]
-        else:
-            x, y = next(it)
-            xo, yo = x, y
+        x, y = next(it)
         lr = 6e-4 * step / steps if steps > 1 else w.lr
-        loss = gpu.forward_backward(x, y)
-        g_gpu = gpu.grads()
-        norm = gpu.clip_and_adamw(lr, step)
-        lref, nref, gref, p, m, v = O.train_step(p, m, v, [(xo, yo)], cfg, lr, step,
-                                                 progress=say if seq * len(xo) >= 1024 else None)
-        gcos = cosine(np.concatenate([g_gpu[n].ravel() for n in gpu.names]),
-                      np.concatenate([gref[n].ravel() for n in gpu.names]))
-        worst = min((cosine(g_gpu[n], gref[n]), n) for n in gpu.names if np.abs(gref[n]).max() > 0)
-        say(f"  step {step}: loss {loss:.5f} vs {lref:.5f}; norm {norm:.4f} vs {nref:.4f}; grad cos {gcos:.5f}; "
-            f"worst tensor {worst[1]} {worst[0]:.4f}")
-        assert abs(loss - lref) / abs(lref) <= 2e-2
-        assert gcos >= 0.99
-        pcos = cosine(np.concatenate([gpu.get_param(n).ravel() for n in gpu.names]),
-                      np.concatenate([p[n].ravel() for n in gpu.names]))
-        assert pcos >= 0.999
+        per_seq = [(x[b:b + 1], y[b:b + 1]) for b in range(batch)]
+        p, m, v = bf16_compare(gpu, cfg, p, m, v, [(x, y)], per_seq, lr, step, f"step {step}")
     return gpu
 
 
@@ -218,36 +272,56 @@ def test_char_bf16_trajectory():
     bf16_check(I.CHAR_BF16, 4, 256, steps=20, max_batch=4)
 
 
-def test_char_bf16_full_batch_single_sequence():
-    """The char-level workload at its full B=64 launch shape, on a batch of one
-    repeated sequence (same loss and gradients as that sequence alone)."""
-    bf16_check(I.CHAR_BF16, 64, 256, single_sequence=True)
-
-
 @pytest.mark.timeout(600)
-def test_gpt2_124m_full_shape_single_sequence():
-    """GPT-2 124M at B=16, T=1024 (the benchmark's launch configuration) on a
-    batch of one repeated sequence, against the oracle on that one sequence."""
-    bf16_check(I.GPT2_124M, 16, 1024, single_sequence=True)
+def test_char_bf16_full_batch():
+    """The char-level workload at its full launch shape (64 distinct sequences of 256)."""
+    bf16_check(I.CHAR_BF16, 64, 256)
 
 
-@pytest.mark.timeout(600)
-def test_speedrun_block_full_shape_single_sequence():
+@pytest.mark.timeout(900)
+def test_gpt2_124m_full_shape():
+    """GPT-2 124M at B=16, T=1024 (the benchmark's launch configuration) on 16
+    distinct sequences of the workload's stream, against the oracle on all 16."""
+    bf16_check(I.GPT2_124M, 16, 1024)
+
+
+@pytest.mark.timeout(900)
+def test_speedrun_block_full_shape():
     """Speedrun block (RoPE, QK-RMSNorm, ReLU^2, windows 256/2048, softcap 30,
-    zero-init projections) at B=8, T=2048 on a batch of one repeated
-    sequence, against the oracle on that one sequence."""
-    bf16_check(I.SPEEDRUN_BLOCK, 8, 2048, single_sequence=True)
+    zero-init projections) at B=8, T=2048 on 8 distinct sequences, against
+    the oracle on all 8."""
+    bf16_check(I.SPEEDRUN_BLOCK, 8, 2048)
+
+
+@pytest.mark.timeout(600)
+def test_gpt2_124m_accumulation_distinct_micro_batches():
+    """Gradient accumulation over distinct consecutive micro-batches at the 124M
+    shape: 4 micro-batches of 1x1024 taken in order from the accumulated
+    workload's stream (each advancing it by 1024 tokens) at grad_scale 1/4,
+    then clip and AdamW at lr = get_lr(1000), against the oracle's train_step
+    on the same 4 sequences."""
+    w = I.GPT2_124M_ACCUM
+    cfg = w.model
+    it = I.batches(w, 1, w.seq_len)
+    mbs = [next(it) for _ in range(4)]
+    assert not np.array_equal(mbs[0][0], mbs[1][0])
+    lr = I_get_lr(1000)
+    assert abs(lr - w.lr) <= 1e-12
+    gpu = make(cfg, w.init_seed)
+    p = O.init_params(cfg, w.init_seed)
+    m = O.zeros_like_params(p)
+    bf16_compare(gpu, cfg, p, m, m, mbs, mbs, lr, 1, "4 distinct micro-batches")
 
 
 @pytest.mark.timeout(600)
 def test_gpt2_124m_accumulation_full_shape():
-    """The 524,288-token step: 32 micro-steps of 16x1024 with grad_scale 1/32,
-    clip, AdamW at lr = get_lr(1000). With every micro-batch equal, the
-    accumulated gradient equals that of one micro-step at scale 1 (scaling by
-    2^-5 is exact in every op; only the fp32 sum of 32 terms rounds), the
-    mean loss equals the single loss, and the clipped update matches. The
-    single micro-step at this shape is pinned to the oracle by the
-    full-shape test above."""
+    """The 524,288-token step at its launch shape: 32 micro-steps of 16x1024
+    with grad_scale 1/32, clip, AdamW at lr = get_lr(1000). With every
+    micro-batch equal, the accumulated gradient equals that of one micro-step
+    at scale 1 (scaling by 2^-5 is exact in every op; only the fp32 sum of 32
+    terms rounds), the mean loss equals the single loss, and the clipped
+    update matches. This compares the GPU with itself; accumulation over
+    distinct micro-batches is pinned to the oracle by the test above."""
     w = I.GPT2_124M_ACCUM
     x, y = I.repeated_sequence_batch(w, w.batch, w.seq_len)
     a = make(w.model, w.init_seed)

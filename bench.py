@@ -140,6 +140,128 @@ def rocprof_summary(d):
               f"{float(r['AverageNs']) / 1e3:.1f} | {100 * float(r['TotalDurationNs']) / tot:.1f} |")
 
 
+def trace_gaps(d, steps):
+    """Idle GPU time per step from a rocprofv3 --kernel-trace kernel_trace.csv.
+
+    Steps are delimited by the AdamW launch that ends each one; the last
+    `steps` steps are analysed (the uninstrumented steps at the end of a bench
+    run). Reports per step: wall time (AdamW end to AdamW end), time with at
+    least one kernel running, the rest (idle), and on the queue with the most
+    launches (the main stream) the sum of gaps between consecutive kernels."""
+    import csv
+    import glob
+    f = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))[0]
+    rows = list(csv.DictReader(open(f)))
+    ks = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r.get("Queue_Id", r.get("Stream_Id", "0")),
+                  r["Kernel_Name"]) for r in rows), key=lambda k: k[0])
+    ends = [k[1] for k in ks if "adamw_kernel" in k[3]]
+    if len(ends) < steps + 1:
+        raise SystemExit(f"trace holds {len(ends)} AdamW launches, need {steps + 1}")
+    out = []
+    for i in range(len(ends) - steps, len(ends)):
+        t0, t1 = ends[i - 1], ends[i]
+        sel = [k for k in ks if k[0] >= t0 and k[1] <= t1]
+        busy, cur_s, cur_e = 0, None, None
+        for a, b, _, _ in sel:
+            if cur_e is None or a > cur_e:
+                if cur_e is not None:
+                    busy += cur_e - cur_s
+                cur_s, cur_e = a, b
+            else:
+                cur_e = max(cur_e, b)
+        if cur_e is not None:
+            busy += cur_e - cur_s
+        queues = {}
+        for k in sel:
+            queues.setdefault(k[2], []).append(k)
+        main = max(queues.values(), key=len)
+        gaps = sum(max(0, main[j + 1][0] - main[j][1]) for j in range(len(main) - 1))
+        out.append({"wall_ms": (t1 - t0) / 1e6, "busy_ms": busy / 1e6, "idle_ms": (t1 - t0 - busy) / 1e6,
+                    "kernels": len(sel), "queues": len(queues), "main_queue_kernels": len(main),
+                    "main_queue_gap_ms": gaps / 1e6})
+    keys = list(out[0])
+    print("| step | " + " | ".join(keys) + " |")
+    print("|---" * (len(keys) + 1) + "|")
+    for i, o in enumerate(out):
+        print(f"| {i} | " + " | ".join(f"{o[k]:.3f}" if isinstance(o[k], float) else str(o[k]) for k in keys) + " |")
+    med = {k: float(np.median([o[k] for o in out])) for k in keys}
+    print("| median | " + " | ".join(f"{med[k]:.3f}" for k in keys) + " |")
+
+
+# rocprofv3 kernel names -> the library's kernel classes of the bandwidth-bound steps
+PMC_CLASSES = [("embed_fwd_kernel", "embed_fwd"), ("layernorm_fwd_kernel", "layernorm_fwd"),
+               ("layernorm_bwd_kernel", "layernorm_bwd"), ("cross_entropy_reg_kernel", "cross_entropy"),
+               ("embed_piece_kernel", "embed_bwd"), ("embed_segment_kernel", "embed_bwd"),
+               ("embed_wpe_kernel", "embed_bwd"), ("reduce_jobs_stage", "partial_reduce"),
+               ("grad_norm_partial_kernel", "grad_norm"), ("grad_norm_final_kernel", "grad_norm"),
+               ("adamw_kernel", "adamw")]
+
+
+def _pmc_means(d, counter):
+    """Mean value of `counter` per dispatch of each kernel name in a rocprofv3 --pmc output dir."""
+    import csv
+    import glob
+    f = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))[0]
+    acc = {}
+    for r in csv.DictReader(open(f)):
+        if r.get("Counter_Name", counter) != counter:
+            continue
+        v = acc.setdefault(r["Kernel_Name"], [0.0, 0])
+        v[0] += float(r["Counter_Value"])
+        v[1] += 1
+    return {k: v[0] / v[1] for k, v in acc.items()}
+
+
+def pmc_table(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernel_json):
+    """Markdown table: per bandwidth-bound kernel class, algorithmic bytes per
+    launch (the library's count), HBM bytes per launch from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch, each scaled by what it reads for a plain copy
+    of known size), and the algorithmic GB/s of the class's launches timed
+    alone (bench.py's all-launches-timed step)."""
+    copy_bytes = 4.0 * (64 << 20)
+    cf = _pmc_means(cal_fetch_dir, "FETCH_SIZE")
+    cw = _pmc_means(cal_write_dir, "WRITE_SIZE")
+    kf = max(cf.items(), key=lambda kv: kv[1])[1]     # the copy kernel dominates the calibration run
+    kw = max(cw.items(), key=lambda kv: kv[1])[1]
+    fetch_factor, write_factor = copy_bytes / (kf * 1024), copy_bytes / (kw * 1024)
+    fm, wm = _pmc_means(fetch_dir, "FETCH_SIZE"), _pmc_means(write_dir, "WRITE_SIZE")
+    kj = json.load(open(kernel_json))
+    cls = {r["name"]: r for r in kj["classes"]}
+    per_step = kj["launch_steps"]
+    print(f"FETCH_SIZE factor {fetch_factor:.4f}, WRITE_SIZE factor {write_factor:.4f} (copy of {copy_bytes:.0f} bytes)")
+    print("| class | launches/step | kernels | algorithmic MB/launch | counter MB/launch | counter/alg | "
+          "alone us/launch | alg GB/s alone | of 8 TB/s |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for c in dict.fromkeys(c for _, c in PMC_CLASSES):
+        names = [n for n in fm if any(sub in n and cc == c for sub, cc in PMC_CLASSES)]
+        r = cls.get(c)
+        if not names or not r or not r["launches"]:
+            continue
+        # every kernel of the class runs once per library launch of it
+        hbm = sum(fm[n] * 1024 * fetch_factor + wm.get(n, 0.0) * 1024 * write_factor for n in names)
+        alg = r["bytes"] / r["launches"]
+        us = 1e3 * r["ms"] / r["launches"]
+        gbs = alg / (us * 1e-6) / 1e9
+        short = ", ".join(sorted({n.split("(")[0].replace("void ", "").replace("gk::", "")[:40] for n in names}))
+        print(f"| {c} | {r['launches'] / per_step:.0f} | {short} | {alg / 1e6:.1f} | {hbm / 1e6:.1f} | "
+              f"{hbm / alg:.2f} | {us:.1f} | {gbs:.0f} | {100 * gbs / PEAK_HBM_GBS:.0f}% |")
+    # the dominant kernel of the step (largest summed time in the all-launches-timed step)
+    dom = max(kj["kernels"], key=lambda r: r["ms"])
+    names = [n for n in fm if dom["name"] in n]
+    if names:
+        n = names[0]
+        fb, wb = fm[n] * 1024 * fetch_factor, wm.get(n, 0.0) * 1024 * write_factor
+        per = dom["flops"] / dom["launches"] if dom["flops"] else dom["bytes"] / dom["launches"]
+        unit = "FLOP" if dom["flops"] else "bytes"
+        print(f"\ndominant kernel: {dom['name']}")
+        print(f"kernel: {dom['name']}")
+        print(f"sources_sha: {sources_sha()}")
+        print(f"fetch_bytes_per_launch: {fb:.0f}")
+        print(f"write_bytes_per_launch: {wb:.0f}")
+        print(f"hbm_bytes_per_launch: {fb + wb:.0f}")
+        print(f"algorithmic {unit} per launch (mean over its launches): {per:.0f}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,9 +272,22 @@ def main():
     ap.add_argument("--kernel-table", action="store_true", help="print per-kernel-class times to stderr")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the counter-calibration copy kernel")
     ap.add_argument("--rocprof-summary", metavar="DIR", help="print a table from a rocprofv3 --stats output dir")
+    ap.add_argument("--trace-gaps", metavar="DIR", help="idle time per step from a rocprofv3 --kernel-trace output "
+                                                         "dir (the last --steps steps)")
+    ap.add_argument("--kernel-json", metavar="PATH", help="write the per-class and per-kernel timings of the "
+                                                          "all-launches-timed step to PATH")
+    ap.add_argument("--pmc-table", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR",
+                                                     "KERNEL_JSON"),
+                    help="HBM traffic table of the bandwidth-bound kernels from rocprofv3 --pmc runs")
     a = ap.parse_args()
+    if a.pmc_table:
+        pmc_table(*a.pmc_table)
+        return
     if a.rocprof_summary:
         rocprof_summary(a.rocprof_summary)
+        return
+    if a.trace_gaps:
+        trace_gaps(a.trace_gaps, a.steps)
         return
     if a.copy_calibration:
         copy_calibration()
@@ -199,6 +334,9 @@ def main():
     torch.cuda.synchronize()
     table = model.kernel_timing()
     names = model.kernel_name_timing()
+    if a.kernel_json:
+        with open(a.kernel_json, "w") as fh:
+            json.dump({"launch_steps": 1, "classes": table, "kernels": names}, fh)
     dom = max(names, key=lambda r: r["ms"])["name"]
     model.set_kernel_timing(0)
     model.set_kernel_timing_filter(dom)

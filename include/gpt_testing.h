@@ -54,6 +54,14 @@ gpt_status gptk_gemm_colsum(int32_t M, int32_t N, int32_t K, const void* A, int6
 gpt_status gptk_gemm_force_config(int32_t cfg, int32_t splits);
 int32_t gptk_gemm_num_configs(void);
 
+/* Test control of the matrix-core GEMM for one product shape: bf16 products
+ * with these M, N, K and operand layouts (gptk_gemm and the training step
+ * alike) use tile configuration cfg with `splits` k-slices (splits 0 = 1);
+ * cfg -1 drops the override. A gptk_gemm_force_config setting takes
+ * precedence. Process-wide, not thread-safe; meant for measurements that
+ * compare configurations of single products inside the whole step. */
+gpt_status gptk_gemm_tune(int32_t M, int32_t N, int32_t K, int32_t a_kc, int32_t b_kc, int32_t cfg, int32_t splits);
+
 /* Causal (optionally windowed: i - j < window) softmax(Q K^T / sqrt(hd)) V per
  * (batch, head), heads interleaved in the columns of row-major [B*T, *]
  * buffers ("El Mecanismo de Atención"). Forward writes o and lse [B, H, T];

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <vector>
 
 namespace gk {
 
@@ -103,6 +104,17 @@ static const Tuned tuned[] = {
     {50304, 768, 16384, false, false, CFG_256_256_K64VW8, 1},
 };
 
+// Per-shape overrides of the tuned table (test control, for measurements).
+static std::vector<Tuned> g_tune_override;
+int gemm_mfma_tune(int M, int N, int K, bool a_kc, bool b_kc, int cfg, int splits) {
+    if (cfg < -1 || cfg >= CFG_COUNT || splits < 0) return -1;
+    g_tune_override.erase(std::remove_if(g_tune_override.begin(), g_tune_override.end(), [&](const Tuned& e) {
+                              return e.M == M && e.N == N && e.K == K && e.a_kc == a_kc && e.b_kc == b_kc;
+                          }), g_tune_override.end());
+    if (cfg >= 0) g_tune_override.push_back({M, N, K, a_kc, b_kc, cfg, splits > 0 ? splits : 1});
+    return 0;
+}
+
 GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
     struct Cand { int cfg; double rate; };
     static const Cand cands[] = {{CFG_256_128, 3.3e12}, {CFG_128_128, 2.8e12}, {CFG_256_256_K64, 3.5e12},
@@ -114,6 +126,15 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
     const int cus = num_cus();
     int fcfg = -1, fsplits = 0;
     bool force = forced(&fcfg, &fsplits);
+    if (!force)
+        for (const Tuned& e : g_tune_override)
+            if (!force && e.M == g.M && e.N == g.N && e.K == g.K && e.a_kc == g.a_kc && e.b_kc == g.b_kc) {
+                int sp = e.splits;
+                while (sp > 1 && (size_t)sp * mn > nscratch) --sp;
+                force = true;
+                fcfg = e.cfg;
+                fsplits = sp;
+            }
     if (!force)
         for (const Tuned& e : tuned)
             if (e.M == g.M && e.N == g.N && e.K == g.K && e.a_kc == g.a_kc && e.b_kc == g.b_kc) {

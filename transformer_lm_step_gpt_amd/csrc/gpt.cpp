@@ -1096,6 +1096,11 @@ gpt_status gptk_gemm_force_config(int32_t cfg, int32_t splits) {
 }
 int32_t gptk_gemm_num_configs(void) { return gk::gemm_mfma_num_configs(); }
 
+gpt_status gptk_gemm_tune(int32_t M, int32_t N, int32_t K, int32_t a_kc, int32_t b_kc, int32_t cfg, int32_t splits) {
+    if (M < 1 || N < 1 || K < 1) return GPT_ERR_INVALID_ARGUMENT;
+    return gk::gemm_mfma_tune(M, N, K, a_kc != 0, b_kc != 0, cfg, splits) == 0 ? GPT_OK : GPT_ERR_INVALID_ARGUMENT;
+}
+
 gpt_status gptk_gemm(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda, int32_t a_kc, const void* B,
                      int64_t ldb, int32_t b_kc, void* C, int64_t ldc, int32_t in_bf16, int32_t c_bf16, int32_t epi,
                      int32_t act, const float* bias, const float* resid, const void* aux, void* C2,

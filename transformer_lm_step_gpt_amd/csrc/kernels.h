@@ -158,6 +158,9 @@ void gemm(const Gemm& g, float* splitk_scratch, size_t splitk_floats, hipStream_
 // test control of the matrix-core tile configuration / split-K (cfg -1: automatic)
 void gemm_mfma_force(int cfg, int splits);
 int gemm_mfma_num_configs();
+// test control: the product of shape (M, N, K, a_kc, b_kc) uses tile
+// configuration cfg with `splits` k-slices (cfg -1 drops the override); 0 or -1 on a bad argument
+int gemm_mfma_tune(int M, int N, int K, bool a_kc, bool b_kc, int cfg, int splits);
 
 // ---------------------------------------------------------------- attention
 struct Attn {

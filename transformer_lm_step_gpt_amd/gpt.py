@@ -96,6 +96,7 @@ _SIGS = [
     # test-only kernel entry points
     ("gptk_gemm_force_config", c_int32, [c_int32, c_int32]),
     ("gptk_gemm_num_configs", c_int32, []),
+    ("gptk_gemm_tune", c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32]),
     ("gptk_gemm", c_int32, [c_int32, c_int32, c_int32, c_void_p, c_int64, c_int32, c_void_p, c_int64, c_int32,
                             c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                             c_void_p, c_void_p, c_int64, c_void_p]),

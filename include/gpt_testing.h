@@ -1,8 +1,10 @@
 /*
- * gpt_testing.h -- test-only entry points of the GPT-2 training-step library.
+ * gpt_testing.h -- per-kernel entry points of the GPT-2 training-step library.
  *
  * Each call launches one kernel family of the training step on raw device
- * buffers so that tests can check it against the CPU reference in isolation.
+ * buffers, so that tests can check it against the CPU reference in isolation
+ * (and, for gptk_layernorm_bwd_noalloc, so that callers that cannot allocate
+ * can run the LayerNorm backward on their own buffers).
  * All pointers are device addresses owned by the caller; calls are
  * asynchronous on `stream` (a hipStream_t passed as void*) and return
  * GPT_ERR_INVALID_ARGUMENT for shapes the kernels do not accept,
@@ -95,6 +97,23 @@ gpt_status gptk_layernorm(int32_t backward, int32_t M, int32_t d, float eps, con
                           void* dres_lp, int32_t overwrite, float* dg, float* db, float* dcol, float* partial,
                           int32_t bf16, void* stream);
 int64_t gptk_layernorm_partial_floats(int32_t M, int32_t d);
+
+/* The LayerNorm backward of gptk_layernorm (backward = 1) for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): same arguments without `partial`,
+ * same kernels and results. The partial sums live in a device array inside
+ * the library, one per GPU, of gptk_layernorm_noalloc_max_floats() floats
+ * (32 MiB, held until the process ends); the call allocates nothing.
+ * A shape whose gptk_layernorm_partial_floats(M, d) exceeds that size is
+ * rejected with GPT_ERR_INVALID_ARGUMENT (every shape with M <= 32768 and
+ * d <= 2048 fits). Calls that overlap on one GPU share the array and race;
+ * calls in stream order do not. dg and db are required, dcol and dres_lp
+ * nullable. GPT_ERR_DEVICE if the array's address cannot be obtained. */
+gpt_status gptk_layernorm_bwd_noalloc(int32_t M, int32_t d, const float* x, const float* g, const float* mean,
+                                      const float* rstd, const float* dy, float* dres, void* dres_lp,
+                                      int32_t overwrite, float* dg, float* db, float* dcol, int32_t bf16,
+                                      void* stream);
+int64_t gptk_layernorm_noalloc_max_floats(void);
 
 /* Fused softmax cross-entropy on logits z [M, Vp] (act, overwritten in place
  * by the gradient (softmax - onehot) * gscale); optional tanh softcap. */

@@ -1214,6 +1214,21 @@ gpt_status gptk_layernorm(int32_t backward, int32_t M, int32_t d, float eps, con
 
 int64_t gptk_layernorm_partial_floats(int32_t M, int32_t d) { return (int64_t)gk::layernorm_bwd_partial_floats(M, d); }
 
+gpt_status gptk_layernorm_bwd_noalloc(int32_t M, int32_t d, const float* x, const float* g, const float* mean,
+                                      const float* rstd, const float* dy, float* dres, void* dres_lp,
+                                      int32_t overwrite, float* dg, float* db, float* dcol, int32_t bf16,
+                                      void* stream) {
+    if (M < 1 || d < 4 || d % 4 || d > 2048 || !x || !g || !mean || !rstd || !dy || !dres || !dg || !db)
+        return GPT_ERR_INVALID_ARGUMENT;
+    const int r = gk::layernorm_bwd_static(bf16, dy, x, mean, rstd, g, dres, dres_lp, overwrite, dg, db, dcol, M, d,
+                                           (hipStream_t)stream);
+    if (r == -1) return GPT_ERR_INVALID_ARGUMENT;
+    if (r != 0) return GPT_ERR_DEVICE;
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
+
+int64_t gptk_layernorm_noalloc_max_floats(void) { return (int64_t)gk::layernorm_bwd_static_capacity_floats(); }
+
 gpt_status gptk_cross_entropy(int32_t M, int32_t Vp, void* z, const int32_t* y, float* row_loss, float gscale,
                               float cap, int32_t* err, int32_t bf16, void* stream) {
     if (M < 1 || Vp < 1) return GPT_ERR_INVALID_ARGUMENT;

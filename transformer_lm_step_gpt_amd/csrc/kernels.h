@@ -49,6 +49,15 @@ void layernorm_bwd(bool bf, const float* dy, const float* x, const float* mean, 
                    const float* g, float* dres, void* dres_lp, bool overwrite, float* dg, float* db,
                    float* dcol, float* partial, int M, int d, hipStream_t s);
 
+// layernorm_bwd with its partial sums in a file-scope device array of
+// layernorm_bwd_static_capacity_floats() floats instead of a caller buffer
+// (nothing allocated). Returns 0, -1 when the shape needs more than the
+// array holds, -4 on a HIP runtime failure.
+size_t layernorm_bwd_static_capacity_floats();
+int layernorm_bwd_static(bool bf, const float* dy, const float* x, const float* mean, const float* rstd,
+                         const float* g, float* dres, void* dres_lp, bool overwrite, float* dg, float* db,
+                         float* dcol, int M, int d, hipStream_t s);
+
 // ---------------------------------------------------------------- column sums
 // out[n] += sum_m Y[m, n] (Y act or fp32 with row stride ld); partial needs
 // colsum_partial_floats(M, N) floats.

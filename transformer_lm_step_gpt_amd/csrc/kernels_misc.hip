@@ -13,6 +13,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <mutex>
+
 #include <type_traits>
 
 namespace gk {
@@ -685,6 +687,42 @@ void layernorm_bwd(bool bf, const float* dy, const float* x, const float* mean, 
     const int nb = ceil_div(M, LNB_ROWS);
     layernorm_bwd_rows(bf, dy, false, x, mean, rstd, g, dres, dres_lp, overwrite, partial, M, d, s);
     reduce_partials(partial, nb, d, dcol ? 3 : 2, partial + (size_t)3 * nb * d, dg, db, dcol, s);
+}
+
+// ---- LayerNorm backward without a caller-provided workspace
+// The row pass's partial sums and the reduction's group sums live in this
+// file-scope device array: one copy per GPU, held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in symbol); it looks up each device's address once with
+// hipGetSymbolAddress and passes that. Every element the kernels read is
+// written earlier in the same call, so nothing needs clearing; calls that
+// overlap on one GPU share the array and race.
+constexpr size_t LNB_STATIC_FLOATS = (size_t)8 << 20;   // 32 MiB
+static __device__ __align__(256) float ln_bwd_scratch[LNB_STATIC_FLOATS];
+constexpr int LNB_STATIC_MAX_DEVICES = 64;
+
+size_t layernorm_bwd_static_capacity_floats() { return LNB_STATIC_FLOATS; }
+
+int layernorm_bwd_static(bool bf, const float* dy, const float* x, const float* mean, const float* rstd,
+                         const float* g, float* dres, void* dres_lp, bool overwrite, float* dg, float* db,
+                         float* dcol, int M, int d, hipStream_t s) {
+    if (layernorm_bwd_partial_floats(M, d) > LNB_STATIC_FLOATS) return -1;
+    static std::mutex mu;
+    static float* addr[LNB_STATIC_MAX_DEVICES] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= LNB_STATIC_MAX_DEVICES) return -4;
+    float* part = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (!addr[dev]) {
+            void* p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(ln_bwd_scratch)) != hipSuccess || !p) return -4;
+            addr[dev] = (float*)p;
+        }
+        part = addr[dev];
+    }
+    layernorm_bwd(bf, dy, x, mean, rstd, g, dres, dres_lp, overwrite, dg, db, dcol, part, M, d, s);
+    return 0;
 }
 
 // =====================================================================

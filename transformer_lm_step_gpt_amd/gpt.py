@@ -114,6 +114,10 @@ _SIGS = [
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_int32, c_void_p]),
     ("gptk_layernorm_partial_floats", c_int64, [c_int32, c_int32]),
+    ("gptk_layernorm_bwd_noalloc", c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
+                                             c_void_p]),
+    ("gptk_layernorm_noalloc_max_floats", c_int64, []),
     ("gptk_cross_entropy", c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_float, c_float, c_void_p,
                                      c_int32, c_void_p]),
     ("gptk_embed_bwd", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,

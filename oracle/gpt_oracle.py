@@ -34,6 +34,10 @@ Sources (page title, section):
     QK-Norm, ReLU^2, logit softcap, zero-initialised projections, long/short
     sliding-window attention. The README names these without formulas; the
     readings used here are stated at each function.
+  * Sampling (generate): "Un GPT desde cero + nanoGPT" 2.1 (autoregressive
+    generate: last position's logits divided by the temperature, softmax, one
+    draw, append, repeat; 0 temperature = greedy) and the lecture's
+    "Генерация и устройство" (top-k sampling with k = 50).
 
 Random initialisation uses Philox4x64-10 (Salmon, Moraes, Dror and Shaw,
 "Parallel random numbers: as easy as 1, 2, 3", SC'11) and the Box-Muller
@@ -503,3 +507,68 @@ def train_step(params, m, v, micro_batches, cfg, lr, step, progress=None):
     coef = clip_coefficient(norm, cfg.max_grad_norm)
     P, Mn, Vn = adamw_update(params, acc, m, v, lr, step, cfg, decay_flags(cfg), grad_coef=coef)
     return loss_sum / k, norm, acc, P, Mn, Vn
+
+
+# ----------------------------------------------------------------------------
+# sampling (generate)
+# ----------------------------------------------------------------------------
+
+SAMPLE_STREAM = 0x73616D706C65   # Philox key word 1 of the sampling draws ("sample")
+
+
+def sample_uniform(seed: int, step: int, row: int) -> float:
+    """The uniform in (0, 1) of draw `step` of sequence `row`: word 0 of the
+    Philox4x64-10 block with counter (step, row, 0, 0) and key
+    (seed, SAMPLE_STREAM), top 53 bits mapped to the open interval."""
+    w0, _, _, _ = philox4x64_10(np.array([step], dtype=np.uint64), np.array([row], dtype=np.uint64), 0, 0,
+                                seed, SAMPLE_STREAM)
+    return float(_unit_open(w0)[0])
+
+
+def softcap(z, cap):
+    """Speedrun logit softcap cap * tanh(z / cap) (cap 0: none)."""
+    return cap * np.tanh(z / cap) if cap else z
+
+
+def sample_next(z, temperature: float, top_k: int, u: float) -> int:
+    """One draw from a row of logits z.
+
+    temperature 0 is greedy (the first index of the maximum). Otherwise the
+    probabilities are softmax(z / temperature); with 0 < top_k < len(z) only
+    the top_k most probable tokens are kept (ties at the k-th value broken
+    towards lower indices) and renormalised; the token is the first index i,
+    in increasing token order, whose cumulative kept probability exceeds u.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    V = z.shape[0]
+    if temperature == 0:
+        return int(np.argmax(z))
+    keep = np.ones(V, dtype=bool)
+    if 0 < top_k < V:
+        order = np.lexsort((np.arange(V), -z))      # by value descending, then index ascending
+        keep[:] = False
+        keep[order[:top_k]] = True
+    w = np.where(keep, np.exp((z - z.max()) / temperature), 0.0)
+    c = np.cumsum(w)
+    i = int(np.searchsorted(c, u * c[-1], side="right"))
+    return min(i, int(np.nonzero(keep)[0][-1]))
+
+
+def generate(params, prompt, cfg, n_new: int, temperature: float, top_k: int, seed: int):
+    """Autoregressive sampling with a full forward pass over the whole sequence
+    at every step (no cache): returns (tokens [B, T0 + n_new], logits of each
+    draw [n_new, B, Vp] after the softcap). The prompt plus the new tokens
+    must fit in block_size (the pages crop longer contexts to block_size)."""
+    seq = np.asarray(prompt, dtype=np.int64)
+    B, T0 = seq.shape
+    if T0 + n_new > cfg.block_size:
+        raise ValueError("prompt + new tokens longer than block_size")
+    logits = []
+    for step in range(n_new):
+        _, _, ex = forward_backward(params, seq, np.zeros_like(seq), cfg, want_grads=False, return_logits=True)
+        z = ex["logits"][:, -1, :]          # the softcap is already applied
+        logits.append(z)
+        nxt = [sample_next(z[b], temperature, top_k, sample_uniform(seed, step, b)) for b in range(B)]
+        seq = np.concatenate([seq, np.array(nxt, dtype=np.int64)[:, None]], axis=1)
+    return seq.astype(np.int32), np.stack(logits) if logits else np.zeros((0, B, cfg.padded_vocab_size))
+

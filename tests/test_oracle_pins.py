@@ -318,6 +318,15 @@ def _torch_loss(params, tokens, targets, cfg, untie=False):
     P = {k: torch.tensor(v, requires_grad=True) for k, v in params.items()}
     if untie:
         P["lm_head"] = torch.tensor(params["wte"], requires_grad=True)
+    z = _torch_logits(P, tokens, cfg, untie)
+    B, T = np.asarray(tokens).shape
+    loss = F.cross_entropy(z.reshape(B * T, -1), torch.tensor(targets, dtype=torch.long).reshape(-1))
+    loss.backward()
+    return loss.item(), {k: v.grad.numpy() for k, v in P.items()}
+
+
+def _torch_logits(P, tokens, cfg, untie=False):
+    """Logits [B, T, Vp] (after the softcap) of the torch-ops model for torch parameters P."""
     tok = torch.tensor(tokens, dtype=torch.long)
     B, T = tok.shape
     d, H = cfg.n_embd, cfg.n_head
@@ -357,9 +366,7 @@ def _torch_loss(params, tokens, targets, cfg, untie=False):
     z = F.linear(x, P["lm_head"] if untie else P["wte"])
     if cfg.logit_softcap:
         z = cfg.logit_softcap * torch.tanh(z / cfg.logit_softcap)
-    loss = F.cross_entropy(z.reshape(B * T, -1), torch.tensor(targets, dtype=torch.long).reshape(-1))
-    loss.backward()
-    return loss.item(), {k: v.grad.numpy() for k, v in P.items()}
+    return z
 
 
 def _perturbed_params(cfg, seed):
@@ -599,3 +606,76 @@ def test_overfit_one_batch():
         loss, _, _, params, m, v = O.train_step(params, m, v, [(tok, tgt)], cfg, 3e-3, step)
         first = loss if first is None else first
     assert first > 4.0 and loss < 0.2 * first
+
+
+# ---------------------------------------------------------------- sampling (generate)
+
+@pytest.mark.parametrize("seed,step,row", [(1, 1, 0), (12345, 7, 3), (2**63 + 11, 2**40, 2**33)])
+def test_sample_uniform_is_philox(seed, step, row):
+    """The draw's uniform is word 0 of the Philox4x64-10 block at counter
+    (step, row, 0, 0), key (seed, stream): numpy's Philox at counter - 1."""
+    bg = np.random.Philox(key=seed + (O.SAMPLE_STREAM << 64), counter=np.array([step - 1, row, 0, 0], np.uint64))
+    w0 = int(bg.random_raw(1)[0])
+    assert O.sample_uniform(seed, step, row) == ((w0 >> 11) + 0.5) * 2.0 ** -53
+
+
+@pytest.mark.parametrize("temperature,top_k", [(1.0, 0), (0.7, 5), (1.3, 39), (1.0, 1)])
+def test_sample_next_draws_with_the_softmax_probabilities(temperature, top_k):
+    """Over a fine grid of u the share of u that gives token i is the
+    probability torch assigns to i: softmax(z / T) over the top_k logits
+    (torch.topk), zero elsewhere."""
+    rng = np.random.default_rng(3)
+    V, N = 40, 200_000
+    z = rng.normal(size=V) * 2
+    zt = torch.tensor(z) / temperature
+    keep = torch.zeros(V, dtype=torch.bool)
+    keep[torch.topk(zt, top_k).indices if 0 < top_k < V else slice(None)] = True
+    p = torch.softmax(torch.where(keep, zt, torch.tensor(-math.inf, dtype=zt.dtype)), 0).numpy()
+    counts = np.zeros(V)
+    for j in range(N):
+        counts[O.sample_next(z, temperature, top_k, (j + 0.5) / N)] += 1
+    assert np.abs(counts / N - p).max() <= 2.0 / N
+
+
+def test_sample_next_greedy_and_ties():
+    z = np.array([1.0, 3.0, 3.0, 0.5, 3.0])
+    assert O.sample_next(z, 0.0, 0, 0.9) == 1            # greedy: first index of the maximum
+    for u in (1e-9, 0.5, 1 - 1e-9):
+        assert O.sample_next(z, 1.0, 1, u) == 1          # top-1 keeps the lowest index among ties
+    got = {O.sample_next(z, 1.0, 2, (j + 0.5) / 1000) for j in range(1000)}
+    assert got == {1, 2}                                  # top-2: the two lowest tied indices, equal shares
+
+
+@pytest.mark.parametrize("cfg", [TINY, TINY_SPEED], ids=["gpt2_tiny", "speedrun_tiny"])
+def test_generate_logits_match_torch_and_draws_follow_them(cfg):
+    """Each step's logits are those of the torch-ops model on the sequence so far
+    (last position), and each new token is the draw sample_next makes from them."""
+    params = _perturbed_params(cfg, 5)
+    rng = np.random.default_rng(8)
+    prompt = rng.integers(0, cfg.vocab_size, (2, 3)).astype(np.int32)
+    n_new = cfg.block_size - 3 if cfg.block_size < 10 else 6
+    toks, logits = O.generate(params, prompt, cfg, n_new, 0.9, 5, 77)
+    assert toks.shape == (2, 3 + n_new) and np.array_equal(toks[:, :3], prompt)
+    P = {k: torch.tensor(v) for k, v in params.items()}
+    for step in range(n_new):
+        with torch.no_grad():
+            zt = _torch_logits(P, toks[:, :3 + step], cfg)[:, -1, :].numpy()
+        assert np.abs(logits[step] - zt).max() <= 1e-10 * max(1.0, np.abs(zt).max())
+        for b in range(2):
+            assert toks[b, 3 + step] == O.sample_next(zt[b], 0.9, 5, O.sample_uniform(77, step, b))
+
+
+def test_generate_greedy_continuation_is_consistent():
+    """Greedy decoding from a prompt extended by its own first token continues
+    with the same tokens (no randomness; causality)."""
+    params = _perturbed_params(TINY, 6)
+    prompt = np.array([[3, 1, 4], [1, 5, 9]], np.int32)
+    a, _ = O.generate(params, prompt, TINY, 5, 0.0, 0, 1)
+    b, _ = O.generate(params, a[:, :4], TINY, 4, 0.0, 0, 2)
+    assert np.array_equal(a, b)
+
+
+def test_generate_rejects_overlong_context():
+    with pytest.raises(ValueError):
+        O.generate(_perturbed_params(TINY, 1), np.zeros((1, TINY.block_size), np.int32), TINY, 1, 1.0, 0, 0)
+

@@ -160,6 +160,30 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* d_tokens,
  * loss_accum). Waits for the stream. */
 gpt_status gpt_loss_accum(gpt_handle* h, float* h_mean_loss);
 
+/* Autoregressive sampling with a key/value cache ("Un GPT desde cero +
+ * nanoGPT" 2.1, generate; the lecture's "Генерация и устройство", top-k
+ * sampling). d_prompt: device int32 [B, T0]; d_out: device int32
+ * [B, T0 + n_new], receives the prompt followed by n_new drawn tokens.
+ * Each draw takes the last position's logits (after the softcap, over all
+ * padded_vocab_size classes) divided by `temperature` (0 = greedy: the first
+ * index of the maximum), keeps the top_k most probable tokens (0 = all; ties
+ * at the k-th value go to the lower ids), and returns the first token, in id
+ * order, whose cumulative kept probability exceeds u; u in (0, 1) is the top
+ * 53 bits of word 0 of Philox4x64-10 at counter (draw index, row, 0, 0) with
+ * key (seed, 0x73616D706C65). The prompt runs through the training forward
+ * pass once (prefill); every later token runs one decode step against the
+ * cached keys and values. d_logits (nullable): device fp32 [n_new, B,
+ * padded_vocab_size], the logits of every draw. Uses the handle's activation
+ * buffers (do not overlap with gpt_forward_backward on the same handle);
+ * parameters, gradients and optimiser state are not touched. Waits for the
+ * stream before returning.
+ * Errors: INVALID_ARGUMENT (null buffers, B outside [1, max_batch], T0 < 1,
+ * n_new < 0, T0 + n_new > block_size, temperature < 0 or not finite,
+ * top_k < 0), TOKEN_RANGE (a prompt id outside [0, padded_vocab_size)),
+ * DEVICE. */
+gpt_status gpt_generate(gpt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T0, int32_t n_new,
+                        float temperature, int32_t top_k, uint64_t seed, int32_t* d_out, float* d_logits);
+
 /* Global gradient clipping then AdamW, in two device passes:
  *   n = sqrt(sum of g^2 over every parameter, the tied wte once);
  *   c = min(1, max_grad_norm / (n + 1e-6));  g <- c g;

@@ -1,0 +1,169 @@
+"""Sampling with the key/value cache (gpt_generate) against the oracle's
+generate, which recomputes the full forward pass at every step.
+
+fp32 models: every draw's logits within 1e-4 (max abs difference over max
+abs value) of the oracle's, and the drawn tokens equal to the oracle's; the
+oracle first checks that each draw's uniform lies at least 1e-4 (relative) from
+the nearest boundary of its cumulative distribution, so that rounding at the
+fp32 bar cannot decide a token. bf16 models (the 124M and speedrun shapes):
+the first draw's logits against the oracle's at the bf16 bar (max difference
+<= 3e-2 of the largest logit, cosine >= 0.999); every drawn token lies in the
+top_k of the GPU's own logits; and each cached decode step agrees with a fresh
+prefill of the same prefix (prompt plus the tokens drawn so far)."""
+
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import gpt_oracle as O
+from transformer_lm_step_gpt_amd import inputs as I
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TINY_SPEED = I.ModelConfig(n_layer=2, n_head=2, n_embd=64, mlp_hidden=256, block_size=48, vocab_size=61,
+                           padded_vocab_size=64, max_batch=3, precision="fp32", pos_encoding="rope",
+                           qk_rmsnorm=True, mlp_act="relu2", window_even=7, window_odd=48, logit_softcap=3.0,
+                           zero_init_proj=False)
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def make(cfg, seed):
+    from transformer_lm_step_gpt_amd.gpt import GPT
+    return GPT(cfg, seed=seed, device="cuda:0")
+
+
+def relmax(a, b):
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-30))
+
+
+def cosine(a, b):
+    a, b = a.ravel().astype(np.float64), b.ravel().astype(np.float64)
+    return float(a @ b / max(np.linalg.norm(a) * np.linalg.norm(b), 1e-300))
+
+
+def draw_margin(z, temperature, top_k, u):
+    """Distance of u from the nearest boundary of the draw's cumulative distribution
+    (for greedy: the gap between the two largest logits relative to the largest)."""
+    z = np.asarray(z, np.float64)
+    if temperature == 0:
+        s = np.sort(z)
+        return (s[-1] - s[-2]) / max(abs(s[-1]), 1e-30)
+    keep = np.ones(z.size, bool)
+    if 0 < top_k < z.size:
+        keep[:] = False
+        keep[np.lexsort((np.arange(z.size), -z))[:top_k]] = True
+    w = np.where(keep, np.exp((z - z.max()) / temperature), 0.0)
+    c = np.cumsum(w) / w.sum()
+    return float(np.abs(c[keep] - u).min())
+
+
+def fp32_case(cfg, seed, B, T0, n_new, temperature, top_k, draw_seed):
+    say(f"generate fp32 {cfg.n_layer}L d{cfg.n_embd} pos={cfg.pos_encoding} B={B} T0={T0} n={n_new} "
+        f"T={temperature} k={top_k}")
+    rng = np.random.default_rng(seed)
+    prompt = rng.integers(0, cfg.vocab_size, (B, T0)).astype(np.int32)
+    gpu = make(cfg, seed)
+    toks, logits = gpu.generate(prompt, n_new, temperature, top_k, draw_seed, return_logits=True)
+    params = O.init_params(cfg, seed)
+    rtoks, rlogits = O.generate(params, prompt, cfg, n_new, temperature, top_k, draw_seed)
+    for step in range(n_new):
+        for b in range(B):
+            m = draw_margin(rlogits[step, b], temperature, top_k, O.sample_uniform(draw_seed, step, b))
+            assert m > 1e-4, (step, b, m)
+    assert np.array_equal(toks, rtoks), (toks, rtoks)
+    err = max(relmax(logits[s], rlogits[s]) for s in range(n_new))
+    say(f"  tokens equal; worst logits rel err {err:.2e}")
+    assert err <= 1e-4
+
+
+def test_generate_tiny_fp32_topk():
+    w = I.TINY_FP32
+    fp32_case(w.model, 1, 3, 5, 20, 0.8, 10, 7)
+
+
+def test_generate_tiny_fp32_greedy_full_context():
+    """Greedy decoding up to block_size (prompt 10 + 54 new tokens)."""
+    w = I.TINY_FP32
+    fp32_case(w.model, 2, 2, 10, 54, 0.0, 0, 0)
+
+
+def test_generate_speedrun_variant_fp32():
+    """RoPE, QK-RMSNorm, windows 7/48 (the decode window slides), ReLU^2, softcap 3."""
+    fp32_case(TINY_SPEED, 21, 2, 4, 30, 1.0, 0, 8)
+
+
+def bf16_case(w, B, T0, n_new, top_k, seed, cfg=None):
+    cfg = w.model if cfg is None else cfg
+    say(f"generate bf16 {w.name} B={B} T0={T0} n={n_new} k={top_k}")
+    prompt = next(I.batches(w, B, T0))[0]
+    gpu = make(cfg, w.init_seed)
+    toks, logits = gpu.generate(prompt, n_new, 1.0, top_k, seed, return_logits=True)
+    assert np.array_equal(toks[:, :T0], prompt)
+    # first draw vs the oracle (the prompt is the only input)
+    params = O.init_params(cfg, w.init_seed)
+    _, _, ex = O.forward_backward(params, prompt, np.zeros_like(prompt), cfg, want_grads=False, return_logits=True)
+    ref = ex["logits"][:, -1, :]
+    err, cos = relmax(logits[0], ref), cosine(logits[0], ref)
+    say(f"  first draw logits vs oracle: rel err {err:.2e}, cosine {cos:.6f}")
+    assert err <= 3e-2 and cos >= 0.999
+    # every token lies in the top_k of the GPU's own logits
+    for step in range(n_new):
+        for b in range(B):
+            z = logits[step, b]
+            kth = np.sort(z)[-top_k]
+            assert z[toks[b, T0 + step]] >= kth, (step, b)
+    # cached decode vs a fresh prefill of the same prefix
+    worst = 0.0
+    for step in range(1, n_new):
+        _, lg = gpu.generate(toks[:, :T0 + step], 1, 1.0, top_k, seed, return_logits=True)
+        e = relmax(logits[step], lg[0])
+        worst = max(worst, e)
+        assert cosine(logits[step], lg[0]) >= 0.999
+    say(f"  cached decode vs prefill: worst rel err {worst:.2e}")
+    assert worst <= 3e-2
+
+
+@pytest.mark.timeout(600)
+def test_generate_gpt2_124m_bf16():
+    bf16_case(I.GPT2_124M, 2, 16, 8, 50, 11)
+
+
+@pytest.mark.timeout(600)
+def test_generate_speedrun_block_bf16_past_window():
+    """Prompt of 300 tokens, beyond the 256-key window of the even layers. The
+    projections start from the ordinary initialisation: zero-initialised ones
+    make every block add exactly zero, so the logits would not depend on the
+    attention or the cache at all."""
+    w = I.SPEEDRUN_BLOCK
+    bf16_case(w, 1, 300, 5, 50, 12, cfg=w.model.replace(zero_init_proj=False))
+
+
+def test_generate_errors_and_determinism():
+    from transformer_lm_step_gpt_amd.gpt import GptError
+    w = I.TINY_FP32
+    gpu = make(w.model, 1)
+    prompt = np.array([[1, 2, 3]], np.int32)
+    with pytest.raises(GptError) as e:
+        gpu.generate(prompt, 62, 1.0, 5, 0)          # 3 + 62 > block_size
+    assert e.value.status == -1
+    with pytest.raises(GptError) as e:
+        gpu.generate(prompt, 2, -1.0, 5, 0)
+    assert e.value.status == -1
+    with pytest.raises(GptError) as e:
+        gpu.generate(prompt, 2, 1.0, -1, 0)
+    assert e.value.status == -1
+    with pytest.raises(GptError) as e:
+        gpu.generate(np.array([[1, 70, 3]], np.int32), 2, 1.0, 5, 0)
+    assert e.value.status == -5
+    a = gpu.generate(prompt, 10, 1.0, 5, 9)
+    b = gpu.generate(prompt, 10, 1.0, 5, 9)
+    c = gpu.generate(prompt, 10, 1.0, 5, 10)
+    assert np.array_equal(a, b) and a.shape == (1, 13)
+    assert not np.array_equal(a, c)
+    assert np.array_equal(gpu.generate(prompt, 0, 1.0, 5, 9), prompt)

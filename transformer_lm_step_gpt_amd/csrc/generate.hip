@@ -1,0 +1,341 @@
+// Decode-shaped kernels of autoregressive sampling with a key/value cache:
+// one new token per sequence and step ("Un GPT desde cero + nanoGPT" 2.1,
+// generate; the lecture notes' "Генерация и устройство", top-k sampling).
+//
+//   gen_embed      x[b] = wte[token at pos] + wpe[pos] for each sequence b
+//   cache_put      rows of k or v (from the qkv / q,k buffers) into the cache
+//                  [B, Tmax, d] of one layer at positions t0 ..
+//   gen_attention  one query per (sequence, head) against the cached keys and
+//                  values 0 .. pos (or the last `window` of them)
+//   gen_sample     one draw per sequence from the last position's logits:
+//                  softcap, temperature, top-k, inverse CDF in token order
+#include "common.h"
+#include "kernels.h"
+
+#include <cfloat>
+#include <climits>
+
+namespace gk {
+
+// ---------------------------------------------------------------- helpers
+
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): 10 rounds on a 4-word
+// counter with a 2-word key advanced by the Weyl constants between rounds.
+GPT_DEV void gen_philox(uint64_t c[4], uint64_t k0, uint64_t k1) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) { k0 += W0; k1 += W1; }
+        const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
+        const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
+        const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+    }
+}
+
+constexpr uint64_t SAMPLE_STREAM = 0x73616D706C65ull;   // key word 1 of the sampling draws
+
+// Monotone map of a float onto uint32 (larger float -> larger key).
+GPT_DEV uint32_t order_key(float z) {
+    const uint32_t u = __float_as_uint(z);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Block-wide reductions and scans over NT threads (NT a multiple of 64, at
+// most 1024), in a fixed order. `sh` holds at least NT / 64 + 1 slots.
+template <int NT>
+GPT_DEV float block_max_f(float v, float* sh) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    float r = sh[0];
+    for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, sh[i]);
+    return r;
+}
+template <int NT>
+GPT_DEV float block_sum_f(float v, float* sh) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    float r = sh[0];
+    for (int i = 1; i < NT / 64; ++i) r += sh[i];
+    return r;
+}
+template <int NT>
+GPT_DEV int block_sum_i(int v, int* sh) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    int r = 0;
+    for (int i = 0; i < NT / 64; ++i) r += sh[i];
+    return r;
+}
+template <int NT>
+GPT_DEV int block_max_i(int v, int* sh) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    int r = sh[0];
+    for (int i = 1; i < NT / 64; ++i) r = max(r, sh[i]);
+    return r;
+}
+// exclusive prefix sum over the threads in thread order; *total receives the sum
+template <int NT, typename V>
+GPT_DEV V block_excl_scan(V v, V* sh, V* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    V incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const V u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+    }
+    __syncthreads();
+    if (lane == 63) sh[w] = incl;
+    __syncthreads();
+    V off = 0, tot = 0;
+    for (int i = 0; i < NT / 64; ++i) {
+        if (i < w) off += sh[i];
+        tot += sh[i];
+    }
+    *total = tot;
+    return off + incl - v;
+}
+
+// ---------------------------------------------------------------- embedding of one token per sequence
+
+__global__ __launch_bounds__(256) void gen_embed_kernel(const int32_t* seq, int64_t ld, int pos, const float* wte,
+                                                        const float* wpe, float* x, int B, int d, int Vp,
+                                                        int32_t* err) {
+    const int dq = d >> 2;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= B * dq) return;
+    const int b = idx / dq, c = (idx % dq) * 4;
+    const int id = seq[(int64_t)b * ld + pos];
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (id >= 0 && id < Vp) v = load4(wte + (int64_t)id * d + c);
+    else if (c == 0) *err = 1;
+    if (wpe) {
+        const float4 p = load4(wpe + (int64_t)pos * d + c);
+        v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+    }
+    store4(x + (int64_t)b * d + c, v);
+}
+
+void gen_embed(const int32_t* seq, int64_t ld, int pos, const float* wte, const float* wpe, float* x, int B, int d,
+               int Vp, int32_t* err, hipStream_t s) {
+    const int n = B * (d / 4);
+    gen_embed_kernel<<<ceil_div(n, 256), 256, 0, s>>>(seq, ld, pos, wte, wpe, x, B, d, Vp, err);
+}
+
+// ---------------------------------------------------------------- cache rows
+
+// dst[(b Tmax + t0 + t) d + c] = src[(b nt + t) src_ld + c]; 16 bytes per thread
+template <typename T>
+__global__ __launch_bounds__(256) void cache_put_kernel(const T* src, int64_t src_ld, T* dst, int B, int nt, int Tmax,
+                                                        int t0, int d) {
+    constexpr int E = 16 / sizeof(T);
+    const int cpr = d / E;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)B * nt * cpr) return;
+    const int c = (int)(idx % cpr) * E;
+    const int64_t r = idx / cpr;
+    const int t = (int)(r % nt), b = (int)(r / nt);
+    const uint4 v = *reinterpret_cast<const uint4*>(src + ((int64_t)b * nt + t) * src_ld + c);
+    *reinterpret_cast<uint4*>(dst + ((int64_t)b * Tmax + t0 + t) * d + c) = v;
+}
+
+void cache_put(bool bf, const void* src, int64_t src_ld, void* dst, int B, int nt, int Tmax, int t0, int d,
+               hipStream_t s) {
+    const int64_t n = (int64_t)B * nt * (d / (bf ? 8 : 4));
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    if (!grid) return;
+    if (bf) cache_put_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)src, src_ld, (bf16*)dst, B, nt, Tmax, t0, d);
+    else cache_put_kernel<float><<<grid, 256, 0, s>>>((const float*)src, src_ld, (float*)dst, B, nt, Tmax, t0, d);
+}
+
+// ---------------------------------------------------------------- attention of one query against the cache
+
+// One workgroup per (sequence, head): scores of the query against keys
+// j0 .. pos in LDS, softmax in fp32, then out[c] = sum_j p_j v_j[c] with the
+// 256 threads split into 256 / hd groups of keys summed in a fixed order.
+template <typename T>
+__global__ __launch_bounds__(256) void gen_attention_kernel(const T* q, int64_t ldq, const T* kc, const T* vc, T* out,
+                                                            int H, int hd, int pos, int Tmax, int window,
+                                                            float scale) {
+    extern __shared__ float sc[];   // [pos + 1] scores, then weights
+    __shared__ float qs[128];
+    __shared__ float red[256];
+    __shared__ float rsh[16];
+    const int b = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x;
+    const int d = H * hd;
+    const int j0 = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;
+    const int n = pos + 1 - j0;
+    if (tid < hd) qs[tid] = to_f32(q[(int64_t)b * ldq + h * hd + tid]);
+    __syncthreads();
+    const T* kb = kc + ((int64_t)b * Tmax + j0) * d + h * hd;
+    float mx = -FLT_MAX;
+    for (int j = tid; j < n; j += 256) {
+        const T* kr = kb + (int64_t)j * d;
+        float acc = 0.f;
+        for (int c = 0; c < hd; ++c) acc += qs[c] * to_f32(kr[c]);
+        const float v = acc * scale;
+        sc[j] = v;
+        mx = fmaxf(mx, v);
+    }
+    mx = block_max_f<256>(mx, rsh);
+    float sum = 0.f;
+    for (int j = tid; j < n; j += 256) {
+        const float e = __expf(sc[j] - mx);
+        sc[j] = e;
+        sum += e;
+    }
+    sum = block_sum_f<256>(sum, rsh);   // its barriers also order the weight writes before the reads below
+    const int G = 256 / hd, c = tid % hd, g = tid / hd;
+    const T* vb = vc + ((int64_t)b * Tmax + j0) * d + h * hd + c;
+    float acc = 0.f;
+    for (int j = g; j < n; j += G) acc += sc[j] * to_f32(vb[(int64_t)j * d]);
+    red[tid] = acc;
+    __syncthreads();
+    if (g == 0) {
+        float a = 0.f;
+        for (int gg = 0; gg < G; ++gg) a += red[gg * hd + c];
+        out[(int64_t)b * d + h * hd + c] = from_f32<T>(a / sum);
+    }
+}
+
+void gen_attention(bool bf, const void* q, int64_t ldq, const void* kc, const void* vc, void* out, int B, int H,
+                   int hd, int pos, int Tmax, int window, hipStream_t s) {
+    const size_t lds = sizeof(float) * (size_t)(pos + 1);
+    const float scale = 1.0f / sqrtf((float)hd);
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute((const void*)gen_attention_kernel<bf16>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 32768);
+        (void)hipFuncSetAttribute((const void*)gen_attention_kernel<float>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 4 * 32768);
+        attr = true;
+    }
+    if (bf)
+        gen_attention_kernel<bf16><<<B * H, 256, lds, s>>>((const bf16*)q, ldq, (const bf16*)kc, (const bf16*)vc,
+                                                           (bf16*)out, H, hd, pos, Tmax, window, scale);
+    else
+        gen_attention_kernel<float><<<B * H, 256, lds, s>>>((const float*)q, ldq, (const float*)kc, (const float*)vc,
+                                                            (float*)out, H, hd, pos, Tmax, window, scale);
+}
+
+// ---------------------------------------------------------------- one draw per sequence
+
+// One workgroup of 1024 threads per sequence; thread t owns the contiguous
+// token range [t C, (t + 1) C), C = ceil(Vp / 1024), so thread order is token
+// order. Steps: softcap in place (and the copy out); the maximum; greedy for
+// temperature 0 (first index of the maximum); for 0 < top_k < Vp the k-th
+// largest value by bisection on the order-preserving keys, keeping every
+// larger value and the lowest-index ties; weights exp((z - max) / T) summed
+// per thread in token order and scanned across threads; the draw is the first
+// token whose running sum exceeds u * total, u from Philox4x64-10 at counter
+// (step, sequence) with key (seed, sampling stream).
+constexpr int GS_THREADS = 1024;
+
+__global__ __launch_bounds__(GS_THREADS) void gen_sample_kernel(float* logits, int Vp, float cap, float temperature,
+                                                                int top_k, uint64_t seed, int step, int32_t* seq,
+                                                                int64_t ld_seq, int pos_out, float* logits_out) {
+    __shared__ float fsh[GS_THREADS / 64 + 1];
+    __shared__ int ish[GS_THREADS / 64 + 1];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    float* z = logits + (int64_t)b * Vp;
+    const int chunk = ceil_div(Vp, GS_THREADS);
+    const int i0 = min(Vp, tid * chunk), i1 = min(Vp, i0 + chunk);
+    float mx = -FLT_MAX;
+    for (int i = i0; i < i1; ++i) {
+        float v = z[i];
+        if (cap > 0.f) {
+            v = cap * tanhf(v / cap);
+            z[i] = v;
+        }
+        if (logits_out) logits_out[(int64_t)b * Vp + i] = v;
+        mx = fmaxf(mx, v);
+    }
+    mx = block_max_f<GS_THREADS>(mx, fsh);
+    int32_t* dst = seq + (int64_t)b * ld_seq + pos_out;
+    if (temperature == 0.f) {
+        int first = INT_MAX;
+        for (int i = i0; i < i1; ++i)
+            if (z[i] == mx) { first = i; break; }
+        first = -block_max_i<GS_THREADS>(-first, ish);
+        if (tid == 0) *dst = first;
+        return;
+    }
+    const bool trunc = top_k > 0 && top_k < Vp;
+    uint32_t thr = 0;
+    int need = 0, tie_before = 0;
+    if (trunc) {
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = thr | (1u << bit);
+            int cnt = 0;
+            for (int i = i0; i < i1; ++i) cnt += order_key(z[i]) >= cand;
+            if (block_sum_i<GS_THREADS>(cnt, ish) >= top_k) thr = cand;
+        }
+        int gt = 0, ties = 0;
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t k = order_key(z[i]);
+            gt += k > thr;
+            ties += k == thr;
+        }
+        need = top_k - block_sum_i<GS_THREADS>(gt, ish);
+        int tot = 0;
+        tie_before = block_excl_scan<GS_THREADS, int>(ties, ish, &tot);
+    }
+    const float inv_t = 1.0f / temperature;
+    float s = 0.f;
+    int last = -1;
+    {
+        int tr = tie_before;
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t k = order_key(z[i]);
+            const bool keep = !trunc || k > thr || (k == thr && tr++ < need);
+            if (keep) {
+                s += __expf((z[i] - mx) * inv_t);
+                last = i;
+            }
+        }
+    }
+    float total = 0.f;
+    const float pre = block_excl_scan<GS_THREADS, float>(s, fsh, &total);
+    uint64_t c4[4] = {(uint64_t)step, (uint64_t)b, 0, 0};
+    gen_philox(c4, seed, SAMPLE_STREAM);
+    const double u = ((double)(c4[0] >> 11) + 0.5) * 0x1.0p-53;
+    const float target = (float)(u * (double)total);
+    // the owner: the last thread with kept weight whose prefix does not exceed the target
+    const int owner = block_max_i<GS_THREADS>((last >= 0 && pre <= target) ? tid : -1, ish);
+    if (tid == owner) {
+        int tr = tie_before, tok = last;
+        float run = pre;
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t k = order_key(z[i]);
+            const bool keep = !trunc || k > thr || (k == thr && tr++ < need);
+            if (!keep) continue;
+            run += __expf((z[i] - mx) * inv_t);
+            if (run > target) { tok = i; break; }
+        }
+        *dst = tok;
+    }
+}
+
+void gen_sample(float* logits, int B, int Vp, float cap, float temperature, int top_k, uint64_t seed, int step,
+                int32_t* seq, int64_t ld_seq, int pos_out, float* logits_out, hipStream_t s) {
+    gen_sample_kernel<<<B, GS_THREADS, 0, s>>>(logits, Vp, cap, temperature, top_k, seed, step, seq, ld_seq, pos_out,
+                                                logits_out);
+}
+
+}  // namespace gk

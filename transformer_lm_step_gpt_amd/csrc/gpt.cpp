@@ -138,6 +138,12 @@ struct Ws {
     float* splitk_side = nullptr;
     size_t splitk_side_floats = 0;
     float *rope_cos = nullptr, *rope_sin = nullptr;
+    // sampling: per-layer key and value caches [max_batch, block_size, d]
+    // (act) and the one-token-per-sequence buffers of a decode step
+    std::vector<void*> kcache, vcache;
+    float *dec_x = nullptr, *dec_x2 = nullptr, *dec_mean = nullptr, *dec_rstd = nullptr, *dec_logits = nullptr;
+    void *dec_y = nullptr, *dec_qkv = nullptr, *dec_qk = nullptr, *dec_att = nullptr, *dec_h1 = nullptr,
+         *dec_h2 = nullptr;
     int32_t* err = nullptr;
     float *loss_last = nullptr, *loss_sum = nullptr, *gnorm = nullptr, *coef = nullptr;
     int32_t* nonfinite = nullptr;
@@ -227,6 +233,24 @@ Ws plan(const gpt_config& c, const Table& tb, void* base) {
         int64_t half = (d / H) / 2;
         w.rope_cos = cv.arr<float>(c.block_size * half);
         w.rope_sin = cv.arr<float>(c.block_size * half);
+    }
+    for (int l = 0; l < L; ++l) {
+        w.kcache.push_back(cv.take(ab * M * d));
+        w.vcache.push_back(cv.take(ab * M * d));
+    }
+    {
+        const int64_t Bm = c.max_batch;
+        w.dec_x = cv.arr<float>(Bm * d);
+        w.dec_x2 = cv.arr<float>(Bm * d);
+        w.dec_mean = cv.arr<float>(Bm);
+        w.dec_rstd = cv.arr<float>(Bm);
+        w.dec_logits = cv.arr<float>(Bm * Vp);
+        w.dec_y = cv.take(ab * Bm * d);
+        w.dec_qkv = cv.take(ab * Bm * 3 * d);
+        w.dec_qk = cv.take(ab * Bm * 2 * d);
+        w.dec_att = cv.take(ab * Bm * d);
+        w.dec_h1 = cv.take(ab * Bm * F);
+        w.dec_h2 = cv.take(ab * Bm * F);
     }
     w.err = cv.arr<int32_t>(4);
     w.loss_last = cv.arr<float>(4);
@@ -444,6 +468,93 @@ gpt_status sync_and_check(gpt_handle* h) {
     return GPT_OK;
 }
 
+// Forward pass of one micro-batch [B, T] up to the final LayerNorm (w.lnf),
+// keeping every activation the backward pass and the key/value caches read.
+void forward_pass(gpt_handle* h, const int32_t* tok, int B, int T) {
+    const gpt_config& c = h->cfg;
+    Ws& w = h->ws;
+    const Table& tb = h->tb;
+    hipStream_t st = h->stream;
+    const int M = B * T, d = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size, H = c.n_head;
+    const int hd = d / H, L = c.n_layer;
+    const bool bf = c.precision == GPT_PREC_BF16;
+    const double ab = bf ? 2 : 4;
+    const bool qkt = qk_transform(c);
+    {
+        Timed t(h, KC_EMBED_FWD, 0, (double)M * d * (tb.wpe >= 0 ? 12 : 8) + 4.0 * M);
+        gk::embed_fwd(tok, P(h, tb.wte), tb.wpe >= 0 ? P(h, tb.wpe) : nullptr, w.x_in[0], M, T, d, Vp, w.err, st);
+    }
+    for (int l = 0; l < L; ++l) {
+        const LayerIdx& li = tb.layers[l];
+        float* mean1 = w.ln_mean + (size_t)(2 * l) * M;
+        float* rstd1 = w.ln_rstd + (size_t)(2 * l) * M;
+        float* mean2 = w.ln_mean + (size_t)(2 * l + 1) * M;
+        float* rstd2 = w.ln_rstd + (size_t)(2 * l + 1) * M;
+        {
+            Timed t(h, KC_LN_FWD, 0, (double)M * d * (4 + ab) + 8.0 * M);
+            gk::layernorm_fwd(bf, w.x_in[l], P(h, li.ln1_w), P(h, li.ln1_b), w.ln1[l], mean1, rstd1, M, d, c.ln_eps, st);
+        }
+        {
+            gk::Gemm g = mk_gemm(h, M, 3 * d, d, w.ln1[l], d, true, Wop(h, li.attn_w), d, true, w.qkv[l], 3 * d, bf,
+                                 gk::EPI_BIAS);
+            g.bias = P(h, li.attn_b);
+            run_gemm(h, KC_GEMM_FWD, g);
+        }
+        const void *q = w.qkv[l], *k = (const char*)w.qkv[l] + (size_t)ab * d;
+        int64_t ldq = 3 * d, ldk = 3 * d;
+        if (qkt) {
+            Timed t(h, KC_QK_PREP, 0, (double)M * 2 * d * 2 * ab);
+            gk::qk_prep_fwd(bf, w.qkv[l], w.qk[l], w.rope_cos, w.rope_sin, M, T, H, hd, c.qk_rmsnorm,
+                            c.pos_encoding == GPT_POS_ROPE, c.qk_norm_eps, st);
+            q = w.qk[l];
+            k = (const char*)w.qk[l] + (size_t)ab * d;
+            ldq = ldk = 2 * d;
+        }
+        gk::Attn a{};
+        a.B = B; a.T = T; a.H = H; a.hd = hd; a.window = window_of(c, l);
+        a.q = q; a.k = k; a.v = (const char*)w.qkv[l] + (size_t)ab * 2 * d;
+        a.ldq = ldq; a.ldk = ldk; a.ldv = 3 * d;
+        a.o = w.att[l]; a.ldo = d; a.lse = w.lse[l]; a.bf = bf;
+        {
+            double pairs = attn_pairs(B, T, H, a.window);
+            Timed t(h, KC_ATTN_FWD, 4.0 * hd * pairs, (double)M * d * 4 * ab + 4.0 * M * H);
+            gk::attention_fwd(a, st);
+        }
+        {
+            gk::Gemm g = mk_gemm(h, M, d, d, w.att[l], d, true, Wop(h, li.proj_w), d, true, w.x_mid[l], d, false,
+                                 gk::EPI_BIAS_RESID);
+            g.bias = P(h, li.proj_b);
+            g.resid = w.x_in[l];
+            run_gemm(h, KC_GEMM_FWD, g);
+        }
+        {
+            Timed t(h, KC_LN_FWD, 0, (double)M * d * (4 + ab) + 8.0 * M);
+            gk::layernorm_fwd(bf, w.x_mid[l], P(h, li.ln2_w), P(h, li.ln2_b), w.ln2[l], mean2, rstd2, M, d, c.ln_eps, st);
+        }
+        {
+            gk::Gemm g = mk_gemm(h, M, F, d, w.ln2[l], d, true, Wop(h, li.fc_w), d, true, w.hdact[l], F, bf,
+                                 gk::EPI_BIAS_ACT);
+            g.bias = P(h, li.fc_b);
+            g.C2 = w.hact[l];
+            run_gemm(h, KC_GEMM_FWD, g);
+        }
+        {
+            float* xo = (l + 1 < L) ? w.x_in[l + 1] : w.x_fin;
+            gk::Gemm g = mk_gemm(h, M, d, F, w.hact[l], F, true, Wop(h, li.mp_w), F, true, xo, d, false,
+                                 gk::EPI_BIAS_RESID);
+            g.bias = P(h, li.mp_b);
+            g.resid = w.x_mid[l];
+            run_gemm(h, KC_GEMM_FWD, g);
+        }
+    }
+    float* meanf = w.ln_mean + (size_t)(2 * L) * M;
+    float* rstdf = w.ln_rstd + (size_t)(2 * L) * M;
+    {
+        Timed t(h, KC_LN_FWD, 0, (double)M * d * (4 + ab) + 8.0 * M);
+        gk::layernorm_fwd(bf, w.x_fin, P(h, tb.lnf_w), P(h, tb.lnf_b), w.lnf, meanf, rstdf, M, d, c.ln_eps, st);
+    }
+}
+
 gpt_status copy_tensor(gpt_handle* h, float* dst, const float* src, int64_t count, int dir_dev_to_host_buf,
                        int on_device) {
     (void)dir_dev_to_host_buf;
@@ -621,79 +732,9 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         if (s != GPT_OK) return s;
     }
     // ------------------------------------------------------------ forward
-    {
-        Timed t(h, KC_EMBED_FWD, 0, (double)M * d * (tb.wpe >= 0 ? 12 : 8) + 4.0 * M);
-        gk::embed_fwd(tok, P(h, tb.wte), tb.wpe >= 0 ? P(h, tb.wpe) : nullptr, w.x_in[0], M, T, d, Vp, w.err, st);
-    }
-    for (int l = 0; l < L; ++l) {
-        const LayerIdx& li = tb.layers[l];
-        float* mean1 = w.ln_mean + (size_t)(2 * l) * M;
-        float* rstd1 = w.ln_rstd + (size_t)(2 * l) * M;
-        float* mean2 = w.ln_mean + (size_t)(2 * l + 1) * M;
-        float* rstd2 = w.ln_rstd + (size_t)(2 * l + 1) * M;
-        {
-            Timed t(h, KC_LN_FWD, 0, (double)M * d * (4 + ab) + 8.0 * M);
-            gk::layernorm_fwd(bf, w.x_in[l], P(h, li.ln1_w), P(h, li.ln1_b), w.ln1[l], mean1, rstd1, M, d, c.ln_eps, st);
-        }
-        {
-            gk::Gemm g = mk_gemm(h, M, 3 * d, d, w.ln1[l], d, true, Wop(h, li.attn_w), d, true, w.qkv[l], 3 * d, bf,
-                                 gk::EPI_BIAS);
-            g.bias = P(h, li.attn_b);
-            run_gemm(h, KC_GEMM_FWD, g);
-        }
-        const void *q = w.qkv[l], *k = (const char*)w.qkv[l] + (size_t)ab * d;
-        int64_t ldq = 3 * d, ldk = 3 * d;
-        if (qkt) {
-            Timed t(h, KC_QK_PREP, 0, (double)M * 2 * d * 2 * ab);
-            gk::qk_prep_fwd(bf, w.qkv[l], w.qk[l], w.rope_cos, w.rope_sin, M, T, H, hd, c.qk_rmsnorm,
-                            c.pos_encoding == GPT_POS_ROPE, c.qk_norm_eps, st);
-            q = w.qk[l];
-            k = (const char*)w.qk[l] + (size_t)ab * d;
-            ldq = ldk = 2 * d;
-        }
-        gk::Attn a{};
-        a.B = B; a.T = T; a.H = H; a.hd = hd; a.window = window_of(c, l);
-        a.q = q; a.k = k; a.v = (const char*)w.qkv[l] + (size_t)ab * 2 * d;
-        a.ldq = ldq; a.ldk = ldk; a.ldv = 3 * d;
-        a.o = w.att[l]; a.ldo = d; a.lse = w.lse[l]; a.bf = bf;
-        {
-            double pairs = attn_pairs(B, T, H, a.window);
-            Timed t(h, KC_ATTN_FWD, 4.0 * hd * pairs, (double)M * d * 4 * ab + 4.0 * M * H);
-            gk::attention_fwd(a, st);
-        }
-        {
-            gk::Gemm g = mk_gemm(h, M, d, d, w.att[l], d, true, Wop(h, li.proj_w), d, true, w.x_mid[l], d, false,
-                                 gk::EPI_BIAS_RESID);
-            g.bias = P(h, li.proj_b);
-            g.resid = w.x_in[l];
-            run_gemm(h, KC_GEMM_FWD, g);
-        }
-        {
-            Timed t(h, KC_LN_FWD, 0, (double)M * d * (4 + ab) + 8.0 * M);
-            gk::layernorm_fwd(bf, w.x_mid[l], P(h, li.ln2_w), P(h, li.ln2_b), w.ln2[l], mean2, rstd2, M, d, c.ln_eps, st);
-        }
-        {
-            gk::Gemm g = mk_gemm(h, M, F, d, w.ln2[l], d, true, Wop(h, li.fc_w), d, true, w.hdact[l], F, bf,
-                                 gk::EPI_BIAS_ACT);
-            g.bias = P(h, li.fc_b);
-            g.C2 = w.hact[l];
-            run_gemm(h, KC_GEMM_FWD, g);
-        }
-        {
-            float* xo = (l + 1 < L) ? w.x_in[l + 1] : w.x_fin;
-            gk::Gemm g = mk_gemm(h, M, d, F, w.hact[l], F, true, Wop(h, li.mp_w), F, true, xo, d, false,
-                                 gk::EPI_BIAS_RESID);
-            g.bias = P(h, li.mp_b);
-            g.resid = w.x_mid[l];
-            run_gemm(h, KC_GEMM_FWD, g);
-        }
-    }
+    forward_pass(h, tok, B, T);
     float* meanf = w.ln_mean + (size_t)(2 * L) * M;
     float* rstdf = w.ln_rstd + (size_t)(2 * L) * M;
-    {
-        Timed t(h, KC_LN_FWD, 0, (double)M * d * (4 + ab) + 8.0 * M);
-        gk::layernorm_fwd(bf, w.x_fin, P(h, tb.lnf_w), P(h, tb.lnf_b), w.lnf, meanf, rstdf, M, d, c.ln_eps, st);
-    }
     {
         gk::Gemm g = mk_gemm(h, M, Vp, d, w.lnf, d, true, Wop(h, tb.wte), d, true, w.logits, Vp, bf, gk::EPI_STORE);
         run_gemm(h, KC_GEMM_LMHEAD, g);
@@ -896,6 +937,112 @@ gpt_status gpt_loss_accum(gpt_handle* h, float* out) {
     if (s != GPT_OK) return s;
     *out = h->micro_count ? sum / h->micro_count : 0.f;
     return GPT_OK;
+}
+
+gpt_status gpt_generate(gpt_handle* h, const int32_t* prompt, int32_t B, int32_t T0, int32_t n_new,
+                        float temperature, int32_t top_k, uint64_t seed, int32_t* out, float* logits_out) {
+    if (!h) return GPT_ERR_INVALID_ARGUMENT;
+    const gpt_config& c = h->cfg;
+    if (!prompt || !out) return fail(h, GPT_ERR_INVALID_ARGUMENT, "null prompt or output buffer");
+    if (B < 1 || B > c.max_batch) return fail(h, GPT_ERR_INVALID_ARGUMENT, "B must be in [1, max_batch]");
+    if (T0 < 1 || n_new < 0 || (int64_t)T0 + n_new > c.block_size)
+        return fail(h, GPT_ERR_INVALID_ARGUMENT, "need T0 >= 1, n_new >= 0 and T0 + n_new <= block_size");
+    if (!(temperature >= 0.f) || !std::isfinite(temperature) || top_k < 0)
+        return fail(h, GPT_ERR_INVALID_ARGUMENT, "temperature must be finite and >= 0, top_k >= 0");
+    Ws& w = h->ws;
+    const Table& tb = h->tb;
+    hipStream_t st = h->stream;
+    const int d = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size, H = c.n_head, hd = d / H, L = c.n_layer;
+    const int Tm = c.block_size, Ttot = T0 + n_new;
+    const bool bf = c.precision == GPT_PREC_BF16, qkt = qk_transform(c);
+    const size_t ab = bf ? 2 : 4;
+    gpt_status s = hip_check(h, hipMemcpy2DAsync(out, sizeof(int32_t) * Ttot, prompt, sizeof(int32_t) * T0,
+                                                 sizeof(int32_t) * T0, B, hipMemcpyDeviceToDevice, st),
+                             "copy prompt");
+    if (s != GPT_OK) return s;
+    if (n_new > 0) {
+        // prefill: the training forward over the prompt, then its keys and
+        // values (q/k-transformed keys for rotary / QK-norm models) into the caches
+        forward_pass(h, prompt, B, T0);
+        for (int l = 0; l < L; ++l) {
+            const void* ks = qkt ? (const char*)w.qk[l] + ab * d : (const char*)w.qkv[l] + ab * d;
+            gk::cache_put(bf, ks, qkt ? 2 * d : 3 * d, w.kcache[l], B, T0, Tm, 0, d, st);
+            gk::cache_put(bf, (const char*)w.qkv[l] + ab * 2 * d, 3 * d, w.vcache[l], B, T0, Tm, 0, d, st);
+        }
+        // logits of each sequence's last prompt position: rows b T0 + T0 - 1 of the final LayerNorm output
+        {
+            gk::Gemm g = mk_gemm(h, B, Vp, d, (const char*)w.lnf + ab * (size_t)(T0 - 1) * d, (int64_t)T0 * d, true,
+                                 Wop(h, tb.wte), d, true, w.dec_logits, Vp, false, gk::EPI_STORE);
+            run_gemm(h, KC_MISC, g);
+        }
+        gk::gen_sample(w.dec_logits, B, Vp, c.logit_softcap, temperature, top_k, seed, 0, out, Ttot, T0,
+                       logits_out, st);
+        for (int step = 1; step < n_new; ++step) {
+            const int pos = T0 + step - 1;   // position of the token drawn last
+            gk::gen_embed(out, Ttot, pos, P(h, tb.wte), tb.wpe >= 0 ? P(h, tb.wpe) : nullptr, w.dec_x, B, d, Vp,
+                          w.err, st);
+            for (int l = 0; l < L; ++l) {
+                const LayerIdx& li = tb.layers[l];
+                gk::layernorm_fwd(bf, w.dec_x, P(h, li.ln1_w), P(h, li.ln1_b), w.dec_y, w.dec_mean, w.dec_rstd, B, d,
+                                  c.ln_eps, st);
+                {
+                    gk::Gemm g = mk_gemm(h, B, 3 * d, d, w.dec_y, d, true, Wop(h, li.attn_w), d, true, w.dec_qkv,
+                                         3 * d, bf, gk::EPI_BIAS);
+                    g.bias = P(h, li.attn_b);
+                    run_gemm(h, KC_MISC, g);
+                }
+                const void* q = w.dec_qkv;
+                const void* kn = (const char*)w.dec_qkv + ab * d;
+                int64_t ldq = 3 * d;
+                if (qkt) {
+                    gk::qk_prep_fwd(bf, w.dec_qkv, w.dec_qk, w.rope_cos, w.rope_sin, B, 1, H, hd, c.qk_rmsnorm,
+                                    c.pos_encoding == GPT_POS_ROPE, c.qk_norm_eps, st, pos);
+                    q = w.dec_qk;
+                    kn = (const char*)w.dec_qk + ab * d;
+                    ldq = 2 * d;
+                }
+                gk::cache_put(bf, kn, ldq, w.kcache[l], B, 1, Tm, pos, d, st);
+                gk::cache_put(bf, (const char*)w.dec_qkv + ab * 2 * d, 3 * d, w.vcache[l], B, 1, Tm, pos, d, st);
+                gk::gen_attention(bf, q, ldq, w.kcache[l], w.vcache[l], w.dec_att, B, H, hd, pos, Tm, window_of(c, l),
+                                  st);
+                {
+                    gk::Gemm g = mk_gemm(h, B, d, d, w.dec_att, d, true, Wop(h, li.proj_w), d, true, w.dec_x2, d, false,
+                                         gk::EPI_BIAS_RESID);
+                    g.bias = P(h, li.proj_b);
+                    g.resid = w.dec_x;
+                    run_gemm(h, KC_MISC, g);
+                }
+                gk::layernorm_fwd(bf, w.dec_x2, P(h, li.ln2_w), P(h, li.ln2_b), w.dec_y, w.dec_mean, w.dec_rstd, B,
+                                  d, c.ln_eps, st);
+                {
+                    gk::Gemm g = mk_gemm(h, B, F, d, w.dec_y, d, true, Wop(h, li.fc_w), d, true, w.dec_h1, F, bf,
+                                         gk::EPI_BIAS_ACT);
+                    g.bias = P(h, li.fc_b);
+                    g.C2 = w.dec_h2;
+                    run_gemm(h, KC_MISC, g);
+                }
+                {
+                    gk::Gemm g = mk_gemm(h, B, d, F, w.dec_h2, F, true, Wop(h, li.mp_w), F, true, w.dec_x, d, false,
+                                         gk::EPI_BIAS_RESID);
+                    g.bias = P(h, li.mp_b);
+                    g.resid = w.dec_x2;
+                    run_gemm(h, KC_MISC, g);
+                }
+            }
+            gk::layernorm_fwd(bf, w.dec_x, P(h, tb.lnf_w), P(h, tb.lnf_b), w.dec_y, w.dec_mean, w.dec_rstd, B, d,
+                              c.ln_eps, st);
+            {
+                gk::Gemm g = mk_gemm(h, B, Vp, d, w.dec_y, d, true, Wop(h, tb.wte), d, true, w.dec_logits, Vp, false,
+                                     gk::EPI_STORE);
+                run_gemm(h, KC_MISC, g);
+            }
+            gk::gen_sample(w.dec_logits, B, Vp, c.logit_softcap, temperature, top_k, seed, step, out, Ttot, pos + 1,
+                           logits_out ? logits_out + (size_t)step * B * Vp : nullptr, st);
+        }
+    }
+    s = hip_check(h, hipGetLastError(), "kernel launch");
+    if (s != GPT_OK) return s;
+    return sync_and_check(h);
 }
 
 gpt_status gpt_clip_and_adamw(gpt_handle* h, float lr, int32_t step, float* h_grad_norm) {

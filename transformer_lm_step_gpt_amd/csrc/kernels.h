@@ -104,12 +104,29 @@ void mean_loss(const float* row_loss, int M, float* loss_out, float* loss_sum, h
 // D[b, h, t] = sum_c dO[m, h*hd + c] * O[m, h*hd + c]
 void attn_rowdot(bool bf, const void* dO, const void* O, float* D, int B, int T, int H, int hd, hipStream_t s);
 // q/k RMS normalisation (no gain) then rotary rotation, per head.
-// fwd: reads q,k from qkv [M, 3d], writes qk_out [M, 2d].
+// fwd: reads q,k from qkv [M, 3d], writes qk_out [M, 2d]; row m is at
+// position pos0 + m % T.
 void qk_prep_fwd(bool bf, const void* qkv, void* qk_out, const float* cos_t, const float* sin_t, int M, int T,
-                 int H, int hd, int norm, int rope, float eps, hipStream_t s);
+                 int H, int hd, int norm, int rope, float eps, hipStream_t s, int pos0 = 0);
 // bwd: in place on the q,k columns of dqkv [M, 3d], raw q,k re-read from qkv.
 void qk_prep_bwd(bool bf, const void* qkv, void* dqkv, const float* cos_t, const float* sin_t, int M, int T,
                  int H, int hd, int norm, int rope, float eps, hipStream_t s);
+
+// ---------------------------------------------------------------- sampling with a key/value cache
+// x[b] = wte[seq[b * ld + pos]] + wpe[pos] (wpe nullable); invalid ids set *err.
+void gen_embed(const int32_t* seq, int64_t ld, int pos, const float* wte, const float* wpe, float* x, int B, int d,
+               int Vp, int32_t* err, hipStream_t s);
+// cache rows: dst[(b Tmax + t0 + t) d + c] = src[(b nt + t) src_ld + c] (act), d % 8 == 0
+void cache_put(bool bf, const void* src, int64_t src_ld, void* dst, int B, int nt, int Tmax, int t0, int d,
+               hipStream_t s);
+// out [B, d] (act): per (b, head) softmax(q k^T / sqrt(hd)) v over cached keys
+// j0 .. pos (j0 = pos - window + 1 with a window, else 0); caches [B, Tmax, d]
+void gen_attention(bool bf, const void* q, int64_t ldq, const void* kc, const void* vc, void* out, int B, int H,
+                   int hd, int pos, int Tmax, int window, hipStream_t s);
+// One draw per row of fp32 logits [B, Vp] (softcapped in place when cap > 0,
+// copied to logits_out when non-null) into seq[b * ld_seq + pos_out].
+void gen_sample(float* logits, int B, int Vp, float cap, float temperature, int top_k, uint64_t seed, int step,
+                int32_t* seq, int64_t ld_seq, int pos_out, float* logits_out, hipStream_t s);
 
 // ---------------------------------------------------------------- optimiser
 // norm = sqrt(sum g^2); coef = min(1, max_norm / (norm + 1e-6)); *skip = 1 when

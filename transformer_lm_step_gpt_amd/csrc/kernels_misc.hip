@@ -1082,7 +1082,7 @@ void attn_rowdot(bool bf, const void* dO, const void* O, float* D, int B, int T,
 template <typename T>
 __global__ __launch_bounds__(256) void qk_prep_fwd_kernel(const T* qkv, T* out, const float* cos_t,
                                                           const float* sin_t, int M, int T_, int H, int hd,
-                                                          int norm, int rope, float eps) {
+                                                          int norm, int rope, float eps, int pos0) {
     int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (wid >= M * H * 2) return;
     int which = wid & 1, mh = wid >> 1, m = mh / H, h = mh % H;
@@ -1097,7 +1097,7 @@ __global__ __launch_bounds__(256) void qk_prep_fwd_kernel(const T* qkv, T* out, 
         a *= r; b *= r;
     }
     if (rope && act) {
-        int t = m % T_;
+        int t = pos0 + m % T_;
         float c = cos_t[t * half + lane], sn = sin_t[t * half + lane];
         float na = a * c - b * sn, nb = a * sn + b * c;
         a = na; b = nb;
@@ -1136,14 +1136,14 @@ __global__ __launch_bounds__(256) void qk_prep_bwd_kernel(const T* qkv, T* dqkv,
 }
 
 void qk_prep_fwd(bool bf, const void* qkv, void* out, const float* cos_t, const float* sin_t, int M, int T, int H,
-                 int hd, int norm, int rope, float eps, hipStream_t s) {
+                 int hd, int norm, int rope, float eps, hipStream_t s, int pos0) {
     int grid = ceil_div((int64_t)M * H * 2, 4);
     if (bf)
         qk_prep_fwd_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)qkv, (bf16*)out, cos_t, sin_t, M, T, H, hd, norm,
-                                                      rope, eps);
+                                                      rope, eps, pos0);
     else
         qk_prep_fwd_kernel<float><<<grid, 256, 0, s>>>((const float*)qkv, (float*)out, cos_t, sin_t, M, T, H, hd,
-                                                       norm, rope, eps);
+                                                       norm, rope, eps, pos0);
 }
 void qk_prep_bwd(bool bf, const void* qkv, void* dqkv, const float* cos_t, const float* sin_t, int M, int T, int H,
                  int hd, int norm, int rope, float eps, hipStream_t s) {

@@ -71,6 +71,8 @@ _SIGS = [
     ("gpt_forward_backward", c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_float, POINTER(c_float)]),
     ("gpt_loss_accum", c_int32, [c_void_p, POINTER(c_float)]),
     ("gpt_clip_and_adamw", c_int32, [c_void_p, c_float, c_int32, POINTER(c_float)]),
+    ("gpt_generate", c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_float, c_int32, c_uint64, c_void_p,
+                               c_void_p]),
     ("gpt_num_tensors", c_int32, [c_void_p, POINTER(c_int32)]),
     ("gpt_tensor_info", c_int32, [c_void_p, c_int32, POINTER(c_char_p), POINTER(c_int32), POINTER(c_int64),
                                   POINTER(c_int32)]),
@@ -246,6 +248,23 @@ class GPT:
         norm = c_float()
         check(self.lib.gpt_clip_and_adamw(self.handle, lr, step, byref(norm) if sync else None), self.handle)
         return norm.value if sync else None
+
+    def generate(self, prompt, n_new: int, temperature: float = 1.0, top_k: int = 50, seed: int = 0,
+                 return_logits: bool = False):
+        """Sampling with the key/value cache (gpt_generate): returns int32
+        [B, T0 + n_new] (numpy) and, on request, the fp32 logits of every draw
+        [n_new, B, padded_vocab_size]."""
+        torch = self.torch
+        self._sync_stream()
+        p = self._device_tokens(prompt)
+        B, T0 = p.shape
+        out = torch.empty((B, T0 + n_new), dtype=torch.int32, device=self.device)
+        lg = (torch.empty((n_new, B, self.cfg.padded_vocab_size), dtype=torch.float32, device=self.device)
+              if return_logits else None)
+        check(self.lib.gpt_generate(self.handle, _ptr(p), B, T0, n_new, temperature, top_k, c_uint64(seed),
+                                    _ptr(out), _ptr(lg) if lg is not None else None), self.handle)
+        toks = out.cpu().numpy()
+        return (toks, lg.cpu().numpy()) if return_logits else toks
 
     def loss_accum(self) -> float:
         out = c_float()

@@ -315,6 +315,45 @@ def cross_entropy_fwd_bwd(z, y, scale):
 
 
 # ----------------------------------------------------------------------------
+# FP8 head (speedrun technique list: FP8 matmul for the output head)
+# ----------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3(x):
+    """Round to the nearest OCP FP8 E4M3 value, ties to even: 3 mantissa bits,
+    exponent bias 7, normal numbers down to 2^-6, subnormal steps of 2^-9,
+    largest finite 448 (no infinities; larger magnitudes saturate to 448)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    step = 2.0 ** (np.maximum(e, -6.0) - 3.0)      # spacing of the binade holding a
+    q = np.minimum(np.round(a / step) * step, E4M3_MAX)   # numpy rounds halves to even
+    return np.copysign(q, x)
+
+
+def fp8_scale(t):
+    """Per-tensor scale 448 / max|t| in fp32 (1 for an all-zero tensor)."""
+    amax = np.float32(np.abs(np.asarray(t)).max())
+    return np.float32(1.0) if amax == 0 else np.float32(E4M3_MAX) / amax
+
+
+def fp8_quantize(t, s):
+    """e4m3 codes of t * s with the product rounded to fp32 first; returned as values."""
+    return e4m3(np.asarray(t).astype(np.float32) * np.float32(s))
+
+
+def fp8_head_logits(xf, wte):
+    """z = xf wte^T with both operands quantised to e4m3 under per-tensor scales
+    s_x = 448 / max|xf|, s_w = 448 / max|wte| (a reading: the README names the
+    technique and an asymmetric rescale but no recipe), the products summed
+    exactly and the result divided by s_x s_w."""
+    sx, sw = fp8_scale(xf), fp8_scale(wte)
+    return (fp8_quantize(xf, sx) @ fp8_quantize(wte, sw).T) / (np.float64(sx) * np.float64(sw))
+
+
+# ----------------------------------------------------------------------------
 # model forward + backward
 # ----------------------------------------------------------------------------
 
@@ -380,7 +419,9 @@ def forward_backward(params, tokens, targets, cfg, grad_scale=1.0, want_grads=Tr
             progress(f"oracle forward layer {l}")
 
     xf, lnf_cache = layernorm_fwd(x, params["ln_f.weight"], params["ln_f.bias"], cfg.ln_eps)
-    zraw = xf @ wte.T
+    # FP8 head: the forward product only; the backward takes the unquantised
+    # operands (straight-through)
+    zraw = fp8_head_logits(xf, wte) if getattr(cfg, "head_fp8", False) else xf @ wte.T
     cap = cfg.logit_softcap
     if cap:
         th = np.tanh(zraw / cap)

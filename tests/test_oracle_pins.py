@@ -364,6 +364,17 @@ def _torch_logits(P, tokens, cfg, untie=False):
         x = x + F.linear(h, P[p + "mlp.c_proj.weight"], P[p + "mlp.c_proj.bias"])
     x = F.layer_norm(x, (d,), P["ln_f.weight"], P["ln_f.bias"], cfg.ln_eps)
     z = F.linear(x, P["lm_head"] if untie else P["wte"])
+    if getattr(cfg, "head_fp8", False):
+        # forward on float8_e4m3fn operands under per-tensor fp32 scales, gradient
+        # of the unquantised product (straight-through)
+        wt = P["lm_head"] if untie else P["wte"]
+
+        def q(t):
+            tf = t.detach().float()
+            s_ = torch.tensor(448.0) / tf.abs().max()
+            return (tf * s_).to(torch.float8_e4m3fn).double(), float(s_)
+        (xq, sx), (wq, sw) = q(x), q(wt)
+        z = z + ((xq @ wq.T) / (sx * sw) - z).detach()
     if cfg.logit_softcap:
         z = cfg.logit_softcap * torch.tanh(z / cfg.logit_softcap)
     return z
@@ -377,7 +388,9 @@ def _perturbed_params(cfg, seed):
     return {k: v + 0.05 * rng.normal(size=v.shape) for k, v in p.items()}
 
 
-@pytest.mark.parametrize("cfg", [TINY, TINY_SPEED], ids=["gpt2_tiny", "speedrun_tiny"])
+@pytest.mark.parametrize("cfg", [TINY, TINY_SPEED, TINY.replace(head_fp8=True),
+                                 TINY_SPEED.replace(head_fp8=True)],
+                         ids=["gpt2_tiny", "speedrun_tiny", "gpt2_tiny_fp8_head", "speedrun_tiny_fp8_head"])
 def test_model_forward_backward_vs_torch_autograd(cfg):
     params = _perturbed_params(cfg, 11)
     rng = np.random.default_rng(12)
@@ -678,4 +691,42 @@ def test_generate_greedy_continuation_is_consistent():
 def test_generate_rejects_overlong_context():
     with pytest.raises(ValueError):
         O.generate(_perturbed_params(TINY, 1), np.zeros((1, TINY.block_size), np.int32), TINY, 1, 1.0, 0, 0)
+
+
+# ---------------------------------------------------------------- FP8 head
+
+def test_e4m3_rounding_matches_torch_float8():
+    """e4m3 against torch's float8_e4m3fn cast (round to nearest even) on
+    normals, subnormals, halfway cases and the range ends."""
+    rng = np.random.default_rng(12)
+    v = np.concatenate([rng.normal(size=4000) * 60, rng.normal(size=2000) * 0.01, rng.uniform(-448, 448, 2000),
+                        [1.0625, 1.1875, 0.001953125, 0.0029296875, 0.00390625 * 1.5, 448.0, -448.0, 0.0, -0.0,
+                         240.0, 232.0, 0.015625, 0.0146484375]])
+    v = np.clip(v, -448, 448).astype(np.float32).astype(np.float64)
+    ref = torch.tensor(v, dtype=torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(O.e4m3(v), ref)
+    # hand-worked: halfway 1.0625 -> 1.0 (even), 1.1875 -> 1.25 (even); smallest subnormal 2^-9;
+    # 2^-10 is halfway between 0 and 2^-9 -> 0 (even); saturation above 448
+    assert list(O.e4m3([1.0625, 1.1875, 2.0 ** -9, 2.0 ** -10, 460.0, -500.0])) == [1.0, 1.25, 2.0 ** -9, 0.0,
+                                                                                     448.0, -448.0]
+
+
+def test_fp8_head_logits_quantisation():
+    """Operands already on the e4m3 grid at scale 1 (max |value| 448) are kept
+    exactly, so the product is exact; otherwise the result equals torch's
+    float8_e4m3fn quantisation of the fp32-scaled operands."""
+    rng = np.random.default_rng(13)
+    x = O.e4m3(rng.uniform(-448, 448, (7, 32)))
+    w = O.e4m3(rng.uniform(-448, 448, (9, 32)))
+    x[0, 0], w[0, 0] = 448.0, -448.0
+    assert np.array_equal(O.fp8_head_logits(x, w), x @ w.T)
+    x = rng.normal(size=(7, 32))
+    w = rng.normal(size=(9, 32)) * 0.02
+    sx = np.float32(448) / np.float32(np.abs(x).max())
+    sw = np.float32(448) / np.float32(np.abs(w).max())
+    q = lambda a, s_: (torch.tensor(a.astype(np.float32)) * torch.tensor(s_)).to(torch.float8_e4m3fn).double()
+    ref = (q(x, sx) @ q(w, sw).T).numpy() / (float(sx) * float(sw))
+    assert np.allclose(O.fp8_head_logits(x, w), ref, rtol=1e-12, atol=0)
+    # and the quantised head stays close to the exact product (3 mantissa bits)
+    assert np.abs(O.fp8_head_logits(x, w) - x @ w.T).max() <= 0.1 * np.abs(x @ w.T).max()
 

@@ -60,6 +60,7 @@ class ModelConfig:
     window_odd: int = 0
     logit_softcap: float = 0.0       # 0 = off
     zero_init_proj: bool = False
+    head_fp8: bool = False           # lm_head forward product on e4m3 operands
     ln_eps: float = 1e-5
     qk_norm_eps: float = 1e-6
     rope_base: float = 10000.0

@@ -262,6 +262,49 @@ def pmc_table(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernel_json):
         print(f"algorithmic {unit} per launch (mean over its launches): {per:.0f}")
 
 
+def generate_bench(a):
+    """Sampling with the key/value cache on the 124M model (a second workload,
+    not the headline): B sequences of a T0-token prompt, n_new tokens each,
+    top-k 50, temperature 1. A decode step is HBM-bound: it reads every bf16
+    weight matrix once (the tied head included) plus the cached keys and values
+    of the tokens so far."""
+    import torch
+    from transformer_lm_step_gpt_amd import inputs as I
+    from transformer_lm_step_gpt_amd.gpt import GPT
+    w = I.GPT2_124M
+    cfg = w.model
+    B, T0, n_new = cfg.max_batch, 128, 128
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    model = GPT(cfg, seed=w.init_seed, device=dev)
+    prompt = torch.tensor(next(I.batches(w, B, T0))[0], device=dev)
+    for _ in range(2):
+        model.generate(prompt, n_new, 1.0, 50, 1)
+    reps = max(1, a.steps // 5)
+    t0 = time.perf_counter()
+    for r in range(reps):
+        model.generate(prompt, 1, 1.0, 50, r)
+    t_prefill = (time.perf_counter() - t0) / reps
+    t0 = time.perf_counter()
+    for r in range(reps):
+        model.generate(prompt, n_new, 1.0, 50, r)
+    t_all = (time.perf_counter() - t0) / reps
+    step_s = (t_all - t_prefill) / (n_new - 1)
+    d, L = cfg.n_embd, cfg.n_layer
+    per_layer_w = 3 * d * d + d * d + 2 * cfg.mlp_hidden * d
+    weight_bytes = 2.0 * (L * per_layer_w + cfg.padded_vocab_size * d)
+    mean_pos = T0 + n_new / 2
+    cache_bytes = 2.0 * B * mean_pos * 2 * d * L
+    achieved = (weight_bytes + cache_bytes) / step_s / 1e9
+    print(json.dumps({
+        "metric": "decode tokens/s, sampling with a key/value cache (GPT-2 124M bf16, B=16, prompt 128, 128 new, "
+                  "top-k 50)", "value": round(B / step_s, 1), "unit": "tokens/s", "ms_per_decode_step": round(1e3 * step_s, 4),
+        "prefill_ms": round(1e3 * t_prefill, 3), "higher_is_better": True, "dtype": "bf16", "n_gpus": 1,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes_per_step": round(weight_bytes + cache_bytes)}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +317,10 @@ def main():
     ap.add_argument("--rocprof-summary", metavar="DIR", help="print a table from a rocprofv3 --stats output dir")
     ap.add_argument("--trace-gaps", metavar="DIR", help="idle time per step from a rocprofv3 --kernel-trace output "
                                                          "dir (the last --steps steps)")
+    ap.add_argument("--head-fp8", action="store_true", help="the same step with the FP8 head (e4m3 lm_head "
+                                                              "forward product; a separate line, not the headline)")
+    ap.add_argument("--generate", action="store_true", help="time sampling with the key/value cache instead "
+                                                               "(a second workload; prints its own line)")
     ap.add_argument("--kernel-json", metavar="PATH", help="write the per-class and per-kernel timings of the "
                                                           "all-launches-timed step to PATH")
     ap.add_argument("--pmc-table", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR",
@@ -292,6 +339,9 @@ def main():
     if a.copy_calibration:
         copy_calibration()
         return
+    if a.generate:
+        generate_bench(a)
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: the step runs on exactly one GPU (asked for {a.gpus}); the multi-GPU data-parallel "
               "path is a design, not an implementation.", file=sys.stderr)
@@ -302,7 +352,7 @@ def main():
     from transformer_lm_step_gpt_amd.gpt import GPT
 
     w = I.WORKLOADS[a.workload]
-    cfg = w.model
+    cfg = w.model.replace(head_fp8=True) if a.head_fp8 else w.model
     B, T = w.batch, w.seq_len
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -404,9 +454,10 @@ def main():
                     print(f"{r['name'][:width]:>{width}s} {r['ms']:9.3f} ms {100 * r['ms'] / tot:5.1f}% "
                           f"x{r['launches']:4d} {rate}", file=sys.stderr)
     out = {
-        "metric": METRIC, "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "metric": METRIC + ("; FP8 head (e4m3 lm_head forward)" if a.head_fp8 else ""), "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(1e3 * dt / a.steps, 3), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg.precision == "bf16" else "fp32",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": ("bf16+fp8 head" if a.head_fp8 else "bf16") if cfg.precision == "bf16" else "fp32",
         "data": "synthetic (seeded Zipf(1.1) tokens with end-of-text document starts; random-init weights)",
         "config": {"workload": f"{w.name}: {w.description}", "global_batch": B * w.accum, "seq_len": T,
                    "parallelism": "single GPU"},

@@ -63,7 +63,9 @@ enum { GPT_ACT_GELU_TANH = 0, GPT_ACT_RELU2 = 1 };
  * sliding-window causal attention with window_even/window_odd keys on
  * even/odd layers (0 = plain causal), a tanh logit softcap
  * (logit_softcap * tanh(z / logit_softcap); 0 = off) and zero-initialised
- * output projections (zero_init_proj).
+ * output projections (zero_init_proj). The same list names an FP8 matmul for
+ * the output head: head_fp8 computes z = LN_f(x) wte^T from e4m3 copies of
+ * both operands (the softcap, when set, applies to that z).
  */
 typedef struct gpt_config {
     int32_t n_layer;
@@ -84,7 +86,10 @@ typedef struct gpt_config {
     int32_t window_even;      /* keys visible to query i: j <= i and i - j < W (W > 0) */
     int32_t window_odd;
     int32_t zero_init_proj;   /* 0 or 1 */
-    int32_t reserved0;
+    int32_t head_fp8;         /* 0 or 1: the tied head's forward product on e4m3
+                                 operands with per-tensor scales 448 / max|t| (bf16
+                                 precision, n_embd % 128 == 0); the backward uses the
+                                 bf16 operands */
     float ln_eps;             /* LayerNorm epsilon, biased variance (1e-5) */
     float qk_norm_eps;        /* 1e-6 */
     float rope_base;          /* 10000 */
@@ -112,7 +117,7 @@ gpt_status gpt_config_default(gpt_config* cfg);
  * by n_head, padded_vocab_size < vocab_size), UNSUPPORTED (head dim not in
  * {16, 32, 64, 128}, n_embd % 8 != 0, mlp_hidden % 8 != 0,
  * max_batch * block_size > 32768, padded_vocab_size > 131071,
- * n_embd > 2048). */
+ * n_embd > 2048, head_fp8 with fp32 precision or n_embd % 128 != 0). */
 gpt_status gpt_workspace_bytes(const gpt_config* cfg, size_t* bytes);
 
 /* Create a handle inside d_workspace (device memory of at least

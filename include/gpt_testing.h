@@ -64,6 +64,17 @@ int32_t gptk_gemm_num_configs(void);
  * compare configurations of single products inside the whole step. */
 gpt_status gptk_gemm_tune(int32_t M, int32_t N, int32_t K, int32_t a_kc, int32_t b_kc, int32_t cfg, int32_t splits);
 
+/* The FP8 head's product (Modded-NanoGPT README technique list, FP8 matmul for
+ * the output head): C [M, N] bf16 = (e4m3(A s_a) . e4m3(B s_b)^T) / (s_a s_b)
+ * for bf16 A [M, K] and B [N, K] (row-major, k-contiguous), s = 448 / max|t|
+ * per tensor in fp32, e4m3 rounding to nearest even. K % 128 == 0, N % 8 == 0,
+ * 16-byte aligned buffers; scratch (256-byte aligned) holds
+ * gptk_gemm_fp8_scratch_bytes(M, N, K) bytes: the e4m3 copies, the scales
+ * (floats 0..3: 1/s_a, 1/s_b, s_a, s_b) and the max-reduction partials. */
+gpt_status gptk_gemm_fp8(int32_t M, int32_t N, int32_t K, const void* A, const void* B, void* C, void* scratch,
+                         int64_t scratch_bytes, void* stream);
+int64_t gptk_gemm_fp8_scratch_bytes(int32_t M, int32_t N, int32_t K);
+
 /* Causal (optionally windowed: i - j < window) softmax(Q K^T / sqrt(hd)) V per
  * (batch, head), heads interleaved in the columns of row-major [B*T, *]
  * buffers ("El Mecanismo de Atención"). Forward writes o and lse [B, H, T];

@@ -232,4 +232,17 @@ void gemm_mfma_reduce(const Gemm& g, const GemmPlan& p, const float* scratch, hi
     }
 }
 
+void gemm_f8(int M, int N, int K, const void* A8, int64_t lda, const void* B8, int64_t ldb, void* C, int64_t ldc,
+             const float* inv_sa_sb, hipStream_t s) {
+    Gemm g{};
+    g.M = M; g.N = N; g.K = K / 2;           // the kernel counts 2-byte units
+    g.A = A8; g.lda = lda / 2; g.a_kc = true;
+    g.B = B8; g.ldb = ldb / 2; g.b_kc = true;
+    g.C = C; g.ldc = ldc; g.c_bf = true;
+    g.epi = EPI_STORE;
+    g.in_bf = true;
+    g.out_scale = inv_sa_sb;
+    gemm_mfma_run_f8(g, s);
+}
+
 }  // namespace gk

@@ -45,6 +45,7 @@ namespace {
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int s32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
@@ -203,8 +204,25 @@ __device__ __attribute__((always_inline)) inline void products(f32x16 (&acc)[FM]
     }
 }
 
+// One 64-deep step on e4m3 operands: the FM x FN products of
+// v_mfma_f32_32x32x64_f8f6f4 (32 bytes of A and of B per lane), with the
+// operations of `extra` between them in program order.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+template <int FM, int FN, class X>
+__device__ __attribute__((always_inline)) inline void products_f8(f32x16 (&acc)[FM][FN], const i32x8 (&ca)[FM],
+                                                                 const i32x8 (&cb)[FN], X&& extra) {
+    constexpr int P = FM * FN;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        acc[p / FN][p % FN] =
+            __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ca[p / FN], cb[p % FN], acc[p / FN][p % FN], 0, 0, 0, 0, 0, 0);
+        extra(p);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 constexpr int GROUP_M = 8;
-enum { PIPE_DMA = 0, PIPE_DMA_RS = 1, PIPE_VGPR = 2 };
+enum { PIPE_DMA = 0, PIPE_DMA_RS = 1, PIPE_VGPR = 2, PIPE_F8 = 3 };
 
 // SPLIT: write fp32 partial sums to part[z][M][N] instead of the epilogue.
 // OUTBF: output storage bf16 (1) or fp32 (0); ACT: activation of the
@@ -217,6 +235,10 @@ enum { PIPE_DMA = 0, PIPE_DMA_RS = 1, PIPE_VGPR = 2 };
 //     are read into registers at the start of the tile, so its LDS stage is
 //     refilled one step into the tile instead of at its end (each copy has
 //     about 1.5 k-tiles of products to land instead of one).
+//   PIPE_F8: e4m3 operands (one byte per element, K and the strides counted
+//     in 2-byte units, so a 64-unit k-tile holds 128 values) with LDS-DMA
+//     copies and register-staged fragments, two 64-deep fp8 products per
+//     k-tile; the store epilogue multiplies by out_scale[0] * out_scale[1].
 //   PIPE_VGPR: two LDS stages; the copy of k-tile t+2 is loaded into
 //     registers (16 bytes per lane per copy) while tile t is multiplied, and
 //     written to LDS with ds_write_b128 during tile t+1, so global-load
@@ -398,6 +420,64 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_mfma_kernel(Gemm g, 
             };
             products<FM, FN>(acc, ra[KS - 1], rb[KS - 1], rd0);
         }
+    } else if constexpr (PIPE == PIPE_F8) {
+        // Each v_mfma_f32_32x32x64_f8f6f4 takes 32 bytes of A and of B per lane:
+        // the fragments of two consecutive 16-unit steps, in the lower and upper
+        // halves of an 8-register operand. A and B put the same k positions in
+        // the same lane halves, so the order in which the instruction walks k
+        // inside a lane does not change the sum. Tile t (two fp8 steps):
+        //   fp8 step 0: products | reads of the second step's fragments
+        //   reads done + barrier: every wave is finished with the stage of
+        //     tile t, and the copy of tile t+NS goes into it
+        //   wait + barrier for tile t+1
+        //   fp8 step 1: products | reads of tile t+1's first-step fragments
+        static_assert(KS == 4, "two fp8 steps per k-tile");
+        constexpr int NF = FM + FN, P = FM * FN;
+        i32x8 fa[2][FM], fb[2][FN];
+        auto rdf = [&](const bf16* as, const bf16* bs, int j, int idx) {
+            const int hh = idx / NF, f = idx % NF, ks = 2 * j + hh;
+            if (f < FM) {
+                const u32x4 v = __builtin_bit_cast(u32x4, TA::get(as, wm + 32 * f, ks, lane));
+                if (hh == 0) fa[j][f].lo = __builtin_bit_cast(s32x4, v);
+                else fa[j][f].hi = __builtin_bit_cast(s32x4, v);
+            } else {
+                const u32x4 v = __builtin_bit_cast(u32x4, TB::get(bs, wn + 32 * (f - FM), ks, lane));
+                if (hh == 0) fb[j][f - FM].lo = __builtin_bit_cast(s32x4, v);
+                else fb[j][f - FM].hi = __builtin_bit_cast(s32x4, v);
+            }
+        };
+        if (nk > 0) {
+            wait_tile(0);
+#pragma unroll
+            for (int idx = 0; idx < 2 * NF; ++idx) rdf(smem, smem + TA::BYTES / 2, 0, idx);
+        }
+        for (int t = 0; t < nk; ++t) {
+            const bf16* as = smem + (t % NS) * STAGE;
+            const bf16* bs = as + TA::BYTES / 2;
+            products_f8<FM, FN>(acc, fa[0], fb[0], [&](int p) {
+#pragma unroll
+                for (int idx = 0; idx < 2 * NF; ++idx)
+                    if (idx * P / (2 * NF) == p) rdf(as, bs, 1, idx);
+            });
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            barrier_no_fence();
+            if (issued < nk) {
+                bf16* st = smem + (issued % NS) * STAGE;
+#pragma unroll
+                for (int q = 0; q < LPT; ++q) dma(q, st);
+                ++issued;
+            }
+            if (t + 1 < nk) wait_tile(t + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // on the last tile these reads see a stage that holds no new tile; the values are never used
+            const bf16* an = smem + ((t + 1) % NS) * STAGE;
+            const bf16* bn = an + TA::BYTES / 2;
+            products_f8<FM, FN>(acc, fa[1], fb[1], [&](int p) {
+#pragma unroll
+                for (int idx = 0; idx < 2 * NF; ++idx)
+                    if (idx * P / (2 * NF) == p) rdf(an, bn, 0, idx);
+            });
+        }
     } else if constexpr (PIPE == PIPE_VGPR) {
         // Tile t (stage t % 2):
         //   step 0 .. : the copy of tile t+1 (in registers since tile t-1) is
@@ -545,6 +625,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_mfma_kernel(Gemm g, 
     float bv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) bv[e] = 0.f;
+    float osc = 1.f;
+    if constexpr (PIPE == PIPE_F8) osc = g.out_scale[0] * g.out_scale[1];
     if constexpr (!SPLIT && (EPI == EPI_BIAS || EPI == EPI_BIAS_ACT || EPI == EPI_BIAS_RESID)) {
         if (cin) {
             const float4 b0 = *reinterpret_cast<const float4*>(g.bias + col);
@@ -586,7 +668,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_mfma_kernel(Gemm g, 
                     reinterpret_cast<f32x4*>(p)[0] = u0;
                     reinterpret_cast<f32x4*>(p)[1] = u1;
                 } else {
-                    const float v[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                    float v[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+                    if constexpr (PIPE == PIPE_F8) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] *= osc;
+                    }
                     const EpiIn in = PRE ? pre[PRE ? it : 0] : EpiIn{};
                     if constexpr (CSUM) {
                         float y[8];
@@ -740,5 +826,7 @@ static void run_cfg(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s
 void gemm_mfma_run_kk(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s);
 void gemm_mfma_run_kc(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s);
 void gemm_mfma_run_cc(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s);
+// e4m3 product X W^T (both k-contiguous), bf16 store scaled by out_scale[0] * out_scale[1]
+void gemm_mfma_run_f8(const Gemm& g, hipStream_t s);
 
 }  // namespace gk

@@ -141,6 +141,10 @@ struct Ws {
     // sampling: per-layer key and value caches [max_batch, block_size, d]
     // (act) and the one-token-per-sequence buffers of a decode step
     std::vector<void*> kcache, vcache;
+    // FP8 head: e4m3 copies of the final LayerNorm output and of wte, their
+    // scales [s_x, 1/s_x, s_w, 1/s_w] and the max-reduction partials
+    uint8_t *xq = nullptr, *wq = nullptr;
+    float *f8_scale = nullptr, *f8_part = nullptr;
     float *dec_x = nullptr, *dec_x2 = nullptr, *dec_mean = nullptr, *dec_rstd = nullptr, *dec_logits = nullptr;
     void *dec_y = nullptr, *dec_qkv = nullptr, *dec_qk = nullptr, *dec_att = nullptr, *dec_h1 = nullptr,
          *dec_h2 = nullptr;
@@ -234,6 +238,12 @@ Ws plan(const gpt_config& c, const Table& tb, void* base) {
         w.rope_cos = cv.arr<float>(c.block_size * half);
         w.rope_sin = cv.arr<float>(c.block_size * half);
     }
+    if (c.head_fp8) {
+        w.xq = cv.arr<uint8_t>(M * d);
+        w.wq = cv.arr<uint8_t>(Vp * d);
+        w.f8_scale = cv.arr<float>(4);
+        w.f8_part = cv.arr<float>(2048);
+    }
     for (int l = 0; l < L; ++l) {
         w.kcache.push_back(cv.take(ab * M * d));
         w.vcache.push_back(cv.take(ab * M * d));
@@ -286,6 +296,9 @@ gpt_status validate(const gpt_config* c, std::string* why) {
     if (c->n_embd > 2048) return bad(GPT_ERR_UNSUPPORTED, "n_embd > 2048");
     if ((int64_t)c->max_batch * c->block_size > 32768) return bad(GPT_ERR_UNSUPPORTED, "max_batch * block_size > 32768");
     if (c->padded_vocab_size > 131071) return bad(GPT_ERR_UNSUPPORTED, "padded_vocab_size > 131071");
+    if (c->head_fp8 != 0 && c->head_fp8 != 1) return bad(GPT_ERR_INVALID_ARGUMENT, "head_fp8 must be 0 or 1");
+    if (c->head_fp8 && (c->precision != GPT_PREC_BF16 || c->n_embd % 128))
+        return bad(GPT_ERR_UNSUPPORTED, "head_fp8 needs bf16 precision and n_embd % 128 == 0");
     return GPT_OK;
 }
 
@@ -294,12 +307,12 @@ gpt_status validate(const gpt_config* c, std::string* why) {
 enum KClass {
     KC_EMBED_FWD, KC_LN_FWD, KC_GEMM_FWD, KC_GEMM_LMHEAD, KC_ATTN_FWD, KC_CE, KC_GEMM_DGRAD, KC_GEMM_WGRAD,
     KC_GEMM_LMHEAD_BWD, KC_LN_BWD, KC_COLSUM, KC_ATTN_BWD, KC_QK_PREP, KC_EMBED_BWD, KC_GRAD_NORM, KC_ADAMW,
-    KC_MISC, KC_PARTIAL_REDUCE, KC_COUNT
+    KC_MISC, KC_PARTIAL_REDUCE, KC_FP8_QUANT, KC_COUNT
 };
 const char* kc_names[KC_COUNT] = {
     "embed_fwd", "layernorm_fwd", "gemm_fwd", "gemm_lm_head", "attention_fwd", "cross_entropy", "gemm_dgrad",
     "gemm_wgrad", "gemm_lm_head_bwd", "layernorm_bwd", "colsum", "attention_bwd", "qk_prep", "embed_bwd",
-    "grad_norm", "adamw", "misc", "partial_reduce"};
+    "grad_norm", "adamw", "misc", "partial_reduce", "fp8_quantize"};
 
 struct Pending { int cls; int name; hipEvent_t a, b; double flops, bytes; };
 struct ClassStat { double ms = 0, flops = 0, bytes = 0; int64_t launches = 0; };
@@ -735,7 +748,19 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
     forward_pass(h, tok, B, T);
     float* meanf = w.ln_mean + (size_t)(2 * L) * M;
     float* rstdf = w.ln_rstd + (size_t)(2 * L) * M;
-    {
+    if (c.head_fp8) {
+        // e4m3 copies of both operands: scales at [2] (x) and [3] (wte), their
+        // inverses at [0] and [1], which the product's store multiplies by
+        {
+            Timed t(h, KC_FP8_QUANT, 0, 3.0 * ((double)M + Vp) * d + 8.0 * 1024);
+            gk::quantize_e4m3(w.lnf, (int64_t)M * d, w.xq, w.f8_scale + 2, w.f8_scale, w.f8_part, st);
+            gk::quantize_e4m3(Wop(h, tb.wte), (int64_t)Vp * d, w.wq, w.f8_scale + 3, w.f8_scale + 1,
+                              w.f8_part + 1024, st);
+        }
+        Timed t(h, KC_GEMM_LMHEAD, 2.0 * M * Vp * d, (double)M * d + (double)Vp * d + 2.0 * M * Vp,
+                "gemm_mfma_kernel<256, 256, 64, 2, 1, 3, 2, 4, true, true, 0, 1, 0, false>");
+        gk::gemm_f8(M, Vp, d, w.xq, d, w.wq, d, w.logits, Vp, w.f8_scale, st);
+    } else {
         gk::Gemm g = mk_gemm(h, M, Vp, d, w.lnf, d, true, Wop(h, tb.wte), d, true, w.logits, Vp, bf, gk::EPI_STORE);
         run_gemm(h, KC_GEMM_LMHEAD, g);
     }
@@ -1384,6 +1409,31 @@ gpt_status gptk_cross_entropy(int32_t M, int32_t Vp, void* z, const int32_t* y, 
 }
 
 int64_t gptk_embed_bwd_scratch_bytes(int32_t M, int32_t d) { return (int64_t)gk::embed_bwd_scratch_bytes(M, d); }
+
+int64_t gptk_gemm_fp8_scratch_bytes(int32_t M, int32_t N, int32_t K) {
+    if (M < 1 || N < 1 || K < 1) return 0;
+    return (((int64_t)M * K + 255) / 256 + ((int64_t)N * K + 255) / 256) * 256 + 256 + 2048 * 4;
+}
+
+gpt_status gptk_gemm_fp8(int32_t M, int32_t N, int32_t K, const void* A, const void* B, void* C, void* scratch,
+                         int64_t scratch_bytes, void* stream) {
+    if (M < 1 || N < 1 || K < 128 || K % 128 || N % 8 || !A || !B || !C || !scratch ||
+        scratch_bytes < gptk_gemm_fp8_scratch_bytes(M, N, K) || (uintptr_t)scratch % 256 || (uintptr_t)A % 16 ||
+        (uintptr_t)B % 16 || (uintptr_t)C % 16)
+        return GPT_ERR_INVALID_ARGUMENT;
+    char* p = (char*)scratch;
+    uint8_t* aq = (uint8_t*)p;
+    p += ((int64_t)M * K + 255) / 256 * 256;
+    uint8_t* bq = (uint8_t*)p;
+    p += ((int64_t)N * K + 255) / 256 * 256;
+    float* sc = (float*)p;
+    float* part = sc + 64;
+    hipStream_t s = (hipStream_t)stream;
+    gk::quantize_e4m3(A, (int64_t)M * K, aq, sc + 2, sc, part, s);
+    gk::quantize_e4m3(B, (int64_t)N * K, bq, sc + 3, sc + 1, part + 1024, s);
+    gk::gemm_f8(M, N, K, aq, K, bq, K, C, N, sc, s);
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
 
 gpt_status gptk_embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, int32_t B, int32_t T,
                           int32_t d, int32_t Vp, void* scratch, void* stream) {

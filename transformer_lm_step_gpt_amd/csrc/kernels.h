@@ -161,6 +161,8 @@ struct Gemm {
     int epi;
     int act;
     bool in_bf;                              // A and B storage (bf16 or fp32)
+    // e4m3 products only: the bf16 store is multiplied by out_scale[0] * out_scale[1]
+    const float* out_scale = nullptr;
     // ACT_GRAD epilogue, plans with bm > 0: cpart[(m / bm) * N + n] = sum over
     // the rows m of one bm-row block of the fp32 output values (column sums
     // for a bias gradient, reduced later)
@@ -181,6 +183,16 @@ GemmPlan gemm_plan(const Gemm& g, size_t splitk_floats);
 void gemm_main(const Gemm& g, const GemmPlan& p, float* splitk_scratch, hipStream_t s);
 void gemm_finish(const Gemm& g, const GemmPlan& p, const float* splitk_scratch, hipStream_t s);
 void gemm(const Gemm& g, float* splitk_scratch, size_t splitk_floats, hipStream_t s);
+// e4m3 product for the FP8 head: C [M, N] bf16 (row stride ldc) =
+// (A8 [M, K] . B8 [N, K]^T) * inv_sa * inv_sb, A8 and B8 e4m3 bytes with row
+// strides lda and ldb (bytes), K % 128 == 0, lda % 16 == ldb % 16 == 0.
+void gemm_f8(int M, int N, int K, const void* A8, int64_t lda, const void* B8, int64_t ldb, void* C, int64_t ldc,
+             const float* inv_sa_sb, hipStream_t s);
+// Per-tensor e4m3 quantisation of a bf16 tensor (n % 8 == 0):
+// *scale = 448 / max|x| (1 for an all-zero tensor), *inv = 1 / *scale,
+// q = e4m3(fp32(x) * scale) rounded to nearest even (saturating at 448);
+// part holds 1024 floats.
+void quantize_e4m3(const void* x, int64_t n, uint8_t* q, float* scale, float* inv, float* part, hipStream_t s);
 // test control of the matrix-core tile configuration / split-K (cfg -1: automatic)
 void gemm_mfma_force(int cfg, int splits);
 int gemm_mfma_num_configs();

@@ -1256,4 +1256,64 @@ void adamw(float* p, const float* g, float* m, float* v, void* wbf, int64_t n, i
                                       rbc1, rbc2);
 }
 
+// =====================================================================
+// FP8 head: per-tensor e4m3 quantisation (OCP E4M3, largest finite 448)
+// =====================================================================
+
+constexpr int AMAX_BLOCKS = 1024;
+
+__global__ __launch_bounds__(256) void amax_bf16_kernel(const bf16* __restrict__ x, int64_t n8, float* part) {
+    __shared__ float sh[4];
+    float m = 0.f;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)AMAX_BLOCKS * 256) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + 8 * i);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)v[e]));
+    }
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+
+__global__ __launch_bounds__(256) void amax_final_kernel(const float* part, float* scale, float* inv) {
+    __shared__ float sh[4];
+    float m = 0.f;
+    for (int i = threadIdx.x; i < AMAX_BLOCKS; i += 256) m = fmaxf(m, part[i]);
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float a = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+        const float sc = a > 0.f ? 448.0f / a : 1.0f;
+        *scale = sc;
+        *inv = 1.0f / sc;
+    }
+}
+
+// eight values per thread: fp32 product with the scale, clamped to [-448, 448],
+// converted in pairs to e4m3 (round to nearest even) by v_cvt_pk_fp8_f32
+__global__ __launch_bounds__(256) void quantize_e4m3_kernel(const bf16* __restrict__ x, int64_t n8,
+                                                            const float* __restrict__ scale, uint8_t* __restrict__ q) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const float sc = *scale;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(x + 8 * i);
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = fminf(fmaxf((float)v[e] * sc, -448.0f), 448.0f);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+    *reinterpret_cast<int2*>(q + 8 * i) = make_int2(lo, hi);
+}
+
+void quantize_e4m3(const void* x, int64_t n, uint8_t* q, float* scale, float* inv, float* part, hipStream_t s) {
+    const int64_t n8 = n / 8;
+    amax_bf16_kernel<<<AMAX_BLOCKS, 256, 0, s>>>((const bf16*)x, n8, part);
+    amax_final_kernel<<<1, 256, 0, s>>>(part, scale, inv);
+    quantize_e4m3_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>((const bf16*)x, n8, scale, q);
+}
+
 }  // namespace gk

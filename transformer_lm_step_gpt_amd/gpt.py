@@ -36,7 +36,7 @@ class GptConfig(ctypes.Structure):
         ("n_layer", c_int32), ("n_head", c_int32), ("n_embd", c_int32), ("mlp_hidden", c_int32),
         ("block_size", c_int32), ("vocab_size", c_int32), ("padded_vocab_size", c_int32), ("max_batch", c_int32),
         ("precision", c_int32), ("pos_encoding", c_int32), ("qk_rmsnorm", c_int32), ("mlp_act", c_int32),
-        ("window_even", c_int32), ("window_odd", c_int32), ("zero_init_proj", c_int32), ("reserved0", c_int32),
+        ("window_even", c_int32), ("window_odd", c_int32), ("zero_init_proj", c_int32), ("head_fp8", c_int32),
         ("ln_eps", c_float), ("qk_norm_eps", c_float), ("rope_base", c_float), ("logit_softcap", c_float),
         ("beta1", c_float), ("beta2", c_float), ("adam_eps", c_float), ("weight_decay", c_float),
         ("max_grad_norm", c_float), ("reserved1", c_int32), ("init_std", c_double),
@@ -53,6 +53,7 @@ def to_c_config(cfg: ModelConfig) -> GptConfig:
     c.qk_rmsnorm = int(cfg.qk_rmsnorm)
     c.mlp_act = {"gelu_tanh": 0, "relu2": 1}[cfg.mlp_act]
     c.zero_init_proj = int(cfg.zero_init_proj)
+    c.head_fp8 = int(getattr(cfg, "head_fp8", False))
     for f in ("ln_eps", "qk_norm_eps", "rope_base", "logit_softcap", "beta1", "beta2", "adam_eps", "weight_decay",
               "max_grad_norm", "init_std"):
         setattr(c, f, float(getattr(cfg, f)))
@@ -125,6 +126,9 @@ _SIGS = [
     ("gptk_embed_bwd", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                  c_void_p, c_void_p]),
     ("gptk_embed_bwd_scratch_bytes", c_int64, [c_int32, c_int32]),
+    ("gptk_gemm_fp8", c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                                c_void_p]),
+    ("gptk_gemm_fp8_scratch_bytes", c_int64, [c_int32, c_int32, c_int32]),
     ("gptk_colsum", c_int32, [c_int32, c_int32, c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
     ("gptk_colsum_partial_floats", c_int64, [c_int32, c_int32]),
 ]

@@ -9,7 +9,11 @@
 //                  values 0 .. pos (or the last `window` of them)
 //   gen_sample     one draw per sequence from the last position's logits:
 //                  softcap, temperature, top-k, inverse CDF in token order
+//   skinny_gemm    the products of a decode step (M = B <= 16 rows): each
+//                  wave streams 16 weight rows and multiplies them with the
+//                  activations held in LDS (v_mfma_f32_16x16x32_bf16)
 #include "common.h"
+#include "gemm_common.h"
 #include "kernels.h"
 
 #include <cfloat>
@@ -188,7 +192,14 @@ __global__ __launch_bounds__(256) void gen_attention_kernel(const T* q, int64_t 
     for (int j = tid; j < n; j += 256) {
         const T* kr = kb + (int64_t)j * d;
         float acc = 0.f;
-        for (int c = 0; c < hd; ++c) acc += qs[c] * to_f32(kr[c]);
+        // 16-byte loads of the key row (hd and d are multiples of 8 elements)
+        constexpr int E = 16 / sizeof(T);
+        for (int c = 0; c < hd; c += E) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(kr + c);
+            const T* kv = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc += qs[c + e] * to_f32(kv[e]);
+        }
         const float v = acc * scale;
         sc[j] = v;
         mx = fmaxf(mx, v);
@@ -204,6 +215,7 @@ __global__ __launch_bounds__(256) void gen_attention_kernel(const T* q, int64_t 
     const int G = 256 / hd, c = tid % hd, g = tid / hd;
     const T* vb = vc + ((int64_t)b * Tmax + j0) * d + h * hd + c;
     float acc = 0.f;
+#pragma unroll 8
     for (int j = g; j < n; j += G) acc += sc[j] * to_f32(vb[(int64_t)j * d]);
     red[tid] = acc;
     __syncthreads();
@@ -236,15 +248,18 @@ void gen_attention(bool bf, const void* q, int64_t ldq, const void* kc, const vo
 
 // ---------------------------------------------------------------- one draw per sequence
 
-// One workgroup of 1024 threads per sequence; thread t owns the contiguous
-// token range [t C, (t + 1) C), C = ceil(Vp / 1024), so thread order is token
-// order. Steps: softcap in place (and the copy out); the maximum; greedy for
-// temperature 0 (first index of the maximum); for 0 < top_k < Vp the k-th
-// largest value by bisection on the order-preserving keys, keeping every
-// larger value and the lowest-index ties; weights exp((z - max) / T) summed
-// per thread in token order and scanned across threads; the draw is the first
-// token whose running sum exceeds u * total, u from Philox4x64-10 at counter
-// (step, sequence) with key (seed, sampling stream).
+// One workgroup of 1024 threads per sequence. Passes that need no order read
+// the row with strided, coalesced accesses; the passes that walk it in token
+// order use contiguous ranges (thread t owns [t C, (t + 1) C), C =
+// ceil(Vp / 1024), so thread order is token order). Steps: softcap in place
+// (and the copy out); the maximum; greedy for temperature 0 (first index of
+// the maximum); for 0 < top_k < Vp the k-th largest value by a radix select
+// over the order-preserving keys (four passes of 256-bin histograms in LDS,
+// most significant byte first), keeping every larger value and the
+// lowest-index ties; weights exp((z - max) / T) summed per thread in token
+// order and scanned across threads; the draw is the first token whose
+// running sum exceeds u * total, u from Philox4x64-10 at counter (step,
+// sequence) with key (seed, sampling stream).
 constexpr int GS_THREADS = 1024;
 
 __global__ __launch_bounds__(GS_THREADS) void gen_sample_kernel(float* logits, int Vp, float cap, float temperature,
@@ -252,12 +267,12 @@ __global__ __launch_bounds__(GS_THREADS) void gen_sample_kernel(float* logits, i
                                                                 int64_t ld_seq, int pos_out, float* logits_out) {
     __shared__ float fsh[GS_THREADS / 64 + 1];
     __shared__ int ish[GS_THREADS / 64 + 1];
+    __shared__ int hist[256];
+    __shared__ uint32_t sel[2];   // selected prefix, count still needed
     const int b = blockIdx.x, tid = threadIdx.x;
     float* z = logits + (int64_t)b * Vp;
-    const int chunk = ceil_div(Vp, GS_THREADS);
-    const int i0 = min(Vp, tid * chunk), i1 = min(Vp, i0 + chunk);
     float mx = -FLT_MAX;
-    for (int i = i0; i < i1; ++i) {
+    for (int i = tid; i < Vp; i += GS_THREADS) {
         float v = z[i];
         if (cap > 0.f) {
             v = cap * tanhf(v / cap);
@@ -266,7 +281,9 @@ __global__ __launch_bounds__(GS_THREADS) void gen_sample_kernel(float* logits, i
         if (logits_out) logits_out[(int64_t)b * Vp + i] = v;
         mx = fmaxf(mx, v);
     }
-    mx = block_max_f<GS_THREADS>(mx, fsh);
+    mx = block_max_f<GS_THREADS>(mx, fsh);   // its barriers order the softcap writes before the reads below
+    const int chunk = ceil_div(Vp, GS_THREADS);
+    const int i0 = min(Vp, tid * chunk), i1 = min(Vp, i0 + chunk);
     int32_t* dst = seq + (int64_t)b * ld_seq + pos_out;
     if (temperature == 0.f) {
         int first = INT_MAX;
@@ -280,12 +297,32 @@ __global__ __launch_bounds__(GS_THREADS) void gen_sample_kernel(float* logits, i
     uint32_t thr = 0;
     int need = 0, tie_before = 0;
     if (trunc) {
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = thr | (1u << bit);
-            int cnt = 0;
-            for (int i = i0; i < i1; ++i) cnt += order_key(z[i]) >= cand;
-            if (block_sum_i<GS_THREADS>(cnt, ish) >= top_k) thr = cand;
+        // radix select of the k-th largest key, most significant byte first
+        if (tid == 0) { sel[0] = 0; sel[1] = (uint32_t)top_k; }
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            const uint32_t hmask = pass ? (0xFFFFFFFFu << (32 - 8 * pass)) : 0u;
+            if (tid < 256) hist[tid] = 0;
+            __syncthreads();
+            const uint32_t prefix = sel[0];
+            for (int i = tid; i < Vp; i += GS_THREADS) {
+                const uint32_t k = order_key(z[i]);
+                if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+            }
+            __syncthreads();
+            if (tid == 0) {
+                uint32_t rem = sel[1];
+                int bin = 255;
+                for (; bin > 0; --bin) {
+                    if ((uint32_t)hist[bin] >= rem) break;
+                    rem -= hist[bin];
+                }
+                sel[0] = prefix | ((uint32_t)bin << shift);
+                sel[1] = rem;
+            }
+            __syncthreads();
         }
+        thr = sel[0];
         int gt = 0, ties = 0;
         for (int i = i0; i < i1; ++i) {
             const uint32_t k = order_key(z[i]);
@@ -336,6 +373,142 @@ void gen_sample(float* logits, int B, int Vp, float cap, float temperature, int 
                 int32_t* seq, int64_t ld_seq, int pos_out, float* logits_out, hipStream_t s) {
     gen_sample_kernel<<<B, GS_THREADS, 0, s>>>(logits, Vp, cap, temperature, top_k, seed, step, seq, ld_seq, pos_out,
                                                 logits_out);
+}
+
+// ---------------------------------------------------------------- products at decode shapes
+
+// C[m, n] = epilogue(sum_k A[m, k] W[n, k]) for m < M <= 16, bf16 A [M, K]
+// (row stride lda) and W [N, K] (row stride ldb), K % 32 == 0. The 16 rows of
+// A (rows past M read as zero) sit in LDS; each workgroup owns 16 consecutive
+// columns and its eight waves split K; a wave loads 16 bytes of each of the 16
+// weight rows per 32-deep step (lane l: row l % 16, k 8 (l / 16) .. + 7; the A
+// fragment the same) into v_mfma_f32_16x16x32_bf16, and the partial 16 x 16
+// tiles (lane l: column l % 16, rows 4 (l / 16) .. + 3) are summed in wave
+// order before the epilogue. Decode steps read every weight once, so the loop
+// is unrolled to keep several loads per lane in flight.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int SK_WAVES = 8;
+
+template <int EPI, typename TC, bool LN>
+__global__ __launch_bounds__(64 * SK_WAVES) void skinny_gemm_kernel(Gemm g) {
+    extern __shared__ __attribute__((aligned(16))) bf16 As[];   // [16][K + 8]
+    __shared__ f32x4_t part[SK_WAVES][64];
+    const int K = g.K, ldl = K + 8;
+    const bf16* W = (const bf16*)g.B;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if constexpr (LN) {
+        // wave w normalises rows w, w + SK_WAVES: the LayerNorm kernel's
+        // arithmetic in its order (lane sums over float4 chunks, wave sums,
+        // biased variance, rsqrt), stored as bf16
+        for (int r = w; r < 16; r += SK_WAVES) {
+            bf16* dst = As + r * ldl;
+            if (r < g.M) {
+                const float* xr = (const float*)g.A + (int64_t)r * g.lda;
+                float sum = 0.f;
+                for (int c = 4 * lane; c < K; c += 256) {
+                    const float4 v = load4(xr + c);
+                    sum += (v.x + v.y) + (v.z + v.w);
+                }
+                const float mu = wave_sum(sum) / K;
+                float s2 = 0.f;
+                for (int c = 4 * lane; c < K; c += 256) {
+                    const float4 v = load4(xr + c);
+                    const float a = v.x - mu, b = v.y - mu, cc = v.z - mu, dd = v.w - mu;
+                    s2 += (a * a + b * b) + (cc * cc + dd * dd);
+                }
+                const float rs = 1.0f / sqrtf(wave_sum(s2) / K + g.ln_eps);
+                for (int c = 4 * lane; c < K; c += 256) {
+                    const float4 v = load4(xr + c), gg = load4(g.ln_g + c), bb = load4(g.ln_b + c);
+                    float4 o;
+                    o.x = (v.x - mu) * rs * gg.x + bb.x;
+                    o.y = (v.y - mu) * rs * gg.y + bb.y;
+                    o.z = (v.z - mu) * rs * gg.z + bb.z;
+                    o.w = (v.w - mu) * rs * gg.w + bb.w;
+                    store4(dst + c, o);
+                }
+            } else {
+                for (int c = 4 * lane; c < K; c += 256) store4(dst + c, make_float4(0.f, 0.f, 0.f, 0.f));
+            }
+        }
+    } else {
+        const bf16* A = (const bf16*)g.A;
+        for (int i = threadIdx.x; i < 16 * (K / 8); i += 64 * SK_WAVES) {
+            const int r = i / (K / 8), c = (i % (K / 8)) * 8;
+            bf16x8_t v = {};
+            if (r < g.M) v = *reinterpret_cast<const bf16x8_t*>(A + (int64_t)r * g.lda + c);
+            *reinterpret_cast<bf16x8_t*>(As + r * ldl + c) = v;
+        }
+    }
+    __syncthreads();
+    const int n0 = blockIdx.x * 16;
+    const int r = lane & 15, kq = lane >> 4;
+    const int nrow = min(n0 + r, g.N - 1);   // columns past N feed only unstored outputs
+    // wave w takes the k range [w K / W, (w + 1) K / W) rounded to 32-deep steps
+    const int nst = K / 32, s0 = w * nst / SK_WAVES, s1 = (w + 1) * nst / SK_WAVES;
+    const bf16* wr = W + (int64_t)nrow * g.ldb + 8 * kq;
+    const bf16* ar = As + r * ldl + 8 * kq;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int st = s0; st < s1; ++st) {
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(wr + 32 * st);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(ar + 32 * st);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+    }
+    part[w][lane] = acc;
+    __syncthreads();
+    if (w == 0) {
+        // the waves' partial tiles, summed in wave order
+        f32x4_t t = part[0][lane];
+#pragma unroll
+        for (int v = 1; v < SK_WAVES; ++v) t += part[v][lane];
+        const int n = n0 + r;
+        if (n < g.N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * kq + i;
+                if (m < g.M) epilogue_store<TC, EPI>(g, m, n, t[i]);
+            }
+        }
+    }
+}
+
+bool skinny_gemm_ok(const Gemm& g) {
+    const bool a_ok = g.ln_g ? (g.K % 4 == 0 && ((uintptr_t)g.A & 15) == 0 && g.lda % 4 == 0 && g.ln_b)
+                             : (g.lda % 8 == 0 && ((uintptr_t)g.A & 15) == 0);
+    return g.in_bf && g.a_kc && g.b_kc && g.M >= 1 && g.M <= 16 && g.K % 32 == 0 && g.K <= 4096 && a_ok &&
+           g.ldb % 8 == 0 && ((uintptr_t)g.B & 15) == 0;
+}
+
+template <int EPI, typename TC>
+static void skinny_launch(const Gemm& g, unsigned grid, size_t lds, hipStream_t s) {
+    static bool attr = false;
+    if (!attr) {
+        const int mx = (int)(sizeof(bf16) * 16 * (4096 + 8));
+        (void)hipFuncSetAttribute((const void*)skinny_gemm_kernel<EPI, TC, false>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+        (void)hipFuncSetAttribute((const void*)skinny_gemm_kernel<EPI, TC, true>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, mx);
+        attr = true;
+    }
+    if (g.ln_g) skinny_gemm_kernel<EPI, TC, true><<<grid, 64 * SK_WAVES, lds, s>>>(g);
+    else skinny_gemm_kernel<EPI, TC, false><<<grid, 64 * SK_WAVES, lds, s>>>(g);
+}
+
+void skinny_gemm(const Gemm& g, hipStream_t s) {
+    const unsigned grid = (unsigned)ceil_div(g.N, 16);
+    const size_t lds = sizeof(bf16) * 16 * (size_t)(g.K + 8);
+    switch (g.epi) {
+        case EPI_STORE:
+            if (g.c_bf) skinny_launch<EPI_STORE, bf16>(g, grid, lds, s);
+            else skinny_launch<EPI_STORE, float>(g, grid, lds, s);
+            break;
+        case EPI_BIAS: skinny_launch<EPI_BIAS, bf16>(g, grid, lds, s); break;
+        case EPI_BIAS_ACT: skinny_launch<EPI_BIAS_ACT, bf16>(g, grid, lds, s); break;
+        case EPI_BIAS_RESID: skinny_launch<EPI_BIAS_RESID, float>(g, grid, lds, s); break;
+        default: break;
+    }
 }
 
 }  // namespace gk

@@ -445,6 +445,16 @@ void run_gemm(gpt_handle* h, int cls, const gk::Gemm& g, bool side = false) {
     }
 }
 
+// the products of a sampling step: the skinny kernel where it applies
+void run_decode_gemm(gpt_handle* h, const gk::Gemm& g) {
+    if (gk::skinny_gemm_ok(g)) {
+        Timed t(h, KC_MISC, 2.0 * g.M * g.N * g.K, 2.0 * ((double)g.M * g.K + (double)g.N * g.K), "skinny_gemm_kernel");
+        gk::skinny_gemm(g, h->stream);
+    } else {
+        run_gemm(h, KC_MISC, g);
+    }
+}
+
 gk::Gemm mk_gemm(gpt_handle* h, int M, int N, int K, const void* A, int64_t lda, bool a_kc, const void* B,
                  int64_t ldb, bool b_kc, void* C, int64_t ldc, bool c_bf, int epi) {
     gk::Gemm g{};
@@ -998,7 +1008,7 @@ gpt_status gpt_generate(gpt_handle* h, const int32_t* prompt, int32_t B, int32_t
         {
             gk::Gemm g = mk_gemm(h, B, Vp, d, (const char*)w.lnf + ab * (size_t)(T0 - 1) * d, (int64_t)T0 * d, true,
                                  Wop(h, tb.wte), d, true, w.dec_logits, Vp, false, gk::EPI_STORE);
-            run_gemm(h, KC_MISC, g);
+            run_decode_gemm(h, g);
         }
         gk::gen_sample(w.dec_logits, B, Vp, c.logit_softcap, temperature, top_k, seed, 0, out, Ttot, T0,
                        logits_out, st);
@@ -1006,15 +1016,31 @@ gpt_status gpt_generate(gpt_handle* h, const int32_t* prompt, int32_t B, int32_t
             const int pos = T0 + step - 1;   // position of the token drawn last
             gk::gen_embed(out, Ttot, pos, P(h, tb.wte), tb.wpe >= 0 ? P(h, tb.wpe) : nullptr, w.dec_x, B, d, Vp,
                           w.err, st);
+            // LayerNorm then product: fused into the skinny product's load of its
+            // activations where that kernel applies, else the two kernels
+            auto ln_gemm = [&](const float* x, int gi, int bi, gk::Gemm g) {
+                gk::Gemm f = g;
+                f.A = x;
+                f.ln_g = P(h, gi);
+                f.ln_b = P(h, bi);
+                f.ln_eps = c.ln_eps;
+                if (gk::skinny_gemm_ok(f)) {
+                    Timed t(h, KC_MISC, 2.0 * g.M * g.N * g.K, 2.0 * (double)g.N * g.K + 4.0 * g.M * g.K,
+                            "skinny_gemm_kernel");
+                    gk::skinny_gemm(f, st);
+                } else {
+                    gk::layernorm_fwd(bf, x, P(h, gi), P(h, bi), (void*)g.A, w.dec_mean, w.dec_rstd, B, d, c.ln_eps,
+                                      st);
+                    run_decode_gemm(h, g);
+                }
+            };
             for (int l = 0; l < L; ++l) {
                 const LayerIdx& li = tb.layers[l];
-                gk::layernorm_fwd(bf, w.dec_x, P(h, li.ln1_w), P(h, li.ln1_b), w.dec_y, w.dec_mean, w.dec_rstd, B, d,
-                                  c.ln_eps, st);
                 {
                     gk::Gemm g = mk_gemm(h, B, 3 * d, d, w.dec_y, d, true, Wop(h, li.attn_w), d, true, w.dec_qkv,
                                          3 * d, bf, gk::EPI_BIAS);
                     g.bias = P(h, li.attn_b);
-                    run_gemm(h, KC_MISC, g);
+                    ln_gemm(w.dec_x, li.ln1_w, li.ln1_b, g);
                 }
                 const void* q = w.dec_qkv;
                 const void* kn = (const char*)w.dec_qkv + ab * d;
@@ -1035,31 +1061,30 @@ gpt_status gpt_generate(gpt_handle* h, const int32_t* prompt, int32_t B, int32_t
                                          gk::EPI_BIAS_RESID);
                     g.bias = P(h, li.proj_b);
                     g.resid = w.dec_x;
-                    run_gemm(h, KC_MISC, g);
+                    run_decode_gemm(h, g);
                 }
-                gk::layernorm_fwd(bf, w.dec_x2, P(h, li.ln2_w), P(h, li.ln2_b), w.dec_y, w.dec_mean, w.dec_rstd, B,
-                                  d, c.ln_eps, st);
                 {
                     gk::Gemm g = mk_gemm(h, B, F, d, w.dec_y, d, true, Wop(h, li.fc_w), d, true, w.dec_h1, F, bf,
                                          gk::EPI_BIAS_ACT);
                     g.bias = P(h, li.fc_b);
                     g.C2 = w.dec_h2;
-                    run_gemm(h, KC_MISC, g);
+                    ln_gemm(w.dec_x2, li.ln2_w, li.ln2_b, g);
                 }
                 {
                     gk::Gemm g = mk_gemm(h, B, d, F, w.dec_h2, F, true, Wop(h, li.mp_w), F, true, w.dec_x, d, false,
                                          gk::EPI_BIAS_RESID);
                     g.bias = P(h, li.mp_b);
                     g.resid = w.dec_x2;
-                    run_gemm(h, KC_MISC, g);
+                    run_decode_gemm(h, g);
                 }
             }
-            gk::layernorm_fwd(bf, w.dec_x, P(h, tb.lnf_w), P(h, tb.lnf_b), w.dec_y, w.dec_mean, w.dec_rstd, B, d,
-                              c.ln_eps, st);
             {
+                // the head's activations are normalised once (its grid has Vp / 16 workgroups)
+                gk::layernorm_fwd(bf, w.dec_x, P(h, tb.lnf_w), P(h, tb.lnf_b), w.dec_y, w.dec_mean, w.dec_rstd, B, d,
+                                  c.ln_eps, st);
                 gk::Gemm g = mk_gemm(h, B, Vp, d, w.dec_y, d, true, Wop(h, tb.wte), d, true, w.dec_logits, Vp, false,
                                      gk::EPI_STORE);
-                run_gemm(h, KC_MISC, g);
+                run_decode_gemm(h, g);
             }
             gk::gen_sample(w.dec_logits, B, Vp, c.logit_softcap, temperature, top_k, seed, step, out, Ttot, pos + 1,
                            logits_out ? logits_out + (size_t)step * B * Vp : nullptr, st);

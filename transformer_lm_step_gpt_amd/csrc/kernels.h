@@ -163,6 +163,12 @@ struct Gemm {
     bool in_bf;                              // A and B storage (bf16 or fp32)
     // e4m3 products only: the bf16 store is multiplied by out_scale[0] * out_scale[1]
     const float* out_scale = nullptr;
+    // decode-shaped products only (skinny_gemm): when ln_g is set, A is the
+    // fp32 residual stream and the product takes LayerNorm(A; ln_g, ln_b, ln_eps)
+    // rounded to bf16, as the separate LayerNorm kernel would store it
+    const float* ln_g = nullptr;
+    const float* ln_b = nullptr;
+    float ln_eps = 0.f;
     // ACT_GRAD epilogue, plans with bm > 0: cpart[(m / bm) * N + n] = sum over
     // the rows m of one bm-row block of the fp32 output values (column sums
     // for a bias gradient, reduced later)
@@ -183,6 +189,11 @@ GemmPlan gemm_plan(const Gemm& g, size_t splitk_floats);
 void gemm_main(const Gemm& g, const GemmPlan& p, float* splitk_scratch, hipStream_t s);
 void gemm_finish(const Gemm& g, const GemmPlan& p, const float* splitk_scratch, hipStream_t s);
 void gemm(const Gemm& g, float* splitk_scratch, size_t splitk_floats, hipStream_t s);
+// Products of a decode step: bf16 (or, with ln_g, a LayerNorm of fp32 rows) A
+// and bf16 W, both k-contiguous, M <= 16, K % 32 == 0, K <= 4096, epilogues
+// STORE / BIAS / BIAS_ACT / BIAS_RESID.
+bool skinny_gemm_ok(const Gemm& g);
+void skinny_gemm(const Gemm& g, hipStream_t s);
 // e4m3 product for the FP8 head: C [M, N] bf16 (row stride ldc) =
 // (A8 [M, K] . B8 [N, K]^T) * inv_sa * inv_sb, A8 and B8 e4m3 bytes with row
 // strides lda and ldb (bytes), K % 128 == 0, lda % 16 == ldb % 16 == 0.

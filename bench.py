@@ -212,7 +212,27 @@ def _pmc_means(d, counter):
     return {k: v[0] / v[1] for k, v in acc.items()}
 
 
-def pmc_table(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernel_json):
+def trace_step_durations(d, step):
+    """Per kernel name: (summed duration in ns, dispatches) of the kernels of
+    AdamW-delimited step `step` (0-based) in a rocprofv3 --kernel-trace run."""
+    import csv
+    import glob
+    f = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))[0]
+    ks = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in csv.DictReader(open(f))),
+                key=lambda k: k[0])
+    ends = [k[1] for k in ks if "adamw_kernel" in k[2]]
+    t0 = ends[step - 1] if step > 0 else 0
+    t1 = ends[step]
+    out = {}
+    for a, b, n in ks:
+        if a >= t0 and b <= t1:
+            v = out.setdefault(n, [0, 0])
+            v[0] += b - a
+            v[1] += 1
+    return out
+
+
+def pmc_table(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernel_json, trace_dir=None, trace_step=1):
     """Markdown table: per bandwidth-bound kernel class, algorithmic bytes per
     launch (the library's count), HBM bytes per launch from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch, each scaled by what it reads for a plain copy
@@ -229,6 +249,9 @@ def pmc_table(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernel_json):
     cls = {r["name"]: r for r in kj["classes"]}
     per_step = kj["launch_steps"]
     print(f"FETCH_SIZE factor {fetch_factor:.4f}, WRITE_SIZE factor {write_factor:.4f} (copy of {copy_bytes:.0f} bytes)")
+    dur = trace_step_durations(trace_dir, trace_step) if trace_dir else None
+    src = ("rocprofv3 kernel durations of the serialized step" if dur else "HIP events around each launch")
+    print(f"alone durations from {src}")
     print("| class | launches/step | kernels | algorithmic MB/launch | counter MB/launch | counter/alg | "
           "alone us/launch | alg GB/s alone | of 8 TB/s |")
     print("|---|---|---|---|---|---|---|---|---|")
@@ -241,6 +264,10 @@ def pmc_table(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernel_json):
         hbm = sum(fm[n] * 1024 * fetch_factor + wm.get(n, 0.0) * 1024 * write_factor for n in names)
         alg = r["bytes"] / r["launches"]
         us = 1e3 * r["ms"] / r["launches"]
+        if dur:
+            tn = [n for n in dur if any(sub in n and cc == c for sub, cc in PMC_CLASSES)]
+            if tn:
+                us = 1e-3 * sum(dur[n][0] for n in tn) / r["launches"]
         gbs = alg / (us * 1e-6) / 1e9
         short = ", ".join(sorted({n.split("(")[0].replace("void ", "").replace("gk::", "")[:40] for n in names}))
         print(f"| {c} | {r['launches'] / per_step:.0f} | {short} | {alg / 1e6:.1f} | {hbm / 1e6:.1f} | "
@@ -326,9 +353,14 @@ def main():
     ap.add_argument("--pmc-table", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR",
                                                      "KERNEL_JSON"),
                     help="HBM traffic table of the bandwidth-bound kernels from rocprofv3 --pmc runs")
+    ap.add_argument("--pmc-trace", metavar="DIR", help="with --pmc-table: take the alone durations from this "
+                                                       "rocprofv3 --kernel-trace run's serialized step")
+    ap.add_argument("--pmc-trace-step", type=int, default=None,
+                    help="with --pmc-trace: AdamW-delimited index of the serialized step (default: --warmup)")
     a = ap.parse_args()
     if a.pmc_table:
-        pmc_table(*a.pmc_table)
+        pmc_table(*a.pmc_table, trace_dir=a.pmc_trace,
+                  trace_step=a.pmc_trace_step if a.pmc_trace_step is not None else a.warmup)
         return
     if a.rocprof_summary:
         rocprof_summary(a.rocprof_summary)

@@ -38,6 +38,12 @@ Sources (page title, section):
     generate: last position's logits divided by the temperature, softmax, one
     draw, append, repeat; 0 temperature = greedy) and the lecture's
     "Генерация и устройство" (top-k sampling with k = 50).
+  * Muon (the hidden matrices' optimiser): the Modded-NanoGPT README's
+    technique list names it and links its article; the pages give no formula,
+    so the steps follow that article (K. Jordan et al., "Muon: An optimizer for
+    hidden layers in neural networks", 2024): Nesterov momentum, then the
+    quintic Newton-Schulz orthogonalisation, then a step scaled by
+    sqrt(max(1, rows / cols)); every other tensor keeps AdamW.
 
 Random initialisation uses Philox4x64-10 (Salmon, Moraes, Dror and Shaw,
 "Parallel random numbers: as easy as 1, 2, 3", SC'11) and the Box-Muller
@@ -532,9 +538,10 @@ def decay_flags(cfg) -> Dict[str, bool]:
     return {name: dec for name, _s, dec, _k in param_table(cfg)}
 
 
-def train_step(params, m, v, micro_batches, cfg, lr, step, progress=None):
+def train_step(params, m, v, micro_batches, cfg, lr, step, progress=None, muon=None):
     """Full optimiser step: accumulate grads over the micro-batches with
-    scale 1/k, clip at cfg.max_grad_norm, AdamW. Returns
+    scale 1/k, clip at cfg.max_grad_norm, AdamW (or, with muon = (muon_lr,
+    momentum), muon_update). Returns
     (mean loss, grad norm, grads (unclipped), new params, new m, new v)."""
     k = len(micro_batches)
     acc = zeros_like_params(params)
@@ -546,8 +553,74 @@ def train_step(params, m, v, micro_batches, cfg, lr, step, progress=None):
             acc[n] += g[n]
     norm = grad_norm(acc)
     coef = clip_coefficient(norm, cfg.max_grad_norm)
-    P, Mn, Vn = adamw_update(params, acc, m, v, lr, step, cfg, decay_flags(cfg), grad_coef=coef)
+    if muon is None:
+        P, Mn, Vn = adamw_update(params, acc, m, v, lr, step, cfg, decay_flags(cfg), grad_coef=coef)
+    else:
+        P, Mn, Vn = muon_update(params, acc, m, v, lr, step, cfg, muon[0], muon[1], grad_coef=coef)
     return loss_sum / k, norm, acc, P, Mn, Vn
+
+
+# ----------------------------------------------------------------------------
+# Muon for the hidden matrices
+# ----------------------------------------------------------------------------
+
+# Quintic Newton-Schulz coefficients of the Muon article (x -> a x + b x^3 + c x^5
+# on the singular values), its five iterations and the normalisation epsilon.
+MUON_NS_COEFFS = (3.4445, -4.7750, 2.0315)
+MUON_NS_STEPS = 5
+MUON_EPS = 1e-7
+
+
+def newton_schulz5(G):
+    """Approximate orthogonalisation (the U V^T of G = U S V^T) by the Muon
+    article's iteration: G is taken wide (transposed when it has more rows than
+    columns), divided by its Frobenius norm plus MUON_EPS, and then, five times,
+    A = X X^T and X <- a X + (b A + c A A) X. The result is oriented back."""
+    a, b, c = MUON_NS_COEFFS
+    X = np.array(G, dtype=np.float64)
+    tall = X.shape[0] > X.shape[1]
+    if tall:
+        X = X.T
+    X = X / (np.linalg.norm(X) + MUON_EPS)
+    for _ in range(MUON_NS_STEPS):
+        A = X @ X.T
+        B = b * A + c * (A @ A)
+        X = a * X + B @ X
+    return X.T if tall else X
+
+
+def muon_tensors(cfg) -> List[str]:
+    """The hidden matrices Muon updates: each block's qkv, attention-output,
+    MLP-up and MLP-down weights. Embeddings (and the tied head), LayerNorm
+    gains and biases keep AdamW."""
+    out = []
+    for l in range(cfg.n_layer):
+        p = f"h.{l}."
+        out += [p + "attn.c_attn.weight", p + "attn.c_proj.weight", p + "mlp.c_fc.weight", p + "mlp.c_proj.weight"]
+    return out
+
+
+def muon_update(params, grads, m, v, lr, step, cfg, muon_lr, muon_momentum, grad_coef=1.0):
+    """One optimiser step with Muon on muon_tensors(cfg) and AdamW (adamw_update,
+    learning rate lr) on the rest. For a hidden matrix W [r, c] with clipped
+    gradient g and momentum buffer B (held where AdamW keeps its first moment):
+        B <- mu B + g;   u = g + mu B   (Nesterov)
+        W <- W - muon_lr sqrt(max(1, r / c)) NS5(u)
+    with no weight decay; its second-moment buffer is left unchanged.
+    Returns new (params, m, v); inputs are not modified."""
+    hidden = set(muon_tensors(cfg))
+    flags = decay_flags(cfg)
+    rest = [n for n in params if n not in hidden]
+    P, Mn, Vn = adamw_update({n: params[n] for n in rest}, grads, m, v, lr, step, cfg, flags, grad_coef=grad_coef)
+    for n in hidden:
+        g = grads[n] * grad_coef
+        buf = muon_momentum * m[n] + g
+        u = g + muon_momentum * buf
+        r, c = params[n].shape
+        P[n] = params[n] - muon_lr * math.sqrt(max(1.0, r / c)) * newton_schulz5(u)
+        Mn[n] = buf
+        Vn[n] = v[n].copy()
+    return {n: P[n] for n in params}, {n: Mn[n] for n in params}, {n: Vn[n] for n in params}
 
 
 # ----------------------------------------------------------------------------

@@ -730,3 +730,114 @@ def test_fp8_head_logits_quantisation():
     # and the quantised head stays close to the exact product (3 mantissa bits)
     assert np.abs(O.fp8_head_logits(x, w) - x @ w.T).max() <= 0.1 * np.abs(x @ w.T).max()
 
+
+
+# ---------------------------------------------------------------- Muon
+
+# The Muon article's iteration acts on each singular value separately: with
+# G = U S V^T and x = S / (|G|_F + 1e-7), five applications of the quintic
+# p(x) = 3.4445 x - 4.7750 x^3 + 2.0315 x^5 give NS5(G) = U p^5(x) V^T. The
+# coefficients are written out here, not read from the oracle.
+def _ns5_via_svd(G):
+    U, S, Vt = np.linalg.svd(np.asarray(G, np.float64), full_matrices=False)
+    x = S / (math.sqrt(float(np.sum(S * S))) + 1e-7)
+    for _ in range(5):
+        x = 3.4445 * x - 4.7750 * x ** 3 + 2.0315 * x ** 5
+    return (U * x) @ Vt
+
+
+def _muon_ns_pin_violations(ns5):
+    rng = np.random.default_rng(21)
+    bad = []
+    for shape in [(24, 40), (40, 24), (32, 32), (1, 9), (9, 1)]:
+        G = rng.normal(size=shape)
+        got, want = ns5(G), _ns5_via_svd(G)
+        if got.shape != G.shape or not np.allclose(got, want, rtol=0, atol=1e-10 * np.abs(want).max()):
+            bad.append(f"singular-value map at {shape}")
+    # 3 Q for an orthogonal 16 x 16 Q: |3 Q|_F = 12, every normalised singular
+    # value is 3 / (12 + 1e-7), and the five-fold quintic takes it to
+    # 0.7145262703642121 (evaluated by hand; 0.25 itself goes to 0.714526261333035)
+    Q, _ = np.linalg.qr(rng.normal(size=(16, 16)))
+    if not np.allclose(ns5(3.0 * Q), 0.7145262703642121 * Q, rtol=0, atol=1e-12):
+        bad.append("scaled orthogonal input")
+    return bad
+
+
+def test_newton_schulz_matches_singular_value_map():
+    assert _muon_ns_pin_violations(O.newton_schulz5) == []
+
+
+def test_newton_schulz_invariances():
+    """Sign and transpose commute with the iteration; a positive scale changes
+    nothing but the epsilon's share; the output's singular values sit in the
+    band the quintic maps (0, 1] into after five steps for a full-rank input."""
+    rng = np.random.default_rng(22)
+    G = rng.normal(size=(12, 30))
+    X = O.newton_schulz5(G)
+    assert np.allclose(O.newton_schulz5(-G), -X, rtol=0, atol=1e-12)
+    assert np.allclose(O.newton_schulz5(G.T), X.T, rtol=0, atol=1e-12)
+    assert np.allclose(O.newton_schulz5(7.5 * G), X, rtol=0, atol=1e-6)
+    s = np.linalg.svd(X, compute_uv=False)
+    assert s.min() > 0.6 and s.max() < 1.25, (s.min(), s.max())
+
+
+def test_newton_schulz_pin_rejects_plausible_mistakes():
+    """The pin fails for swapped cubic/quintic coefficients, four iterations,
+    and a missing normalisation (mistakes planted in local copies)."""
+    def ns(G, coeffs=(3.4445, -4.7750, 2.0315), steps=5, normalise=True):
+        a, b, c = coeffs
+        X = np.array(G, np.float64)
+        if normalise:
+            X = X / (np.linalg.norm(X) + 1e-7)
+        for _ in range(steps):
+            A = X @ X.T
+            X = a * X + (b * A + c * A @ A) @ X
+        return X
+
+    assert _muon_ns_pin_violations(ns) == []            # the local copy itself is right
+    assert _muon_ns_pin_violations(lambda G: ns(G, coeffs=(3.4445, 2.0315, -4.7750)))
+    assert _muon_ns_pin_violations(lambda G: ns(G, steps=4))
+    with np.errstate(over="ignore", invalid="ignore"):   # unnormalised iterates overflow
+        assert _muon_ns_pin_violations(lambda G: ns(G, normalise=False))
+
+
+def test_muon_update_momentum_nesterov_scale_and_selection():
+    """Two steps with gradients g and -g/2 from a zero buffer (mu = 0.95):
+    buffer g then 0.45 g; Nesterov directions 1.95 g then -0.0725 g (plain
+    momentum would give +0.45 g: the opposite sign); step factors sqrt(3)
+    (qkv, 3d x d), 2 (MLP up, 4d x d) and 1 (the square and wide matrices).
+    Every other tensor follows AdamW, and Muon's second moments stay zero."""
+    cfg = TINY
+    rng = np.random.default_rng(23)
+    params = O.init_params(cfg, 4)
+    zeros = O.zeros_like_params(params)
+    g1 = {n: rng.normal(size=p.shape) for n, p in params.items()}
+    g2 = {n: -0.5 * g for n, g in g1.items()}
+    lr, mlr, mu = 1e-3, 0.02, 0.95
+    P1, M1, V1 = O.muon_update(params, g1, zeros, zeros, lr, 1, cfg, mlr, mu)
+    P2, M2, V2 = O.muon_update(P1, g2, M1, V1, lr, 2, cfg, mlr, mu)
+    factor = {"attn.c_attn.weight": math.sqrt(3.0), "attn.c_proj.weight": 1.0, "mlp.c_fc.weight": 2.0,
+              "mlp.c_proj.weight": 1.0}
+    hidden = set()
+    for l in range(cfg.n_layer):
+        for suffix, f in factor.items():
+            n = f"h.{l}.{suffix}"
+            hidden.add(n)
+            g = g1[n]
+            assert np.allclose(M1[n], g, rtol=0, atol=1e-15)
+            assert np.allclose(M2[n], 0.45 * g, rtol=0, atol=1e-14)
+            assert np.allclose(P1[n], params[n] - mlr * f * _ns5_via_svd(1.95 * g), rtol=0, atol=1e-12)
+            assert np.allclose(P2[n], P1[n] - mlr * f * _ns5_via_svd(-0.0725 * g), rtol=0, atol=1e-12)
+            assert not np.any(V1[n]) and not np.any(V2[n])
+    assert hidden == set(O.muon_tensors(cfg))
+    flags = O.decay_flags(cfg)
+    rest = [n for n in params if n not in hidden]
+    A1, _, _ = O.adamw_update({n: params[n] for n in rest}, g1, zeros, zeros, lr, 1, cfg, flags)
+    for n in rest:
+        assert np.array_equal(P1[n], A1[n]), n
+    # the training step routes to it
+    tok, tgt = next(I.batches(I.TINY_FP32, 2, 16))
+    _, norm, acc, Pa, Ma, _ = O.train_step(params, zeros, zeros, [(tok, tgt)], cfg, lr, 1, muon=(mlr, mu))
+    Pb, Mb, _ = O.muon_update(params, acc, zeros, zeros, lr, 1, cfg, mlr, mu,
+                              grad_coef=O.clip_coefficient(norm, cfg.max_grad_norm))
+    assert all(np.array_equal(Pa[n], Pb[n]) and np.array_equal(Ma[n], Mb[n]) for n in params)

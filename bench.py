@@ -45,7 +45,11 @@ def model_flops_per_token(cfg, T):
     return 6 * N + attn
 
 
-def cpu_baseline(w, seq):
+# Muon's learning rate and momentum for the --muon line (the article's defaults)
+MUON_LR, MUON_MOMENTUM = 0.02, 0.95
+
+
+def cpu_baseline(w, seq, muon=False):
     """Time the float64 CPU oracle on one sequence of the same workload."""
     from oracle import gpt_oracle as O
     from transformer_lm_step_gpt_amd import inputs as I
@@ -62,10 +66,11 @@ def cpu_baseline(w, seq):
     m = O.zeros_like_params(params)
     x, y = next(I.batches(w, 1, seq))
     t0 = time.perf_counter()
-    O.train_step(params, m, m, [(x, y)], cfg, w.lr, 1)
+    O.train_step(params, m, m, [(x, y)], cfg, w.lr, 1, muon=(MUON_LR, MUON_MOMENTUM) if muon else None)
     dt = time.perf_counter() - t0
+    opt = "Muon on the hidden matrices and AdamW on the rest" if muon else "AdamW"
     return {"value": round(seq / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one {seq}-token sequence of {w.name}: float64 forward, backward, clip and AdamW over all "
+            "sample": f"one {seq}-token sequence of {w.name}: float64 forward, backward, clip and {opt} over all "
                       f"{sum(int(np.prod(s)) for _, s, _, _ in O.param_table(cfg))} parameters, {dt:.1f} s"}
 
 
@@ -346,6 +351,8 @@ def main():
                                                          "dir (the last --steps steps)")
     ap.add_argument("--head-fp8", action="store_true", help="the same step with the FP8 head (e4m3 lm_head "
                                                               "forward product; a separate line, not the headline)")
+    ap.add_argument("--muon", action="store_true", help="the same step with Muon on the blocks' hidden matrices "
+                    "and AdamW on the rest (gpt_clip_and_muon) instead of AdamW everywhere")
     ap.add_argument("--generate", action="store_true", help="time sampling with the key/value cache instead "
                                                                "(a second workload; prints its own line)")
     ap.add_argument("--kernel-json", metavar="PATH", help="write the per-class and per-kernel timings of the "
@@ -403,7 +410,10 @@ def main():
             x, y = toks[(i * w.accum + j) % len(toks)]
             model.forward_backward(x, y, 1.0 / w.accum, sync=False)
         step_no[0] += 1
-        model.clip_and_adamw(w.lr, step_no[0], sync=False)
+        if a.muon:
+            model.clip_and_muon(w.lr, MUON_LR, MUON_MOMENTUM, step_no[0], sync=False)
+        else:
+            model.clip_and_adamw(w.lr, step_no[0], sync=False)
 
     for i in range(a.warmup):
         step(i)
@@ -486,7 +496,9 @@ def main():
                     print(f"{r['name'][:width]:>{width}s} {r['ms']:9.3f} ms {100 * r['ms'] / tot:5.1f}% "
                           f"x{r['launches']:4d} {rate}", file=sys.stderr)
     out = {
-        "metric": METRIC + ("; FP8 head (e4m3 lm_head forward)" if a.head_fp8 else ""), "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "metric": METRIC + ("; FP8 head (e4m3 lm_head forward)" if a.head_fp8 else "") +
+                  ("; Muon on the hidden matrices" if a.muon else ""),
+        "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(1e3 * dt / a.steps, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": ("bf16+fp8 head" if a.head_fp8 else "bf16") if cfg.precision == "bf16" else "fp32",
@@ -500,8 +512,11 @@ def main():
                            "value": round(tokens / dt_plain, 1),
                            "mfma_util_pct": round(100 * tokens / dt_plain * fpt / (PEAK_BF16_TFLOPS * 1e12), 2)},
     }
+    if a.muon:
+        out["optimizer"] = {"hidden_matrices": f"muon (lr {MUON_LR}, momentum {MUON_MOMENTUM}, Nesterov, 5 "
+                                               "Newton-Schulz steps in bf16)", "rest": f"adamw (lr {w.lr})"}
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, T)
+        out["cpu_baseline"] = cpu_baseline(w, T, muon=a.muon)
     print(json.dumps(out), flush=True)
 
 

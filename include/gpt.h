@@ -206,6 +206,25 @@ gpt_status gpt_generate(gpt_handle* h, const int32_t* d_prompt, int32_t B, int32
  * waits), DEVICE. */
 gpt_status gpt_clip_and_adamw(gpt_handle* h, float lr, int32_t step, float* h_grad_norm);
 
+/* Optimiser step with Muon on the blocks' hidden matrices (Modded-NanoGPT
+ * README, technique list: "Muon optimizer"; the README gives no formula, the
+ * steps are those of the article it links, K. Jordan et al., "Muon: An
+ * optimizer for hidden layers in neural networks", 2024). Same clip and skip
+ * rules, errors and waiting as gpt_clip_and_adamw; AdamW (learning rate lr,
+ * the config's betas, eps and decay) updates the embeddings, LayerNorm gains
+ * and every bias. Each h.{l}.attn.c_attn / attn.c_proj / mlp.c_fc /
+ * mlp.c_proj weight W [r, c] with clipped gradient g and momentum buffer B
+ * (kept where AdamW keeps its first moment; its second moment is untouched):
+ *   B <- mu B + g;  u = g + mu B                       (Nesterov)
+ *   X = u / (|u|_F + 1e-7), taken [c, r] when r > c;
+ *   five times: A = X X^T, X <- 3.4445 X + (-4.7750 A + 2.0315 A A) X;
+ *   W <- W - muon_lr sqrt(max(1, r / c)) X (oriented back), no weight decay.
+ * The products and X are bf16 with fp32 accumulation on bf16 models, fp32
+ * otherwise. INVALID_ARGUMENT also for muon_lr < 0 or not finite and for
+ * muon_momentum outside [0, 1). */
+gpt_status gpt_clip_and_muon(gpt_handle* h, float lr, float muon_lr, float muon_momentum, int32_t step,
+                             float* h_grad_norm);
+
 /* Parameter table: tensor names follow the lecture's Hugging-Face names
  * ("wte", "wpe", "h.{l}.ln_1.weight", "h.{l}.attn.c_attn.weight", ...,
  * "ln_f.bias"); linear weights are [out, in]; the tied wte appears once.

@@ -75,6 +75,16 @@ gpt_status gptk_gemm_fp8(int32_t M, int32_t N, int32_t K, const void* A, const v
                          int64_t scratch_bytes, void* stream);
 int64_t gptk_gemm_fp8_scratch_bytes(int32_t M, int32_t N, int32_t K);
 
+/* Muon's orthogonalisation of one matrix (the iteration of gpt_clip_and_muon
+ * on a single gradient, momentum 0): O [r, c] (fp32, row-major) = the five
+ * quintic Newton-Schulz steps applied to G [r, c] (fp32, row-major) normalised
+ * by |G|_F + 1e-7, iterates and products bf16 with fp32 accumulation when
+ * bf16, fp32 otherwise. scratch (256-byte aligned) holds
+ * gptk_muon_scratch_bytes(r, c, bf16) bytes. */
+gpt_status gptk_muon_orthogonalize(int32_t r, int32_t c, const float* G, float* O, int32_t bf16, void* scratch,
+                                   int64_t scratch_bytes, void* stream);
+int64_t gptk_muon_scratch_bytes(int32_t r, int32_t c, int32_t bf16);
+
 /* Causal (optionally windowed: i - j < window) softmax(Q K^T / sqrt(hd)) V per
  * (batch, head), heads interleaved in the columns of row-major [B*T, *]
  * buffers ("El Mecanismo de Atención"). Forward writes o and lse [B, H, T];

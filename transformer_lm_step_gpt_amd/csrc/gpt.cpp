@@ -145,6 +145,11 @@ struct Ws {
     // scales [s_x, 1/s_x, s_w, 1/s_w] and the max-reduction partials
     uint8_t *xq = nullptr, *wq = nullptr;
     float *f8_scale = nullptr, *f8_part = nullptr;
+    // Muon: the direction u (fp32, wide), the iterates X (two), A, A A and
+    // a I + b A + c A A (act), per-tile sums of squares and the normalisation
+    float* mu_u = nullptr;
+    void *mu_x0 = nullptr, *mu_x1 = nullptr, *mu_a = nullptr, *mu_aa = nullptr, *mu_b = nullptr;
+    float *mu_part = nullptr, *mu_scale = nullptr;
     float *dec_x = nullptr, *dec_x2 = nullptr, *dec_mean = nullptr, *dec_rstd = nullptr, *dec_logits = nullptr;
     void *dec_y = nullptr, *dec_qkv = nullptr, *dec_qk = nullptr, *dec_att = nullptr, *dec_h1 = nullptr,
          *dec_h2 = nullptr;
@@ -244,6 +249,20 @@ Ws plan(const gpt_config& c, const Table& tb, void* base) {
         w.f8_scale = cv.arr<float>(4);
         w.f8_part = cv.arr<float>(2048);
     }
+    {
+        // hidden matrices: [3d, d], [d, d], [F, d], [d, F]; the wide side m <= d
+        const int64_t mn = std::max<int64_t>(3 * d * d, F * d), mm = d * d;
+        const int64_t np = std::max({gk::muon_part_floats((int)(3 * d), (int)d), gk::muon_part_floats((int)F, (int)d),
+                                     gk::muon_part_floats((int)d, (int)d)});
+        w.mu_u = cv.arr<float>(mn);
+        w.mu_x0 = cv.take(ab * mn);
+        w.mu_x1 = cv.take(ab * mn);
+        w.mu_a = cv.take(ab * mm);
+        w.mu_aa = cv.take(ab * mm);
+        w.mu_b = cv.take(ab * mm);
+        w.mu_part = cv.arr<float>(np);
+        w.mu_scale = cv.arr<float>(1);
+    }
     for (int l = 0; l < L; ++l) {
         w.kcache.push_back(cv.take(ab * M * d));
         w.vcache.push_back(cv.take(ab * M * d));
@@ -307,12 +326,12 @@ gpt_status validate(const gpt_config* c, std::string* why) {
 enum KClass {
     KC_EMBED_FWD, KC_LN_FWD, KC_GEMM_FWD, KC_GEMM_LMHEAD, KC_ATTN_FWD, KC_CE, KC_GEMM_DGRAD, KC_GEMM_WGRAD,
     KC_GEMM_LMHEAD_BWD, KC_LN_BWD, KC_COLSUM, KC_ATTN_BWD, KC_QK_PREP, KC_EMBED_BWD, KC_GRAD_NORM, KC_ADAMW,
-    KC_MISC, KC_PARTIAL_REDUCE, KC_FP8_QUANT, KC_COUNT
+    KC_MISC, KC_PARTIAL_REDUCE, KC_FP8_QUANT, KC_MUON, KC_COUNT
 };
 const char* kc_names[KC_COUNT] = {
     "embed_fwd", "layernorm_fwd", "gemm_fwd", "gemm_lm_head", "attention_fwd", "cross_entropy", "gemm_dgrad",
     "gemm_wgrad", "gemm_lm_head_bwd", "layernorm_bwd", "colsum", "attention_bwd", "qk_prep", "embed_bwd",
-    "grad_norm", "adamw", "misc", "partial_reduce", "fp8_quantize"};
+    "grad_norm", "adamw", "misc", "partial_reduce", "fp8_quantize", "muon"};
 
 struct Pending { int cls; int name; hipEvent_t a, b; double flops, bytes; };
 struct ClassStat { double ms = 0, flops = 0, bytes = 0; int64_t launches = 0; };
@@ -1095,27 +1114,64 @@ gpt_status gpt_generate(gpt_handle* h, const int32_t* prompt, int32_t B, int32_t
     return sync_and_check(h);
 }
 
-gpt_status gpt_clip_and_adamw(gpt_handle* h, float lr, int32_t step, float* h_grad_norm) {
+// Global-norm clip, then AdamW on every tensor, or (muon non-null: learning
+// rate, momentum) Muon on the blocks' hidden matrices and AdamW on the rest.
+static gpt_status optimizer_step(gpt_handle* h, float lr, int32_t step, float* h_grad_norm, const float* muon) {
     if (!h) return GPT_ERR_INVALID_ARGUMENT;
     if (step < 1) return fail(h, GPT_ERR_INVALID_ARGUMENT, "step must be >= 1");
     if (!(lr >= 0.f) || !std::isfinite(lr)) return fail(h, GPT_ERR_INVALID_ARGUMENT, "lr must be finite and >= 0");
+    if (muon && (!(muon[0] >= 0.f) || !std::isfinite(muon[0])))
+        return fail(h, GPT_ERR_INVALID_ARGUMENT, "muon_lr must be finite and >= 0");
+    if (muon && (!(muon[1] >= 0.f) || !(muon[1] < 1.f)))
+        return fail(h, GPT_ERR_INVALID_ARGUMENT, "muon_momentum must be in [0, 1)");
     const gpt_config& c = h->cfg;
     Ws& w = h->ws;
-    const int64_t n = h->tb.n_total;
+    const Table& tb = h->tb;
+    hipStream_t st = h->stream;
+    const int64_t n = tb.n_total;
+    const bool bf = c.precision == GPT_PREC_BF16;
     if (h->grads_dirty) {   // no micro-step since the last update: gradients are zero
-        gk::fill_f32(w.grads, n, 0.f, h->stream);
+        gk::fill_f32(w.grads, n, 0.f, st);
     }
     {
         Timed t(h, KC_GRAD_NORM, 0, 4.0 * n);
-        gk::grad_norm(w.grads, n, w.gn_partial, w.gnorm, w.coef, w.nonfinite, w.err, c.max_grad_norm, h->stream);
+        gk::grad_norm(w.grads, n, w.gn_partial, w.gnorm, w.coef, w.nonfinite, w.err, c.max_grad_norm, st);
     }
     double b1 = c.beta1, b2 = c.beta2;
     float rbc1 = (float)(1.0 / (1.0 - std::pow(b1, step)));
     float rbc2 = (float)(1.0 / (1.0 - std::pow(b2, step)));
-    {
-        Timed t(h, KC_ADAMW, 0, 28.0 * n + 2.0 * h->tb.n_decay);
-        gk::adamw(w.params, w.grads, w.m, w.v, w.wbf, n, h->tb.n_decay, w.coef, w.nonfinite, lr, c.beta1, c.beta2,
-                  c.adam_eps, c.weight_decay, rbc1, rbc2, h->stream);
+    if (!muon) {
+        Timed t(h, KC_ADAMW, 0, 28.0 * n + 2.0 * tb.n_decay);
+        gk::adamw(w.params, w.grads, w.m, w.v, w.wbf, n, tb.n_decay, w.coef, w.nonfinite, lr, c.beta1, c.beta2,
+                  c.adam_eps, c.weight_decay, rbc1, rbc2, st);
+    } else {
+        // the hidden matrices follow the embeddings in the flat layout and end
+        // the decayed range: AdamW covers [0, lo) and the undecayed tensors
+        const int64_t lo = tb.t[tb.layers[0].attn_w].offset, nu = n - tb.n_decay;
+        {
+            Timed t(h, KC_ADAMW, 0, 28.0 * (lo + nu) + 2.0 * lo);
+            gk::adamw(w.params, w.grads, w.m, w.v, w.wbf, lo, lo, w.coef, w.nonfinite, lr, c.beta1, c.beta2,
+                      c.adam_eps, c.weight_decay, rbc1, rbc2, st);
+            gk::adamw(w.params + tb.n_decay, w.grads + tb.n_decay, w.m + tb.n_decay, w.v + tb.n_decay, nullptr, nu, 0,
+                      w.coef, w.nonfinite, lr, c.beta1, c.beta2, c.adam_eps, c.weight_decay, rbc1, rbc2, st);
+        }
+        const double ab = bf ? 2 : 4;
+        for (const LayerIdx& li : tb.layers)
+            for (int idx : {li.attn_w, li.proj_w, li.fc_w, li.mp_w}) {
+                const TensorInfo& ti = tb.t[idx];
+                const int r = (int)ti.shape[0], cc = (int)ti.shape[1], mr = std::min(r, cc), nr = std::max(r, cc);
+                const double mn = (double)mr * nr, m2 = (double)mr * mr;
+                // five iterations of three products: 2 m n m + 2 m m m + 2 m m n flops
+                Timed t(h, KC_MUON, 5.0 * (4.0 * mn * mr + 2.0 * m2 * mr),
+                        20.0 * mn + 5.0 * ab * (3.0 * mn + 5.0 * m2) + 12.0 * mn);
+                gk::muon_direction(w.grads + ti.offset, w.m + ti.offset, w.mu_u, w.mu_part, r, cc, muon[1], w.coef,
+                                   w.nonfinite, w.mu_scale, st);
+                void* X = gk::muon_newton_schulz(bf, w.mu_u, w.mu_scale, mr, nr, w.mu_x0, w.mu_x1, w.mu_a, w.mu_aa,
+                                                 w.mu_b, w.splitk, w.splitk_floats, st);
+                const float stepsz = (float)(muon[0] * std::sqrt(std::max(1.0, (double)r / cc)));
+                gk::muon_apply(bf, w.params + ti.offset, bf ? (char*)w.wbf + 2 * ti.offset : nullptr, X, r, cc,
+                               stepsz, w.nonfinite, st);
+            }
     }
     h->grads_dirty = true;
     gpt_status s = hip_check(h, hipGetLastError(), "kernel launch");
@@ -1137,6 +1193,16 @@ gpt_status gpt_clip_and_adamw(gpt_handle* h, float lr, int32_t step, float* h_gr
         if (nf) return fail(h, GPT_ERR_NONFINITE, "gradient norm is not finite: update skipped");
     }
     return GPT_OK;
+}
+
+gpt_status gpt_clip_and_adamw(gpt_handle* h, float lr, int32_t step, float* h_grad_norm) {
+    return optimizer_step(h, lr, step, h_grad_norm, nullptr);
+}
+
+gpt_status gpt_clip_and_muon(gpt_handle* h, float lr, float muon_lr, float muon_momentum, int32_t step,
+                             float* h_grad_norm) {
+    const float mu[2] = {muon_lr, muon_momentum};
+    return optimizer_step(h, lr, step, h_grad_norm, mu);
 }
 
 gpt_status gpt_num_tensors(const gpt_handle* h, int32_t* n) {
@@ -1457,6 +1523,52 @@ gpt_status gptk_gemm_fp8(int32_t M, int32_t N, int32_t K, const void* A, const v
     gk::quantize_e4m3(A, (int64_t)M * K, aq, sc + 2, sc, part, s);
     gk::quantize_e4m3(B, (int64_t)N * K, bq, sc + 3, sc + 1, part + 1024, s);
     gk::gemm_f8(M, N, K, aq, K, bq, K, C, N, sc, s);
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
+
+// scratch layout of gptk_muon_orthogonalize: buffer and direction (fp32, r c
+// each), two iterates (m n), A, A A, a I + b A + c A A (m m), tile sums, the
+// unit clip coefficient and the normalisation (two floats), and a cleared skip flag
+static int64_t muon_test_layout(int32_t r, int32_t c, int32_t bf16, int64_t off[10]) {
+    const int64_t rc = (int64_t)r * c, m = std::min(r, c), ab = bf16 ? 2 : 4;
+    const int64_t sz[10] = {4 * rc, 4 * rc, ab * rc, ab * rc, ab * m * m, ab * m * m, ab * m * m,
+                            4 * gk::muon_part_floats(r, c), 8, 4};
+    int64_t o = 0;
+    for (int i = 0; i < 10; ++i) {
+        off[i] = o;
+        o += (sz[i] + 255) / 256 * 256;
+    }
+    return o;
+}
+
+int64_t gptk_muon_scratch_bytes(int32_t r, int32_t c, int32_t bf16) {
+    if (r < 1 || c < 1) return 0;
+    int64_t off[10];
+    return muon_test_layout(r, c, bf16, off);
+}
+
+gpt_status gptk_muon_orthogonalize(int32_t r, int32_t c, const float* G, float* O, int32_t bf16, void* scratch,
+                                   int64_t scratch_bytes, void* stream) {
+    if (r < 1 || c < 1 || !G || !O || !scratch || (uintptr_t)scratch % 256 ||
+        scratch_bytes < gptk_muon_scratch_bytes(r, c, bf16))
+        return GPT_ERR_INVALID_ARGUMENT;
+    int64_t off[10];
+    (void)muon_test_layout(r, c, bf16, off);
+    char* p = (char*)scratch;
+    auto at = [&](int i) { return (void*)(p + off[i]); };
+    hipStream_t s = (hipStream_t)stream;
+    const int m = std::min(r, c), n = std::max(r, c);
+    float* one = (float*)at(8);
+    int32_t* skip = (int32_t*)at(9);
+    gk::fill_f32((float*)at(0), (int64_t)r * c, 0.f, s);
+    gk::fill_f32(one, 1, 1.f, s);
+    gk::fill_i32(skip, 1, 0, s);
+    gk::fill_f32(O, (int64_t)r * c, 0.f, s);
+    // momentum 0 from a zero buffer: the direction is G itself
+    gk::muon_direction(G, (float*)at(0), (float*)at(1), (float*)at(7), r, c, 0.f, one, skip, one + 1, s);
+    void* X = gk::muon_newton_schulz(bf16 != 0, (float*)at(1), one + 1, m, n, at(2), at(3), at(4), at(5), at(6),
+                                     nullptr, 0, s);
+    gk::muon_apply(bf16 != 0, O, nullptr, X, r, c, -1.f, skip, s);
     return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
 }
 

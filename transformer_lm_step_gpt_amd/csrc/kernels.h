@@ -199,6 +199,20 @@ void skinny_gemm(const Gemm& g, hipStream_t s);
 // strides lda and ldb (bytes), K % 128 == 0, lda % 16 == ldb % 16 == 0.
 void gemm_f8(int M, int N, int K, const void* A8, int64_t lda, const void* B8, int64_t ldb, void* C, int64_t ldc,
              const float* inv_sa_sb, hipStream_t s);
+// Muon for a hidden matrix W [r, c] (muon.hip). muon_direction: buf <- mu buf +
+// coef g, u = coef g + mu buf written wide ([c, r] when r > c), scale[0] =
+// 1 / (|u|_F + 1e-7) (part: muon_part_floats(r, c) floats). muon_newton_schulz:
+// five quintic iterations on X [m, n] = u * scale (m <= n; X0, X1 m n and A,
+// AA, Bp m m elements, bf16 when bf), returning the buffer with the result.
+// muon_apply: W -= step * X oriented back, bf16 shadow wbf (nullable) refreshed.
+// The momentum and apply kernels do nothing when *nonfinite is set.
+int64_t muon_part_floats(int r, int c);
+void muon_direction(const float* g, float* buf, float* u, float* part, int r, int c, float mu, const float* coef,
+                    const int32_t* nonfinite, float* scale, hipStream_t s);
+void* muon_newton_schulz(bool bf, const float* u, const float* scale, int m, int n, void* X0, void* X1, void* A,
+                         void* AA, void* Bp, float* splitk, size_t splitk_floats, hipStream_t s);
+void muon_apply(bool bf, float* W, void* wbf, const void* X, int r, int c, float step, const int32_t* nonfinite,
+                hipStream_t s);
 // Per-tensor e4m3 quantisation of a bf16 tensor (n % 8 == 0):
 // *scale = 448 / max|x| (1 for an all-zero tensor), *inv = 1 / *scale,
 // q = e4m3(fp32(x) * scale) rounded to nearest even (saturating at 448);

@@ -72,6 +72,7 @@ _SIGS = [
     ("gpt_forward_backward", c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_float, POINTER(c_float)]),
     ("gpt_loss_accum", c_int32, [c_void_p, POINTER(c_float)]),
     ("gpt_clip_and_adamw", c_int32, [c_void_p, c_float, c_int32, POINTER(c_float)]),
+    ("gpt_clip_and_muon", c_int32, [c_void_p, c_float, c_float, c_float, c_int32, POINTER(c_float)]),
     ("gpt_generate", c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_float, c_int32, c_uint64, c_void_p,
                                c_void_p]),
     ("gpt_num_tensors", c_int32, [c_void_p, POINTER(c_int32)]),
@@ -129,6 +130,9 @@ _SIGS = [
     ("gptk_gemm_fp8", c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
                                 c_void_p]),
     ("gptk_gemm_fp8_scratch_bytes", c_int64, [c_int32, c_int32, c_int32]),
+    ("gptk_muon_orthogonalize", c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_int32, c_void_p, c_int64,
+                                          c_void_p]),
+    ("gptk_muon_scratch_bytes", c_int64, [c_int32, c_int32, c_int32]),
     ("gptk_colsum", c_int32, [c_int32, c_int32, c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
     ("gptk_colsum_partial_floats", c_int64, [c_int32, c_int32]),
 ]
@@ -251,6 +255,15 @@ class GPT:
         self._sync_stream()
         norm = c_float()
         check(self.lib.gpt_clip_and_adamw(self.handle, lr, step, byref(norm) if sync else None), self.handle)
+        return norm.value if sync else None
+
+    def clip_and_muon(self, lr: float, muon_lr: float, muon_momentum: float, step: int,
+                      sync: bool = True) -> Optional[float]:
+        """Clip, Muon on the hidden matrices, AdamW on the rest (gpt_clip_and_muon)."""
+        self._sync_stream()
+        norm = c_float()
+        check(self.lib.gpt_clip_and_muon(self.handle, lr, muon_lr, muon_momentum, step,
+                                         byref(norm) if sync else None), self.handle)
         return norm.value if sync else None
 
     def generate(self, prompt, n_new: int, temperature: float = 1.0, top_k: int = 50, seed: int = 0,

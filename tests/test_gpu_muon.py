@@ -193,13 +193,14 @@ def test_muon_train_step_tiny_fp32_vs_oracle_end_to_end():
 @pytest.mark.timeout(600)
 def test_muon_step_gpt2_124m_bf16():
     """124M shape, one micro-batch of two distinct sequences, then a Muon step;
-    the four hidden matrices of the first and last block against the oracle fed
-    with the GPU's gradients, wte (AdamW) to 1e-6."""
+    the four hidden matrices of the first, a middle and the last block (first,
+    middle and last entries of each batched orthogonalisation) against the
+    oracle fed with the GPU's gradients, wte (AdamW) to 1e-6."""
     w = I.GPT2_124M
     cfg = w.model
     gpu = make(cfg, w.init_seed)
     x, y = next(I.batches(w, 2, 1024))
-    names = [n for n in hidden_names(cfg) if n.startswith("h.0.") or n.startswith(f"h.{cfg.n_layer - 1}.")]
+    names = [n for n in hidden_names(cfg) if n.split(".")[1] in ("0", "5", str(cfg.n_layer - 1))]
     p0 = {n: gpu.get_param(n).astype(np.float64) for n in names + ["wte"]}
     gpu.forward_backward(x, y)
     g = {n: a.astype(np.float64) for n, a in gpu.grads().items()}
@@ -215,6 +216,29 @@ def test_muon_step_gpt2_124m_bf16():
         check_bf16_subspace(gpu.get_param(n) - p0[n], want, u, n)
         m1, v1 = gpu.get_opt_state(n)
         assert relmax(m1, g[n] * coef) <= 1e-6 and not np.any(v1), n
+
+
+@pytest.mark.timeout(600)
+def test_muon_step_char_bf16_every_matrix():
+    """bf16 char model (6 layers, d 384, F 1536): every hidden matrix of a Muon
+    step (four batched orthogonalisations of six entries) against the oracle
+    fed with the GPU's gradients; the momentum buffers to 1e-6."""
+    w = I.CHAR_BF16
+    cfg = w.model
+    gpu = make(cfg, w.init_seed)
+    x, y = next(I.batches(w, 8, w.seq_len))
+    names = hidden_names(cfg)
+    p0 = {n: gpu.get_param(n).astype(np.float64) for n in names}
+    gpu.forward_backward(x, y)
+    g = {n: a.astype(np.float64) for n, a in gpu.grads().items()}
+    gpu.clip_and_muon(LR, MUON_LR, MU, 1)
+    coef = O.clip_coefficient(O.grad_norm(g), cfg.max_grad_norm)
+    for n in names:
+        r, c = p0[n].shape
+        u = g[n] * coef * (1 + MU)
+        want = -MUON_LR * np.sqrt(max(1.0, r / c)) * O.newton_schulz5(u)
+        check_bf16_subspace(gpu.get_param(n) - p0[n], want, u, n)
+        assert relmax(gpu.get_opt_state(n)[0], g[n] * coef) <= 1e-6, n
 
 
 def test_muon_rejects_bad_arguments_and_skips_nonfinite():

@@ -120,7 +120,20 @@ void gemm_finish(const Gemm& g, const GemmPlan& p, const float* splitk_scratch, 
     if (p.cfg >= 0) gemm_mfma_reduce(g, p, splitk_scratch, s);
 }
 void gemm(const Gemm& g, float* splitk_scratch, size_t splitk_floats, hipStream_t s) {
-    const GemmPlan p = gemm_plan(g, splitk_floats);
+    if (g.batch > 1 && !gemm_mfma_ok(g)) {
+        // the portable kernel takes one entry per launch
+        Gemm e = g;
+        e.batch = 1;
+        const int64_t ea = g.in_bf ? 2 : 4, ec = g.c_bf ? 2 : 4;
+        for (int b = 0; b < g.batch; ++b) {
+            e.A = (const char*)g.A + b * g.sa * ea;
+            e.B = (const char*)g.B + b * g.sb * ea;
+            e.C = (char*)g.C + b * g.sc * ec;
+            gemm_simple(e, s);
+        }
+        return;
+    }
+    const GemmPlan p = gemm_plan(g, g.batch > 1 ? 0 : splitk_floats);
     gemm_main(g, p, splitk_scratch, s);
     gemm_finish(g, p, splitk_scratch, s);
 }

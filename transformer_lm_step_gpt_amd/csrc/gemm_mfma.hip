@@ -62,6 +62,7 @@ bool gemm_mfma_ok(const Gemm& g) {
     if (g.N % 8 || g.N < 8 || g.ldc % 8) return false;     // 16-byte epilogue chunks
     if (!g.a_kc && g.b_kc) return false;     // orientation not used by the training step
     if (!layout_has_epi(g.a_kc, g.b_kc, g.epi)) return false;   // not instantiated for this layout
+    if (g.batch > 1 && (g.epi != EPI_STORE || g.sa % 8 || g.sb % 8 || g.sc % 8 || g.batch > 65535)) return false;
     const bool bias = g.epi == EPI_BIAS || g.epi == EPI_BIAS_ACT || g.epi == EPI_BIAS_RESID;
     if (!aligned16(g.C) || (g.epi == EPI_BIAS_ACT && !aligned16(g.C2)) || (bias && !aligned16(g.bias)) ||
         (g.epi == EPI_BIAS_RESID && !aligned16(g.resid)) || (g.epi == EPI_ACT_GRAD && !aligned16(g.aux)))
@@ -160,8 +161,8 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
             const int kps = ceil_div(ceil_div(g.K, sp), cfg_bk[ci]) * cfg_bk[ci];
             const int used = ceil_div(g.K, kps);
             if (used != sp) continue;
-            if (sp > 1 && ((size_t)sp * mn > nscratch || kps < 256)) continue;
-            const int64_t wgs = (int64_t)ceil_div(g.M, bm) * ceil_div(g.N, bn) * sp;
+            if (sp > 1 && ((size_t)sp * mn > nscratch || kps < 256 || g.batch > 1)) continue;
+            const int64_t wgs = (int64_t)ceil_div(g.M, bm) * ceil_div(g.N, bn) * sp * std::max(1, g.batch);
             const int64_t per_cu = (wgs + cus - 1) / cus, rounds = (wgs + (int64_t)cus * occ - 1) / ((int64_t)cus * occ);
             // with two workgroups per CU the rate holds for pairs; a workgroup
             // alone on its CU reaches about 60% of it
@@ -190,6 +191,7 @@ GemmPlan gemm_mfma_plan(const Gemm& g, size_t nscratch) {
             }
         }
     }
+    if (g.batch > 1) bsplits = 1;   // batched products run every entry over the whole K
     GemmPlan p{};
     p.cfg = bcfg;
     p.splits = bsplits;

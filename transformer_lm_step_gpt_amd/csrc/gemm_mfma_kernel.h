@@ -265,15 +265,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_mfma_kernel(Gemm g, 
     const int tn = ceil_div(g.N, BN), tm = ceil_div(g.M, BM), ntiles = tn * tm;
     // XCD-aware renumbering: workgroups are dispatched in order of the
     // flattened id lin = x + ntiles * z, workgroup lin runs on XCD lin % 8, and
-    // XCD x takes a contiguous range of the work items (k-slice, tile) numbered
-    // slice by slice, tiles in the grouped order below. So one XCD's items
+    // XCD x takes a contiguous range of the work items (k-slice or batch
+    // entry, tile) numbered slice by slice, tiles in the grouped order below. So one XCD's items
     // cover one or two k-slices and a compact group of tiles inside each: its
     // L2 fetches the operand panels of those slices once instead of every
     // slice's whole dY^T panel.
     const int nitems = ntiles * (int)gridDim.z;
     const int lin = blockIdx.x + ntiles * blockIdx.z, xcd = lin & 7, q8 = nitems >> 3, r8 = nitems & 7;
     const int item = xcd * q8 + min(xcd, r8) + (lin >> 3);
-    const int kz = item / ntiles, tile = item - kz * ntiles;
+    int kz = item / ntiles;
+    const int tile = item - kz * ntiles;
+    const bf16* A = (const bf16*)g.A;
+    const bf16* B = (const bf16*)g.B;
+    if constexpr (!SPLIT && EPI == EPI_STORE) {
+        if (g.batch > 1) {   // batched product: z is the batch entry, each over the whole K
+            A += kz * g.sa;
+            B += kz * g.sb;
+            g.C = (TC*)g.C + kz * g.sc;
+            kz = 0;
+        }
+    }
     // grouped order: bands of GROUP_M tile-rows, column by column inside a
     // band, so the tiles resident on one XCD at a time share a few A and B
     // panels in its L2
@@ -283,8 +294,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_mfma_kernel(Gemm g, 
     const int wm = (w / WGN) * WM, wn = (w % WGN) * WN;
     const int kb = kz * kps;
     const int nk = max(0, (min(g.K, kb + kps) - kb) / BK);    // K and kps are multiples of BK
-    const bf16* A = (const bf16*)g.A;
-    const bf16* B = (const bf16*)g.B;
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -775,7 +784,7 @@ static int out_bf(const Gemm& g) {
 
 template <int BM, int BN, int BK, int NS, int OCC, int PIPE, int WGM, int WGN, bool AKC, bool BKC>
 static void run_main(const Gemm& g, const GemmPlan& p, float* part, hipStream_t s) {
-    dim3 grid(ceil_div(g.N, BN) * ceil_div(g.M, BM), 1, p.splits);
+    dim3 grid(ceil_div(g.N, BN) * ceil_div(g.M, BM), 1, g.batch > 1 ? g.batch : p.splits);
     const int kps = ceil_div(ceil_div(g.K, p.splits), BK) * BK;
     if (p.splits > 1) { launch<BM, BN, BK, NS, OCC, PIPE, WGM, WGN, AKC, BKC, EPI_STORE, 0, 0, true>(g, grid, kps, part, s); return; }
     const bool relu = g.act == ACT_RELU2;

@@ -145,11 +145,13 @@ struct Ws {
     // scales [s_x, 1/s_x, s_w, 1/s_w] and the max-reduction partials
     uint8_t *xq = nullptr, *wq = nullptr;
     float *f8_scale = nullptr, *f8_part = nullptr;
-    // Muon: the direction u (fp32, wide), the iterates X (two), A, A A and
-    // a I + b A + c A A (act), per-tile sums of squares and the normalisation
+    // Muon, for the n_layer matrices of one kind at a time: the directions u
+    // (fp32, wide), the iterates X (two sets), A, A A and a I + b A + c A A
+    // (act), per-tile sums of squares and the normalisations
     float* mu_u = nullptr;
     void *mu_x0 = nullptr, *mu_x1 = nullptr, *mu_a = nullptr, *mu_aa = nullptr, *mu_b = nullptr;
     float *mu_part = nullptr, *mu_scale = nullptr;
+    int64_t mu_part_stride = 0;
     float *dec_x = nullptr, *dec_x2 = nullptr, *dec_mean = nullptr, *dec_rstd = nullptr, *dec_logits = nullptr;
     void *dec_y = nullptr, *dec_qkv = nullptr, *dec_qk = nullptr, *dec_att = nullptr, *dec_h1 = nullptr,
          *dec_h2 = nullptr;
@@ -251,7 +253,7 @@ Ws plan(const gpt_config& c, const Table& tb, void* base) {
     }
     {
         // hidden matrices: [3d, d], [d, d], [F, d], [d, F]; the wide side m <= d
-        const int64_t mn = std::max<int64_t>(3 * d * d, F * d), mm = d * d;
+        const int64_t mn = L * std::max<int64_t>(3 * d * d, F * d), mm = L * d * d;
         const int64_t np = std::max({gk::muon_part_floats((int)(3 * d), (int)d), gk::muon_part_floats((int)F, (int)d),
                                      gk::muon_part_floats((int)d, (int)d)});
         w.mu_u = cv.arr<float>(mn);
@@ -260,8 +262,9 @@ Ws plan(const gpt_config& c, const Table& tb, void* base) {
         w.mu_a = cv.take(ab * mm);
         w.mu_aa = cv.take(ab * mm);
         w.mu_b = cv.take(ab * mm);
-        w.mu_part = cv.arr<float>(np);
-        w.mu_scale = cv.arr<float>(1);
+        w.mu_part = cv.arr<float>(L * np);
+        w.mu_part_stride = np;
+        w.mu_scale = cv.arr<float>(L);
     }
     for (int l = 0; l < L; ++l) {
         w.kcache.push_back(cv.take(ab * M * d));
@@ -1155,23 +1158,35 @@ static gpt_status optimizer_step(gpt_handle* h, float lr, int32_t step, float* h
             gk::adamw(w.params + tb.n_decay, w.grads + tb.n_decay, w.m + tb.n_decay, w.v + tb.n_decay, nullptr, nu, 0,
                       w.coef, w.nonfinite, lr, c.beta1, c.beta2, c.adam_eps, c.weight_decay, rbc1, rbc2, st);
         }
+        // one kind of hidden matrix at a time, its n_layer matrices as one batch
         const double ab = bf ? 2 : 4;
-        for (const LayerIdx& li : tb.layers)
-            for (int idx : {li.attn_w, li.proj_w, li.fc_w, li.mp_w}) {
-                const TensorInfo& ti = tb.t[idx];
-                const int r = (int)ti.shape[0], cc = (int)ti.shape[1], mr = std::min(r, cc), nr = std::max(r, cc);
-                const double mn = (double)mr * nr, m2 = (double)mr * mr;
-                // five iterations of three products: 2 m n m + 2 m m m + 2 m m n flops
-                Timed t(h, KC_MUON, 5.0 * (4.0 * mn * mr + 2.0 * m2 * mr),
-                        20.0 * mn + 5.0 * ab * (3.0 * mn + 5.0 * m2) + 12.0 * mn);
-                gk::muon_direction(w.grads + ti.offset, w.m + ti.offset, w.mu_u, w.mu_part, r, cc, muon[1], w.coef,
-                                   w.nonfinite, w.mu_scale, st);
-                void* X = gk::muon_newton_schulz(bf, w.mu_u, w.mu_scale, mr, nr, w.mu_x0, w.mu_x1, w.mu_a, w.mu_aa,
-                                                 w.mu_b, w.splitk, w.splitk_floats, st);
-                const float stepsz = (float)(muon[0] * std::sqrt(std::max(1.0, (double)r / cc)));
-                gk::muon_apply(bf, w.params + ti.offset, bf ? (char*)w.wbf + 2 * ti.offset : nullptr, X, r, cc,
-                               stepsz, w.nonfinite, st);
+        const int L = c.n_layer;
+        for (int kind = 0; kind < 4; ++kind) {
+            auto idx_of = [&](int l) {
+                const LayerIdx& li = tb.layers[l];
+                return kind == 0 ? li.attn_w : kind == 1 ? li.proj_w : kind == 2 ? li.fc_w : li.mp_w;
+            };
+            const TensorInfo& t0 = tb.t[idx_of(0)];
+            const int r = (int)t0.shape[0], cc = (int)t0.shape[1], mr = std::min(r, cc), nr = std::max(r, cc);
+            const int64_t mn = (int64_t)mr * nr;
+            const double m2 = (double)mr * mr;
+            // five iterations of three products: 2 m n m + 2 m m m + 2 m m n flops per matrix
+            Timed t(h, KC_MUON, L * 5.0 * (4.0 * (double)mn * mr + 2.0 * m2 * mr),
+                    L * (20.0 * mn + 5.0 * ab * (3.0 * mn + 5.0 * m2) + 12.0 * mn));
+            for (int l = 0; l < L; ++l) {
+                const TensorInfo& ti = tb.t[idx_of(l)];
+                gk::muon_direction(w.grads + ti.offset, w.m + ti.offset, w.mu_u + l * mn, w.mu_part + l * w.mu_part_stride,
+                                   r, cc, muon[1], w.coef, w.nonfinite, w.mu_scale + l, st);
             }
+            char* X = (char*)gk::muon_newton_schulz(bf, w.mu_u, w.mu_scale, mr, nr, L, w.mu_x0, w.mu_x1, w.mu_a,
+                                                    w.mu_aa, w.mu_b, w.splitk, w.splitk_floats, st);
+            const float stepsz = (float)(muon[0] * std::sqrt(std::max(1.0, (double)r / cc)));
+            for (int l = 0; l < L; ++l) {
+                const TensorInfo& ti = tb.t[idx_of(l)];
+                gk::muon_apply(bf, w.params + ti.offset, bf ? (char*)w.wbf + 2 * ti.offset : nullptr,
+                               X + (size_t)ab * l * mn, r, cc, stepsz, w.nonfinite, st);
+            }
+        }
     }
     h->grads_dirty = true;
     gpt_status s = hip_check(h, hipGetLastError(), "kernel launch");
@@ -1566,7 +1581,7 @@ gpt_status gptk_muon_orthogonalize(int32_t r, int32_t c, const float* G, float* 
     gk::fill_f32(O, (int64_t)r * c, 0.f, s);
     // momentum 0 from a zero buffer: the direction is G itself
     gk::muon_direction(G, (float*)at(0), (float*)at(1), (float*)at(7), r, c, 0.f, one, skip, one + 1, s);
-    void* X = gk::muon_newton_schulz(bf16 != 0, (float*)at(1), one + 1, m, n, at(2), at(3), at(4), at(5), at(6),
+    void* X = gk::muon_newton_schulz(bf16 != 0, (float*)at(1), one + 1, m, n, 1, at(2), at(3), at(4), at(5), at(6),
                                      nullptr, 0, s);
     gk::muon_apply(bf16 != 0, O, nullptr, X, r, c, -1.f, skip, s);
     return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;

@@ -173,6 +173,10 @@ struct Gemm {
     // the rows m of one bm-row block of the fp32 output values (column sums
     // for a bias gradient, reduced later)
     float* cpart = nullptr;
+    // batched products (STORE epilogue only, no split-K): entry b reads A + b sa
+    // and B + b sb and writes C + b sc (element strides)
+    int batch = 1;
+    int64_t sa = 0, sb = 0, sc = 0;
 };
 // How a product runs: kernel (matrix-core tile configuration, or cfg = -1
 // for the portable kernel), split-K factor, and the name of the main kernel
@@ -202,15 +206,16 @@ void gemm_f8(int M, int N, int K, const void* A8, int64_t lda, const void* B8, i
 // Muon for a hidden matrix W [r, c] (muon.hip). muon_direction: buf <- mu buf +
 // coef g, u = coef g + mu buf written wide ([c, r] when r > c), scale[0] =
 // 1 / (|u|_F + 1e-7) (part: muon_part_floats(r, c) floats). muon_newton_schulz:
-// five quintic iterations on X [m, n] = u * scale (m <= n; X0, X1 m n and A,
-// AA, Bp m m elements, bf16 when bf), returning the buffer with the result.
+// five quintic iterations on a batch of X_e [m, n] = u_e * scale[e] (m <= n;
+// X0, X1 batch m n and A, AA, Bp batch m m elements, bf16 when bf), returning
+// the buffer with the results.
 // muon_apply: W -= step * X oriented back, bf16 shadow wbf (nullable) refreshed.
 // The momentum and apply kernels do nothing when *nonfinite is set.
 int64_t muon_part_floats(int r, int c);
 void muon_direction(const float* g, float* buf, float* u, float* part, int r, int c, float mu, const float* coef,
                     const int32_t* nonfinite, float* scale, hipStream_t s);
-void* muon_newton_schulz(bool bf, const float* u, const float* scale, int m, int n, void* X0, void* X1, void* A,
-                         void* AA, void* Bp, float* splitk, size_t splitk_floats, hipStream_t s);
+void* muon_newton_schulz(bool bf, const float* u, const float* scale, int m, int n, int batch, void* X0, void* X1,
+                         void* A, void* AA, void* Bp, float* splitk, size_t splitk_floats, hipStream_t s);
 void muon_apply(bool bf, float* W, void* wbf, const void* X, int r, int c, float step, const int32_t* nonfinite,
                 hipStream_t s);
 // Per-tensor e4m3 quantisation of a bf16 tensor (n % 8 == 0):

@@ -87,28 +87,34 @@ __global__ __launch_bounds__(256) void muon_norm_kernel(const float* __restrict_
     if (threadIdx.x == 0) scale[0] = (float)(1.0 / (sqrt((red[0] + red[1]) + (red[2] + red[3])) + (double)eps));
 }
 
-// X = u * scale[0] (storage TX)
+// X_e = u_e * scale[e] for the entries e of a batch of mn-element matrices (storage TX)
 template <typename TX>
-__global__ __launch_bounds__(256) void muon_scale_kernel(const float* __restrict__ u, TX* __restrict__ X, int64_t n,
-                                                         const float* __restrict__ scale) {
+__global__ __launch_bounds__(256) void muon_scale_kernel(const float* __restrict__ u, TX* __restrict__ X, int64_t mn,
+                                                         int batch, const float* __restrict__ scale) {
+    const int e = blockIdx.y;
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= n) return;
-    const float s = scale[0];
-    if (i + 4 <= n) {
-        const float4 v = load4(u + i);
-        store4(X + i, make_float4(v.x * s, v.y * s, v.z * s, v.w * s));
+    if (i >= mn) return;
+    const float s = scale[e];
+    const float* ue = u + e * mn;
+    TX* xe = X + e * mn;
+    if (i + 4 <= mn && mn % 4 == 0) {
+        const float4 v = load4(ue + i);
+        store4(xe + i, make_float4(v.x * s, v.y * s, v.z * s, v.w * s));
     } else {
-        for (int64_t j = i; j < n; ++j) X[j] = (TX)(u[j] * s);
+        const int64_t end = i + 4 < mn ? i + 4 : mn;
+        for (int64_t j = i; j < end; ++j) xe[j] = (TX)(ue[j] * s);
     }
 }
 
-// Bp = a I + b A + c AA over [m, m]
+// Bp = a I + b A + c AA over a batch of [m, m] matrices
 template <typename TX>
 __global__ __launch_bounds__(256) void muon_poly_kernel(const TX* __restrict__ A, const TX* __restrict__ AA,
-                                                        TX* __restrict__ Bp, int m, float a, float b, float c) {
+                                                        TX* __restrict__ Bp, int m, int64_t total, float a, float b,
+                                                        float c) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)m * m) return;
-    const int row = (int)(i / m), col = (int)(i - (int64_t)row * m);
+    if (i >= total) return;
+    const int64_t k = i % ((int64_t)m * m);
+    const int row = (int)(k / m), col = (int)(k - (int64_t)row * m);
     float v = b * (float)A[i] + c * (float)AA[i];
     if (row == col) v += a;
     Bp[i] = (TX)v;
@@ -155,16 +161,19 @@ void muon_direction(const float* g, float* buf, float* u, float* part, int r, in
     muon_norm_kernel<<<1, 256, 0, s>>>(part, (int)(grid.x * grid.y), 1e-7f, scale);
 }
 
-// Five Newton-Schulz iterations on X [m, n] (m <= n), X normalised from u.
-// X0 and X1 hold m * n elements, A, AA, Bp m * m (storage bf16 when bf).
-// Returns the buffer that holds the result (X1: an odd number of iterations).
-void* muon_newton_schulz(bool bf, const float* u, const float* scale, int m, int n, void* X0, void* X1, void* A,
-                         void* AA, void* Bp, float* splitk, size_t splitk_floats, hipStream_t s) {
-    const int64_t mn = (int64_t)m * n;
-    const unsigned nb = (unsigned)ceil_div(ceil_div(mn, (int64_t)4), (int64_t)256);
-    if (bf) muon_scale_kernel<bf16><<<nb, 256, 0, s>>>(u, (bf16*)X0, mn, scale);
-    else muon_scale_kernel<float><<<nb, 256, 0, s>>>(u, (float*)X0, mn, scale);
-    auto prod = [&](int M, int N, int K, const void* Ap, int64_t lda, const void* Bq, int64_t ldb, bool b_kc, void* C) {
+// Five Newton-Schulz iterations on a batch of matrices X_e [m, n] (m <= n),
+// X_e = u_e * scale[e] with u_e at u + e m n. X0 and X1 hold batch * m * n
+// elements, A, AA, Bp batch * m * m (storage bf16 when bf); the products of
+// all entries run as one batched launch each. Returns the buffer that holds
+// the results (X1: an odd number of iterations).
+void* muon_newton_schulz(bool bf, const float* u, const float* scale, int m, int n, int batch, void* X0, void* X1,
+                         void* A, void* AA, void* Bp, float* splitk, size_t splitk_floats, hipStream_t s) {
+    const int64_t mn = (int64_t)m * n, mm = (int64_t)m * m;
+    const dim3 gs((unsigned)ceil_div(ceil_div(mn, (int64_t)4), (int64_t)256), (unsigned)batch);
+    if (bf) muon_scale_kernel<bf16><<<gs, 256, 0, s>>>(u, (bf16*)X0, mn, batch, scale);
+    else muon_scale_kernel<float><<<gs, 256, 0, s>>>(u, (float*)X0, mn, batch, scale);
+    auto prod = [&](int M, int N, int K, const void* Ap, int64_t lda, int64_t sa, const void* Bq, int64_t ldb,
+                    int64_t sb, bool b_kc, void* C, int64_t sc) {
         Gemm g{};
         g.M = M; g.N = N; g.K = K;
         g.A = Ap; g.lda = lda; g.a_kc = true;
@@ -172,19 +181,20 @@ void* muon_newton_schulz(bool bf, const float* u, const float* scale, int m, int
         g.C = C; g.ldc = N; g.c_bf = bf;
         g.epi = EPI_STORE;
         g.in_bf = bf;
+        g.batch = batch; g.sa = sa; g.sb = sb; g.sc = sc;
         gemm(g, splitk, splitk_floats, s);
     };
     void* X = X0;
     void* Y = X1;
-    const unsigned nbm = (unsigned)ceil_div((int64_t)m * m, (int64_t)256);
+    const unsigned nbm = (unsigned)ceil_div(batch * mm, (int64_t)256);
     for (int it = 0; it < 5; ++it) {
-        prod(m, m, n, X, n, X, n, true, A);       // A = X X^T
-        prod(m, m, m, A, m, A, m, false, AA);     // A A
-        if (bf) muon_poly_kernel<bf16><<<nbm, 256, 0, s>>>((const bf16*)A, (const bf16*)AA, (bf16*)Bp, m, 3.4445f,
-                                                            -4.7750f, 2.0315f);
-        else muon_poly_kernel<float><<<nbm, 256, 0, s>>>((const float*)A, (const float*)AA, (float*)Bp, m, 3.4445f,
-                                                          -4.7750f, 2.0315f);
-        prod(m, n, m, Bp, m, X, n, false, Y);     // (a I + b A + c A A) X
+        prod(m, m, n, X, n, mn, X, n, mn, true, A, mm);       // A = X X^T
+        prod(m, m, m, A, m, mm, A, m, mm, false, AA, mm);     // A A
+        if (bf) muon_poly_kernel<bf16><<<nbm, 256, 0, s>>>((const bf16*)A, (const bf16*)AA, (bf16*)Bp, m, batch * mm,
+                                                            3.4445f, -4.7750f, 2.0315f);
+        else muon_poly_kernel<float><<<nbm, 256, 0, s>>>((const float*)A, (const float*)AA, (float*)Bp, m, batch * mm,
+                                                          3.4445f, -4.7750f, 2.0315f);
+        prod(m, n, m, Bp, m, mm, X, n, mn, false, Y, mn);     // (a I + b A + c A A) X
         std::swap(X, Y);
     }
     return X;

@@ -1173,18 +1173,32 @@ static gpt_status optimizer_step(gpt_handle* h, float lr, int32_t step, float* h
             // five iterations of three products: 2 m n m + 2 m m m + 2 m m n flops per matrix
             Timed t(h, KC_MUON, L * 5.0 * (4.0 * (double)mn * mr + 2.0 * m2 * mr),
                     L * (20.0 * mn + 5.0 * ab * (3.0 * mn + 5.0 * m2) + 12.0 * mn));
-            for (int l = 0; l < L; ++l) {
-                const TensorInfo& ti = tb.t[idx_of(l)];
-                gk::muon_direction(w.grads + ti.offset, w.m + ti.offset, w.mu_u + l * mn, w.mu_part + l * w.mu_part_stride,
-                                   r, cc, muon[1], w.coef, w.nonfinite, w.mu_scale + l, st);
+            // the layers' matrices of one kind sit at a constant stride in the flat layout
+            const int64_t o0 = t0.offset, os = L > 1 ? tb.t[idx_of(1)].offset - o0 : 0;
+            bool strided = true;
+            for (int l = 0; l < L; ++l) strided = strided && tb.t[idx_of(l)].offset == o0 + l * os;
+            const float stepsz = (float)(muon[0] * std::sqrt(std::max(1.0, (double)r / cc)));
+            if (strided) {
+                gk::muon_direction(w.grads + o0, w.m + o0, os, L, w.mu_u, w.mu_part, w.mu_part_stride, r, cc, muon[1],
+                                   w.coef, w.nonfinite, w.mu_scale, st);
+            } else {
+                for (int l = 0; l < L; ++l) {
+                    const int64_t ol = tb.t[idx_of(l)].offset;
+                    gk::muon_direction(w.grads + ol, w.m + ol, 0, 1, w.mu_u + l * mn, w.mu_part + l * w.mu_part_stride,
+                                       0, r, cc, muon[1], w.coef, w.nonfinite, w.mu_scale + l, st);
+                }
             }
             char* X = (char*)gk::muon_newton_schulz(bf, w.mu_u, w.mu_scale, mr, nr, L, w.mu_x0, w.mu_x1, w.mu_a,
                                                     w.mu_aa, w.mu_b, w.splitk, w.splitk_floats, st);
-            const float stepsz = (float)(muon[0] * std::sqrt(std::max(1.0, (double)r / cc)));
-            for (int l = 0; l < L; ++l) {
-                const TensorInfo& ti = tb.t[idx_of(l)];
-                gk::muon_apply(bf, w.params + ti.offset, bf ? (char*)w.wbf + 2 * ti.offset : nullptr,
-                               X + (size_t)ab * l * mn, r, cc, stepsz, w.nonfinite, st);
+            if (strided) {
+                gk::muon_apply(bf, w.params + o0, bf ? (char*)w.wbf + 2 * o0 : nullptr, os, L, X, r, cc, stepsz,
+                               w.nonfinite, st);
+            } else {
+                for (int l = 0; l < L; ++l) {
+                    const int64_t ol = tb.t[idx_of(l)].offset;
+                    gk::muon_apply(bf, w.params + ol, bf ? (char*)w.wbf + 2 * ol : nullptr, 0, 1,
+                                   X + (size_t)ab * l * mn, r, cc, stepsz, w.nonfinite, st);
+                }
             }
         }
     }
@@ -1580,10 +1594,10 @@ gpt_status gptk_muon_orthogonalize(int32_t r, int32_t c, const float* G, float* 
     gk::fill_i32(skip, 1, 0, s);
     gk::fill_f32(O, (int64_t)r * c, 0.f, s);
     // momentum 0 from a zero buffer: the direction is G itself
-    gk::muon_direction(G, (float*)at(0), (float*)at(1), (float*)at(7), r, c, 0.f, one, skip, one + 1, s);
+    gk::muon_direction(G, (float*)at(0), 0, 1, (float*)at(1), (float*)at(7), 0, r, c, 0.f, one, skip, one + 1, s);
     void* X = gk::muon_newton_schulz(bf16 != 0, (float*)at(1), one + 1, m, n, 1, at(2), at(3), at(4), at(5), at(6),
                                      nullptr, 0, s);
-    gk::muon_apply(bf16 != 0, O, nullptr, X, r, c, -1.f, skip, s);
+    gk::muon_apply(bf16 != 0, O, nullptr, 0, 1, X, r, c, -1.f, skip, s);
     return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
 }
 

@@ -203,21 +203,23 @@ void skinny_gemm(const Gemm& g, hipStream_t s);
 // strides lda and ldb (bytes), K % 128 == 0, lda % 16 == ldb % 16 == 0.
 void gemm_f8(int M, int N, int K, const void* A8, int64_t lda, const void* B8, int64_t ldb, void* C, int64_t ldc,
              const float* inv_sa_sb, hipStream_t s);
-// Muon for a hidden matrix W [r, c] (muon.hip). muon_direction: buf <- mu buf +
-// coef g, u = coef g + mu buf written wide ([c, r] when r > c), scale[0] =
-// 1 / (|u|_F + 1e-7) (part: muon_part_floats(r, c) floats). muon_newton_schulz:
-// five quintic iterations on a batch of X_e [m, n] = u_e * scale[e] (m <= n;
-// X0, X1 batch m n and A, AA, Bp batch m m elements, bf16 when bf), returning
-// the buffer with the results.
-// muon_apply: W -= step * X oriented back, bf16 shadow wbf (nullable) refreshed.
-// The momentum and apply kernels do nothing when *nonfinite is set.
+// Muon for the hidden matrices (muon.hip), a batch of same-shaped W_e [r, c]
+// at element stride os in the flat parameter, gradient and buffer arrays.
+// muon_direction: buf <- mu buf + coef g, u_e = coef g + mu buf written wide
+// ([c, r] when r > c) at u + e r c, scale[e] = 1 / (|u_e|_F + 1e-7) (part: ps >=
+// muon_part_floats(r, c) floats per entry). muon_newton_schulz: five quintic
+// iterations on X_e [m, n] = u_e * scale[e] (m <= n; X0, X1 batch m n and A, AA,
+// Bp batch m m elements, bf16 when bf), returning the buffer with the results.
+// muon_apply: W_e -= step * X_e oriented back, bf16 shadow wbf (nullable, same
+// stride) refreshed. The momentum and apply kernels do nothing when *nonfinite
+// is set.
 int64_t muon_part_floats(int r, int c);
-void muon_direction(const float* g, float* buf, float* u, float* part, int r, int c, float mu, const float* coef,
-                    const int32_t* nonfinite, float* scale, hipStream_t s);
+void muon_direction(const float* g, float* buf, int64_t os, int batch, float* u, float* part, int64_t ps, int r, int c,
+                    float mu, const float* coef, const int32_t* nonfinite, float* scale, hipStream_t s);
 void* muon_newton_schulz(bool bf, const float* u, const float* scale, int m, int n, int batch, void* X0, void* X1,
                          void* A, void* AA, void* Bp, float* splitk, size_t splitk_floats, hipStream_t s);
-void muon_apply(bool bf, float* W, void* wbf, const void* X, int r, int c, float step, const int32_t* nonfinite,
-                hipStream_t s);
+void muon_apply(bool bf, float* W, void* wbf, int64_t os, int batch, const void* X, int r, int c, float step,
+                const int32_t* nonfinite, hipStream_t s);
 // Per-tensor e4m3 quantisation of a bf16 tensor (n % 8 == 0):
 // *scale = 448 / max|x| (1 for an all-zero tensor), *inv = 1 / *scale,
 // q = e4m3(fp32(x) * scale) rounded to nearest even (saturating at 448);

@@ -460,6 +460,7 @@ void layernorm_fwd(bool bf, const float* x, const float* g, const float* b, void
 }
 
 constexpr int LNB_ROWS = 32;   // rows per workgroup in the backward pass (8 per wavefront)
+constexpr int LNB_AHEAD = 2;   // rows whose loads are in flight while one is processed
 
 // partial sums: [3][nb][d] (dgamma, dbeta, column sums of the new dres) + reduction scratch
 size_t layernorm_bwd_partial_floats(int M, int d) {
@@ -529,7 +530,7 @@ GPT_DEV void lnb_row(const LnbIn<NV>& in, const float4* gg, float* __restrict__ 
 // Rows are processed with the next row's loads in flight (software pipeline).
 // dy (the gradient at the LayerNorm output) is fp32 or bf16 (TD).
 template <typename TL, typename TD, int NV>
-__global__ __launch_bounds__(256) void layernorm_bwd_kernel(const TD* __restrict__ dy, const float* __restrict__ x,
+__global__ __launch_bounds__(256, 2) void layernorm_bwd_kernel(const TD* __restrict__ dy, const float* __restrict__ x,
                                                             const float* __restrict__ mean,
                                                             const float* __restrict__ rstd, const float* __restrict__ g,
                                                             float* __restrict__ dres, TL* __restrict__ dres_lp,
@@ -544,21 +545,27 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(const TD* __restrict
         int c = lane + 64 * i;
         gg[i] = 4 * c < d ? load4(g + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    const int r0 = blockIdx.x * LNB_ROWS + w * (LNB_ROWS / 4);
-    const int r1 = min(M, r0 + LNB_ROWS / 4);
-    LnbIn<NV> cur, nxt;
-    if (r0 < r1) {
-        const int64_t o = (int64_t)r0 * d;
-        lnb_load<TD, NV>(cur, dy + o, x + o, dres + o, mean[r0], rstd[r0], overwrite, lane, d);
-    }
-    for (int r = r0; r < r1; ++r) {
-        if (r + 1 < r1) {
-            const int64_t o = (int64_t)(r + 1) * d;
-            lnb_load<TD, NV>(nxt, dy + o, x + o, dres + o, mean[r + 1], rstd[r + 1], overwrite, lane, d);
-        }
+    constexpr int RPW = LNB_ROWS / 4;   // rows per wave
+    const int r0 = blockIdx.x * LNB_ROWS + w * RPW;
+    const int r1 = min(M, r0 + RPW);
+    // the loads of the next LNB_AHEAD rows are in flight while a row is processed
+    // (a ring of LNB_AHEAD + 1 row buffers; the unrolled loop names each one)
+    LnbIn<NV> ring[LNB_AHEAD + 1];
+    auto load_row = [&](LnbIn<NV>& in, int r) {
         const int64_t o = (int64_t)r * d;
-        lnb_row<TL, NV>(cur, gg, dres + o, dres_lp ? dres_lp + o : nullptr, lane, d, ag, ab, ac);
-        cur = nxt;
+        lnb_load<TD, NV>(in, dy + o, x + o, dres + o, mean[r], rstd[r], overwrite, lane, d);
+    };
+#pragma unroll
+    for (int k = 0; k < LNB_AHEAD; ++k)
+        if (r0 + k < r1) load_row(ring[k], r0 + k);
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+        if (r0 + k + LNB_AHEAD < r1) load_row(ring[(k + LNB_AHEAD) % (LNB_AHEAD + 1)], r0 + k + LNB_AHEAD);
+        if (r0 + k < r1) {
+            const int64_t o = (int64_t)(r0 + k) * d;
+            lnb_row<TL, NV>(ring[k % (LNB_AHEAD + 1)], gg, dres + o, dres_lp ? dres_lp + o : nullptr, lane, d, ag, ab,
+                            ac);
+        }
     }
     float4* sets[3] = {ag, ab, ac};
 #pragma unroll

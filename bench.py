@@ -294,6 +294,49 @@ def pmc_table(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernel_json, t
         print(f"algorithmic {unit} per launch (mean over its launches): {per:.0f}")
 
 
+# counters of one rocprofv3 pass (eight SQ counters and one GRBM counter) for --sq-table
+SQ_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
+               "SQ_LDS_BANK_CONFLICT", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+SQ_KERNELS = ["attn_fwd_mfma_kernel", "attn_bwd_dq_mfma_kernel", "attn_bwd_dkdv_mfma_kernel", "layernorm_bwd_kernel",
+              "layernorm_fwd_kernel", "cross_entropy_reg_kernel",
+              "gemm_mfma_kernel<256, 256, 64, 2, 1, 2, 2, 4, false, false, 0, 0, 0, true>",
+              "gemm_mfma_kernel<256, 256, 64, 2, 1, 2, 2, 4, true, true, 0, 1, 0, false>"]
+
+
+def sq_table(d):
+    """Markdown table of instruction-mix counters per kernel (means per dispatch)
+    from a rocprofv3 --pmc run with SQ_COUNTERS; rocprofv3 serialises dispatches
+    while it collects counters, so each figure is the kernel alone.
+    GRBM_GUI_ACTIVE is summed over the XCDs (Num_Xcc in the run's agent info),
+    so the kernel's GPU cycles are GRBM_GUI_ACTIVE / Num_Xcc; MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (cycles x SIMDs) and VALU busy =
+    4 SQ_ACTIVE_INST_VALU / (cycles x SIMDs)."""
+    import csv
+    import glob
+    m = {c: _pmc_means(d, c) for c in SQ_COUNTERS}
+    info = sorted(glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True))[0]
+    gpu = next(r for r in csv.DictReader(open(info)) if r["Agent_Type"] == "GPU")
+    xcc, simds = int(gpu["Num_Xcc"]), int(gpu["Simd_Count"])
+    print(f"{xcc} XCDs, {simds} SIMDs; cycles = GRBM_GUI_ACTIVE / {xcc} (2400 cycles per us at 2.4 GHz)")
+    print("| kernel | cycles | MFMA busy | VALU busy | VALU instr per MFMA instr | LDS instr | "
+          "LDS bank-conflict cycles per LDS instr |")
+    print("|---|---|---|---|---|---|---|")
+    for sub in SQ_KERNELS:
+        names = [n for n in m["GRBM_GUI_ACTIVE"] if sub in n]
+        if not names:
+            continue
+        n = names[0]
+        g = m["GRBM_GUI_ACTIVE"][n] / xcc
+        get = lambda c: m[c].get(n, 0.0)
+        mf = 100 * get("SQ_VALU_MFMA_BUSY_CYCLES") / max(g * simds, 1)
+        va = 100 * 4 * get("SQ_ACTIVE_INST_VALU") / max(g * simds, 1)
+        ratio = get("SQ_INSTS_VALU") / get("SQ_INSTS_MFMA") if get("SQ_INSTS_MFMA") else float("nan")
+        lds = get("SQ_INSTS_LDS")
+        conf = get("SQ_LDS_BANK_CONFLICT") / lds if lds else 0.0
+        short = n.split("(")[0].replace("void ", "").replace("gk::", "")
+        print(f"| `{short}` | {g:.0f} | {mf:.1f}% | {va:.1f}% | {ratio:.1f} | {lds:.0f} | {conf:.3f} |")
+
+
 def generate_bench(a):
     """Sampling with the key/value cache on the 124M model (a second workload,
     not the headline): B sequences of a T0-token prompt, n_new tokens each,
@@ -360,6 +403,8 @@ def main():
     ap.add_argument("--pmc-table", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR",
                                                      "KERNEL_JSON"),
                     help="HBM traffic table of the bandwidth-bound kernels from rocprofv3 --pmc runs")
+    ap.add_argument("--sq-table", metavar="DIR", help="instruction-mix and utilisation table from a rocprofv3 --pmc "
+                    "run with the counters of SQ_COUNTERS")
     ap.add_argument("--pmc-trace", metavar="DIR", help="with --pmc-table: take the alone durations from this "
                                                        "rocprofv3 --kernel-trace run's serialized step")
     ap.add_argument("--pmc-trace-step", type=int, default=None,
@@ -371,6 +416,9 @@ def main():
         return
     if a.rocprof_summary:
         rocprof_summary(a.rocprof_summary)
+        return
+    if a.sq_table:
+        sq_table(a.sq_table)
         return
     if a.trace_gaps:
         trace_gaps(a.trace_gaps, a.steps)

@@ -198,14 +198,17 @@ struct TileRing {
 // accumulator set f32x16[NDF] (rows 8*(e/4) + 4*(lane/32) + e%4 of 32-row blocks
 // are head dims, lanes are the workgroup's queries or keys), scaled by `scale`,
 // lanes with ok = false counting as zero. Summed in LDS in a fixed order (waves,
-// then lanes) and written to out[0 .. HD). red: 4 * NDF * 16 * 64 floats of LDS
+// then lanes) and written to out[0 .. HD). red: 4 * NDF * 16 * COLSUM_LD floats of LDS
 // that no wave reads or writes any more; every thread of the workgroup calls it.
+// Rows of red are COLSUM_LD floats apart, so that the reads of the second phase
+// (one row per head dim, the same column across the wave) fall in distinct banks.
+constexpr int COLSUM_LD = 65;
 template <int HD, int NDF>
 GPT_DEV void block_colsum(const f32x16 (&acc)[NDF], float scale, bool ok, float* red, float* out, int w, int lane) {
     constexpr int NV = NDF * 16;
     barrier_no_fence();
 #pragma unroll
-    for (int v = 0; v < NV; ++v) red[(w * NV + v) * 64 + lane] = ok ? acc[v / 16][v % 16] * scale : 0.f;
+    for (int v = 0; v < NV; ++v) red[(w * NV + v) * COLSUM_LD + lane] = ok ? acc[v / 16][v % 16] * scale : 0.f;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     barrier_no_fence();
     const int d = threadIdx.x;
@@ -214,7 +217,7 @@ GPT_DEV void block_colsum(const f32x16 (&acc)[NDF], float scale, bool ok, float*
         const int v = df * 16 + e;
         float sum = 0.f;
         for (int ww = 0; ww < 4; ++ww)
-            for (int lr = 0; lr < 32; ++lr) sum += red[(ww * NV + v) * 64 + 32 * half + lr];
+            for (int lr = 0; lr < 32; ++lr) sum += red[(ww * NV + v) * COLSUM_LD + 32 * half + lr];
         out[d] = sum;
     }
 }
@@ -342,7 +345,7 @@ template <int HD>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(Attn a) {
     constexpr int NDS = HD / 16, NDF = HD / 32;
     using TL = HTile<HD>;
-    static_assert(2 * ATT_NS * TileRing<HD>::STAGE >= 4 * NDF * 16 * 64 * 4, "column-sum scratch fits in the ring");
+    static_assert(2 * ATT_NS * TileRing<HD>::STAGE >= 4 * NDF * 16 * COLSUM_LD * 4, "column-sum scratch fits in the ring");
     __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
     __shared__ __attribute__((aligned(16))) float Lrow[ATT_MAX_T], Drow[ATT_MAX_T];
     // key blocks in y, (batch, head) in x: the heaviest (first) key blocks of
@@ -464,7 +467,7 @@ template <int HD>
 __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
     constexpr int NDS = HD / 16, NDF = HD / 32;
     using TL = HTile<HD>;
-    static_assert(2 * ATT_NS * TileRing<HD>::STAGE >= 4 * NDF * 16 * 64 * 4, "column-sum scratch fits in the ring");
+    static_assert(2 * ATT_NS * TileRing<HD>::STAGE >= 4 * NDF * 16 * COLSUM_LD * 4, "column-sum scratch fits in the ring");
     __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
     const int qtile = gridDim.y - 1 - blockIdx.y;   // heaviest query tiles of every head first
     const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;

@@ -398,6 +398,19 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_gemm_kernel(Gemm g) {
     const int K = g.K, ldl = K + 8;
     const bf16* W = (const bf16*)g.B;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n0 = blockIdx.x * 16;
+    const int r = lane & 15, kq = lane >> 4;
+    const int nrow = min(n0 + r, g.N - 1);   // columns past N feed only unstored outputs
+    // wave w takes the k range [w K / W, (w + 1) K / W) rounded to 32-deep steps;
+    // its weight fragments are loaded first, so that their latency overlaps the
+    // staging (or LayerNorm) of the activations below
+    const int nst = K / 32, s0 = w * nst / SK_WAVES, s1 = (w + 1) * nst / SK_WAVES;
+    const bf16* wr = W + (int64_t)nrow * g.ldb + 8 * kq;
+    constexpr int MAXST = 4096 / 32 / SK_WAVES;   // K <= 4096
+    bf16x8_t wv[MAXST];
+#pragma unroll
+    for (int i = 0; i < MAXST; ++i)
+        if (s0 + i < s1) wv[i] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * (s0 + i));
     if constexpr (LN) {
         // wave w normalises rows w, w + SK_WAVES: the LayerNorm kernel's
         // arithmetic in its order (lane sums over float4 chunks, wave sums,
@@ -442,20 +455,14 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_gemm_kernel(Gemm g) {
         }
     }
     __syncthreads();
-    const int n0 = blockIdx.x * 16;
-    const int r = lane & 15, kq = lane >> 4;
-    const int nrow = min(n0 + r, g.N - 1);   // columns past N feed only unstored outputs
-    // wave w takes the k range [w K / W, (w + 1) K / W) rounded to 32-deep steps
-    const int nst = K / 32, s0 = w * nst / SK_WAVES, s1 = (w + 1) * nst / SK_WAVES;
-    const bf16* wr = W + (int64_t)nrow * g.ldb + 8 * kq;
     const bf16* ar = As + r * ldl + 8 * kq;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int st = s0; st < s1; ++st) {
-        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(wr + 32 * st);
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(ar + 32 * st);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
-    }
+#pragma unroll
+    for (int i = 0; i < MAXST; ++i)
+        if (s0 + i < s1) {
+            const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(ar + 32 * (s0 + i));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, wv[i], acc, 0, 0, 0);
+        }
     part[w][lane] = acc;
     __syncthreads();
     if (w == 0) {

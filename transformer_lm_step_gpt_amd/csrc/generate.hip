@@ -170,13 +170,15 @@ void cache_put(bool bf, const void* src, int64_t src_ld, void* dst, int B, int n
 
 // ---------------------------------------------------------------- attention of one query against the cache
 
-// One workgroup per (sequence, head): scores of the query against keys
-// j0 .. pos in LDS, softmax in fp32, then out[c] = sum_j p_j v_j[c] with the
-// 256 threads split into 256 / hd groups of keys summed in a fixed order.
+// One workgroup per (sequence, head): the new key and value rows of the
+// head are copied into the caches at position pos (the barrier below makes
+// them visible to the whole workgroup), then the scores of the query against
+// keys j0 .. pos in LDS, softmax in fp32, then out[c] = sum_j p_j v_j[c] with
+// the 256 threads split into 256 / hd groups of keys summed in a fixed order.
 template <typename T>
-__global__ __launch_bounds__(256) void gen_attention_kernel(const T* q, int64_t ldq, const T* kc, const T* vc, T* out,
-                                                            int H, int hd, int pos, int Tmax, int window,
-                                                            float scale) {
+__global__ __launch_bounds__(256) void gen_attention_kernel(const T* q, int64_t ldq, const T* knew, int64_t ldk,
+                                                            const T* vnew, int64_t ldv, T* kc, T* vc, T* out, int H,
+                                                            int hd, int pos, int Tmax, int window, float scale) {
     extern __shared__ float sc[];   // [pos + 1] scores, then weights
     __shared__ float qs[128];
     __shared__ float red[256];
@@ -185,7 +187,12 @@ __global__ __launch_bounds__(256) void gen_attention_kernel(const T* q, int64_t 
     const int d = H * hd;
     const int j0 = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;
     const int n = pos + 1 - j0;
-    if (tid < hd) qs[tid] = to_f32(q[(int64_t)b * ldq + h * hd + tid]);
+    if (tid < hd) {
+        qs[tid] = to_f32(q[(int64_t)b * ldq + h * hd + tid]);
+        const int64_t o = ((int64_t)b * Tmax + pos) * d + h * hd + tid;
+        kc[o] = knew[(int64_t)b * ldk + h * hd + tid];
+        vc[o] = vnew[(int64_t)b * ldv + h * hd + tid];
+    }
     __syncthreads();
     const T* kb = kc + ((int64_t)b * Tmax + j0) * d + h * hd;
     float mx = -FLT_MAX;
@@ -226,8 +233,8 @@ __global__ __launch_bounds__(256) void gen_attention_kernel(const T* q, int64_t 
     }
 }
 
-void gen_attention(bool bf, const void* q, int64_t ldq, const void* kc, const void* vc, void* out, int B, int H,
-                   int hd, int pos, int Tmax, int window, hipStream_t s) {
+void gen_attention(bool bf, const void* q, int64_t ldq, const void* knew, int64_t ldk, const void* vnew, int64_t ldv,
+                   void* kc, void* vc, void* out, int B, int H, int hd, int pos, int Tmax, int window, hipStream_t s) {
     const size_t lds = sizeof(float) * (size_t)(pos + 1);
     const float scale = 1.0f / sqrtf((float)hd);
     static bool attr = false;
@@ -239,10 +246,12 @@ void gen_attention(bool bf, const void* q, int64_t ldq, const void* kc, const vo
         attr = true;
     }
     if (bf)
-        gen_attention_kernel<bf16><<<B * H, 256, lds, s>>>((const bf16*)q, ldq, (const bf16*)kc, (const bf16*)vc,
-                                                           (bf16*)out, H, hd, pos, Tmax, window, scale);
+        gen_attention_kernel<bf16><<<B * H, 256, lds, s>>>((const bf16*)q, ldq, (const bf16*)knew, ldk,
+                                                           (const bf16*)vnew, ldv, (bf16*)kc, (bf16*)vc, (bf16*)out, H,
+                                                           hd, pos, Tmax, window, scale);
     else
-        gen_attention_kernel<float><<<B * H, 256, lds, s>>>((const float*)q, ldq, (const float*)kc, (const float*)vc,
+        gen_attention_kernel<float><<<B * H, 256, lds, s>>>((const float*)q, ldq, (const float*)knew, ldk,
+                                                            (const float*)vnew, ldv, (float*)kc, (float*)vc,
                                                             (float*)out, H, hd, pos, Tmax, window, scale);
 }
 
@@ -260,15 +269,21 @@ void gen_attention(bool bf, const void* q, int64_t ldq, const void* kc, const vo
 // order and scanned across threads; the draw is the first token whose
 // running sum exceeds u * total, u from Philox4x64-10 at counter (step,
 // sequence) with key (seed, sampling stream).
+// Each histogram bin has GS_SUB copies (lane % GS_SUB picks one): the logits
+// of a row share their leading key bytes, so with one counter per bin the
+// first passes would send nearly every increment to the same LDS word. The
+// bin holding the k-th largest key comes from a scan of the bin totals in
+// descending bin order.
 constexpr int GS_THREADS = 1024;
+constexpr int GS_SUB = 32;
 
 __global__ __launch_bounds__(GS_THREADS) void gen_sample_kernel(float* logits, int Vp, float cap, float temperature,
                                                                 int top_k, uint64_t seed, int step, int32_t* seq,
                                                                 int64_t ld_seq, int pos_out, float* logits_out) {
     __shared__ float fsh[GS_THREADS / 64 + 1];
     __shared__ int ish[GS_THREADS / 64 + 1];
-    __shared__ int hist[256];
-    __shared__ uint32_t sel[2];   // selected prefix, count still needed
+    __shared__ int hist[256 * GS_SUB];   // [bin][copy]
+    __shared__ uint32_t sel[2];         // selected prefix, count still needed
     const int b = blockIdx.x, tid = threadIdx.x;
     float* z = logits + (int64_t)b * Vp;
     float mx = -FLT_MAX;
@@ -299,26 +314,33 @@ __global__ __launch_bounds__(GS_THREADS) void gen_sample_kernel(float* logits, i
     if (trunc) {
         // radix select of the k-th largest key, most significant byte first
         if (tid == 0) { sel[0] = 0; sel[1] = (uint32_t)top_k; }
+        const int sub = tid & (GS_SUB - 1);
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass;
             const uint32_t hmask = pass ? (0xFFFFFFFFu << (32 - 8 * pass)) : 0u;
-            if (tid < 256) hist[tid] = 0;
+            for (int i = tid; i < 256 * GS_SUB; i += GS_THREADS) hist[i] = 0;
             __syncthreads();
-            const uint32_t prefix = sel[0];
+            const uint32_t prefix = sel[0], rem = sel[1];
             for (int i = tid; i < Vp; i += GS_THREADS) {
                 const uint32_t k = order_key(z[i]);
-                if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+                if ((k & hmask) == prefix) atomicAdd(&hist[((k >> shift) & 255) * GS_SUB + sub], 1);
             }
             __syncthreads();
-            if (tid == 0) {
-                uint32_t rem = sel[1];
-                int bin = 255;
-                for (; bin > 0; --bin) {
-                    if ((uint32_t)hist[bin] >= rem) break;
-                    rem -= hist[bin];
-                }
-                sel[0] = prefix | ((uint32_t)bin << shift);
-                sel[1] = rem;
+            // thread t < 256 takes bin 255 - t: its total, and by an exclusive
+            // scan the number of keys in higher bins
+            int cnt = 0;
+            if (tid < 256) {
+                const int* hb = hist + (255 - tid) * GS_SUB;
+#pragma unroll 8
+                for (int u = 0; u < GS_SUB; ++u) cnt += hb[(u + tid) & (GS_SUB - 1)];
+            }
+            int all = 0;
+            const int above = block_excl_scan<GS_THREADS, int>(cnt, ish, &all);
+            // the bin where the count of higher keys first reaches rem (bin 0
+            // takes what is left); its scan barriers ordered every read of sel
+            if (tid < 256 && (uint32_t)above < rem && ((uint32_t)(above + cnt) >= rem || tid == 255)) {
+                sel[0] = prefix | ((uint32_t)(255 - tid) << shift);
+                sel[1] = rem - (uint32_t)above;
             }
             __syncthreads();
         }
@@ -411,6 +433,18 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_gemm_kernel(Gemm g) {
 #pragma unroll
     for (int i = 0; i < MAXST; ++i)
         if (s0 + i < s1) wv[i] = *reinterpret_cast<const bf16x8_t*>(wr + 32 * (s0 + i));
+    // the epilogue's own operands (bias, residual) are loaded by the storing
+    // wave now, so their latency overlaps the products
+    constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_ACT || EPI == EPI_BIAS_RESID;
+    float bias_n = 0.f, res[4] = {0.f, 0.f, 0.f, 0.f};
+    if (w == 0 && n0 + r < g.N) {
+        if constexpr (HAS_BIAS) bias_n = g.bias[n0 + r];
+        if constexpr (EPI == EPI_BIAS_RESID) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * kq + i < g.M) res[i] = g.resid[(int64_t)(4 * kq + i) * g.ldc + n0 + r];
+        }
+    }
     if constexpr (LN) {
         // wave w normalises rows w, w + SK_WAVES: the LayerNorm kernel's
         // arithmetic in its order (lane sums over float4 chunks, wave sums,
@@ -475,7 +509,21 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_gemm_kernel(Gemm g) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * kq + i;
-                if (m < g.M) epilogue_store<TC, EPI>(g, m, n, t[i]);
+                if (m >= g.M) continue;
+                // the arithmetic of epilogue_store, with the preloaded operands
+                const int64_t o = (int64_t)m * g.ldc + n;
+                if constexpr (EPI == EPI_BIAS_RESID) {
+                    ((float*)g.C)[o] = res[i] + (t[i] + bias_n);
+                } else if constexpr (EPI == EPI_BIAS) {
+                    ((TC*)g.C)[o] = from_f32<TC>(t[i] + bias_n);
+                } else if constexpr (EPI == EPI_BIAS_ACT) {
+                    float a, da;
+                    act_and_grad_rt(g.act, t[i] + bias_n, a, da);
+                    ((TC*)g.C)[o] = from_f32<TC>(da);
+                    ((TC*)g.C2)[o] = from_f32<TC>(a);
+                } else {
+                    epilogue_store<TC, EPI>(g, m, n, t[i]);
+                }
             }
         }
     }

@@ -975,10 +975,8 @@ gpt_status gpt_generate(gpt_handle* h, const int32_t* prompt, int32_t B, int32_t
                     kn = (const char*)w.dec_qk + ab * d;
                     ldq = 2 * d;
                 }
-                gk::cache_put(bf, kn, ldq, w.kcache[l], B, 1, Tm, pos, d, st);
-                gk::cache_put(bf, (const char*)w.dec_qkv + ab * 2 * d, 3 * d, w.vcache[l], B, 1, Tm, pos, d, st);
-                gk::gen_attention(bf, q, ldq, w.kcache[l], w.vcache[l], w.dec_att, B, H, hd, pos, Tm, window_of(c, l),
-                                  st);
+                gk::gen_attention(bf, q, ldq, kn, ldq, (const char*)w.dec_qkv + ab * 2 * d, 3 * d, w.kcache[l],
+                                  w.vcache[l], w.dec_att, B, H, hd, pos, Tm, window_of(c, l), st);
                 {
                     gk::Gemm g = mk_gemm(h, B, d, d, w.dec_att, d, true, Wop(h, li.proj_w), d, true, w.dec_x2, d, false,
                                          gk::EPI_BIAS_RESID);

@@ -120,9 +120,11 @@ void gen_embed(const int32_t* seq, int64_t ld, int pos, const float* wte, const 
 void cache_put(bool bf, const void* src, int64_t src_ld, void* dst, int B, int nt, int Tmax, int t0, int d,
                hipStream_t s);
 // out [B, d] (act): per (b, head) softmax(q k^T / sqrt(hd)) v over cached keys
-// j0 .. pos (j0 = pos - window + 1 with a window, else 0); caches [B, Tmax, d]
-void gen_attention(bool bf, const void* q, int64_t ldq, const void* kc, const void* vc, void* out, int B, int H,
-                   int hd, int pos, int Tmax, int window, hipStream_t s);
+// j0 .. pos (j0 = pos - window + 1 with a window, else 0); caches [B, Tmax, d].
+// The key and value of position pos (rows b of knew and vnew, strides ldk and
+// ldv) are first written into the caches by the same workgroups.
+void gen_attention(bool bf, const void* q, int64_t ldq, const void* knew, int64_t ldk, const void* vnew, int64_t ldv,
+                   void* kc, void* vc, void* out, int B, int H, int hd, int pos, int Tmax, int window, hipStream_t s);
 // One draw per row of fp32 logits [B, Vp] (softcapped in place when cap > 0,
 // copied to logits_out when non-null) into seq[b * ld_seq + pos_out].
 void gen_sample(float* logits, int B, int Vp, float cap, float temperature, int top_k, uint64_t seed, int step,

@@ -147,6 +147,20 @@ gpt_status gptk_embed_bwd(const int32_t* tok, const float* dx, float* dwte, floa
                           int32_t d, int32_t Vp, void* scratch, void* stream);
 int64_t gptk_embed_bwd_scratch_bytes(int32_t M, int32_t d);
 
+/* One draw per row of fp32 logits [B, Vp] into tokens[b], by the sampler of
+ * gpt_generate (the logit softcap applied in place first when cap > 0):
+ * temperature 0 takes the first index of the largest logit; otherwise the
+ * weights exp((z - max) / temperature), restricted for 0 < top_k < Vp to the
+ * top_k largest logits (lower indices first among equal values), and the
+ * token is the first in token order whose running weight exceeds u times
+ * their sum, u = ((x >> 11) + 0.5) 2^-53 for the first output word x of
+ * Philox4x64-10 at counter (step, b, 0, 0) with key (seed, sampling stream);
+ * "Un GPT desde cero + nanoGPT" 2.1, generate, and the lecture's "Генерация
+ * и устройство", top-k 50. Device pointers; logits is modified when
+ * cap > 0. Invalid sizes return GPT_ERR_INVALID_ARGUMENT. */
+gpt_status gptk_sample(float* logits, int32_t B, int32_t Vp, float cap, float temperature, int32_t top_k, uint64_t seed,
+                       int32_t step, int32_t* tokens, void* stream);
+
 /* out[n] += sum_m Y[m*ld + n] (bias gradients); partial holds
  * gptk_colsum_partial_floats(M, N) floats. */
 gpt_status gptk_colsum(int32_t M, int32_t N, const void* Y, int64_t ld, int32_t bf16, float* out, float* partial,

@@ -167,3 +167,62 @@ def test_generate_errors_and_determinism():
     assert np.array_equal(a, b) and a.shape == (1, 13)
     assert not np.array_equal(a, c)
     assert np.array_equal(gpu.generate(prompt, 0, 1.0, 5, 9), prompt)
+
+
+def test_sampler_rows_against_oracle():
+    """The sampler alone (gptk_sample) on engineered rows against O.sample_next:
+    logits on a coarse grid, so that many tokens tie at the k-th value and the
+    lowest ids must be the ones kept; rows of equal logits; top_k 1, 50, 1024
+    and 2000 (past the gathered top-k path), the whole distribution (top_k 0),
+    greedy draws with tied maxima (first index), softcapped rows, and a small
+    vocabulary (the whole-distribution case uses 777 tokens, so that the
+    boundaries of its cumulative distribution lie further apart than the
+    rounding of an fp32 running sum). Tokens must equal the oracle's wherever the uniform lies more
+    than 1e-5 from a boundary of the cumulative distribution (at least 75% of
+    the draws of each case); greedy draws always."""
+    from transformer_lm_step_gpt_amd.gpt import load_library
+    lib = load_library()
+    s = torch.cuda.current_stream().cuda_stream
+    rng = np.random.default_rng(11)
+    V = 50304
+    grid = (np.round(rng.normal(0.0, 1.0, (8, V)) * 4) / 4).astype(np.float32)
+    cases = [
+        ("normal k50", rng.normal(0.0, 2.0, (8, V)).astype(np.float32), 0.0, 1.0, 50),
+        ("grid k50", grid, 0.0, 1.0, 50),
+        ("grid k1", grid, 0.0, 1.0, 1),
+        ("grid k1024 T0.8", grid, 0.0, 0.8, 1024),
+        ("grid k2000 T0.8", grid, 0.0, 0.8, 2000),
+        ("grid whole distribution", grid[:4, :777], 0.0, 1.0, 0),
+        ("equal rows k50", np.zeros((4, 3000), np.float32), 0.0, 1.0, 50),
+        ("softcap 30 k50", rng.normal(0.0, 40.0, (4, 4096)).astype(np.float32), 30.0, 1.0, 50),
+        ("small vocab k7", (np.round(rng.normal(0.0, 1.0, (5, 61)) * 2) / 2).astype(np.float32), 0.0, 1.3, 7),
+        ("greedy ties", grid[:4], 0.0, 0.0, 50),
+    ]
+    for name, rows, cap, temperature, top_k in cases:
+        B, Vp = rows.shape
+        compared = total = 0
+        for step in range(4):
+            seed = 977 + 31 * step
+            d = torch.tensor(rows, device="cuda")
+            tok = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+            say(f"sampler {name}: B={B} Vp={Vp} step {step}")
+            assert lib.gptk_sample(d.data_ptr(), B, Vp, cap, temperature, top_k, seed, step, tok.data_ptr(), s) == 0
+            torch.cuda.synchronize()
+            zc = d.cpu().numpy().astype(np.float64)
+            if cap:
+                ref = O.softcap(rows.astype(np.float64), cap)
+                assert np.abs(zc - ref).max() <= 2e-6 * cap
+            got = tok.cpu().numpy()
+            for b in range(B):
+                total += 1
+                if temperature == 0:
+                    assert got[b] == int(np.argmax(zc[b])), (name, step, b)
+                    compared += 1
+                    continue
+                u = O.sample_uniform(seed, step, b)
+                if draw_margin(zc[b], temperature, top_k, u) <= 1e-5:
+                    continue
+                assert got[b] == O.sample_next(zc[b], temperature, top_k, u), (name, step, b, got[b])
+                compared += 1
+        say(f"  {compared} of {total} draws compared")
+        assert compared >= 0.75 * total, (name, compared, total)

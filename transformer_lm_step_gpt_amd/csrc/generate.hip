@@ -391,10 +391,148 @@ __global__ __launch_bounds__(GS_THREADS) void gen_sample_kernel(float* logits, i
     }
 }
 
+// Top-k draw (temperature > 0, 0 < top_k <= GS_MAXK, top_k < Vp); the same
+// draw as gen_sample_kernel with every pass over the row coalesced: thread t
+// visits tokens t, t + 1024, ... The k-th largest key by the same radix
+// select; the kept set (every larger key and the lowest-index ties, ranked
+// with ballots over the strided layout) is gathered in LDS, put in token
+// order by counting smaller indices, and one thread sums its weights
+// exp((z - max) / T) in token order and walks them to the first running sum
+// above u * total.
+constexpr int GS_MAXK = 1024;
+constexpr int GS_MAXROUND = 64;   // rounds of 1024 tokens: Vp <= 65536
+
+__global__ __launch_bounds__(GS_THREADS) void gen_sample_topk_kernel(float* logits, int Vp, float cap,
+                                                                     float temperature, int top_k, uint64_t seed,
+                                                                     int step, int32_t* seq, int64_t ld_seq,
+                                                                     int pos_out, float* logits_out) {
+    __shared__ float fsh[GS_THREADS / 64 + 1];
+    __shared__ int ish[GS_THREADS / 64 + 1];
+    __shared__ int hist[256 * GS_SUB];   // [bin][copy]; later the tie counts and the sorted kept set
+    __shared__ uint32_t sel[2];
+    __shared__ int kcount;
+    __shared__ int kidx[GS_MAXK];
+    __shared__ float kval[GS_MAXK];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    float* z = logits + (int64_t)b * Vp;
+    float mx = -FLT_MAX;
+    for (int i = tid; i < Vp; i += GS_THREADS) {
+        float v = z[i];
+        if (cap > 0.f) {
+            v = cap * tanhf(v / cap);
+            z[i] = v;
+        }
+        if (logits_out) logits_out[(int64_t)b * Vp + i] = v;
+        mx = fmaxf(mx, v);
+    }
+    mx = block_max_f<GS_THREADS>(mx, fsh);   // its barriers order the softcap writes before the reads below
+    // radix select of the k-th largest key, most significant byte first
+    if (tid == 0) { sel[0] = 0; sel[1] = (uint32_t)top_k; kcount = 0; }
+    const int sub = tid & (GS_SUB - 1);
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        const uint32_t hmask = pass ? (0xFFFFFFFFu << (32 - 8 * pass)) : 0u;
+        for (int i = tid; i < 256 * GS_SUB; i += GS_THREADS) hist[i] = 0;
+        __syncthreads();
+        const uint32_t prefix = sel[0], rem = sel[1];
+#pragma unroll 4
+        for (int i = tid; i < Vp; i += GS_THREADS) {
+            const uint32_t k = order_key(z[i]);
+            if ((k & hmask) == prefix) atomicAdd(&hist[((k >> shift) & 255) * GS_SUB + sub], 1);
+        }
+        __syncthreads();
+        int cnt = 0;
+        if (tid < 256) {
+            const int* hb = hist + (255 - tid) * GS_SUB;
+#pragma unroll 8
+            for (int u = 0; u < GS_SUB; ++u) cnt += hb[(u + tid) & (GS_SUB - 1)];
+        }
+        int all = 0;
+        const int above = block_excl_scan<GS_THREADS, int>(cnt, ish, &all);
+        if (tid < 256 && (uint32_t)above < rem && ((uint32_t)(above + cnt) >= rem || tid == 255)) {
+            sel[0] = prefix | ((uint32_t)(255 - tid) << shift);
+            sel[1] = rem - (uint32_t)above;
+        }
+        __syncthreads();
+    }
+    const uint32_t thr = sel[0];
+    // ties ranked in token order: per round u (tokens u * 1024 .. + 1023) a
+    // ballot per wave; an exclusive scan of the (round, wave) counts gives the
+    // ties before each wave's slice
+    constexpr int NW = GS_THREADS / 64;
+    int* tcnt = hist;   // [GS_MAXROUND][NW]
+    const int rounds = ceil_div(Vp, GS_THREADS);
+    int gt = 0;
+    for (int u = 0; u < rounds; ++u) {
+        const int i = u * GS_THREADS + tid;
+        const uint32_t k = i < Vp ? order_key(z[i]) : 0u;
+        gt += i < Vp && k > thr;
+        const uint64_t tm = __ballot(i < Vp && k == thr);
+        if (lane == 0) tcnt[u * NW + w] = __popcll(tm);
+    }
+    const int need = top_k - block_sum_i<GS_THREADS>(gt, ish);   // its barriers publish tcnt
+    {
+        const int n = rounds * NW;   // <= GS_THREADS
+        const int v = tid < n ? tcnt[tid] : 0;
+        int tot = 0;
+        const int ex = block_excl_scan<GS_THREADS, int>(v, ish, &tot);   // its barriers order the read above
+        if (tid < n) tcnt[tid] = ex;
+    }
+    __syncthreads();
+    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+    for (int u = 0; u < rounds; ++u) {
+        const int i = u * GS_THREADS + tid;
+        const float v = i < Vp ? z[i] : 0.f;
+        const uint32_t k = order_key(v);
+        const bool tie = i < Vp && k == thr;
+        const uint64_t tm = __ballot(tie);
+        const bool keep = i < Vp && (k > thr || (tie && tcnt[u * NW + w] + __popcll(tm & lt) < need));
+        if (keep) {
+            const int slot = atomicAdd(&kcount, 1);   // exactly top_k slots are taken
+            if (slot < GS_MAXK) {
+                kidx[slot] = i;
+                kval[slot] = v;
+            }
+        }
+    }
+    __syncthreads();
+    // exactly top_k kept: each finds its place in token order
+    int* sidx = hist;
+    float* sw = reinterpret_cast<float*>(hist + GS_MAXK);
+    const float inv_t = 1.0f / temperature;
+    if (tid < top_k) {
+        const int mine = kidx[tid];
+        int rank = 0;
+        for (int m = 0; m < top_k; ++m) rank += kidx[m] < mine;
+        sidx[rank] = mine;
+        sw[rank] = __expf((kval[tid] - mx) * inv_t);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float total = 0.f;
+        for (int j = 0; j < top_k; ++j) total += sw[j];
+        uint64_t c4[4] = {(uint64_t)step, (uint64_t)b, 0, 0};
+        gen_philox(c4, seed, SAMPLE_STREAM);
+        const double uu = ((double)(c4[0] >> 11) + 0.5) * 0x1.0p-53;
+        const float target = (float)(uu * (double)total);
+        int tok = sidx[top_k - 1];
+        float run = 0.f;
+        for (int j = 0; j < top_k; ++j) {
+            run += sw[j];
+            if (run > target) { tok = sidx[j]; break; }
+        }
+        seq[(int64_t)b * ld_seq + pos_out] = tok;
+    }
+}
+
 void gen_sample(float* logits, int B, int Vp, float cap, float temperature, int top_k, uint64_t seed, int step,
                 int32_t* seq, int64_t ld_seq, int pos_out, float* logits_out, hipStream_t s) {
-    gen_sample_kernel<<<B, GS_THREADS, 0, s>>>(logits, Vp, cap, temperature, top_k, seed, step, seq, ld_seq, pos_out,
-                                                logits_out);
+    if (temperature > 0.f && top_k > 0 && top_k <= GS_MAXK && top_k < Vp && Vp <= GS_THREADS * GS_MAXROUND)
+        gen_sample_topk_kernel<<<B, GS_THREADS, 0, s>>>(logits, Vp, cap, temperature, top_k, seed, step, seq, ld_seq,
+                                                         pos_out, logits_out);
+    else
+        gen_sample_kernel<<<B, GS_THREADS, 0, s>>>(logits, Vp, cap, temperature, top_k, seed, step, seq, ld_seq,
+                                                    pos_out, logits_out);
 }
 
 // ---------------------------------------------------------------- products at decode shapes

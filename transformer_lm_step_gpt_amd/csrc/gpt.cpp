@@ -1512,4 +1512,12 @@ gpt_status gptk_colsum(int32_t M, int32_t N, const void* Y, int64_t ld, int32_t 
 
 int64_t gptk_colsum_partial_floats(int32_t M, int32_t N) { return (int64_t)gk::colsum_partial_floats(M, N); }
 
+gpt_status gptk_sample(float* logits, int32_t B, int32_t Vp, float cap, float temperature, int32_t top_k, uint64_t seed,
+                       int32_t step, int32_t* tokens, void* stream) {
+    if (B < 1 || Vp < 1 || !logits || !tokens || !(temperature >= 0.f) || !(cap >= 0.f))
+        return GPT_ERR_INVALID_ARGUMENT;
+    gk::gen_sample(logits, B, Vp, cap, temperature, top_k, seed, step, tokens, 1, 0, nullptr, (hipStream_t)stream);
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
+
 }  // extern "C"

@@ -135,6 +135,8 @@ _SIGS = [
     ("gptk_muon_scratch_bytes", c_int64, [c_int32, c_int32, c_int32]),
     ("gptk_colsum", c_int32, [c_int32, c_int32, c_void_p, c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
     ("gptk_colsum_partial_floats", c_int64, [c_int32, c_int32]),
+    ("gptk_sample", c_int32, [c_void_p, c_int32, c_int32, c_float, c_float, c_int32, c_uint64, c_int32, c_void_p,
+                              c_void_p]),
 ]
 
 EXPORTED = [s[0] for s in _SIGS]

@@ -392,15 +392,19 @@ __global__ __launch_bounds__(GS_THREADS) void gen_sample_kernel(float* logits, i
 }
 
 // Top-k draw (temperature > 0, 0 < top_k <= GS_MAXK, top_k < Vp); the same
-// draw as gen_sample_kernel with every pass over the row coalesced: thread t
-// visits tokens t, t + 1024, ... The k-th largest key by the same radix
-// select; the kept set (every larger key and the lowest-index ties, ranked
-// with ballots over the strided layout) is gathered in LDS, put in token
-// order by counting smaller indices, and one thread sums its weights
-// exp((z - max) / T) in token order and walks them to the first running sum
-// above u * total.
+// draw as gen_sample_kernel with every pass over the row coalesced (thread t
+// visits tokens t, t + 1024, ..., eight loads in flight) and five passes in
+// all: the softcap, the maximum and the first radix histogram share one; the
+// k-th largest key thr comes from the same radix select, whose last pass
+// also gives the count of keys equal to thr and how many of them are kept
+// (rem). The kept set (every larger key and the rem lowest-index ties, which
+// are ranked with ballots over the strided layout in an extra pass only when
+// some ties are dropped) is gathered in LDS, put in token order by counting
+// smaller indices, and one thread sums its weights exp((z - max) / T) in
+// token order and walks them to the first running sum above u * total.
 constexpr int GS_MAXK = 1024;
 constexpr int GS_MAXROUND = 64;   // rounds of 1024 tokens: Vp <= 65536
+constexpr int GS_BATCH = 8;       // loads in flight per thread and sweep step
 
 __global__ __launch_bounds__(GS_THREADS) void gen_sample_topk_kernel(float* logits, int Vp, float cap,
                                                                      float temperature, int top_k, uint64_t seed,
@@ -409,38 +413,54 @@ __global__ __launch_bounds__(GS_THREADS) void gen_sample_topk_kernel(float* logi
     __shared__ float fsh[GS_THREADS / 64 + 1];
     __shared__ int ish[GS_THREADS / 64 + 1];
     __shared__ int hist[256 * GS_SUB];   // [bin][copy]; later the tie counts and the sorted kept set
-    __shared__ uint32_t sel[2];
+    __shared__ uint32_t sel[3];          // selected prefix, keys still needed from it, keys equal to it
     __shared__ int kcount;
     __shared__ int kidx[GS_MAXK];
     __shared__ float kval[GS_MAXK];
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     float* z = logits + (int64_t)b * Vp;
+    // f(i, z[i]) for every token of this thread, GS_BATCH loads issued together
+    auto sweep = [&](auto&& f) {
+        for (int base = tid; base < Vp; base += GS_BATCH * GS_THREADS) {
+            float v[GS_BATCH];
+#pragma unroll
+            for (int j = 0; j < GS_BATCH; ++j) v[j] = z[min(base + j * GS_THREADS, Vp - 1)];
+#pragma unroll
+            for (int j = 0; j < GS_BATCH; ++j)
+                if (base + j * GS_THREADS < Vp) f(base + j * GS_THREADS, v[j]);
+        }
+    };
+    const int sub = tid & (GS_SUB - 1);
+    for (int i = tid; i < 256 * GS_SUB; i += GS_THREADS) hist[i] = 0;
+    if (tid == 0) { sel[0] = 0; sel[1] = (uint32_t)top_k; sel[2] = 0; kcount = 0; }
+    __syncthreads();
+    // pass 0: softcap in place (and the copy out), the maximum, the histogram of the leading key byte
     float mx = -FLT_MAX;
-    for (int i = tid; i < Vp; i += GS_THREADS) {
-        float v = z[i];
+    sweep([&](int i, float v) {
         if (cap > 0.f) {
             v = cap * tanhf(v / cap);
             z[i] = v;
         }
         if (logits_out) logits_out[(int64_t)b * Vp + i] = v;
         mx = fmaxf(mx, v);
-    }
-    mx = block_max_f<GS_THREADS>(mx, fsh);   // its barriers order the softcap writes before the reads below
-    // radix select of the k-th largest key, most significant byte first
-    if (tid == 0) { sel[0] = 0; sel[1] = (uint32_t)top_k; kcount = 0; }
-    const int sub = tid & (GS_SUB - 1);
+        atomicAdd(&hist[(order_key(v) >> 24) * GS_SUB + sub], 1);
+    });
+    mx = block_max_f<GS_THREADS>(mx, fsh);   // its barriers order the softcap writes and the histogram
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        const uint32_t hmask = pass ? (0xFFFFFFFFu << (32 - 8 * pass)) : 0u;
-        for (int i = tid; i < 256 * GS_SUB; i += GS_THREADS) hist[i] = 0;
-        __syncthreads();
         const uint32_t prefix = sel[0], rem = sel[1];
-#pragma unroll 4
-        for (int i = tid; i < Vp; i += GS_THREADS) {
-            const uint32_t k = order_key(z[i]);
-            if ((k & hmask) == prefix) atomicAdd(&hist[((k >> shift) & 255) * GS_SUB + sub], 1);
+        if (pass > 0) {
+            const uint32_t hmask = 0xFFFFFFFFu << (32 - 8 * pass);
+            for (int i = tid; i < 256 * GS_SUB; i += GS_THREADS) hist[i] = 0;
+            __syncthreads();
+            sweep([&](int, float v) {
+                const uint32_t k = order_key(v);
+                if ((k & hmask) == prefix) atomicAdd(&hist[((k >> shift) & 255) * GS_SUB + sub], 1);
+            });
+            __syncthreads();
         }
-        __syncthreads();
+        // thread t < 256 takes bin 255 - t: its total, and by an exclusive
+        // scan the number of keys in higher bins
         int cnt = 0;
         if (tid < 256) {
             const int* hb = hist + (255 - tid) * GS_SUB;
@@ -449,50 +469,57 @@ __global__ __launch_bounds__(GS_THREADS) void gen_sample_topk_kernel(float* logi
         }
         int all = 0;
         const int above = block_excl_scan<GS_THREADS, int>(cnt, ish, &all);
+        // the bin where the count of higher keys first reaches rem (bin 0 takes
+        // what is left); the scan's barriers ordered every read of sel
         if (tid < 256 && (uint32_t)above < rem && ((uint32_t)(above + cnt) >= rem || tid == 255)) {
             sel[0] = prefix | ((uint32_t)(255 - tid) << shift);
             sel[1] = rem - (uint32_t)above;
+            sel[2] = (uint32_t)cnt;
         }
         __syncthreads();
     }
     const uint32_t thr = sel[0];
-    // ties ranked in token order: per round u (tokens u * 1024 .. + 1023) a
-    // ballot per wave; an exclusive scan of the (round, wave) counts gives the
-    // ties before each wave's slice
-    constexpr int NW = GS_THREADS / 64;
-    int* tcnt = hist;   // [GS_MAXROUND][NW]
-    const int rounds = ceil_div(Vp, GS_THREADS);
-    int gt = 0;
-    for (int u = 0; u < rounds; ++u) {
-        const int i = u * GS_THREADS + tid;
-        const uint32_t k = i < Vp ? order_key(z[i]) : 0u;
-        gt += i < Vp && k > thr;
-        const uint64_t tm = __ballot(i < Vp && k == thr);
-        if (lane == 0) tcnt[u * NW + w] = __popcll(tm);
-    }
-    const int need = top_k - block_sum_i<GS_THREADS>(gt, ish);   // its barriers publish tcnt
-    {
-        const int n = rounds * NW;   // <= GS_THREADS
-        const int v = tid < n ? tcnt[tid] : 0;
-        int tot = 0;
-        const int ex = block_excl_scan<GS_THREADS, int>(v, ish, &tot);   // its barriers order the read above
-        if (tid < n) tcnt[tid] = ex;
-    }
-    __syncthreads();
-    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-    for (int u = 0; u < rounds; ++u) {
-        const int i = u * GS_THREADS + tid;
-        const float v = i < Vp ? z[i] : 0.f;
-        const uint32_t k = order_key(v);
-        const bool tie = i < Vp && k == thr;
-        const uint64_t tm = __ballot(tie);
-        const bool keep = i < Vp && (k > thr || (tie && tcnt[u * NW + w] + __popcll(tm & lt) < need));
-        if (keep) {
-            const int slot = atomicAdd(&kcount, 1);   // exactly top_k slots are taken
-            if (slot < GS_MAXK) {
-                kidx[slot] = i;
-                kval[slot] = v;
-            }
+    const int need = (int)sel[1], ties = (int)sel[2];   // keys equal to thr: kept, and in all
+    auto gather = [&](int i, float v) {
+        const int slot = atomicAdd(&kcount, 1);   // exactly top_k slots are taken
+        if (slot < GS_MAXK) {
+            kidx[slot] = i;
+            kval[slot] = v;
+        }
+    };
+    if (ties == need) {
+        sweep([&](int i, float v) {
+            if (order_key(v) >= thr) gather(i, v);
+        });
+    } else {
+        // ties ranked in token order: per round u (tokens u * 1024 .. + 1023) a
+        // ballot per wave; an exclusive scan of the (round, wave) counts gives
+        // the ties before each wave's slice
+        constexpr int NW = GS_THREADS / 64;
+        int* tcnt = hist;   // [GS_MAXROUND][NW]
+        const int rounds = ceil_div(Vp, GS_THREADS);
+        for (int u = 0; u < rounds; ++u) {
+            const int i = u * GS_THREADS + tid;
+            const uint64_t tm = __ballot(i < Vp && order_key(z[min(i, Vp - 1)]) == thr);
+            if (lane == 0) tcnt[u * NW + w] = __popcll(tm);
+        }
+        __syncthreads();
+        {
+            const int n = rounds * NW;   // <= GS_THREADS
+            const int v = tid < n ? tcnt[tid] : 0;
+            int tot = 0;
+            const int ex = block_excl_scan<GS_THREADS, int>(v, ish, &tot);   // its barriers order the read above
+            if (tid < n) tcnt[tid] = ex;
+        }
+        __syncthreads();
+        const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+        for (int u = 0; u < rounds; ++u) {
+            const int i = u * GS_THREADS + tid;
+            const float v = z[min(i, Vp - 1)];
+            const uint32_t k = order_key(v);
+            const bool tie = i < Vp && k == thr;
+            const uint64_t tm = __ballot(tie);
+            if (i < Vp && (k > thr || (tie && tcnt[u * NW + w] + __popcll(tm & lt) < need))) gather(i, v);
         }
     }
     __syncthreads();

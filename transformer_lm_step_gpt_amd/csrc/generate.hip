@@ -577,6 +577,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int SK_WAVES = 8;
+constexpr int SK_LNV = 3;      // float4 per lane of a normalised row kept in registers: K <= 768
+constexpr int SK_ABATCH = 6;   // 16-byte activation pieces loaded together per thread
 
 template <int EPI, typename TC, bool LN>
 __global__ __launch_bounds__(64 * SK_WAVES) void skinny_gemm_kernel(Gemm g) {
@@ -614,43 +616,109 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_gemm_kernel(Gemm g) {
         // wave w normalises rows w, w + SK_WAVES: the LayerNorm kernel's
         // arithmetic in its order (lane sums over float4 chunks, wave sums,
         // biased variance, rsqrt), stored as bf16
-        for (int r = w; r < 16; r += SK_WAVES) {
-            bf16* dst = As + r * ldl;
-            if (r < g.M) {
-                const float* xr = (const float*)g.A + (int64_t)r * g.lda;
-                float sum = 0.f;
-                for (int c = 4 * lane; c < K; c += 256) {
-                    const float4 v = load4(xr + c);
-                    sum += (v.x + v.y) + (v.z + v.w);
+        const int r0 = w, r1 = w + SK_WAVES;
+        if (K <= 256 * SK_LNV) {
+            // the rows, gains and biases loaded once, together
+            float4 xv[2][SK_LNV], gv[SK_LNV], bv[SK_LNV];
+            const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int j = 0; j < SK_LNV; ++j) {
+                const int c = 4 * lane + 256 * j;
+                gv[j] = c < K ? load4(g.ln_g + c) : z4;
+                bv[j] = c < K ? load4(g.ln_b + c) : z4;
+                xv[0][j] = c < K && r0 < g.M ? load4((const float*)g.A + (int64_t)r0 * g.lda + c) : z4;
+                xv[1][j] = c < K && r1 < g.M ? load4((const float*)g.A + (int64_t)r1 * g.lda + c) : z4;
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int rr = q ? r1 : r0;
+                bf16* dst = As + rr * ldl;
+                if (rr < g.M) {
+                    float sum = 0.f;
+#pragma unroll
+                    for (int j = 0; j < SK_LNV; ++j)
+                        if (4 * lane + 256 * j < K) sum += (xv[q][j].x + xv[q][j].y) + (xv[q][j].z + xv[q][j].w);
+                    const float mu = wave_sum(sum) / K;
+                    float s2 = 0.f;
+#pragma unroll
+                    for (int j = 0; j < SK_LNV; ++j)
+                        if (4 * lane + 256 * j < K) {
+                            const float4 v = xv[q][j];
+                            const float a = v.x - mu, b = v.y - mu, cc = v.z - mu, dd = v.w - mu;
+                            s2 += (a * a + b * b) + (cc * cc + dd * dd);
+                        }
+                    const float rs = 1.0f / sqrtf(wave_sum(s2) / K + g.ln_eps);
+#pragma unroll
+                    for (int j = 0; j < SK_LNV; ++j) {
+                        const int c = 4 * lane + 256 * j;
+                        if (c < K) {
+                            const float4 v = xv[q][j], gg = gv[j], bb = bv[j];
+                            float4 o;
+                            o.x = (v.x - mu) * rs * gg.x + bb.x;
+                            o.y = (v.y - mu) * rs * gg.y + bb.y;
+                            o.z = (v.z - mu) * rs * gg.z + bb.z;
+                            o.w = (v.w - mu) * rs * gg.w + bb.w;
+                            store4(dst + c, o);
+                        }
+                    }
+                } else {
+                    for (int c = 4 * lane; c < K; c += 256) store4(dst + c, z4);
                 }
-                const float mu = wave_sum(sum) / K;
-                float s2 = 0.f;
-                for (int c = 4 * lane; c < K; c += 256) {
-                    const float4 v = load4(xr + c);
-                    const float a = v.x - mu, b = v.y - mu, cc = v.z - mu, dd = v.w - mu;
-                    s2 += (a * a + b * b) + (cc * cc + dd * dd);
+            }
+        } else {
+            for (int r = w; r < 16; r += SK_WAVES) {
+                bf16* dst = As + r * ldl;
+                if (r < g.M) {
+                    const float* xr = (const float*)g.A + (int64_t)r * g.lda;
+                    float sum = 0.f;
+                    for (int c = 4 * lane; c < K; c += 256) {
+                        const float4 v = load4(xr + c);
+                        sum += (v.x + v.y) + (v.z + v.w);
+                    }
+                    const float mu = wave_sum(sum) / K;
+                    float s2 = 0.f;
+                    for (int c = 4 * lane; c < K; c += 256) {
+                        const float4 v = load4(xr + c);
+                        const float a = v.x - mu, b = v.y - mu, cc = v.z - mu, dd = v.w - mu;
+                        s2 += (a * a + b * b) + (cc * cc + dd * dd);
+                    }
+                    const float rs = 1.0f / sqrtf(wave_sum(s2) / K + g.ln_eps);
+                    for (int c = 4 * lane; c < K; c += 256) {
+                        const float4 v = load4(xr + c), gg = load4(g.ln_g + c), bb = load4(g.ln_b + c);
+                        float4 o;
+                        o.x = (v.x - mu) * rs * gg.x + bb.x;
+                        o.y = (v.y - mu) * rs * gg.y + bb.y;
+                        o.z = (v.z - mu) * rs * gg.z + bb.z;
+                        o.w = (v.w - mu) * rs * gg.w + bb.w;
+                        store4(dst + c, o);
+                    }
+                } else {
+                    for (int c = 4 * lane; c < K; c += 256) store4(dst + c, make_float4(0.f, 0.f, 0.f, 0.f));
                 }
-                const float rs = 1.0f / sqrtf(wave_sum(s2) / K + g.ln_eps);
-                for (int c = 4 * lane; c < K; c += 256) {
-                    const float4 v = load4(xr + c), gg = load4(g.ln_g + c), bb = load4(g.ln_b + c);
-                    float4 o;
-                    o.x = (v.x - mu) * rs * gg.x + bb.x;
-                    o.y = (v.y - mu) * rs * gg.y + bb.y;
-                    o.z = (v.z - mu) * rs * gg.z + bb.z;
-                    o.w = (v.w - mu) * rs * gg.w + bb.w;
-                    store4(dst + c, o);
-                }
-            } else {
-                for (int c = 4 * lane; c < K; c += 256) store4(dst + c, make_float4(0.f, 0.f, 0.f, 0.f));
             }
         }
     } else {
+        // the 16-byte pieces of the 16 rows in batches of SK_ABATCH per
+        // thread, each batch loaded before its first piece is stored (one
+        // batch covers K <= 1536)
         const bf16* A = (const bf16*)g.A;
-        for (int i = threadIdx.x; i < 16 * (K / 8); i += 64 * SK_WAVES) {
-            const int r = i / (K / 8), c = (i % (K / 8)) * 8;
-            bf16x8_t v = {};
-            if (r < g.M) v = *reinterpret_cast<const bf16x8_t*>(A + (int64_t)r * g.lda + c);
-            *reinterpret_cast<bf16x8_t*>(As + r * ldl + c) = v;
+        const int nch = 16 * (K / 8);
+        for (int i0 = threadIdx.x; i0 < nch; i0 += SK_ABATCH * 64 * SK_WAVES) {
+            bf16x8_t av[SK_ABATCH];
+#pragma unroll
+            for (int u = 0; u < SK_ABATCH; ++u) {
+                const int i = i0 + u * 64 * SK_WAVES;
+                const int r = i / (K / 8), c = (i % (K / 8)) * 8;
+                bf16x8_t v = {};
+                if (i < nch && r < g.M) v = *reinterpret_cast<const bf16x8_t*>(A + (int64_t)r * g.lda + c);
+                av[u] = v;
+            }
+#pragma unroll
+            for (int u = 0; u < SK_ABATCH; ++u) {
+                const int i = i0 + u * 64 * SK_WAVES;
+                const int r = i / (K / 8), c = (i % (K / 8)) * 8;
+                if (i < nch) *reinterpret_cast<bf16x8_t*>(As + r * ldl + c) = av[u];
+            }
         }
     }
     __syncthreads();

@@ -172,17 +172,22 @@ void cache_put(bool bf, const void* src, int64_t src_ld, void* dst, int B, int n
 
 // One workgroup per (sequence, head): the new key and value rows of the
 // head are copied into the caches at position pos (the barrier below makes
-// them visible to the whole workgroup), then the scores of the query against
-// keys j0 .. pos in LDS, softmax in fp32, then out[c] = sum_j p_j v_j[c] with
-// the 256 threads split into 256 / hd groups of keys summed in a fixed order.
+// them visible to the whole workgroup); the scores of the query against keys
+// j0 .. pos in LDS (one key per thread and pass), softmax in fp32; then
+// out[c] = sum_j p_j v_j[c] with thread (g, ch) accumulating the 16-byte
+// chunk ch of the value rows j = g, g + KG, ... (the first GA_VPRE of them
+// loaded before the softmax, beside the keys), and the KG partial rows
+// summed in a fixed order.
+constexpr int GA_VPRE = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void gen_attention_kernel(const T* q, int64_t ldq, const T* knew, int64_t ldk,
                                                             const T* vnew, int64_t ldv, T* kc, T* vc, T* out, int H,
                                                             int hd, int pos, int Tmax, int window, float scale) {
-    extern __shared__ float sc[];   // [pos + 1] scores, then weights
+    extern __shared__ float sc[];   // [pos + 1] scores, then weights; then the partial output rows
     __shared__ float qs[128];
-    __shared__ float red[256];
     __shared__ float rsh[16];
+    constexpr int E = 16 / sizeof(T);   // elements per 16-byte chunk
     const int b = blockIdx.x / H, h = blockIdx.x % H, tid = threadIdx.x;
     const int d = H * hd;
     const int j0 = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;
@@ -194,13 +199,20 @@ __global__ __launch_bounds__(256) void gen_attention_kernel(const T* q, int64_t 
         vc[o] = vnew[(int64_t)b * ldv + h * hd + tid];
     }
     __syncthreads();
+    const int CH = hd / E, KG = 256 / CH, ch = tid % CH, g = tid / CH;
+    const T* vb = vc + ((int64_t)b * Tmax + j0) * d + h * hd + ch * E;
+    uint4 vpre[GA_VPRE];
+#pragma unroll
+    for (int u = 0; u < GA_VPRE; ++u) {
+        const int j = g + u * KG;
+        vpre[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)min(j, n - 1) * d);
+    }
     const T* kb = kc + ((int64_t)b * Tmax + j0) * d + h * hd;
     float mx = -FLT_MAX;
     for (int j = tid; j < n; j += 256) {
         const T* kr = kb + (int64_t)j * d;
         float acc = 0.f;
         // 16-byte loads of the key row (hd and d are multiples of 8 elements)
-        constexpr int E = 16 / sizeof(T);
         for (int c = 0; c < hd; c += E) {
             const uint4 raw = *reinterpret_cast<const uint4*>(kr + c);
             const T* kv = reinterpret_cast<const T*>(&raw);
@@ -219,23 +231,42 @@ __global__ __launch_bounds__(256) void gen_attention_kernel(const T* q, int64_t 
         sum += e;
     }
     sum = block_sum_f<256>(sum, rsh);   // its barriers also order the weight writes before the reads below
-    const int G = 256 / hd, c = tid % hd, g = tid / hd;
-    const T* vb = vc + ((int64_t)b * Tmax + j0) * d + h * hd + c;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int j = g; j < n; j += G) acc += sc[j] * to_f32(vb[(int64_t)j * d]);
-    red[tid] = acc;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int u = 0; u < GA_VPRE; ++u) {
+        const int j = g + u * KG;
+        if (j < n) {
+            const float p = sc[j];
+            const T* vv = reinterpret_cast<const T*>(&vpre[u]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] += p * to_f32(vv[e]);
+        }
+    }
+    for (int j = g + GA_VPRE * KG; j < n; j += KG) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(vb + (int64_t)j * d);
+        const T* vv = reinterpret_cast<const T*>(&raw);
+        const float p = sc[j];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += p * to_f32(vv[e]);
+    }
+    __syncthreads();   // every weight read before the partial rows overwrite sc
+    float* red = sc;   // [KG][hd]
+#pragma unroll
+    for (int e = 0; e < E; ++e) red[g * hd + ch * E + e] = acc[e];
     __syncthreads();
-    if (g == 0) {
+    if (tid < hd) {
         float a = 0.f;
-        for (int gg = 0; gg < G; ++gg) a += red[gg * hd + c];
-        out[(int64_t)b * d + h * hd + c] = from_f32<T>(a / sum);
+        for (int gg = 0; gg < KG; ++gg) a += red[gg * hd + tid];
+        out[(int64_t)b * d + h * hd + tid] = from_f32<T>(a / sum);
     }
 }
 
 void gen_attention(bool bf, const void* q, int64_t ldq, const void* knew, int64_t ldk, const void* vnew, int64_t ldv,
                    void* kc, void* vc, void* out, int B, int H, int hd, int pos, int Tmax, int window, hipStream_t s) {
-    const size_t lds = sizeof(float) * (size_t)(pos + 1);
+    // the scores, or the partial output rows (256 threads x one 16-byte chunk of floats each)
+    const size_t lds = sizeof(float) * (size_t)(pos + 1 > 256 * (bf ? 8 : 4) ? pos + 1 : 256 * (bf ? 8 : 4));
     const float scale = 1.0f / sqrtf((float)hd);
     static bool attr = false;
     if (!attr) {

@@ -131,6 +131,35 @@ def copy_calibration():
                       "copy_GBps": round(8 * n / (ms * 1e-3) / 1e9, 1)}))
 
 
+def stream_ceiling():
+    """PyTorch's own streaming rates on this GPU, the practical ceiling the
+    bandwidth-bound kernels are read against: a device copy (read + write)
+    and a sum (read) of fp32 buffers of 200 MB to 3.3 GB."""
+    import torch
+
+    def timed(f, n=20):
+        for _ in range(3):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e-3
+
+    rows = []
+    for mb in (200, 800, 1650, 3300):
+        n = mb * 2**20 // 4
+        a = torch.randn(n, device="cuda:0")
+        b = torch.empty_like(a)
+        t_copy = timed(lambda: b.copy_(a))
+        t_sum = timed(lambda: a.sum())
+        rows.append({"MB": mb, "copy_GBps": round(8 * n / t_copy / 1e9, 1), "sum_GBps": round(4 * n / t_sum / 1e9, 1)})
+        del a, b
+    print(json.dumps({"stream_ceiling": rows, "peak_GBps": PEAK_HBM_GBS}))
+
+
 def rocprof_summary(d):
     """Markdown table from a rocprofv3 --stats kernel_stats.csv (per-kernel totals)."""
     import csv
@@ -389,6 +418,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-table", action="store_true", help="print per-kernel-class times to stderr")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the counter-calibration copy kernel")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="print PyTorch's copy and sum rates on this GPU (the practical streaming ceiling)")
     ap.add_argument("--rocprof-summary", metavar="DIR", help="print a table from a rocprofv3 --stats output dir")
     ap.add_argument("--trace-gaps", metavar="DIR", help="idle time per step from a rocprofv3 --kernel-trace output "
                                                          "dir (the last --steps steps)")
@@ -425,6 +456,9 @@ def main():
         return
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.stream_ceiling:
+        stream_ceiling()
         return
     if a.generate:
         generate_bench(a)

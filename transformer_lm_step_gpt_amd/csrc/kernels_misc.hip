@@ -292,16 +292,36 @@ __global__ __launch_bounds__(EMB_THREADS) void embed_sort_kernel(const int32_t* 
     }
 }
 
+// acc += rows src(0) .. src(n-1), added one by one in that order, with the
+// loads of EMB_AHEAD rows in flight at a time (a row's address comes from
+// the sorted order, so a plain loop would wait for every row in turn)
+constexpr int EMB_AHEAD = 8;
+template <typename F>
+GPT_DEV float4 emb_sum_rows(float4 acc, int n, F src) {
+    int r = 0;
+    for (; r + EMB_AHEAD <= n; r += EMB_AHEAD) {
+        float4 v[EMB_AHEAD];
+#pragma unroll
+        for (int u = 0; u < EMB_AHEAD; ++u) v[u] = load4(src(r + u));
+#pragma unroll
+        for (int u = 0; u < EMB_AHEAD; ++u) {
+            acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+        }
+    }
+    for (; r < n; ++r) {
+        const float4 v = load4(src(r));
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    return acc;
+}
+
 __global__ __launch_bounds__(256) void embed_piece_kernel(const float* dx, int d, EmbScratch e) {
     int p = blockIdx.x;
     if (p >= e.counts[1]) return;
     int r0 = e.piece_start[p], r1 = e.piece_start[p + 1];
     for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int r = r0; r < r1; ++r) {
-            float4 v = load4(dx + (int64_t)e.sorted_pos[r] * d + c);
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-        }
+        const float4 acc = emb_sum_rows(make_float4(0.f, 0.f, 0.f, 0.f), r1 - r0,
+                                        [&](int r) { return dx + (int64_t)e.sorted_pos[r0 + r] * d + c; });
         store4(e.partial + (int64_t)p * d + c, acc);
     }
 }
@@ -312,11 +332,8 @@ __global__ __launch_bounds__(256) void embed_segment_kernel(float* dwte, int d, 
     int p0 = e.seg_piece[sidx], p1 = e.seg_piece[sidx + 1];
     int64_t row = e.seg_tok[sidx];
     for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
-        float4 acc = load4(dwte + row * d + c);
-        for (int p = p0; p < p1; ++p) {
-            float4 v = load4(e.partial + (int64_t)p * d + c);
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-        }
+        const float4 acc = emb_sum_rows(load4(dwte + row * d + c), p1 - p0,
+                                        [&](int q) { return e.partial + (int64_t)(p0 + q) * d + c; });
         store4(dwte + row * d + c, acc);
     }
 }
@@ -326,11 +343,8 @@ __global__ __launch_bounds__(256) void embed_wpe_kernel(const float* dx, float* 
     int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= T * dq) return;
     int t = idx / dq, c = (idx % dq) * 4;
-    float4 acc = load4(dwpe + (int64_t)t * d + c);
-    for (int b = 0; b < B; ++b) {
-        float4 v = load4(dx + ((int64_t)b * T + t) * d + c);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
+    const float4 acc = emb_sum_rows(load4(dwpe + (int64_t)t * d + c), B,
+                                    [&](int b) { return dx + ((int64_t)b * T + t) * d + c; });
     store4(dwpe + (int64_t)t * d + c, acc);
 }
 

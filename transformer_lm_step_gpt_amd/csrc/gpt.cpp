@@ -659,13 +659,19 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
     const int gelu_or_relu = c.mlp_act == GPT_ACT_RELU2 ? 1 : 0;
     (void)gelu_or_relu;
 
+    // The first micro-step after an update (gradients logically zero) writes
+    // every gradient instead of adding to it: the weight-gradient products
+    // store, the tied head's product stores all of wte before the embedding
+    // rows are added to it, and the bias / LayerNorm reductions, dwpe and the
+    // loss sum overwrite. Every element of a tensor is written exactly once by
+    // one of them, so no zero fill is needed (0 + x and x are the same value;
+    // the padding between tensors is zero from creation and never written).
+    const bool first = h->grads_dirty;
     if (h->grads_dirty) {
-        Timed t(h, KC_MISC, 0, 4.0 * tb.n_total);
-        gk::fill_f32(w.grads, tb.n_total, 0.f, st);
-        gk::fill_f32(w.loss_sum, 1, 0.f, st);
         h->grads_dirty = false;
         h->micro_count = 0;
     }
+    const int wg_epi = first ? gk::EPI_STORE : gk::EPI_ACCUM;
     // token sort of the embedding backward, on the side stream: it waits for
     // the work queued so far on the main stream (the tokens), and the main
     // stream waits for it before the embedding gradient
@@ -700,7 +706,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
     {
         Timed t(h, KC_CE, 0, (double)M * Vp * 2 * ab + 8.0 * M);
         gk::cross_entropy(bf, w.logits, tgt, w.row_loss, M, Vp, grad_scale / (float)M, c.logit_softcap, w.err, st);
-        gk::mean_loss(w.row_loss, M, w.loss_last, w.loss_sum, st);
+        gk::mean_loss(w.row_loss, M, w.loss_last, w.loss_sum, st, first);
     }
     // ------------------------------------------------------------ backward
     // The weight-gradient products (they only read activations and upstream
@@ -721,7 +727,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         // first, beside its input gradient and the layers' input-gradient chain
         record(E_DZ, st);
         wait_ev(sw, E_DZ);
-        gk::Gemm g2 = mk_gemm(h, Vp, d, M, w.logits, Vp, false, w.lnf, d, false, G(h, tb.wte), d, false, gk::EPI_ACCUM);
+        gk::Gemm g2 = mk_gemm(h, Vp, d, M, w.logits, Vp, false, w.lnf, d, false, G(h, tb.wte), d, false, wg_epi);
         run_gemm(h, KC_GEMM_LMHEAD_BWD, g2, conc);
         gk::Gemm g = mk_gemm(h, M, d, Vp, w.logits, Vp, true, Wop(h, tb.wte), d, false, w.dln, d, bf, gk::EPI_STORE);
         run_gemm(h, KC_GEMM_LMHEAD_BWD, g);
@@ -775,14 +781,13 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
             run_gemm(h, KC_GEMM_DGRAD, g);
             record(E_DH, st);
             wait_ev(sw, E_DH);
-            gk::Gemm g2 = mk_gemm(h, d, F, M, dR_mlp, d, false, w.hact[l], F, false, G(h, li.mp_w), F, false,
-                                  gk::EPI_ACCUM);
+            gk::Gemm g2 = mk_gemm(h, d, F, M, dR_mlp, d, false, w.hact[l], F, false, G(h, li.mp_w), F, false, wg_epi);
             run_gemm(h, KC_GEMM_WGRAD, g2, conc);
         }
         {
             gk::Gemm g = mk_gemm(h, M, d, F, dh, F, true, Wop(h, li.fc_w), d, false, w.dln, d, bf, gk::EPI_STORE);
             run_gemm(h, KC_GEMM_DGRAD, g);
-            gk::Gemm g2 = mk_gemm(h, F, d, M, dh, F, false, w.ln2[l], d, false, G(h, li.fc_w), d, false, gk::EPI_ACCUM);
+            gk::Gemm g2 = mk_gemm(h, F, d, M, dh, F, false, w.ln2[l], d, false, G(h, li.fc_w), d, false, wg_epi);
             run_gemm(h, KC_GEMM_WGRAD, g2, conc);
         }
         if (!fc_b_fused) col_sum(dh, F, G(h, li.fc_b));
@@ -830,10 +835,10 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
             run_gemm(h, KC_GEMM_DGRAD, g);
             wait_ev(sw, E_DQKV);
             gk::Gemm g2 = mk_gemm(h, d, d, M, dR_attn, d, false, w.att[l], d, false, G(h, li.proj_w), d, false,
-                                  gk::EPI_ACCUM);
+                                  wg_epi);
             run_gemm(h, KC_GEMM_WGRAD, g2, conc);
             gk::Gemm g3 = mk_gemm(h, 3 * d, d, M, dqkv, 3 * d, false, w.ln1[l], d, false, G(h, li.attn_w), d, false,
-                                  gk::EPI_ACCUM);
+                                  wg_epi);
             run_gemm(h, KC_GEMM_WGRAD, g3, conc);
         }
         if (!attn_b_fused) {
@@ -866,13 +871,14 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         for (const gk::RedJob& j : h->jobs) bytes += 4.0 * j.np * j.n + 8.0 * j.n;
         Timed t(h, KC_PARTIAL_REDUCE, 0, bytes);
         gk::reduce_jobs(w.red_jobs, (int)h->jobs.size(), std::max({nbl, npc, npa}),
-                        (int)std::max<int64_t>(d, std::max<int64_t>(3 * d, F)), w.red_tmp, st);
+                        (int)std::max<int64_t>(d, std::max<int64_t>(3 * d, F)), w.red_tmp, st, first);
     }
     {
         Timed t(h, KC_EMBED_BWD, 0, 4.0 * M * d + 8.0 * M * d);
         gpt_status s = hip_check(h, hipStreamWaitEvent(st, h->ev_join, 0), "hipStreamWaitEvent");
         if (s != GPT_OK) return s;
-        gk::embed_bwd_accumulate(w.dres, G(h, tb.wte), tb.wpe >= 0 ? G(h, tb.wpe) : nullptr, B, T, d, w.emb_scratch, st);
+        gk::embed_bwd_accumulate(w.dres, G(h, tb.wte), tb.wpe >= 0 ? G(h, tb.wpe) : nullptr, B, T, d, w.emb_scratch, st,
+                                 first);
     }
     h->micro_count += 1;
     gpt_status s = hip_check(h, hipGetLastError(), "kernel launch");

@@ -33,8 +33,10 @@ void embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, in
 // embed_bwd in two parts: the token sort (depends on the tokens only, so it
 // can run early on another stream) and the accumulation that reads dx.
 void embed_bwd_sort(const int32_t* tok, int B, int T, int d, int Vp, void* scratch, hipStream_t s);
+// dwte rows += their dx rows; dwpe (+)= the position sums (overwritten when
+// overwrite_wpe: the first contribution of a pass whose gradients start empty).
 void embed_bwd_accumulate(const float* dx, float* dwte, float* dwpe, int B, int T, int d, void* scratch,
-                          hipStream_t s);
+                          hipStream_t s, bool overwrite_wpe = false);
 
 // ---------------------------------------------------------------- LayerNorm
 // y = (x - mean) rstd * g + b over rows of width d (fp32 x, act y); saves mean, rstd.
@@ -89,7 +91,10 @@ size_t reduce_jobs_tmp_floats(int njobs, int max_np, int max_n);
 // out[c] += sum over p < np of part[p * n + c] (one job, the same fixed order);
 // tmp holds ceil(np / 64) * n floats
 void reduce_rows(const float* part, int np, int n, float* out, float* tmp, hipStream_t s);
-void reduce_jobs(const RedJob* jobs, int njobs, int max_np, int max_n, float* tmp, hipStream_t s);
+// every job's out (+)= its partial sums; overwrite stores them instead (the
+// first contribution to outputs that no earlier work of the pass wrote)
+void reduce_jobs(const RedJob* jobs, int njobs, int max_np, int max_n, float* tmp, hipStream_t s,
+                 bool overwrite = false);
 
 // ---------------------------------------------------------------- cross-entropy
 // Per row of logits z (act, [M, Vp], in place): z' = cap tanh(z/cap) if cap > 0;
@@ -97,8 +102,9 @@ void reduce_jobs(const RedJob* jobs, int njobs, int max_np, int max_n, float* tm
 // (times 1 - tanh^2 with the cap). Invalid targets: loss 0, zero row, *err = 1.
 void cross_entropy(bool bf, void* z, const int32_t* y, float* row_loss, int M, int Vp, float gscale,
                    float cap, int32_t* err, hipStream_t s);
-// *loss_out = mean(row_loss[0..M)); *loss_sum += that mean (deterministic).
-void mean_loss(const float* row_loss, int M, float* loss_out, float* loss_sum, hipStream_t s);
+// *loss_out = mean(row_loss[0..M)); *loss_sum += that mean (deterministic),
+// or = that mean when first.
+void mean_loss(const float* row_loss, int M, float* loss_out, float* loss_sum, hipStream_t s, bool first = false);
 
 // ---------------------------------------------------------------- attention helpers
 // D[b, h, t] = sum_c dO[m, h*hd + c] * O[m, h*hd + c]

@@ -338,12 +338,14 @@ __global__ __launch_bounds__(256) void embed_segment_kernel(float* dwte, int d, 
     }
 }
 
-__global__ __launch_bounds__(256) void embed_wpe_kernel(const float* dx, float* dwpe, int B, int T, int d) {
+// dwpe[t] (+)= sum over b of dx[b, t] (the previous value dropped when overwrite)
+__global__ __launch_bounds__(256) void embed_wpe_kernel(const float* dx, float* dwpe, int B, int T, int d,
+                                                        int overwrite) {
     int dq = d >> 2;
     int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= T * dq) return;
     int t = idx / dq, c = (idx % dq) * 4;
-    const float4 acc = emb_sum_rows(load4(dwpe + (int64_t)t * d + c), B,
+    const float4 acc = emb_sum_rows(overwrite ? make_float4(0.f, 0.f, 0.f, 0.f) : load4(dwpe + (int64_t)t * d + c), B,
                                     [&](int b) { return dx + ((int64_t)b * T + t) * d + c; });
     store4(dwpe + (int64_t)t * d + c, acc);
 }
@@ -364,12 +366,13 @@ void embed_bwd_sort(const int32_t* tok, int B, int T, int d, int Vp, void* scrat
 }
 
 void embed_bwd_accumulate(const float* dx, float* dwte, float* dwpe, int B, int T, int d, void* scratch,
-                          hipStream_t s) {
+                          hipStream_t s, bool overwrite_wpe) {
     const int M = B * T;
     EmbScratch e = carve_emb(scratch, M, d);
     embed_piece_kernel<<<M, 256, 0, s>>>(dx, d, e);
     embed_segment_kernel<<<M, 256, 0, s>>>(dwte, d, e);
-    if (dwpe) embed_wpe_kernel<<<ceil_div((int64_t)T * (d / 4), 256), 256, 0, s>>>(dx, dwpe, B, T, d);
+    if (dwpe)
+        embed_wpe_kernel<<<ceil_div((int64_t)T * (d / 4), 256), 256, 0, s>>>(dx, dwpe, B, T, d, overwrite_wpe ? 1 : 0);
 }
 
 void embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, int B, int T, int d, int Vp,
@@ -660,21 +663,22 @@ __global__ __launch_bounds__(256) void reduce_jobs_stage1(const RedJob* __restri
 
 // out[c] += sum of the job's group sums, in group order
 __global__ __launch_bounds__(256) void reduce_jobs_stage2(const RedJob* __restrict__ jobs, int G, int max_n,
-                                                          const float* __restrict__ tmp) {
+                                                          const float* __restrict__ tmp, int overwrite) {
     const RedJob jb = jobs[blockIdx.y];
     const int c = blockIdx.x * 256 + threadIdx.x;
     if (c >= jb.n) return;
     const int ng = ceil_div(jb.np, 64);
     float a = 0.f;
     for (int grp = 0; grp < ng; ++grp) a += tmp[((int64_t)blockIdx.y * G + grp) * max_n + c];
-    jb.out[c] += a;
+    if (overwrite) jb.out[c] = a;
+    else jb.out[c] += a;
 }
 
-void reduce_jobs(const RedJob* jobs, int njobs, int max_np, int max_n, float* tmp, hipStream_t s) {
+void reduce_jobs(const RedJob* jobs, int njobs, int max_np, int max_n, float* tmp, hipStream_t s, bool overwrite) {
     if (njobs <= 0) return;
     const int G = ceil_div(max_np, 64);
     reduce_jobs_stage1<<<dim3(ceil_div(max_n, 256), G, njobs), 256, 0, s>>>(jobs, G, max_n, tmp);
-    reduce_jobs_stage2<<<dim3(ceil_div(max_n, 256), njobs), 256, 0, s>>>(jobs, G, max_n, tmp);
+    reduce_jobs_stage2<<<dim3(ceil_div(max_n, 256), njobs), 256, 0, s>>>(jobs, G, max_n, tmp, overwrite ? 1 : 0);
 }
 
 void reduce_rows(const float* part, int np, int n, float* out, float* tmp, hipStream_t s) {
@@ -1059,7 +1063,7 @@ void cross_entropy(bool bf, void* z, const int32_t* y, float* row_loss, int M, i
     else cross_entropy_kernel<float><<<M, 256, 0, s>>>((float*)z, y, row_loss, Vp, gscale, cap, err);
 }
 
-__global__ __launch_bounds__(256) void mean_loss_kernel(const float* rl, int M, float* out, float* sum) {
+__global__ __launch_bounds__(256) void mean_loss_kernel(const float* rl, int M, float* out, float* sum, int first) {
     __shared__ double sh[4];
     double a = 0.0;
     for (int i = threadIdx.x; i < M; i += 256) a += rl[i];
@@ -1070,11 +1074,11 @@ __global__ __launch_bounds__(256) void mean_loss_kernel(const float* rl, int M, 
         double t = ((sh[0] + sh[1]) + sh[2]) + sh[3];
         float mval = (float)(t / M);
         *out = mval;
-        *sum += mval;
+        *sum = first ? mval : *sum + mval;
     }
 }
-void mean_loss(const float* row_loss, int M, float* loss_out, float* loss_sum, hipStream_t s) {
-    mean_loss_kernel<<<1, 256, 0, s>>>(row_loss, M, loss_out, loss_sum);
+void mean_loss(const float* row_loss, int M, float* loss_out, float* loss_sum, hipStream_t s, bool first) {
+    mean_loss_kernel<<<1, 256, 0, s>>>(row_loss, M, loss_out, loss_sum, first ? 1 : 0);
 }
 
 // =====================================================================

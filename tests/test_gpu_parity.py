@@ -143,6 +143,46 @@ def test_determinism_bitwise():
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("which", ["tiny_fp32", "tiny_speedrun_fp32", "char_bf16"])
+def test_first_micro_step_writes_every_gradient(which):
+    """The first micro-step after an update writes every gradient element
+    (the products store, the reductions overwrite) instead of zero-filling the
+    buffer and adding. After a full step, which leaves the previous step's
+    gradients in the buffer, that micro-step must give exactly the gradients
+    of the same micro-step added onto zeros (set_grad zero-fills the buffer
+    and makes the next micro-step accumulate): a tensor or element that the
+    pass did not write would keep the previous step's value."""
+    if which == "tiny_fp32":
+        w, cfg = I.TINY_FP32, I.TINY_FP32.model
+        B, T = 4, 64
+    elif which == "tiny_speedrun_fp32":
+        w, cfg = I.TINY_FP32, TINY_SPEED
+        B, T = 3, 48
+    else:
+        w, cfg = I.CHAR_BF16, I.CHAR_BF16.model.replace(max_batch=4)
+        B, T = 4, 256
+    it = I.batches(w, B, T) if which != "tiny_speedrun_fp32" else None
+    rng = np.random.default_rng(5)
+    if it is None:
+        data = [(rng.integers(0, cfg.vocab_size, (B, T)).astype(np.int32),
+                 rng.integers(0, cfg.vocab_size, (B, T)).astype(np.int32)) for _ in range(2)]
+    else:
+        data = [next(it) for _ in range(2)]
+    grads = []
+    for zero_first in (False, True):
+        say(f"first micro-step writes: {which}, zero-filled buffer first: {zero_first}")
+        gpu = make(cfg, 3)
+        gpu.forward_backward(*data[0])
+        gpu.clip_and_adamw(6e-4, 1)
+        if zero_first:
+            gpu.set_grad(gpu.names[0], np.zeros(gpu.shapes[0], np.float32))
+        gpu.forward_backward(*data[1])
+        grads.append(gpu.grads())
+        gpu.close()
+    for n in grads[0]:
+        assert np.array_equal(grads[0][n], grads[1][n]), n
+
+
 def test_error_paths():
     from transformer_lm_step_gpt_amd.gpt import GptError
     w = I.TINY_FP32

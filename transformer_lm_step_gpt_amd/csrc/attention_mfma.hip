@@ -146,8 +146,8 @@ struct HTile {
     }
 };
 
-// Ring of ATT_NS stages, each holding two HTiles (X then Y).
-template <int HD>
+// Ring of NS stages, each holding two HTiles (X then Y).
+template <int HD, int NS = ATT_NS>
 struct TileRing {
     using TL = HTile<HD>;
     static constexpr int STAGE = 2 * TL::ELEMS;
@@ -170,7 +170,7 @@ struct TileRing {
     }
     GPT_DEV void issue_next() {
         if (issued < ntiles) {
-            bf16* st = smem + (issued % ATT_NS) * STAGE;
+            bf16* st = smem + (issued % NS) * STAGE;
             const int r0 = first + issued * ATT_BT;
             if (KEEP && r0 + ATT_BT <= T) {
                 // whole tile inside the sequence: wave-uniform base plus the lane's offset
@@ -190,8 +190,8 @@ struct TileRing {
         barrier_no_fence();
         issue_next();
     }
-    GPT_DEV const bf16* x(int u) const { return smem + (u % ATT_NS) * STAGE; }
-    GPT_DEV const bf16* y(int u) const { return smem + (u % ATT_NS) * STAGE + TL::ELEMS; }
+    GPT_DEV const bf16* x(int u) const { return smem + (u % NS) * STAGE; }
+    GPT_DEV const bf16* y(int u) const { return smem + (u % NS) * STAGE + TL::ELEMS; }
 };
 
 // Column sums over the 128 rows of a workgroup (4 waves x 32 lanes) of one
@@ -226,11 +226,13 @@ GPT_DEV void block_colsum(const f32x16 (&acc)[NDF], float scale, bool ok, float*
 
 // ============================================================== forward
 
+constexpr int ATT_FWD_NS = 2;   // forward: two stages, so four workgroups fit a CU's LDS
 template <int HD>
-__global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
+__global__ __launch_bounds__(256, HD == 64 ? 4 : 1) void attn_fwd_mfma_kernel(Attn a) {
     constexpr int NDS = HD / 16, NDF = HD / 32;
     using TL = HTile<HD>;
-    __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
+    constexpr int FNS = HD == 64 ? ATT_FWD_NS : ATT_NS;
+    __shared__ __attribute__((aligned(1024))) bf16 smem[FNS * TileRing<HD, FNS>::STAGE];
     // workgroups are dispatched x-fastest: every (batch, head) of the heaviest
     // query tile goes first (longest-first over the whole grid)
     const int qt = gridDim.y - 1 - blockIdx.y;
@@ -245,11 +247,11 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(Attn a) {
     const int kend = min(T, q0 + ATT_BQ);
     int kbeg = W > 0 ? max(0, q0 - W + 1) : 0;
     kbeg = (kbeg / ATT_BT) * ATT_BT;
-    TileRing<HD> ring{smem, (const bf16*)a.k + (int64_t)b * T * a.ldk + h * HD,
-                      (const bf16*)a.v + (int64_t)b * T * a.ldv + h * HD, a.ldk, a.ldv, kbeg,
-                      ceil_div(kend - kbeg, ATT_BT), T, w, lane};
+    TileRing<HD, FNS> ring{smem, (const bf16*)a.k + (int64_t)b * T * a.ldk + h * HD,
+                           (const bf16*)a.v + (int64_t)b * T * a.ldv + h * HD, a.ldk, a.ldv, kbeg,
+                           ceil_div(kend - kbeg, ATT_BT), T, w, lane};
     ring.init();
-    for (int s = 0; s < ATT_NS - 1; ++s) ring.issue_next();
+    for (int s = 0; s < FNS - 1; ++s) ring.issue_next();
 
     bf16x8 qf[NDS];
 #pragma unroll

@@ -610,23 +610,29 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int SK_WAVES = 8;
 constexpr int SK_LNV = 3;      // float4 per lane of a normalised row kept in registers: K <= 768
 constexpr int SK_ABATCH = 6;   // 16-byte activation pieces loaded together per thread
+constexpr int SK_SPLIT_WIDE = 2;   // waves splitting K per column group of a wide product
 
-template <int EPI, typename TC, bool LN>
+// CG groups of 16 columns per workgroup (CG = 1: all eight waves split K; CG
+// = 4, for wide products such as the head: two waves per group, so the
+// staged activations serve 64 columns)
+template <int EPI, typename TC, bool LN, int CG>
 __global__ __launch_bounds__(64 * SK_WAVES) void skinny_gemm_kernel(Gemm g) {
     extern __shared__ __attribute__((aligned(16))) bf16 As[];   // [16][K + 8]
     __shared__ f32x4_t part[SK_WAVES][64];
+    constexpr int KW = SK_WAVES / CG;   // waves splitting K in a column group
     const int K = g.K, ldl = K + 8;
     const bf16* W = (const bf16*)g.B;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int n0 = blockIdx.x * 16;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, cg = w / KW, kw = w % KW;
+    const int n0 = (blockIdx.x * CG + cg) * 16;
     const int r = lane & 15, kq = lane >> 4;
     const int nrow = min(n0 + r, g.N - 1);   // columns past N feed only unstored outputs
-    // wave w takes the k range [w K / W, (w + 1) K / W) rounded to 32-deep steps;
-    // its weight fragments are loaded first, so that their latency overlaps the
-    // staging (or LayerNorm) of the activations below
-    const int nst = K / 32, s0 = w * nst / SK_WAVES, s1 = (w + 1) * nst / SK_WAVES;
+    // wave kw of a group takes the k range [kw K / KW, (kw + 1) K / KW) rounded
+    // to 32-deep steps; its weight fragments are loaded first, so that their
+    // latency overlaps the staging (or LayerNorm) of the activations below
+    const int nst = K / 32, s0 = kw * nst / KW, s1 = (kw + 1) * nst / KW;
     const bf16* wr = W + (int64_t)nrow * g.ldb + 8 * kq;
-    constexpr int MAXST = 4096 / 32 / SK_WAVES;   // K <= 4096
+    constexpr int MAXST = 4096 / 32 / SK_WAVES;   // steps per wave: K <= 4096 / CG
+    static_assert(MAXST * 32 * KW == 4096 / CG, "weight steps per wave");
     bf16x8_t wv[MAXST];
 #pragma unroll
     for (int i = 0; i < MAXST; ++i)
@@ -635,7 +641,7 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_gemm_kernel(Gemm g) {
     // wave now, so their latency overlaps the products
     constexpr bool HAS_BIAS = EPI == EPI_BIAS || EPI == EPI_BIAS_ACT || EPI == EPI_BIAS_RESID;
     float bias_n = 0.f, res[4] = {0.f, 0.f, 0.f, 0.f};
-    if (w == 0 && n0 + r < g.N) {
+    if (kw == 0 && n0 + r < g.N) {
         if constexpr (HAS_BIAS) bias_n = g.bias[n0 + r];
         if constexpr (EPI == EPI_BIAS_RESID) {
 #pragma unroll
@@ -763,11 +769,11 @@ __global__ __launch_bounds__(64 * SK_WAVES) void skinny_gemm_kernel(Gemm g) {
         }
     part[w][lane] = acc;
     __syncthreads();
-    if (w == 0) {
-        // the waves' partial tiles, summed in wave order
-        f32x4_t t = part[0][lane];
+    if (kw == 0) {
+        // the group's partial tiles, summed in wave order
+        f32x4_t t = part[w][lane];
 #pragma unroll
-        for (int v = 1; v < SK_WAVES; ++v) t += part[v][lane];
+        for (int v = 1; v < KW; ++v) t += part[w + v][lane];
         const int n = n0 + r;
         if (n < g.N) {
 #pragma unroll
@@ -800,19 +806,29 @@ bool skinny_gemm_ok(const Gemm& g) {
            g.ldb % 8 == 0 && ((uintptr_t)g.B & 15) == 0;
 }
 
-template <int EPI, typename TC>
-static void skinny_launch(const Gemm& g, unsigned grid, size_t lds, hipStream_t s) {
+template <int EPI, typename TC, int CG>
+static void skinny_launch_cg(const Gemm& g, size_t lds, hipStream_t s) {
     static bool attr = false;
     if (!attr) {
         const int mx = (int)(sizeof(bf16) * 16 * (4096 + 8));
-        (void)hipFuncSetAttribute((const void*)skinny_gemm_kernel<EPI, TC, false>,
+        (void)hipFuncSetAttribute((const void*)skinny_gemm_kernel<EPI, TC, false, CG>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, mx);
-        (void)hipFuncSetAttribute((const void*)skinny_gemm_kernel<EPI, TC, true>,
+        (void)hipFuncSetAttribute((const void*)skinny_gemm_kernel<EPI, TC, true, CG>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, mx);
         attr = true;
     }
-    if (g.ln_g) skinny_gemm_kernel<EPI, TC, true><<<grid, 64 * SK_WAVES, lds, s>>>(g);
-    else skinny_gemm_kernel<EPI, TC, false><<<grid, 64 * SK_WAVES, lds, s>>>(g);
+    const unsigned grid = (unsigned)ceil_div(g.N, 16 * CG);
+    if (g.ln_g) skinny_gemm_kernel<EPI, TC, true, CG><<<grid, 64 * SK_WAVES, lds, s>>>(g);
+    else skinny_gemm_kernel<EPI, TC, false, CG><<<grid, 64 * SK_WAVES, lds, s>>>(g);
+}
+
+// wide products (the head) stage the activations once per 64 columns; a
+// wave holds at most MAXST 32-deep steps of weights, so with CG groups K <= 4096 / CG
+template <int EPI, typename TC>
+static void skinny_launch(const Gemm& g, unsigned, size_t lds, hipStream_t s) {
+    constexpr int CGW = SK_WAVES / SK_SPLIT_WIDE;
+    if (g.N >= 4096 && g.K <= 4096 / CGW) skinny_launch_cg<EPI, TC, CGW>(g, lds, s);
+    else skinny_launch_cg<EPI, TC, 1>(g, lds, s);
 }
 
 void skinny_gemm(const Gemm& g, hipStream_t s) {

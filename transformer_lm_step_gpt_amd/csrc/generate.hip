@@ -4,11 +4,13 @@
 //
 //   gen_embed      x[b] = wte[token at pos] + wpe[pos] for each sequence b
 //   cache_put      rows of k or v (from the qkv / q,k buffers) into the cache
-//                  [B, Tmax, d] of one layer at positions t0 ..
-//   gen_attention  one query per (sequence, head) against the cached keys and
+//                  [B, Tmax, d] of one layer at positions t0 .. (prefill)
+//   gen_attention  writes the step's key and value rows into the caches, then
+//                  one query per (sequence, head) against the cached keys and
 //                  values 0 .. pos (or the last `window` of them)
 //   gen_sample     one draw per sequence from the last position's logits:
 //                  softcap, temperature, top-k, inverse CDF in token order
+//                  (a gathered top-k path and a general token-order path)
 //   skinny_gemm    the products of a decode step (M = B <= 16 rows): each
 //                  wave streams 16 weight rows and multiplies them with the
 //                  activations held in LDS (v_mfma_f32_16x16x32_bf16)

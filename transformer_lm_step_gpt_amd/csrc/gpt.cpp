@@ -718,7 +718,7 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
     // about 12 us of idle GPU between its kernels. Not while per-class timing
     // is on (its class totals assume one stream).
     const bool conc = bf && h->timing_mask == 0;
-    enum { E_DH = 0, E_DQKV, E_DZ, S_END };
+    enum { E_DH = 0, E_DQKV, E_DZ, S_END, E_MAIN_END };
     auto record = [&](int e, hipStream_t s_) { if (conc) (void)hipEventRecord(h->ev_dep[e], s_); };
     auto wait_ev = [&](hipStream_t s_, int e) { if (conc) (void)hipStreamWaitEvent(s_, h->ev_dep[e], 0); };
     hipStream_t sw = conc ? h->side : st;
@@ -849,8 +849,12 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
         ln_bwd(w.x_in[l], mean1, rstd1, P(h, li.ln1_w), false, G(h, li.ln1_w), G(h, li.ln1_b),
                l > 0 ? G(h, tb.layers[l - 1].mp_b) : nullptr);
     }
-    record(S_END, sw);
-    wait_ev(st, S_END);   // every side-stream product is done (the side stream runs in order)
+    // The bias / LayerNorm reductions read partial sums written on the main
+    // stream only, so they run there at once; the embedding gradient (after the
+    // tied head's product and the token sort, both earlier on the side stream,
+    // and the main stream's last LayerNorm backward, which wrote dres) runs on
+    // the side stream beside them; then the main stream waits for the side.
+    record(E_MAIN_END, st);
     if (!h->jobs.empty()) {
         auto same = [](const gk::RedJob& a, const gk::RedJob& b) {
             return a.part == b.part && a.out == b.out && a.np == b.np && a.n == b.n;
@@ -875,11 +879,19 @@ gpt_status gpt_forward_backward(gpt_handle* h, const int32_t* tok, const int32_t
     }
     {
         Timed t(h, KC_EMBED_BWD, 0, 4.0 * M * d + 8.0 * M * d);
-        gpt_status s = hip_check(h, hipStreamWaitEvent(st, h->ev_join, 0), "hipStreamWaitEvent");
-        if (s != GPT_OK) return s;
-        gk::embed_bwd_accumulate(w.dres, G(h, tb.wte), tb.wpe >= 0 ? G(h, tb.wpe) : nullptr, B, T, d, w.emb_scratch, st,
-                                 first);
+        if (conc) {
+            wait_ev(sw, E_MAIN_END);
+            gk::embed_bwd_accumulate(w.dres, G(h, tb.wte), tb.wpe >= 0 ? G(h, tb.wpe) : nullptr, B, T, d, w.emb_scratch,
+                                     sw, first);
+        } else {
+            gpt_status s = hip_check(h, hipStreamWaitEvent(st, h->ev_join, 0), "hipStreamWaitEvent");
+            if (s != GPT_OK) return s;
+            gk::embed_bwd_accumulate(w.dres, G(h, tb.wte), tb.wpe >= 0 ? G(h, tb.wpe) : nullptr, B, T, d, w.emb_scratch,
+                                     st, first);
+        }
     }
+    record(S_END, sw);
+    wait_ev(st, S_END);   // every side-stream product and the embedding gradient are done
     h->micro_count += 1;
     gpt_status s = hip_check(h, hipGetLastError(), "kernel launch");
     if (s != GPT_OK) return s;

@@ -74,6 +74,31 @@ def cpu_baseline(w, seq, muon=False):
                       f"{sum(int(np.prod(s)) for _, s, _, _ in O.param_table(cfg))} parameters, {dt:.1f} s"}
 
 
+def cpu_table():
+    """The float64 CPU oracle on one sequence of each parity configuration's
+    shape, with all host threads and with one: 64 tokens of the tiny fp32
+    model, 256 of the char model and 1024 of GPT-2 124M (that one with all
+    threads only); a full step, clip and update included."""
+    from transformer_lm_step_gpt_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        threadpool_limits = None
+    rows = []
+    for w, seq, one in ((I.TINY_FP32, 64, True), (I.CHAR_BF16, 256, True), (I.GPT2_124M, 1024, False)):
+        for single in ((False, True) if one else (False,)):
+            if single and threadpool_limits is None:
+                continue
+            if single:
+                with threadpool_limits(limits=1):
+                    r = cpu_baseline(w, seq)
+                r["cores"] = 1
+            else:
+                r = cpu_baseline(w, seq)
+            rows.append({"workload": w.name, **r})
+            print(json.dumps(rows[-1]), flush=True)
+
+
 # Sources of the kernels whose HBM traffic is recorded in profiles/traffic.txt:
 # a recorded figure is used only while these files are unchanged.
 KERNEL_SOURCES = ["transformer_lm_step_gpt_amd/csrc/gemm_mfma_kernel.h", "transformer_lm_step_gpt_amd/csrc/gemm_common.h",
@@ -418,6 +443,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-table", action="store_true", help="print per-kernel-class times to stderr")
     ap.add_argument("--copy-calibration", action="store_true", help="run only the counter-calibration copy kernel")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="time the float64 CPU oracle on the parity configurations with all threads and with one")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="print PyTorch's copy and sum rates on this GPU (the practical streaming ceiling)")
     ap.add_argument("--rocprof-summary", metavar="DIR", help="print a table from a rocprofv3 --stats output dir")
@@ -459,6 +486,9 @@ def main():
         return
     if a.stream_ceiling:
         stream_ceiling()
+        return
+    if a.cpu_table:
+        cpu_table()
         return
     if a.generate:
         generate_bench(a)

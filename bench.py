@@ -45,6 +45,13 @@ def model_flops_per_token(cfg, T):
     return 6 * N + attn
 
 
+def full_square_flops_per_token(cfg, T):
+    """6 N + 12 L d T: the same N, attention counted over the full T x T
+    score matrix (the PaLM-paper convention), reported beside the causal count."""
+    return model_flops_per_token(cfg, T) - 6 * cfg.n_layer * cfg.n_embd * (T + 1) + 12 * cfg.n_layer * cfg.n_embd * T \
+        if not (cfg.window_even or cfg.window_odd) else None
+
+
 # Muon's learning rate and momentum for the --muon line (the article's defaults)
 MUON_LR, MUON_MOMENTUM = 0.02, 0.95
 
@@ -546,12 +553,18 @@ def main():
     model.set_kernel_timing_filter(dom)
     model.reset_kernel_timing()
 
+    # one event on the main stream at every step boundary: per-step times for
+    # the median and minimum beside the mean
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    bounds[0].record()
     for i in range(a.steps):
         step(i)
+        bounds[i + 1].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    per_step = sorted(bounds[i].elapsed_time(bounds[i + 1]) for i in range(a.steps))
     timed = next(r for r in model.kernel_name_timing() if r["name"] == dom)
     model.set_kernel_timing_filter(None)
     # the same steps again with no timing event anywhere (reported beside the
@@ -619,11 +632,18 @@ def main():
                    "parallelism": "single GPU"},
         "mfma_util_pct": round(100 * mfu, 2),
         "model_flops_per_token": fpt,
+        "ms_per_step_median": round(per_step[len(per_step) // 2] if len(per_step) % 2 else
+                                    0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2]), 3),
+        "ms_per_step_min": round(per_step[0], 3),
         "roofline": roof,
         "uninstrumented": {"ms_per_step": round(1e3 * dt_plain / a.steps, 3),
                            "value": round(tokens / dt_plain, 1),
                            "mfma_util_pct": round(100 * tokens / dt_plain * fpt / (PEAK_BF16_TFLOPS * 1e12), 2)},
     }
+    fsq = full_square_flops_per_token(cfg, T)
+    if fsq is not None:
+        out["full_square"] = {"model_flops_per_token": fsq,
+                              "mfma_util_pct": round(100 * tps * fsq / (PEAK_BF16_TFLOPS * 1e12), 2)}
     if a.muon:
         out["optimizer"] = {"hidden_matrices": f"muon (lr {MUON_LR}, momentum {MUON_MOMENTUM}, Nesterov, 5 "
                                                "Newton-Schulz steps in bf16)", "rest": f"adamw (lr {w.lr})"}

@@ -477,7 +477,6 @@ void layernorm_fwd(bool bf, const float* x, const float* g, const float* b, void
 }
 
 constexpr int LNB_ROWS = 32;   // rows per workgroup in the backward pass (8 per wavefront)
-constexpr int LNB_AHEAD = 2;   // rows whose loads are in flight while one is processed
 
 // partial sums: [3][nb][d] (dgamma, dbeta, column sums of the new dres) + reduction scratch
 size_t layernorm_bwd_partial_floats(int M, int d) {
@@ -485,15 +484,27 @@ size_t layernorm_bwd_partial_floats(int M, int d) {
     return (size_t)3 * nb * d + (size_t)3 * ceil_div(nb, 64) * d;
 }
 
+// dy as loaded: 4 fp32, or 4 bf16 kept packed until the row is processed
+template <typename TD> struct LnbDy { using T = float4; };
+template <> struct LnbDy<bf16> { using T = uint2; };
+GPT_DEV float4 lnb_dy_load(const float* p) { return load4(p); }
+GPT_DEV uint2 lnb_dy_load(const bf16* p) { return *reinterpret_cast<const uint2*>(p); }
+GPT_DEV float4 lnb_dy_f(const float4& v) { return v; }
+GPT_DEV float4 lnb_dy_f(const uint2& v) {
+    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                       __uint_as_float(v.y & 0xffff0000u));
+}
+
 // one row's inputs in registers: x, dy and the previous residual gradient
-template <int NV>
+template <typename TD, int NV>
 struct LnbIn {
-    float4 x[NV], dy[NV], old[NV];
+    float4 x[NV], old[NV];
+    typename LnbDy<TD>::T dy[NV];
     float mu, rs;
 };
 
 template <typename TD, int NV>
-GPT_DEV void lnb_load(LnbIn<NV>& in, const TD* __restrict__ dy, const float* __restrict__ x,
+GPT_DEV void lnb_load(LnbIn<TD, NV>& in, const TD* __restrict__ dy, const float* __restrict__ x,
                       const float* __restrict__ dres, float mu, float rs, int overwrite, int lane, int d) {
     in.mu = mu;
     in.rs = rs;
@@ -503,20 +514,24 @@ GPT_DEV void lnb_load(LnbIn<NV>& in, const TD* __restrict__ dy, const float* __r
         const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
         const bool in_row = 4 * c < d;
         in.x[i] = in_row ? load4(x + 4 * c) : z;
-        in.dy[i] = in_row ? load4(dy + 4 * c) : z;
+        in.dy[i] = in_row ? lnb_dy_load(dy + 4 * c) : typename LnbDy<TD>::T{};
         in.old[i] = (in_row && !overwrite) ? load4(dres + 4 * c) : z;
     }
 }
 
-template <typename TL, int NV>
-GPT_DEV void lnb_row(const LnbIn<NV>& in, const float4* gg, float* __restrict__ dres, TL* __restrict__ dres_lp,
-                     int lane, int d, float4* ag, float4* ab, float4* ac) {
+// One row: dx = rstd (dh - mean(dh) - xhat mean(dh xhat)), dh = dy * gamma,
+// added to the previous residual gradient; acc(q, i, a, b) adds a * b to the
+// lane's column sums q of dy * xhat (dgamma), dy (dbeta) and the new residual
+// gradient (b = 1 for the last two)
+template <typename TL, typename TD, int NV, typename ACC>
+GPT_DEV void lnb_row(const LnbIn<TD, NV>& in, const float4* gg, float* __restrict__ dres, TL* __restrict__ dres_lp,
+                     int lane, int d, ACC&& acc) {
     const float mu = in.mu, rs = in.rs;
     float4 xh[NV], dh[NV];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const float4 xv = in.x[i], dyv = in.dy[i];
+        const float4 xv = in.x[i], dyv = lnb_dy_f(in.dy[i]);
         xh[i] = make_float4((xv.x - mu) * rs, (xv.y - mu) * rs, (xv.z - mu) * rs, (xv.w - mu) * rs);
         dh[i] = make_float4(dyv.x * gg[i].x, dyv.y * gg[i].y, dyv.z * gg[i].z, dyv.w * gg[i].w);
         s1 += (dh[i].x + dh[i].y) + (dh[i].z + dh[i].w);
@@ -528,7 +543,7 @@ GPT_DEV void lnb_row(const LnbIn<NV>& in, const float4* gg, float* __restrict__ 
     for (int i = 0; i < NV; ++i) {
         const int c = lane + 64 * i;
         if (4 * c < d) {
-            const float4 old = in.old[i], dyv = in.dy[i];
+            const float4 old = in.old[i], dyv = lnb_dy_f(in.dy[i]);
             float4 o;
             o.x = old.x + rs * (dh[i].x - s1 - xh[i].x * s2);
             o.y = old.y + rs * (dh[i].y - s1 - xh[i].y * s2);
@@ -536,66 +551,86 @@ GPT_DEV void lnb_row(const LnbIn<NV>& in, const float4* gg, float* __restrict__ 
             o.w = old.w + rs * (dh[i].w - s1 - xh[i].w * s2);
             store4(dres + 4 * c, o);
             if (dres_lp) store4(dres_lp + 4 * c, o);
-            ag[i].x += dyv.x * xh[i].x; ag[i].y += dyv.y * xh[i].y;
-            ag[i].z += dyv.z * xh[i].z; ag[i].w += dyv.w * xh[i].w;
-            ab[i].x += dyv.x; ab[i].y += dyv.y; ab[i].z += dyv.z; ab[i].w += dyv.w;
-            ac[i].x += o.x; ac[i].y += o.y; ac[i].z += o.z; ac[i].w += o.w;
+            acc(0, i, dyv, xh[i]);
+            acc(1, i, dyv, make_float4(1.f, 1.f, 1.f, 1.f));
+            acc(2, i, o, make_float4(1.f, 1.f, 1.f, 1.f));
         }
     }
 }
 
-// Rows are processed with the next row's loads in flight (software pipeline).
-// dy (the gradient at the LayerNorm output) is fp32 or bf16 (TD).
+// Rows are processed with the next row's loads in flight (two row buffers).
+// dy (the gradient at the LayerNorm output) is fp32 or bf16 (TD), kept packed
+// until its row is processed. Up to d = 1024 each wave keeps its three column
+// sums in its own LDS rows (lane-private slots: 36 KiB per workgroup at
+// d = 768), so the registers hold only the row buffers and, up to d = 768,
+// three workgroups fit a CU; wider rows keep the sums in registers and stage
+// one set at a time for the workgroup's sum.
+template <int NV>
+constexpr bool lnb_acc_lds() { return NV <= 4; }
 template <typename TL, typename TD, int NV>
-__global__ __launch_bounds__(256, 2) void layernorm_bwd_kernel(const TD* __restrict__ dy, const float* __restrict__ x,
-                                                            const float* __restrict__ mean,
-                                                            const float* __restrict__ rstd, const float* __restrict__ g,
-                                                            float* __restrict__ dres, TL* __restrict__ dres_lp,
-                                                            int overwrite, float* __restrict__ part, int M, int d) {
-    __shared__ float red[4][2048 + 4];
+__global__ __launch_bounds__(256, NV <= 3 ? 3 : 2) void layernorm_bwd_kernel(
+    const TD* __restrict__ dy, const float* __restrict__ x, const float* __restrict__ mean,
+    const float* __restrict__ rstd, const float* __restrict__ g, float* __restrict__ dres, TL* __restrict__ dres_lp,
+    int overwrite, float* __restrict__ part, int M, int d) {
+    constexpr bool ACC_LDS = lnb_acc_lds<NV>();
+    constexpr int DW = 256 * NV, NSET = ACC_LDS ? 3 : 1;
+    __shared__ __attribute__((aligned(16))) float red[4][NSET][DW];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nb = gridDim.x;
-    float4 ag[NV], ab[NV], ac[NV], gg[NV];
+    float4 gg[NV];
+    float4 racc[ACC_LDS ? 1 : 3][NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        ag[i] = ab[i] = ac[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        int c = lane + 64 * i;
+        const int c = lane + 64 * i;
         gg[i] = 4 * c < d ? load4(g + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            if constexpr (ACC_LDS) *reinterpret_cast<float4*>(&red[w][ACC_LDS ? q : 0][4 * c]) = make_float4(0.f, 0.f, 0.f, 0.f);
+            else racc[ACC_LDS ? 0 : q][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
+    auto acc = [&](int q, int i, float4 a, float4 b) {
+        float4* p = ACC_LDS ? reinterpret_cast<float4*>(&red[w][ACC_LDS ? q : 0][4 * (lane + 64 * i)])
+                            : &racc[ACC_LDS ? 0 : q][i];
+        float4 v = *p;
+        v.x = fmaf(a.x, b.x, v.x); v.y = fmaf(a.y, b.y, v.y); v.z = fmaf(a.z, b.z, v.z); v.w = fmaf(a.w, b.w, v.w);
+        *p = v;
+    };
     constexpr int RPW = LNB_ROWS / 4;   // rows per wave
     const int r0 = blockIdx.x * LNB_ROWS + w * RPW;
     const int r1 = min(M, r0 + RPW);
-    // the loads of the next LNB_AHEAD rows are in flight while a row is processed
-    // (a ring of LNB_AHEAD + 1 row buffers; the unrolled loop names each one)
-    LnbIn<NV> ring[LNB_AHEAD + 1];
-    auto load_row = [&](LnbIn<NV>& in, int r) {
+    auto load_row = [&](LnbIn<TD, NV>& in, int r) {
         const int64_t o = (int64_t)r * d;
         lnb_load<TD, NV>(in, dy + o, x + o, dres + o, mean[r], rstd[r], overwrite, lane, d);
     };
-#pragma unroll
-    for (int k = 0; k < LNB_AHEAD; ++k)
-        if (r0 + k < r1) load_row(ring[k], r0 + k);
-#pragma unroll
-    for (int k = 0; k < RPW; ++k) {
-        if (r0 + k + LNB_AHEAD < r1) load_row(ring[(k + LNB_AHEAD) % (LNB_AHEAD + 1)], r0 + k + LNB_AHEAD);
-        if (r0 + k < r1) {
-            const int64_t o = (int64_t)(r0 + k) * d;
-            lnb_row<TL, NV>(ring[k % (LNB_AHEAD + 1)], gg, dres + o, dres_lp ? dres_lp + o : nullptr, lane, d, ag, ab,
-                            ac);
-        }
+    auto do_row = [&](const LnbIn<TD, NV>& in, int r) {
+        const int64_t o = (int64_t)r * d;
+        lnb_row<TL, TD, NV>(in, gg, dres + o, dres_lp ? dres_lp + o : nullptr, lane, d, acc);
+    };
+    LnbIn<TD, NV> b0, b1;
+    if (r0 < r1) load_row(b0, r0);
+#pragma unroll 1
+    for (int k = 0; k < RPW; k += 2) {
+        if (r0 + k + 1 < r1) load_row(b1, r0 + k + 1);
+        if (r0 + k < r1) do_row(b0, r0 + k);
+        if (r0 + k + 2 < r1) load_row(b0, r0 + k + 2);
+        if (r0 + k + 1 < r1) do_row(b1, r0 + k + 1);
     }
-    float4* sets[3] = {ag, ab, ac};
+    // the workgroup's partial sums, its waves added in a fixed order
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
+        if constexpr (!ACC_LDS) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            int c = lane + 64 * i;
-            if (4 * c < d) *reinterpret_cast<float4*>(&red[w][4 * c]) = sets[q][i];
+            for (int i = 0; i < NV; ++i) {
+                const int c = lane + 64 * i;
+                if (4 * c < d) *reinterpret_cast<float4*>(&red[w][0][4 * c]) = racc[ACC_LDS ? 0 : q][i];
+            }
         }
-        __syncthreads();
+        if (!ACC_LDS || q == 0) __syncthreads();
+        const int sq = ACC_LDS ? q : 0;
         for (int c = threadIdx.x; c < d; c += 256)
-            part[((int64_t)q * nb + blockIdx.x) * d + c] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
-        __syncthreads();
+            part[((int64_t)q * nb + blockIdx.x) * d + c] = ((red[0][sq][c] + red[1][sq][c]) + red[2][sq][c]) + red[3][sq][c];
+        if (!ACC_LDS) __syncthreads();
     }
 }
 

@@ -141,6 +141,22 @@ int64_t gptk_layernorm_noalloc_max_floats(void);
 gpt_status gptk_cross_entropy(int32_t M, int32_t Vp, void* z, const int32_t* y, float* row_loss, float gscale,
                               float cap, int32_t* err, int32_t bf16, void* stream);
 
+/* The speedrun block's query/key preparation (Modded-NanoGPT README (oa0.com),
+ * technique list: QK-Norm then rotary positions): per row m (position m % T),
+ * head h and each of q and k, parameter-free RMS normalisation over the head's
+ * hd values (norm = 1; eps inside the root) and the rotary rotation of each
+ * rotate-half pair (i, i + hd/2) by the angle (m % T) * base^(-2i/hd)
+ * (rope = 1). backward = 0: qkv [M, 3 H hd] (q = columns [0, H hd), k the next
+ * H hd) -> out [M, 2 H hd] (q then k). backward = 1: out is dqkv [M, 3 H hd],
+ * whose q and k parts (gradients at the prepared q and k) are replaced in
+ * place by the gradients at the raw q and k, given the same qkv. tables:
+ * caller-owned device scratch of T * hd floats (the cos and sin tables,
+ * rebuilt on every call). bf16 selects bf16 storage of qkv and out. hd even,
+ * at most 128; anything else is GPT_ERR_INVALID_ARGUMENT. */
+gpt_status gptk_qk_prep(int32_t backward, int32_t M, int32_t T, int32_t H, int32_t hd, const void* qkv, void* out,
+                        float* tables, double base, int32_t norm, int32_t rope, float eps, int32_t bf16,
+                        void* stream);
+
 /* dwte[tok[m]] += dx[m] and dwpe[t] += sum_b dx[b, t] (dwpe may be null),
  * deterministic and atomic-free; scratch holds gptk_embed_bwd_scratch_bytes. */
 gpt_status gptk_embed_bwd(const int32_t* tok, const float* dx, float* dwte, float* dwpe, int32_t B, int32_t T,

@@ -476,3 +476,54 @@ def test_colsum(lib, M, N, bf):
     assert lib.gptk_colsum(M, N, Yt.data_ptr(), N, bf, out.data_ptr(), part.data_ptr(), stream()) == 0
     torch.cuda.synchronize()
     assert relmax(host(out), out0 + host(Yt).sum(0)) < 1e-5
+
+
+# ---------------------------------------------------------------- QK-Norm and rotary positions
+
+@pytest.mark.parametrize("bf", [0, 1], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("M,T,H,hd,norm,rope", [(300, 100, 3, 128, 1, 1), (260, 64, 4, 64, 1, 1), (70, 70, 2, 16, 1, 1),
+                                                 (130, 65, 6, 128, 0, 1), (130, 65, 2, 32, 1, 0), (50, 50, 3, 24, 1, 1)])
+def test_qk_prep(lib, M, T, H, hd, norm, rope, bf):
+    """q/k RMS normalisation and rotary positions, forward and backward, against
+    the oracle's rmsnorm / rope pieces (row m at position m % T); the value
+    columns are left alone by the backward."""
+    say(f"qk prep M={M} T={T} H={H} hd={hd} norm={norm} rope={rope} bf={bf}")
+    rng = np.random.default_rng(M + 7 * hd + T)
+    d = H * hd
+    qt = dev(rng.normal(size=(M, 3 * d)) * 1.5, bf)
+    qkv = host(qt)
+    out = torch.zeros((M, 2 * d), dtype=torch.bfloat16 if bf else torch.float32, device="cuda")
+    tables = torch.zeros(T * hd, dtype=torch.float32, device="cuda")
+    assert lib.gptk_qk_prep(0, M, T, H, hd, qt.data_ptr(), out.data_ptr(), tables.data_ptr(), 10000.0, norm, rope, 1e-6,
+                            bf, stream()) == 0
+    cos, sin = O.rope_tables(T, hd, 10000.0)
+    pos = np.arange(M) % T
+    c, s = cos[pos][:, None, :], sin[pos][:, None, :]
+    gt = dev(rng.normal(size=(M, 3 * d)), bf)
+    g = host(gt)
+    ref_out, ref_g = [], g.copy()
+    for which in (0, 1):
+        x = qkv[:, which * d:(which + 1) * d].reshape(M, H, hd)
+        y, r = O.rmsnorm_fwd(x, 1e-6) if norm else (x, None)
+        ref_out.append((O.rope_fwd(y, c, s) if rope else y).reshape(M, d))
+        dy = g[:, which * d:(which + 1) * d].reshape(M, H, hd)
+        if rope:
+            dy = O.rope_bwd(dy, c, s)
+        if norm:
+            dy = O.rmsnorm_bwd(dy, y, r)
+        ref_g[:, which * d:(which + 1) * d] = dy.reshape(M, d)
+    torch.cuda.synchronize()
+    assert relmax(host(out), np.concatenate(ref_out, axis=1)) < (1e-2 if bf else 1e-5)
+    assert lib.gptk_qk_prep(1, M, T, H, hd, qt.data_ptr(), gt.data_ptr(), tables.data_ptr(), 10000.0, norm, rope, 1e-6,
+                            bf, stream()) == 0
+    torch.cuda.synchronize()
+    got = host(gt)
+    assert relmax(got[:, :2 * d], ref_g[:, :2 * d]) < (1e-2 if bf else 1e-5)
+    assert np.array_equal(got[:, 2 * d:], g[:, 2 * d:])
+
+
+def test_qk_prep_rejects_bad_shapes(lib):
+    t = torch.zeros(64, dtype=torch.float32, device="cuda")
+    for hd in (0, 3, 130):
+        assert lib.gptk_qk_prep(0, 2, 2, 1, hd, t.data_ptr(), t.data_ptr(), t.data_ptr(), 10000.0, 1, 1, 1e-6, 0,
+                                stream()) == -1

@@ -1441,6 +1441,22 @@ gpt_status gptk_cross_entropy(int32_t M, int32_t Vp, void* z, const int32_t* y, 
     return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
 }
 
+gpt_status gptk_qk_prep(int32_t backward, int32_t M, int32_t T, int32_t H, int32_t hd, const void* qkv, void* out,
+                        float* tables, double base, int32_t norm, int32_t rope, float eps, int32_t bf16,
+                        void* stream) {
+    if (M < 1 || T < 1 || H < 1 || hd < 2 || hd % 2 || hd > 128 || !qkv || !out || !tables || !(base > 0.0))
+        return GPT_ERR_INVALID_ARGUMENT;
+    const hipStream_t s = (hipStream_t)stream;
+    float* cos_t = tables;
+    float* sin_t = tables + (size_t)T * (hd / 2);
+    gk::rope_tables(cos_t, sin_t, T, hd, base, s);
+    if (backward)
+        gk::qk_prep_bwd(bf16, qkv, out, cos_t, sin_t, M, T, H, hd, norm, rope, eps, s);
+    else
+        gk::qk_prep_fwd(bf16, qkv, out, cos_t, sin_t, M, T, H, hd, norm, rope, eps, s, 0);
+    return hipGetLastError() == hipSuccess ? GPT_OK : GPT_ERR_DEVICE;
+}
+
 int64_t gptk_embed_bwd_scratch_bytes(int32_t M, int32_t d) { return (int64_t)gk::embed_bwd_scratch_bytes(M, d); }
 
 int64_t gptk_gemm_fp8_scratch_bytes(int32_t M, int32_t N, int32_t K) {

@@ -1160,8 +1160,9 @@ void attn_rowdot(bool bf, const void* dO, const void* O, float* D, int B, int T,
 }
 
 // =====================================================================
-// q/k RMS normalisation + rotary positions (one wavefront per (row, head, q|k);
-// lane i < hd/2 holds the rotate-half pair (i, i + hd/2))
+// q/k RMS normalisation + rotary positions. Portable form: one wavefront per
+// (row, head, q|k), lane i < hd/2 holding the rotate-half pair (i, i + hd/2);
+// bf16 with hd in {16, 32, 64, 128} takes the vectorised form below.
 // =====================================================================
 
 template <typename T>
@@ -1220,9 +1221,145 @@ __global__ __launch_bounds__(256) void qk_prep_bwd_kernel(const T* qkv, T* dqkv,
     if (act) { g[lane] = from_f32<T>(ga); g[lane + half] = from_f32<T>(gb); }
 }
 
+// bf16 with hd a multiple of 16: LPU = hd / 16 lanes per (row, head, q|k),
+// lane j holding elements 8j .. 8j+7 of the first half and their rotate-half
+// partners 8j + hd/2 .. in 16-byte pieces (the rotation needs no exchange
+// between lanes; the RMS sum is a butterfly over the unit's lanes)
+template <int LPU>
+GPT_DEV float unit_sum(float v) {
+#pragma unroll
+    for (int o = 1; o < LPU; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+GPT_DEV void unpack8(const bf16x8& v, float (&f)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (float)v[e];
+}
+GPT_DEV bf16x8 pack8(const float (&f)[8]) {
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (bf16)f[e];
+    return v;
+}
+GPT_DEV void load8f(const float* p, float (&f)[8]) {
+    const float4 u = reinterpret_cast<const float4*>(p)[0], w = reinterpret_cast<const float4*>(p)[1];
+    f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w; f[4] = w.x; f[5] = w.y; f[6] = w.z; f[7] = w.w;
+}
+
+template <int LPU>
+__global__ __launch_bounds__(256) void qk_prep_fwd_vec_kernel(const bf16* qkv, bf16* out, const float* cos_t,
+                                                              const float* sin_t, int M, int T_, int H, int norm,
+                                                              int rope, float eps, int pos0) {
+    constexpr int HD = 16 * LPU, HALF = HD / 2;
+    const int64_t u = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPU;   // (row, head, q|k)
+    const int j = threadIdx.x % LPU;
+    if (u >= (int64_t)M * H * 2) return;   // whole units: every lane of a unit returns together
+    const int which = (int)(u & 1), mh = (int)(u >> 1), m = mh / H, h = mh % H, d = H * HD;
+    const bf16* src = qkv + (int64_t)m * 3 * d + which * d + h * HD + 8 * j;
+    bf16* dst = out + (int64_t)m * 2 * d + which * d + h * HD + 8 * j;
+    float a[8], b[8];
+    unpack8(*reinterpret_cast<const bf16x8*>(src), a);
+    unpack8(*reinterpret_cast<const bf16x8*>(src + HALF), b);
+    if (norm) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += a[e] * a[e] + b[e] * b[e];
+        const float r = 1.0f / sqrtf(unit_sum<LPU>(ss) / HD + eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { a[e] *= r; b[e] *= r; }
+    }
+    if (rope) {
+        const int t = pos0 + m % T_;
+        float c[8], sn[8];
+        load8f(cos_t + (int64_t)t * HALF + 8 * j, c);
+        load8f(sin_t + (int64_t)t * HALF + 8 * j, sn);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float na = a[e] * c[e] - b[e] * sn[e], nb = a[e] * sn[e] + b[e] * c[e];
+            a[e] = na; b[e] = nb;
+        }
+    }
+    *reinterpret_cast<bf16x8*>(dst) = pack8(a);
+    *reinterpret_cast<bf16x8*>(dst + HALF) = pack8(b);
+}
+
+template <int LPU>
+__global__ __launch_bounds__(256) void qk_prep_bwd_vec_kernel(const bf16* qkv, bf16* dqkv, const float* cos_t,
+                                                              const float* sin_t, int M, int T_, int H, int norm,
+                                                              int rope, float eps) {
+    constexpr int HD = 16 * LPU, HALF = HD / 2;
+    const int64_t u = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPU;
+    const int j = threadIdx.x % LPU;
+    if (u >= (int64_t)M * H * 2) return;
+    const int which = (int)(u & 1), mh = (int)(u >> 1), m = mh / H, h = mh % H, d = H * HD;
+    const bf16* src = qkv + (int64_t)m * 3 * d + which * d + h * HD + 8 * j;
+    bf16* g = dqkv + (int64_t)m * 3 * d + which * d + h * HD + 8 * j;
+    float ga[8], gb[8];
+    unpack8(*reinterpret_cast<const bf16x8*>(g), ga);
+    unpack8(*reinterpret_cast<const bf16x8*>(g + HALF), gb);
+    float a[8], b[8];
+    if (norm) {
+        unpack8(*reinterpret_cast<const bf16x8*>(src), a);
+        unpack8(*reinterpret_cast<const bf16x8*>(src + HALF), b);
+    }
+    if (rope) {
+        const int t = m % T_;
+        float c[8], sn[8];
+        load8f(cos_t + (int64_t)t * HALF + 8 * j, c);
+        load8f(sin_t + (int64_t)t * HALF + 8 * j, sn);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float na = ga[e] * c[e] + gb[e] * sn[e], nb = -ga[e] * sn[e] + gb[e] * c[e];
+            ga[e] = na; gb[e] = nb;
+        }
+    }
+    if (norm) {
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += a[e] * a[e] + b[e] * b[e];
+        const float r = 1.0f / sqrtf(unit_sum<LPU>(ss) / HD + eps);
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += ga[e] * (a[e] * r) + gb[e] * (b[e] * r);
+        dot = unit_sum<LPU>(dot) / HD;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ga[e] = r * (ga[e] - a[e] * r * dot);
+            gb[e] = r * (gb[e] - b[e] * r * dot);
+        }
+    }
+    *reinterpret_cast<bf16x8*>(g) = pack8(ga);
+    *reinterpret_cast<bf16x8*>(g + HALF) = pack8(gb);
+}
+
+template <template <int> class K, typename... A>
+static bool qk_vec_launch(int hd, int64_t units, hipStream_t s, A... args) {
+    const unsigned grid = (unsigned)ceil_div(units * (hd / 16), 256);
+    switch (hd) {
+        case 16: K<1>::launch(grid, s, args...); return true;
+        case 32: K<2>::launch(grid, s, args...); return true;
+        case 64: K<4>::launch(grid, s, args...); return true;
+        case 128: K<8>::launch(grid, s, args...); return true;
+        default: return false;
+    }
+}
+template <int LPU>
+struct QkFwdVec {
+    template <typename... A>
+    static void launch(unsigned grid, hipStream_t s, A... args) { qk_prep_fwd_vec_kernel<LPU><<<grid, 256, 0, s>>>(args...); }
+};
+template <int LPU>
+struct QkBwdVec {
+    template <typename... A>
+    static void launch(unsigned grid, hipStream_t s, A... args) { qk_prep_bwd_vec_kernel<LPU><<<grid, 256, 0, s>>>(args...); }
+};
+
 void qk_prep_fwd(bool bf, const void* qkv, void* out, const float* cos_t, const float* sin_t, int M, int T, int H,
                  int hd, int norm, int rope, float eps, hipStream_t s, int pos0) {
     int grid = ceil_div((int64_t)M * H * 2, 4);
+    if (bf && qk_vec_launch<QkFwdVec>(hd, (int64_t)M * H * 2, s, (const bf16*)qkv, (bf16*)out, cos_t, sin_t, M, T, H,
+                                      norm, rope, eps, pos0))
+        return;
     if (bf)
         qk_prep_fwd_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)qkv, (bf16*)out, cos_t, sin_t, M, T, H, hd, norm,
                                                       rope, eps, pos0);
@@ -1233,6 +1370,9 @@ void qk_prep_fwd(bool bf, const void* qkv, void* out, const float* cos_t, const 
 void qk_prep_bwd(bool bf, const void* qkv, void* dqkv, const float* cos_t, const float* sin_t, int M, int T, int H,
                  int hd, int norm, int rope, float eps, hipStream_t s) {
     int grid = ceil_div((int64_t)M * H * 2, 4);
+    if (bf && qk_vec_launch<QkBwdVec>(hd, (int64_t)M * H * 2, s, (const bf16*)qkv, (bf16*)dqkv, cos_t, sin_t, M, T, H,
+                                      norm, rope, eps))
+        return;
     if (bf)
         qk_prep_bwd_kernel<bf16><<<grid, 256, 0, s>>>((const bf16*)qkv, (bf16*)dqkv, cos_t, sin_t, M, T, H, hd, norm,
                                                       rope, eps);

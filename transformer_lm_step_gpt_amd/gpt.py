@@ -122,6 +122,8 @@ _SIGS = [
                                              c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
                                              c_void_p]),
     ("gptk_layernorm_noalloc_max_floats", c_int64, []),
+    ("gptk_qk_prep", c_int32, [c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_double,
+                               c_int32, c_int32, c_float, c_int32, c_void_p]),
     ("gptk_cross_entropy", c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_float, c_float, c_void_p,
                                      c_int32, c_void_p]),
     ("gptk_embed_bwd", c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,

@@ -228,10 +228,10 @@ GPT_DEV void block_colsum(const f32x16 (&acc)[NDF], float scale, bool ok, float*
 
 constexpr int ATT_FWD_NS = 2;   // forward: two stages, so four workgroups fit a CU's LDS
 template <int HD>
-__global__ __launch_bounds__(256, HD == 64 ? 4 : 1) void attn_fwd_mfma_kernel(Attn a) {
+__global__ __launch_bounds__(256, HD == 64 ? 4 : 2) void attn_fwd_mfma_kernel(Attn a) {
     constexpr int NDS = HD / 16, NDF = HD / 32;
     using TL = HTile<HD>;
-    constexpr int FNS = HD == 64 ? ATT_FWD_NS : ATT_NS;
+    constexpr int FNS = ATT_FWD_NS;
     __shared__ __attribute__((aligned(1024))) bf16 smem[FNS * TileRing<HD, FNS>::STAGE];
     // workgroups are dispatched x-fastest: every (batch, head) of the heaviest
     // query tile goes first (longest-first over the whole grid)
@@ -466,11 +466,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma_kernel(Attn a) {
 // ============================================================== backward: dQ
 
 template <int HD>
-__global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
+__global__ __launch_bounds__(256, HD == 128 ? 2 : 1) void attn_bwd_dq_mfma_kernel(Attn a) {
     constexpr int NDS = HD / 16, NDF = HD / 32;
     using TL = HTile<HD>;
-    static_assert(2 * ATT_NS * TileRing<HD>::STAGE >= 4 * NDF * 16 * COLSUM_LD * 4, "column-sum scratch fits in the ring");
-    __shared__ __attribute__((aligned(1024))) bf16 smem[ATT_NS * TileRing<HD>::STAGE];
+    // hd 128: two stages (64 KiB of tiles, 65 KiB with the column-sum scratch), so
+    // two workgroups fit a CU; hd 64: three stages (three workgroups per CU by registers)
+    constexpr int DNS = HD == 128 ? 2 : ATT_NS;
+    constexpr int RING = DNS * TileRing<HD, DNS>::STAGE, CSUM = 2 * NDF * 16 * COLSUM_LD * 4;   // bf16 elements
+    __shared__ __attribute__((aligned(1024))) bf16 smem[RING > CSUM ? RING : CSUM];
     const int qtile = gridDim.y - 1 - blockIdx.y;   // heaviest query tiles of every head first
     const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
     const int T = a.T, W = a.window;
@@ -484,11 +487,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma_kernel(Attn a) {
     const int kend = min(T, q0 + ATT_BQ);
     int kbeg = W > 0 ? max(0, q0 - W + 1) : 0;
     kbeg = (kbeg / ATT_BT) * ATT_BT;
-    TileRing<HD> ring{smem, (const bf16*)a.k + (int64_t)b * T * a.ldk + h * HD,
+    TileRing<HD, DNS> ring{smem, (const bf16*)a.k + (int64_t)b * T * a.ldk + h * HD,
                       (const bf16*)a.v + (int64_t)b * T * a.ldv + h * HD, a.ldk, a.ldv, kbeg,
                       ceil_div(kend - kbeg, ATT_BT), T, w, lane};
     ring.init();
-    for (int s = 0; s < ATT_NS - 1; ++s) ring.issue_next();
+    for (int s = 0; s < DNS - 1; ++s) ring.issue_next();
 
     bf16x8 qf[NDS], gf[NDS];
 #pragma unroll
